@@ -1,0 +1,22 @@
+"""Float64 CPU oracle for paged flash-decode attention over an E4M3 KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
+links this package; only the tests, the smoke check and the CPU-baseline leg
+of the benchmark do.  It shares no code with the HIP library: it decodes
+E4M3 bit by bit, gathers pages with plain indexing and evaluates the softmax
+from its definition, in float64, with no blocking, fusion or online
+rescaling.
+
+Every function is pinned by the `-m "not gpu"` tests in tests/test_oracle.py
+(library routines, closed forms, invariants and a brute-force twin).  No
+function here is "parity unpinned".
+"""
+
+from .fp8pa_ref import (  # noqa: F401
+    E4M3_TABLE,
+    e4m3_decode_code,
+    bf16_bits_to_f64,
+    attended_range,
+    decode,
+    merge,
+)

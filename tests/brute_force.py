@@ -1,0 +1,88 @@
+"""Brute-force twin of the oracle for tiny inputs (pure Python loops).
+
+Written independently of oracle/: it decodes E4M3 through torch's
+float8_e4m3fn dtype (a library routine), copies the pages into a contiguous
+[seq, Hkv, D] layout first, and evaluates each attention row with scalar
+loops and the math module.  Used only to pin the oracle on tiny shapes.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+
+def _codes_to_float(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _bf16_to_float(bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def depage(cache: np.ndarray, table_row: np.ndarray, seq_len: int) -> np.ndarray:
+    """Contiguous [seq_len, Hkv, D] codes of one sequence, page by page."""
+    bt = cache.shape[1]
+    rows = []
+    for t in range(seq_len):
+        rows.append(cache[int(table_row[t // bt]), t % bt])
+    if not rows:
+        return np.zeros((0,) + cache.shape[2:], dtype=cache.dtype)
+    return np.stack(rows)
+
+
+def brute_decode(wl, key_range=None, sinks="from_workload"):
+    """Attention of every (b, i, h) row by plain loops; returns (out, lse)."""
+    B, q_len, Hq, D = wl.q_bits.shape
+    Hkv = wl.k_cache.shape[2]
+    G = Hq // Hkv
+    sk = wl.sinks if isinstance(sinks, str) else sinks
+    q = _bf16_to_float(wl.q_bits)
+    out = np.zeros((B, q_len, Hq, D))
+    lse = np.zeros((B, q_len, Hq))
+    ks_all = np.asarray(wl.k_scale, dtype=np.float64).reshape(-1)
+    vs_all = np.asarray(wl.v_scale, dtype=np.float64).reshape(-1)
+    for b in range(B):
+        L = int(wl.seq_lens[b])
+        K = _codes_to_float(depage(wl.k_cache, wl.block_table[b], L))
+        V = _codes_to_float(depage(wl.v_cache, wl.block_table[b], L))
+        for i in range(q_len):
+            pos = L - q_len + i
+            for h in range(Hq):
+                g = h // G
+                ks = ks_all[g] if ks_all.size > 1 else ks_all[0]
+                vs = vs_all[g] if vs_all.size > 1 else vs_all[0]
+                keys = []
+                for t in range(L):
+                    if t > pos:
+                        continue
+                    if wl.window > 0 and t < pos - wl.window + 1:
+                        continue
+                    if key_range is not None and not (key_range[0] <= t < key_range[1]):
+                        continue
+                    keys.append(t)
+                scores = []
+                for t in keys:
+                    acc = 0.0
+                    for d in range(D):
+                        acc += q[b, i, h, d] * (K[t, g, d] * ks)
+                    scores.append(wl.sm_scale * acc)
+                terms = list(scores)
+                if sk is not None:
+                    terms.append(float(sk[h]))
+                m = max(terms) if terms else -math.inf
+                if m == -math.inf:
+                    lse[b, i, h] = -math.inf
+                    continue
+                denom = sum(math.exp(x - m) for x in terms)
+                for d in range(D):
+                    acc = 0.0
+                    for t, s in zip(keys, scores):
+                        acc += math.exp(s - m) * (V[t, g, d] * vs)
+                    out[b, i, h, d] = acc / denom
+                lse[b, i, h] = m + math.log(denom)
+    return out, lse

@@ -1,0 +1,222 @@
+"""Seeded input generator: five named workloads plus arbitrary small shapes.
+
+Recipe (the same for every workload, drawn in this order from
+numpy.random.default_rng(seed)):
+
+1. seq_lens (fixed, a list, or uniform integers in [lo, hi]);
+2. the block table: a random permutation of the page pool handed out to the
+   sequences in order (or the identity);
+3. scales: one float32 per tensor, or one per kv head drawn U[lo, hi]
+   (k_scale first, then v_scale);
+4. q ~ N(0, 1), rounded to bf16 (round to nearest even);
+5. K then V: for every position that some query row attends,
+   N(0, 1) / scale, clamped to +-448 and rounded to E4M3 (nearest even);
+6. sinks ~ N(0, 1) float32 [Hq] when the workload has sinks.
+
+Every other byte of the pools (positions no row attends, pages no sequence
+uses) is the E4M3 NaN code 0x7F when `poison` is on (default), so a kernel
+that reads them or lets them leak produces NaN.  Unused block-table entries
+are -1.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+POISON_CODE = 0x7F
+
+# The five named workloads.  seq: ("fixed", n) | ("list", [..]) | ("uniform", lo, hi)
+CONFIGS = {
+    1: dict(name="tiny", B=1, q_len=1, Hq=8, Hkv=1, D=128, bt=16, seq=("fixed", 512),
+            table="identity", pool=None, scale=("tensor", 0.05), window=0, sinks=False,
+            sm_scale=1.0 / math.sqrt(128)),
+    2: dict(name="ragged_gqa", B=16, q_len=1, Hq=32, Hkv=8, D=128, bt=16,
+            seq=("uniform", 1024, 8192), table="perm", pool=8192,
+            scale=("per_head", 0.02, 0.1), window=0, sinks=False,
+            sm_scale=1.0 / math.sqrt(128)),
+    3: dict(name="window_sinks", B=32, q_len=1, Hq=64, Hkv=8, D=64, bt=16,
+            seq=("fixed", 32768), table="perm", pool=None, scale=("tensor", 0.05),
+            window=4096, sinks=True, sm_scale=0.125),
+    4: dict(name="long_splitkv", B=4, q_len=1, Hq=24, Hkv=4, D=256, bt=64,
+            seq=("list", [196608, 131072, 65536, 8192]), table="perm", pool=None,
+            scale=("per_head", 0.02, 0.1), window=0, sinks=False, sm_scale=0.08),
+    5: dict(name="mtp_q4", B=256, q_len=4, Hq=32, Hkv=8, D=128, bt=16,
+            seq=("uniform", 1024, 4096), table="perm", pool=None, scale=("tensor", 0.05),
+            window=2048, sinks=True, sm_scale=1.0 / math.sqrt(128)),
+}
+
+
+@dataclass
+class Workload:
+    """Host copies of every input of one decode call (numpy arrays)."""
+
+    name: str
+    q_bits: np.ndarray        # uint16 [B, q_len, Hq, D], bf16 bit patterns
+    k_cache: np.ndarray       # uint8 [num_blocks, bt, Hkv, D], E4M3 codes
+    v_cache: np.ndarray       # uint8 [num_blocks, bt, Hkv, D]
+    block_table: np.ndarray   # int32 [B, max_blocks]
+    seq_lens: np.ndarray      # int32 [B]
+    k_scale: np.ndarray       # float32 [1] or [Hkv]
+    v_scale: np.ndarray       # float32 [1] or [Hkv]
+    sinks: np.ndarray | None  # float32 [Hq] or None
+    window: int
+    sm_scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self):
+        return self.q_bits.shape[0]
+
+    @property
+    def q_len(self):
+        return self.q_bits.shape[1]
+
+    @property
+    def Hq(self):
+        return self.q_bits.shape[2]
+
+    @property
+    def D(self):
+        return self.q_bits.shape[3]
+
+    @property
+    def Hkv(self):
+        return self.k_cache.shape[2]
+
+    @property
+    def bt(self):
+        return self.k_cache.shape[1]
+
+    @property
+    def num_blocks(self):
+        return self.k_cache.shape[0]
+
+    def oracle_kwargs(self):
+        return dict(q_bits=self.q_bits, k_cache=self.k_cache, v_cache=self.v_cache,
+                    block_table=self.block_table, seq_lens=self.seq_lens,
+                    k_scale=self.k_scale, v_scale=self.v_scale, sinks=self.sinks,
+                    window=self.window, sm_scale=self.sm_scale)
+
+    def key_union(self, b):
+        """[lo, hi) of positions some query row of sequence b attends."""
+        L = int(self.seq_lens[b])
+        hi = L
+        lo = 0
+        if self.window > 0:
+            lo = max(0, L - self.q_len - self.window + 1)
+        return lo, hi
+
+    def attended_positions(self):
+        """Sum over sequences of attended positions (the union over rows)."""
+        return int(sum(self.key_union(b)[1] - self.key_union(b)[0] for b in range(self.B)))
+
+
+def _e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 codes, clamped to +-448, round to nearest even (torch cast)."""
+    import torch
+
+    t = torch.from_numpy(np.clip(x, -448.0, 448.0).astype(np.float32, copy=False))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(x.astype(np.float32, copy=False)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", pool=None,
+                  scale=("tensor", 0.05), window=0, sinks=False, sm_scale=None,
+                  poison=True, name="custom", q_zero=False, extra_table_cols=0,
+                  key_chunk=8192):
+    """Build one seeded workload.
+
+    seq_lens: an int, a list, or ("uniform", lo, hi).  scale: ("tensor", s) or
+    ("per_head", lo, hi).  table: "perm" or "identity".  pool: minimum pool
+    size in pages.  extra_table_cols adds -1 columns to every table row.
+    """
+    rng = np.random.default_rng(seed)
+    # 1. sequence lengths
+    if isinstance(seq_lens, tuple) and seq_lens and seq_lens[0] == "uniform":
+        sl = rng.integers(seq_lens[1], seq_lens[2] + 1, size=B).astype(np.int32)
+    elif np.isscalar(seq_lens):
+        sl = np.full((B,), int(seq_lens), dtype=np.int32)
+    else:
+        sl = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    pages_needed = [(int(n) + bt - 1) // bt for n in sl]
+    n_need = int(sum(pages_needed))
+    num_blocks = max(n_need, int(pool or 0), 1)
+    max_blocks = max(max(pages_needed) if pages_needed else 1, 1) + int(extra_table_cols)
+    # 2. block table
+    if table == "identity":
+        order = np.arange(num_blocks, dtype=np.int64)
+    else:
+        order = rng.permutation(num_blocks)
+    bt_arr = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = pages_needed[b]
+        bt_arr[b, :n] = order[off:off + n]
+        off += n
+    # 3. scales
+    if scale[0] == "tensor":
+        k_scale = np.array([scale[1]], dtype=np.float32)
+        v_scale = np.array([scale[1]], dtype=np.float32)
+    else:
+        k_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
+        v_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
+    # 4. queries
+    qf = rng.standard_normal((B, q_len, Hq, D), dtype=np.float32)
+    if q_zero:
+        qf[:] = 0.0
+    q_bits = _bf16_bits(qf)
+    # 5. caches
+    fill = POISON_CODE if poison else 0
+    caches = []
+    wl_tmp = Workload(name, q_bits, np.empty((0, bt, Hkv, D), np.uint8), None, bt_arr, sl,
+                      k_scale, v_scale, None, int(window), 0.0)
+    for which, sc in (("k", k_scale), ("v", v_scale)):
+        cache = np.full((num_blocks, bt, Hkv, D), fill, dtype=np.uint8)
+        flat = cache.reshape(num_blocks * bt, Hkv, D)
+        for b in range(B):
+            lo, hi = wl_tmp.key_union(b)
+            if not poison:
+                lo = 0
+                hi = pages_needed[b] * bt
+            for c0 in range(lo, hi, key_chunk):
+                c1 = min(c0 + key_chunk, hi)
+                x = rng.standard_normal((c1 - c0, Hkv, D), dtype=np.float32)
+                x /= sc.reshape(1, -1, 1) if sc.size > 1 else sc[0]
+                ts = np.arange(c0, c1)
+                phys = bt_arr[b, ts // bt].astype(np.int64) * bt + ts % bt
+                flat[phys] = _e4m3_encode(x)
+        caches.append(cache)
+    # 6. sinks
+    sk = rng.standard_normal((Hq,), dtype=np.float32) if sinks else None
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    return Workload(name=name, q_bits=q_bits, k_cache=caches[0], v_cache=caches[1],
+                    block_table=bt_arr, seq_lens=sl, k_scale=k_scale, v_scale=v_scale,
+                    sinks=sk, window=int(window), sm_scale=float(sm_scale),
+                    meta=dict(seed=seed, poison=poison))
+
+
+def make_config(k: int, seed: int | None = None, poison: bool = True) -> Workload:
+    """One of the five named workloads, seeded with 1000 + k by default."""
+    c = CONFIGS[k]
+    seq = c["seq"]
+    if seq[0] == "fixed":
+        seq_lens = seq[1]
+    elif seq[0] == "list":
+        seq_lens = list(seq[1])
+    else:
+        seq_lens = ("uniform", seq[1], seq[2])
+    return make_workload(B=c["B"], q_len=c["q_len"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"],
+                         bt=c["bt"], seq_lens=seq_lens, seed=1000 + k if seed is None else seed,
+                         table=c["table"], pool=c["pool"], scale=c["scale"],
+                         window=c["window"], sinks=c["sinks"], sm_scale=c["sm_scale"],
+                         poison=poison, name=f"cfg{k}_{c['name']}")
