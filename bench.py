@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of paged FP8 decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 1,2,3,4,5]
+
+A step is one fp8pa_decode call (split-KV partial kernel, then the LSE merge
+kernel when the plan has more than one split) over one batch of synthetic
+input already resident in HBM.  The headline workload is the ragged GQA
+decode (B=16, q_len=1, Hq=32, Hkv=8, D=128, bt=16, seq_lens U[1024, 8192]);
+the other four named workloads are measured the same way and reported under
+"per_workload".
+
+Cold-cache discipline: each workload keeps C copies of its K/V page pools
+(same block table) and the steps rotate through them, so that between two
+reads of the same bytes at least 1 GiB of other KV has streamed through the
+256 MB Infinity Cache.  The K timed steps run back to back on torch's
+current stream (the stream the library launches on), bracketed by
+torch.cuda.synchronize() and HIP events.
+
+Prints ONE JSON line (rank 0, N=1):
+  value = attended KV bytes read per step / step time, in GB/s;
+  roofline = the partial kernel's KV bytes / its average duration (the step's
+    event time minus a live measurement of the merge alone), against 8 TB/s;
+  cpu_baseline = the float64 CPU oracle on a time-bounded sample of the
+    headline workload, in the same unit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-read HBM GB/s (% of MI355X peak) and decode tokens/s, FP8 paged attn"
+PEAK_GBPS = 8000.0
+HEADLINE = 2
+MALL_FLUSH_BYTES = 1 << 30
+
+
+def kv_bytes(wl):
+    """Algorithmic KV bytes of one call: each attended K and V byte once.
+
+    Per attended token per kv head the method must read D bytes of K and D
+    of V; tokens outside every row's window are not counted.
+    """
+    return wl.attended_positions() * wl.Hkv * wl.D * 2
+
+
+def other_bytes(wl):
+    """q, out, lse, the table entries of touched pages and seq_lens."""
+    rows = wl.B * wl.q_len * wl.Hq
+    pages = 0
+    for b in range(wl.B):
+        lo, hi = wl.key_union(b)
+        if hi > lo:
+            pages += (hi - 1) // wl.bt - lo // wl.bt + 1
+    return rows * wl.D * 2 * 2 + rows * 4 + pages * 4 + wl.B * 4
+
+
+def describe(wl):
+    seq = wl.seq_lens
+    return (f"{wl.name}: B={wl.B} q_len={wl.q_len} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bt={wl.bt} "
+            f"seq_lens[min={int(seq.min())},max={int(seq.max())},sum={int(seq.sum())}] "
+            f"window={wl.window} sinks={'yes' if wl.sinks is not None else 'no'} "
+            f"sm_scale={wl.sm_scale:.6g} k_scale={'per-kv-head' if wl.k_scale.size > 1 else 'per-tensor'}")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "host.cpp", "plan.h"):
+        with open(os.path.join(ROOT, "decode_attention_paged_fp8pa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def measure(k, steps, warmup, log):
+    import torch
+
+    import decode_attention_paged_fp8pa_amd as fp
+    from workloads import make_config
+
+    t_gen = time.time()
+    wl = make_config(k)
+    log(f"[bench] cfg{k}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
+    dev = torch.device("cuda")
+    kvb = kv_bytes(wl)
+    copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / max(kvb, 1)))))
+    q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    kc0 = torch.from_numpy(wl.k_cache).to(dev)
+    vc0 = torch.from_numpy(wl.v_cache).to(dev)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(copies - 1)]
+    btab = torch.from_numpy(wl.block_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    ks = torch.from_numpy(wl.k_scale).to(dev)
+    vs = torch.from_numpy(wl.v_scale).to(dev)
+    sinks = None if wl.sinks is None else torch.from_numpy(wl.sinks).to(dev)
+    shape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
+                         max_seq_len=int(wl.seq_lens.max()))
+    plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    nws = fp.fp8pa_workspace_bytes(shape)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(tuple(wl.q_bits.shape[:3]), dtype=torch.float32, device=dev)
+
+    def step(i):
+        kc, vc = pools[i % copies]
+        fp.fp8pa_decode(shape, q, kc, vc, btab, sl, ks, vs, sinks, out, lse,
+                        ws if nws else None, nws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = e0.elapsed_time(e1) / steps
+
+    merge_ms = 0.0
+    if plan["merge_launched"]:
+        rows = wl.B * wl.q_len * wl.Hq
+        po = ws
+        pl_ptr = ws.data_ptr() + plan["workspace_lse_offset"]
+        for _ in range(3):
+            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, po, pl_ptr, sinks, out, lse)
+        torch.cuda.synchronize()
+        m0 = torch.cuda.Event(enable_timing=True)
+        m1 = torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for _ in range(steps):
+            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, po, pl_ptr, sinks, out, lse)
+        m1.record()
+        torch.cuda.synchronize()
+        merge_ms = m0.elapsed_time(m1) / steps
+        # leave the outputs as one full step writes them
+        step(0)
+        torch.cuda.synchronize()
+    partial_ms = max(step_ms - merge_ms, 1e-6)
+    res = dict(
+        workload=wl.name,
+        describe=describe(wl),
+        kv_bytes=kvb,
+        other_bytes=other_bytes(wl),
+        copies=copies,
+        plan=plan,
+        step_ms=step_ms,
+        wall_ms_per_step=wall_ms,
+        partial_ms=partial_ms,
+        merge_ms=merge_ms,
+        kv_gbps=kvb / (step_ms * 1e-3) / 1e9,
+        partial_kv_gbps=kvb / (partial_ms * 1e-3) / 1e9,
+        tokens_per_s=wl.B * wl.q_len / (step_ms * 1e-3),
+    )
+    res["pct_peak"] = 100.0 * res["kv_gbps"] / PEAK_GBPS
+    log(f"[bench] cfg{k}: step {step_ms * 1e3:.1f} us (partial {partial_ms * 1e3:.1f} us, merge "
+        f"{merge_ms * 1e3:.1f} us), KV {res['kv_gbps']:.0f} GB/s = {res['pct_peak']:.1f}% of peak, "
+        f"{res['tokens_per_s']:.3g} tok/s, splits {plan['num_splits']}, copies {copies}")
+    del pools, kc0, vc0
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def cpu_baseline(wl, budget_s, log):
+    """The float64 oracle, as it stands, on whole sequences until the budget is used."""
+    import oracle
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    ncores = len(os.sched_getaffinity(0))
+    limiter = threadpool_limits(limits=ncores)
+    t0 = time.perf_counter()
+    done_bytes = 0
+    done_tokens = 0
+    seqs = 0
+    for b in range(wl.B):
+        rows = [(b, i, h) for i in range(wl.q_len) for h in range(wl.Hq)]
+        oracle.decode(**wl.oracle_kwargs(), rows=rows)
+        lo, hi = wl.key_union(b)
+        done_bytes += (hi - lo) * wl.Hkv * wl.D * 2
+        done_tokens += wl.q_len
+        seqs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = int(infos[0].get("num_threads", ncores)) if infos else 1
+    limiter.restore_original_limits()
+    log(f"[bench] cpu oracle: {seqs} sequences in {el:.1f}s, {done_bytes / el / 1e9:.3f} GB/s")
+    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: sequences 0..{seqs - 1} of {wl.B} (all {wl.Hq} heads, "
+                      f"{done_bytes} KV bytes) in {el:.1f}s; {done_tokens / el:.3g} tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--configs", default="1,2,3,4,5")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU form in this library)", file=sys.stderr)
+        sys.exit(2)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import decode_attention_paged_fp8pa_amd as fp
+
+    fp.lib()
+    cfgs = [int(x) for x in args.configs.split(",") if x]
+    if HEADLINE not in cfgs:
+        cfgs.insert(0, HEADLINE)
+    results = {}
+    head_wl = None
+    for k in cfgs:
+        res, wl = measure(k, args.steps, args.warmup, log)
+        results[k] = res
+        if k == HEADLINE:
+            head_wl = wl
+        else:
+            del wl
+    h = results[HEADLINE]
+    traffic = load_traffic(h["workload"])
+    roof = {
+        "bound": "hbm",
+        "achieved": round(h["partial_kv_gbps"], 1),
+        "peak": PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(h["partial_kv_gbps"] / PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": "partial_mfma_kernel<128>",
+        "kernel_avg_us": round(h["partial_ms"] * 1e3, 2),
+        "algorithmic_bytes_per_launch": h["kv_bytes"],
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head_wl, args.cpu_budget, log)
+    line = {
+        "metric": METRIC,
+        "value": round(h["kv_gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-mfma+f32",
+        "data": "synthetic (seeded; E4M3 K/V of N(0,1)/scale, bf16 q ~ N(0,1))",
+        "config": {"workload": h["describe"], "parallelism": "none (1 GPU)",
+                   "pct_of_peak": round(h["pct_peak"], 2),
+                   "tokens_per_s": round(h["tokens_per_s"], 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_workload": {
+            f"cfg{k}": {
+                "workload": r["describe"], "step_us": round(r["step_ms"] * 1e3, 2),
+                "partial_us": round(r["partial_ms"] * 1e3, 2), "merge_us": round(r["merge_ms"] * 1e3, 2),
+                "kv_bytes": r["kv_bytes"], "kv_gbps": round(r["kv_gbps"], 1),
+                "partial_kv_gbps": round(r["partial_kv_gbps"], 1),
+                "pct_peak": round(r["pct_peak"], 2), "tokens_per_s": round(r["tokens_per_s"], 1),
+                "num_splits": r["plan"]["num_splits"], "grid_wgs": r["plan"]["grid_wgs"],
+                "variant": "mfma" if r["plan"]["variant"] == 1 else "dot",
+                "wall_us_per_step": round(r["wall_ms_per_step"] * 1e3, 2),
+            } for k, r in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

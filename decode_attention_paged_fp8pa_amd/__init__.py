@@ -1,0 +1,104 @@
+"""Paged flash-decode attention over an FP8 (E4M3) KV cache for MI355X.
+
+The work is done by libfp8pa.so (hand-written gfx950 HIP kernels behind a
+C ABI, include/fp8pa.h).  This package is a thin binding: `_lib` mirrors the
+C entry points one to one (fp8pa_decode, fp8pa_workspace_bytes,
+fp8pa_merge, fp8pa_plan), and `decode` below fills the shape descriptor
+from torch tensors and allocates the outputs.  PyTorch provides device
+memory and streams only.
+"""
+
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    FP8PA_FLAG_FORCE_DOT,
+    FP8PA_FLAG_FORCE_MFMA,
+    Fp8paError,
+    LIB_PATH,
+    PlanInfo,
+    Shape,
+    fp8pa_debug_e4m3_to_f32,
+    fp8pa_debug_mfma_fp8,
+    fp8pa_decode,
+    fp8pa_merge,
+    fp8pa_plan,
+    fp8pa_workspace_bytes,
+    lib,
+    make_shape,
+    status_string,
+    version,
+)
+
+__all__ = [
+    "decode",
+    "shape_for",
+    "fp8pa_decode",
+    "fp8pa_merge",
+    "fp8pa_plan",
+    "fp8pa_workspace_bytes",
+    "Fp8paError",
+    "FP8PA_FLAG_FORCE_DOT",
+    "FP8PA_FLAG_FORCE_MFMA",
+]
+
+
+def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=None,
+              max_seq_len, num_splits=0, flags=0) -> Shape:
+    """fp8pa_shape for tensors q [B, q_len, Hq, D] and k_cache [blocks, bt, Hkv, D]."""
+    B, q_len, Hq, D = q.shape
+    nb, bt, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    return make_shape(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      block_tokens=bt, num_blocks=nb, block_table_stride=block_table.stride(0),
+                      max_seq_len=int(max_seq_len), k_scale_count=k_scale.numel(),
+                      v_scale_count=v_scale.numel(), window=int(window), sm_scale=sm_scale,
+                      num_splits=int(num_splits), flags=int(flags))
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=None, *,
+           window=0, sm_scale=None, max_seq_len=None, num_splits=0, flags=0, out=None, lse=None,
+           workspace=None, stream=None):
+    """Runs fp8pa_decode on torch device tensors; returns (out bf16, lse fp32).
+
+    q bf16 [B, q_len, Hq, D]; k_cache, v_cache uint8 or float8_e4m3fn
+    [num_blocks, bt, Hkv, D]; block_table int32 [B, stride] (unit column
+    stride); seq_lens int32 [B]; k_scale, v_scale float32 [1] or [Hkv];
+    sinks float32 [Hq] or None.  max_seq_len should be given by callers that
+    must not synchronise (it is read from seq_lens otherwise).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit column stride")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens),
+                    ("k_scale", k_scale), ("v_scale", v_scale)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item())
+    shape = shape_for(q, k_cache, block_table, k_scale, v_scale, window=window, sm_scale=sm_scale,
+                      max_seq_len=max_seq_len, num_splits=num_splits, flags=flags)
+    B, q_len, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, q_len, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, q_len, Hq), dtype=torch.float32, device=q.device)
+    nbytes = fp8pa_workspace_bytes(shape, q.device.index if q.device.index is not None else 0)
+    if nbytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fp8pa_decode(shape, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, out,
+                 lse, workspace if nbytes > 0 else None, ws_bytes if nbytes > 0 else 0, stream)
+    return out, lse

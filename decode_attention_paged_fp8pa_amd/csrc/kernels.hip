@@ -1,0 +1,890 @@
+// libfp8pa device code for gfx950 (MI355X): paged flash-decode attention over
+// an E4M3 KV cache, and the C-ABI entry points that launch it.
+//
+// Method (solution record "How do I run paged decode attention over an FP8
+// KV cache for a quantized MoE serving path, with sliding windows, attention
+// sinks and a custom scale?", fields `title`/`summary`): split-KV flash
+// decode with the online softmax of FlashAttention v2/v3 (credited in the
+// fish-scales-ops README, Acknowledgments), sink and window folded in, and a
+// log-sum-exp reducer over the splits (FlashInfer PR #5591, Summary).
+//
+// MI355X design:
+//  * One wavefront owns one work item (sequence b, kv head g, row group,
+//    KV split) and walks 32-token tiles of its key range; a workgroup packs
+//    1, 2 or 4 wavefronts on adjacent kv heads, so a workgroup's loads of
+//    one token slot are neighbouring bytes of the same page.
+//  * Pages are read with raw buffer loads whose descriptor base is the page
+//    (wave-uniform, from one scalar block-table load per 16 tokens); lanes
+//    of tokens outside the attended range use an offset past the
+//    descriptor's range, which the hardware turns into zeros.  So no page
+//    outside the range is touched, no table entry of such a page is read,
+//    and NaN bytes there cannot reach an MFMA.
+//  * MFMA kernel: QK^T on v_mfma_f32_16x16x32_fp8_fp8 with keys on the M
+//    side and the query rows of one kv head on the N side (heads on the N
+//    side for small head groups: the SwapsAb choice of FlashInfer PR #5591).
+//    The bf16 query row is split into two E4M3 parts, hi + lo, under a
+//    per-row power-of-two scale, so the scores keep ~2^-8 relative
+//    precision while the K codes go straight from HBM into the MFMA.
+//    The fp32 score accumulator already holds, per lane, the 8 keys that the
+//    PV MFMA's B operand needs, so P = 2^(s - m + 8) is packed to E4M3 in
+//    place (the +8 keeps P in E4M3's normal range; it cancels in O / l).
+//    V is transposed to keys-along-K with v_perm byte shuffles in registers
+//    (no LDS).
+//  * VALU kernel ("dot"): 16 bytes per lane, D/16 lanes per key, E4M3
+//    decoded with v_cvt_pk_f32_fp8, fp32 FMAs and cross-lane reductions;
+//    used for kv heads with one or two query rows and pages under 16 tokens.
+//  * Merge kernel: one wavefront per output row.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fp8pa.h"
+#include "../../include/fp8pa_debug.h"
+#include "plan.h"
+
+namespace fp8pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// An offset past any buffer range: raw buffer loads at it return zeros.
+constexpr uint32_t kOob = 0x80000000u;
+// Word 3 of a raw (untyped, unswizzled) buffer descriptor on gfx9 parts.
+constexpr int kRsrcWord3 = 0x00020000;
+// P is stored as E4M3 of p * 2^kPShift, p in [0, 1].
+constexpr float kPShift = 8.0f;
+
+struct Params {
+  const uint16_t* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* k_scale;
+  const float* v_scale;
+  const float* sinks;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int64_t page_bytes;  // bt * Hkv * D
+  int32_t tok_stride;  // Hkv * D: bytes between token slots of a page
+  int32_t q_len, Hq, Hkv, G, rows, row_groups, hg, units, num_splits, tps;
+  int32_t bt_shift, bt_mask, table_stride, window;
+  int32_t k_per_head, v_per_head, direct;
+  float sm_scale;
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+}
+
+// Loads BYTES (4, 8 or a multiple of 16) at byte offset `off` of buffer `r`.
+template <int BYTES>
+__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint32_t* dst) {
+  if constexpr (BYTES == 4) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (BYTES == 8) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+    static_assert(BYTES % 16 == 0, "load size");
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, 0);
+      dst[4 * i + 0] = v.x;
+      dst[4 * i + 1] = v.y;
+      dst[4 * i + 2] = v.z;
+      dst[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// 4x4 byte transpose: out[x] byte y = in[y] byte x.
+__device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                             uint32_t* out) {
+  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.b0 a1.b0 a0.b1 a1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);  // a2.b0 a3.b0 a2.b1 a3.b1
+  const uint32_t t2 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.b2 a1.b2 a0.b3 a1.b3
+  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);  // a2.b2 a3.b2 a2.b3 a3.b3
+  out[0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+}
+
+__device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
+  return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// Work item of this workgroup: (b, kv head group, row group, split).
+struct Work {
+  int b, g, rg, split;
+};
+
+__device__ __forceinline__ Work work_of(const Params& p) {
+  Work w;
+  const int wg = blockIdx.x;
+  w.split = wg / p.units;
+  const int unit = wg - w.split * p.units;
+  w.rg = unit % p.row_groups;
+  const int t = unit / p.row_groups;
+  const int ngg = p.Hkv / p.hg;
+  const int gg = t % ngg;
+  w.b = t / ngg;
+  w.g = gg * p.hg + int(threadIdx.x >> 6);
+  return w;
+}
+
+// Query row `r` (0 <= r < rows) of kv head g: its token index, head and
+// attended key range [klo, khi) for a sequence of L tokens.
+struct Row {
+  bool valid;
+  int qi, h, klo, khi;
+  size_t out_row;  // (b * q_len + qi) * Hq + h
+};
+
+__device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int L) {
+  Row o;
+  o.valid = r < p.rows;
+  const int rr = o.valid ? r : 0;
+  o.qi = rr / p.G;
+  o.h = g * p.G + (rr - o.qi * p.G);
+  const int pos = L - p.q_len + o.qi;
+  o.khi = min(pos + 1, L);
+  o.klo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  if (!o.valid || o.khi <= o.klo) {
+    o.klo = 0;
+    o.khi = 0;
+  }
+  o.out_row = ((size_t)b * p.q_len + o.qi) * p.Hq + o.h;
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// FP8-MFMA partial kernel.
+//
+// Lane l of a wavefront: n = l % 16 is the MFMA N column, i.e. the query row
+// of the row group; qd = l / 16 is the lane group.  Per 32-token tile:
+//   K, group A (tokens 0..15) and B (16..31): lane holds D/4 bytes of token n
+//     of the group, bytes [D/4 * qd, D/4 * (qd + 1)) of its row;
+//   V: lane holds D/16 bytes (d = D/16 * n ...) of the 8 tokens
+//     kap(qd, j) = 4 qd + j (j < 4) and 16 + 4 qd + j - 4 (j >= 4), which are
+//     exactly the tokens whose scores the QK accumulators give this lane.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
+  constexpr int S = D / 16;       // V bytes per lane per token
+  constexpr int KB = D / 4;       // K bytes per lane per token
+  constexpr int KSTEPS = D / 32;  // QK k-steps of 32 dims
+  constexpr int KW = KB / 4;      // K dwords per lane per group
+  constexpr int SW = S / 4;       // V dwords per lane per token
+
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int qd = lane >> 4;
+  const Work w = work_of(p);
+  const int L = p.seq_lens[w.b];
+  const int ulo = p.window > 0 ? max(0, L - p.q_len - p.window + 1) : 0;
+  const int uhi = L;
+  const int tile0 = ulo / kTileTokens;
+  const int tile1 = uhi > ulo ? (uhi - 1) / kTileTokens + 1 : tile0;
+  const int ts = tile0 + w.split * p.tps;
+  const int te = min(ts + p.tps, tile1);
+  const Row row = row_of(p, w.b, w.g, w.rg * kRowsMfma + n, L);
+
+  if (ts >= te && !p.direct) {
+    if (row.valid && qd == 0) p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
+    return;
+  }
+
+  // ---- stage the query row: per-row power-of-two scale, E4M3 hi + lo parts
+  long qhi[KSTEPS], qlo[KSTEPS];
+  float cr;  // score scale into log2 units
+  {
+    float qf[KB];
+    if (row.valid) {
+      const uint16_t* qrow = p.q + row.out_row * D + KB * qd;
+#pragma unroll
+      for (int i = 0; i < KB / 8; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * i);
+        qf[8 * i + 0] = bf16_lo(v.x);
+        qf[8 * i + 1] = bf16_hi(v.x);
+        qf[8 * i + 2] = bf16_lo(v.y);
+        qf[8 * i + 3] = bf16_hi(v.y);
+        qf[8 * i + 4] = bf16_lo(v.z);
+        qf[8 * i + 5] = bf16_hi(v.z);
+        qf[8 * i + 6] = bf16_lo(v.w);
+        qf[8 * i + 7] = bf16_hi(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) qf[i] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) amax = fmaxf(amax, fabsf(qf[i]));
+    amax = fmaxf(amax, xor_shfl(amax, 16));
+    amax = fmaxf(amax, xor_shfl(amax, 32));
+    // 2^(7 - floor(log2 amax)) puts the largest element in [128, 256).
+    int se = 0;
+    if (amax > 0.f) {
+      const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+      se = min(max(7 - e, -120), 120);
+    }
+    const float qs = __uint_as_float(uint32_t(se + 127) << 23);
+    const float ks = p.k_scale[p.k_per_head ? w.g : 0];
+    cr = p.sm_scale * ks * kLog2e / qs;
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = qf[8 * c + j] * qs;
+      uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
+      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
+      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
+      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
+      const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
+      const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
+      const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
+      const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
+      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - d0.x, x[1] - d0.y, l0, false);
+      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x, x[3] - d1.y, l0, true);
+      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x, x[5] - d2.y, l1, false);
+      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
+      qhi[c] = as_long(h0, h1);
+      qlo[c] = as_long(l0, l1);
+    }
+  }
+
+  // ---- online softmax state (log2 units); the sink enters as a score whose
+  // value vector is zero when this split writes the final output.
+  const float sink2 = (p.sinks && p.direct && row.valid) ? p.sinks[row.h] * kLog2e : -INFINITY;
+  float m = sink2;
+  float lsum = (qd == 0 && sink2 > -INFINITY) ? exp2_fast(kPShift) : 0.f;
+  f32x4 O[S];
+#pragma unroll
+  for (int e = 0; e < S; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tok = p.tok_stride;
+  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D;
+  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D;
+  const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
+  const uint32_t koff = uint32_t(n * tok + KB * qd);
+  uint32_t voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) voff[j] = uint32_t((4 * qd + j) * tok + S * n);
+
+  for (int tt = ts; tt < te; ++tt) {
+    const int kb = tt * kTileTokens;
+    uint32_t kr[2][KW];
+    uint32_t vr[8][SW];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const int gk = kb + 16 * grp;
+      Rsrc rk, rv;
+      if (gk < uhi && gk + 16 > ulo) {
+        const int page = btab[gk >> p.bt_shift];
+        const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
+        rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + base), 0, 16 * tok, kRsrcWord3);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + base), 0, 16 * tok, kRsrcWord3);
+      } else {
+        rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase_g, 0, 0, kRsrcWord3);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase_g, 0, 0, kRsrcWord3);
+      }
+      const int kt = gk + n;
+      buf_load<KB>(rk, (kt >= ulo && kt < uhi) ? koff : kOob, kr[grp]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vt = gk + 4 * qd + j;
+        buf_load<S>(rv, (vt >= ulo && vt < uhi) ? voff[j] : kOob, vr[4 * grp + j]);
+      }
+    }
+
+    // S^T = K . Q^T for both 16-token groups
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const long ka = as_long(kr[0][2 * c], kr[0][2 * c + 1]);
+      const long kbv = as_long(kr[1][2 * c], kr[1][2 * c + 1]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qhi[c], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[c], sb, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[c], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[c], sb, 0, 0, 0);
+    }
+
+    // scale, mask, online softmax
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+      const float s = j < 4 ? sa[j] : sb[j - 4];
+      x[j] = (key >= row.klo && key < row.khi) ? s * cr : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    mx = fmaxf(mx, xor_shfl(mx, 16));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2_fast(m - muse);
+    const float off = muse - kPShift;
+    float pj[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pj[j] = exp2_fast(x[j] - off);
+      psum += pj[j];
+    }
+    lsum = lsum * alpha + psum;
+    m = mnew;
+#pragma unroll
+    for (int e = 0; e < S; ++e) O[e] *= alpha;
+
+    uint32_t p0 = 0, p1 = 0;
+    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0], pj[1], p0, false);
+    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2], pj[3], p0, true);
+    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4], pj[5], p1, false);
+    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6], pj[7], p1, true);
+    const long P = as_long(p0, p1);
+
+    // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
+#pragma unroll
+    for (int wd = 0; wd < SW; ++wd) {
+      uint32_t lo4[4], hi4[4];
+      transpose4x4(vr[0][wd], vr[1][wd], vr[2][wd], vr[3][wd], lo4);
+      transpose4x4(vr[4][wd], vr[5][wd], vr[6][wd], vr[7][wd], hi4);
+#pragma unroll
+      for (int x4 = 0; x4 < 4; ++x4) {
+        const int e = 4 * wd + x4;
+        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(lo4[x4], hi4[x4]), P, O[e], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: l over the 4 lane groups, normalise, write
+  lsum += xor_shfl(lsum, 16);
+  lsum += xor_shfl(lsum, 32);
+  if (!row.valid) return;
+  const bool empty = !(lsum > 0.f);
+  const float vs = p.v_scale[p.v_per_head ? w.g : 0];
+  const float inv = empty ? 0.f : vs / lsum;
+  const float lse = empty ? -INFINITY : (m + log2_fast(lsum) - kPShift) * kLn2;
+  // O[e][i] is output dim S * (4 qd + i) + e of this lane's row.
+  if (p.direct) {
+    uint16_t* orow = p.out + row.out_row * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pk[S / 2];
+#pragma unroll
+      for (int e = 0; e < S; e += 2) pk[e / 2] = pack_bf16x2(O[e][i] * inv, O[e + 1][i] * inv);
+      uint16_t* dst = orow + S * (4 * qd + i);
+      if constexpr (S == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+      } else {
+#pragma unroll
+        for (int v = 0; v < S / 8; ++v)
+          reinterpret_cast<u32x4*>(dst)[v] = u32x4{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
+      }
+    }
+    if (p.lse && qd == 0) p.lse[row.out_row] = lse;
+  } else {
+    const size_t slot = row.out_row * p.num_splits + w.split;
+    if (!empty) {
+      float* prow = p.part_o + slot * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = prow + S * (4 * qd + i);
+#pragma unroll
+        for (int v = 0; v < S / 4; ++v)
+          reinterpret_cast<f32x4*>(dst)[v] =
+              f32x4{O[4 * v][i] * inv, O[4 * v + 1][i] * inv, O[4 * v + 2][i] * inv, O[4 * v + 3][i] * inv};
+      }
+    }
+    if (qd == 0) p.part_lse[slot] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU dot-product partial kernel: D/16 lanes per token, 16 bytes per lane,
+// 4 query rows per wavefront.  Lane l: token kk = l / (D/16) of a round,
+// chunk c = l % (D/16), dims [16 c, 16 c + 16).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void partial_dot_kernel(Params p) {
+  constexpr int LPK = D / 16;    // lanes per token
+  constexpr int KPI = 64 / LPK;  // tokens per round
+  constexpr int R = kTileTokens / KPI;
+  constexpr int RPG = kRowsDot;
+
+  const int lane = threadIdx.x & 63;
+  const int kk = lane / LPK;
+  const int c = lane % LPK;
+  const Work w = work_of(p);
+  const int L = p.seq_lens[w.b];
+  const int ulo = p.window > 0 ? max(0, L - p.q_len - p.window + 1) : 0;
+  const int uhi = L;
+  const int tile0 = ulo / kTileTokens;
+  const int tile1 = uhi > ulo ? (uhi - 1) / kTileTokens + 1 : tile0;
+  const int ts = tile0 + w.split * p.tps;
+  const int te = min(ts + p.tps, tile1);
+
+  Row rows[RPG];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) rows[rr] = row_of(p, w.b, w.g, w.rg * RPG + rr, L);
+
+  if (ts >= te && !p.direct) {
+    if (lane == 0) {
+#pragma unroll
+      for (int rr = 0; rr < RPG; ++rr)
+        if (rows[rr].valid) p.part_lse[rows[rr].out_row * p.num_splits + w.split] = -INFINITY;
+    }
+    return;
+  }
+
+  const float ks = p.k_scale[p.k_per_head ? w.g : 0];
+  const float cq = p.sm_scale * ks * kLog2e;
+  float qf[RPG][16];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+    if (rows[rr].valid) {
+      const uint16_t* qrow = p.q + rows[rr].out_row * D + 16 * c;
+      const u32x4 a = reinterpret_cast<const u32x4*>(qrow)[0];
+      const u32x4 b = reinterpret_cast<const u32x4*>(qrow)[1];
+      const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qf[rr][2 * j] = bf16_lo(wv[j]) * cq;
+        qf[rr][2 * j + 1] = bf16_hi(wv[j]) * cq;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qf[rr][j] = 0.f;
+    }
+  }
+
+  float m[RPG], lsum[RPG], acc[RPG][16];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+    const float sink2 =
+        (p.sinks && p.direct && rows[rr].valid) ? p.sinks[rows[rr].h] * kLog2e : -INFINITY;
+    m[rr] = sink2;
+    lsum[rr] = (kk == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[rr][j] = 0.f;
+  }
+
+  const int tok = p.tok_stride;
+  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D + 16 * c;
+  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D + 16 * c;
+  const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
+
+  for (int tt = ts; tt < te; ++tt) {
+    const int kb = tt * kTileTokens;
+    u32x4 kr[R], vr[R];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+      const int key = kb + rho * KPI + kk;
+      kr[rho] = u32x4{0u, 0u, 0u, 0u};
+      vr[rho] = u32x4{0u, 0u, 0u, 0u};
+      if (key >= ulo && key < uhi) {
+        const int page = btab[key >> p.bt_shift];
+        const size_t off = (size_t)page * (size_t)p.page_bytes + (size_t)(key & p.bt_mask) * tok;
+        kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
+        vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
+      }
+    }
+    float x[R][RPG];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+      float kf[16];
+      const uint32_t kw[4] = {kr[rho].x, kr[rho].y, kr[rho].z, kr[rho].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], true);
+        kf[4 * j + 0] = lo.x;
+        kf[4 * j + 1] = lo.y;
+        kf[4 * j + 2] = hi.x;
+        kf[4 * j + 3] = hi.y;
+      }
+      const int key = kb + rho * KPI + kk;
+#pragma unroll
+      for (int rr = 0; rr < RPG; ++rr) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) d = fmaf(kf[j], qf[rr][j], d);
+#pragma unroll
+        for (int s = 1; s < LPK; s <<= 1) d += xor_shfl(d, s);
+        x[rho][rr] = (key >= rows[rr].klo && key < rows[rr].khi) ? d : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+      float mx = x[0][rr];
+#pragma unroll
+      for (int rho = 1; rho < R; ++rho) mx = fmaxf(mx, x[rho][rr]);
+#pragma unroll
+      for (int s = LPK; s < 64; s <<= 1) mx = fmaxf(mx, xor_shfl(mx, s));
+      const float mnew = fmaxf(m[rr], mx);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2_fast(m[rr] - muse);
+      m[rr] = mnew;
+      lsum[rr] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[rr][j] *= alpha;
+#pragma unroll
+      for (int rho = 0; rho < R; ++rho) x[rho][rr] = exp2_fast(x[rho][rr] - muse);
+    }
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+      float vf[16];
+      const uint32_t vw[4] = {vr[rho].x, vr[rho].y, vr[rho].z, vr[rho].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], true);
+        vf[4 * j + 0] = lo.x;
+        vf[4 * j + 1] = lo.y;
+        vf[4 * j + 2] = hi.x;
+        vf[4 * j + 3] = hi.y;
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPG; ++rr) {
+        const float pp = x[rho][rr];
+        lsum[rr] += pp;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[rr][j] = fmaf(pp, vf[j], acc[rr][j]);
+      }
+    }
+  }
+
+  // reduce over the tokens of a round (lanes with equal c)
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+#pragma unroll
+    for (int s = LPK; s < 64; s <<= 1) {
+      lsum[rr] += xor_shfl(lsum[rr], s);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[rr][j] += xor_shfl(acc[rr][j], s);
+    }
+  }
+  if (kk != 0) return;
+  const float vs = p.v_scale[p.v_per_head ? w.g : 0];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr) {
+    if (!rows[rr].valid) continue;
+    const bool empty = !(lsum[rr] > 0.f);
+    const float inv = empty ? 0.f : vs / lsum[rr];
+    const float lse = empty ? -INFINITY : (m[rr] + log2_fast(lsum[rr])) * kLn2;
+    if (p.direct) {
+      uint16_t* dst = p.out + rows[rr].out_row * D + 16 * c;
+      uint32_t pk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(acc[rr][2 * j] * inv, acc[rr][2 * j + 1] * inv);
+      reinterpret_cast<u32x4*>(dst)[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      reinterpret_cast<u32x4*>(dst)[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+      if (p.lse && c == 0) p.lse[rows[rr].out_row] = lse;
+    } else {
+      const size_t slot = rows[rr].out_row * p.num_splits + w.split;
+      if (!empty) {
+        float* dst = p.part_o + slot * D + 16 * c;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          reinterpret_cast<f32x4*>(dst)[v] = f32x4{acc[rr][4 * v] * inv, acc[rr][4 * v + 1] * inv,
+                                                   acc[rr][4 * v + 2] * inv, acc[rr][4 * v + 3] * inv};
+      }
+      if (c == 0) p.part_lse[slot] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge: one wavefront per row, D/64 dims per lane.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows, int Hq,
+                                                     const float* __restrict__ po,
+                                                     const float* __restrict__ pl,
+                                                     const float* __restrict__ sinks,
+                                                     uint16_t* __restrict__ out,
+                                                     float* __restrict__ lse_out) {
+  constexpr int E = D / 64;
+  const int row = blockIdx.x * 4 + int(threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* lrow = pl + (size_t)row * num_splits;
+  const float sink2 = sinks ? sinks[row % Hq] * kLog2e : -INFINITY;
+  float M = sink2;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lrow[s] * kLog2e);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float Lsum = 0.f;
+  if (M > -INFINITY) {
+    const float* obase = po + (size_t)row * num_splits * D + E * lane;
+    for (int s = 0; s < num_splits; ++s) {
+      const float ls = lrow[s];
+      if (ls == -INFINITY) continue;
+      const float wgt = exp2_fast(ls * kLog2e - M);
+      Lsum += wgt;
+      const float* src = obase + (size_t)s * D;
+      if constexpr (E == 1) {
+        acc[0] = fmaf(wgt, src[0], acc[0]);
+      } else if constexpr (E == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+        acc[0] = fmaf(wgt, v.x, acc[0]);
+        acc[1] = fmaf(wgt, v.y, acc[1]);
+      } else {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+        acc[0] = fmaf(wgt, v.x, acc[0]);
+        acc[1] = fmaf(wgt, v.y, acc[1]);
+        acc[2] = fmaf(wgt, v.z, acc[2]);
+        acc[3] = fmaf(wgt, v.w, acc[3]);
+      }
+    }
+    if (sink2 > -INFINITY) Lsum += exp2_fast(sink2 - M);
+  }
+  const bool empty = !(Lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / Lsum;
+  uint16_t* dst = out + (size_t)row * D + E * lane;
+  if constexpr (E == 1) {
+    dst[0] = uint16_t(f32_to_bf16(acc[0] * inv));
+  } else if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
+  if (lse_out && lane == 0) lse_out[row] = empty ? -INFINITY : (M + log2_fast(Lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostics: the conversion instruction and the MFMA operand layout the
+// kernels rely on.
+// ---------------------------------------------------------------------------
+__global__ void debug_e4m3_kernel(const uint8_t* codes, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(uint32_t(codes[i]), false);
+  out[i] = v.x;
+}
+
+__global__ void debug_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  uint32_t aw[2], bw[2];
+  for (int h = 0; h < 2; ++h) {
+    uint32_t va = 0, vb = 0;
+    for (int j = 0; j < 4; ++j) {
+      va |= uint32_t(a[n * 32 + 8 * qd + 4 * h + j]) << (8 * j);   // A[m = n][k]
+      vb |= uint32_t(b[(8 * qd + 4 * h + j) * 16 + n]) << (8 * j);  // B[k][n]
+    }
+    aw[h] = va;
+    bw[h] = vb;
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(aw[0], aw[1]), as_long(bw[0], bw[1]), acc,
+                                                   0, 0, 0);
+  for (int i = 0; i < 4; ++i) c[(4 * qd + i) * 16 + n] = acc[i];
+}
+
+// ---------------------------------------------------------------------------
+// Host helpers
+// ---------------------------------------------------------------------------
+std::atomic<int> g_cu_count[64];
+
+int cu_count_of(int dev) {
+  if (dev >= 0 && dev < 64) {
+    const int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+    return -1;
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+template <int D>
+hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
+  const dim3 grid(pl.grid_wgs), block(64 * pl.hg);
+  if (pl.variant == kVariantMfma)
+    partial_mfma_kernel<D><<<grid, block, 0, st>>>(prm);
+  else
+    partial_dot_kernel<D><<<grid, block, 0, st>>>(prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int D, int num_splits, int num_rows, int Hq, const float* po,
+                        const float* plse, const float* sinks, uint16_t* out, float* lse,
+                        hipStream_t st) {
+  if (num_rows == 0) return hipSuccess;
+  const dim3 grid((num_rows + 3) / 4), block(256);
+  switch (D) {
+    case 64: merge_kernel<64><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
+    case 128: merge_kernel<128><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
+    default: merge_kernel<256><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp8pa
+
+using namespace fp8pa;
+
+extern "C" {
+
+fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t* bytes) {
+  if (!shape || !bytes) return FP8PA_ERR_INVALID_ARG;
+  Plan pl;
+  fp8pa_status st = make_plan(shape, 1, &pl);
+  if (st != FP8PA_OK) return st;
+  const int cu = cu_count_of(device);
+  if (cu < 1) return FP8PA_ERR_HIP;
+  st = make_plan(shape, cu, &pl);
+  if (st != FP8PA_OK) return st;
+  *bytes = pl.ws_bytes;
+  return FP8PA_OK;
+}
+
+fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                          const float* sinks, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!shape) return FP8PA_ERR_INVALID_ARG;
+  Plan pl;
+  fp8pa_status st = make_plan(shape, 1, &pl);  // shape checks before touching the GPU
+  if (st != FP8PA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !k_scale || !v_scale || !out)
+    return FP8PA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4) || (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)) ||
+      (workspace && !aligned(workspace, kWorkspaceAlign)))
+    return FP8PA_ERR_MISALIGNED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
+  const int cu = cu_count_of(dev);
+  if (cu < 1) return FP8PA_ERR_HIP;
+  st = make_plan(shape, cu, &pl);
+  if (st != FP8PA_OK) return st;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
+    return FP8PA_ERR_WORKSPACE_TOO_SMALL;
+
+  Params prm;
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k_cache = static_cast<const uint8_t*>(k_cache);
+  prm.v_cache = static_cast<const uint8_t*>(v_cache);
+  prm.block_table = block_table;
+  prm.seq_lens = seq_lens;
+  prm.k_scale = k_scale;
+  prm.v_scale = v_scale;
+  prm.sinks = sinks;
+  prm.out = static_cast<uint16_t*>(out);
+  prm.lse = lse;
+  prm.part_o = pl.direct ? nullptr : static_cast<float*>(workspace);
+  prm.part_lse =
+      pl.direct ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.off_lse);
+  prm.page_bytes = int64_t(pl.bt) * pl.Hkv * pl.D;
+  prm.tok_stride = pl.Hkv * pl.D;
+  prm.q_len = pl.q_len;
+  prm.Hq = pl.Hq;
+  prm.Hkv = pl.Hkv;
+  prm.G = pl.G;
+  prm.rows = pl.rows;
+  prm.row_groups = pl.row_groups;
+  prm.hg = pl.hg;
+  prm.units = pl.units;
+  prm.num_splits = pl.num_splits;
+  prm.tps = pl.tps;
+  prm.bt_shift = pl.bt_shift;
+  prm.bt_mask = pl.bt - 1;
+  prm.table_stride = shape->block_table_stride;
+  prm.window = shape->window > 0 ? shape->window : 0;
+  prm.k_per_head = shape->k_scale_count > 1 ? 1 : 0;
+  prm.v_per_head = shape->v_scale_count > 1 ? 1 : 0;
+  prm.direct = pl.direct;
+  prm.sm_scale = shape->sm_scale;
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (pl.D) {
+    case 64: e = launch_partial<64>(pl, prm, hs); break;
+    case 128: e = launch_partial<128>(pl, prm, hs); break;
+    default: e = launch_partial<256>(pl, prm, hs); break;
+  }
+  if (e != hipSuccess) return FP8PA_ERR_HIP;
+  if (!pl.direct) {
+    e = launch_merge(pl.D, pl.num_splits, pl.B * pl.q_len * pl.Hq, pl.Hq, prm.part_o, prm.part_lse,
+                     sinks, prm.out, lse, hs);
+    if (e != hipSuccess) return FP8PA_ERR_HIP;
+  }
+  return FP8PA_OK;
+}
+
+fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_heads,
+                         int32_t head_dim, const float* partial_o, const float* partial_lse,
+                         const float* sinks, void* out, float* lse, void* stream) {
+  const fp8pa_status st = check_merge_args(num_splits, num_rows, num_q_heads, head_dim);
+  if (st != FP8PA_OK) return st;
+  if (!partial_o || !partial_lse || !out) return FP8PA_ERR_INVALID_ARG;
+  if (!aligned(partial_o, 16) || !aligned(out, 16) || !aligned(partial_lse, 4) ||
+      (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
+    return FP8PA_ERR_MISALIGNED;
+  const hipError_t e = launch_merge(head_dim, num_splits, num_rows, num_q_heads, partial_o,
+                                    partial_lse, sinks, static_cast<uint16_t*>(out), lse,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!codes || !out))) return FP8PA_ERR_INVALID_ARG;
+  if (n == 0) return FP8PA_OK;
+  debug_e4m3_kernel<<<dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      codes, out, n);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, void* stream) {
+  if (!a || !b || !c) return FP8PA_ERR_INVALID_ARG;
+  debug_mfma_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(a, b, c);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+const char* fp8pa_version(void) {
+  return "fp8pa 0.1.0 (HIP, gfx950; FP8-MFMA and VALU partial kernels, LSE merge)";
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal launch plan shared by the host planner (host.cpp) and the kernel
+// launcher (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/fp8pa.h"
+
+namespace fp8pa {
+
+constexpr int kTileTokens = 32;      // tokens per tile: one PV MFMA k-step (16x16x32 fp8)
+constexpr int kRowsMfma = 16;        // query rows per wavefront: the MFMA N dimension
+constexpr int kRowsDot = 4;          // query rows per wavefront in the VALU dot kernel
+constexpr int kTargetWavesPerCu = 8; // wavefronts the split plan aims to put on each CU
+constexpr size_t kWorkspaceAlign = 256;
+
+enum Variant : int32_t { kVariantDot = 0, kVariantMfma = 1 };
+
+struct Plan {
+  int32_t variant;
+  int32_t B, q_len, Hq, Hkv, D, G;
+  int32_t rows;            // G * q_len query rows per kv head
+  int32_t rpg;             // rows per wavefront (row group)
+  int32_t row_groups;
+  int32_t hg;              // kv heads (wavefronts) per workgroup
+  int32_t units;           // B * (Hkv / hg) * row_groups
+  int32_t num_splits;
+  int32_t tps;             // tiles per split
+  int32_t bt, bt_shift;
+  int32_t grid_wgs;
+  int32_t direct;          // 1: the partial kernel writes the final output (one split)
+  size_t ws_bytes;         // 0 when direct
+  size_t off_lse;          // byte offset of partial_lse in the workspace
+};
+
+// Validates `s` (host-known fields only) and fills `plan` for a device with
+// `cu_count` compute units.
+fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan);
+
+// Validates fp8pa_merge's scalar arguments.
+fp8pa_status check_merge_args(int32_t num_splits, int32_t num_rows, int32_t num_q_heads,
+                              int32_t head_dim);
+
+}  // namespace fp8pa

@@ -1,0 +1,191 @@
+/*
+ * fp8pa.h: paged flash-decode attention over an FP8 (OCP E4M3) KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one named by the solution record "How do I run paged
+ * decode attention over an FP8 KV cache for a quantized MoE serving path,
+ * with sliding windows, attention sinks and a custom scale?"
+ * (cerinamroth.com, fields `title` and `summary`): decode-time attention of
+ * new query tokens against a paged E4M3 key/value cache, with grouped KV
+ * heads (`install.environment.special_requirements` of that record), an
+ * optional sliding window, per-head attention-sink logits and a
+ * caller-supplied softmax scale.  For every sequence b, query token i and
+ * query head h, with g = h / (Hq / Hkv) and pos = seq_lens[b] - q_len + i:
+ *
+ *   K[t] = e4m3(k_cache[block_table[b][t / bt], t % bt, g, :]) * k_scale[g]
+ *   V[t] = e4m3(v_cache[...same page and slot...]) * v_scale[g]
+ *   s_t  = sm_scale * dot(q[b, i, h, :], K[t])       for attended t
+ *   out  = sum_t e^{s_t} V[t] / (sum_t e^{s_t} + e^{sinks[h]})
+ *   lse  = ln(sum_t e^{s_t} + e^{sinks[h]})            (natural log)
+ *
+ * Attended keys: 0 <= t <= pos, and t >= pos - window + 1 when window > 0
+ * (the last `window` positions, the query's own included).  The sink term
+ * is absent when `sinks` is NULL.  A row with nothing to attend gets
+ * out = 0 and lse = -inf (or the sink).  The cache writer multiplies by
+ * 1 / k_scale before encoding (gist "Qwen3.8-27B ... on a single RTX 5090",
+ * kernel `reshape_and_cache_nvfp4_kernel`), so codes decode to code * scale.
+ *
+ * Work is a split-KV partial pass plus a log-sum-exp merge of the splits, the
+ * structure of FlashInfer PR #5591 (Summary: split producers and one LSE
+ * reducer; workspace commit: caller-owned workspace carved into partial O
+ * and partial LSE, no device allocation on any call path).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; they must
+ *    stay valid until the work queued on `stream` has finished.  The library
+ *    allocates nothing, keeps no per-call state and never synchronises; the
+ *    only state it holds is a cache of each device's compute-unit count.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is queued on it and the call returns at once; a call can be
+ *    captured into a hipGraph from its first use.
+ *  - Errors are reported as a status; nothing is printed, thrown or aborted.
+ *    Host-checkable preconditions are checked before any work is queued.
+ *    Device-resident values (seq_lens, block_table) are not checked, as that
+ *    would need a synchronisation; see fp8pa_decode for their preconditions.
+ */
+#ifndef FP8PA_H_
+#define FP8PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8pa_status {
+  FP8PA_OK = 0,
+  FP8PA_ERR_INVALID_ARG = 1,        /* a null required pointer, a bad size or count */
+  FP8PA_ERR_UNSUPPORTED = 2,        /* a shape no kernel variant handles (e.g. head_dim 96) */
+  FP8PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  FP8PA_ERR_MISALIGNED = 4,         /* a pointer breaks the documented alignment */
+  FP8PA_ERR_HIP = 5                 /* the HIP runtime reported an error */
+} fp8pa_status;
+
+/* fp8pa_shape.flags bits.  Both are for testing; production calls pass 0. */
+#define FP8PA_FLAG_FORCE_DOT  1 /* use the VALU dot-product kernel */
+#define FP8PA_FLAG_FORCE_MFMA 2 /* use the FP8-MFMA kernel (needs block_tokens >= 16) */
+
+/* Host-known description of one decode call. */
+typedef struct fp8pa_shape {
+  int32_t batch;              /* B >= 1 sequences */
+  int32_t q_len;              /* query tokens per sequence, >= 1 (q_len > 1: draft
+                                 tokens, causal among themselves) */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D: 64, 128 or 256 */
+  int32_t block_tokens;       /* bt: tokens per page, a power of two in [1, 1024] */
+  int32_t num_blocks;         /* pages in each of the two pools, >= 1 */
+  int32_t block_table_stride; /* elements between rows of block_table, >= 1 */
+  int32_t max_seq_len;        /* an upper bound of every seq_lens[b], >= 1; sizes the
+                                 split plan and the workspace */
+  int32_t k_scale_count;      /* 1 (per tensor) or Hkv (per kv head) */
+  int32_t v_scale_count;      /* 1 or Hkv */
+  int32_t window;             /* <= 0: none; W > 0: the last W positions */
+  float sm_scale;             /* softmax scale applied to q.K; finite */
+  int32_t num_splits;         /* 0: the library plans; > 0 caps the KV splits */
+  int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
+} fp8pa_shape;
+
+/* The plan one call will run (see fp8pa_plan). */
+typedef struct fp8pa_plan_info {
+  int32_t variant;          /* 0 = VALU dot kernel, 1 = FP8-MFMA kernel */
+  int32_t num_splits;       /* KV splits per (sequence, kv head, row group) */
+  int32_t tiles_per_split;  /* 32-token tiles per split */
+  int32_t tile_tokens;      /* tokens per tile (32) */
+  int32_t heads_per_wg;     /* kv heads (one wavefront each) per workgroup */
+  int32_t rows_per_group;   /* query rows (q heads x q tokens) per wavefront */
+  int32_t row_groups;       /* ceil(Hq / Hkv * q_len / rows_per_group) */
+  int32_t grid_wgs;         /* workgroups of the partial kernel */
+  int32_t merge_launched;   /* 1 when num_splits > 1 and a merge kernel follows */
+  int32_t reserved;         /* 0 */
+  uint64_t workspace_bytes; /* bytes fp8pa_decode needs in `workspace` */
+  uint64_t workspace_lse_offset; /* byte offset of the partial LSE block in the
+                                    workspace; the partial outputs start at 0.
+                                    Both blocks use fp8pa_merge's layout
+                                    ([B*q_len*Hq rows][num_splits](x head_dim)). */
+} fp8pa_plan_info;
+
+/*
+ * fp8pa_plan: the plan fp8pa_decode would run for `shape` on a device with
+ * `cu_count` compute units.  Pure host arithmetic; no GPU is touched.
+ * Returns FP8PA_ERR_INVALID_ARG / FP8PA_ERR_UNSUPPORTED for shapes that
+ * fp8pa_decode rejects.  The plan is a deterministic function of its
+ * arguments, so a captured graph replays the same launches.
+ */
+fp8pa_status fp8pa_plan(const fp8pa_shape* shape, int32_t cu_count, fp8pa_plan_info* out);
+
+/*
+ * fp8pa_workspace_bytes: bytes of device workspace fp8pa_decode needs for
+ * `shape` on HIP device `device` (its compute-unit count enters the plan).
+ * 0 means no workspace.  Host only; queries the device attribute once.
+ */
+fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t* bytes);
+
+/*
+ * fp8pa_decode: out[b, i, h, :] and lse[b, i, h] for every row, as defined at
+ * the top of this file, on the current HIP device.
+ *
+ *   q            bf16  [B, q_len, Hq, D] contiguous
+ *   k_cache      e4m3  [num_blocks, bt, Hkv, D] contiguous (token-major pages)
+ *   v_cache      e4m3  [num_blocks, bt, Hkv, D] contiguous
+ *   block_table  int32 [B, block_table_stride]; entry j of row b is the page
+ *                that holds tokens [j*bt, (j+1)*bt) of sequence b
+ *   seq_lens     int32 [B]; tokens of each sequence, its q_len new ones included
+ *   k_scale      float [k_scale_count], v_scale float [v_scale_count]
+ *   sinks        float [Hq] or NULL
+ *   out          bf16  [B, q_len, Hq, D] contiguous (written)
+ *   lse          float [B, q_len, Hq] or NULL (written when not NULL)
+ *   workspace    device bytes, at least fp8pa_workspace_bytes(); may be NULL
+ *                when that is 0.  Contents on entry are ignored.
+ *
+ * Alignment: q, k_cache, v_cache and out 16 bytes; workspace 256 bytes;
+ * block_table, seq_lens, scales, sinks and lse 4 bytes.
+ * Device-side preconditions (not checked): q_len <= seq_lens[b] <= max_seq_len,
+ * and block_table[b][j] in [0, num_blocks) for every page j that holds an
+ * attended token.  Entries of pages holding no attended token are never
+ * read and may be -1; cache bytes of tokens no row attends are never used
+ * (they may hold NaN codes).
+ * Returns FP8PA_ERR_WORKSPACE_TOO_SMALL when workspace_bytes is short and
+ * FP8PA_ERR_HIP when a launch fails.
+ */
+fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, const float* k_scale,
+                          const float* v_scale, const float* sinks, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8pa_merge: the log-sum-exp merge of split-KV partials (FlashInfer PR
+ * #5591, Summary: one LSE reducer after the split producers).  For each row
+ * r < num_rows, with M = max(partial_lse[r, s], sink):
+ *   out[r, :] = sum_s e^{lse_s - M} partial_o[r, s, :] / L,
+ *   lse[r]    = M + ln L,   L = sum_s e^{lse_s - M} + e^{sink - M}.
+ * A split with lse_s = -inf contributes nothing (its partial_o is not read);
+ * a row with no finite term gets out = 0, lse = -inf.
+ *
+ *   partial_o    float [num_rows, num_splits, head_dim]
+ *   partial_lse  float [num_rows, num_splits], natural log
+ *   sinks        float [num_q_heads] or NULL; row r uses sinks[r % num_q_heads]
+ *   out          bf16  [num_rows, head_dim]
+ *   lse          float [num_rows] or NULL
+ * head_dim is 64, 128 or 256; num_splits >= 1; num_rows >= 0.  partial_o and
+ * out 16-byte aligned, the rest 4-byte aligned.  This is the kernel
+ * fp8pa_decode runs after its partial pass; it also merges partials that
+ * another device computed over its own slice of each sequence.
+ */
+fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_heads,
+                         int32_t head_dim, const float* partial_o, const float* partial_lse,
+                         const float* sinks, void* out, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* fp8pa_status_string(fp8pa_status status);
+
+/* Library version and build description (static text). */
+const char* fp8pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8PA_H_ */

@@ -1,0 +1,43 @@
+/*
+ * fp8pa_debug.h: two diagnostic entry points of libfp8pa.  They expose the
+ * hardware behaviour the decode kernels rely on, so a test can check it
+ * against the definitions directly:
+ *
+ *  - the E4M3 decode done by gfx950's v_cvt_pk_f32_fp8, which must be the
+ *    OCP "e4m3fn" variant named on the FlashInfer page
+ *    `flashinfer.gemm.fp8_qkv_qknorm_rope` (Parameters: torch.float8_e4m3fn),
+ *    not the FNUZ variant of earlier CDNA parts;
+ *  - the operand and result lane layout of v_mfma_f32_16x16x32_fp8_fp8 that
+ *    the decode kernels assume.
+ *
+ * Same conventions as fp8pa.h: device pointers owned by the caller, work
+ * queued on `stream` (a hipStream_t passed as void*), a status returned.
+ */
+#ifndef FP8PA_DEBUG_H_
+#define FP8PA_DEBUG_H_
+
+#include <stdint.h>
+
+#include "fp8pa.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* out[i] = value of E4M3 code codes[i] as decoded by the hardware conversion
+ * instruction, for i < n.  codes: uint8 [n]; out: float [n]. */
+fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
+
+/* c = a x b for one 16x16x32 FP8 MFMA: a is E4M3 [16][32] (row-major, M x K),
+ * b is E4M3 [32][16] (K x N), c is float [16][16] row-major.  The kernel
+ * loads the operands and stores the result with the lane layout the decode
+ * kernels use (lane l: A row l%16 and B column l%16, k = 8*(l/16) .. +7;
+ * result rows 4*(l/16) + i, column l%16), so c equals the exact product only
+ * if that layout is the hardware's. */
+fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8PA_DEBUG_H_ */

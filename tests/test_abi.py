@@ -1,0 +1,196 @@
+"""C-ABI checks that need no GPU: exported symbols, the planner, validation.
+
+fp8pa_plan is pure host arithmetic, and fp8pa_decode / fp8pa_merge check
+every host-known argument before their first HIP call, so these error paths
+run on any host.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import decode_attention_paged_fp8pa_amd as fp
+from decode_attention_paged_fp8pa_amd import _lib
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(fp8pa_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "fp8pa_decode" in names and "fp8pa_merge" in names and "fp8pa_workspace_bytes" in names
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings_and_version():
+    assert fp.status_string(0) == "ok"
+    for s in range(1, 6):
+        assert fp.status_string(s) not in ("ok", "unknown status")
+    assert "gfx950" in fp.version()
+
+
+def cfg_shape(k, **over):
+    c = CONFIGS[k]
+    seq = c["seq"]
+    max_seq = {"fixed": lambda: seq[1], "list": lambda: max(seq[1]), "uniform": lambda: seq[2]}[seq[0]]()
+    bt = c["bt"]
+    kw = dict(batch=c["B"], q_len=c["q_len"], num_q_heads=c["Hq"], num_kv_heads=c["Hkv"],
+              head_dim=c["D"], block_tokens=bt, num_blocks=max(c["pool"] or 0, 1 << 16),
+              block_table_stride=(max_seq + bt - 1) // bt, max_seq_len=max_seq,
+              k_scale_count=c["Hkv"] if c["scale"][0] == "per_head" else 1,
+              v_scale_count=c["Hkv"] if c["scale"][0] == "per_head" else 1, window=c["window"],
+              sm_scale=c["sm_scale"], num_splits=0, flags=0)
+    kw.update(over)
+    return fp.make_shape(**kw)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_plan_of_each_workload(k):
+    s = cfg_shape(k)
+    p = fp.fp8pa_plan(s, 256)
+    c = CONFIGS[k]
+    rows = c["Hq"] // c["Hkv"] * c["q_len"]
+    assert p["variant"] == 1  # every named workload has >= 3 rows per kv head and bt >= 16
+    assert p["rows_per_group"] == 16 and p["row_groups"] == math.ceil(rows / 16)
+    assert c["Hkv"] % p["heads_per_wg"] == 0
+    units = c["B"] * (c["Hkv"] // p["heads_per_wg"]) * p["row_groups"]
+    assert p["grid_wgs"] == units * p["num_splits"]
+    # the splits cover every tile a sequence can span
+    max_keys = s.max_seq_len if c["window"] <= 0 else min(s.max_seq_len, c["window"] + c["q_len"] - 1)
+    n_tiles = math.ceil(max_keys / 32) + (1 if c["window"] > 0 else 0)
+    assert p["num_splits"] * p["tiles_per_split"] >= n_tiles
+    assert (p["num_splits"] - 1) * p["tiles_per_split"] < n_tiles
+    rows_total = c["B"] * c["q_len"] * c["Hq"]
+    if p["num_splits"] == 1:
+        assert p["merge_launched"] == 0 and p["workspace_bytes"] == 0
+    else:
+        po = rows_total * p["num_splits"] * c["D"] * 4
+        pl = rows_total * p["num_splits"] * 4
+        want = math.ceil(po / 256) * 256 + math.ceil(pl / 256) * 256
+        assert p["merge_launched"] == 1 and p["workspace_bytes"] == want
+
+
+def test_plan_is_deterministic_and_forced_splits():
+    s = cfg_shape(4)
+    assert fp.fp8pa_plan(s, 256) == fp.fp8pa_plan(s, 256)
+    for n in (1, 2, 7, 64):
+        p = fp.fp8pa_plan(cfg_shape(4, num_splits=n), 256)
+        assert 1 <= p["num_splits"] <= n
+    assert fp.fp8pa_plan(cfg_shape(4, num_splits=1), 256)["workspace_bytes"] == 0
+
+
+def test_variant_selection():
+    # one query row per kv head (MHA decode): the VALU dot kernel
+    s = fp.make_shape(batch=2, q_len=1, num_q_heads=8, num_kv_heads=8, head_dim=128,
+                      block_tokens=16, num_blocks=64, block_table_stride=32, max_seq_len=512,
+                      sm_scale=0.1)
+    assert fp.fp8pa_plan(s, 256)["variant"] == 0
+    # pages of 8 tokens: only the dot kernel handles them
+    s.block_tokens = 8
+    s.block_table_stride = 64
+    s.num_q_heads = 32
+    assert fp.fp8pa_plan(s, 256)["variant"] == 0
+    s.flags = fp.FP8PA_FLAG_FORCE_MFMA
+    with pytest.raises(fp.Fp8paError) as e:
+        fp.fp8pa_plan(s, 256)
+    assert e.value.status == _lib.FP8PA_ERR_UNSUPPORTED
+    s.block_tokens = 16
+    s.block_table_stride = 32
+    assert fp.fp8pa_plan(s, 256)["variant"] == 1
+    s.flags = fp.FP8PA_FLAG_FORCE_DOT
+    p = fp.fp8pa_plan(s, 256)
+    assert p["variant"] == 0 and p["rows_per_group"] == 4 and p["row_groups"] == 1
+
+
+BAD = [
+    (dict(batch=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(q_len=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), _lib.FP8PA_ERR_INVALID_ARG),      # not a multiple of Hkv = 8
+    (dict(head_dim=96), _lib.FP8PA_ERR_UNSUPPORTED),
+    (dict(head_dim=512), _lib.FP8PA_ERR_UNSUPPORTED),
+    (dict(block_tokens=24), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(block_tokens=2048), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(block_table_stride=10), _lib.FP8PA_ERR_INVALID_ARG),  # too short for max_seq_len
+    (dict(max_seq_len=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(k_scale_count=3), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(v_scale_count=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(sm_scale=float("nan")), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(sm_scale=float("inf")), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(flags=4), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(flags=3), _lib.FP8PA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("over,status", BAD)
+def test_plan_rejects_bad_shapes(over, status):
+    with pytest.raises(fp.Fp8paError) as e:
+        fp.fp8pa_plan(cfg_shape(2, **over), 256)
+    assert e.value.status == status
+
+
+def test_plan_rejects_bad_cu_count_and_q_len_above_max_seq():
+    with pytest.raises(fp.Fp8paError):
+        fp.fp8pa_plan(cfg_shape(2), 0)
+    with pytest.raises(fp.Fp8paError):
+        fp.fp8pa_plan(cfg_shape(5, max_seq_len=3, block_table_stride=1), 256)
+
+
+def _call_decode(shape, **ptrs):
+    base = dict(q=0x10000, k=0x20000, v=0x30000, bt=0x40000, sl=0x50000, ks=0x60000, vs=0x70000,
+                sinks=None, out=0x80000, lse=None, ws=None, ws_bytes=0)
+    base.update(ptrs)
+    L = _lib.lib()
+    return L.fp8pa_decode(ctypes.byref(shape), base["q"], base["k"], base["v"], base["bt"],
+                          base["sl"], base["ks"], base["vs"], base["sinks"], base["out"],
+                          base["lse"], base["ws"], base["ws_bytes"], None)
+
+
+def test_decode_checks_pointers_before_the_gpu():
+    s = cfg_shape(3)
+    for name in ("q", "k", "v", "bt", "sl", "ks", "vs", "out"):
+        assert _call_decode(s, **{name: None}) == _lib.FP8PA_ERR_INVALID_ARG, name
+    for name, addr in (("q", 0x10008), ("k", 0x20004), ("v", 0x30001), ("out", 0x80002),
+                       ("bt", 0x40002), ("lse", 0x90001), ("sinks", 0xa0003), ("ws", 0xb0010)):
+        assert _call_decode(s, **{name: addr}) == _lib.FP8PA_ERR_MISALIGNED, name
+    bad = cfg_shape(3, head_dim=80)
+    assert _call_decode(bad) == _lib.FP8PA_ERR_UNSUPPORTED
+    assert _lib.lib().fp8pa_decode(None, 1, 1, 1, 1, 1, 1, 1, None, 1, None, None, 0, None) \
+        == _lib.FP8PA_ERR_INVALID_ARG
+
+
+def test_merge_checks_arguments_before_the_gpu():
+    L = _lib.lib()
+    assert L.fp8pa_merge(0, 4, 8, 128, 0x1000, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_merge(2, -1, 8, 128, 0x1000, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_merge(2, 4, 0, 128, 0x1000, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_merge(2, 4, 8, 100, 0x1000, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_UNSUPPORTED
+    assert L.fp8pa_merge(2, 4, 8, 128, None, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_merge(2, 4, 8, 128, 0x1000, 0x2000, None, None, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_merge(2, 4, 8, 128, 0x1004, 0x2000, None, 0x3000, None, None) == _lib.FP8PA_ERR_MISALIGNED
+    assert L.fp8pa_merge(2, 4, 8, 128, 0x1000, 0x2002, None, 0x3000, None, None) == _lib.FP8PA_ERR_MISALIGNED
+
+
+def test_debug_entry_points_check_arguments():
+    L = _lib.lib()
+    assert L.fp8pa_debug_e4m3_to_f32(None, None, -1, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_e4m3_to_f32(None, None, 0, None) == _lib.FP8PA_OK
+    assert L.fp8pa_debug_mfma_fp8(None, 0x1000, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG

@@ -1,0 +1,262 @@
+"""GPU parity of libfp8pa against the float64 oracle, through the C ABI.
+
+Small cases compare every output element; the five named workloads run at
+full size in the launch configuration the benchmark times and compare
+sampled rows (the oracle computes rows one by one).  Invariance tests
+compare GPU runs with each other bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_harness import compare, run, sample_rows, to_host, upload
+from workloads import make_config, make_workload
+
+torch = pytest.importorskip("torch")
+fp = pytest.importorskip("decode_attention_paged_fp8pa_amd")
+
+pytestmark = pytest.mark.gpu
+
+DOT = fp.FP8PA_FLAG_FORCE_DOT
+MFMA = fp.FP8PA_FLAG_FORCE_MFMA
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp.lib()  # fails loudly when the library is not built
+
+
+# ------------------------------------------------------------- hardware pins
+
+def test_hw_e4m3_decode_matches_oracle_table():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    fp.fp8pa_debug_e4m3_to_f32(codes, out, 256)
+    got = out.cpu().numpy().astype(np.float64)
+    want = oracle.E4M3_TABLE
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_hw_mfma_fp8_layout():
+    rng = np.random.default_rng(0)
+    a = rng.integers(0, 0x78, size=(16, 32)).astype(np.uint8)   # finite codes of either sign below
+    b = rng.integers(0, 0x78, size=(32, 16)).astype(np.uint8)
+    a |= (rng.integers(0, 2, size=a.shape) << 7).astype(np.uint8)
+    c = torch.empty((16, 16), dtype=torch.float32, device="cuda")
+    fp.fp8pa_debug_mfma_fp8(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), c)
+    want = oracle.E4M3_TABLE[a] @ oracle.E4M3_TABLE[b]
+    np.testing.assert_allclose(c.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------- small, every element
+
+SMALL = {
+    "cfg1_twin": dict(B=1, q_len=1, Hq=8, Hkv=1, D=128, bt=16, seq_lens=[512]),
+    "gqa4_ragged": dict(B=4, q_len=1, Hq=32, Hkv=8, D=128, bt=16, seq_lens=[33, 700, 129, 1000],
+                        scale=("per_head", 0.02, 0.1)),
+    "d64_window_sinks": dict(B=2, q_len=1, Hq=64, Hkv=8, D=64, bt=16, seq_lens=[300, 517],
+                             window=100, sinks=True),
+    "d256_bt64": dict(B=3, q_len=1, Hq=24, Hkv=4, D=256, bt=64, seq_lens=[1000, 65, 200],
+                      scale=("per_head", 0.02, 0.1), sm_scale=0.08),
+    "mtp4_window_sinks": dict(B=4, q_len=4, Hq=32, Hkv=8, D=128, bt=16, seq_lens=[20, 300, 4, 155],
+                              window=40, sinks=True),
+    "rows32_two_groups": dict(B=2, q_len=2, Hq=16, Hkv=1, D=128, bt=32, seq_lens=[100, 250]),
+    "g3_q3_window1": dict(B=2, q_len=3, Hq=6, Hkv=2, D=64, bt=16, seq_lens=[50, 3], window=1,
+                          sinks=True),
+    "d256_bt128_long": dict(B=1, q_len=1, Hq=16, Hkv=2, D=256, bt=128, seq_lens=[2000]),
+    "q4_window5": dict(B=2, q_len=4, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[64, 97], window=5),
+    "seq_eq_qlen": dict(B=2, q_len=4, Hq=8, Hkv=2, D=64, bt=16, seq_lens=[4, 4], sinks=True),
+    "tiny_seqs": dict(B=4, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[1, 17, 32, 33]),
+    "mha_rows1": dict(B=2, q_len=1, Hq=8, Hkv=8, D=128, bt=16, seq_lens=[100, 513]),
+    "bt1_pages": dict(B=2, q_len=2, Hq=4, Hkv=2, D=64, bt=1, seq_lens=[37, 90], window=10, sinks=True),
+    "bt8_d256": dict(B=1, q_len=1, Hq=8, Hkv=4, D=256, bt=8, seq_lens=[300]),
+    "window_ge_seq": dict(B=2, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[40, 70], window=5000,
+                          sinks=True),
+    "big_negative_sinks": dict(B=2, q_len=1, Hq=8, Hkv=2, D=64, bt=32, seq_lens=[77, 130], sinks=True),
+}
+
+# (case, flags, num_splits)
+SMALL_RUNS = []
+for name in SMALL:
+    for flags in (0, DOT):
+        for ns in (0, 1, 3):
+            SMALL_RUNS.append((name, flags, ns))
+    if SMALL[name]["bt"] >= 16:
+        SMALL_RUNS.append((name, MFMA, 0))
+
+_small_cache = {}
+
+
+def _small(name):
+    if name not in _small_cache:
+        kw = dict(SMALL[name])
+        wl = make_workload(seed=100 + list(SMALL).index(name), **kw)
+        if name == "big_negative_sinks":
+            wl.sinks[:] = -30.0
+        ref = oracle.decode(**wl.oracle_kwargs())
+        _small_cache[name] = (wl, upload(wl), ref)
+    return _small_cache[name]
+
+
+@pytest.mark.parametrize("name,flags,ns", SMALL_RUNS)
+def test_parity_small(name, flags, ns):
+    wl, t, (ro, rl) = _small(name)
+    out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"{name} flags={flags} splits={ns}")
+
+
+def test_parity_output_without_lse_pointer():
+    wl, t, (ro, rl) = _small("mtp4_window_sinks")
+    out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                         sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()))
+    n = fp.fp8pa_workspace_bytes(shape)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    fp.fp8pa_decode(shape, t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
+                    out, None, ws if n else None, n)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    compare(o, rl, ro, rl, label="lse=NULL")
+
+
+def test_workspace_too_small_is_reported():
+    wl, t, _ = _small("gqa4_ragged")
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                         sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()), num_splits=3)
+    n = fp.fp8pa_workspace_bytes(shape)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fp.Fp8paError) as e:
+        fp.fp8pa_decode(shape, t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], None,
+                        out, None, ws, n - 1)
+    assert e.value.status == 3
+
+
+# ------------------------------------------------------------------ merge
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_merge_matches_oracle(D):
+    rng = np.random.default_rng(D)
+    R, S, Hq = 40, 5, 8
+    po = rng.standard_normal((R, S, D)).astype(np.float32)
+    pl = (rng.standard_normal((R, S)) * 3).astype(np.float32)
+    pl[rng.random((R, S)) < 0.25] = -np.inf
+    pl[3, :] = -np.inf
+    po[np.isneginf(pl)] = np.nan            # never read for an empty split
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    for use_sinks in (False, True):
+        out = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((R,), dtype=torch.float32, device="cuda")
+        sk = torch.from_numpy(sinks).cuda() if use_sinks else None
+        fp.fp8pa_merge(S, R, Hq, D, torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), sk,
+                       out, lse)
+        torch.cuda.synchronize()
+        ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64),
+                              np.tile(sinks, R // Hq + 1)[:R] if use_sinks else None)
+        compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"merge D={D}")
+
+
+# --------------------------------------------------- full-size named workloads
+
+_cfg_cache = {}
+
+
+def _cfg(k):
+    if k not in _cfg_cache:
+        _cfg_cache.clear()
+        torch.cuda.empty_cache()
+        wl = make_config(k)
+        _cfg_cache[k] = (wl, upload(wl))
+    return _cfg_cache[k]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_parity_full_workload(k):
+    wl, t = _cfg(k)
+    out, lse = run(wl, t)  # the launch configuration the benchmark times
+    o, l = to_host(out, lse)
+    rows = sample_rows(wl, 8 if k == 1 else 40, seed=k)
+    ro, rl = oracle.decode(**wl.oracle_kwargs(), rows=rows)
+    idx = tuple(np.array(rows).T)
+    compare(o[idx], l[idx], ro, rl, label=f"cfg{k}")
+    # properties over every row: finite outputs, finite LSE, |out| <= max |V|
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_parity_full_workload_dot_kernel(k):
+    wl, t = _cfg(k)
+    o, l = to_host(*run(wl, t, flags=DOT))
+    rows = sample_rows(wl, 16, seed=10 + k)
+    ro, rl = oracle.decode(**wl.oracle_kwargs(), rows=rows)
+    idx = tuple(np.array(rows).T)
+    compare(o[idx], l[idx], ro, rl, label=f"cfg{k} dot")
+
+
+def test_determinism_and_split_invariance_cfg2():
+    wl, t = _cfg(2)
+    a = to_host(*run(wl, t))
+    b = to_host(*run(wl, t))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "run-to-run bits differ"
+    for ns in (1, 7):
+        c = to_host(*run(wl, t, num_splits=ns))
+        # different split counts change only rounding
+        assert np.max(np.abs(c[0] - a[0])) < 2e-2
+        assert np.max(np.abs(c[1] - a[1])) < 1e-3
+
+
+def test_block_permutation_invariance_cfg2():
+    wl, t = _cfg(2)
+    a = to_host(*run(wl, t))
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(wl.num_blocks, generator=g)          # page j moves to perm[j]
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(wl.num_blocks)
+    t2 = dict(t)
+    t2["k"] = t["k"][inv.cuda()].contiguous()
+    t2["v"] = t["v"][inv.cuda()].contiguous()
+    btab = t["bt"].long()
+    t2["bt"] = torch.where(btab >= 0, perm.cuda()[btab.clamp(min=0)], btab).int().contiguous()
+    b = to_host(*run(wl, t2))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_graph_capture_replay_cfg5():
+    wl, t = _cfg(5)
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                         sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()), num_splits=3)
+    n = fp.fp8pa_workspace_bytes(shape)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(tuple(wl.q_bits.shape[:3]), dtype=torch.float32, device="cuda")
+
+    def call():
+        fp.fp8pa_decode(shape, t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"],
+                        t["sinks"], out, lse, ws, n)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    out.zero_()
+    lse.zero_()
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    assert torch.cuda.memory_allocated() == before
+    for it in range(3):
+        out.fill_(float(it))
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {it} differs"
