@@ -26,8 +26,9 @@
 //    per-row power-of-two scale, so the scores keep ~2^-8 relative
 //    precision while the K codes go straight from HBM into the MFMA.
 //    The fp32 score accumulator already holds, per lane, the 8 keys that the
-//    PV MFMA's B operand needs, so P = 2^(s - m + 8) is packed to E4M3 in
-//    place (the +8 keeps P in E4M3's normal range; it cancels in O / l).
+//    PV MFMA's B operand needs, so P = 2^(s - m + 8) is packed in place as
+//    two E4M3 parts, hi + lo, both fed to the PV MFMA (the +8 keeps P in
+//    E4M3's normal range; it cancels in O / l).
 //    V is transposed to keys-along-K with v_perm byte shuffles in registers
 //    (no LDS).
 //  * VALU kernel ("dot"): 16 bytes per lane, D/16 lanes per key, E4M3
@@ -368,12 +369,25 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < S; ++e) O[e] *= alpha;
 
-    uint32_t p0 = 0, p1 = 0;
+    // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
+    // which short, peaked rows need (one E4M3 P alone errs by up to 2^-4).
+    uint32_t p0 = 0, p1 = 0, r0 = 0, r1 = 0;
     p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0], pj[1], p0, false);
     p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2], pj[3], p0, true);
     p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4], pj[5], p1, false);
     p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6], pj[7], p1, true);
+    {
+      const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, false);
+      const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, true);
+      const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, false);
+      const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, true);
+      r0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0] - d0.x, pj[1] - d0.y, r0, false);
+      r0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2] - d1.x, pj[3] - d1.y, r0, true);
+      r1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4] - d2.x, pj[5] - d2.y, r1, false);
+      r1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6] - d3.x, pj[7] - d3.y, r1, true);
+    }
     const long P = as_long(p0, p1);
+    const long Plo = as_long(r0, r1);
 
     // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
 #pragma unroll
@@ -384,7 +398,9 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
 #pragma unroll
       for (int x4 = 0; x4 < 4; ++x4) {
         const int e = 4 * wd + x4;
-        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(lo4[x4], hi4[x4]), P, O[e], 0, 0, 0);
+        const long vt = as_long(lo4[x4], hi4[x4]);
+        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt, P, O[e], 0, 0, 0);
+        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt, Plo, O[e], 0, 0, 0);
       }
     }
   }

@@ -44,15 +44,34 @@ def test_hw_e4m3_decode_matches_oracle_table():
     assert np.array_equal(got[ok], want[ok])
 
 
-def test_hw_mfma_fp8_layout():
-    rng = np.random.default_rng(0)
-    a = rng.integers(0, 0x78, size=(16, 32)).astype(np.uint8)   # finite codes of either sign below
-    b = rng.integers(0, 0x78, size=(32, 16)).astype(np.uint8)
-    a |= (rng.integers(0, 2, size=a.shape) << 7).astype(np.uint8)
+def _mfma(a, b):
     c = torch.empty((16, 16), dtype=torch.float32, device="cuda")
     fp.fp8pa_debug_mfma_fp8(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), c)
+    return c.cpu().numpy().astype(np.float64)
+
+
+def test_hw_mfma_fp8_layout_exact():
+    # codes of 0, +-0.5, +-1, +-2: every product and partial sum is exact, so any
+    # mistake in the assumed lane layout shows as a mismatch.
+    rng = np.random.default_rng(0)
+    vals = np.array([0x00, 0x30, 0x38, 0x40, 0xB0, 0xB8, 0xC0], dtype=np.uint8)
+    a = vals[rng.integers(0, len(vals), size=(16, 32))]
+    b = vals[rng.integers(0, len(vals), size=(32, 16))]
     want = oracle.E4M3_TABLE[a] @ oracle.E4M3_TABLE[b]
-    np.testing.assert_allclose(c.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+    assert np.array_equal(_mfma(a, b), want)
+
+
+def test_hw_mfma_fp8_accumulation_precision():
+    # Random finite codes: the MFMA sums 32 products with less than fp32
+    # precision; the error stays below 2^-10 of the sum of |products|.
+    rng = np.random.default_rng(1)
+    a = rng.integers(0, 0x78, size=(16, 32)).astype(np.uint8)
+    b = rng.integers(0, 0x78, size=(32, 16)).astype(np.uint8)
+    a |= (rng.integers(0, 2, size=a.shape) << 7).astype(np.uint8)
+    A, Bm = oracle.E4M3_TABLE[a], oracle.E4M3_TABLE[b]
+    want = A @ Bm
+    scale = np.abs(A) @ np.abs(Bm)
+    assert np.all(np.abs(_mfma(a, b) - want) <= scale * 2.0 ** -10)
 
 
 # ------------------------------------------------------- small, every element
@@ -248,11 +267,12 @@ def test_graph_capture_replay_cfg5():
     out.zero_()
     lse.zero_()
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
+        before = torch.cuda.memory_allocated()
         call()
-    assert torch.cuda.memory_allocated() == before
+        after = torch.cuda.memory_allocated()
+    assert after == before  # the library allocates nothing, also under capture
     for it in range(3):
         out.fill_(float(it))
         lse.zero_()
