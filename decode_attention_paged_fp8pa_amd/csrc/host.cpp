@@ -84,7 +84,14 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
   const int32_t rows_eff = p.rows < p.rpg ? p.rows : p.rpg;
 
-  p.hg = (p.Hkv % 4 == 0) ? 4 : (p.Hkv % 2 == 0) ? 2 : 1;
+  // A workgroup takes adjacent kv heads (one wavefront each), so the bytes of
+  // one token slot are read by one workgroup at about the same time.  The
+  // MFMA kernel's register budget sets how many wavefronts share a SIMD
+  // (4 at D = 64, 2 at D = 128, 1 at D = 256): groups of 8 at D = 64 and 4
+  // otherwise let whole groups fill a compute unit.
+  const int32_t max_hg = (p.variant == kVariantMfma && p.D != 64) ? 4 : 8;
+  p.hg = 1;
+  while (p.hg * 2 <= max_hg && p.Hkv % (p.hg * 2) == 0) p.hg *= 2;
   const int64_t units = int64_t(p.B) * (p.Hkv / p.hg) * p.row_groups;
   if (units > (int64_t(1) << 30)) return FP8PA_ERR_UNSUPPORTED;
   p.units = int32_t(units);
@@ -116,6 +123,11 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     if (tps < lift) tps = lift;
   }
   if (tps < 1) tps = 1;
+  if (p.variant == kVariantMfma) {
+    // the MFMA kernel holds a split's block-table entries in registers
+    const int64_t max_tps = ((int64_t(kMaxSplitPages) - 1) * p.bt) / kTileTokens - 1;
+    if (tps > max_tps) tps = max_tps;
+  }
   int64_t splits = ceil_div(n_tiles, tps);
   if (splits < 1) splits = 1;
   if (splits * units > (int64_t(1) << 31) - 1) return FP8PA_ERR_UNSUPPORTED;

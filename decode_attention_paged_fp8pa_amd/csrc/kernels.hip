@@ -11,7 +11,7 @@
 // MI355X design:
 //  * One wavefront owns one work item (sequence b, kv head g, row group,
 //    KV split) and walks 32-token tiles of its key range; a workgroup packs
-//    1, 2 or 4 wavefronts on adjacent kv heads, so a workgroup's loads of
+//    1 to 8 wavefronts on adjacent kv heads, so a workgroup's loads of
 //    one token slot are neighbouring bytes of the same page.
 //  * Pages are read with raw buffer loads whose descriptor base is the page
 //    (wave-uniform, from one scalar block-table load per 16 tokens); lanes
@@ -60,8 +60,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kOob = 0x80000000u;
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on gfx9 parts.
 constexpr int kRsrcWord3 = 0x00020000;
-// P is stored as E4M3 of p * 2^kPShift, p in [0, 1].
-constexpr float kPShift = 8.0f;
+// P is stored as E4M3 of p * 2^kPShift with p = 2^(s - m) <= 2^kLazy, where
+// the reference max m trails the true max by at most kLazy (log2 units):
+// 2^(kLazy + kPShift) = 256 stays below E4M3's 448.
+constexpr float kPShift = 4.0f;
+constexpr float kLazy = 4.0f;
 
 struct Params {
   const uint16_t* q;
@@ -126,6 +129,16 @@ __device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint32_t* dst) {
   }
 }
 
+
+// Maximum of v over lanes l, l^16, l^32 and l^48 (the four lane groups that
+// hold one MFMA column), with the gfx950 permlane swaps (no LDS round trip).
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
 // 4x4 byte transpose: out[x] byte y = in[y] byte x.
 __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
                                              uint32_t* out) {
@@ -158,7 +171,9 @@ __device__ __forceinline__ Work work_of(const Params& p) {
   const int ngg = p.Hkv / p.hg;
   const int gg = t % ngg;
   w.b = t / ngg;
-  w.g = gg * p.hg + int(threadIdx.x >> 6);
+  // the wavefront index is uniform across the wave; saying so keeps every
+  // address derived from it (descriptor bases, table rows) in scalar registers
+  w.g = gg * p.hg + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   return w;
 }
 
@@ -199,7 +214,8 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
 //     exactly the tokens whose scores the QK accumulators give this lane.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
+__global__ __launch_bounds__(D == 64 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void partial_mfma_kernel(Params p) {
   constexpr int S = D / 16;       // V bytes per lane per token
   constexpr int KB = D / 4;       // K bytes per lane per token
   constexpr int KSTEPS = D / 32;  // QK k-steps of 32 dims
@@ -224,65 +240,8 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
     return;
   }
 
-  // ---- stage the query row: per-row power-of-two scale, E4M3 hi + lo parts
-  long qhi[KSTEPS], qlo[KSTEPS];
-  float cr;  // score scale into log2 units
-  {
-    float qf[KB];
-    if (row.valid) {
-      const uint16_t* qrow = p.q + row.out_row * D + KB * qd;
-#pragma unroll
-      for (int i = 0; i < KB / 8; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * i);
-        qf[8 * i + 0] = bf16_lo(v.x);
-        qf[8 * i + 1] = bf16_hi(v.x);
-        qf[8 * i + 2] = bf16_lo(v.y);
-        qf[8 * i + 3] = bf16_hi(v.y);
-        qf[8 * i + 4] = bf16_lo(v.z);
-        qf[8 * i + 5] = bf16_hi(v.z);
-        qf[8 * i + 6] = bf16_lo(v.w);
-        qf[8 * i + 7] = bf16_hi(v.w);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KB; ++i) qf[i] = 0.f;
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < KB; ++i) amax = fmaxf(amax, fabsf(qf[i]));
-    amax = fmaxf(amax, xor_shfl(amax, 16));
-    amax = fmaxf(amax, xor_shfl(amax, 32));
-    // 2^(7 - floor(log2 amax)) puts the largest element in [128, 256).
-    int se = 0;
-    if (amax > 0.f) {
-      const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
-      se = min(max(7 - e, -120), 120);
-    }
-    const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-    const float ks = p.k_scale[p.k_per_head ? w.g : 0];
-    cr = p.sm_scale * ks * kLog2e / qs;
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = qf[8 * c + j] * qs;
-      uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
-      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
-      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
-      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
-      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
-      const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
-      const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
-      const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
-      const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
-      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - d0.x, x[1] - d0.y, l0, false);
-      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x, x[3] - d1.y, l0, true);
-      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x, x[5] - d2.y, l1, false);
-      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
-      qhi[c] = as_long(h0, h1);
-      qlo[c] = as_long(l0, l1);
-    }
-  }
+  long qhi[KSTEPS], qlo[KSTEPS];  // the query row in E4M3 hi + lo parts (set below)
+  float cr;                       // score scale into log2 units
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
   // value vector is zero when this split writes the final output.
@@ -298,20 +257,70 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
   const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
   const uint32_t koff = uint32_t(n * tok + KB * qd);
+
+  // Block-table entries of this split's pages, read once before the loop:
+  // lane i of tab[w] holds the entry of page pg_lo + 64 w + i.  Only pages in
+  // [pg_lo, pg_hi], which all hold attended tokens, are read (the plan keeps
+  // a split within kMaxSplitPages pages).  A tile's page number then comes
+  // from readlanes, so the loop has no table loads and no waits on them.
+  const int pg_lo = max(ulo, ts * kTileTokens) >> p.bt_shift;
+  const int pg_hi = ts < te ? (min(uhi, te * kTileTokens) - 1) >> p.bt_shift : -1;
+  int tab[kMaxSplitPages / 64];
+#pragma unroll
+  for (int wi = 0; wi < kMaxSplitPages / 64; ++wi) {
+    const int pi = pg_lo + 64 * wi + lane;
+    tab[wi] = pi <= pg_hi ? btab[pi] : 0;
+  }
+  // The query row's raw bf16 bits; converted after the first tiles' loads
+  // are issued, so the two round trips overlap.
+  u32x4 qraw[KB / 8];
+  {
+    const uint16_t* qrow = p.q + row.out_row * D + KB * qd;
+#pragma unroll
+    for (int i = 0; i < KB / 8; ++i)
+      qraw[i] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+  }
+  auto page_of = [&](int pi) -> int {
+    const int rel = pi - pg_lo;
+    const int ls = rel & 63;
+    if (rel < 64) return __builtin_amdgcn_readlane(tab[0], ls);
+    if (rel < 128) return __builtin_amdgcn_readlane(tab[1], ls);
+    if (rel < 192) return __builtin_amdgcn_readlane(tab[2], ls);
+    return __builtin_amdgcn_readlane(tab[3], ls);
+  };
+
   uint32_t voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = uint32_t((4 * qd + j) * tok + S * n);
 
-  for (int tt = ts; tt < te; ++tt) {
+  // Tokens every valid row of the wave attends: a tile inside [all_lo,
+  // all_hi) needs no per-token mask.
+  int all_lo = row.valid ? row.klo : 0;
+  int all_hi = row.valid ? row.khi : 0x7fffffff;
+#pragma unroll
+  for (int s2 = 1; s2 < 16; s2 <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, s2, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, s2, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+
+  // Loads of one 32-token tile into registers.  A tile at or past `te`, or a
+  // 16-token group holding no attended token, gets an empty descriptor: its
+  // loads return zeros and touch no memory, and no table entry is read.
+  struct TileRegs {
+    uint32_t k[2][KW];
+    uint32_t v[8][SW];
+  };
+  auto load_tile = [&](int tt, TileRegs& r) {
     const int kb = tt * kTileTokens;
-    uint32_t kr[2][KW];
-    uint32_t vr[8][SW];
+    const bool inner = kb >= ulo && kb + kTileTokens <= uhi;
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       const int gk = kb + 16 * grp;
       Rsrc rk, rv;
-      if (gk < uhi && gk + 16 > ulo) {
-        const int page = btab[gk >> p.bt_shift];
+      if (tt < te && gk < uhi && gk + 16 > ulo) {
+        const int page = page_of(gk >> p.bt_shift);
         const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
         rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + base), 0, 16 * tok, kRsrcWord3);
         rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + base), 0, 16 * tok, kRsrcWord3);
@@ -319,55 +328,69 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
         rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase_g, 0, 0, kRsrcWord3);
         rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase_g, 0, 0, kRsrcWord3);
       }
-      const int kt = gk + n;
-      buf_load<KB>(rk, (kt >= ulo && kt < uhi) ? koff : kOob, kr[grp]);
+      if (inner) {
+        buf_load<KB>(rk, koff, r.k[grp]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int vt = gk + 4 * qd + j;
-        buf_load<S>(rv, (vt >= ulo && vt < uhi) ? voff[j] : kOob, vr[4 * grp + j]);
+        for (int j = 0; j < 4; ++j) buf_load<S>(rv, voff[j], r.v[4 * grp + j]);
+      } else {
+        const int kt = gk + n;
+        buf_load<KB>(rk, (kt >= ulo && kt < uhi) ? koff : kOob, r.k[grp]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int vt = gk + 4 * qd + j;
+          buf_load<S>(rv, (vt >= ulo && vt < uhi) ? voff[j] : kOob, r.v[4 * grp + j]);
+        }
       }
     }
+  };
 
-    // S^T = K . Q^T for both 16-token groups
+  // One tile: S^T = K Q^T, mask, online softmax with a lazy reference max,
+  // P = hi + lo E4M3 parts, O^T += V^T P^T.
+  auto compute_tile = [&](int tt, const TileRegs& r) {
+    const int kb = tt * kTileTokens;
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const long ka = as_long(kr[0][2 * c], kr[0][2 * c + 1]);
-      const long kbv = as_long(kr[1][2 * c], kr[1][2 * c + 1]);
+      const long ka = as_long(r.k[0][2 * c], r.k[0][2 * c + 1]);
+      const long kbv = as_long(r.k[1][2 * c], r.k[1][2 * c + 1]);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qhi[c], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[c], sb, 0, 0, 0);
       sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[c], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[c], sb, 0, 0, 0);
     }
-
-    // scale, mask, online softmax
-    float x[8];
+    // raw scores; a token no row of this lane attends becomes -inf (edge
+    // tiles only: interior tiles are attended by every row of the wave)
+    float sv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-      const float s = j < 4 ? sa[j] : sb[j - 4];
-      x[j] = (key >= row.klo && key < row.khi) ? s * cr : -INFINITY;
+    for (int j = 0; j < 8; ++j) sv[j] = j < 4 ? sa[j] : sb[j - 4];
+    if (!(kb >= all_lo && kb + kTileTokens <= all_hi)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+        sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
+      }
     }
-    float mx = x[0];
+    float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    ms = max_over_groups(ms);
+    const float mx = ms * cr;  // cr > 0, so the scaled max is the max of the scaled
+    // Lazy reference max: move m only when this tile exceeds it by more than
+    // kLazy (log2 units), so most tiles skip the O rescale; P stays
+    // <= 2^(kLazy + kPShift).
+    const bool bump = mx > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      const float mnew = bump ? mx : m;
+      const float alpha = bump ? exp2_fast(m - mnew) : 1.f;
+      lsum *= alpha;
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2_fast(m - muse);
-    const float off = muse - kPShift;
+      for (int e = 0; e < S; ++e) O[e] *= alpha;
+      m = mnew;
+    }
+    const float noff = kPShift - (m == -INFINITY ? 0.f : m);
     float pj[8];
-    float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pj[j] = exp2_fast(x[j] - off);
-      psum += pj[j];
-    }
-    lsum = lsum * alpha + psum;
-    m = mnew;
-#pragma unroll
-    for (int e = 0; e < S; ++e) O[e] *= alpha;
+    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], cr, noff));
+    lsum += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
 
     // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
     // which short, peaked rows need (one E4M3 P alone errs by up to 2^-4).
@@ -393,8 +416,8 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
 #pragma unroll
     for (int wd = 0; wd < SW; ++wd) {
       uint32_t lo4[4], hi4[4];
-      transpose4x4(vr[0][wd], vr[1][wd], vr[2][wd], vr[3][wd], lo4);
-      transpose4x4(vr[4][wd], vr[5][wd], vr[6][wd], vr[7][wd], hi4);
+      transpose4x4(r.v[0][wd], r.v[1][wd], r.v[2][wd], r.v[3][wd], lo4);
+      transpose4x4(r.v[4][wd], r.v[5][wd], r.v[6][wd], r.v[7][wd], hi4);
 #pragma unroll
       for (int x4 = 0; x4 < 4; ++x4) {
         const int e = 4 * wd + x4;
@@ -403,6 +426,80 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
         O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt, Plo, O[e], 0, 0, 0);
       }
     }
+  };
+  // Two register buffers in turn: while one tile computes, the next tile's
+  // loads are in flight (8 KB per wavefront at D = 128).  Deeper pipelines
+  // measured slower on MI355X: more than ~8 KB in flight per wavefront only
+  // adds queueing in the memory system.
+  TileRegs ta, tb;
+  load_tile(ts, ta);
+
+  // ---- stage the query row: per-row power-of-two scale, E4M3 hi + lo parts
+  {
+    float qf[KB];
+    {
+#pragma unroll
+      for (int i = 0; i < KB / 8; ++i) {
+        const u32x4 v = qraw[i];
+        qf[8 * i + 0] = bf16_lo(v.x);
+        qf[8 * i + 1] = bf16_hi(v.x);
+        qf[8 * i + 2] = bf16_lo(v.y);
+        qf[8 * i + 3] = bf16_hi(v.y);
+        qf[8 * i + 4] = bf16_lo(v.z);
+        qf[8 * i + 5] = bf16_hi(v.z);
+        qf[8 * i + 6] = bf16_lo(v.w);
+        qf[8 * i + 7] = bf16_hi(v.w);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) amax = fmaxf(amax, fabsf(qf[i]));
+    amax = fmaxf(amax, xor_shfl(amax, 16));
+    amax = fmaxf(amax, xor_shfl(amax, 32));
+    // 2^(7 - floor(log2 amax)) puts the largest element in [128, 256).
+    int se = 0;
+    if (amax > 0.f) {
+      const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+      se = min(max(7 - e, -120), 120);
+    }
+    const float qs = __uint_as_float(uint32_t(se + 127) << 23);
+    const float ks = p.k_scale[p.k_per_head ? w.g : 0];
+    cr = p.sm_scale * ks * kLog2e / qs;
+    // Scores are scaled as fma(S, cr, .) with cr > 0, so a -inf mask stays
+    // -inf: a negative scale's sign moves into the query, and a zero scale
+    // becomes a tiny positive one (its scores stay ~0).
+    const float qsign = cr < 0.f ? -qs : qs;
+    cr = fmaxf(fabsf(cr), 1e-30f);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = qf[8 * c + j] * qsign;
+      uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
+      h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
+      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
+      h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
+      const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
+      const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
+      const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
+      const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
+      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - d0.x, x[1] - d0.y, l0, false);
+      l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x, x[3] - d1.y, l0, true);
+      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x, x[5] - d2.y, l1, false);
+      l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
+      qhi[c] = as_long(h0, h1);
+      qlo[c] = as_long(l0, l1);
+    }
+  }
+
+
+  for (int tt = ts; tt < te; tt += 2) {
+    load_tile(tt + 1, tb);
+    compute_tile(tt, ta);
+    if (tt + 1 >= te) break;
+    load_tile(tt + 2, ta);
+    compute_tile(tt + 1, tb);
   }
 
   // ---- epilogue: l over the 4 lane groups, normalise, write
@@ -454,7 +551,7 @@ __global__ __launch_bounds__(256) void partial_mfma_kernel(Params p) {
 // chunk c = l % (D/16), dims [16 c, 16 c + 16).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void partial_dot_kernel(Params p) {
+__global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   constexpr int LPK = D / 16;    // lanes per token
   constexpr int KPI = 64 / LPK;  // tokens per round
   constexpr int R = kTileTokens / KPI;
@@ -643,8 +740,34 @@ __global__ __launch_bounds__(256) void partial_dot_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge: one wavefront per row, D/64 dims per lane.
+// Log-sum-exp merge: one wavefront per row, D/64 dims per lane.  Lane s
+// loads the LSE of split s (64 splits per pass), the wave reduces their
+// maximum, and each lane then accumulates its dims of the partial outputs,
+// sixteen splits per step with the weights read from the owning lanes.  A split
+// whose weight is 0 (LSE = -inf) is skipped by a select, so whatever its
+// partial output holds (never written, possibly NaN) cannot leak.
 // ---------------------------------------------------------------------------
+template <int E>
+__device__ __forceinline__ void load_dims(const float* src, float* o) {
+  if constexpr (E == 1) {
+    o[0] = src[0];
+  } else if constexpr (E == 2) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+    o[0] = v.x;
+    o[1] = v.y;
+  } else {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows, int Hq,
                                                      const float* __restrict__ po,
@@ -653,41 +776,57 @@ __global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows
                                                      uint16_t* __restrict__ out,
                                                      float* __restrict__ lse_out) {
   constexpr int E = D / 64;
+  constexpr int U = 16;  // splits whose partial outputs are loaded together
   const int row = blockIdx.x * 4 + int(threadIdx.x >> 6);
   if (row >= num_rows) return;
   const int lane = threadIdx.x & 63;
   const float* lrow = pl + (size_t)row * num_splits;
+  const float* obase = po + (size_t)row * num_splits * D + E * lane;
   const float sink2 = sinks ? sinks[row % Hq] * kLog2e : -INFINITY;
+  // The first U splits' partial outputs do not depend on the weights: their
+  // loads are issued first and stay in flight while the LSEs are reduced.
+  const int n_first = min(num_splits, 64);
+  float o0[U][E];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_dims<E>(obase + (size_t)min(u, n_first - 1) * D, o0[u]);
   float M = sink2;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lrow[s] * kLog2e);
+  for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lrow[s] * kLog2e);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_shfl(M, m));
+  const float Mu = M == -INFINITY ? 0.f : M;  // every weight is 0 then
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  float Lsum = 0.f;
-  if (M > -INFINITY) {
-    const float* obase = po + (size_t)row * num_splits * D + E * lane;
-    for (int s = 0; s < num_splits; ++s) {
-      const float ls = lrow[s];
-      if (ls == -INFINITY) continue;
-      const float wgt = exp2_fast(ls * kLog2e - M);
-      Lsum += wgt;
-      const float* src = obase + (size_t)s * D;
-      if constexpr (E == 1) {
-        acc[0] = fmaf(wgt, src[0], acc[0]);
-      } else if constexpr (E == 2) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(src);
-        acc[0] = fmaf(wgt, v.x, acc[0]);
-        acc[1] = fmaf(wgt, v.y, acc[1]);
+  float lpart = 0.f;
+  for (int s0 = 0; s0 < num_splits; s0 += 64) {
+    const int s = s0 + lane;
+    const float w = s < num_splits ? exp2_fast(lrow[s] * kLog2e - Mu) : 0.f;
+    lpart += w;
+    const int n = min(64, num_splits - s0);
+    for (int j0 = 0; j0 < n; j0 += U) {
+      // U splits' loads in flight together; an index past the last split
+      // re-reads the last one and gets weight 0
+      float o[U][E];
+      if (s0 == 0 && j0 == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[u][e] = o0[u][e];
       } else {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src);
-        acc[0] = fmaf(wgt, v.x, acc[0]);
-        acc[1] = fmaf(wgt, v.y, acc[1]);
-        acc[2] = fmaf(wgt, v.z, acc[2]);
-        acc[3] = fmaf(wgt, v.w, acc[3]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_dims<E>(obase + (size_t)(s0 + min(j0 + u, n - 1)) * D, o[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = j0 + u < n ? lane_value(w, min(j0 + u, 63)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = wu > 0.f ? fmaf(wu, o[u][e], acc[e]) : acc[e];
       }
     }
-    if (sink2 > -INFINITY) Lsum += exp2_fast(sink2 - M);
   }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) lpart += xor_shfl(lpart, m);
+  const float Lsum = lpart + (sink2 > -INFINITY ? exp2_fast(sink2 - Mu) : 0.f);
   const bool empty = !(Lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / Lsum;
   uint16_t* dst = out + (size_t)row * D + E * lane;
@@ -699,7 +838,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows
     *reinterpret_cast<u32x2*>(dst) =
         u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   }
-  if (lse_out && lane == 0) lse_out[row] = empty ? -INFINITY : (M + log2_fast(Lsum)) * kLn2;
+  if (lse_out && lane == 0) lse_out[row] = empty ? -INFINITY : (Mu + log2_fast(Lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------

@@ -14,6 +14,7 @@ constexpr int kRowsMfma = 16;        // query rows per wavefront: the MFMA N dim
 constexpr int kRowsDot = 4;          // query rows per wavefront in the VALU dot kernel
 constexpr int kTargetWavesPerCu = 8; // wavefronts the split plan aims to put on each CU
 constexpr size_t kWorkspaceAlign = 256;
+constexpr int kMaxSplitPages = 256;   // block-table entries an MFMA wavefront holds
 
 enum Variant : int32_t { kVariantDot = 0, kVariantMfma = 1 };
 

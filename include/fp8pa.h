@@ -83,7 +83,9 @@ typedef struct fp8pa_shape {
   int32_t v_scale_count;      /* 1 or Hkv */
   int32_t window;             /* <= 0: none; W > 0: the last W positions */
   float sm_scale;             /* softmax scale applied to q.K; finite */
-  int32_t num_splits;         /* 0: the library plans; > 0 caps the KV splits */
+  int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
+                                 splits at most (the MFMA kernel still splits so
+                                 that no split spans more than 256 pages) */
   int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
 } fp8pa_shape;
 
@@ -161,7 +163,8 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
  * r < num_rows, with M = max(partial_lse[r, s], sink):
  *   out[r, :] = sum_s e^{lse_s - M} partial_o[r, s, :] / L,
  *   lse[r]    = M + ln L,   L = sum_s e^{lse_s - M} + e^{sink - M}.
- * A split with lse_s = -inf contributes nothing (its partial_o is not read);
+ * A split with lse_s = -inf contributes nothing (its partial_o values are
+ * ignored and may be NaN or garbage);
  * a row with no finite term gets out = 0, lse = -inf.
  *
  *   partial_o    float [num_rows, num_splits, head_dim]

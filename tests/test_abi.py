@@ -90,10 +90,18 @@ def test_plan_of_each_workload(k):
 def test_plan_is_deterministic_and_forced_splits():
     s = cfg_shape(4)
     assert fp.fp8pa_plan(s, 256) == fp.fp8pa_plan(s, 256)
+    # a split of the MFMA kernel spans at most 256 pages: 196608 tokens at 64
+    # tokens per page need at least ceil(6144 tiles / 509 tiles) = 13 splits
+    max_tps = (255 * 64) // 32 - 1
+    min_splits = math.ceil(6144 / max_tps)
     for n in (1, 2, 7, 64):
         p = fp.fp8pa_plan(cfg_shape(4, num_splits=n), 256)
-        assert 1 <= p["num_splits"] <= n
-    assert fp.fp8pa_plan(cfg_shape(4, num_splits=1), 256)["workspace_bytes"] == 0
+        assert 1 <= p["num_splits"] <= max(n, min_splits)
+        assert p["tiles_per_split"] <= max_tps
+    # with a shorter sequence bound one split is possible: no workspace then
+    s1 = cfg_shape(5, num_splits=1)
+    assert fp.fp8pa_plan(s1, 256)["num_splits"] == 1
+    assert fp.fp8pa_plan(s1, 256)["workspace_bytes"] == 0
 
 
 def test_variant_selection():
