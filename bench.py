@@ -13,9 +13,17 @@ the other four named workloads are measured the same way and reported under
 Cold-cache discipline: each workload keeps C copies of its K/V page pools
 (same block table) and the steps rotate through them, so that between two
 reads of the same bytes at least 1 GiB of other KV has streamed through the
-256 MB Infinity Cache.  The K timed steps run back to back on torch's
-current stream (the stream the library launches on), bracketed by
-torch.cuda.synchronize() and HIP events.
+256 MB Infinity Cache.  The K timed steps are captured once in a HIP graph
+(after W eager warmup steps and an eager timing pass) and replayed back to
+back on torch's current stream, bracketed by torch.cuda.synchronize() and
+HIP events; the replayed output is checked bit for bit against the eager
+one.  The merge kernel alone is timed the same way.
+
+HBM traffic (roofline.traffic): four rocprofv3 --pmc passes, FETCH_SIZE and
+WRITE_SIZE over this workload and over `--calibrate-copy` (device copies of
+a known size), turned into bytes per launch by `--write-traffic`; see the
+profiles/ summary for the commands.  The figure is dropped (null) when the
+kernel sources have changed since the counters were taken.
 
 Prints ONE JSON line (rank 0, N=1):
   value = attended KV bytes read per step / step time, in GB/s;
@@ -91,10 +99,11 @@ def load_traffic(workload_name):
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    h = t.get("hbm_bytes_per_launch")
+    return None if not h else int(h["read"] + h["write"])
 
 
-def measure(k, steps, warmup, log):
+def measure(k, steps, warmup, log, use_graph=True):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
@@ -131,6 +140,7 @@ def measure(k, steps, warmup, log):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # eager: one library call per step from Python (CPU launch cost included)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -140,27 +150,65 @@ def measure(k, steps, warmup, log):
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    step_ms = e0.elapsed_time(e1) / steps
+    eager_ms = e0.elapsed_time(e1) / steps
+    eager_out = out.clone()
 
+    # timed: the same K steps captured once in a HIP graph and replayed, so
+    # the GPU runs them back to back without Python launch gaps
+    if not use_graph:
+        return _result(wl, k, kvb, copies, plan, eager_ms, eager_ms, wall_ms, wall_ms, False, 0.0, log), wl
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(out, eager_out))
+    if not graph_ok:
+        log(f"[bench] cfg{k}: graph replay output differs from eager; reporting eager timing")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = e0.elapsed_time(e1) / steps if graph_ok else eager_ms
+    del graph
+
+    # the merge kernel alone (same workspace), also from a graph
     merge_ms = 0.0
     if plan["merge_launched"]:
         rows = wl.B * wl.q_len * wl.Hq
-        po = ws
         pl_ptr = ws.data_ptr() + plan["workspace_lse_offset"]
+
+        def merge_only():
+            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, ws, pl_ptr, sinks, out, lse)
+
         for _ in range(3):
-            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, po, pl_ptr, sinks, out, lse)
+            merge_only()
         torch.cuda.synchronize()
-        m0 = torch.cuda.Event(enable_timing=True)
-        m1 = torch.cuda.Event(enable_timing=True)
-        m0.record()
-        for _ in range(steps):
-            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, po, pl_ptr, sinks, out, lse)
-        m1.record()
+        mgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(mgraph):
+            for _ in range(steps):
+                merge_only()
+        mgraph.replay()
         torch.cuda.synchronize()
-        merge_ms = m0.elapsed_time(m1) / steps
-        # leave the outputs as one full step writes them
-        step(0)
+        e0.record()
+        mgraph.replay()
+        e1.record()
         torch.cuda.synchronize()
+        merge_ms = e0.elapsed_time(e1) / steps
+        del mgraph
+        step(0)  # leave the outputs as one full step writes them
+        torch.cuda.synchronize()
+    res = _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok, merge_ms, log)
+    del pools, kc0, vc0
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok, merge_ms, log):
     partial_ms = max(step_ms - merge_ms, 1e-6)
     res = dict(
         workload=wl.name,
@@ -170,7 +218,10 @@ def measure(k, steps, warmup, log):
         copies=copies,
         plan=plan,
         step_ms=step_ms,
+        eager_ms=eager_ms,
         wall_ms_per_step=wall_ms,
+        graph_wall_ms_per_step=graph_wall_ms,
+        graph_ok=graph_ok,
         partial_ms=partial_ms,
         merge_ms=merge_ms,
         kv_gbps=kvb / (step_ms * 1e-3) / 1e9,
@@ -181,9 +232,7 @@ def measure(k, steps, warmup, log):
     log(f"[bench] cfg{k}: step {step_ms * 1e3:.1f} us (partial {partial_ms * 1e3:.1f} us, merge "
         f"{merge_ms * 1e3:.1f} us), KV {res['kv_gbps']:.0f} GB/s = {res['pct_peak']:.1f}% of peak, "
         f"{res['tokens_per_s']:.3g} tok/s, splits {plan['num_splits']}, copies {copies}")
-    del pools, kc0, vc0
-    torch.cuda.empty_cache()
-    return res, wl
+    return res
 
 
 def cpu_baseline(wl, budget_s, log):
@@ -198,23 +247,100 @@ def cpu_baseline(wl, budget_s, log):
     done_bytes = 0
     done_tokens = 0
     seqs = 0
-    for b in range(wl.B):
-        rows = [(b, i, h) for i in range(wl.q_len) for h in range(wl.Hq)]
-        oracle.decode(**wl.oracle_kwargs(), rows=rows)
-        lo, hi = wl.key_union(b)
-        done_bytes += (hi - lo) * wl.Hkv * wl.D * 2
-        done_tokens += wl.q_len
-        seqs += 1
+    passes = 0
+    # whole sequences (all heads), in order, repeating the workload until the
+    # time budget is used (at least one full pass)
+    while True:
+        for b in range(wl.B):
+            rows = [(b, i, h) for i in range(wl.q_len) for h in range(wl.Hq)]
+            oracle.decode(**wl.oracle_kwargs(), rows=rows)
+            lo, hi = wl.key_union(b)
+            done_bytes += (hi - lo) * wl.Hkv * wl.D * 2
+            done_tokens += wl.q_len
+            seqs += 1
+            if passes > 0 and time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
     infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = int(infos[0].get("num_threads", ncores)) if infos else 1
     limiter.restore_original_limits()
-    log(f"[bench] cpu oracle: {seqs} sequences in {el:.1f}s, {done_bytes / el / 1e9:.3f} GB/s")
+    log(f"[bench] cpu oracle: {seqs} sequence decodes in {el:.1f}s, {done_bytes / el / 1e9:.3f} GB/s")
     return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{wl.name}: sequences 0..{seqs - 1} of {wl.B} (all {wl.Hq} heads, "
-                      f"{done_bytes} KV bytes) in {el:.1f}s; {done_tokens / el:.3g} tokens/s"}
+            "sample": f"{wl.name}: {seqs} sequence decodes (all {wl.Hq} heads each; the {wl.B}-sequence "
+                      f"batch repeated, {passes} pass(es)), {done_bytes} KV bytes in {el:.1f}s; "
+                      f"{done_tokens / el:.3g} tokens/s"}
+
+
+CALIB_BYTES = 256 << 20
+CALIB_COPIES = 8
+
+
+def calibrate_copy():
+    """Device-to-device copies of CALIB_BYTES each: the counter scale reference."""
+    import torch
+
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(CALIB_COPIES):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copies": CALIB_COPIES, "bytes_each": CALIB_BYTES}), flush=True)
+
+
+def _counter_rows(csv_dir, counter):
+    import csv
+    import glob
+    import re
+
+    rows = []
+    for f in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                m = re.search(r"(\w+<[\d, ]+>|__amd_\w+)", r["Kernel_Name"])
+                rows.append((int(r["Dispatch_Id"]), m.group(1) if m else r["Kernel_Name"][:40],
+                             float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def write_traffic(wl_fetch, wl_write, cal_fetch, cal_write, workload_name):
+    """Bytes per launch of each decode kernel from FETCH_SIZE / WRITE_SIZE (KiB),
+    each scaled by what the same counter reads for a copy of known size."""
+    cf = [v for _, k, v in _counter_rows(cal_fetch, "FETCH_SIZE") if k.startswith("__amd")]
+    cw = [v for _, k, v in _counter_rows(cal_write, "WRITE_SIZE") if k.startswith("__amd")]
+    cf = [v for v in cf if v > 0][-CALIB_COPIES:]
+    cw = [v for v in cw if v > 0][-CALIB_COPIES:]
+    fetch_scale = CALIB_BYTES / (sum(cf) / len(cf) * 1024.0)
+    write_scale = CALIB_BYTES / (sum(cw) / len(cw) * 1024.0)
+    out = {"workload": workload_name, "kernel_source_hash": kernel_source_hash(),
+           "calibration": {"copy_bytes": CALIB_BYTES, "fetch_kib_read": sum(cf) / len(cf),
+                           "write_kib_read": sum(cw) / len(cw), "fetch_scale": fetch_scale,
+                           "write_scale": write_scale}, "kernels": {}}
+    for name, rows_f, rows_w in (("fetch", _counter_rows(wl_fetch, "FETCH_SIZE"), None),
+                                 ("write", _counter_rows(wl_write, "WRITE_SIZE"), None)):
+        per = {}
+        for _, k, v in rows_f:
+            if k.startswith("__amd"):
+                continue
+            per.setdefault(k, []).append(v)
+        for k, vals in per.items():
+            d = out["kernels"].setdefault(k, {})
+            scale = fetch_scale if name == "fetch" else write_scale
+            d[name + "_bytes_per_launch"] = sum(vals) / len(vals) * 1024.0 * scale
+            d[name + "_launches"] = len(vals)
+    partial = [k for k in out["kernels"] if k.startswith("partial_")]
+    if partial:
+        d = out["kernels"][partial[0]]
+        out["hbm_bytes_per_launch"] = {"kernel": partial[0],
+                                       "read": round(d.get("fetch_bytes_per_launch", 0.0)),
+                                       "write": round(d.get("write_bytes_per_launch", 0.0))}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -223,9 +349,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--configs", default="1,2,3,4,5")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for profiler passes that do not follow graphs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the known-size device copies used to scale traffic counters")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("WL_FETCH", "WL_WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc output dirs -> profiles/traffic_<workload>.json (no GPU)")
     args = ap.parse_args()
+    if args.write_traffic:
+        from workloads import CONFIGS
+
+        write_traffic(*args.write_traffic, workload_name=f"cfg{HEADLINE}_{CONFIGS[HEADLINE]['name']}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU form in this library)", file=sys.stderr)
@@ -239,6 +376,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import decode_attention_paged_fp8pa_amd as fp
 
     fp.lib()
@@ -248,7 +388,7 @@ def main():
     results = {}
     head_wl = None
     for k in cfgs:
-        res, wl = measure(k, args.steps, args.warmup, log)
+        res, wl = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph)
         results[k] = res
         if k == HEADLINE:
             head_wl = wl
@@ -297,7 +437,8 @@ def main():
                 "pct_peak": round(r["pct_peak"], 2), "tokens_per_s": round(r["tokens_per_s"], 1),
                 "num_splits": r["plan"]["num_splits"], "grid_wgs": r["plan"]["grid_wgs"],
                 "variant": "mfma" if r["plan"]["variant"] == 1 else "dot",
-                "wall_us_per_step": round(r["wall_ms_per_step"] * 1e3, 2),
+                "eager_us_per_step": round(r["eager_ms"] * 1e3, 2),
+                "timing": "hip graph replay" if r["graph_ok"] else "eager",
             } for k, r in results.items()},
     }
     print(json.dumps(line), flush=True)

@@ -293,18 +293,6 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = uint32_t((4 * qd + j) * tok + S * n);
 
-  // Tokens every valid row of the wave attends: a tile inside [all_lo,
-  // all_hi) needs no per-token mask.
-  int all_lo = row.valid ? row.klo : 0;
-  int all_hi = row.valid ? row.khi : 0x7fffffff;
-#pragma unroll
-  for (int s2 = 1; s2 < 16; s2 <<= 1) {
-    all_lo = max(all_lo, __shfl_xor(all_lo, s2, 64));
-    all_hi = min(all_hi, __shfl_xor(all_hi, s2, 64));
-  }
-  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
-  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
-
   // Loads of one 32-token tile into registers.  A tile at or past `te`, or a
   // 16-token group holding no attended token, gets an empty descriptor: its
   // loads return zeros and touch no memory, and no table entry is read.
@@ -358,17 +346,14 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
       sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[c], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[c], sb, 0, 0, 0);
     }
-    // raw scores; a token no row of this lane attends becomes -inf (edge
-    // tiles only: interior tiles are attended by every row of the wave)
+    // raw scores; a token this lane's row does not attend becomes -inf.  (A
+    // branch that skips the masks on interior tiles measured slower: it moves
+    // the waits on the next tile's loads.)
     float sv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = j < 4 ? sa[j] : sb[j - 4];
-    if (!(kb >= all_lo && kb + kTileTokens <= all_hi)) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-        sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+      sv[j] = (key >= row.klo && key < row.khi) ? (j < 4 ? sa[j] : sb[j - 4]) : -INFINITY;
     }
     float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
