@@ -15,6 +15,9 @@ import math
 from ._lib import (  # noqa: F401
     FP8PA_FLAG_FORCE_DOT,
     FP8PA_FLAG_FORCE_MFMA,
+    FP8PA_SPLIT_BALANCED,
+    FP8PA_SPLIT_DIRECT,
+    FP8PA_SPLIT_FIXED,
     Fp8paError,
     LIB_PATH,
     PlanInfo,
@@ -41,6 +44,9 @@ __all__ = [
     "Fp8paError",
     "FP8PA_FLAG_FORCE_DOT",
     "FP8PA_FLAG_FORCE_MFMA",
+    "FP8PA_SPLIT_BALANCED",
+    "FP8PA_SPLIT_DIRECT",
+    "FP8PA_SPLIT_FIXED",
 ]
 
 

@@ -22,6 +22,9 @@ FP8PA_ERR_HIP = 5
 
 FP8PA_FLAG_FORCE_DOT = 1
 FP8PA_FLAG_FORCE_MFMA = 2
+FP8PA_SPLIT_DIRECT = 0
+FP8PA_SPLIT_FIXED = 1
+FP8PA_SPLIT_BALANCED = 2
 
 
 class Fp8paError(RuntimeError):
@@ -59,10 +62,14 @@ class PlanInfo(ctypes.Structure):
 
     _fields_ = [
         ("variant", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("tiles_per_split", ctypes.c_int32),
+        ("max_tiles_per_split", ctypes.c_int32),
+        ("target_items", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32),
         ("heads_per_wg", ctypes.c_int32),
+        ("waves_per_head", ctypes.c_int32),
         ("rows_per_group", ctypes.c_int32),
         ("row_groups", ctypes.c_int32),
         ("grid_wgs", ctypes.c_int32),

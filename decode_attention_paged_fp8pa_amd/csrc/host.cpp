@@ -5,9 +5,10 @@
 // split producers plus one LSE reducer; split only as far as one wave of
 // work needs) re-derived for MI355X: each wavefront owns one
 // (sequence, kv head, row group, split) work item and walks 32-token tiles
-// of its key range; the split count is raised until the grid holds about
-// kTargetWavesPerCu wavefronts per compute unit, but a split keeps enough
-// keys that its partial output stays small next to the KV bytes it reads.
+// of its key range.  Splits are sized so that the busy wavefronts fill the
+// compute units about once (as many as their registers let one hold); for
+// batches of up to 256 sequences the kernel sizes them from the real
+// seq_lens, which only the device holds.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -89,12 +90,14 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // MFMA kernel's register budget sets how many wavefronts share a SIMD
   // (4 at D = 64, 2 at D = 128, 1 at D = 256): groups of 8 at D = 64 and 4
   // otherwise let whole groups fill a compute unit.
-  const int32_t max_hg = (p.variant == kVariantMfma && p.D != 64) ? 4 : 8;
+  // At D = 256 the MFMA kernel splits head_dim over two wavefronts (they
+  // exchange partial scores through LDS), which halves their registers.
+  p.ds = (p.variant == kVariantMfma && p.D == 256) ? 2 : 1;
+  const int32_t max_hg = (p.variant == kVariantMfma && p.D != 64) ? 4 / p.ds : 8;
   p.hg = 1;
   while (p.hg * 2 <= max_hg && p.Hkv % (p.hg * 2) == 0) p.hg *= 2;
-  const int64_t units = int64_t(p.B) * (p.Hkv / p.hg) * p.row_groups;
-  if (units > (int64_t(1) << 30)) return FP8PA_ERR_UNSUPPORTED;
-  p.units = int32_t(units);
+  p.upi = (p.Hkv / p.hg) * p.row_groups;
+  const int64_t waves_per_item = int64_t(p.upi) * p.hg * p.ds;
 
   // Tiles a sequence can span: its attended keys, plus one when a window
   // start need not fall on a tile boundary.
@@ -104,45 +107,88 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     if (wk < max_keys) max_keys = wk;
   }
   const int64_t n_tiles = ceil_div(max_keys, kTileTokens) + (s->window > 0 ? 1 : 0);
+  // The MFMA kernel holds a split's block-table entries in registers.
+  const int64_t tps_cap = p.variant == kVariantMfma
+                              ? ((int64_t(kMaxSplitPages) - 1) * p.bt) / kTileTokens - 1
+                              : n_tiles;
+  p.tps_cap = int32_t(tps_cap < n_tiles ? tps_cap : n_tiles);
 
-  const int64_t waves_per_split = units * p.hg;
-  int64_t tps;
+  // Splits: enough (sequence, split) items that the busy wavefronts fill the
+  // device about once.  The host knows only max_seq_len, so for a batch of
+  // up to kMaxBalancedBatch sequences the kernel itself reads seq_lens and
+  // sizes one chunk for the batch's real tile count (BALANCED); longer
+  // batches, or a caller's split count, get splits of a fixed size.
+  // Wavefronts of the partial kernel one compute unit holds at once: the
+  // MFMA kernel's registers allow 4 per SIMD at D = 64 and 2 otherwise
+  // (head_dim 256 is split over two wavefronts); the dot kernel's 2.
+  const int64_t waves_per_cu = (p.variant == kVariantMfma && p.D == 64) ? 16 : 8;
+  const int64_t target_waves = int64_t(cu_count) * waves_per_cu;
+  int64_t target_items = target_waves / waves_per_item;
+  if (target_items < 1) target_items = 1;
+  int64_t tps = 0, splits = 1, items = 0;
+  // Each split writes rows * D floats of partial output (and the merge reads
+  // them back) against 2 * D bytes of KV per key: at least ~64 keys per
+  // query row keep that small, where parallelism allows.
+  p.min_tiles = int32_t(ceil_div(int64_t(rows_eff) * 64, kTileTokens));
+  p.split_mode = FP8PA_SPLIT_FIXED;
   if (s->num_splits > 0) {
     tps = ceil_div(n_tiles, s->num_splits);
+  } else if (p.B <= kMaxBalancedBatch && target_items > 2 * int64_t(p.B) &&
+             n_tiles > 1) {
+    // Every sequence's last split may be short, so up to B items more than
+    // T / c: aiming at target - B keeps all items in one round.
+    p.split_mode = FP8PA_SPLIT_BALANCED;
+    target_items -= p.B;
+    // The kernel's chunk is at least min(min_tiles, 2 T / target_items) and
+    // T / target_items: one tile at the least, so the slots must allow one
+    // split per tile up to the target.
+    tps = p.min_tiles;
+    splits = n_tiles < target_items ? n_tiles : target_items;
+    const int64_t need = ceil_div(n_tiles, int64_t(p.tps_cap));
+    if (splits < need) splits = need;
+    // sum_b max(1, ceil(n_b / c)) <= T / c + B, and the kernel's chunk c is at
+    // least T / target_items unless the cap binds
+    int64_t bound = ceil_div(int64_t(p.B) * n_tiles, int64_t(p.tps_cap));
+    if (bound < target_items) bound = target_items;
+    items = bound + p.B;
+    if (items > int64_t(p.B) * splits) items = int64_t(p.B) * splits;
   } else {
-    const int64_t target = int64_t(cu_count) * kTargetWavesPerCu;
-    const int64_t want = ceil_div(target, waves_per_split);
+    const int64_t want = ceil_div(target_items, int64_t(p.B));
     tps = ceil_div(n_tiles, want);
     // Keep each split's partial (rows * D floats) small next to the KV it
     // reads (2 * D bytes per key): at least ~64 keys per query row, as long
     // as that still leaves half the target parallelism.
-    const int64_t min_tiles = ceil_div(int64_t(rows_eff) * 64, kTileTokens);
-    int64_t cap = (n_tiles * waves_per_split) / (target / 2 > 0 ? target / 2 : 1);
+    const int64_t min_tiles = p.min_tiles;
+    const int64_t per_split = int64_t(p.B) * waves_per_item;
+    int64_t cap = (n_tiles * per_split) / (target_waves / 2 > 0 ? target_waves / 2 : 1);
     if (cap < 1) cap = 1;
     const int64_t lift = min_tiles < cap ? min_tiles : cap;
     if (tps < lift) tps = lift;
   }
-  if (tps < 1) tps = 1;
-  if (p.variant == kVariantMfma) {
-    // the MFMA kernel holds a split's block-table entries in registers
-    const int64_t max_tps = ((int64_t(kMaxSplitPages) - 1) * p.bt) / kTileTokens - 1;
-    if (tps > max_tps) tps = max_tps;
+  if (p.split_mode == FP8PA_SPLIT_FIXED) {
+    if (tps < 1) tps = 1;
+    if (tps > p.tps_cap) tps = p.tps_cap;
+    splits = ceil_div(n_tiles, tps);
+    if (splits < 1) splits = 1;
+    items = int64_t(p.B) * splits;
+    if (splits == 1) p.split_mode = FP8PA_SPLIT_DIRECT;
   }
-  int64_t splits = ceil_div(n_tiles, tps);
-  if (splits < 1) splits = 1;
-  if (splits * units > (int64_t(1) << 31) - 1) return FP8PA_ERR_UNSUPPORTED;
+  if (items * p.upi > (int64_t(1) << 31) - 1) return FP8PA_ERR_UNSUPPORTED;
   p.tps = int32_t(tps);
   p.num_splits = int32_t(splits);
-  p.grid_wgs = int32_t(splits * units);
-  p.direct = splits == 1 ? 1 : 0;
+  p.target_items = p.split_mode == FP8PA_SPLIT_BALANCED ? int32_t(target_items) : 0;
+  p.items = int32_t(items);
+  p.grid_wgs = int32_t(items * p.upi);
+  p.direct = p.split_mode == FP8PA_SPLIT_DIRECT ? 1 : 0;
 
   if (!p.direct) {
     const int64_t rows_total = int64_t(p.B) * p.q_len * p.Hq;
-    const int64_t po = rows_total * splits * p.D * 4;
+    const int64_t po = rows_total * splits * p.D * 4;  // splits = p.num_splits
     const int64_t pl = rows_total * splits * 4;
     const int64_t off = ceil_div(po, kWorkspaceAlign) * kWorkspaceAlign;
     p.off_lse = size_t(off);
-    p.ws_bytes = size_t(off + ceil_div(pl, kWorkspaceAlign) * kWorkspaceAlign);
+    p.off_chunk = size_t(off + ceil_div(pl, kWorkspaceAlign) * kWorkspaceAlign);
+    p.ws_bytes = p.off_chunk + kWorkspaceAlign;
   }
   *plan = p;
   return FP8PA_OK;
@@ -152,6 +198,8 @@ fp8pa_status check_merge_args(int32_t num_splits, int32_t num_rows, int32_t num_
                               int32_t head_dim) {
   if (num_splits < 1 || num_rows < 0 || num_q_heads < 1) return FP8PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FP8PA_ERR_UNSUPPORTED;
+  // one merge wavefront per (row, 64 dims)
+  if (int64_t(num_rows) * (head_dim / 64) > (int64_t(1) << 31) - 1) return FP8PA_ERR_UNSUPPORTED;
   return FP8PA_OK;
 }
 
@@ -166,10 +214,14 @@ fp8pa_status fp8pa_plan(const fp8pa_shape* shape, int32_t cu_count, fp8pa_plan_i
   if (st != FP8PA_OK) return st;
   std::memset(out, 0, sizeof(*out));
   out->variant = p.variant;
+  out->split_mode = p.split_mode;
   out->num_splits = p.num_splits;
   out->tiles_per_split = p.tps;
+  out->max_tiles_per_split = p.tps_cap;
+  out->target_items = p.target_items;
   out->tile_tokens = fp8pa::kTileTokens;
   out->heads_per_wg = p.hg;
+  out->waves_per_head = p.ds;
   out->rows_per_group = p.rpg;
   out->row_groups = p.row_groups;
   out->grid_wgs = p.grid_wgs;

@@ -81,9 +81,19 @@ struct Params {
   float* part_lse;
   int64_t page_bytes;  // bt * Hkv * D
   int32_t tok_stride;  // Hkv * D: bytes between token slots of a page
-  int32_t q_len, Hq, Hkv, G, rows, row_groups, hg, units, num_splits, tps;
+  int32_t B, q_len, Hq, Hkv, G, rows, row_groups, hg;
+  int32_t upi;           // workgroups per (sequence, split) item
+  int32_t num_splits;    // partial slots per query row
+  int32_t tps;           // tiles per split; balanced plan: the least chunk
+  int32_t tps_cap;       // the largest chunk
+  int32_t balanced;      // 1: the chunk comes from the batch's seq_lens
+  int32_t target_items;  // balanced plan: items the chunk size aims at
+  int32_t min_tiles;     // balanced plan: chunk floor that keeps partials small
+  int32_t* chunk_out;    // balanced plan: the chosen chunk, for the merge
+  int32_t max_seq_len;
   int32_t bt_shift, bt_mask, table_stride, window;
   int32_t k_per_head, v_per_head, direct;
+  int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
   float sm_scale;
 };
 
@@ -156,24 +166,153 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
   return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
 }
 
-// Work item of this workgroup: (b, kv head group, row group, split).
-struct Work {
-  int b, g, rg, split;
+__device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_scan_i(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Keys of sequence b that some query row attends: [ulo, uhi), covered by the
+// 32-token tiles [tile0, tile1) (tiles are aligned to absolute positions).
+struct Span {
+  int ulo, uhi, tile0, tile1;
 };
 
-__device__ __forceinline__ Work work_of(const Params& p) {
+__device__ __forceinline__ Span span_of(int L, int q_len, int window) {
+  Span sp;
+  sp.uhi = L;
+  sp.ulo = window > 0 ? max(0, L - q_len - window + 1) : 0;
+  sp.tile0 = sp.ulo / kTileTokens;
+  sp.tile1 = sp.uhi > sp.ulo ? (sp.uhi - 1) / kTileTokens + 1 : sp.tile0;
+  return sp;
+}
+
+// Splits of a sequence with n tiles at chunk c (an empty sequence keeps one
+// split, which writes LSE -inf), at most num_splits.
+__device__ __forceinline__ int splits_of(int n, int c, int num_splits) {
+  return n > 0 ? min(ceil_div_i(n, c), num_splits) : 1;
+}
+
+// seq_lens[b] limited to [0, max_seq_len], which bounds every table and page
+// access of the kernels whatever the device array holds.
+__device__ __forceinline__ int seq_len_of(const Params& p, int b) {
+  return min(max(p.seq_lens[b], 0), p.max_seq_len);
+}
+
+// Work of one wavefront: (sequence b, kv head g, row group rg, split) and
+// the split's tiles [ts, te).  Workgroup x takes item x / upi, an index into
+// the batch's (sequence, split) pairs in sequence-major order, and kv head
+// group and row group x % upi.
+struct Work {
+  int b, g, rg, split;
+  int half;    // which part of head_dim this wavefront owns (0 unless head_dim is split)
+  int nsplit;  // splits of sequence b; its slots [nsplit, num_splits) stay unused
+  int L, ts, te;
+  Span sp;
+  bool active;  // false: the item index lies past the batch's last split
+};
+
+__device__ __forceinline__ Work work_of(const Params& p, int ds) {
   Work w;
   const int wg = blockIdx.x;
-  w.split = wg / p.units;
-  const int unit = wg - w.split * p.units;
+  const int item = wg / p.upi;
+  const int unit = wg - item * p.upi;
   w.rg = unit % p.row_groups;
-  const int t = unit / p.row_groups;
-  const int ngg = p.Hkv / p.hg;
-  const int gg = t % ngg;
-  w.b = t / ngg;
+  const int gg = unit / p.row_groups;
   // the wavefront index is uniform across the wave; saying so keeps every
   // address derived from it (descriptor bases, table rows) in scalar registers
-  w.g = gg * p.hg + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  w.g = gg * p.hg + wv / ds;
+  w.half = wv - (wv / ds) * ds;
+  w.active = true;
+
+  if (!p.balanced) {
+    w.b = item / p.num_splits;
+    w.split = item - w.b * p.num_splits;
+    w.nsplit = p.num_splits;
+    w.L = seq_len_of(p, w.b);
+    w.sp = span_of(w.L, p.q_len, p.window);
+    w.ts = w.sp.tile0 + w.split * p.tps;
+    w.te = min(w.ts + p.tps, w.sp.tile1);
+    return w;
+  }
+
+  // Balanced plan.  Every wavefront derives the same chunk c from the whole
+  // batch: T tiles in all, M in the longest sequence.  c >= T / target_items
+  // keeps the items near the target; c >= min(min_tiles, 2 T / target_items)
+  // keeps each split's partial output small next to the KV bytes it reads
+  // while leaving at least about half the target; c >= M / num_splits keeps
+  // every sequence within its slots, and c <= tps_cap within the table
+  // registers (the plan makes num_splits * tps_cap cover M).  Sequence b
+  // then gets splits_of(n_b, c) splits.  Lane l holds sequences l + 64 j.
+  const int lane = threadIdx.x & 63;
+  int Lj[4], nj[4];
+  int tsum = 0, tmax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = lane + 64 * j;
+    Lj[j] = b < p.B ? seq_len_of(p, b) : 0;
+    const Span sp = span_of(Lj[j], p.q_len, p.window);
+    nj[j] = b < p.B ? sp.tile1 - sp.tile0 : 0;
+    tsum += nj[j];
+    tmax = max(tmax, nj[j]);
+  }
+  // (reductions leave the same value in every lane; readfirstlane says so,
+  // which keeps the tile range, and so every buffer descriptor, scalar)
+  const int T = __builtin_amdgcn_readfirstlane(wave_sum_i(tsum));
+  const int M = __builtin_amdgcn_readfirstlane(wave_max_i(tmax));
+  int c = ceil_div_i(T, p.target_items);
+  c = max(c, min(p.min_tiles, max(1, (2 * T) / p.target_items)));
+  c = max(c, ceil_div_i(M, p.num_splits));
+  c = min(c, p.tps_cap);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.chunk_out = c;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (64 * j >= p.B) break;
+    const int b = lane + 64 * j;
+    const int ns = b < p.B ? splits_of(nj[j], c, p.num_splits) : 0;
+    const int incl = wave_scan_i(ns, lane);
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    if (item < base + tot) {
+      const uint64_t mask = __ballot(base + incl > item);
+      const int ln = __builtin_ctzll(mask);
+      w.b = 64 * j + ln;
+      w.nsplit = __builtin_amdgcn_readlane(ns, ln);
+      w.split = item - base - (__builtin_amdgcn_readlane(incl, ln) - w.nsplit);
+      w.L = __builtin_amdgcn_readlane(Lj[j], ln);
+      w.sp = span_of(w.L, p.q_len, p.window);
+      w.ts = w.sp.tile0 + w.split * c;
+      w.te = min(w.ts + c, w.sp.tile1);
+      return w;
+    }
+    base += tot;
+  }
+  w.active = false;
+  w.b = 0;
+  w.split = 0;
+  w.nsplit = 0;
+  w.L = 0;
+  w.sp = span_of(0, p.q_len, p.window);
+  w.ts = w.te = 0;
   return w;
 }
 
@@ -213,32 +352,35 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
 //     kap(qd, j) = 4 qd + j (j < 4) and 16 + 4 qd + j - 4 (j >= 4), which are
 //     exactly the tokens whose scores the QK accumulators give this lane.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D == 64 ? 512 : 256)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void partial_mfma_kernel(Params p) {
-  constexpr int S = D / 16;       // V bytes per lane per token
-  constexpr int KB = D / 4;       // K bytes per lane per token
-  constexpr int KSTEPS = D / 32;  // QK k-steps of 32 dims
-  constexpr int KW = KB / 4;      // K dwords per lane per group
-  constexpr int SW = S / 4;       // V dwords per lane per token
+template <int D, int DS>
+__global__ __launch_bounds__(D / DS == 64 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(D / DS == 64 ? 4 : D / DS == 128 ? 2 : 1, 8))) void
+partial_mfma_kernel(Params p) {
+  static_assert(DS == 1 || DS == 2, "head_dim split");
+  constexpr int DW = D / DS;       // head_dim slice of this wavefront
+  constexpr int S = DW / 16;       // V bytes per lane per token
+  constexpr int KB = DW / 4;       // K bytes per lane per token
+  constexpr int KSTEPS = DW / 32;  // QK k-steps of 32 dims
+  constexpr int KW = KB / 4;       // K dwords per lane per group
+  constexpr int SW = S / 4;        // V dwords per lane per token
+  // Partial scores of the two wavefronts that share a kv head (DS = 2):
+  // [wavefront][tile parity][lane][2 x f32x4].
+  __shared__ f32x4 xch[DS == 2 ? 4 * 2 * 64 * 2 : 1];
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int qd = lane >> 4;
-  const Work w = work_of(p);
-  const int L = p.seq_lens[w.b];
-  const int ulo = p.window > 0 ? max(0, L - p.q_len - p.window + 1) : 0;
-  const int uhi = L;
-  const int tile0 = ulo / kTileTokens;
-  const int tile1 = uhi > ulo ? (uhi - 1) / kTileTokens + 1 : tile0;
-  const int ts = tile0 + w.split * p.tps;
-  const int te = min(ts + p.tps, tile1);
+  const Work w = work_of(p, DS);
+  if (!w.active) return;  // uniform over the workgroup
+  const int d0 = w.half * DW;      // first dim of this wavefront's slice
+  const int L = w.L;
+  const int ulo = w.sp.ulo, uhi = w.sp.uhi;
+  const int ts = w.ts, te = w.te;
   const Row row = row_of(p, w.b, w.g, w.rg * kRowsMfma + n, L);
 
-  if (ts >= te && !p.direct) {
-    if (row.valid && qd == 0) p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
-    return;
-  }
+  if (ts >= te && !p.direct && w.half == 0 && row.valid && qd == 0)
+    p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
+  if (ts >= te && !p.direct) return;
 
   long qhi[KSTEPS], qlo[KSTEPS];  // the query row in E4M3 hi + lo parts (set below)
   float cr;                       // score scale into log2 units
@@ -253,8 +395,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
   for (int e = 0; e < S; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int tok = p.tok_stride;
-  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D;
-  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D;
+  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D + d0;
+  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D + d0;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
   const uint32_t koff = uint32_t(n * tok + KB * qd);
 
@@ -275,7 +417,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
   // are issued, so the two round trips overlap.
   u32x4 qraw[KB / 8];
   {
-    const uint16_t* qrow = p.q + row.out_row * D + KB * qd;
+    const uint16_t* qrow = p.q + row.out_row * D + d0 + KB * qd;
 #pragma unroll
     for (int i = 0; i < KB / 8; ++i)
       qraw[i] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
@@ -346,19 +488,45 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
       sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[c], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[c], sb, 0, 0, 0);
     }
-    // raw scores; a token this lane's row does not attend becomes -inf.  (A
-    // branch that skips the masks on interior tiles measured slower: it moves
-    // the waits on the next tile's loads.)
+    // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc (one
+    // head_dim slice per wavefront), or, when two wavefronts split head_dim,
+    // the sum of both slices' scaled scores exchanged through LDS.
     float sv[8];
+    float csc = cr;
+    if constexpr (DS == 2) {
+      const int parity = (tt - ts) & 1;
+      const int wv = int(threadIdx.x >> 6);
+      f32x4* mine = &xch[((wv * 2 + parity) * 64 + lane) * 2];
+      mine[0] = sa * cr;
+      mine[1] = sb * cr;
+      __syncthreads();
+      const f32x4* other = &xch[(((wv ^ 1) * 2 + parity) * 64 + lane) * 2];
+      const f32x4 oa = other[0], ob = other[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = sa[j] * cr + oa[j];
+        sv[j + 4] = sb[j] * cr + ob[j];
+      }
+      csc = 1.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = sa[j];
+        sv[j + 4] = sb[j];
+      }
+    }
+    // a token this lane's row does not attend becomes -inf.  (A branch that
+    // skips the masks on interior tiles measured slower: it moves the waits
+    // on the next tile's loads.)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-      sv[j] = (key >= row.klo && key < row.khi) ? (j < 4 ? sa[j] : sb[j - 4]) : -INFINITY;
+      sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
     }
     float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     ms = max_over_groups(ms);
-    const float mx = ms * cr;  // cr > 0, so the scaled max is the max of the scaled
+    const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
     // Lazy reference max: move m only when this tile exceeds it by more than
     // kLazy (log2 units), so most tiles skip the O rescale; P stays
     // <= 2^(kLazy + kPShift).
@@ -374,7 +542,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
     const float noff = kPShift - (m == -INFINITY ? 0.f : m);
     float pj[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], cr, noff));
+    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
     lsum += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
 
     // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
@@ -497,7 +665,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
   const float lse = empty ? -INFINITY : (m + log2_fast(lsum) - kPShift) * kLn2;
   // O[e][i] is output dim S * (4 qd + i) + e of this lane's row.
   if (p.direct) {
-    uint16_t* orow = p.out + row.out_row * D;
+    uint16_t* orow = p.out + row.out_row * D + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t pk[S / 2];
@@ -512,11 +680,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
           reinterpret_cast<u32x4*>(dst)[v] = u32x4{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
       }
     }
-    if (p.lse && qd == 0) p.lse[row.out_row] = lse;
+    if (p.lse && qd == 0 && w.half == 0) p.lse[row.out_row] = lse;
   } else {
     const size_t slot = row.out_row * p.num_splits + w.split;
     if (!empty) {
-      float* prow = p.part_o + slot * D;
+      float* prow = p.part_o + slot * D + d0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float* dst = prow + S * (4 * qd + i);
@@ -526,7 +694,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : D == 128 ? 2 : 1, 8))) void par
               f32x4{O[4 * v][i] * inv, O[4 * v + 1][i] * inv, O[4 * v + 2][i] * inv, O[4 * v + 3][i] * inv};
       }
     }
-    if (qd == 0) p.part_lse[slot] = lse;
+    if (qd == 0 && w.half == 0) p.part_lse[slot] = lse;
   }
 }
 
@@ -545,14 +713,11 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int kk = lane / LPK;
   const int c = lane % LPK;
-  const Work w = work_of(p);
-  const int L = p.seq_lens[w.b];
-  const int ulo = p.window > 0 ? max(0, L - p.q_len - p.window + 1) : 0;
-  const int uhi = L;
-  const int tile0 = ulo / kTileTokens;
-  const int tile1 = uhi > ulo ? (uhi - 1) / kTileTokens + 1 : tile0;
-  const int ts = tile0 + w.split * p.tps;
-  const int te = min(ts + p.tps, tile1);
+  const Work w = work_of(p, 1);
+  if (!w.active) return;  // uniform over the workgroup
+  const int L = w.L;
+  const int ulo = w.sp.ulo, uhi = w.sp.uhi;
+  const int ts = w.ts, te = w.te;
 
   Row rows[RPG];
 #pragma unroll
@@ -732,81 +897,87 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
 // whose weight is 0 (LSE = -inf) is skipped by a select, so whatever its
 // partial output holds (never written, possibly NaN) cannot leak.
 // ---------------------------------------------------------------------------
-template <int E>
-__device__ __forceinline__ void load_dims(const float* src, float* o) {
-  if constexpr (E == 1) {
-    o[0] = src[0];
-  } else if constexpr (E == 2) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(src);
-    o[0] = v.x;
-    o[1] = v.y;
-  } else {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src);
-    o[0] = v.x;
-    o[1] = v.y;
-    o[2] = v.z;
-    o[3] = v.w;
-  }
-}
-
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+struct MergeArgs {
+  int num_splits, num_rows, Hq;
+  const float* po;
+  const float* pl;
+  const float* sinks;
+  uint16_t* out;
+  float* lse_out;
+  // Optional: the split plan that wrote the partials, so that a row reads
+  // only the splits its sequence has.  seq_lens == nullptr: num_splits each.
+  const int32_t* seq_lens;
+  const int32_t* chunk;  // the balanced plan's chunk (device word), or nullptr
+  int fixed_chunk;       // the fixed plan's tiles per split
+  int q_len, window, max_seq_len;
+};
+
+// One wavefront per (query row, 64 dims of head_dim): lane l owns dim
+// 64 c + l.  Only splits with a nonzero weight are read: a ballot over the
+// weights gives their indices, taken U at a time.  The first 64 LSEs and the
+// first U splits' partial outputs are loaded before the split count and the
+// weights are known (slots fill from 0 upwards), which hides a round trip.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows, int Hq,
-                                                     const float* __restrict__ po,
-                                                     const float* __restrict__ pl,
-                                                     const float* __restrict__ sinks,
-                                                     uint16_t* __restrict__ out,
-                                                     float* __restrict__ lse_out) {
-  constexpr int E = D / 64;
-  constexpr int U = 16;  // splits whose partial outputs are loaded together
-  const int row = blockIdx.x * 4 + int(threadIdx.x >> 6);
-  if (row >= num_rows) return;
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int C = D / 64;  // wavefronts per row
+  constexpr int U = 16;      // partial outputs in flight together
+  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int row = wave / C;
+  const int chunk = wave - row * C;
+  if (row >= a.num_rows) return;
   const int lane = threadIdx.x & 63;
-  const float* lrow = pl + (size_t)row * num_splits;
-  const float* obase = po + (size_t)row * num_splits * D + E * lane;
-  const float sink2 = sinks ? sinks[row % Hq] * kLog2e : -INFINITY;
-  // The first U splits' partial outputs do not depend on the weights: their
-  // loads are issued first and stay in flight while the LSEs are reduced.
-  const int n_first = min(num_splits, 64);
-  float o0[U][E];
+  const int S = a.num_splits;
+  const float* lrow = a.pl + (size_t)row * S;
+  const float* obase = a.po + (size_t)row * S * D + 64 * chunk + lane;
+  const float sink2 = a.sinks ? a.sinks[row % a.Hq] * kLog2e : -INFINITY;
+  const float l0 = lane < S ? lrow[lane] : -INFINITY;
+  float o0[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) load_dims<E>(obase + (size_t)min(u, n_first - 1) * D, o0[u]);
-  float M = sink2;
-  for (int s = lane; s < num_splits; s += 64) M = fmaxf(M, lrow[s] * kLog2e);
+  for (int u = 0; u < U; ++u) o0[u] = u < S ? obase[(size_t)u * D] : 0.f;
+  int ns = S;
+  if (a.seq_lens) {
+    const int b = row / (a.q_len * a.Hq);
+    const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+    const Span sp = span_of(L, a.q_len, a.window);
+    const int c = a.chunk ? *a.chunk : a.fixed_chunk;
+    ns = __builtin_amdgcn_readfirstlane(splits_of(sp.tile1 - sp.tile0, c, S));
+  }
+  float M = fmaxf(sink2, lane < ns ? l0 * kLog2e : -INFINITY);
+  for (int s = 64 + lane; s < ns; s += 64) M = fmaxf(M, lrow[s] * kLog2e);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_shfl(M, m));
   const float Mu = M == -INFINITY ? 0.f : M;  // every weight is 0 then
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  float lpart = 0.f;
-  for (int s0 = 0; s0 < num_splits; s0 += 64) {
+  float acc = 0.f, lpart = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float w = s < num_splits ? exp2_fast(lrow[s] * kLog2e - Mu) : 0.f;
+    const float ls = s0 == 0 ? l0 : (s < ns ? lrow[s] : -INFINITY);
+    const float w = s < ns ? exp2_fast(ls * kLog2e - Mu) : 0.f;
     lpart += w;
-    const int n = min(64, num_splits - s0);
-    for (int j0 = 0; j0 < n; j0 += U) {
-      // U splits' loads in flight together; an index past the last split
-      // re-reads the last one and gets weight 0
-      float o[U][E];
-      if (s0 == 0 && j0 == 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int e = 0; e < E; ++e) o[u][e] = o0[u][e];
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_dims<E>(obase + (size_t)(s0 + min(j0 + u, n - 1)) * D, o[u]);
-      }
+    uint64_t mask = __ballot(w > 0.f);
+    if (s0 == 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float wu = j0 + u < n ? lane_value(w, min(j0 + u, 63)) : 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = wu > 0.f ? fmaf(wu, o[u][e], acc[e]) : acc[e];
+        const float wu = lane_value(w, u);
+        acc = wu > 0.f ? fmaf(wu, o0[u], acc) : acc;
       }
+      mask &= ~((uint64_t(1) << U) - 1);
+    }
+    while (mask) {
+      int idx[U];
+      float o[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        idx[u] = mask ? __builtin_ctzll(mask) : -1;
+        mask &= mask - 1;
+        o[u] = idx[u] >= 0 ? obase[(size_t)(s0 + idx[u]) * D] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (idx[u] >= 0) acc = fmaf(lane_value(w, idx[u]), o[u], acc);
     }
   }
 #pragma unroll
@@ -814,16 +985,9 @@ __global__ __launch_bounds__(256) void merge_kernel(int num_splits, int num_rows
   const float Lsum = lpart + (sink2 > -INFINITY ? exp2_fast(sink2 - Mu) : 0.f);
   const bool empty = !(Lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / Lsum;
-  uint16_t* dst = out + (size_t)row * D + E * lane;
-  if constexpr (E == 1) {
-    dst[0] = uint16_t(f32_to_bf16(acc[0] * inv));
-  } else if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  } else {
-    *reinterpret_cast<u32x2*>(dst) =
-        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  }
-  if (lse_out && lane == 0) lse_out[row] = empty ? -INFINITY : (Mu + log2_fast(Lsum)) * kLn2;
+  a.out[(size_t)row * D + 64 * chunk + lane] = uint16_t(f32_to_bf16(acc * inv));
+  if (a.lse_out && chunk == 0 && lane == 0)
+    a.lse_out[row] = empty ? -INFINITY : (Mu + log2_fast(Lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -877,23 +1041,22 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 
 template <int D>
 hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
-  const dim3 grid(pl.grid_wgs), block(64 * pl.hg);
+  const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
   if (pl.variant == kVariantMfma)
-    partial_mfma_kernel<D><<<grid, block, 0, st>>>(prm);
+    partial_mfma_kernel<D, (D == 256 ? 2 : 1)><<<grid, block, 0, st>>>(prm);
   else
     partial_dot_kernel<D><<<grid, block, 0, st>>>(prm);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(int D, int num_splits, int num_rows, int Hq, const float* po,
-                        const float* plse, const float* sinks, uint16_t* out, float* lse,
-                        hipStream_t st) {
-  if (num_rows == 0) return hipSuccess;
-  const dim3 grid((num_rows + 3) / 4), block(256);
+hipError_t launch_merge(int D, const MergeArgs& a, hipStream_t st) {
+  if (a.num_rows == 0) return hipSuccess;
+  const int64_t waves = int64_t(a.num_rows) * (D / 64);
+  const dim3 grid(unsigned((waves + 3) / 4)), block(256);
   switch (D) {
-    case 64: merge_kernel<64><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
-    case 128: merge_kernel<128><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
-    default: merge_kernel<256><<<grid, block, 0, st>>>(num_splits, num_rows, Hq, po, plse, sinks, out, lse); break;
+    case 64: merge_kernel<64><<<grid, block, 0, st>>>(a); break;
+    case 128: merge_kernel<128><<<grid, block, 0, st>>>(a); break;
+    default: merge_kernel<256><<<grid, block, 0, st>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -965,10 +1128,18 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.G = pl.G;
   prm.rows = pl.rows;
   prm.row_groups = pl.row_groups;
+  prm.B = pl.B;
   prm.hg = pl.hg;
-  prm.units = pl.units;
+  prm.upi = pl.upi;
   prm.num_splits = pl.num_splits;
   prm.tps = pl.tps;
+  prm.tps_cap = pl.tps_cap;
+  prm.balanced = pl.split_mode == FP8PA_SPLIT_BALANCED ? 1 : 0;
+  prm.target_items = pl.target_items > 0 ? pl.target_items : 1;
+  prm.max_seq_len = shape->max_seq_len;
+  prm.min_tiles = pl.min_tiles;
+  prm.chunk_out =
+      pl.direct ? nullptr : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.off_chunk);
   prm.bt_shift = pl.bt_shift;
   prm.bt_mask = pl.bt - 1;
   prm.table_stride = shape->block_table_stride;
@@ -976,6 +1147,7 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.k_per_head = shape->k_scale_count > 1 ? 1 : 0;
   prm.v_per_head = shape->v_scale_count > 1 ? 1 : 0;
   prm.direct = pl.direct;
+  prm.ds = pl.ds;
   prm.sm_scale = shape->sm_scale;
 
   const hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -987,8 +1159,22 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   }
   if (e != hipSuccess) return FP8PA_ERR_HIP;
   if (!pl.direct) {
-    e = launch_merge(pl.D, pl.num_splits, pl.B * pl.q_len * pl.Hq, pl.Hq, prm.part_o, prm.part_lse,
-                     sinks, prm.out, lse, hs);
+    MergeArgs ma;
+    ma.num_splits = pl.num_splits;
+    ma.num_rows = pl.B * pl.q_len * pl.Hq;
+    ma.Hq = pl.Hq;
+    ma.po = prm.part_o;
+    ma.pl = prm.part_lse;
+    ma.sinks = sinks;
+    ma.out = prm.out;
+    ma.lse_out = lse;
+    ma.seq_lens = seq_lens;
+    ma.chunk = prm.balanced ? prm.chunk_out : nullptr;
+    ma.fixed_chunk = pl.tps;
+    ma.q_len = pl.q_len;
+    ma.window = prm.window;
+    ma.max_seq_len = prm.max_seq_len;
+    e = launch_merge(pl.D, ma, hs);
     if (e != hipSuccess) return FP8PA_ERR_HIP;
   }
   return FP8PA_OK;
@@ -1003,9 +1189,17 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
   if (!aligned(partial_o, 16) || !aligned(out, 16) || !aligned(partial_lse, 4) ||
       (sinks && !aligned(sinks, 4)) || (lse && !aligned(lse, 4)))
     return FP8PA_ERR_MISALIGNED;
-  const hipError_t e = launch_merge(head_dim, num_splits, num_rows, num_q_heads, partial_o,
-                                    partial_lse, sinks, static_cast<uint16_t*>(out), lse,
-                                    static_cast<hipStream_t>(stream));
+  MergeArgs ma{};
+  ma.num_splits = num_splits;
+  ma.num_rows = num_rows;
+  ma.Hq = num_q_heads;
+  ma.po = partial_o;
+  ma.pl = partial_lse;
+  ma.sinks = sinks;
+  ma.out = static_cast<uint16_t*>(out);
+  ma.lse_out = lse;
+  ma.seq_lens = nullptr;  // every row merges all num_splits slots
+  const hipError_t e = launch_merge(head_dim, ma, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

@@ -12,9 +12,9 @@ namespace fp8pa {
 constexpr int kTileTokens = 32;      // tokens per tile: one PV MFMA k-step (16x16x32 fp8)
 constexpr int kRowsMfma = 16;        // query rows per wavefront: the MFMA N dimension
 constexpr int kRowsDot = 4;          // query rows per wavefront in the VALU dot kernel
-constexpr int kTargetWavesPerCu = 8; // wavefronts the split plan aims to put on each CU
 constexpr size_t kWorkspaceAlign = 256;
 constexpr int kMaxSplitPages = 256;   // block-table entries an MFMA wavefront holds
+constexpr int kMaxBalancedBatch = 256; // sequences a wavefront scans (4 per lane)
 
 enum Variant : int32_t { kVariantDot = 0, kVariantMfma = 1 };
 
@@ -24,15 +24,22 @@ struct Plan {
   int32_t rows;            // G * q_len query rows per kv head
   int32_t rpg;             // rows per wavefront (row group)
   int32_t row_groups;
-  int32_t hg;              // kv heads (wavefronts) per workgroup
-  int32_t units;           // B * (Hkv / hg) * row_groups
-  int32_t num_splits;
-  int32_t tps;             // tiles per split
+  int32_t hg;              // kv heads per workgroup
+  int32_t ds;              // wavefronts per kv head (head_dim split; MFMA at D = 256: 2)
+  int32_t upi;             // workgroups per (sequence, split) item: (Hkv / hg) * row_groups
+  int32_t split_mode;      // FP8PA_SPLIT_*
+  int32_t num_splits;      // partial slots per query row
+  int32_t tps;             // tiles per split (BALANCED: min_tiles, unused by the kernels)
+  int32_t tps_cap;         // largest chunk
+  int32_t target_items;    // BALANCED: items the chunk size aims at
+  int32_t items;           // (sequence, split) items the grid covers
   int32_t bt, bt_shift;
-  int32_t grid_wgs;
+  int32_t grid_wgs;        // items * upi
   int32_t direct;          // 1: the partial kernel writes the final output (one split)
   size_t ws_bytes;         // 0 when direct
   size_t off_lse;          // byte offset of partial_lse in the workspace
+  size_t off_chunk;        // byte offset of the balanced plan's chunk word
+  int32_t min_tiles;       // balanced plan: chunk floor (64 keys per query row)
 };
 
 // Validates `s` (host-known fields only) and fills `plan` for a device with

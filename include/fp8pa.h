@@ -89,13 +89,28 @@ typedef struct fp8pa_shape {
   int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
 } fp8pa_shape;
 
+/* How the keys of a sequence are divided among workgroups. */
+#define FP8PA_SPLIT_DIRECT   0 /* one split; the partial kernel writes out/lse, no merge */
+#define FP8PA_SPLIT_FIXED    1 /* every sequence: splits of tiles_per_split tiles */
+#define FP8PA_SPLIT_BALANCED 2 /* the kernel reads all seq_lens and picks one chunk size
+                                  (<= max_tiles_per_split) so that the (sequence, split)
+                                  items of the whole batch come to about target_items;
+                                  idle workgroups exit */
+
 /* The plan one call will run (see fp8pa_plan). */
 typedef struct fp8pa_plan_info {
   int32_t variant;          /* 0 = VALU dot kernel, 1 = FP8-MFMA kernel */
-  int32_t num_splits;       /* KV splits per (sequence, kv head, row group) */
-  int32_t tiles_per_split;  /* 32-token tiles per split */
+  int32_t split_mode;       /* FP8PA_SPLIT_* */
+  int32_t num_splits;       /* partial slots per query row: the most splits one
+                               sequence can get */
+  int32_t tiles_per_split;  /* 32-token tiles per split (BALANCED: the chunk floor,
+                               64 keys per query row, kept while at least half of
+                               target_items remain) */
+  int32_t max_tiles_per_split; /* the largest chunk a split may take */
+  int32_t target_items;     /* BALANCED: (sequence, split) items aimed at; else 0 */
   int32_t tile_tokens;      /* tokens per tile (32) */
-  int32_t heads_per_wg;     /* kv heads (one wavefront each) per workgroup */
+  int32_t heads_per_wg;     /* kv heads per workgroup (waves_per_head wavefronts each) */
+  int32_t waves_per_head;   /* wavefronts sharing one kv head's head_dim (1, or 2 at D = 256) */
   int32_t rows_per_group;   /* query rows (q heads x q tokens) per wavefront */
   int32_t row_groups;       /* ceil(Hq / Hkv * q_len / rows_per_group) */
   int32_t grid_wgs;         /* workgroups of the partial kernel */
@@ -105,7 +120,8 @@ typedef struct fp8pa_plan_info {
   uint64_t workspace_lse_offset; /* byte offset of the partial LSE block in the
                                     workspace; the partial outputs start at 0.
                                     Both blocks use fp8pa_merge's layout
-                                    ([B*q_len*Hq rows][num_splits](x head_dim)). */
+                                    ([B*q_len*Hq rows][num_splits](x head_dim)),
+                                    followed by one word of plan state. */
 } fp8pa_plan_info;
 
 /*

@@ -70,20 +70,37 @@ def test_plan_of_each_workload(k):
     assert p["variant"] == 1  # every named workload has >= 3 rows per kv head and bt >= 16
     assert p["rows_per_group"] == 16 and p["row_groups"] == math.ceil(rows / 16)
     assert c["Hkv"] % p["heads_per_wg"] == 0
-    units = c["B"] * (c["Hkv"] // p["heads_per_wg"]) * p["row_groups"]
-    assert p["grid_wgs"] == units * p["num_splits"]
-    # the splits cover every tile a sequence can span
+    # head_dim 256 is split over two wavefronts per kv head
+    assert p["waves_per_head"] == (2 if c["D"] == 256 else 1)
+    assert p["heads_per_wg"] * p["waves_per_head"] <= (8 if c["D"] == 64 else 4)
+    upi = (c["Hkv"] // p["heads_per_wg"]) * p["row_groups"]
+    assert p["grid_wgs"] % upi == 0
+    items = p["grid_wgs"] // upi
     max_keys = s.max_seq_len if c["window"] <= 0 else min(s.max_seq_len, c["window"] + c["q_len"] - 1)
     n_tiles = math.ceil(max_keys / 32) + (1 if c["window"] > 0 else 0)
-    assert p["num_splits"] * p["tiles_per_split"] >= n_tiles
-    assert (p["num_splits"] - 1) * p["tiles_per_split"] < n_tiles
+    if p["split_mode"] == fp.FP8PA_SPLIT_BALANCED:
+        # the kernel sizes the chunk in [tiles_per_split, max_tiles_per_split];
+        # the slots must hold the longest sequence even at the largest chunk
+        assert p["tiles_per_split"] == math.ceil(min(rows, 16) * 64 / 32)
+        assert p["num_splits"] * p["max_tiles_per_split"] >= n_tiles
+        assert p["num_splits"] == max(min(p["target_items"], n_tiles),
+                                      math.ceil(n_tiles / p["max_tiles_per_split"]))
+        # enough items for sum_b max(1, ceil(n_b / c)) at any chunk the kernel picks
+        assert items == min(c["B"] * p["num_splits"], max(p["target_items"],
+                            math.ceil(c["B"] * n_tiles / p["max_tiles_per_split"])) + c["B"])
+    else:
+        assert items == c["B"] * p["num_splits"]
+        # the splits cover every tile a sequence can span
+        assert p["num_splits"] * p["tiles_per_split"] >= n_tiles
+        assert (p["num_splits"] - 1) * p["tiles_per_split"] < n_tiles
+        assert (p["split_mode"] == fp.FP8PA_SPLIT_DIRECT) == (p["num_splits"] == 1)
     rows_total = c["B"] * c["q_len"] * c["Hq"]
     if p["num_splits"] == 1:
         assert p["merge_launched"] == 0 and p["workspace_bytes"] == 0
     else:
         po = rows_total * p["num_splits"] * c["D"] * 4
         pl = rows_total * p["num_splits"] * 4
-        want = math.ceil(po / 256) * 256 + math.ceil(pl / 256) * 256
+        want = math.ceil(po / 256) * 256 + math.ceil(pl / 256) * 256 + 256
         assert p["merge_launched"] == 1 and p["workspace_bytes"] == want
 
 
@@ -202,3 +219,65 @@ def test_debug_entry_points_check_arguments():
     assert L.fp8pa_debug_e4m3_to_f32(None, None, -1, None) == _lib.FP8PA_ERR_INVALID_ARG
     assert L.fp8pa_debug_e4m3_to_f32(None, None, 0, None) == _lib.FP8PA_OK
     assert L.fp8pa_debug_mfma_fp8(None, 0x1000, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+
+
+def _balanced_items(plan, seq_lens, q_len, window):
+    """The balanced split rule the kernels apply, written out for checking the
+    planner's bounds: returns {b: [(ts, te), ...]} and the chunk size."""
+    def span(L):
+        ulo = max(0, L - q_len - window + 1) if window > 0 else 0
+        t0 = ulo // 32
+        t1 = (L - 1) // 32 + 1 if L > ulo else t0
+        return t0, t1
+    n = [span(L)[1] - span(L)[0] for L in seq_lens]
+    T, M = sum(n), max(n)
+    tgt = plan["target_items"]
+    c = max(-(-T // tgt), min(plan["tiles_per_split"], max(1, 2 * T // tgt)), -(-M // plan["num_splits"]))
+    c = min(c, plan["max_tiles_per_split"])
+    out = {}
+    for b, L in enumerate(seq_lens):
+        t0, t1 = span(L)
+        ns = min(-(-n[b] // c), plan["num_splits"]) if n[b] > 0 else 1
+        out[b] = [(t0 + s * c, min(t0 + s * c + c, t1)) for s in range(ns)]
+    return out, c
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_balanced_plan_covers_every_tile(seed):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 257))
+    q_len = int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 3, 4, 8]))
+    D = int(rng.choice([64, 128, 256]))
+    bt = int(rng.choice([16, 32, 64]))
+    window = int(rng.choice([0, 0, 7, 1000]))
+    max_seq = int(rng.integers(q_len, 300000 if B < 8 else 20000))
+    seq = rng.integers(q_len, max_seq + 1, size=B).tolist()
+    seq[0] = max_seq
+    s = fp.make_shape(batch=B, q_len=q_len, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                      block_tokens=bt, num_blocks=1 << 16, block_table_stride=-(-max_seq // bt),
+                      max_seq_len=max_seq, window=window, sm_scale=0.1)
+    for cu in (8, 80, 256):
+        p = fp.fp8pa_plan(s, cu)
+        if p["split_mode"] != fp.FP8PA_SPLIT_BALANCED:
+            continue
+        items, c = _balanced_items(p, seq, q_len, window)
+        upi = (Hkv // p["heads_per_wg"]) * p["row_groups"]
+        # every (sequence, split) item has a workgroup slot and a partial slot
+        assert sum(len(v) for v in items.values()) <= p["grid_wgs"] // upi
+        assert max(len(v) for v in items.values()) <= p["num_splits"]
+        # the splits of a sequence tile its key span exactly, each within the
+        # block-table registers (<= 256 pages)
+        for b, L in enumerate(seq):
+            spans = items[b]
+            lo = (max(0, L - q_len - window + 1) if window > 0 else 0) // 32
+            assert spans[0][0] == lo and spans[-1][1] == max(lo, (L - 1) // 32 + 1)
+            for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+                assert a1 == b0 and a0 < a1
+            for a0, a1 in spans:
+                if p["variant"] == 1 and a1 > a0:
+                    first = max(a0 * 32, lo * 32) // bt
+                    last = (min(L, a1 * 32) - 1) // bt
+                    assert last - first + 1 <= 256

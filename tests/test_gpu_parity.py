@@ -99,6 +99,14 @@ SMALL = {
     "window_ge_seq": dict(B=2, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[40, 70], window=5000,
                           sinks=True),
     "big_negative_sinks": dict(B=2, q_len=1, Hq=8, Hkv=2, D=64, bt=32, seq_lens=[77, 130], sinks=True),
+    # batches that span several 64-sequence groups of the balanced split plan
+    # (130 and 256 sequences) and one just past it (257: fixed-size splits)
+    "batch130_mqa": dict(B=130, q_len=1, Hq=8, Hkv=1, D=128, bt=16,
+                         seq_lens=[1 + (37 * i * i + 11 * i) % 600 for i in range(130)]),
+    "batch256_d64": dict(B=256, q_len=1, Hq=4, Hkv=1, D=64, bt=16,
+                         seq_lens=[1 + (13 * i * i + 5 * i) % 300 for i in range(256)]),
+    "batch257_d64": dict(B=257, q_len=1, Hq=4, Hkv=1, D=64, bt=16,
+                         seq_lens=[1 + (13 * i * i + 5 * i) % 300 for i in range(257)]),
 }
 
 # (case, flags, num_splits)
