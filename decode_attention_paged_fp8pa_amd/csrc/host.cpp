@@ -108,9 +108,7 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   }
   const int64_t n_tiles = ceil_div(max_keys, kTileTokens) + (s->window > 0 ? 1 : 0);
   // The MFMA kernel holds a split's block-table entries in registers.
-  const int64_t tps_cap = p.variant == kVariantMfma
-                              ? ((int64_t(kMaxSplitPages) - 1) * p.bt) / kTileTokens - 1
-                              : n_tiles;
+  const int64_t tps_cap = p.variant == kVariantMfma ? kMaxSplitTiles : n_tiles;
   p.tps_cap = int32_t(tps_cap < n_tiles ? tps_cap : n_tiles);
 
   // Splits: enough (sequence, split) items that the busy wavefronts fill the

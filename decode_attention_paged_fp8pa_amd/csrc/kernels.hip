@@ -117,20 +117,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
 }
 
-// Loads BYTES (4, 8 or a multiple of 16) at byte offset `off` of buffer `r`.
-template <int BYTES>
+// Cache policy of a K/V load: non-temporal (the gfx950 `nt` bit).  Each K/V
+// byte is read once per call, so streaming it keeps the small data that is
+// reused (seq_lens, block table, queries, split partials) in the caches.
+// Only where a wavefront reads whole 128-byte lines: at head_dim 64 two kv
+// heads share a line, and an early-evicted line would be fetched twice.
+constexpr int kLoadNT = 2;
+
+// Loads BYTES (4, 8 or a multiple of 16) at byte offset `off` of buffer `r`
+// with cache policy AUX.
+template <int BYTES, int AUX>
 __device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint32_t* dst) {
   if constexpr (BYTES == 4) {
-    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
   } else if constexpr (BYTES == 8) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
     dst[0] = v.x;
     dst[1] = v.y;
   } else {
     static_assert(BYTES % 16 == 0, "load size");
 #pragma unroll
     for (int i = 0; i < BYTES / 16; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, AUX);
       dst[4 * i + 0] = v.x;
       dst[4 * i + 1] = v.y;
       dst[4 * i + 2] = v.z;
@@ -230,11 +238,13 @@ struct Work {
   bool active;  // false: the item index lies past the batch's last split
 };
 
-__device__ __forceinline__ Work work_of(const Params& p, int ds) {
+// The kv head, row group and head_dim part of this wavefront: these follow
+// from the workgroup index alone, so loads that need only them can be issued
+// before the (sequence, split) item is resolved.
+__device__ __forceinline__ Work work_head(const Params& p, int ds) {
   Work w;
-  const int wg = blockIdx.x;
-  const int item = wg / p.upi;
-  const int unit = wg - item * p.upi;
+  const int item = blockIdx.x / p.upi;
+  const int unit = blockIdx.x - item * p.upi;
   w.rg = unit % p.row_groups;
   const int gg = unit / p.row_groups;
   // the wavefront index is uniform across the wave; saying so keeps every
@@ -242,6 +252,11 @@ __device__ __forceinline__ Work work_of(const Params& p, int ds) {
   const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   w.g = gg * p.hg + wv / ds;
   w.half = wv - (wv / ds) * ds;
+  return w;
+}
+
+__device__ __forceinline__ void work_item(const Params& p, Work& w) {
+  const int item = blockIdx.x / p.upi;
   w.active = true;
 
   if (!p.balanced) {
@@ -252,7 +267,7 @@ __device__ __forceinline__ Work work_of(const Params& p, int ds) {
     w.sp = span_of(w.L, p.q_len, p.window);
     w.ts = w.sp.tile0 + w.split * p.tps;
     w.te = min(w.ts + p.tps, w.sp.tile1);
-    return w;
+    return;
   }
 
   // Balanced plan.  Every wavefront derives the same chunk c from the whole
@@ -302,7 +317,7 @@ __device__ __forceinline__ Work work_of(const Params& p, int ds) {
       w.sp = span_of(w.L, p.q_len, p.window);
       w.ts = w.sp.tile0 + w.split * c;
       w.te = min(w.ts + c, w.sp.tile1);
-      return w;
+      return;
     }
     base += tot;
   }
@@ -313,6 +328,11 @@ __device__ __forceinline__ Work work_of(const Params& p, int ds) {
   w.L = 0;
   w.sp = span_of(0, p.q_len, p.window);
   w.ts = w.te = 0;
+}
+
+__device__ __forceinline__ Work work_of(const Params& p, int ds) {
+  Work w = work_head(p, ds);
+  work_item(p, w);
   return w;
 }
 
@@ -363,6 +383,7 @@ partial_mfma_kernel(Params p) {
   constexpr int KSTEPS = DW / 32;  // QK k-steps of 32 dims
   constexpr int KW = KB / 4;       // K dwords per lane per group
   constexpr int SW = S / 4;        // V dwords per lane per token
+  constexpr int AUX = DW >= 128 ? kLoadNT : 0;  // K/V load cache policy
   // Partial scores of the two wavefronts that share a kv head (DS = 2):
   // [wavefront][tile parity][lane][2 x f32x4].
   __shared__ f32x4 xch[DS == 2 ? 4 * 2 * 64 * 2 : 1];
@@ -370,7 +391,20 @@ partial_mfma_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int qd = lane >> 4;
-  const Work w = work_of(p, DS);
+  Work w = work_head(p, DS);
+  // Loads that need only the kv head and the row go first, so that their
+  // round trips overlap the item's.
+  const float ks = p.k_scale[p.k_per_head ? w.g : 0];
+  const float vs = p.v_scale[p.v_per_head ? w.g : 0];
+  float sink2 = -INFINITY;
+  {
+    const int r = w.rg * kRowsMfma + n;
+    if (p.sinks && p.direct && r < p.rows) {
+      const int qi = r / p.G;
+      sink2 = p.sinks[w.g * p.G + (r - qi * p.G)] * kLog2e;
+    }
+  }
+  work_item(p, w);
   if (!w.active) return;  // uniform over the workgroup
   const int d0 = w.half * DW;      // first dim of this wavefront's slice
   const int L = w.L;
@@ -387,7 +421,6 @@ partial_mfma_kernel(Params p) {
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
   // value vector is zero when this split writes the final output.
-  const float sink2 = (p.sinks && p.direct && row.valid) ? p.sinks[row.h] * kLog2e : -INFINITY;
   float m = sink2;
   float lsum = (qd == 0 && sink2 > -INFINITY) ? exp2_fast(kPShift) : 0.f;
   f32x4 O[S];
@@ -400,18 +433,19 @@ partial_mfma_kernel(Params p) {
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
   const uint32_t koff = uint32_t(n * tok + KB * qd);
 
-  // Block-table entries of this split's pages, read once before the loop:
-  // lane i of tab[w] holds the entry of page pg_lo + 64 w + i.  Only pages in
-  // [pg_lo, pg_hi], which all hold attended tokens, are read (the plan keeps
-  // a split within kMaxSplitPages pages).  A tile's page number then comes
-  // from readlanes, so the loop has no table loads and no waits on them.
-  const int pg_lo = max(ulo, ts * kTileTokens) >> p.bt_shift;
-  const int pg_hi = ts < te ? (min(uhi, te * kTileTokens) - 1) >> p.bt_shift : -1;
-  int tab[kMaxSplitPages / 64];
+  // Block-table entries of the split, read once before the loop: lane k of
+  // tab[g] holds the page of 16-token group g & 1 of tile ts + 2 k + (g >> 1),
+  // i.e. of the four groups that loop step k loads (0 for a group that holds
+  // no attended token).  A split spans at most kMaxSplitTiles tiles (64
+  // steps), so the loop reads each page number with one readlane from a
+  // fixed register, and has no table loads and no waits on them.
+  int tab[4];
 #pragma unroll
-  for (int wi = 0; wi < kMaxSplitPages / 64; ++wi) {
-    const int pi = pg_lo + 64 * wi + lane;
-    tab[wi] = pi <= pg_hi ? btab[pi] : 0;
+  for (int g = 0; g < 4; ++g) {
+    const int tt = ts + 2 * lane + (g >> 1);
+    const int gk = tt * kTileTokens + 16 * (g & 1);
+    const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+    tab[g] = live ? btab[gk >> p.bt_shift] : 0;
   }
   // The query row's raw bf16 bits; converted after the first tiles' loads
   // are issued, so the two round trips overlap.
@@ -422,62 +456,55 @@ partial_mfma_kernel(Params p) {
     for (int i = 0; i < KB / 8; ++i)
       qraw[i] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
   }
-  auto page_of = [&](int pi) -> int {
-    const int rel = pi - pg_lo;
-    const int ls = rel & 63;
-    if (rel < 64) return __builtin_amdgcn_readlane(tab[0], ls);
-    if (rel < 128) return __builtin_amdgcn_readlane(tab[1], ls);
-    if (rel < 192) return __builtin_amdgcn_readlane(tab[2], ls);
-    return __builtin_amdgcn_readlane(tab[3], ls);
-  };
+  // Keys every row of this wavefront attends: [ilo, ihi).  A tile inside it
+  // needs no score masks; only the others ("edge" tiles: at most the first
+  // two and last two of a sequence) are masked.
+  int ilo, ihi;
+  {
+    const int r0 = w.rg * kRowsMfma;
+    const int r1 = min(r0 + kRowsMfma, p.rows) - 1;
+    const int qmin = r0 / p.G, qmax = r1 / p.G;
+    ihi = L - p.q_len + qmin + 1;
+    ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
+  }
 
   uint32_t voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = uint32_t((4 * qd + j) * tok + S * n);
 
-  // Loads of one 32-token tile into registers.  A tile at or past `te`, or a
-  // 16-token group holding no attended token, gets an empty descriptor: its
-  // loads return zeros and touch no memory, and no table entry is read.
+  // Loads of one 32-token tile into registers, without branches.  A tile at
+  // or past `te`, or a 16-token group holding no attended token, gets a
+  // descriptor of size 0: its loads return zeros and touch no memory.  A
+  // group that holds some attended tokens is read whole from its page; the
+  // bytes of its other tokens are cleared in the edge-tile path.
   struct TileRegs {
     uint32_t k[2][KW];
     uint32_t v[8][SW];
   };
-  auto load_tile = [&](int tt, TileRegs& r) {
+  // `odd` is (tt - ts) & 1, a constant at every call site.
+  auto load_tile = [&](int tt, TileRegs& r, int odd) {
     const int kb = tt * kTileTokens;
-    const bool inner = kb >= ulo && kb + kTileTokens <= uhi;
+    const int step = ((tt - ts) >> 1) & 63;
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       const int gk = kb + 16 * grp;
-      Rsrc rk, rv;
-      if (tt < te && gk < uhi && gk + 16 > ulo) {
-        const int page = page_of(gk >> p.bt_shift);
-        const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
-        rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + base), 0, 16 * tok, kRsrcWord3);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + base), 0, 16 * tok, kRsrcWord3);
-      } else {
-        rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase_g, 0, 0, kRsrcWord3);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase_g, 0, 0, kRsrcWord3);
-      }
-      if (inner) {
-        buf_load<KB>(rk, koff, r.k[grp]);
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      const int page = __builtin_amdgcn_readlane(tab[2 * odd + grp], step);
+      const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
+      const int nrec = live ? 16 * tok : 0;
+      const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + base), 0, nrec, kRsrcWord3);
+      const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + base), 0, nrec, kRsrcWord3);
+      buf_load<KB, AUX>(rk, koff, r.k[grp]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) buf_load<S>(rv, voff[j], r.v[4 * grp + j]);
-      } else {
-        const int kt = gk + n;
-        buf_load<KB>(rk, (kt >= ulo && kt < uhi) ? koff : kOob, r.k[grp]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int vt = gk + 4 * qd + j;
-          buf_load<S>(rv, (vt >= ulo && vt < uhi) ? voff[j] : kOob, r.v[4 * grp + j]);
-        }
-      }
+      for (int j = 0; j < 4; ++j) buf_load<S, AUX>(rv, voff[j], r.v[4 * grp + j]);
     }
   };
 
   // One tile: S^T = K Q^T, mask, online softmax with a lazy reference max,
   // P = hi + lo E4M3 parts, O^T += V^T P^T.
-  auto compute_tile = [&](int tt, const TileRegs& r) {
+  auto compute_tile = [&](int tt, TileRegs& r) {
     const int kb = tt * kTileTokens;
+    const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
@@ -515,13 +542,18 @@ partial_mfma_kernel(Params p) {
         sv[j + 4] = sb[j];
       }
     }
-    // a token this lane's row does not attend becomes -inf.  (A branch that
-    // skips the masks on interior tiles measured slower: it moves the waits
-    // on the next tile's loads.)
+    if (edge) {
+      // A token this lane's row does not attend scores -inf, and the V bytes
+      // of a token outside the sequence's attended span (read whole with its
+      // group, possibly NaN codes) become 0, since P = 0 times NaN is NaN.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-      sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) {
+        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+        sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
+        const bool in_span = key >= ulo && key < uhi;
+#pragma unroll
+        for (int e = 0; e < SW; ++e) r.v[j][e] = in_span ? r.v[j][e] : 0u;
+      }
     }
     float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -585,7 +617,8 @@ partial_mfma_kernel(Params p) {
   // measured slower on MI355X: more than ~8 KB in flight per wavefront only
   // adds queueing in the memory system.
   TileRegs ta, tb;
-  load_tile(ts, ta);
+  load_tile(ts, ta, 0);
+  load_tile(ts + 1, tb, 1);
 
   // ---- stage the query row: per-row power-of-two scale, E4M3 hi + lo parts
   {
@@ -616,7 +649,6 @@ partial_mfma_kernel(Params p) {
       se = min(max(7 - e, -120), 120);
     }
     const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-    const float ks = p.k_scale[p.k_per_head ? w.g : 0];
     cr = p.sm_scale * ks * kLog2e / qs;
     // Scores are scaled as fma(S, cr, .) with cr > 0, so a -inf mask stays
     // -inf: a negative scale's sign moves into the query, and a zero scale
@@ -647,12 +679,13 @@ partial_mfma_kernel(Params p) {
   }
 
 
+  // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {
-    load_tile(tt + 1, tb);
     compute_tile(tt, ta);
     if (tt + 1 >= te) break;
-    load_tile(tt + 2, ta);
+    load_tile(tt + 2, ta, 0);
     compute_tile(tt + 1, tb);
+    load_tile(tt + 3, tb, 1);
   }
 
   // ---- epilogue: l over the 4 lane groups, normalise, write
@@ -660,7 +693,6 @@ partial_mfma_kernel(Params p) {
   lsum += xor_shfl(lsum, 32);
   if (!row.valid) return;
   const bool empty = !(lsum > 0.f);
-  const float vs = p.v_scale[p.v_per_head ? w.g : 0];
   const float inv = empty ? 0.f : vs / lsum;
   const float lse = empty ? -INFINITY : (m + log2_fast(lsum) - kPShift) * kLn2;
   // O[e][i] is output dim S * (4 qd + i) + e of this lane's row.

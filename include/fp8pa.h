@@ -85,7 +85,7 @@ typedef struct fp8pa_shape {
   float sm_scale;             /* softmax scale applied to q.K; finite */
   int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
                                  splits at most (the MFMA kernel still splits so
-                                 that no split spans more than 256 pages) */
+                                 that no split spans more than 128 tiles) */
   int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
 } fp8pa_shape;
 
