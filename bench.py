@@ -82,6 +82,13 @@ def describe(wl):
             f"sm_scale={wl.sm_scale:.6g} k_scale={'per-kv-head' if wl.k_scale.size > 1 else 'per-tensor'}")
 
 
+def partial_kernel_name(plan, D):
+    """The partial kernel a plan launches, as rocprofv3 names it."""
+    if plan["variant"] == 1:
+        return f"partial_mfma_kernel<{D}, {plan['waves_per_head']}>"
+    return f"partial_dot_kernel<{D}>"
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("kernels.hip", "host.cpp", "plan.h"):
@@ -156,7 +163,8 @@ def measure(k, steps, warmup, log, use_graph=True):
     # timed: the same K steps captured once in a HIP graph and replayed, so
     # the GPU runs them back to back without Python launch gaps
     if not use_graph:
-        return _result(wl, k, kvb, copies, plan, eager_ms, eager_ms, wall_ms, wall_ms, False, 0.0, log), wl
+        return _result(wl, k, kvb, copies, plan, eager_ms, eager_ms, wall_ms, wall_ms, False,
+                       eager_ms, 0.0, log), wl
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(steps):
@@ -176,40 +184,45 @@ def measure(k, steps, warmup, log, use_graph=True):
     step_ms = e0.elapsed_time(e1) / steps if graph_ok else eager_ms
     del graph
 
-    # the merge kernel alone (same workspace), also from a graph
-    merge_ms = 0.0
+    # the partial kernel alone: the same K steps with the merge launch left
+    # out (FP8PA_FLAG_PARTIAL_ONLY), also captured and replayed, on the
+    # stream the kernel is launched on
+    partial_ms = step_ms
     if plan["merge_launched"]:
-        rows = wl.B * wl.q_len * wl.Hq
-        pl_ptr = ws.data_ptr() + plan["workspace_lse_offset"]
+        pshape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
+                              max_seq_len=int(wl.seq_lens.max()), flags=fp.FP8PA_FLAG_PARTIAL_ONLY)
 
-        def merge_only():
-            fp.fp8pa_merge(plan["num_splits"], rows, wl.Hq, wl.D, ws, pl_ptr, sinks, out, lse)
+        def partial_only(i):
+            kc, vc = pools[i % copies]
+            fp.fp8pa_decode(pshape, q, kc, vc, btab, sl, ks, vs, sinks, out, lse, ws, nws)
 
-        for _ in range(3):
-            merge_only()
+        for i in range(3):
+            partial_only(i)
         torch.cuda.synchronize()
-        mgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(mgraph):
-            for _ in range(steps):
-                merge_only()
-        mgraph.replay()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph):
+            for i in range(steps):
+                partial_only(i)
+        pgraph.replay()
         torch.cuda.synchronize()
         e0.record()
-        mgraph.replay()
+        pgraph.replay()
         e1.record()
         torch.cuda.synchronize()
-        merge_ms = e0.elapsed_time(e1) / steps
-        del mgraph
+        partial_ms = e0.elapsed_time(e1) / steps
+        del pgraph
         step(0)  # leave the outputs as one full step writes them
         torch.cuda.synchronize()
-    res = _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok, merge_ms, log)
+    merge_ms = max(step_ms - partial_ms, 0.0)
+    res = _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
+                  partial_ms, merge_ms, log)
     del pools, kc0, vc0
     torch.cuda.empty_cache()
     return res, wl
 
 
-def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok, merge_ms, log):
-    partial_ms = max(step_ms - merge_ms, 1e-6)
+def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
+            partial_ms, merge_ms, log):
     res = dict(
         workload=wl.name,
         describe=describe(wl),
@@ -403,7 +416,7 @@ def main():
         "unit": "GB/s",
         "frac": round(h["partial_kv_gbps"] / PEAK_GBPS, 4),
         "traffic": traffic,
-        "kernel": "partial_mfma_kernel<128>",
+        "kernel": partial_kernel_name(h["plan"], head_wl.D),
         "kernel_avg_us": round(h["partial_ms"] * 1e3, 2),
         "algorithmic_bytes_per_launch": h["kv_bytes"],
     }

@@ -15,6 +15,7 @@ import math
 from ._lib import (  # noqa: F401
     FP8PA_FLAG_FORCE_DOT,
     FP8PA_FLAG_FORCE_MFMA,
+    FP8PA_FLAG_PARTIAL_ONLY,
     FP8PA_SPLIT_BALANCED,
     FP8PA_SPLIT_DIRECT,
     FP8PA_SPLIT_FIXED,
@@ -44,6 +45,7 @@ __all__ = [
     "Fp8paError",
     "FP8PA_FLAG_FORCE_DOT",
     "FP8PA_FLAG_FORCE_MFMA",
+    "FP8PA_FLAG_PARTIAL_ONLY",
     "FP8PA_SPLIT_BALANCED",
     "FP8PA_SPLIT_DIRECT",
     "FP8PA_SPLIT_FIXED",

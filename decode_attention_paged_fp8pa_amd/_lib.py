@@ -22,6 +22,7 @@ FP8PA_ERR_HIP = 5
 
 FP8PA_FLAG_FORCE_DOT = 1
 FP8PA_FLAG_FORCE_MFMA = 2
+FP8PA_FLAG_PARTIAL_ONLY = 4
 FP8PA_SPLIT_DIRECT = 0
 FP8PA_SPLIT_FIXED = 1
 FP8PA_SPLIT_BALANCED = 2

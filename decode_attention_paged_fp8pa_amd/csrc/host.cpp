@@ -46,9 +46,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   if (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads) return FP8PA_ERR_INVALID_ARG;
   if (!std::isfinite(s->sm_scale)) return FP8PA_ERR_INVALID_ARG;
   if (s->num_splits < 0) return FP8PA_ERR_INVALID_ARG;
-  const int32_t known = FP8PA_FLAG_FORCE_DOT | FP8PA_FLAG_FORCE_MFMA;
-  if (s->flags & ~known) return FP8PA_ERR_INVALID_ARG;
-  if ((s->flags & known) == known) return FP8PA_ERR_INVALID_ARG;
+  const int32_t variants = FP8PA_FLAG_FORCE_DOT | FP8PA_FLAG_FORCE_MFMA;
+  if (s->flags & ~(variants | FP8PA_FLAG_PARTIAL_ONLY)) return FP8PA_ERR_INVALID_ARG;
+  if ((s->flags & variants) == variants) return FP8PA_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return FP8PA_ERR_UNSUPPORTED;
 
   Plan p;

@@ -948,28 +948,35 @@ struct MergeArgs {
   int q_len, window, max_seq_len;
 };
 
-// One wavefront per (query row, 64 dims of head_dim): lane l owns dim
-// 64 c + l.  Only splits with a nonzero weight are read: a ballot over the
-// weights gives their indices, taken U at a time.  The first 64 LSEs and the
-// first U splits' partial outputs are loaded before the split count and the
-// weights are known (slots fill from 0 upwards), which hides a round trip.
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int C = D / 64;  // wavefronts per row
-  constexpr int U = 16;      // partial outputs in flight together
-  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int row = wave / C;
-  const int chunk = wave - row * C;
-  if (row >= a.num_rows) return;
+// One workgroup per (query row, 64 dims of head_dim); lane l owns dim
+// 64 c + l.  Its W wavefronts take the splits in turn (wavefront w: splits
+// w, w + W, ...) and reduce them to a local (max, sum, weighted sum), which
+// LDS combines when W > 1: rows with many splits so need few dependent
+// round trips.  Each wavefront loads its first LSEs and its first 16 / W
+// partial outputs before the row's split count and the weights are known
+// (the plans fill slots from 0 upwards), which hides a round trip for rows
+// of up to 16 splits; further splits are read only where their weight is
+// nonzero (a ballot over the weights gives their indices, 16 at a time).
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
+  constexpr int C = D / 64;  // workgroups per row
+  constexpr int U = 16;      // partial outputs in flight together per wavefront
+  constexpr int U0 = 16 / W; // of which loaded before the weights are known
+  __shared__ float red_acc[W][64];
+  __shared__ float red_ml[W][2];
+  const int row = blockIdx.x / C;
+  const int chunk = blockIdx.x - row * C;
   const int lane = threadIdx.x & 63;
+  const int wv = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int S = a.num_splits;
   const float* lrow = a.pl + (size_t)row * S;
   const float* obase = a.po + (size_t)row * S * D + 64 * chunk + lane;
-  const float sink2 = a.sinks ? a.sinks[row % a.Hq] * kLog2e : -INFINITY;
-  const float l0 = lane < S ? lrow[lane] : -INFINITY;
-  float o0[U];
+  // lane i of this wavefront stands for split wv + W * (i0 + i)
+  const int sl0 = wv + W * lane;
+  const float l0 = sl0 < S ? lrow[sl0] : -INFINITY;
+  float o0[U0];
 #pragma unroll
-  for (int u = 0; u < U; ++u) o0[u] = u < S ? obase[(size_t)u * D] : 0.f;
+  for (int u = 0; u < U0; ++u) o0[u] = wv + W * u < S ? obase[(size_t)(wv + W * u) * D] : 0.f;
   int ns = S;
   if (a.seq_lens) {
     const int b = row / (a.q_len * a.Hq);
@@ -978,25 +985,27 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int c = a.chunk ? *a.chunk : a.fixed_chunk;
     ns = __builtin_amdgcn_readfirstlane(splits_of(sp.tile1 - sp.tile0, c, S));
   }
-  float M = fmaxf(sink2, lane < ns ? l0 * kLog2e : -INFINITY);
-  for (int s = 64 + lane; s < ns; s += 64) M = fmaxf(M, lrow[s] * kLog2e);
+  // this wavefront's splits: wv + W * i for i < nw
+  const int nw = ns > wv ? (ns - wv + W - 1) / W : 0;
+  float M = lane < nw ? l0 * kLog2e : -INFINITY;
+  for (int i = 64 + lane; i < nw; i += 64) M = fmaxf(M, lrow[wv + W * i] * kLog2e);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_shfl(M, m));
   const float Mu = M == -INFINITY ? 0.f : M;  // every weight is 0 then
   float acc = 0.f, lpart = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    const float ls = s0 == 0 ? l0 : (s < ns ? lrow[s] : -INFINITY);
-    const float w = s < ns ? exp2_fast(ls * kLog2e - Mu) : 0.f;
+  for (int i0 = 0; i0 < nw; i0 += 64) {
+    const int i = i0 + lane;
+    const float ls = i0 == 0 ? l0 : (i < nw ? lrow[wv + W * i] : -INFINITY);
+    const float w = i < nw ? exp2_fast(ls * kLog2e - Mu) : 0.f;
     lpart += w;
     uint64_t mask = __ballot(w > 0.f);
-    if (s0 == 0) {
+    if (i0 == 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U0; ++u) {
         const float wu = lane_value(w, u);
         acc = wu > 0.f ? fmaf(wu, o0[u], acc) : acc;
       }
-      mask &= ~((uint64_t(1) << U) - 1);
+      mask &= ~((uint64_t(1) << U0) - 1);
     }
     while (mask) {
       int idx[U];
@@ -1005,7 +1014,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       for (int u = 0; u < U; ++u) {
         idx[u] = mask ? __builtin_ctzll(mask) : -1;
         mask &= mask - 1;
-        o[u] = idx[u] >= 0 ? obase[(size_t)(s0 + idx[u]) * D] : 0.f;
+        o[u] = idx[u] >= 0 ? obase[(size_t)(wv + W * (i0 + idx[u])) * D] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -1014,12 +1023,38 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) lpart += xor_shfl(lpart, m);
-  const float Lsum = lpart + (sink2 > -INFINITY ? exp2_fast(sink2 - Mu) : 0.f);
+  if constexpr (W > 1) {
+    red_acc[wv][lane] = acc;
+    if (lane == 0) {
+      red_ml[wv][0] = M;
+      red_ml[wv][1] = lpart;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+  }
+  // combine: the sink joins once, in log2 units like the partial maxima
+  const float sink2 = a.sinks ? a.sinks[row % a.Hq] * kLog2e : -INFINITY;
+  float Mt = sink2, Lsum = 0.f, o = 0.f;
+  if constexpr (W > 1) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) Mt = fmaxf(Mt, red_ml[k][0]);
+  } else {
+    Mt = fmaxf(Mt, M);
+  }
+  const float Mtu = Mt == -INFINITY ? 0.f : Mt;
+  if (sink2 > -INFINITY) Lsum = exp2_fast(sink2 - Mtu);
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const float mk = W > 1 ? red_ml[k][0] : M;
+    const float f = mk > -INFINITY ? exp2_fast(mk - Mtu) : 0.f;
+    Lsum = fmaf(f, W > 1 ? red_ml[k][1] : lpart, Lsum);
+    o = fmaf(f, W > 1 ? red_acc[k][lane] : acc, o);
+  }
   const bool empty = !(Lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / Lsum;
-  a.out[(size_t)row * D + 64 * chunk + lane] = uint16_t(f32_to_bf16(acc * inv));
+  a.out[(size_t)row * D + 64 * chunk + lane] = uint16_t(f32_to_bf16(o * inv));
   if (a.lse_out && chunk == 0 && lane == 0)
-    a.lse_out[row] = empty ? -INFINITY : (Mu + log2_fast(Lsum)) * kLn2;
+    a.lse_out[row] = empty ? -INFINITY : (Mtu + log2_fast(Lsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1081,14 +1116,26 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(int D, const MergeArgs& a, hipStream_t st) {
+// Wavefronts per merge workgroup: one while the rows alone give each compute
+// unit a few workgroups, four (splits of a row in parallel) for few rows.
+int merge_waves(int64_t workgroups, int cu) { return workgroups >= 4 * int64_t(cu) ? 1 : 4; }
+
+template <int D>
+void launch_merge_d(const MergeArgs& a, int waves, hipStream_t st) {
+  const dim3 grid(unsigned(int64_t(a.num_rows) * (D / 64)));
+  if (waves == 1)
+    merge_kernel<D, 1><<<grid, dim3(64), 0, st>>>(a);
+  else
+    merge_kernel<D, 4><<<grid, dim3(256), 0, st>>>(a);
+}
+
+hipError_t launch_merge(int D, const MergeArgs& a, int cu, hipStream_t st) {
   if (a.num_rows == 0) return hipSuccess;
-  const int64_t waves = int64_t(a.num_rows) * (D / 64);
-  const dim3 grid(unsigned((waves + 3) / 4)), block(256);
+  const int waves = merge_waves(int64_t(a.num_rows) * (D / 64), cu);
   switch (D) {
-    case 64: merge_kernel<64><<<grid, block, 0, st>>>(a); break;
-    case 128: merge_kernel<128><<<grid, block, 0, st>>>(a); break;
-    default: merge_kernel<256><<<grid, block, 0, st>>>(a); break;
+    case 64: launch_merge_d<64>(a, waves, st); break;
+    case 128: launch_merge_d<128>(a, waves, st); break;
+    default: launch_merge_d<256>(a, waves, st); break;
   }
   return hipGetLastError();
 }
@@ -1190,7 +1237,7 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
     default: e = launch_partial<256>(pl, prm, hs); break;
   }
   if (e != hipSuccess) return FP8PA_ERR_HIP;
-  if (!pl.direct) {
+  if (!pl.direct && !(shape->flags & FP8PA_FLAG_PARTIAL_ONLY)) {
     MergeArgs ma;
     ma.num_splits = pl.num_splits;
     ma.num_rows = pl.B * pl.q_len * pl.Hq;
@@ -1206,7 +1253,7 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
     ma.q_len = pl.q_len;
     ma.window = prm.window;
     ma.max_seq_len = prm.max_seq_len;
-    e = launch_merge(pl.D, ma, hs);
+    e = launch_merge(pl.D, ma, cu, hs);
     if (e != hipSuccess) return FP8PA_ERR_HIP;
   }
   return FP8PA_OK;
@@ -1231,7 +1278,11 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
   ma.out = static_cast<uint16_t*>(out);
   ma.lse_out = lse;
   ma.seq_lens = nullptr;  // every row merges all num_splits slots
-  const hipError_t e = launch_merge(head_dim, ma, static_cast<hipStream_t>(stream));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
+  const int cu = cu_count_of(dev);
+  if (cu < 1) return FP8PA_ERR_HIP;
+  const hipError_t e = launch_merge(head_dim, ma, cu, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

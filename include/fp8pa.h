@@ -62,9 +62,12 @@ typedef enum fp8pa_status {
   FP8PA_ERR_HIP = 5                 /* the HIP runtime reported an error */
 } fp8pa_status;
 
-/* fp8pa_shape.flags bits.  Both are for testing; production calls pass 0. */
+/* fp8pa_shape.flags bits, for testing and measurement; production calls pass 0. */
 #define FP8PA_FLAG_FORCE_DOT  1 /* use the VALU dot-product kernel */
 #define FP8PA_FLAG_FORCE_MFMA 2 /* use the FP8-MFMA kernel (needs block_tokens >= 16) */
+#define FP8PA_FLAG_PARTIAL_ONLY 4 /* run the partial pass only: when the plan has a
+                                     merge, it is not launched and out / lse are
+                                     left unwritten (times the partial kernel) */
 
 /* Host-known description of one decode call. */
 typedef struct fp8pa_shape {

@@ -160,7 +160,7 @@ BAD = [
     (dict(sm_scale=float("nan")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(num_splits=-1), _lib.FP8PA_ERR_INVALID_ARG),
-    (dict(flags=4), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(flags=8), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(flags=3), _lib.FP8PA_ERR_INVALID_ARG),
 ]
 

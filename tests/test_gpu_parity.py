@@ -153,6 +153,32 @@ def test_parity_output_without_lse_pointer():
     compare(o, rl, ro, rl, label="lse=NULL")
 
 
+def test_partial_only_flag_skips_the_merge():
+    # a merge plan: the partial pass alone leaves out / lse untouched
+    wl, t, (ro, rl) = _small("gqa4_ragged")
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                         sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()),
+                         flags=fp.FP8PA_FLAG_PARTIAL_ONLY)
+    assert fp.fp8pa_plan(shape, 256)["merge_launched"] == 1
+    n = fp.fp8pa_workspace_bytes(shape)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.full(tuple(wl.q_bits.shape), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(tuple(wl.q_bits.shape[:3]), 7.0, dtype=torch.float32, device="cuda")
+    fp.fp8pa_decode(shape, t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
+                    out, lse, ws, n)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
+    # a one-split plan has no merge to skip: the flag changes nothing
+    shape1 = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                          sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()), num_splits=1,
+                          flags=fp.FP8PA_FLAG_PARTIAL_ONLY)
+    assert fp.fp8pa_plan(shape1, 256)["merge_launched"] == 0
+    fp.fp8pa_decode(shape1, t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
+                    out, lse, None, 0)
+    o, l = to_host(out, lse)
+    compare(o, l, ro, rl, label="partial-only, one split")
+
+
 def test_workspace_too_small_is_reported():
     wl, t, _ = _small("gqa4_ragged")
     shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
