@@ -85,15 +85,14 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
   const int32_t rows_eff = p.rows < p.rpg ? p.rows : p.rpg;
 
-  // A workgroup takes adjacent kv heads (one wavefront each), so the bytes of
-  // one token slot are read by one workgroup at about the same time.  The
-  // MFMA kernel's register budget sets how many wavefronts share a SIMD
-  // (4 at D = 64, 2 at D = 128, 1 at D = 256): groups of 8 at D = 64 and 4
-  // otherwise let whole groups fill a compute unit.
-  // At D = 256 the MFMA kernel splits head_dim over two wavefronts (they
-  // exchange partial scores through LDS), which halves their registers.
+  // A workgroup takes adjacent kv heads, up to 8 wavefronts: at 8 kv heads
+  // per page token slot it reads whole token slots, so each page comes from
+  // HBM in one pass (two workgroups reading halves of a page at different
+  // times cost measurably more).  At D = 256 the MFMA kernel splits head_dim
+  // over two wavefronts (they exchange partial scores through LDS), which
+  // halves their registers.
   p.ds = (p.variant == kVariantMfma && p.D == 256) ? 2 : 1;
-  const int32_t max_hg = (p.variant == kVariantMfma && p.D != 64) ? 4 / p.ds : 8;
+  const int32_t max_hg = kMaxWgWaves / p.ds;
   p.hg = 1;
   while (p.hg * 2 <= max_hg && p.Hkv % (p.hg * 2) == 0) p.hg *= 2;
   p.upi = (p.Hkv / p.hg) * p.row_groups;

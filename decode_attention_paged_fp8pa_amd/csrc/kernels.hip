@@ -373,7 +373,7 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
 //     exactly the tokens whose scores the QK accumulators give this lane.
 // ---------------------------------------------------------------------------
 template <int D, int DS>
-__global__ __launch_bounds__(D / DS == 64 ? 512 : 256)
+__global__ __launch_bounds__(64 * kMaxWgWaves)
 __attribute__((amdgpu_waves_per_eu(D / DS == 64 ? 4 : D / DS == 128 ? 2 : 1, 8))) void
 partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
@@ -385,8 +385,9 @@ partial_mfma_kernel(Params p) {
   constexpr int SW = S / 4;        // V dwords per lane per token
   constexpr int AUX = DW >= 128 ? kLoadNT : 0;  // K/V load cache policy
   // Partial scores of the two wavefronts that share a kv head (DS = 2):
-  // [wavefront][tile parity][lane][2 x f32x4].
-  __shared__ f32x4 xch[DS == 2 ? 4 * 2 * 64 * 2 : 1];
+  // [wavefront][tile parity][lane][2 x f32x4], for the at most kMaxWgWaves
+  // wavefronts of a workgroup.
+  __shared__ f32x4 xch[DS == 2 ? kMaxWgWaves * 2 * 64 * 2 : 1];
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;

@@ -13,6 +13,7 @@ constexpr int kTileTokens = 32;      // tokens per tile: one PV MFMA k-step (16x
 constexpr int kRowsMfma = 16;        // query rows per wavefront: the MFMA N dimension
 constexpr int kRowsDot = 4;          // query rows per wavefront in the VALU dot kernel
 constexpr size_t kWorkspaceAlign = 256;
+constexpr int kMaxWgWaves = 8;       // wavefronts of a partial-kernel workgroup, at most
 constexpr int kMaxSplitTiles = 128;  // tiles an MFMA split may span (64 two-tile steps, a lane each)
 constexpr int kMaxBalancedBatch = 256; // sequences a wavefront scans (4 per lane)
 

@@ -72,7 +72,7 @@ def test_plan_of_each_workload(k):
     assert c["Hkv"] % p["heads_per_wg"] == 0
     # head_dim 256 is split over two wavefronts per kv head
     assert p["waves_per_head"] == (2 if c["D"] == 256 else 1)
-    assert p["heads_per_wg"] * p["waves_per_head"] <= (8 if c["D"] == 64 else 4)
+    assert p["heads_per_wg"] * p["waves_per_head"] <= 8
     upi = (c["Hkv"] // p["heads_per_wg"]) * p["row_groups"]
     assert p["grid_wgs"] % upi == 0
     items = p["grid_wgs"] // upi
