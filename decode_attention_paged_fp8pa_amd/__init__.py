@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     Shape,
     fp8pa_debug_e4m3_to_f32,
     fp8pa_debug_mfma_fp8,
+    fp8pa_debug_wave_ops,
     fp8pa_decode,
     fp8pa_merge,
     fp8pa_plan,

@@ -99,6 +99,7 @@ _SIGS = {
     "fp8pa_version": (ctypes.c_char_p, []),
     "fp8pa_debug_e4m3_to_f32": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+    "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
 }
 
 
@@ -196,6 +197,12 @@ def fp8pa_debug_e4m3_to_f32(codes, out, n, stream=None) -> None:
     st = lib().fp8pa_debug_e4m3_to_f32(_ptr(codes), _ptr(out), int(n), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_e4m3_to_f32")
+
+
+def fp8pa_debug_wave_ops(inp, vmax, out, stream=None) -> None:
+    st = lib().fp8pa_debug_wave_ops(_ptr(inp), int(vmax), _ptr(out), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_wave_ops")
 
 
 def fp8pa_debug_mfma_fp8(a, b, c, stream=None) -> None:

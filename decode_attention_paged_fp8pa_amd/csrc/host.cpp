@@ -131,7 +131,8 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   if (s->num_splits > 0) {
     tps = ceil_div(n_tiles, s->num_splits);
   } else if (p.B <= kMaxBalancedBatch && target_items > 2 * int64_t(p.B) &&
-             n_tiles > 1) {
+             n_tiles > 1 && int64_t(p.B) * n_tiles < (int64_t(1) << 30)) {
+    // (the kernel sums the batch's tiles in 32-bit integers)
     // Every sequence's last split may be short, so up to B items more than
     // T / c: aiming at target - B keeps all items in one round.
     p.split_mode = FP8PA_SPLIT_BALANCED;

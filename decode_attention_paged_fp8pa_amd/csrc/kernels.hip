@@ -176,26 +176,55 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
+// Wavefront reductions without LDS: DPP within each row of 16 lanes (quad
+// swaps, then half-row and row mirrors), then the gfx950 permlane swaps,
+// which pair lane l with l ^ 32 and l ^ 16.  Every lane gets the result.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto s32 = __builtin_amdgcn_permlane32_swap(uint32_t(v), uint32_t(v), false, false);
+  v = op(int(s32[0]), int(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+  return op(int(s16[0]), int(s16[1]));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f(float v, Op op) {
+  const auto as_i = [](float x) { return __float_as_int(x); };
+  const auto as_f = [](int x) { return __int_as_float(x); };
+  v = op(v, as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x141, 0xF, 0xF, false)));
+  v = op(v, as_f(__builtin_amdgcn_update_dpp(0, as_i(v), 0x140, 0xF, 0xF, false)));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  return wave_reduce_i(v, [](int a, int b) { return a + b; });
 }
 
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m, 64));
-  return v;
+  return wave_reduce_i(v, [](int a, int b) { return max(a, b); });
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_scan_i(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
+// Exclusive prefix sum over the 64 lanes of v, 0 <= v <= vmax, and the
+// total: one ballot and one mbcnt per bit of vmax (no LDS).
+__device__ __forceinline__ int wave_excl_prefix_i(int v, int vmax, int& total) {
+  int pre = 0, tot = 0;
+  for (int k = 0; (vmax >> k) != 0; ++k) {
+    const uint64_t m = __ballot((v >> k) & 1);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+    pre += int(below) << k;
+    tot += __popcll(m) << k;
   }
-  return v;
+  total = tot;
+  return pre;
 }
 
 // Keys of sequence b that some query row attends: [ulo, uhi), covered by the
@@ -305,14 +334,15 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
     if (64 * j >= p.B) break;
     const int b = lane + 64 * j;
     const int ns = b < p.B ? splits_of(nj[j], c, p.num_splits) : 0;
-    const int incl = wave_scan_i(ns, lane);
-    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    int tot;
+    const int excl = wave_excl_prefix_i(ns, p.num_splits, tot);
+    tot = __builtin_amdgcn_readfirstlane(tot);
     if (item < base + tot) {
-      const uint64_t mask = __ballot(base + incl > item);
+      const uint64_t mask = __ballot(base + excl + ns > item);
       const int ln = __builtin_ctzll(mask);
       w.b = 64 * j + ln;
       w.nsplit = __builtin_amdgcn_readlane(ns, ln);
-      w.split = item - base - (__builtin_amdgcn_readlane(incl, ln) - w.nsplit);
+      w.split = item - base - __builtin_amdgcn_readlane(excl, ln);
       w.L = __builtin_amdgcn_readlane(Lj[j], ln);
       w.sp = span_of(w.L, p.q_len, p.window);
       w.ts = w.sp.tile0 + w.split * c;
@@ -990,8 +1020,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   const int nw = ns > wv ? (ns - wv + W - 1) / W : 0;
   float M = lane < nw ? l0 * kLog2e : -INFINITY;
   for (int i = 64 + lane; i < nw; i += 64) M = fmaxf(M, lrow[wv + W * i] * kLog2e);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_shfl(M, m));
+  M = wave_reduce_f(M, [](float x, float y) { return fmaxf(x, y); });
   const float Mu = M == -INFINITY ? 0.f : M;  // every weight is 0 then
   float acc = 0.f, lpart = 0.f;
   for (int i0 = 0; i0 < nw; i0 += 64) {
@@ -1022,8 +1051,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
         if (idx[u] >= 0) acc = fmaf(lane_value(w, idx[u]), o[u], acc);
     }
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) lpart += xor_shfl(lpart, m);
+  lpart = wave_reduce_f(lpart, [](float x, float y) { return x + y; });
   if constexpr (W > 1) {
     red_acc[wv][lane] = acc;
     if (lane == 0) {
@@ -1067,6 +1095,16 @@ __global__ void debug_e4m3_kernel(const uint8_t* codes, float* out, int n) {
   if (i >= n) return;
   const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(uint32_t(codes[i]), false);
   out[i] = v.x;
+}
+
+__global__ void debug_wave_ops_kernel(const int32_t* in, int vmax, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int v = in[lane];
+  int tot = 0;
+  out[lane] = wave_excl_prefix_i(v, vmax, tot);
+  out[64 + lane] = wave_sum_i(v);
+  out[128 + lane] = wave_max_i(v);
+  out[192 + lane] = tot;
 }
 
 __global__ void debug_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c) {
@@ -1292,6 +1330,12 @@ fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n
   if (n == 0) return FP8PA_OK;
   debug_e4m3_kernel<<<dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       codes, out, n);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream) {
+  if (!in || !out || vmax < 0) return FP8PA_ERR_INVALID_ARG;
+  debug_wave_ops_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(in, vmax, out);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

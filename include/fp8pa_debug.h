@@ -1,5 +1,5 @@
 /*
- * fp8pa_debug.h: two diagnostic entry points of libfp8pa.  They expose the
+ * fp8pa_debug.h: diagnostic entry points of libfp8pa.  They expose the
  * hardware behaviour the decode kernels rely on, so a test can check it
  * against the definitions directly:
  *
@@ -8,7 +8,10 @@
  *    `flashinfer.gemm.fp8_qkv_qknorm_rope` (Parameters: torch.float8_e4m3fn),
  *    not the FNUZ variant of earlier CDNA parts;
  *  - the operand and result lane layout of v_mfma_f32_16x16x32_fp8_fp8 that
- *    the decode kernels assume.
+ *    the decode kernels assume;
+ *  - the wavefront-wide integer sum, maximum and prefix sum (DPP row ops,
+ *    permlane swaps, ballot + mbcnt) with which the kernels size a batch's
+ *    KV splits on the device.
  *
  * Same conventions as fp8pa.h: device pointers owned by the caller, work
  * queued on `stream` (a hipStream_t passed as void*), a status returned.
@@ -35,6 +38,13 @@ fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n
  * result rows 4*(l/16) + i, column l%16), so c equals the exact product only
  * if that layout is the hardware's. */
 fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, void* stream);
+
+/* One wavefront of 64 lanes, lane l holding in[l] (int32 [64], each in
+ * [0, vmax], vmax >= 0): out[l] = the exclusive prefix sum in[0] + ... +
+ * in[l-1], out[64 + l] = the wavefront sum, out[128 + l] = the wavefront
+ * maximum, out[192 + l] = the total the prefix routine reports.  out: int32
+ * [256]. */
+fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -219,6 +219,8 @@ def test_debug_entry_points_check_arguments():
     assert L.fp8pa_debug_e4m3_to_f32(None, None, -1, None) == _lib.FP8PA_ERR_INVALID_ARG
     assert L.fp8pa_debug_e4m3_to_f32(None, None, 0, None) == _lib.FP8PA_OK
     assert L.fp8pa_debug_mfma_fp8(None, 0x1000, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_wave_ops(None, 5, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_wave_ops(0x1000, -1, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
 
 
 def _balanced_items(plan, seq_lens, q_len, window):

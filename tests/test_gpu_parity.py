@@ -74,6 +74,22 @@ def test_hw_mfma_fp8_accumulation_precision():
     assert np.all(np.abs(_mfma(a, b) - want) <= scale * 2.0 ** -10)
 
 
+@pytest.mark.parametrize("vmax", [0, 1, 7, 300, 65535])
+def test_hw_wave_reductions_and_prefix(vmax):
+    rng = np.random.default_rng(vmax)
+    x = rng.integers(0, vmax + 1, size=64).astype(np.int32)
+    if vmax:
+        x[rng.integers(0, 64)] = vmax
+    out = torch.empty(256, dtype=torch.int32, device="cuda")
+    fp.fp8pa_debug_wave_ops(torch.from_numpy(x).cuda(), vmax, out)
+    got = out.cpu().numpy().astype(np.int64)
+    x64 = x.astype(np.int64)
+    assert np.array_equal(got[:64], np.concatenate([[0], np.cumsum(x64)[:-1]]))
+    assert np.all(got[64:128] == x64.sum())
+    assert np.all(got[128:192] == x64.max())
+    assert np.all(got[192:] == x64.sum())
+
+
 # ------------------------------------------------------- small, every element
 
 SMALL = {
