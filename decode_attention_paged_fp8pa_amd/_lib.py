@@ -75,13 +75,13 @@ class PlanInfo(ctypes.Structure):
         ("row_groups", ctypes.c_int32),
         ("grid_wgs", ctypes.c_int32),
         ("merge_launched", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("heads_per_wave", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
         ("workspace_lse_offset", ctypes.c_uint64),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib = None

@@ -92,10 +92,15 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // over two wavefronts (they exchange partial scores through LDS), which
   // halves their registers.
   p.ds = (p.variant == kVariantMfma && p.D == 256) ? 2 : 1;
+  // At D = 64 with at most 8 query rows per kv head, the MFMA kernel runs
+  // two kv heads per wavefront (one 128-byte line per token, all 16 MFMA
+  // columns in use); hg then counts head pairs.
+  p.pr = (p.variant == kVariantMfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
+  const int32_t units = p.Hkv / p.pr;  // wavefront head units per sequence
   const int32_t max_hg = kMaxWgWaves / p.ds;
   p.hg = 1;
-  while (p.hg * 2 <= max_hg && p.Hkv % (p.hg * 2) == 0) p.hg *= 2;
-  p.upi = (p.Hkv / p.hg) * p.row_groups;
+  while (p.hg * 2 <= max_hg && units % (p.hg * 2) == 0) p.hg *= 2;
+  p.upi = (units / p.hg) * p.row_groups;
   const int64_t waves_per_item = int64_t(p.upi) * p.hg * p.ds;
 
   // Tiles a sequence can span: its attended keys, plus one when a window
@@ -118,7 +123,7 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // Wavefronts of the partial kernel one compute unit holds at once: the
   // MFMA kernel's registers allow 4 per SIMD at D = 64 and 2 otherwise
   // (head_dim 256 is split over two wavefronts); the dot kernel's 2.
-  const int64_t waves_per_cu = (p.variant == kVariantMfma && p.D == 64) ? 16 : 8;
+  const int64_t waves_per_cu = (p.variant == kVariantMfma && p.D == 64 && p.pr == 1) ? 16 : 8;
   const int64_t target_waves = int64_t(cu_count) * waves_per_cu;
   int64_t target_items = target_waves / waves_per_item;
   if (target_items < 1) target_items = 1;
@@ -218,8 +223,9 @@ fp8pa_status fp8pa_plan(const fp8pa_shape* shape, int32_t cu_count, fp8pa_plan_i
   out->max_tiles_per_split = p.tps_cap;
   out->target_items = p.target_items;
   out->tile_tokens = fp8pa::kTileTokens;
-  out->heads_per_wg = p.hg;
+  out->heads_per_wg = p.hg * p.pr;
   out->waves_per_head = p.ds;
+  out->heads_per_wave = p.pr;
   out->rows_per_group = p.rpg;
   out->row_groups = p.row_groups;
   out->grid_wgs = p.grid_wgs;

@@ -94,6 +94,7 @@ struct Params {
   int32_t bt_shift, bt_mask, table_stride, window;
   int32_t k_per_head, v_per_head, direct;
   int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
+  int32_t pr;  // kv heads per wavefront (MFMA kernel: 2 pairs heads at D = 64)
   float sm_scale;
 };
 
@@ -402,11 +403,21 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
 //     kap(qd, j) = 4 qd + j (j < 4) and 16 + 4 qd + j - 4 (j >= 4), which are
 //     exactly the tokens whose scores the QK accumulators give this lane.
 // ---------------------------------------------------------------------------
-template <int D, int DS>
+//
+// PR = 2 (head_dim 64, at most 8 query rows per kv head): a wavefront takes
+// kv heads 2 g and 2 g + 1 as one problem of head_dim D = 128.  A token's two
+// 64-byte head slices are one contiguous 128-byte line; MFMA rows 0-7 are
+// the rows of head 2 g with the query in dims 0-63 and zeros in 64-127, rows
+// 8-15 those of head 2 g + 1 the other way round, so each row's scores see
+// only its own head's keys, and of the output only its own head's dims are
+// kept.  All 16 MFMA columns do work and every load reads whole lines.
+template <int D, int DS, int PR>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
 __attribute__((amdgpu_waves_per_eu(D / DS == 64 ? 4 : D / DS == 128 ? 2 : 1, 8))) void
 partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
+  static_assert(PR == 1 || (PR == 2 && D == 128 && DS == 1), "paired heads");
+  constexpr int DH = D / PR;       // head_dim of the output rows
   constexpr int DW = D / DS;       // head_dim slice of this wavefront
   constexpr int S = DW / 16;       // V bytes per lane per token
   constexpr int KB = DW / 4;       // K bytes per lane per token
@@ -423,17 +434,17 @@ partial_mfma_kernel(Params p) {
   const int n = lane & 15;
   const int qd = lane >> 4;
   Work w = work_head(p, DS);
+  // This lane's row: kv head kvh, row r of that head's rows.
+  const int kvh = PR == 2 ? 2 * w.g + (n >> 3) : w.g;
+  const int rlane = PR == 2 ? (n & 7) : w.rg * kRowsMfma + n;
   // Loads that need only the kv head and the row go first, so that their
   // round trips overlap the item's.
-  const float ks = p.k_scale[p.k_per_head ? w.g : 0];
-  const float vs = p.v_scale[p.v_per_head ? w.g : 0];
+  const float ks = p.k_scale[p.k_per_head ? kvh : 0];
+  const float vs = p.v_scale[p.v_per_head ? kvh : 0];
   float sink2 = -INFINITY;
-  {
-    const int r = w.rg * kRowsMfma + n;
-    if (p.sinks && p.direct && r < p.rows) {
-      const int qi = r / p.G;
-      sink2 = p.sinks[w.g * p.G + (r - qi * p.G)] * kLog2e;
-    }
+  if (p.sinks && p.direct && rlane < p.rows) {
+    const int qi = rlane / p.G;
+    sink2 = p.sinks[kvh * p.G + (rlane - qi * p.G)] * kLog2e;
   }
   work_item(p, w);
   if (!w.active) return;  // uniform over the workgroup
@@ -441,7 +452,10 @@ partial_mfma_kernel(Params p) {
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
   const int ts = w.ts, te = w.te;
-  const Row row = row_of(p, w.b, w.g, w.rg * kRowsMfma + n, L);
+  const Row row = row_of(p, w.b, kvh, rlane, L);
+  // With paired heads a lane's 32 query / output dims (of the wavefront's
+  // 128) belong to one head: `mine` says whether it is this lane's row's.
+  const bool mine = PR == 1 || (qd >> 1) == (n >> 3);
 
   if (ts >= te && !p.direct && w.half == 0 && row.valid && qd == 0)
     p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
@@ -482,18 +496,18 @@ partial_mfma_kernel(Params p) {
   // are issued, so the two round trips overlap.
   u32x4 qraw[KB / 8];
   {
-    const uint16_t* qrow = p.q + row.out_row * D + d0 + KB * qd;
+    const uint16_t* qrow = p.q + row.out_row * DH + d0 + KB * (PR == 2 ? (qd & 1) : qd);
 #pragma unroll
     for (int i = 0; i < KB / 8; ++i)
-      qraw[i] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+      qraw[i] = (row.valid && mine) ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
   }
   // Keys every row of this wavefront attends: [ilo, ihi).  A tile inside it
   // needs no score masks; only the others ("edge" tiles: at most the first
   // two and last two of a sequence) are masked.
   int ilo, ihi;
   {
-    const int r0 = w.rg * kRowsMfma;
-    const int r1 = min(r0 + kRowsMfma, p.rows) - 1;
+    const int r0 = PR == 2 ? 0 : w.rg * kRowsMfma;
+    const int r1 = PR == 2 ? p.rows - 1 : min(r0 + kRowsMfma, p.rows) - 1;
     const int qmin = r0 / p.G, qmax = r1 / p.G;
     ihi = L - p.q_len + qmin + 1;
     ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
@@ -726,15 +740,18 @@ partial_mfma_kernel(Params p) {
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : vs / lsum;
   const float lse = empty ? -INFINITY : (m + log2_fast(lsum) - kPShift) * kLn2;
-  // O[e][i] is output dim S * (4 qd + i) + e of this lane's row.
+  // O[e][i] is output dim S * (4 qd + i) + e of this lane's row (with paired
+  // heads: of the wavefront's 128, the row's own 64 start at 64 * (n >> 3)).
+  const int dlane = PR == 2 ? S * 4 * (qd & 1) : S * 4 * qd;
   if (p.direct) {
-    uint16_t* orow = p.out + row.out_row * D + d0;
+    uint16_t* orow = p.out + row.out_row * DH + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t pk[S / 2];
 #pragma unroll
       for (int e = 0; e < S; e += 2) pk[e / 2] = pack_bf16x2(O[e][i] * inv, O[e + 1][i] * inv);
-      uint16_t* dst = orow + S * (4 * qd + i);
+      uint16_t* dst = orow + dlane + S * i;
+      if (!mine) continue;
       if constexpr (S == 4) {
         *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
       } else {
@@ -746,11 +763,11 @@ partial_mfma_kernel(Params p) {
     if (p.lse && qd == 0 && w.half == 0) p.lse[row.out_row] = lse;
   } else {
     const size_t slot = row.out_row * p.num_splits + w.split;
-    if (!empty) {
-      float* prow = p.part_o + slot * D + d0;
+    if (!empty && mine) {
+      float* prow = p.part_o + slot * DH + d0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float* dst = prow + S * (4 * qd + i);
+        float* dst = prow + dlane + S * i;
 #pragma unroll
         for (int v = 0; v < S / 4; ++v)
           reinterpret_cast<f32x4*>(dst)[v] =
@@ -1149,7 +1166,10 @@ template <int D>
 hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
   if (pl.variant == kVariantMfma)
-    partial_mfma_kernel<D, (D == 256 ? 2 : 1)><<<grid, block, 0, st>>>(prm);
+    if (D == 64 && pl.pr == 2)
+      partial_mfma_kernel<128, 1, 2><<<grid, block, 0, st>>>(prm);
+    else
+      partial_mfma_kernel<D, (D == 256 ? 2 : 1), 1><<<grid, block, 0, st>>>(prm);
   else
     partial_dot_kernel<D><<<grid, block, 0, st>>>(prm);
   return hipGetLastError();
@@ -1266,6 +1286,7 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.v_per_head = shape->v_scale_count > 1 ? 1 : 0;
   prm.direct = pl.direct;
   prm.ds = pl.ds;
+  prm.pr = pl.pr;
   prm.sm_scale = shape->sm_scale;
 
   const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -112,13 +112,16 @@ typedef struct fp8pa_plan_info {
   int32_t max_tiles_per_split; /* the largest chunk a split may take */
   int32_t target_items;     /* BALANCED: (sequence, split) items aimed at; else 0 */
   int32_t tile_tokens;      /* tokens per tile (32) */
-  int32_t heads_per_wg;     /* kv heads per workgroup (waves_per_head wavefronts each) */
+  int32_t heads_per_wg;     /* kv heads per workgroup */
   int32_t waves_per_head;   /* wavefronts sharing one kv head's head_dim (1, or 2 at D = 256) */
   int32_t rows_per_group;   /* query rows (q heads x q tokens) per wavefront */
   int32_t row_groups;       /* ceil(Hq / Hkv * q_len / rows_per_group) */
   int32_t grid_wgs;         /* workgroups of the partial kernel */
   int32_t merge_launched;   /* 1 when num_splits > 1 and a merge kernel follows */
-  int32_t reserved;         /* 0 */
+  int32_t heads_per_wave;   /* kv heads one wavefront takes (2 at head_dim 64 with
+                               at most 8 query rows per kv head, else 1); a
+                               workgroup has heads_per_wg / heads_per_wave *
+                               waves_per_head wavefronts */
   uint64_t workspace_bytes; /* bytes fp8pa_decode needs in `workspace` */
   uint64_t workspace_lse_offset; /* byte offset of the partial LSE block in the
                                     workspace; the partial outputs start at 0.

@@ -72,7 +72,9 @@ def test_plan_of_each_workload(k):
     assert c["Hkv"] % p["heads_per_wg"] == 0
     # head_dim 256 is split over two wavefronts per kv head
     assert p["waves_per_head"] == (2 if c["D"] == 256 else 1)
-    assert p["heads_per_wg"] * p["waves_per_head"] <= 8
+    # head_dim 64 with <= 8 rows per kv head pairs two kv heads per wavefront
+    assert p["heads_per_wave"] == (2 if c["D"] == 64 and rows <= 8 and c["Hkv"] % 2 == 0 else 1)
+    assert p["heads_per_wg"] // p["heads_per_wave"] * p["waves_per_head"] <= 8
     upi = (c["Hkv"] // p["heads_per_wg"]) * p["row_groups"]
     assert p["grid_wgs"] % upi == 0
     items = p["grid_wgs"] // upi

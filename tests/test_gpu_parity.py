@@ -115,6 +115,9 @@ SMALL = {
     "window_ge_seq": dict(B=2, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[40, 70], window=5000,
                           sinks=True),
     "big_negative_sinks": dict(B=2, q_len=1, Hq=8, Hkv=2, D=64, bt=32, seq_lens=[77, 130], sinks=True),
+    # head_dim 64 with 8 rows per kv head: two kv heads per wavefront
+    "pair_q2_perhead": dict(B=3, q_len=2, Hq=16, Hkv=4, D=64, bt=16, seq_lens=[50, 300, 130],
+                            window=77, sinks=True, scale=("per_head", 0.02, 0.1)),
     # batches that span several 64-sequence groups of the balanced split plan
     # (130 and 256 sequences) and one just past it (257: fixed-size splits)
     "batch130_mqa": dict(B=130, q_len=1, Hq=8, Hkv=1, D=128, bt=16,
