@@ -17,7 +17,11 @@ reads of the same bytes at least 1 GiB of other KV has streamed through the
 (after W eager warmup steps and an eager timing pass) and replayed back to
 back on torch's current stream, bracketed by torch.cuda.synchronize() and
 HIP events; the replayed output is checked bit for bit against the eager
-one.  The merge kernel alone is timed the same way.
+one.  The graph is replayed REPLAYS times: the step time is the median of
+the per-replay averages, reported with p10 / p90.  The partial kernel alone
+is timed from a second graph of the same steps run with
+FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
+timed as the practical HBM ceiling ("copy_ceiling").
 
 HBM traffic (roofline.traffic): four rocprofv3 --pmc passes, FETCH_SIZE and
 WRITE_SIZE over this workload and over `--calibrate-copy` (device copies of
@@ -27,8 +31,8 @@ kernel sources have changed since the counters were taken.
 
 Prints ONE JSON line (rank 0, N=1):
   value = attended KV bytes read per step / step time, in GB/s;
-  roofline = the partial kernel's KV bytes / its average duration (the step's
-    event time minus a live measurement of the merge alone), against 8 TB/s;
+  roofline = the partial kernel's KV bytes / its average duration (the
+    partial-only graph above), against 8 TB/s;
   cpu_baseline = the float64 CPU oracle on a time-bounded sample of the
     headline workload, in the same unit.
 """
@@ -52,6 +56,8 @@ METRIC = "KV-read HBM GB/s (% of MI355X peak) and decode tokens/s, FP8 paged att
 PEAK_GBPS = 8000.0
 HEADLINE = 2
 MALL_FLUSH_BYTES = 1 << 30
+REPLAYS = 5                # timed replays of the captured K steps
+COPY_BYTES = 1 << 30       # device-copy ceiling measurement
 
 
 def kv_bytes(wl):
@@ -176,13 +182,23 @@ def measure(k, steps, warmup, log, use_graph=True):
     if not graph_ok:
         log(f"[bench] cfg{k}: graph replay output differs from eager; reporting eager timing")
     torch.cuda.synchronize()
+    # REPLAYS timed replays of the K steps: the step time is their median,
+    # reported with the spread over replays
+    per_replay = []
     t0 = time.perf_counter()
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    step_ms = e0.elapsed_time(e1) / steps if graph_ok else eager_ms
+    for _ in range(REPLAYS):
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_replay.append(e0.elapsed_time(e1) / steps)
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / (steps * REPLAYS)
+    per_replay.sort()
+    step_ms = per_replay[len(per_replay) // 2] if graph_ok else eager_ms
+    spread = {"p10_us": round(float(np.percentile(per_replay, 10)) * 1e3, 2),
+              "median_us": round(step_ms * 1e3, 2),
+              "p90_us": round(float(np.percentile(per_replay, 90)) * 1e3, 2),
+              "replays": REPLAYS}
     del graph
 
     # the partial kernel alone: the same K steps with the merge launch left
@@ -217,6 +233,7 @@ def measure(k, steps, warmup, log, use_graph=True):
     merge_ms = max(step_ms - partial_ms, 0.0)
     res = _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
                   partial_ms, merge_ms, log)
+    res["spread"] = spread
     del pools, kc0, vc0
     torch.cuda.empty_cache()
     return res, wl
@@ -247,6 +264,36 @@ def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms,
         f"{merge_ms * 1e3:.1f} us), KV {res['kv_gbps']:.0f} GB/s = {res['pct_peak']:.1f}% of peak, "
         f"{res['tokens_per_s']:.3g} tok/s, splits {plan['num_splits']}, copies {copies}")
     return res
+
+
+def copy_ceiling(log):
+    """A plain 1 GiB device-to-device copy: (read + write bytes) / time, the
+    practical HBM ceiling the decode kernels are compared with."""
+    import torch
+
+    n = COPY_BYTES
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(5):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    gbps = 2 * n / t / 1e9
+    log(f"[bench] device copy of {n >> 20} MiB: {t * 1e6:.1f} us, {gbps:.0f} GB/s read+write "
+        f"({gbps / PEAK_GBPS * 100:.1f}% of {PEAK_GBPS:.0f} GB/s)")
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read_plus_written": 2 * n, "median_us": round(t * 1e6, 1), "gbps": round(gbps, 1),
+            "pct_of_peak": round(gbps / PEAK_GBPS * 100, 2)}
 
 
 def cpu_baseline(wl, budget_s, log):
@@ -401,6 +448,7 @@ def main():
         cfgs.insert(0, HEADLINE)
     results = {}
     head_wl = None
+    ceiling = copy_ceiling(log)
     for k in cfgs:
         res, wl = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph)
         results[k] = res
@@ -442,6 +490,7 @@ def main():
                    "tokens_per_s": round(h["tokens_per_s"], 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "copy_ceiling": ceiling,
         "per_workload": {
             f"cfg{k}": {
                 "workload": r["describe"], "step_us": round(r["step_ms"] * 1e3, 2),
@@ -453,6 +502,7 @@ def main():
                 "variant": "mfma" if r["plan"]["variant"] == 1 else "dot",
                 "eager_us_per_step": round(r["eager_ms"] * 1e3, 2),
                 "timing": "hip graph replay" if r["graph_ok"] else "eager",
+                "step_spread": r.get("spread"),
             } for k, r in results.items()},
     }
     print(json.dumps(line), flush=True)

@@ -333,3 +333,41 @@ def test_graph_capture_replay_cfg5():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {it} differs"
+
+
+# ------------------------------------------- sharded KV (context parallel)
+
+def test_context_parallel_shards_merge():
+    # The way the path shards a long sequence over devices, on one GPU: each
+    # shard holds a page range of every sequence and runs fp8pa_decode over
+    # it with no sink; fp8pa_merge then combines the shards' (out, lse) pairs
+    # and adds the sink once.  q_len 1 and no window, so a shard's query
+    # attends all its keys.
+    wl = make_workload(seed=77, B=2, q_len=1, Hq=24, Hkv=4, D=256, bt=64, seq_lens=[3000, 1300],
+                       scale=("per_head", 0.02, 0.1), sinks=True, sm_scale=0.08)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    t = upload(wl)
+    split_pages = 12  # shard 0: tokens [0, 768) of each sequence; shard 1: the rest
+    cut = split_pages * wl.bt
+    assert all(L > cut for L in wl.seq_lens)
+    rows = wl.B * wl.q_len * wl.Hq
+    po = torch.empty((rows, 2, wl.D), dtype=torch.float32, device="cuda")
+    pl = torch.empty((rows, 2), dtype=torch.float32, device="cuda")
+    tables = [t["bt"][:, :split_pages].contiguous(), t["bt"][:, split_pages:].contiguous()]
+    lens = [torch.full_like(t["sl"], cut), t["sl"] - cut]
+    for s in range(2):
+        shape = fp.shape_for(t["q"], t["k"], tables[s], t["ks"], t["vs"], window=0, sm_scale=wl.sm_scale,
+                             max_seq_len=int(lens[s].max()))
+        n = fp.fp8pa_workspace_bytes(shape)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(tuple(wl.q_bits.shape[:3]), dtype=torch.float32, device="cuda")
+        fp.fp8pa_decode(shape, t["q"], t["k"], t["v"], tables[s], lens[s], t["ks"], t["vs"], None,
+                        out, lse, ws if n else None, n)
+        po[:, s, :] = out.reshape(rows, wl.D).float()
+        pl[:, s] = lse.reshape(rows)
+    out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(tuple(wl.q_bits.shape[:3]), dtype=torch.float32, device="cuda")
+    fp.fp8pa_merge(2, rows, wl.Hq, wl.D, po, pl, t["sinks"], out, lse)
+    o, l = to_host(out, lse)
+    compare(o, l, ro, rl, label="two KV shards + merge")
