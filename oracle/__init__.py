@@ -1,4 +1,5 @@
-"""Float64 CPU oracle for paged flash-decode attention over an E4M3 KV cache.
+"""Float64 CPU oracle for paged flash-decode attention over an E4M3 KV cache,
+and for the writer that fills that cache from bf16 keys and values.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
 links this package; only the tests, the smoke check and the CPU-baseline leg
@@ -19,4 +20,9 @@ from .fp8pa_ref import (  # noqa: F401
     attended_range,
     decode,
     merge,
+)
+from .fp8pa_write_ref import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_encode,
+    cache_write,
 )

@@ -1,0 +1,99 @@
+"""Pins of the KV-cache writer oracle (oracle/fp8pa_write_ref.py), no GPU.
+
+The E4M3 encoder is checked against the decode table (every code round
+trips), against the definition of ties-to-even at every midpoint between
+neighbouring values, at the saturation and subnormal edges, and against
+torch's float8_e4m3fn cast; the cache writer against hand-placed slots and
+the decode of what it wrote.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+
+T = oracle.E4M3_TABLE
+FINITE = [c for c in range(256) if not np.isnan(T[c])]
+
+
+def test_every_code_round_trips():
+    got = oracle.e4m3_encode(T[FINITE])
+    assert got.tolist() == FINITE  # includes 0x80 for -0.0
+
+
+def test_midpoints_round_to_the_even_code():
+    pos = sorted((T[c], c) for c in range(0x00, 0x7F))  # +0 .. 448
+    for (a, ca), (b, cb) in zip(pos, pos[1:]):
+        mid = (a + b) / 2
+        even = ca if ca % 2 == 0 else cb
+        assert oracle.e4m3_encode(mid) == even, (a, b)
+        assert oracle.e4m3_encode(-mid) == even | 0x80
+        assert oracle.e4m3_encode(np.nextafter(mid, a)) == ca
+        assert oracle.e4m3_encode(np.nextafter(mid, b)) == cb
+
+
+def test_saturation_and_special_values():
+    assert oracle.e4m3_encode(448.0) == 0x7E
+    for x in (449.0, 463.99, 464.0, 480.0, 1e30, np.inf):
+        assert oracle.e4m3_encode(x) == 0x7E
+        assert oracle.e4m3_encode(-x) == 0xFE
+    assert oracle.e4m3_encode(0.0) == 0x00 and oracle.e4m3_encode(-0.0) == 0x80
+    assert np.isnan(T[oracle.e4m3_encode(np.nan)])
+    # the subnormal grid is 2^-9; half of it rounds to the even neighbour 0
+    assert oracle.e4m3_encode(2.0 ** -9) == 0x01
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00
+    assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02
+    assert oracle.e4m3_encode(-2.0 ** -11) == 0x80
+    assert oracle.e4m3_encode(2.0 ** -6) == 0x08  # smallest normal
+    assert oracle.e4m3_encode(7.5 * 2.0 ** -9) == 0x08  # 7.5 -> 8 (even)
+
+
+def test_encoder_matches_torch_cast_in_range():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-12, 9, size=20000))).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x.astype(np.float64)), want)
+
+
+def _bf16_bits(x):
+    b = np.asarray(x, np.float32).view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_cache_write_places_and_skips():
+    nb, bt, hkv, d = 3, 4, 2, 8
+    k0 = np.full((nb, bt, hkv, d), 0x11, np.uint8)
+    v0 = np.full((nb, bt, hkv, d), 0x22, np.uint8)
+    key = np.arange(3 * hkv * d, dtype=np.float32).reshape(3, hkv, d) / 16
+    val = -key
+    slots = np.array([5, -1, 11])  # page 1 offset 1, skipped, page 2 offset 3
+    ks = np.array([0.5, 2.0], np.float32)
+    vs = np.array([1.0], np.float32)
+    k1, v1 = oracle.cache_write(_bf16_bits(key), _bf16_bits(val), slots, ks, vs, k0, v0)
+    touched = np.zeros((nb, bt), bool)
+    touched[1, 1] = touched[2, 3] = True
+    assert np.all(k1[~touched] == 0x11) and np.all(v1[~touched] == 0x22)
+    for t, (pg, off) in ((0, (1, 1)), (2, (2, 3))):
+        for h in range(hkv):
+            assert np.array_equal(k1[pg, off, h], oracle.e4m3_encode(key[t, h] / ks[h]))
+            assert np.array_equal(v1[pg, off, h], oracle.e4m3_encode(val[t, h] / vs[0]))
+    # a slot past the cache is skipped too
+    k2, _ = oracle.cache_write(_bf16_bits(key[:1]), _bf16_bits(val[:1]), [nb * bt], ks, vs, k0, v0)
+    assert np.array_equal(k2, k0)
+
+
+def test_cache_write_then_decode_is_close():
+    rng = np.random.default_rng(5)
+    nb, bt, hkv, d = 6, 16, 2, 64
+    key = rng.standard_normal((40, hkv, d)).astype(np.float32)
+    ks = np.array([0.03, 0.07], np.float32)
+    slots = rng.permutation(nb * bt)[:40]
+    zeros = np.zeros((nb, bt, hkv, d), np.uint8)
+    k1, _ = oracle.cache_write(_bf16_bits(key), _bf16_bits(key), slots, ks, ks, zeros, zeros)
+    xb = (_bf16_bits(key).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for t, s in enumerate(slots):
+        back = T[k1[s // bt, s % bt]] * ks[:, None]
+        # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 for normal values
+        assert np.all(np.abs(back - xb[t]) <= 2.0 ** -4 * np.abs(xb[t]) + 2.0 ** -10 * ks[:, None])
