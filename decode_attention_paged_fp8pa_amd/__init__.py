@@ -3,8 +3,9 @@
 The work is done by libfp8pa.so (hand-written gfx950 HIP kernels behind a
 C ABI, include/fp8pa.h).  This package is a thin binding: `_lib` mirrors the
 C entry points one to one (fp8pa_decode, fp8pa_workspace_bytes,
-fp8pa_merge, fp8pa_plan), and `decode` below fills the shape descriptor
-from torch tensors and allocates the outputs.  PyTorch provides device
+fp8pa_merge, fp8pa_plan, fp8pa_cache_write), `decode` below fills the shape
+descriptor from torch tensors and allocates the outputs, and `cache_write`
+does the same for the KV-cache writer.  PyTorch provides device
 memory and streams only.
 """
 
@@ -23,6 +24,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PlanInfo,
     Shape,
+    WriteShape,
+    fp8pa_cache_write,
     fp8pa_debug_e4m3_to_f32,
     fp8pa_debug_mfma_fp8,
     fp8pa_debug_wave_ops,
@@ -37,6 +40,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
+    "cache_write",
+    "fp8pa_cache_write",
     "decode",
     "shape_for",
     "fp8pa_decode",
@@ -111,3 +116,33 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
     fp8pa_decode(shape, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks, out,
                  lse, workspace if nbytes > 0 else None, ws_bytes if nbytes > 0 else 0, stream)
     return out, lse
+
+
+def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *, stream=None):
+    """Runs fp8pa_cache_write on torch device tensors (in place on the caches).
+
+    key, value bf16 [T, Hkv, D] with unit stride inside a token row;
+    slot_mapping int64 [T] (negative: skip); k_scale, v_scale float32 [1] or
+    [Hkv]; k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D],
+    contiguous.
+    """
+    import torch
+
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name} must be bfloat16 [T, Hkv, D] with contiguous token rows")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous E4M3 pool (uint8 or float8_e4m3fn)")
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int64")
+    T, Hkv, D = key.shape
+    if tuple(value.shape) != (T, Hkv, D) or slot_mapping.numel() != T:
+        raise ValueError("key, value and slot_mapping disagree on the token count or shape")
+    nb, bt, Hkv_c, D_c = k_cache.shape
+    if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match key / value")
+    shape = WriteShape(T, key.stride(0), value.stride(0), Hkv, D, bt, nb, k_scale.numel(),
+                       v_scale.numel())
+    fp8pa_cache_write(shape, key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, stream)
+    return k_cache, v_cache

@@ -58,6 +58,22 @@ class Shape(ctypes.Structure):
     ]
 
 
+class WriteShape(ctypes.Structure):
+    """Mirror of fp8pa_write_shape (include/fp8pa.h)."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("key_stride", ctypes.c_int64),
+        ("value_stride", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("k_scale_count", ctypes.c_int32),
+        ("v_scale_count", ctypes.c_int32),
+    ]
+
+
 class PlanInfo(ctypes.Structure):
     """Mirror of fp8pa_plan_info (include/fp8pa.h)."""
 
@@ -97,6 +113,8 @@ _SIGS = {
                                    _VP, _VP, _VP, _VP, _VP, _VP]),
     "fp8pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8pa_version": (ctypes.c_char_p, []),
+    "fp8pa_cache_write": (ctypes.c_int, [ctypes.POINTER(WriteShape), _VP, _VP, _VP, _VP, _VP, _VP,
+                                         _VP, _VP]),
     "fp8pa_debug_e4m3_to_f32": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
@@ -191,6 +209,15 @@ def fp8pa_merge(num_splits, num_rows, num_q_heads, head_dim, partial_o, partial_
                            _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_merge")
+
+
+def fp8pa_cache_write(shape: WriteShape, key, value, slot_mapping, k_scale, v_scale, k_cache,
+                      v_cache, stream=None) -> None:
+    st = lib().fp8pa_cache_write(ctypes.byref(shape), _ptr(key), _ptr(value), _ptr(slot_mapping),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache),
+                                 _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_cache_write")
 
 
 def fp8pa_debug_e4m3_to_f32(codes, out, n, stream=None) -> None:

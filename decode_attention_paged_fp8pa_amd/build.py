@@ -2,9 +2,9 @@
 
     python -m decode_attention_paged_fp8pa_amd.build      (or build() from Python)
 
-The host TU (validation and planning) and the HIP TU (kernels and entry
-points) are compiled separately and linked into one shared library next to
-this file.
+The host TU (validation and planning) and the HIP TUs (decode kernels and
+entry points; the KV-cache writer) are compiled separately and linked into
+one shared library next to this file.
 """
 
 from __future__ import annotations
@@ -49,9 +49,12 @@ def build(verbose: bool = False) -> str:
     _run([hipcc, *common, "-c", os.path.join(CSRC, "host.cpp"), "-o", host_o])
     _run([hipcc, *common, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-x", "hip", "-c",
           os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
+    write_o = os.path.join(bdir, "cache_write.o")
+    _run([hipcc, *common, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-x", "hip", "-c",
+          os.path.join(CSRC, "cache_write.hip"), "-o", write_o])
     out = os.path.join(HERE, LIB_NAME)
     tmp = out + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, kern_o, "-o", tmp])
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, kern_o, write_o, "-o", tmp])
     os.replace(tmp, out)
     if verbose:
         print("built", out)

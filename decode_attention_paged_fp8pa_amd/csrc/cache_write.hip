@@ -1,0 +1,148 @@
+// KV-cache writer: bf16 keys / values of new tokens -> E4M3 pages.
+//
+// The cache writer of the gist "Qwen3.8-27B ... 451K tokens of KV on a single
+// RTX 5090" (kernel reshape_and_cache_nvfp4_kernel) takes a token's slot from
+// slot_mapping (a negative slot is skipped), splits it into page and place in
+// the page, and multiplies each element by the fp32 reciprocal of its scale
+// before encoding; here the encoding is OCP E4M3 ("e4m3fn", the type the
+// FlashInfer page `flashinfer.gemm.fp8_qkv_qknorm_rope` names), the format
+// the decode kernels read.
+//
+// One thread converts 8 consecutive elements of one token row: a 16-byte
+// bf16 load, four gfx950 v_cvt_pk_fp8_f32 conversions (round to nearest
+// even), one 8-byte store.  Consecutive threads take consecutive chunks of a
+// row, so both the reads and the writes of a token are contiguous.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fp8pa.h"
+
+namespace fp8pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.f;
+
+struct WriteParams {
+  const uint16_t* src[2];   // key, value
+  int64_t stride[2];        // elements between token rows
+  const float* scale[2];
+  int32_t per_head[2];      // 1: one scale per kv head
+  uint8_t* cache[2];
+  const int64_t* slots;
+  int64_t num_tokens;
+  int64_t chunks;           // num_tokens * chunks_per_token
+  int64_t num_slots;        // num_blocks * bt
+  int64_t page_bytes;       // bt * Hkv * D
+  int32_t chunks_per_token; // Hkv * D / 8
+  int32_t chunks_per_head;  // D / 8
+  int32_t token_bytes;      // Hkv * D
+  int32_t bt_shift, bt_mask;
+};
+
+// x * inv in fp32, kept NaN but saturated to +-448 (the encoding has no
+// infinity; fminf / fmaxf would turn a NaN into a bound).
+__device__ __forceinline__ float scaled(uint32_t bf16_bits, float inv) {
+  const float v = __uint_as_float(bf16_bits << 16) * inv;
+  return fabsf(v) > kE4M3Max ? copysignf(kE4M3Max, v) : v;
+}
+
+// Eight bf16 values (four dwords) -> eight E4M3 codes (two dwords).
+__device__ __forceinline__ u32x2 encode8(u32x4 x, float inv) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x.x & 0xffffu, inv), scaled(x.x >> 16, inv), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x.y & 0xffffu, inv), scaled(x.y >> 16, inv), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x.z & 0xffffu, inv), scaled(x.z >> 16, inv), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(x.w & 0xffffu, inv), scaled(x.w >> 16, inv), hi, true);
+  return u32x2{lo, hi};
+}
+
+// blockIdx.y: 0 keys, 1 values.  Grid-stride over (token, 8-element chunk).
+__global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
+  const int kv = blockIdx.y;
+  const uint16_t* src = p.src[kv];
+  uint8_t* cache = p.cache[kv];
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < p.chunks;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = i / p.chunks_per_token;
+    const int c = int(i - t * p.chunks_per_token);
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const int h = c / p.chunks_per_head;
+    const float inv = 1.f / p.scale[kv][p.per_head[kv] ? h : 0];
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 8 * int64_t(c));
+    uint8_t* dst = cache + (slot >> p.bt_shift) * p.page_bytes +
+                   int64_t(slot & p.bt_mask) * p.token_bytes + 8 * c;
+    *reinterpret_cast<u32x2*>(dst) = encode8(x, inv);
+  }
+}
+
+bool aligned_to(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return (1 << s) == v ? s : -1;
+}
+
+}  // namespace
+}  // namespace fp8pa
+
+using namespace fp8pa;
+
+extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void* key,
+                                          const void* value, const int64_t* slot_mapping,
+                                          const float* k_scale, const float* v_scale,
+                                          void* k_cache, void* v_cache, void* stream) {
+  if (!s) return FP8PA_ERR_INVALID_ARG;
+  if (s->num_tokens < 0 || s->num_kv_heads < 1 || s->num_blocks < 1) return FP8PA_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return FP8PA_ERR_UNSUPPORTED;
+  const int bt_shift = log2_exact(s->block_tokens);
+  if (s->block_tokens < 1 || s->block_tokens > 1024 || bt_shift < 0) return FP8PA_ERR_INVALID_ARG;
+  const int64_t row = int64_t(s->num_kv_heads) * s->head_dim;
+  if (s->key_stride < row || s->value_stride < row) return FP8PA_ERR_INVALID_ARG;
+  if (s->key_stride % 8 != 0 || s->value_stride % 8 != 0) return FP8PA_ERR_MISALIGNED;
+  if ((s->k_scale_count != 1 && s->k_scale_count != s->num_kv_heads) ||
+      (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads))
+    return FP8PA_ERR_INVALID_ARG;
+  if (s->num_tokens == 0) return FP8PA_OK;
+  if (!key || !value || !slot_mapping || !k_scale || !v_scale || !k_cache || !v_cache)
+    return FP8PA_ERR_INVALID_ARG;
+  if (!aligned_to(key, 16) || !aligned_to(value, 16) || !aligned_to(k_cache, 8) ||
+      !aligned_to(v_cache, 8) || !aligned_to(slot_mapping, 8) || !aligned_to(k_scale, 4) ||
+      !aligned_to(v_scale, 4))
+    return FP8PA_ERR_MISALIGNED;
+  const int64_t cpt = row / 8;
+  if (s->num_tokens > (int64_t(1) << 40) / cpt) return FP8PA_ERR_UNSUPPORTED;
+
+  WriteParams p;
+  p.src[0] = static_cast<const uint16_t*>(key);
+  p.src[1] = static_cast<const uint16_t*>(value);
+  p.stride[0] = s->key_stride;
+  p.stride[1] = s->value_stride;
+  p.scale[0] = k_scale;
+  p.scale[1] = v_scale;
+  p.per_head[0] = s->k_scale_count > 1 ? 1 : 0;
+  p.per_head[1] = s->v_scale_count > 1 ? 1 : 0;
+  p.cache[0] = static_cast<uint8_t*>(k_cache);
+  p.cache[1] = static_cast<uint8_t*>(v_cache);
+  p.slots = slot_mapping;
+  p.num_tokens = s->num_tokens;
+  p.chunks = s->num_tokens * cpt;
+  p.num_slots = int64_t(s->num_blocks) * s->block_tokens;
+  p.page_bytes = int64_t(s->block_tokens) * row;
+  p.chunks_per_token = int32_t(cpt);
+  p.chunks_per_head = s->head_dim / 8;
+  p.token_bytes = int32_t(row);
+  p.bt_shift = bt_shift;
+  p.bt_mask = s->block_tokens - 1;
+
+  const int64_t blocks = (p.chunks + 255) / 256;
+  const dim3 grid(unsigned(blocks < 4096 ? blocks : 4096), 2), block(256);
+  cache_write_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}

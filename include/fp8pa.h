@@ -203,6 +203,52 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
                          int32_t head_dim, const float* partial_o, const float* partial_lse,
                          const float* sinks, void* out, float* lse, void* stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * The KV-cache writer: new tokens' bf16 keys and values into the E4M3 pages
+ * fp8pa_decode reads.  The gist "Qwen3.8-27B ... 451K tokens of KV on a
+ * single RTX 5090" (kernel reshape_and_cache_nvfp4_kernel) writes NVFP4
+ * pages the same way: token t goes to slot slot_mapping[t], i.e. page
+ * slot / block_tokens at position slot % block_tokens, a negative slot
+ * meaning "skip", and each element is multiplied by the fp32 reciprocal of
+ * its scale before encoding.  Here element x of kv head h is stored as
+ * e4m3(x * (1 / scale_h)), the reciprocal and the product in fp32, rounded
+ * to nearest with ties to even and saturated to +-448 (the FN format has no
+ * infinity); a NaN element gives a NaN code.  fp8pa_decode then reads
+ * decode(code) * scale_h.
+ */
+typedef struct fp8pa_write_shape {
+  int64_t num_tokens;      /* T >= 0 rows of key, value and slot_mapping */
+  int64_t key_stride;      /* elements between token rows of key: >= Hkv * D, a multiple of 8 */
+  int64_t value_stride;    /* the same for value */
+  int32_t num_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;        /* D: 64, 128 or 256 */
+  int32_t block_tokens;    /* bt: tokens per page, a power of two in [1, 1024] */
+  int32_t num_blocks;      /* pages in each pool, >= 1 */
+  int32_t k_scale_count;   /* 1 (per tensor) or Hkv (per kv head) */
+  int32_t v_scale_count;   /* 1 or Hkv */
+} fp8pa_write_shape;
+
+/*
+ * fp8pa_cache_write: writes every token t < T whose slot lies in
+ * [0, num_blocks * bt) into both pools; other slots are skipped.
+ *
+ *   key, value    bf16 [T, Hkv, D], token rows key_stride / value_stride
+ *                 elements apart (16-byte aligned)
+ *   slot_mapping  int64 [T]
+ *   k_scale       float [k_scale_count]; v_scale float [v_scale_count]
+ *   k_cache       e4m3 [num_blocks, bt, Hkv, D] (8-byte aligned); v_cache alike
+ *
+ * Only the slots named are written.  Two tokens with the same slot race
+ * (either may win).  All pointers are device pointers owned by the caller;
+ * work is queued on `stream`.  Returns FP8PA_ERR_INVALID_ARG /
+ * FP8PA_ERR_UNSUPPORTED / FP8PA_ERR_MISALIGNED for bad host-known
+ * arguments (nothing is queued then), FP8PA_ERR_HIP if the launch fails.
+ */
+fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* shape, const void* key, const void* value,
+                               const int64_t* slot_mapping, const float* k_scale,
+                               const float* v_scale, void* k_cache, void* v_cache, void* stream);
+
 /* Static text for a status code. */
 const char* fp8pa_status_string(fp8pa_status status);
 

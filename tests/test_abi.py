@@ -283,3 +283,52 @@ def test_balanced_plan_covers_every_tile(seed):
             for a0, a1 in spans:
                 if p["variant"] == 1:
                     assert a1 - a0 <= 128
+
+
+def _write_shape(**over):
+    kw = dict(num_tokens=4, key_stride=1024, value_stride=1024, num_kv_heads=8, head_dim=128,
+              block_tokens=16, num_blocks=8, k_scale_count=8, v_scale_count=1)
+    kw.update(over)
+    return _lib.WriteShape(kw["num_tokens"], kw["key_stride"], kw["value_stride"], kw["num_kv_heads"],
+                           kw["head_dim"], kw["block_tokens"], kw["num_blocks"], kw["k_scale_count"],
+                           kw["v_scale_count"])
+
+
+def _call_write(shape, **ptrs):
+    base = dict(key=0x10000, value=0x20000, slots=0x30000, ks=0x40000, vs=0x50000, kc=0x60000,
+                vc=0x70000)
+    base.update(ptrs)
+    return _lib.lib().fp8pa_cache_write(ctypes.byref(shape), base["key"], base["value"], base["slots"],
+                                        base["ks"], base["vs"], base["kc"], base["vc"], None)
+
+
+WRITE_BAD = [
+    (dict(num_tokens=-1), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(head_dim=96), _lib.FP8PA_ERR_UNSUPPORTED),
+    (dict(block_tokens=24), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(block_tokens=2048), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(key_stride=1000), _lib.FP8PA_ERR_INVALID_ARG),       # shorter than a token row
+    (dict(value_stride=1028), _lib.FP8PA_ERR_MISALIGNED),       # not a multiple of 8 elements
+    (dict(k_scale_count=3), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(v_scale_count=0), _lib.FP8PA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("over,status", WRITE_BAD)
+def test_cache_write_rejects_bad_shapes(over, status):
+    assert _call_write(_write_shape(**over)) == status
+
+
+def test_cache_write_checks_pointers_before_the_gpu():
+    L = _lib.lib()
+    assert L.fp8pa_cache_write(None, 1, 1, 1, 1, 1, 1, 1, None) == _lib.FP8PA_ERR_INVALID_ARG
+    s = _write_shape()
+    for name in ("key", "value", "slots", "ks", "vs", "kc", "vc"):
+        assert _call_write(s, **{name: None}) == _lib.FP8PA_ERR_INVALID_ARG, name
+    for name, addr in (("key", 0x10008), ("value", 0x20004), ("kc", 0x60004), ("vc", 0x70002),
+                       ("slots", 0x30004), ("ks", 0x40002)):
+        assert _call_write(s, **{name: addr}) == _lib.FP8PA_ERR_MISALIGNED, name
+    # nothing to write: no pointer is needed and nothing is queued
+    assert _call_write(_write_shape(num_tokens=0), key=None, value=None, slots=None) == _lib.FP8PA_OK

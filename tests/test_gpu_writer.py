@@ -1,0 +1,125 @@
+"""GPU parity of the KV-cache writer (fp8pa_cache_write) against the oracle.
+
+Codes are compared bit for bit (a NaN input only has to give a NaN code);
+a round trip writes a sequence's keys and values with the library and reads
+them with fp8pa_decode.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_harness import compare, to_host
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+fp = pytest.importorskip("decode_attention_paged_fp8pa_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp.lib()
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _inputs(rng, T, Hkv, D, pad, specials):
+    """bf16 [T, Hkv, D] views with `pad` extra elements per token row, values
+    spread from the E4M3 subnormal range to past saturation."""
+    mag = np.exp2(rng.uniform(-14, 11, size=(T, Hkv, D)))
+    x = (rng.standard_normal((T, Hkv, D)) * mag).astype(np.float32)
+    if specials:
+        x[0, 0, :4] = [np.nan, np.inf, -np.inf, -0.0]
+        x[min(1, T - 1), -1, -3:] = [448.0, 464.0, -1e6]
+    full = torch.zeros((T, Hkv * D + pad), dtype=torch.bfloat16)
+    full[:, : Hkv * D] = torch.from_numpy(x.reshape(T, Hkv * D)).to(torch.bfloat16)
+    return full.cuda()[:, : Hkv * D].view(T, Hkv, D) if pad == 0 else \
+        full.cuda().as_strided((T, Hkv, D), (Hkv * D + pad, D, 1))
+
+
+CASES = [
+    # T, Hkv, D, bt, num_blocks, pad, per_head
+    (37, 8, 128, 16, 5, 0, True),
+    (64, 4, 256, 64, 2, 24, False),
+    (100, 8, 64, 16, 10, 8, True),
+    (9, 2, 128, 1, 16, 0, True),
+    (1, 1, 64, 32, 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("T,Hkv,D,bt,nb,pad,per_head", CASES)
+def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head):
+    rng = np.random.default_rng(T * 7 + D)
+    key = _inputs(rng, T, Hkv, D, pad, True)
+    value = _inputs(rng, T, Hkv, D, pad, False)
+    nslots = nb * bt
+    slots = rng.permutation(nslots)[:T] if T <= nslots else rng.integers(0, nslots, size=T)
+    slots = slots.astype(np.int64)
+    slots[rng.random(T) < 0.15] = -1          # skipped tokens
+    if T > 2:
+        slots[2] = nslots + 3                  # past the cache: skipped as well
+    if T > nslots:                             # keep written slots distinct (no races)
+        seen = set()
+        for i, sl in enumerate(slots):
+            if sl in seen:
+                slots[i] = -1
+            seen.add(sl)
+    nsc = Hkv if per_head else 1
+    ks = rng.uniform(0.01, 0.2, size=nsc).astype(np.float32)
+    vs = rng.uniform(0.01, 0.2, size=nsc).astype(np.float32)
+    k0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
+    v0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
+    kc, vc = torch.from_numpy(k0).cuda(), torch.from_numpy(v0).cuda()
+    fp.cache_write(key, value, torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
+                   torch.from_numpy(vs).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, k0, v0)
+    for got, want, name in ((kc.cpu().numpy(), want_k, "k"), (vc.cpu().numpy(), want_v, "v")):
+        nan_w = np.isnan(oracle.E4M3_TABLE[want])
+        assert np.array_equal(np.isnan(oracle.E4M3_TABLE[got]), nan_w), name
+        diff = (got != want) & ~nan_w
+        assert not diff.any(), (name, np.argwhere(diff)[:5], got[diff][:5], want[diff][:5])
+
+
+def test_writer_then_decode_round_trip():
+    # keys and values of two sequences written by the library, then read back
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, D, bt = 2, 16, 4, 128, 16
+    lens = [300, 77]
+    nb = sum((L + bt - 1) // bt for L in lens) + 3
+    perm = rng.permutation(nb)
+    table = np.full((B, max((L + bt - 1) // bt for L in lens)), -1, np.int32)
+    slots, k_rows, v_rows, off = [], [], [], 0
+    for b, L in enumerate(lens):
+        pages = perm[off: off + (L + bt - 1) // bt]
+        off += len(pages)
+        table[b, : len(pages)] = pages
+        slots.extend(int(pages[t // bt]) * bt + t % bt for t in range(L))
+    T = len(slots)
+    key = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    value = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    ks = rng.uniform(0.02, 0.1, size=Hkv).astype(np.float32)
+    vs = rng.uniform(0.02, 0.1, size=Hkv).astype(np.float32)
+    zeros = np.zeros((nb, bt, Hkv, D), np.uint8)
+    kc, vc = torch.from_numpy(zeros).cuda(), torch.from_numpy(zeros).cuda()
+    slot_t = torch.tensor(slots, dtype=torch.int64).cuda()
+    ks_t, vs_t = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    fp.cache_write(key, value, slot_t, ks_t, vs_t, kc, vc)
+    k_or, v_or = oracle.cache_write(_bits(key), _bits(value), np.array(slots), ks, vs, zeros, zeros)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), k_or) and np.array_equal(vc.cpu().numpy(), v_or)
+    q = torch.from_numpy(rng.standard_normal((B, 1, Hq, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32).cuda()
+    bt_t = torch.from_numpy(table).cuda()
+    out, lse = fp.decode(q, kc, vc, bt_t, sl, ks_t, vs_t, None, sm_scale=1 / np.sqrt(D))
+    ro, rl = oracle.decode(q_bits=_bits(q), k_cache=k_or, v_cache=v_or, block_table=table,
+                           seq_lens=np.array(lens, np.int32), k_scale=ks, v_scale=vs,
+                           sm_scale=1 / np.sqrt(D))
+    o, l = to_host(out, lse)
+    compare(o, l, ro, rl, label="cache_write -> decode")
