@@ -21,7 +21,8 @@ one.  The graph is replayed REPLAYS times: the step time is the median of
 the per-replay averages, reported with p10 / p90.  The partial kernel alone
 is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
-timed as the practical HBM ceiling ("copy_ceiling").
+timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
+fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
 
 HBM traffic (roofline.traffic): four rocprofv3 --pmc passes, FETCH_SIZE and
 WRITE_SIZE over this workload and over `--calibrate-copy` (device copies of
@@ -296,6 +297,57 @@ def copy_ceiling(log):
             "pct_of_peak": round(gbps / PEAK_GBPS * 100, 2)}
 
 
+def measure_writer(steps, log):
+    """fp8pa_cache_write: new tokens' bf16 keys and values into E4M3 pages
+    (Hkv = 8, D = 128, 16-token pages, per-kv-head scales), at the size of
+    one MTP decode step (256 sequences x 4 tokens) and of a prefill chunk
+    (65536 tokens).  Bytes moved per call = T * Hkv * D * (2 + 2 read + 1 + 1
+    written) + 8 T of slots; timed from graph replays like the decode."""
+    import torch
+
+    import decode_attention_paged_fp8pa_amd as fp
+
+    out = {}
+    Hkv, D, bt = 8, 128, 16
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for name, T in (("decode_step_1024_tokens", 1024), ("prefill_65536_tokens", 65536)):
+        nb = (T + bt - 1) // bt + 64
+        key = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16).cuda()
+        value = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16).cuda()
+        slots = torch.randperm(nb * bt, generator=gen)[:T].to(torch.int64).cuda()
+        ks = torch.full((Hkv,), 0.05).cuda()
+        vs = torch.full((Hkv,), 0.05).cuda()
+        kc = torch.zeros((nb, bt, Hkv, D), dtype=torch.uint8, device="cuda")
+        vc = torch.zeros_like(kc)
+        for _ in range(3):
+            fp.cache_write(key, value, slots, ks, vs, kc, vc)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fp.cache_write(key, value, slots, ks, vs, kc, vc)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(REPLAYS):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps * 1e-3)
+        t = sorted(per)[len(per) // 2]
+        nbytes = T * Hkv * D * 6 + 8 * T
+        out[name] = {"tokens": T, "us": round(t * 1e6, 2), "bytes": nbytes,
+                     "gbps": round(nbytes / t / 1e9, 1), "pct_of_peak": round(nbytes / t / 1e9 / PEAK_GBPS * 100, 2)}
+        log(f"[bench] writer {name}: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s read+write "
+            f"({nbytes / t / 1e9 / PEAK_GBPS * 100:.1f}% of peak)")
+        del g, key, value, kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, budget_s, log):
     """The float64 oracle, as it stands, on whole sequences until the budget is used."""
     import oracle
@@ -469,6 +521,7 @@ def main():
         "kernel_avg_us": round(h["partial_ms"] * 1e3, 2),
         "algorithmic_bytes_per_launch": h["kv_bytes"],
     }
+    writer = measure_writer(min(args.steps, 100), log)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head_wl, args.cpu_budget, log)
@@ -491,6 +544,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "copy_ceiling": ceiling,
+        "writer": writer,
         "per_workload": {
             f"cfg{k}": {
                 "workload": r["describe"], "step_us": round(r["step_ms"] * 1e3, 2),
