@@ -18,6 +18,7 @@ from .fp8pa_ref import (  # noqa: F401
     e4m3_decode_code,
     bf16_bits_to_f64,
     attended_range,
+    k_scale_of_head,
     decode,
     merge,
 )

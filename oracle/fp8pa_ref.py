@@ -38,6 +38,7 @@ __all__ = [
     "E4M3_TABLE",
     "e4m3_decode_code",
     "bf16_bits_to_f64",
+    "k_scale_of_head",
     "attended_range",
     "decode",
     "merge",
@@ -91,18 +92,35 @@ def attended_range(seq_len: int, q_len: int, i: int, window: int) -> tuple[int, 
 
 
 def _gather(cache: np.ndarray, block_table_row: np.ndarray, g: int, ts: np.ndarray,
-            scale: float) -> np.ndarray:
+            scale) -> np.ndarray:
     """Dequantised rows [len(ts), D] of kv head g at logical positions ts.
 
     Token t of the sequence lives in page block_table_row[t // bt] at slot
-    t % bt [P4 writer index arithmetic]; the value is decode(code) * scale [P4].
-    Only the table entries of the positions asked for are read.
+    t % bt [P4 writer index arithmetic]; the value is decode(code) * scale [P4],
+    `scale` one number or one per head_dim element.  Only the table entries
+    of the positions asked for are read.
     """
     bt = cache.shape[1]
     pages = block_table_row[ts // bt].astype(np.int64)
     slots = ts % bt
     codes = cache[pages, slots, g, :]
-    return E4M3_TABLE[codes] * float(scale)
+    return E4M3_TABLE[codes] * np.asarray(scale, dtype=np.float64)
+
+
+def k_scale_of_head(k_scale, g: int, D: int, k_groups: int = 1) -> np.ndarray:
+    """The K scale of every head_dim element of kv head g, float64 [D].
+
+    [P1 `special_requirements`]: K scales may come in k_groups in
+    (1, 2, 4, 8, 16) groups along head_dim, head_dim / k_groups >= 32 (V
+    keeps one).  Reading: group j covers dims [j D/k_groups, (j+1) D/k_groups);
+    k_scale holds k_groups numbers (one set for all kv heads) or Hkv * k_groups
+    numbers, kv head major ([Hkv][k_groups]).
+    """
+    ks = np.asarray(k_scale, dtype=np.float64).reshape(-1)
+    kg = max(1, int(k_groups))
+    per_head = ks.size > kg
+    base = g * kg if per_head else 0
+    return ks[base + np.arange(D) // (D // kg)]
 
 
 def _softmax_rows(scores: np.ndarray, sink: float | None):
@@ -128,7 +146,7 @@ def _softmax_rows(scores: np.ndarray, sink: float | None):
 
 def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
            sinks=None, window=0, sm_scale=None, rows=None, key_range=None,
-           key_chunk=16384):
+           key_chunk=16384, k_groups=1):
     """Reference paged decode attention [P1 title/summary], float64.
 
     Arguments (numpy arrays, as the library receives them):
@@ -137,7 +155,9 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
       v_cache     uint8  [num_blocks, bt, Hkv, D]
       block_table int32  [B, max_blocks]  page of each logical page index
       seq_lens    int32  [B]  tokens in each sequence, the q_len new ones included
-      k_scale, v_scale  float32 [1] (per tensor) or [Hkv] (per kv head)
+      k_scale, v_scale  float32 [1] (per tensor) or [Hkv] (per kv head); with
+                  k_groups > 1, k_scale is [k_groups] or [Hkv, k_groups]
+                  (see k_scale_of_head)
       sinks       float32 [Hq] or None  per-head sink logits
       window      int, <= 0 for none
       sm_scale    float, the softmax scale (default 1/sqrt(D))
@@ -179,7 +199,7 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
 
     for (b, g), members in groups.items():
         L = int(seq_lens[b])
-        ks = float(k_scale[g if k_scale.size > 1 else 0])
+        ks = k_scale_of_head(k_scale, g, D, k_groups)
         vs = float(v_scale[g if v_scale.size > 1 else 0])
         ranges = []
         for n in members:

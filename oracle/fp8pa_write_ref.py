@@ -24,7 +24,8 @@ Readings of what the pages leave open (listed in the design doc):
   as the page's kernel does, and the encoding rounds that fp32 number;
 * slots outside the cache (slot >= num_blocks * block_tokens) are skipped
   like negative ones;
-* scales are one float per tensor or one per kv head, as in the decode.
+* scales are one float per tensor or one per kv head, as in the decode; K
+  scales may come in k_groups groups along head_dim, as the decode reads them.
 """
 
 from __future__ import annotations
@@ -69,17 +70,26 @@ def e4m3_encode(x) -> np.ndarray:
     return flat.reshape(x.shape)
 
 
-def cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_cache, v_cache):
+def cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_cache, v_cache,
+                k_groups=1):
     """Returns copies of (k_cache, v_cache) [num_blocks, bt, Hkv, D] (uint8)
     with every token t whose slot is valid written: element (h, d) of token t
-    becomes e4m3(fp32(x * fp32(1 / scale_h))), x the bf16 value of
-    key_bits[t, h, d] (uint16 bit patterns, [T, Hkv, D])."""
+    becomes e4m3(fp32(x * fp32(1 / scale))), x the bf16 value of
+    key_bits[t, h, d] (uint16 bit patterns, [T, Hkv, D]) and scale the one
+    the decode reads for that element (K: per head_dim group when
+    k_groups > 1, laid out as in the decode oracle's k_scale_of_head)."""
     k_out = np.array(k_cache, dtype=np.uint8, copy=True)
     v_out = np.array(v_cache, dtype=np.uint8, copy=True)
     nb, bt, hkv, d = k_out.shape
     ks = np.asarray(k_scale, dtype=np.float32).reshape(-1)
     vs = np.asarray(v_scale, dtype=np.float32).reshape(-1)
-    for src_bits, scales, dst in ((key_bits, ks, k_out), (value_bits, vs, v_out)):
+    kg = max(1, int(k_groups))
+
+    def scales_of(arr, groups, h):  # float32 [D]: the scale of each element of head h
+        base = h * groups if arr.size > groups else 0
+        return arr[base + np.arange(d) // (d // groups)]
+
+    for src_bits, scales, groups, dst in ((key_bits, ks, kg, k_out), (value_bits, vs, 1, v_out)):
         src = np.asarray(src_bits, dtype=np.uint16)
         vals = (src.astype(np.uint32) << 16).view(np.float32)  # exact bf16 values
         for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).reshape(-1)):
@@ -87,8 +97,7 @@ def cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_cache, v
                 continue
             page, off = int(slot) // bt, int(slot) % bt
             for h in range(hkv):
-                s = scales[h if scales.size > 1 else 0]
-                inv = np.float32(1.0) / s
+                inv = (np.float32(1.0) / scales_of(scales, groups, h)).astype(np.float32)
                 prod = (vals[t, h, :] * inv).astype(np.float32)
                 dst[page, off, h, :] = e4m3_encode(prod.astype(np.float64))
     return k_out, v_out

@@ -44,7 +44,9 @@ def brute_decode(wl, key_range=None, sinks="from_workload"):
     q = _bf16_to_float(wl.q_bits)
     out = np.zeros((B, q_len, Hq, D))
     lse = np.zeros((B, q_len, Hq))
-    ks_all = np.asarray(wl.k_scale, dtype=np.float64).reshape(-1)
+    kg = getattr(wl, "k_groups", 1)
+    # K scale as a [heads or 1, k_groups] grid; dim d falls in column d * kg // D
+    ks_grid = np.asarray(wl.k_scale, dtype=np.float64).reshape(-1, kg)
     vs_all = np.asarray(wl.v_scale, dtype=np.float64).reshape(-1)
     for b in range(B):
         L = int(wl.seq_lens[b])
@@ -54,7 +56,7 @@ def brute_decode(wl, key_range=None, sinks="from_workload"):
             pos = L - q_len + i
             for h in range(Hq):
                 g = h // G
-                ks = ks_all[g] if ks_all.size > 1 else ks_all[0]
+                ks_row = ks_grid[g] if ks_grid.shape[0] > 1 else ks_grid[0]
                 vs = vs_all[g] if vs_all.size > 1 else vs_all[0]
                 keys = []
                 for t in range(L):
@@ -69,7 +71,7 @@ def brute_decode(wl, key_range=None, sinks="from_workload"):
                 for t in keys:
                     acc = 0.0
                     for d in range(D):
-                        acc += q[b, i, h, d] * (K[t, g, d] * ks)
+                        acc += q[b, i, h, d] * (K[t, g, d] * ks_row[d * kg // D])
                     scores.append(wl.sm_scale * acc)
                 terms = list(scores)
                 if sk is not None:

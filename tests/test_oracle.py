@@ -160,6 +160,72 @@ def test_scale_folding_invariance():
     np.testing.assert_allclose(lse, lse2, rtol=1e-12, atol=1e-13)
 
 
+# ------------------------------------------------ K scale groups along head_dim
+
+KG_TINY = [
+    dict(B=2, q_len=1, Hq=4, Hkv=2, D=8, bt=4, seq_lens=[9, 17], window=0, sinks=True,
+         scale=("per_head", 0.02, 0.1), k_groups=2),
+    dict(B=1, q_len=2, Hq=2, Hkv=1, D=16, bt=8, seq_lens=[23], window=7, sinks=False,
+         scale=("tensor", 0.05), k_groups=4),
+    dict(B=2, q_len=1, Hq=6, Hkv=3, D=16, bt=4, seq_lens=[5, 14], window=0, sinks=True,
+         scale=("per_head", 0.01, 0.2), k_groups=8),
+]
+
+
+@pytest.mark.parametrize("k", range(len(KG_TINY)))
+def test_k_groups_oracle_matches_brute_force(k):
+    wl = make_workload(seed=40 + k, **KG_TINY[k])
+    assert wl.k_scale.size in (wl.k_groups, wl.Hkv * wl.k_groups)
+    out, lse = oracle.decode(**wl.oracle_kwargs())
+    bo, bl = brute_decode(wl)
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-13)
+
+
+def test_k_groups_with_equal_scales_is_one_scale():
+    wl = _wl(scale=("per_head", 0.02, 0.1), sinks=True, window=40)
+    out, lse = oracle.decode(**wl.oracle_kwargs())
+    kw = wl.oracle_kwargs()
+    kw.update(k_scale=np.repeat(wl.k_scale, 4), k_groups=4)   # [Hkv, 4], equal within a head
+    out2, lse2 = oracle.decode(**kw)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_k_groups_scale_moves_into_the_query():
+    """Multiplying group j's K scale by a power of two and the query's dims of
+    that group by its inverse changes no score, so no output (bf16 queries
+    stay exact under power-of-two scaling)."""
+    import torch
+    wl = make_workload(B=2, q_len=1, Hq=8, Hkv=2, D=32, bt=16, seq_lens=[70, 33], seed=8,
+                       scale=("per_head", 0.02, 0.1), sinks=True, k_groups=4)
+    out, lse = oracle.decode(**wl.oracle_kwargs())
+    f = np.array([2.0, 0.5, 4.0, 0.25])
+    ks2 = (wl.k_scale.reshape(wl.Hkv, 4) * f).astype(np.float32).reshape(-1)
+    q = torch.from_numpy(wl.q_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    q = q / torch.from_numpy(np.repeat(f, 8))
+    q_bits = q.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    kw = wl.oracle_kwargs()
+    kw.update(q_bits=q_bits, k_scale=ks2)
+    out2, lse2 = oracle.decode(**kw)
+    np.testing.assert_allclose(out, out2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-12, atol=1e-13)
+
+
+def test_k_groups_per_tensor_scale_layout():
+    """A [k_groups] scale serves every kv head: it equals the [Hkv, k_groups]
+    scale that repeats it per head."""
+    wl = make_workload(B=1, q_len=1, Hq=4, Hkv=2, D=32, bt=8, seq_lens=[30], seed=9,
+                       scale=("tensor", 0.05), k_groups=2)
+    assert wl.k_scale.size == 2
+    out, lse = oracle.decode(**wl.oracle_kwargs())
+    kw = wl.oracle_kwargs()
+    kw.update(k_scale=np.tile(wl.k_scale, 2))
+    out2, lse2 = oracle.decode(**kw)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    d = oracle.k_scale_of_head(np.arange(6, dtype=np.float32), 1, 12, 3)
+    assert list(d) == [3] * 4 + [4] * 4 + [5] * 4
+
+
 def _scores_row(wl, b, h, ts, i=0):
     """Scores of row (b, i, h) at positions ts computed with torch's E4M3 decode."""
     from tests.brute_force import depage, _codes_to_float, _bf16_to_float

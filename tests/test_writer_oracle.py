@@ -97,3 +97,26 @@ def test_cache_write_then_decode_is_close():
         back = T[k1[s // bt, s % bt]] * ks[:, None]
         # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 for normal values
         assert np.all(np.abs(back - xb[t]) <= 2.0 ** -4 * np.abs(xb[t]) + 2.0 ** -10 * ks[:, None])
+
+
+def test_cache_write_k_groups():
+    """With k_groups, each head_dim group of the key is encoded against its own
+    scale ([Hkv, k_groups] or [k_groups] for all heads); values keep one."""
+    nb, bt, hkv, d = 2, 4, 2, 16
+    rng = np.random.default_rng(3)
+    key = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    slots = np.array([1, 6, -3])
+    zeros = np.zeros((nb, bt, hkv, d), np.uint8)
+    xb = (_bf16_bits(key).astype(np.uint32) << 16).view(np.float32)
+    for ks in (np.array([0.5, 0.25, 2.0, 1.0, 0.125, 4.0, 8.0, 0.5], np.float32),
+               np.array([0.5, 0.25, 2.0, 1.0], np.float32)):
+        k1, v1 = oracle.cache_write(_bf16_bits(key), _bf16_bits(key), slots, ks, np.array([1.0], np.float32),
+                                    zeros, zeros, k_groups=4)
+        grid = ks.reshape(-1, 4)
+        for t, s in ((0, 1), (1, 6)):
+            for h in range(hkv):
+                row = grid[h] if grid.shape[0] > 1 else grid[0]
+                # power-of-two scales: x * (1/s) is exact, so encode(x / s) is the answer
+                want = oracle.e4m3_encode(xb[t, h].astype(np.float64) / np.repeat(row, d // 4))
+                assert np.array_equal(k1[s // bt, s % bt, h], want)
+                assert np.array_equal(v1[s // bt, s % bt, h], oracle.e4m3_encode(xb[t, h].astype(np.float64)))

@@ -7,10 +7,13 @@ numpy.random.default_rng(seed)):
 2. the block table: a random permutation of the page pool handed out to the
    sequences in order (or the identity);
 3. scales: one float32 per tensor, or one per kv head drawn U[lo, hi]
-   (k_scale first, then v_scale);
+   (k_scale first, then v_scale); with k_groups > 1 the K scale has one
+   number per head_dim group as well ([k_groups] drawn U[s/2, 2s] for a
+   per-tensor scale s, or [Hkv, k_groups] drawn U[lo, hi]);
 4. q ~ N(0, 1), rounded to bf16 (round to nearest even);
 5. K then V: for every position that some query row attends,
-   N(0, 1) / scale, clamped to +-448 and rounded to E4M3 (nearest even);
+   N(0, 1) / scale (the scale of that element's head and group), clamped to
+   +-448 and rounded to E4M3 (nearest even);
 6. sinks ~ N(0, 1) float32 [Hq] when the workload has sinks.
 
 Every other byte of the pools (positions no row attends, pages no sequence
@@ -59,12 +62,13 @@ class Workload:
     v_cache: np.ndarray       # uint8 [num_blocks, bt, Hkv, D]
     block_table: np.ndarray   # int32 [B, max_blocks]
     seq_lens: np.ndarray      # int32 [B]
-    k_scale: np.ndarray       # float32 [1] or [Hkv]
+    k_scale: np.ndarray       # float32 [1] or [Hkv]; [k_groups] or [Hkv * k_groups]
     v_scale: np.ndarray       # float32 [1] or [Hkv]
     sinks: np.ndarray | None  # float32 [Hq] or None
     window: int
     sm_scale: float
     meta: dict = field(default_factory=dict)
+    k_groups: int = 1
 
     @property
     def B(self):
@@ -98,7 +102,7 @@ class Workload:
         return dict(q_bits=self.q_bits, k_cache=self.k_cache, v_cache=self.v_cache,
                     block_table=self.block_table, seq_lens=self.seq_lens,
                     k_scale=self.k_scale, v_scale=self.v_scale, sinks=self.sinks,
-                    window=self.window, sm_scale=self.sm_scale)
+                    window=self.window, sm_scale=self.sm_scale, k_groups=self.k_groups)
 
     def key_union(self, b):
         """[lo, hi) of positions some query row of sequence b attends."""
@@ -132,12 +136,13 @@ def _bf16_bits(x: np.ndarray) -> np.ndarray:
 def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", pool=None,
                   scale=("tensor", 0.05), window=0, sinks=False, sm_scale=None,
                   poison=True, name="custom", q_zero=False, extra_table_cols=0,
-                  key_chunk=8192):
+                  key_chunk=8192, k_groups=1):
     """Build one seeded workload.
 
     seq_lens: an int, a list, or ("uniform", lo, hi).  scale: ("tensor", s) or
     ("per_head", lo, hi).  table: "perm" or "identity".  pool: minimum pool
     size in pages.  extra_table_cols adds -1 columns to every table row.
+    k_groups > 1 gives the K scale one number per head_dim group.
     """
     rng = np.random.default_rng(seed)
     # 1. sequence lengths
@@ -163,11 +168,15 @@ def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", poo
         bt_arr[b, :n] = order[off:off + n]
         off += n
     # 3. scales
+    kg = max(1, int(k_groups))
     if scale[0] == "tensor":
-        k_scale = np.array([scale[1]], dtype=np.float32)
+        if kg > 1:
+            k_scale = rng.uniform(scale[1] / 2, scale[1] * 2, size=kg).astype(np.float32)
+        else:
+            k_scale = np.array([scale[1]], dtype=np.float32)
         v_scale = np.array([scale[1]], dtype=np.float32)
     else:
-        k_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
+        k_scale = rng.uniform(scale[1], scale[2], size=Hkv * kg).astype(np.float32)
         v_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
     # 4. queries
     qf = rng.standard_normal((B, q_len, Hq, D), dtype=np.float32)
@@ -179,7 +188,10 @@ def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", poo
     caches = []
     wl_tmp = Workload(name, q_bits, np.empty((0, bt, Hkv, D), np.uint8), None, bt_arr, sl,
                       k_scale, v_scale, None, int(window), 0.0)
-    for which, sc in (("k", k_scale), ("v", v_scale)):
+    for which, sc, groups in (("k", k_scale, kg), ("v", v_scale, 1)):
+        # the scale of every (head, dim) element, [Hkv, D]
+        per_head = sc.reshape(-1, groups) if sc.size > groups else np.tile(sc.reshape(1, groups), (Hkv, 1))
+        el_scale = np.repeat(per_head, D // groups, axis=1)
         cache = np.full((num_blocks, bt, Hkv, D), fill, dtype=np.uint8)
         flat = cache.reshape(num_blocks * bt, Hkv, D)
         for b in range(B):
@@ -190,7 +202,7 @@ def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", poo
             for c0 in range(lo, hi, key_chunk):
                 c1 = min(c0 + key_chunk, hi)
                 x = rng.standard_normal((c1 - c0, Hkv, D), dtype=np.float32)
-                x /= sc.reshape(1, -1, 1) if sc.size > 1 else sc[0]
+                x /= el_scale[None]
                 ts = np.arange(c0, c1)
                 phys = bt_arr[b, ts // bt].astype(np.int64) * bt + ts % bt
                 flat[phys] = _e4m3_encode(x)
@@ -202,7 +214,7 @@ def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", poo
     return Workload(name=name, q_bits=q_bits, k_cache=caches[0], v_cache=caches[1],
                     block_table=bt_arr, seq_lens=sl, k_scale=k_scale, v_scale=v_scale,
                     sinks=sk, window=int(window), sm_scale=float(sm_scale),
-                    meta=dict(seed=seed, poison=poison))
+                    meta=dict(seed=seed, poison=poison), k_groups=kg)
 
 
 def make_config(k: int, seed: int | None = None, poison: bool = True) -> Workload:
