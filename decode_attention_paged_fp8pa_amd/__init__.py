@@ -59,7 +59,7 @@ __all__ = [
 
 
 def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=None,
-              max_seq_len, num_splits=0, flags=0) -> Shape:
+              max_seq_len, num_splits=0, flags=0, k_groups=1) -> Shape:
     """fp8pa_shape for tensors q [B, q_len, Hq, D] and k_cache [blocks, bt, Hkv, D]."""
     B, q_len, Hq, D = q.shape
     nb, bt, Hkv, Dk = k_cache.shape
@@ -70,18 +70,21 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
     return make_shape(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                       block_tokens=bt, num_blocks=nb, block_table_stride=block_table.stride(0),
                       max_seq_len=int(max_seq_len), k_scale_count=k_scale.numel(),
-                      v_scale_count=v_scale.numel(), window=int(window), sm_scale=sm_scale,
+                      v_scale_count=v_scale.numel(), k_groups=int(k_groups), window=int(window),
+                      sm_scale=sm_scale,
                       num_splits=int(num_splits), flags=int(flags))
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=None, *,
            window=0, sm_scale=None, max_seq_len=None, num_splits=0, flags=0, out=None, lse=None,
-           workspace=None, stream=None):
+           workspace=None, stream=None, k_groups=1):
     """Runs fp8pa_decode on torch device tensors; returns (out bf16, lse fp32).
 
     q bf16 [B, q_len, Hq, D]; k_cache, v_cache uint8 or float8_e4m3fn
     [num_blocks, bt, Hkv, D]; block_table int32 [B, stride] (unit column
-    stride); seq_lens int32 [B]; k_scale, v_scale float32 [1] or [Hkv];
+    stride); seq_lens int32 [B]; k_scale, v_scale float32 [1] or [Hkv] (with
+    k_groups > 1, k_scale is [k_groups] or [Hkv, k_groups]: one scale per
+    head_dim group);
     sinks float32 [Hq] or None.  max_seq_len should be given by callers that
     must not synchronise (it is read from seq_lens otherwise).
     """
@@ -103,7 +106,8 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item())
     shape = shape_for(q, k_cache, block_table, k_scale, v_scale, window=window, sm_scale=sm_scale,
-                      max_seq_len=max_seq_len, num_splits=num_splits, flags=flags)
+                      max_seq_len=max_seq_len, num_splits=num_splits, flags=flags,
+                      k_groups=k_groups)
     B, q_len, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, q_len, Hq, D), dtype=torch.bfloat16, device=q.device)
@@ -118,12 +122,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
     return out, lse
 
 
-def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *, stream=None):
+def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *, stream=None,
+                k_groups=1):
     """Runs fp8pa_cache_write on torch device tensors (in place on the caches).
 
     key, value bf16 [T, Hkv, D] with unit stride inside a token row;
     slot_mapping int64 [T] (negative: skip); k_scale, v_scale float32 [1] or
-    [Hkv]; k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D],
+    [Hkv] (k_scale [k_groups] or [Hkv, k_groups] with k_groups > 1);
+    k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D],
     contiguous.
     """
     import torch
@@ -143,6 +149,6 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
     if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("cache shape does not match key / value")
     shape = WriteShape(T, key.stride(0), value.stride(0), Hkv, D, bt, nb, k_scale.numel(),
-                       v_scale.numel())
+                       v_scale.numel(), int(k_groups))
     fp8pa_cache_write(shape, key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, stream)
     return k_cache, v_cache

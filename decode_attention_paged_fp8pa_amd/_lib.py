@@ -51,6 +51,7 @@ class Shape(ctypes.Structure):
         ("max_seq_len", ctypes.c_int32),
         ("k_scale_count", ctypes.c_int32),
         ("v_scale_count", ctypes.c_int32),
+        ("k_groups", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
@@ -71,6 +72,7 @@ class WriteShape(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("k_scale_count", ctypes.c_int32),
         ("v_scale_count", ctypes.c_int32),
+        ("k_groups", ctypes.c_int32),
     ]
 
 
@@ -165,11 +167,13 @@ def _stream(stream):
 
 
 def make_shape(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, block_tokens, num_blocks,
-               block_table_stride, max_seq_len, k_scale_count=1, v_scale_count=1, window=0,
-               sm_scale, num_splits=0, flags=0) -> Shape:
-    return Shape(batch, q_len, num_q_heads, num_kv_heads, head_dim, block_tokens, num_blocks,
-                 block_table_stride, max_seq_len, k_scale_count, v_scale_count, window,
-                 float(sm_scale), num_splits, flags)
+               block_table_stride, max_seq_len, k_scale_count=1, v_scale_count=1, k_groups=1,
+               window=0, sm_scale, num_splits=0, flags=0) -> Shape:
+    return Shape(batch=batch, q_len=q_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                 head_dim=head_dim, block_tokens=block_tokens, num_blocks=num_blocks,
+                 block_table_stride=block_table_stride, max_seq_len=max_seq_len,
+                 k_scale_count=k_scale_count, v_scale_count=v_scale_count, k_groups=k_groups,
+                 window=window, sm_scale=float(sm_scale), num_splits=num_splits, flags=flags)
 
 
 def fp8pa_plan(shape: Shape, cu_count: int) -> dict:

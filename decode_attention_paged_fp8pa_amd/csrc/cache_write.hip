@@ -18,6 +18,7 @@
 #include <cstdint>
 
 #include "../../include/fp8pa.h"
+#include "plan.h"
 
 namespace fp8pa {
 namespace {
@@ -31,7 +32,9 @@ struct WriteParams {
   const uint16_t* src[2];   // key, value
   int64_t stride[2];        // elements between token rows
   const float* scale[2];
-  int32_t per_head[2];      // 1: one scale per kv head
+  int32_t per_head[2];      // 1: one set of scales per kv head
+  int32_t groups[2];        // scales per head (K: k_groups along head_dim; V: 1)
+  int32_t group_shift[2];   // log2 of the 8-element chunks per group
   uint8_t* cache[2];
   const int64_t* slots;
   int64_t num_tokens;
@@ -73,7 +76,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
     const int64_t slot = p.slots[t];
     if (slot < 0 || slot >= p.num_slots) continue;
     const int h = c / p.chunks_per_head;
-    const float inv = 1.f / p.scale[kv][p.per_head[kv] ? h : 0];
+    const int grp = (c - h * p.chunks_per_head) >> p.group_shift[kv];
+    const float inv = 1.f / p.scale[kv][(p.per_head[kv] ? h * p.groups[kv] : 0) + grp];
     const u32x4 x = *reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 8 * int64_t(c));
     uint8_t* dst = cache + (slot >> p.bt_shift) * p.page_bytes +
                    int64_t(slot & p.bt_mask) * p.token_bytes + 8 * c;
@@ -106,7 +110,9 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   const int64_t row = int64_t(s->num_kv_heads) * s->head_dim;
   if (s->key_stride < row || s->value_stride < row) return FP8PA_ERR_INVALID_ARG;
   if (s->key_stride % 8 != 0 || s->value_stride % 8 != 0) return FP8PA_ERR_MISALIGNED;
-  if ((s->k_scale_count != 1 && s->k_scale_count != s->num_kv_heads) ||
+  if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
+  const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
+  if ((s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg) ||
       (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads))
     return FP8PA_ERR_INVALID_ARG;
   if (s->num_tokens == 0) return FP8PA_OK;
@@ -126,8 +132,12 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   p.stride[1] = s->value_stride;
   p.scale[0] = k_scale;
   p.scale[1] = v_scale;
-  p.per_head[0] = s->k_scale_count > 1 ? 1 : 0;
+  p.per_head[0] = s->k_scale_count > kg ? 1 : 0;
   p.per_head[1] = s->v_scale_count > 1 ? 1 : 0;
+  p.groups[0] = kg;
+  p.groups[1] = 1;
+  p.group_shift[0] = k_group_shift(kg, s->head_dim) - 3;
+  p.group_shift[1] = k_group_shift(1, s->head_dim) - 3;
   p.cache[0] = static_cast<uint8_t*>(k_cache);
   p.cache[1] = static_cast<uint8_t*>(v_cache);
   p.slots = slot_mapping;

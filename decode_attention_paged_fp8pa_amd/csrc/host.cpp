@@ -42,7 +42,10 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   if (!is_pow2(s->block_tokens) || s->block_tokens > 1024) return FP8PA_ERR_INVALID_ARG;
   if (ceil_div(s->max_seq_len, s->block_tokens) > s->block_table_stride)
     return FP8PA_ERR_INVALID_ARG;
-  if (s->k_scale_count != 1 && s->k_scale_count != s->num_kv_heads) return FP8PA_ERR_INVALID_ARG;
+  if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
+  const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
+  if (s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg)
+    return FP8PA_ERR_INVALID_ARG;
   if (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads) return FP8PA_ERR_INVALID_ARG;
   if (!std::isfinite(s->sm_scale)) return FP8PA_ERR_INVALID_ARG;
   if (s->num_splits < 0) return FP8PA_ERR_INVALID_ARG;

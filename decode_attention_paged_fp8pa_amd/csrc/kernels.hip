@@ -93,6 +93,8 @@ struct Params {
   int32_t max_seq_len;
   int32_t bt_shift, bt_mask, table_stride, window;
   int32_t k_per_head, v_per_head, direct;
+  int32_t k_groups;  // K scales per kv head (groups along head_dim), >= 1
+  int32_t kg_shift;  // log2 of the dims per K scale group
   int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
   int32_t pr;  // kv heads per wavefront (MFMA kernel: 2 pairs heads at D = 64)
   float sm_scale;
@@ -439,7 +441,11 @@ partial_mfma_kernel(Params p) {
   const int rlane = PR == 2 ? (n & 7) : w.rg * kRowsMfma + n;
   // Loads that need only the kv head and the row go first, so that their
   // round trips overlap the item's.
-  const float ks = p.k_scale[p.k_per_head ? kvh : 0];
+  // The K scale of the dims this lane stages: its kv head's (or the
+  // tensor's), or with scale groups along head_dim the group's; a lane's KB
+  // dims never straddle two groups.
+  const int qdim = w.half * DW + KB * (PR == 2 ? (qd & 1) : qd);
+  const float ks = p.k_scale[(p.k_per_head ? kvh * p.k_groups : 0) + (qdim >> p.kg_shift)];
   const float vs = p.v_scale[p.v_per_head ? kvh : 0];
   float sink2 = -INFINITY;
   if (p.sinks && p.direct && rlane < p.rows) {
@@ -682,6 +688,13 @@ partial_mfma_kernel(Params p) {
         qf[8 * i + 7] = bf16_hi(v.w);
       }
     }
+    // One K scale per head goes into the score scale below; group scales
+    // differ along the row, so each lane folds its own into its query dims.
+    const bool grouped = p.k_groups > 1;
+    if (grouped) {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) qf[i] *= ks;
+    }
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < KB; ++i) amax = fmaxf(amax, fabsf(qf[i]));
@@ -694,7 +707,7 @@ partial_mfma_kernel(Params p) {
       se = min(max(7 - e, -120), 120);
     }
     const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-    cr = p.sm_scale * ks * kLog2e / qs;
+    cr = p.sm_scale * (grouped ? 1.f : ks) * kLog2e / qs;
     // Scores are scaled as fma(S, cr, .) with cr > 0, so a -inf mask stays
     // -inf: a negative scale's sign moves into the query, and a zero scale
     // becomes a tiny positive one (its scores stay ~0).
@@ -812,7 +825,8 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
     return;
   }
 
-  const float ks = p.k_scale[p.k_per_head ? w.g : 0];
+  // this lane's 16 dims lie in one K scale group
+  const float ks = p.k_scale[(p.k_per_head ? w.g * p.k_groups : 0) + ((16 * c) >> p.kg_shift)];
   const float cq = p.sm_scale * ks * kLog2e;
   float qf[RPG][16];
 #pragma unroll
@@ -1282,7 +1296,9 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.bt_mask = pl.bt - 1;
   prm.table_stride = shape->block_table_stride;
   prm.window = shape->window > 0 ? shape->window : 0;
-  prm.k_per_head = shape->k_scale_count > 1 ? 1 : 0;
+  prm.k_groups = shape->k_groups > 1 ? shape->k_groups : 1;
+  prm.kg_shift = k_group_shift(prm.k_groups, shape->head_dim);
+  prm.k_per_head = shape->k_scale_count > prm.k_groups ? 1 : 0;
   prm.v_per_head = shape->v_scale_count > 1 ? 1 : 0;
   prm.direct = pl.direct;
   prm.ds = pl.ds;

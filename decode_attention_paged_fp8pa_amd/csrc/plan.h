@@ -17,6 +17,23 @@ constexpr int kMaxWgWaves = 8;       // wavefronts of a partial-kernel workgroup
 constexpr int kMaxSplitTiles = 128;  // tiles an MFMA split may span (64 two-tile steps, a lane each)
 constexpr int kMaxBalancedBatch = 256; // sequences a wavefront scans (4 per lane)
 
+// K scale groups along head_dim: 0 and 1 both mean one group; otherwise 2, 4,
+// 8 or 16 groups of at least 32 dims (so that every 16-byte slice a lane
+// stages, of at most 32 dims at a 32-dim boundary, lies in one group).
+inline bool k_groups_ok(int32_t k_groups, int32_t head_dim) {
+  if (k_groups == 0 || k_groups == 1) return true;
+  if (k_groups != 2 && k_groups != 4 && k_groups != 8 && k_groups != 16) return false;
+  return head_dim / k_groups >= 32;
+}
+
+// log2 of the dims per K scale group.
+inline int32_t k_group_shift(int32_t k_groups, int32_t head_dim) {
+  const int32_t per = head_dim / (k_groups > 1 ? k_groups : 1);
+  int32_t s = 0;
+  while ((1 << s) < per) ++s;
+  return s;
+}
+
 enum Variant : int32_t { kVariantDot = 0, kVariantMfma = 1 };
 
 struct Plan {

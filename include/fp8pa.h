@@ -14,6 +14,10 @@
  *
  *   K[t] = e4m3(k_cache[block_table[b][t / bt], t % bt, g, :]) * k_scale[g]
  *   V[t] = e4m3(v_cache[...same page and slot...]) * v_scale[g]
+ *
+ * (K scales may also come in k_groups groups along head_dim, the same
+ * record's special requirements: element d of K[t] then takes
+ * k_scale[g][d / (D / k_groups)]; V keeps one scale per head or tensor.)
  *   s_t  = sm_scale * dot(q[b, i, h, :], K[t])       for attended t
  *   out  = sum_t e^{s_t} V[t] / (sum_t e^{s_t} + e^{sinks[h]})
  *   lse  = ln(sum_t e^{s_t} + e^{sinks[h]})            (natural log)
@@ -82,8 +86,12 @@ typedef struct fp8pa_shape {
   int32_t block_table_stride; /* elements between rows of block_table, >= 1 */
   int32_t max_seq_len;        /* an upper bound of every seq_lens[b], >= 1; sizes the
                                  split plan and the workspace */
-  int32_t k_scale_count;      /* 1 (per tensor) or Hkv (per kv head) */
+  int32_t k_scale_count;      /* kg (per tensor) or Hkv * kg (per kv head, [Hkv][kg]),
+                                 kg = max(k_groups, 1) */
   int32_t v_scale_count;      /* 1 or Hkv */
+  int32_t k_groups;           /* 0 or 1: one K scale per head (or tensor); 2, 4, 8 or
+                                 16: K scale groups along head_dim, D / k_groups >= 32,
+                                 group j covering dims [j D / k_groups, (j+1) D / k_groups) */
   int32_t window;             /* <= 0: none; W > 0: the last W positions */
   float sm_scale;             /* softmax scale applied to q.K; finite */
   int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
@@ -225,8 +233,10 @@ typedef struct fp8pa_write_shape {
   int32_t head_dim;        /* D: 64, 128 or 256 */
   int32_t block_tokens;    /* bt: tokens per page, a power of two in [1, 1024] */
   int32_t num_blocks;      /* pages in each pool, >= 1 */
-  int32_t k_scale_count;   /* 1 (per tensor) or Hkv (per kv head) */
+  int32_t k_scale_count;   /* kg (per tensor) or Hkv * kg (per kv head), kg = max(k_groups, 1) */
   int32_t v_scale_count;   /* 1 or Hkv */
+  int32_t k_groups;        /* as in fp8pa_shape: each key element is encoded against
+                              the scale of its head_dim group */
 } fp8pa_write_shape;
 
 /*

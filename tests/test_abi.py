@@ -159,12 +159,27 @@ BAD = [
     (dict(max_seq_len=0), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(k_scale_count=3), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(v_scale_count=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(k_groups=-1), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(k_groups=3, k_scale_count=24), _lib.FP8PA_ERR_INVALID_ARG),   # not a power of two
+    (dict(k_groups=32, k_scale_count=256), _lib.FP8PA_ERR_INVALID_ARG),  # above 16
+    (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),   # 16 dims per group at D = 128
+    (dict(k_groups=4), _lib.FP8PA_ERR_INVALID_ARG),                     # Hkv scales, not Hkv * 4
     (dict(sm_scale=float("nan")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(num_splits=-1), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(flags=8), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(flags=3), _lib.FP8PA_ERR_INVALID_ARG),
 ]
+
+
+def test_plan_accepts_k_groups():
+    c = CONFIGS[2]
+    assert c["D"] == 128 and c["scale"][0] == "per_head"
+    for kg, count in ((0, c["Hkv"]), (1, 1), (2, 2), (4, 4), (4, 4 * c["Hkv"]), (2, 2 * c["Hkv"])):
+        fp.fp8pa_plan(cfg_shape(2, k_groups=kg, k_scale_count=count), 256)
+    s = cfg_shape(4, k_groups=8, k_scale_count=8)   # head_dim 256: 32 dims per group
+    assert CONFIGS[4]["D"] == 256
+    fp.fp8pa_plan(s, 256)
 
 
 @pytest.mark.parametrize("over,status", BAD)
@@ -287,11 +302,9 @@ def test_balanced_plan_covers_every_tile(seed):
 
 def _write_shape(**over):
     kw = dict(num_tokens=4, key_stride=1024, value_stride=1024, num_kv_heads=8, head_dim=128,
-              block_tokens=16, num_blocks=8, k_scale_count=8, v_scale_count=1)
+              block_tokens=16, num_blocks=8, k_scale_count=8, v_scale_count=1, k_groups=1)
     kw.update(over)
-    return _lib.WriteShape(kw["num_tokens"], kw["key_stride"], kw["value_stride"], kw["num_kv_heads"],
-                           kw["head_dim"], kw["block_tokens"], kw["num_blocks"], kw["k_scale_count"],
-                           kw["v_scale_count"])
+    return _lib.WriteShape(**kw)
 
 
 def _call_write(shape, **ptrs):
@@ -313,6 +326,10 @@ WRITE_BAD = [
     (dict(value_stride=1028), _lib.FP8PA_ERR_MISALIGNED),       # not a multiple of 8 elements
     (dict(k_scale_count=3), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(v_scale_count=0), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(k_groups=4), _lib.FP8PA_ERR_INVALID_ARG),                      # Hkv scales, not Hkv * 4
+    (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),    # 16 dims per group
+    (dict(k_groups=6, k_scale_count=48), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(k_groups=4, v_scale_count=32), _lib.FP8PA_ERR_INVALID_ARG),    # V keeps one per head
 ]
 
 

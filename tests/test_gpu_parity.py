@@ -126,6 +126,19 @@ SMALL = {
                          seq_lens=[1 + (13 * i * i + 5 * i) % 300 for i in range(256)]),
     "batch257_d64": dict(B=257, q_len=1, Hq=4, Hkv=1, D=64, bt=16,
                          seq_lens=[1 + (13 * i * i + 5 * i) % 300 for i in range(257)]),
+    # K scales in groups along head_dim: [Hkv, k_groups] or [k_groups]
+    "kg4_gqa_ragged": dict(B=3, q_len=1, Hq=32, Hkv=8, D=128, bt=16, seq_lens=[45, 800, 260],
+                           scale=("per_head", 0.005, 0.2), sinks=True, k_groups=4),
+    "kg2_d64_pair": dict(B=2, q_len=2, Hq=8, Hkv=4, D=64, bt=16, seq_lens=[90, 333], window=60,
+                         scale=("per_head", 0.02, 0.1), k_groups=2),
+    "kg2_d64_rows16": dict(B=2, q_len=1, Hq=32, Hkv=2, D=64, bt=32, seq_lens=[200, 71],
+                           scale=("tensor", 0.05), sinks=True, k_groups=2),
+    "kg8_d256_window": dict(B=2, q_len=1, Hq=16, Hkv=2, D=256, bt=16, seq_lens=[700, 150], window=300,
+                            scale=("tensor", 0.05), k_groups=8),
+    "kg4_mha": dict(B=2, q_len=1, Hq=4, Hkv=4, D=128, bt=16, seq_lens=[150, 61],
+                    scale=("per_head", 0.01, 0.1), k_groups=4),
+    "kg4_q4_mtp": dict(B=2, q_len=4, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[130, 44], window=50,
+                       scale=("per_head", 0.02, 0.1), sinks=True, k_groups=4),
 }
 
 # (case, flags, num_splits)

@@ -44,17 +44,22 @@ def _inputs(rng, T, Hkv, D, pad, specials):
 
 
 CASES = [
-    # T, Hkv, D, bt, num_blocks, pad, per_head
-    (37, 8, 128, 16, 5, 0, True),
-    (64, 4, 256, 64, 2, 24, False),
-    (100, 8, 64, 16, 10, 8, True),
-    (9, 2, 128, 1, 16, 0, True),
-    (1, 1, 64, 32, 1, 0, False),
+    # T, Hkv, D, bt, num_blocks, pad, per_head, k_groups
+    (37, 8, 128, 16, 5, 0, True, 1),
+    (64, 4, 256, 64, 2, 24, False, 1),
+    (100, 8, 64, 16, 10, 8, True, 1),
+    (9, 2, 128, 1, 16, 0, True, 1),
+    (1, 1, 64, 32, 1, 0, False, 1),
+    # K scales in groups along head_dim
+    (37, 8, 128, 16, 5, 0, True, 4),
+    (64, 4, 256, 64, 2, 24, False, 8),
+    (100, 8, 64, 16, 10, 8, True, 2),
+    (20, 2, 256, 16, 3, 0, True, 8),
 ]
 
 
-@pytest.mark.parametrize("T,Hkv,D,bt,nb,pad,per_head", CASES)
-def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head):
+@pytest.mark.parametrize("T,Hkv,D,bt,nb,pad,per_head,kg", CASES)
+def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head, kg):
     rng = np.random.default_rng(T * 7 + D)
     key = _inputs(rng, T, Hkv, D, pad, True)
     value = _inputs(rng, T, Hkv, D, pad, False)
@@ -71,15 +76,15 @@ def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head):
                 slots[i] = -1
             seen.add(sl)
     nsc = Hkv if per_head else 1
-    ks = rng.uniform(0.01, 0.2, size=nsc).astype(np.float32)
+    ks = rng.uniform(0.01, 0.2, size=nsc * kg).astype(np.float32)
     vs = rng.uniform(0.01, 0.2, size=nsc).astype(np.float32)
     k0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
     v0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
     kc, vc = torch.from_numpy(k0).cuda(), torch.from_numpy(v0).cuda()
     fp.cache_write(key, value, torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
-                   torch.from_numpy(vs).cuda(), kc, vc)
+                   torch.from_numpy(vs).cuda(), kc, vc, k_groups=kg)
     torch.cuda.synchronize()
-    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, k0, v0)
+    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, k0, v0, k_groups=kg)
     for got, want, name in ((kc.cpu().numpy(), want_k, "k"), (vc.cpu().numpy(), want_v, "v")):
         nan_w = np.isnan(oracle.E4M3_TABLE[want])
         assert np.array_equal(np.isnan(oracle.E4M3_TABLE[got]), nan_w), name
@@ -87,9 +92,10 @@ def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head):
         assert not diff.any(), (name, np.argwhere(diff)[:5], got[diff][:5], want[diff][:5])
 
 
-def test_writer_then_decode_round_trip():
+@pytest.mark.parametrize("kg", [1, 4])
+def test_writer_then_decode_round_trip(kg):
     # keys and values of two sequences written by the library, then read back
-    rng = np.random.default_rng(11)
+    rng = np.random.default_rng(11 + kg)
     B, Hq, Hkv, D, bt = 2, 16, 4, 128, 16
     lens = [300, 77]
     nb = sum((L + bt - 1) // bt for L in lens) + 3
@@ -104,22 +110,23 @@ def test_writer_then_decode_round_trip():
     T = len(slots)
     key = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(torch.bfloat16).cuda()
     value = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(torch.bfloat16).cuda()
-    ks = rng.uniform(0.02, 0.1, size=Hkv).astype(np.float32)
+    ks = rng.uniform(0.02, 0.1, size=Hkv * kg).astype(np.float32)
     vs = rng.uniform(0.02, 0.1, size=Hkv).astype(np.float32)
     zeros = np.zeros((nb, bt, Hkv, D), np.uint8)
     kc, vc = torch.from_numpy(zeros).cuda(), torch.from_numpy(zeros).cuda()
     slot_t = torch.tensor(slots, dtype=torch.int64).cuda()
     ks_t, vs_t = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
-    fp.cache_write(key, value, slot_t, ks_t, vs_t, kc, vc)
-    k_or, v_or = oracle.cache_write(_bits(key), _bits(value), np.array(slots), ks, vs, zeros, zeros)
+    fp.cache_write(key, value, slot_t, ks_t, vs_t, kc, vc, k_groups=kg)
+    k_or, v_or = oracle.cache_write(_bits(key), _bits(value), np.array(slots), ks, vs, zeros, zeros,
+                                    k_groups=kg)
     torch.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy(), k_or) and np.array_equal(vc.cpu().numpy(), v_or)
     q = torch.from_numpy(rng.standard_normal((B, 1, Hq, D)).astype(np.float32)).to(torch.bfloat16).cuda()
     sl = torch.tensor(lens, dtype=torch.int32).cuda()
     bt_t = torch.from_numpy(table).cuda()
-    out, lse = fp.decode(q, kc, vc, bt_t, sl, ks_t, vs_t, None, sm_scale=1 / np.sqrt(D))
+    out, lse = fp.decode(q, kc, vc, bt_t, sl, ks_t, vs_t, None, sm_scale=1 / np.sqrt(D), k_groups=kg)
     ro, rl = oracle.decode(q_bits=_bits(q), k_cache=k_or, v_cache=v_or, block_table=table,
                            seq_lens=np.array(lens, np.int32), k_scale=ks, v_scale=vs,
-                           sm_scale=1 / np.sqrt(D))
+                           sm_scale=1 / np.sqrt(D), k_groups=kg)
     o, l = to_host(out, lse)
     compare(o, l, ro, rl, label="cache_write -> decode")
