@@ -394,6 +394,21 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
   return o;
 }
 
+// Tiles [ts, te) of a split clipped to the keys that some query position in
+// qmin..qmax attends (positions L - q_len + q, each over its window).
+struct TileRange {
+  int ts, te;
+};
+__device__ __forceinline__ TileRange rows_tiles(const Params& p, int L, int qmin, int qmax, int ts,
+                                                int te) {
+  const int hi = L - p.q_len + qmax + 1;
+  const int lo = p.window > 0 ? max(0, L - p.q_len + qmin - p.window + 1) : 0;
+  TileRange r;
+  r.ts = max(ts, lo / kTileTokens);
+  r.te = min(te, (hi + kTileTokens - 1) / kTileTokens);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // FP8-MFMA partial kernel.
 //
@@ -457,7 +472,16 @@ partial_mfma_kernel(Params p) {
   const int d0 = w.half * DW;      // first dim of this wavefront's slice
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
-  const int ts = w.ts, te = w.te;
+  // The wavefront's rows (the same for every wavefront of the workgroup) and
+  // the query positions qmin..qmax they belong to.
+  const int r0 = PR == 2 ? 0 : w.rg * kRowsMfma;
+  const int r1 = PR == 2 ? p.rows - 1 : min(r0 + kRowsMfma, p.rows) - 1;
+  const int qmin = r0 / p.G, qmax = r1 / p.G;
+  // The split's tiles outside the keys some row attends are skipped: with
+  // many query rows per sequence (chunked prefill) a row group's causal
+  // range ends before the sequence does.
+  const TileRange tr = rows_tiles(p, L, qmin, qmax, w.ts, w.te);
+  const int ts = tr.ts, te = tr.te;
   const Row row = row_of(p, w.b, kvh, rlane, L);
   // With paired heads a lane's 32 query / output dims (of the wavefront's
   // 128) belong to one head: `mine` says whether it is this lane's row's.
@@ -510,14 +534,8 @@ partial_mfma_kernel(Params p) {
   // Keys every row of this wavefront attends: [ilo, ihi).  A tile inside it
   // needs no score masks; only the others ("edge" tiles: at most the first
   // two and last two of a sequence) are masked.
-  int ilo, ihi;
-  {
-    const int r0 = PR == 2 ? 0 : w.rg * kRowsMfma;
-    const int r1 = PR == 2 ? p.rows - 1 : min(r0 + kRowsMfma, p.rows) - 1;
-    const int qmin = r0 / p.G, qmax = r1 / p.G;
-    ihi = L - p.q_len + qmin + 1;
-    ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
-  }
+  const int ihi = L - p.q_len + qmin + 1;
+  const int ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
 
   uint32_t voff[4];
 #pragma unroll
@@ -810,7 +828,9 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   if (!w.active) return;  // uniform over the workgroup
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
-  const int ts = w.ts, te = w.te;
+  const int r0 = w.rg * RPG, r1 = min(r0 + RPG, p.rows) - 1;
+  const TileRange tr = rows_tiles(p, L, r0 / p.G, r1 / p.G, w.ts, w.te);
+  const int ts = tr.ts, te = tr.te;
 
   Row rows[RPG];
 #pragma unroll

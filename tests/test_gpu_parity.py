@@ -137,6 +137,16 @@ SMALL = {
                             scale=("tensor", 0.05), k_groups=8),
     "kg4_mha": dict(B=2, q_len=1, Hq=4, Hkv=4, D=128, bt=16, seq_lens=[150, 61],
                     scale=("per_head", 0.01, 0.1), k_groups=4),
+    # many query rows per sequence (chunked prefill, causal over the new
+    # tokens): a row group's tiles end where its last row's keys end
+    "prefill_q64": dict(B=2, q_len=64, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[64, 300], sinks=True),
+    "prefill_q128_window": dict(B=1, q_len=128, Hq=16, Hkv=4, D=64, bt=16, seq_lens=[500],
+                                window=100, scale=("per_head", 0.02, 0.1)),
+    "prefill_q16_d256": dict(B=2, q_len=16, Hq=8, Hkv=2, D=256, bt=64, seq_lens=[16, 1000],
+                             scale=("per_head", 0.02, 0.1), sinks=True),
+    "prefill_q512": dict(B=1, q_len=512, Hq=4, Hkv=1, D=128, bt=16, seq_lens=[1500]),
+    "prefill_q32_mha_kg": dict(B=2, q_len=32, Hq=4, Hkv=4, D=128, bt=32, seq_lens=[40, 233],
+                               window=64, k_groups=2, scale=("per_head", 0.02, 0.1)),
     "kg4_q4_mtp": dict(B=2, q_len=4, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[130, 44], window=50,
                        scale=("per_head", 0.02, 0.1), sinks=True, k_groups=4),
 }
