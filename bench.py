@@ -23,6 +23,10 @@ is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
 timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
 fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
+Two widenings are timed after the decode: the headline workload with K
+scales in four head_dim groups ("k_groups_variant"), and chunked prefill,
+q_len 16 to 512 new tokens over a paged context ("prefill", in algorithmic
+TFLOP/s against the dense FP8 peak).
 
 HBM traffic (roofline.traffic): four rocprofv3 --pmc passes, FETCH_SIZE and
 WRITE_SIZE over this workload and over `--calibrate-copy` (device copies of
@@ -86,7 +90,8 @@ def describe(wl):
     return (f"{wl.name}: B={wl.B} q_len={wl.q_len} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} bt={wl.bt} "
             f"seq_lens[min={int(seq.min())},max={int(seq.max())},sum={int(seq.sum())}] "
             f"window={wl.window} sinks={'yes' if wl.sinks is not None else 'no'} "
-            f"sm_scale={wl.sm_scale:.6g} k_scale={'per-kv-head' if wl.k_scale.size > 1 else 'per-tensor'}")
+            f"sm_scale={wl.sm_scale:.6g} k_scale={'per-kv-head' if wl.k_scale.size > wl.k_groups else 'per-tensor'}"
+            + (f" x {wl.k_groups} head_dim groups" if wl.k_groups > 1 else ""))
 
 
 def partial_kernel_name(plan, D):
@@ -118,15 +123,16 @@ def load_traffic(workload_name):
     return None if not h else int(h["read"] + h["write"])
 
 
-def measure(k, steps, warmup, log, use_graph=True):
+def measure(k, steps, warmup, log, use_graph=True, k_groups=1):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
     from workloads import make_config
 
     t_gen = time.time()
-    wl = make_config(k)
-    log(f"[bench] cfg{k}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
+    wl = make_config(k, k_groups=k_groups)
+    label = f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "")
+    log(f"[bench] {label}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
     dev = torch.device("cuda")
     kvb = kv_bytes(wl)
     copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / max(kvb, 1)))))
@@ -140,7 +146,7 @@ def measure(k, steps, warmup, log, use_graph=True):
     vs = torch.from_numpy(wl.v_scale).to(dev)
     sinks = None if wl.sinks is None else torch.from_numpy(wl.sinks).to(dev)
     shape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
-                         max_seq_len=int(wl.seq_lens.max()))
+                         max_seq_len=int(wl.seq_lens.max()), k_groups=wl.k_groups)
     plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
     nws = fp.fp8pa_workspace_bytes(shape)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
@@ -171,7 +177,7 @@ def measure(k, steps, warmup, log, use_graph=True):
     # timed: the same K steps captured once in a HIP graph and replayed, so
     # the GPU runs them back to back without Python launch gaps
     if not use_graph:
-        return _result(wl, k, kvb, copies, plan, eager_ms, eager_ms, wall_ms, wall_ms, False,
+        return _result(wl, label, kvb, copies, plan, eager_ms, eager_ms, wall_ms, wall_ms, False,
                        eager_ms, 0.0, log), wl
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -181,7 +187,7 @@ def measure(k, steps, warmup, log, use_graph=True):
     torch.cuda.synchronize()
     graph_ok = bool(torch.equal(out, eager_out))
     if not graph_ok:
-        log(f"[bench] cfg{k}: graph replay output differs from eager; reporting eager timing")
+        log(f"[bench] {label}: graph replay output differs from eager; reporting eager timing")
     torch.cuda.synchronize()
     # REPLAYS timed replays of the K steps: the step time is their median,
     # reported with the spread over replays
@@ -208,7 +214,8 @@ def measure(k, steps, warmup, log, use_graph=True):
     partial_ms = step_ms
     if plan["merge_launched"]:
         pshape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
-                              max_seq_len=int(wl.seq_lens.max()), flags=fp.FP8PA_FLAG_PARTIAL_ONLY)
+                              max_seq_len=int(wl.seq_lens.max()), flags=fp.FP8PA_FLAG_PARTIAL_ONLY,
+                              k_groups=wl.k_groups)
 
         def partial_only(i):
             kc, vc = pools[i % copies]
@@ -232,7 +239,7 @@ def measure(k, steps, warmup, log, use_graph=True):
         step(0)  # leave the outputs as one full step writes them
         torch.cuda.synchronize()
     merge_ms = max(step_ms - partial_ms, 0.0)
-    res = _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
+    res = _result(wl, label, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
                   partial_ms, merge_ms, log)
     res["spread"] = spread
     del pools, kc0, vc0
@@ -240,7 +247,7 @@ def measure(k, steps, warmup, log, use_graph=True):
     return res, wl
 
 
-def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
+def _result(wl, label, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
             partial_ms, merge_ms, log):
     res = dict(
         workload=wl.name,
@@ -261,7 +268,7 @@ def _result(wl, k, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms,
         tokens_per_s=wl.B * wl.q_len / (step_ms * 1e-3),
     )
     res["pct_peak"] = 100.0 * res["kv_gbps"] / PEAK_GBPS
-    log(f"[bench] cfg{k}: step {step_ms * 1e3:.1f} us (partial {partial_ms * 1e3:.1f} us, merge "
+    log(f"[bench] {label}: step {step_ms * 1e3:.1f} us (partial {partial_ms * 1e3:.1f} us, merge "
         f"{merge_ms * 1e3:.1f} us), KV {res['kv_gbps']:.0f} GB/s = {res['pct_peak']:.1f}% of peak, "
         f"{res['tokens_per_s']:.3g} tok/s, splits {plan['num_splits']}, copies {copies}")
     return res
@@ -344,6 +351,83 @@ def measure_writer(steps, log):
         log(f"[bench] writer {name}: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s read+write "
             f"({nbytes / t / 1e9 / PEAK_GBPS * 100:.1f}% of peak)")
         del g, key, value, kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+PREFILL_SHAPES = (
+    # name, B, q_len, Hq, Hkv, D, bt, context (seq_len, the chunk included)
+    ("chunk512_ctx32k", 2, 512, 32, 8, 128, 16, 32768),
+    ("chunk128_ctx8k", 8, 128, 32, 8, 128, 16, 8192),
+    ("chunk16_ctx8k", 16, 16, 32, 8, 128, 16, 8192),
+)
+
+
+def measure_prefill(log, steps=5):
+    """Chunked prefill through fp8pa_decode: q_len new tokens per sequence,
+    causal among themselves, over a paged E4M3 context.  MFMA-bound, so the
+    rate is algorithmic FLOP/s, 4 D per (query row, attended key) (q.K and
+    P.V, a multiply and an add each), against the dense FP8 peak; the
+    kernel issues twice that on the matrix cores (query and P each go in as
+    an E4M3 hi + lo pair).  Timed from graph replays like the decode."""
+    import torch
+
+    import decode_attention_paged_fp8pa_amd as fp
+    from workloads import make_workload
+
+    out = {}
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for name, B, ql, Hq, Hkv, D, bt, ctx in PREFILL_SHAPES:
+        wl = make_workload(B=B, q_len=ql, Hq=Hq, Hkv=Hkv, D=D, bt=bt, seq_lens=[ctx] * B, seed=17,
+                           poison=False, scale=("per_head", 0.02, 0.1), name=name)
+        flops = sum(4 * D * Hq * (ctx - ql + i + 1) for i in range(ql)) * B
+        dev = "cuda"
+        q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        kc = torch.from_numpy(wl.k_cache).to(dev)
+        vc = torch.from_numpy(wl.v_cache).to(dev)
+        btab = torch.from_numpy(wl.block_table).to(dev)
+        sl = torch.from_numpy(wl.seq_lens).to(dev)
+        ks = torch.from_numpy(wl.k_scale).to(dev)
+        vs = torch.from_numpy(wl.v_scale).to(dev)
+        shape = fp.shape_for(q, kc, btab, ks, vs, sm_scale=wl.sm_scale, max_seq_len=ctx)
+        plan = fp.fp8pa_plan(shape, cu)
+        nws = fp.fp8pa_workspace_bytes(shape)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+        o = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(tuple(wl.q_bits.shape[:3]), dtype=torch.float32, device=dev)
+
+        def step():
+            fp.fp8pa_decode(shape, q, kc, vc, btab, sl, ks, vs, None, o, lse, ws if nws else None, nws)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(REPLAYS):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps * 1e-3)
+        t = sorted(per)[len(per) // 2]
+        tflops = flops / t / 1e12
+        out[name] = {"workload": f"B={B} q_len={ql} Hq={Hq} Hkv={Hkv} D={D} bt={bt} seq_len={ctx}",
+                     "us": round(t * 1e6, 1), "algorithmic_flops": flops, "tflops": round(tflops, 1),
+                     "pct_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS * 100, 2),
+                     "variant": "mfma" if plan["variant"] == 1 else "dot",
+                     "num_splits": plan["num_splits"], "grid_wgs": plan["grid_wgs"]}
+        log(f"[bench] prefill {name}: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
+            f"({tflops / PEAK_FP8_TFLOPS * 100:.2f}% of dense FP8 peak), splits {plan['num_splits']}")
+        del g, kc, vc, q, ws
         torch.cuda.empty_cache()
     return out
 
@@ -522,6 +606,11 @@ def main():
         "algorithmic_bytes_per_launch": h["kv_bytes"],
     }
     writer = measure_writer(min(args.steps, 100), log)
+    # the headline workload with K scales in 4 head_dim groups per kv head
+    kg_res, kg_wl = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph,
+                            k_groups=4)
+    del kg_wl
+    prefill = measure_prefill(log)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head_wl, args.cpu_budget, log)
@@ -545,6 +634,13 @@ def main():
         "cpu_baseline": cpu,
         "copy_ceiling": ceiling,
         "writer": writer,
+        "k_groups_variant": {
+            "workload": kg_res["describe"], "step_us": round(kg_res["step_ms"] * 1e3, 2),
+            "partial_us": round(kg_res["partial_ms"] * 1e3, 2),
+            "kv_gbps": round(kg_res["kv_gbps"], 1), "pct_peak": round(kg_res["pct_peak"], 2),
+            "partial_kv_gbps": round(kg_res["partial_kv_gbps"], 1),
+        },
+        "prefill": prefill,
         "per_workload": {
             f"cfg{k}": {
                 "workload": r["describe"], "step_us": round(r["step_ms"] * 1e3, 2),

@@ -217,8 +217,9 @@ def make_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", poo
                     meta=dict(seed=seed, poison=poison), k_groups=kg)
 
 
-def make_config(k: int, seed: int | None = None, poison: bool = True) -> Workload:
-    """One of the five named workloads, seeded with 1000 + k by default."""
+def make_config(k: int, seed: int | None = None, poison: bool = True, k_groups: int = 1) -> Workload:
+    """One of the five named workloads, seeded with 1000 + k by default
+    (k_groups > 1: the same workload with K scales in head_dim groups)."""
     c = CONFIGS[k]
     seq = c["seq"]
     if seq[0] == "fixed":
@@ -231,4 +232,5 @@ def make_config(k: int, seed: int | None = None, poison: bool = True) -> Workloa
                          bt=c["bt"], seq_lens=seq_lens, seed=1000 + k if seed is None else seed,
                          table=c["table"], pool=c["pool"], scale=c["scale"],
                          window=c["window"], sinks=c["sinks"], sm_scale=c["sm_scale"],
-                         poison=poison, name=f"cfg{k}_{c['name']}")
+                         poison=poison, k_groups=k_groups,
+                         name=f"cfg{k}_{c['name']}" + (f"_kg{k_groups}" if k_groups > 1 else ""))
