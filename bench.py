@@ -98,7 +98,8 @@ def partial_kernel_name(plan, D):
     """The partial kernel a plan launches, as rocprofv3 names it."""
     if plan["variant"] == 1:
         pr = plan["heads_per_wave"]
-        return f"partial_mfma_kernel<{D * pr}, {plan['waves_per_head']}, {pr}>"
+        return (f"partial_mfma_kernel<{D * pr}, {plan['waves_per_head']}, {pr}, "
+                f"{plan['row_blocks']}, {plan['nontemporal_kv']}>")
     return f"partial_dot_kernel<{D}>"
 
 

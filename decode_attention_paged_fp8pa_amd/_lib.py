@@ -94,6 +94,8 @@ class PlanInfo(ctypes.Structure):
         ("grid_wgs", ctypes.c_int32),
         ("merge_launched", ctypes.c_int32),
         ("heads_per_wave", ctypes.c_int32),
+        ("row_blocks", ctypes.c_int32),
+        ("nontemporal_kv", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
         ("workspace_lse_offset", ctypes.c_uint64),
     ]

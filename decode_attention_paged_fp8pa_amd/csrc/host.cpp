@@ -84,10 +84,6 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   } else {
     p.variant = (mfma_ok && p.rows >= 3) ? kVariantMfma : kVariantDot;
   }
-  p.rpg = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;
-  p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
-  const int32_t rows_eff = p.rows < p.rpg ? p.rows : p.rpg;
-
   // A workgroup takes adjacent kv heads, up to 8 wavefronts: at 8 kv heads
   // per page token slot it reads whole token slots, so each page comes from
   // HBM in one pass (two workgroups reading halves of a page at different
@@ -99,6 +95,21 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // two kv heads per wavefront (one 128-byte line per token, all 16 MFMA
   // columns in use); hg then counts head pairs.
   p.pr = (p.variant == kVariantMfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
+  // More than 16 query rows per kv head (chunked prefill, wide MTP): a
+  // wavefront carries two blocks of 16 rows over the same K/V registers, so
+  // a tile's loads and V transposes serve both.  (Four blocks need more
+  // than the 256 registers MFMA operands can use and measured slower.)
+  p.nb = 1;
+  if (p.variant == kVariantMfma && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
+  p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;
+  p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
+  const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;
+  const int32_t rows_eff = p.rows < rows_unit ? p.rows : rows_unit;
+  // Non-temporal K/V loads keep streamed bytes from pushing reused ones out
+  // of the caches; they pay only when no other wavefront reads the same
+  // bytes (one row group) and a wavefront reads whole 128-byte lines.
+  p.nt = (p.variant == kVariantMfma && p.row_groups == 1 && p.D * p.pr / p.ds >= 128) ? 1 : 0;
+
   const int32_t units = p.Hkv / p.pr;  // wavefront head units per sequence
   const int32_t max_hg = kMaxWgWaves / p.ds;
   p.hg = 1;
@@ -126,7 +137,8 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // Wavefronts of the partial kernel one compute unit holds at once: the
   // MFMA kernel's registers allow 4 per SIMD at D = 64 and 2 otherwise
   // (head_dim 256 is split over two wavefronts); the dot kernel's 2.
-  const int64_t waves_per_cu = (p.variant == kVariantMfma && p.D == 64 && p.pr == 1) ? 16 : 8;
+  const int64_t waves_per_cu =
+      (p.variant == kVariantMfma && p.D == 64 && p.pr == 1 && p.nb == 1) ? 16 : 8;
   const int64_t target_waves = int64_t(cu_count) * waves_per_cu;
   int64_t target_items = target_waves / waves_per_item;
   if (target_items < 1) target_items = 1;
@@ -229,6 +241,8 @@ fp8pa_status fp8pa_plan(const fp8pa_shape* shape, int32_t cu_count, fp8pa_plan_i
   out->heads_per_wg = p.hg * p.pr;
   out->waves_per_head = p.ds;
   out->heads_per_wave = p.pr;
+  out->row_blocks = p.variant == fp8pa::kVariantMfma ? p.nb : 1;
+  out->nontemporal_kv = p.nt;
   out->rows_per_group = p.rpg;
   out->row_groups = p.row_groups;
   out->grid_wgs = p.grid_wgs;

@@ -428,12 +428,20 @@ __device__ __forceinline__ TileRange rows_tiles(const Params& p, int L, int qmin
 // 8-15 those of head 2 g + 1 the other way round, so each row's scores see
 // only its own head's keys, and of the output only its own head's dims are
 // kept.  All 16 MFMA columns do work and every load reads whole lines.
-template <int D, int DS, int PR>
+//
+// NB = 2 (more than 16 query rows per kv head: chunked prefill, wide MTP):
+// a wavefront takes two blocks of 16 rows over the same K/V registers, so
+// each tile's loads and V transposes serve 32 rows.
+//
+// NT selects non-temporal K/V loads: right when each K/V byte is read by one
+// wavefront (one row group), wrong when several row groups re-read it.
+template <int D, int DS, int PR, int NB, int NT>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
-__attribute__((amdgpu_waves_per_eu(D / DS == 64 ? 4 : D / DS == 128 ? 2 : 1, 8))) void
+__attribute__((amdgpu_waves_per_eu(NB == 1 && D / DS == 64 ? 4 : D / DS <= 128 ? 2 : 1, 8))) void
 partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
   static_assert(PR == 1 || (PR == 2 && D == 128 && DS == 1), "paired heads");
+  static_assert(NB == 1 || (DS == 1 && PR == 1), "row blocks need one whole head per wavefront");
   constexpr int DH = D / PR;       // head_dim of the output rows
   constexpr int DW = D / DS;       // head_dim slice of this wavefront
   constexpr int S = DW / 16;       // V bytes per lane per token
@@ -441,7 +449,7 @@ partial_mfma_kernel(Params p) {
   constexpr int KSTEPS = DW / 32;  // QK k-steps of 32 dims
   constexpr int KW = KB / 4;       // K dwords per lane per group
   constexpr int SW = S / 4;        // V dwords per lane per token
-  constexpr int AUX = DW >= 128 ? kLoadNT : 0;  // K/V load cache policy
+  constexpr int AUX = NT ? kLoadNT : 0;  // K/V load cache policy
   // Partial scores of the two wavefronts that share a kv head (DS = 2):
   // [wavefront][tile parity][lane][2 x f32x4], for the at most kMaxWgWaves
   // wavefronts of a workgroup.
@@ -451,10 +459,12 @@ partial_mfma_kernel(Params p) {
   const int n = lane & 15;
   const int qd = lane >> 4;
   Work w = work_head(p, DS);
-  // This lane's row: kv head kvh, row r of that head's rows.
+  // This lane's rows: kv head kvh, row rlane[b] of that head's rows in block b.
   const int kvh = PR == 2 ? 2 * w.g + (n >> 3) : w.g;
-  const int rlane = PR == 2 ? (n & 7) : w.rg * kRowsMfma + n;
-  // Loads that need only the kv head and the row go first, so that their
+  int rlane[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rlane[b] = PR == 2 ? (n & 7) : (w.rg * NB + b) * kRowsMfma + n;
+  // Loads that need only the kv head and the rows go first, so that their
   // round trips overlap the item's.
   // The K scale of the dims this lane stages: its kv head's (or the
   // tensor's), or with scale groups along head_dim the group's; a lane's KB
@@ -462,10 +472,14 @@ partial_mfma_kernel(Params p) {
   const int qdim = w.half * DW + KB * (PR == 2 ? (qd & 1) : qd);
   const float ks = p.k_scale[(p.k_per_head ? kvh * p.k_groups : 0) + (qdim >> p.kg_shift)];
   const float vs = p.v_scale[p.v_per_head ? kvh : 0];
-  float sink2 = -INFINITY;
-  if (p.sinks && p.direct && rlane < p.rows) {
-    const int qi = rlane / p.G;
-    sink2 = p.sinks[kvh * p.G + (rlane - qi * p.G)] * kLog2e;
+  float sink2[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    sink2[b] = -INFINITY;
+    if (p.sinks && p.direct && rlane[b] < p.rows) {
+      const int qi = rlane[b] / p.G;
+      sink2[b] = p.sinks[kvh * p.G + (rlane[b] - qi * p.G)] * kLog2e;
+    }
   }
   work_item(p, w);
   if (!w.active) return;  // uniform over the workgroup
@@ -474,33 +488,44 @@ partial_mfma_kernel(Params p) {
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
   // The wavefront's rows (the same for every wavefront of the workgroup) and
   // the query positions qmin..qmax they belong to.
-  const int r0 = PR == 2 ? 0 : w.rg * kRowsMfma;
-  const int r1 = PR == 2 ? p.rows - 1 : min(r0 + kRowsMfma, p.rows) - 1;
+  const int r0 = PR == 2 ? 0 : w.rg * NB * kRowsMfma;
+  const int r1 = PR == 2 ? p.rows - 1 : min(r0 + NB * kRowsMfma, p.rows) - 1;
   const int qmin = r0 / p.G, qmax = r1 / p.G;
   // The split's tiles outside the keys some row attends are skipped: with
   // many query rows per sequence (chunked prefill) a row group's causal
   // range ends before the sequence does.
   const TileRange tr = rows_tiles(p, L, qmin, qmax, w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
-  const Row row = row_of(p, w.b, kvh, rlane, L);
+  Row row[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) row[b] = row_of(p, w.b, kvh, rlane[b], L);
   // With paired heads a lane's 32 query / output dims (of the wavefront's
   // 128) belong to one head: `mine` says whether it is this lane's row's.
   const bool mine = PR == 1 || (qd >> 1) == (n >> 3);
 
-  if (ts >= te && !p.direct && w.half == 0 && row.valid && qd == 0)
-    p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
-  if (ts >= te && !p.direct) return;
+  if (ts >= te && !p.direct) {
+    if (w.half == 0 && qd == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (row[b].valid) p.part_lse[row[b].out_row * p.num_splits + w.split] = -INFINITY;
+    }
+    return;
+  }
 
-  long qhi[KSTEPS], qlo[KSTEPS];  // the query row in E4M3 hi + lo parts (set below)
-  float cr;                       // score scale into log2 units
+  long qhi[NB][KSTEPS], qlo[NB][KSTEPS];  // query rows in E4M3 hi + lo parts (set below)
+  float cr[NB];                           // score scales into log2 units
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
   // value vector is zero when this split writes the final output.
-  float m = sink2;
-  float lsum = (qd == 0 && sink2 > -INFINITY) ? exp2_fast(kPShift) : 0.f;
-  f32x4 O[S];
+  float m[NB], lsum[NB];
+  f32x4 O[NB][S];
 #pragma unroll
-  for (int e = 0; e < S; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) {
+    m[b] = sink2[b];
+    lsum[b] = (qd == 0 && sink2[b] > -INFINITY) ? exp2_fast(kPShift) : 0.f;
+#pragma unroll
+    for (int e = 0; e < S; ++e) O[b][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int tok = p.tok_stride;
   const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D + d0;
@@ -522,14 +547,16 @@ partial_mfma_kernel(Params p) {
     const bool live = tt < te && gk < uhi && gk + 16 > ulo;
     tab[g] = live ? btab[gk >> p.bt_shift] : 0;
   }
-  // The query row's raw bf16 bits; converted after the first tiles' loads
+  // The query rows' raw bf16 bits; converted after the first tiles' loads
   // are issued, so the two round trips overlap.
-  u32x4 qraw[KB / 8];
-  {
-    const uint16_t* qrow = p.q + row.out_row * DH + d0 + KB * (PR == 2 ? (qd & 1) : qd);
+  u32x4 qraw[NB][KB / 8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint16_t* qrow = p.q + row[b].out_row * DH + d0 + KB * (PR == 2 ? (qd & 1) : qd);
 #pragma unroll
     for (int i = 0; i < KB / 8; ++i)
-      qraw[i] = (row.valid && mine) ? *reinterpret_cast<const u32x4*>(qrow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+      qraw[b][i] = (row[b].valid && mine) ? *reinterpret_cast<const u32x4*>(qrow + 8 * i)
+                                          : u32x4{0u, 0u, 0u, 0u};
   }
   // Keys every row of this wavefront attends: [ilo, ihi).  A tile inside it
   // needs no score masks; only the others ("edge" tiles: at most the first
@@ -570,115 +597,130 @@ partial_mfma_kernel(Params p) {
   };
 
   // One tile: S^T = K Q^T, mask, online softmax with a lazy reference max,
-  // P = hi + lo E4M3 parts, O^T += V^T P^T.
+  // P = hi + lo E4M3 parts, O^T += V^T P^T.  The V^T operands are built
+  // once and, with the K operands, serve every row block, which then runs
+  // start to finish before the next (one block's temporaries live at a time).
   auto compute_tile = [&](int tt, TileRegs& r) {
     const int kb = tt * kTileTokens;
     const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      const long ka = as_long(r.k[0][2 * c], r.k[0][2 * c + 1]);
-      const long kbv = as_long(r.k[1][2 * c], r.k[1][2 * c + 1]);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qhi[c], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[c], sb, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[c], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[c], sb, 0, 0, 0);
-    }
-    // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc (one
-    // head_dim slice per wavefront), or, when two wavefronts split head_dim,
-    // the sum of both slices' scaled scores exchanged through LDS.
-    float sv[8];
-    float csc = cr;
-    if constexpr (DS == 2) {
-      const int parity = (tt - ts) & 1;
-      const int wv = int(threadIdx.x >> 6);
-      f32x4* mine = &xch[((wv * 2 + parity) * 64 + lane) * 2];
-      mine[0] = sa * cr;
-      mine[1] = sb * cr;
-      __syncthreads();
-      const f32x4* other = &xch[(((wv ^ 1) * 2 + parity) * 64 + lane) * 2];
-      const f32x4 oa = other[0], ob = other[1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[j] = sa[j] * cr + oa[j];
-        sv[j + 4] = sb[j] * cr + ob[j];
-      }
-      csc = 1.f;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[j] = sa[j];
-        sv[j + 4] = sb[j];
-      }
-    }
     if (edge) {
-      // A token this lane's row does not attend scores -inf, and the V bytes
-      // of a token outside the sequence's attended span (read whole with its
-      // group, possibly NaN codes) become 0, since P = 0 times NaN is NaN.
+      // The V bytes of a token outside the sequence's attended span (read
+      // whole with its group, possibly NaN codes) become 0, since P = 0
+      // times NaN is NaN.
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-        sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
         const bool in_span = key >= ulo && key < uhi;
 #pragma unroll
         for (int e = 0; e < SW; ++e) r.v[j][e] = in_span ? r.v[j][e] : 0u;
       }
     }
-    float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    ms = max_over_groups(ms);
-    const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
-    // Lazy reference max: move m only when this tile exceeds it by more than
-    // kLazy (log2 units), so most tiles skip the O rescale; P stays
-    // <= 2^(kLazy + kPShift).
-    const bool bump = mx > m + kLazy;
-    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
-      const float mnew = bump ? mx : m;
-      const float alpha = bump ? exp2_fast(m - mnew) : 1.f;
-      lsum *= alpha;
-#pragma unroll
-      for (int e = 0; e < S; ++e) O[e] *= alpha;
-      m = mnew;
-    }
-    const float noff = kPShift - (m == -INFINITY ? 0.f : m);
-    float pj[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
-    lsum += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
-
-    // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
-    // which short, peaked rows need (one E4M3 P alone errs by up to 2^-4).
-    uint32_t p0 = 0, p1 = 0, r0 = 0, r1 = 0;
-    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0], pj[1], p0, false);
-    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2], pj[3], p0, true);
-    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4], pj[5], p1, false);
-    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6], pj[7], p1, true);
-    {
-      const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, false);
-      const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, true);
-      const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, false);
-      const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, true);
-      r0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0] - d0.x, pj[1] - d0.y, r0, false);
-      r0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2] - d1.x, pj[3] - d1.y, r0, true);
-      r1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4] - d2.x, pj[5] - d2.y, r1, false);
-      r1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6] - d3.x, pj[7] - d3.y, r1, true);
-    }
-    const long P = as_long(p0, p1);
-    const long Plo = as_long(r0, r1);
-
     // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
+    long vt[S];
 #pragma unroll
     for (int wd = 0; wd < SW; ++wd) {
       uint32_t lo4[4], hi4[4];
       transpose4x4(r.v[0][wd], r.v[1][wd], r.v[2][wd], r.v[3][wd], lo4);
       transpose4x4(r.v[4][wd], r.v[5][wd], r.v[6][wd], r.v[7][wd], hi4);
 #pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) {
-        const int e = 4 * wd + x4;
-        const long vt = as_long(lo4[x4], hi4[x4]);
-        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt, P, O[e], 0, 0, 0);
-        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt, Plo, O[e], 0, 0, 0);
+      for (int x4 = 0; x4 < 4; ++x4) vt[4 * wd + x4] = as_long(lo4[x4], hi4[x4]);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const long ka = as_long(r.k[0][2 * c], r.k[0][2 * c + 1]);
+        const long kbv = as_long(r.k[1][2 * c], r.k[1][2 * c + 1]);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qhi[b][c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[b][c], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[b][c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[b][c], sb, 0, 0, 0);
       }
+      // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc
+      // (one head_dim slice per wavefront), or, when two wavefronts split
+      // head_dim, the sum of both slices' scaled scores exchanged through LDS.
+      float sv[8];
+      float csc = cr[b];
+      if constexpr (DS == 2) {
+        const int parity = (tt - ts) & 1;
+        const int wv = int(threadIdx.x >> 6);
+        f32x4* own = &xch[((wv * 2 + parity) * 64 + lane) * 2];
+        own[0] = sa * csc;
+        own[1] = sb * csc;
+        __syncthreads();
+        const f32x4* other = &xch[(((wv ^ 1) * 2 + parity) * 64 + lane) * 2];
+        const f32x4 oa = other[0], ob = other[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[j] = sa[j] * csc + oa[j];
+          sv[j + 4] = sb[j] * csc + ob[j];
+        }
+        csc = 1.f;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[j] = sa[j];
+          sv[j + 4] = sb[j];
+        }
+      }
+      if (edge) {
+        // a token this row does not attend scores -inf
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+          sv[j] = (key >= row[b].klo && key < row[b].khi) ? sv[j] : -INFINITY;
+        }
+      }
+      float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      ms = max_over_groups(ms);
+      const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
+      // Lazy reference max: move m only when this tile exceeds it by more
+      // than kLazy (log2 units), so most tiles skip the O rescale; P stays
+      // <= 2^(kLazy + kPShift).
+      const bool bump = mx > m[b] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+        const float mnew = bump ? mx : m[b];
+        const float alpha = bump ? exp2_fast(m[b] - mnew) : 1.f;
+        lsum[b] *= alpha;
+#pragma unroll
+        for (int e = 0; e < S; ++e) O[b][e] *= alpha;
+        m[b] = mnew;
+      }
+      const float noff = kPShift - (m[b] == -INFINITY ? 0.f : m[b]);
+      float pj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
+      lsum[b] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+
+      // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
+      // which short, peaked rows need (one E4M3 P alone errs by up to 2^-4).
+      uint32_t p0 = 0, p1 = 0, q0 = 0, q1 = 0;
+      p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0], pj[1], p0, false);
+      p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2], pj[3], p0, true);
+      p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4], pj[5], p1, false);
+      p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6], pj[7], p1, true);
+      {
+        const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, false);
+        const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, true);
+        const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, false);
+        const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, true);
+        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0] - d0.x, pj[1] - d0.y, q0, false);
+        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2] - d1.x, pj[3] - d1.y, q0, true);
+        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4] - d2.x, pj[5] - d2.y, q1, false);
+        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6] - d3.x, pj[7] - d3.y, q1, true);
+      }
+      const long P = as_long(p0, p1);
+      const long Plo = as_long(q0, q1);
+#pragma unroll
+      for (int e = 0; e < S; ++e) {
+        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt[e], P, O[b][e], 0, 0, 0);
+        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt[e], Plo, O[b][e], 0, 0, 0);
+      }
+      // keep the scheduler from interleaving blocks (their temporaries would
+      // all be live at once)
+      if constexpr (NB > 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Two register buffers in turn: while one tile computes, the next tile's
@@ -689,26 +731,25 @@ partial_mfma_kernel(Params p) {
   load_tile(ts, ta, 0);
   load_tile(ts + 1, tb, 1);
 
-  // ---- stage the query row: per-row power-of-two scale, E4M3 hi + lo parts
-  {
-    float qf[KB];
-    {
+  // ---- stage the query rows: per-row power-of-two scale, E4M3 hi + lo parts
+  // One K scale per head goes into the score scale; group scales differ
+  // along the row, so each lane folds its own into its query dims.
+  const bool grouped = p.k_groups > 1;
 #pragma unroll
-      for (int i = 0; i < KB / 8; ++i) {
-        const u32x4 v = qraw[i];
-        qf[8 * i + 0] = bf16_lo(v.x);
-        qf[8 * i + 1] = bf16_hi(v.x);
-        qf[8 * i + 2] = bf16_lo(v.y);
-        qf[8 * i + 3] = bf16_hi(v.y);
-        qf[8 * i + 4] = bf16_lo(v.z);
-        qf[8 * i + 5] = bf16_hi(v.z);
-        qf[8 * i + 6] = bf16_lo(v.w);
-        qf[8 * i + 7] = bf16_hi(v.w);
-      }
+  for (int b = 0; b < NB; ++b) {
+    float qf[KB];
+#pragma unroll
+    for (int i = 0; i < KB / 8; ++i) {
+      const u32x4 v = qraw[b][i];
+      qf[8 * i + 0] = bf16_lo(v.x);
+      qf[8 * i + 1] = bf16_hi(v.x);
+      qf[8 * i + 2] = bf16_lo(v.y);
+      qf[8 * i + 3] = bf16_hi(v.y);
+      qf[8 * i + 4] = bf16_lo(v.z);
+      qf[8 * i + 5] = bf16_hi(v.z);
+      qf[8 * i + 6] = bf16_lo(v.w);
+      qf[8 * i + 7] = bf16_hi(v.w);
     }
-    // One K scale per head goes into the score scale below; group scales
-    // differ along the row, so each lane folds its own into its query dims.
-    const bool grouped = p.k_groups > 1;
     if (grouped) {
 #pragma unroll
       for (int i = 0; i < KB; ++i) qf[i] *= ks;
@@ -725,12 +766,12 @@ partial_mfma_kernel(Params p) {
       se = min(max(7 - e, -120), 120);
     }
     const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-    cr = p.sm_scale * (grouped ? 1.f : ks) * kLog2e / qs;
+    float c0 = p.sm_scale * (grouped ? 1.f : ks) * kLog2e / qs;
     // Scores are scaled as fma(S, cr, .) with cr > 0, so a -inf mask stays
     // -inf: a negative scale's sign moves into the query, and a zero scale
     // becomes a tiny positive one (its scores stay ~0).
-    const float qsign = cr < 0.f ? -qs : qs;
-    cr = fmaxf(fabsf(cr), 1e-30f);
+    const float qsign = c0 < 0.f ? -qs : qs;
+    cr[b] = fmaxf(fabsf(c0), 1e-30f);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       float x[8];
@@ -749,11 +790,10 @@ partial_mfma_kernel(Params p) {
       l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x, x[3] - d1.y, l0, true);
       l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x, x[5] - d2.y, l1, false);
       l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
-      qhi[c] = as_long(h0, h1);
-      qlo[c] = as_long(l0, l1);
+      qhi[b][c] = as_long(h0, h1);
+      qlo[b][c] = as_long(l0, l1);
     }
   }
-
 
   // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {
@@ -765,47 +805,54 @@ partial_mfma_kernel(Params p) {
   }
 
   // ---- epilogue: l over the 4 lane groups, normalise, write
-  lsum += xor_shfl(lsum, 16);
-  lsum += xor_shfl(lsum, 32);
-  if (!row.valid) return;
-  const bool empty = !(lsum > 0.f);
-  const float inv = empty ? 0.f : vs / lsum;
-  const float lse = empty ? -INFINITY : (m + log2_fast(lsum) - kPShift) * kLn2;
-  // O[e][i] is output dim S * (4 qd + i) + e of this lane's row (with paired
-  // heads: of the wavefront's 128, the row's own 64 start at 64 * (n >> 3)).
+  // O[b][e][i] is output dim S * (4 qd + i) + e of this lane's row in block
+  // b (with paired heads: of the wavefront's 128, the row's own 64 start at
+  // 64 * (n >> 3)).
   const int dlane = PR == 2 ? S * 4 * (qd & 1) : S * 4 * qd;
-  if (p.direct) {
-    uint16_t* orow = p.out + row.out_row * DH + d0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t pk[S / 2];
-#pragma unroll
-      for (int e = 0; e < S; e += 2) pk[e / 2] = pack_bf16x2(O[e][i] * inv, O[e + 1][i] * inv);
-      uint16_t* dst = orow + dlane + S * i;
-      if (!mine) continue;
-      if constexpr (S == 4) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
-      } else {
-#pragma unroll
-        for (int v = 0; v < S / 8; ++v)
-          reinterpret_cast<u32x4*>(dst)[v] = u32x4{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
-      }
-    }
-    if (p.lse && qd == 0 && w.half == 0) p.lse[row.out_row] = lse;
-  } else {
-    const size_t slot = row.out_row * p.num_splits + w.split;
-    if (!empty && mine) {
-      float* prow = p.part_o + slot * DH + d0;
+  for (int b = 0; b < NB; ++b) {
+    float l = lsum[b];
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    if (!row[b].valid) continue;
+    const bool empty = !(l > 0.f);
+    const float inv = empty ? 0.f : vs / l;
+    const float lse = empty ? -INFINITY : (m[b] + log2_fast(l) - kPShift) * kLn2;
+    if (p.direct) {
+      uint16_t* orow = p.out + row[b].out_row * DH + d0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float* dst = prow + dlane + S * i;
+        uint32_t pk[S / 2];
 #pragma unroll
-        for (int v = 0; v < S / 4; ++v)
-          reinterpret_cast<f32x4*>(dst)[v] =
-              f32x4{O[4 * v][i] * inv, O[4 * v + 1][i] * inv, O[4 * v + 2][i] * inv, O[4 * v + 3][i] * inv};
+        for (int e = 0; e < S; e += 2)
+          pk[e / 2] = pack_bf16x2(O[b][e][i] * inv, O[b][e + 1][i] * inv);
+        uint16_t* dst = orow + dlane + S * i;
+        if (!mine) continue;
+        if constexpr (S == 4) {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+        } else {
+#pragma unroll
+          for (int v = 0; v < S / 8; ++v)
+            reinterpret_cast<u32x4*>(dst)[v] =
+                u32x4{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
+        }
       }
+      if (p.lse && qd == 0 && w.half == 0) p.lse[row[b].out_row] = lse;
+    } else {
+      const size_t slot = row[b].out_row * p.num_splits + w.split;
+      if (!empty && mine) {
+        float* prow = p.part_o + slot * DH + d0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* dst = prow + dlane + S * i;
+#pragma unroll
+          for (int v = 0; v < S / 4; ++v)
+            reinterpret_cast<f32x4*>(dst)[v] = f32x4{O[b][4 * v][i] * inv, O[b][4 * v + 1][i] * inv,
+                                                     O[b][4 * v + 2][i] * inv, O[b][4 * v + 3][i] * inv};
+        }
+      }
+      if (qd == 0 && w.half == 0) p.part_lse[slot] = lse;
     }
-    if (qd == 0 && w.half == 0) p.part_lse[slot] = lse;
   }
 }
 
@@ -1199,13 +1246,34 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 template <int D>
 hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
-  if (pl.variant == kVariantMfma)
-    if (D == 64 && pl.pr == 2)
-      partial_mfma_kernel<128, 1, 2><<<grid, block, 0, st>>>(prm);
-    else
-      partial_mfma_kernel<D, (D == 256 ? 2 : 1), 1><<<grid, block, 0, st>>>(prm);
-  else
+  if (pl.variant != kVariantMfma) {
     partial_dot_kernel<D><<<grid, block, 0, st>>>(prm);
+  } else if constexpr (D == 64) {
+    // non-temporal loads only where a wavefront reads whole lines (paired heads)
+    if (pl.pr == 2)
+      partial_mfma_kernel<128, 1, 2, 1, 1><<<grid, block, 0, st>>>(prm);
+    else if (pl.nb == 2)
+      partial_mfma_kernel<64, 1, 1, 2, 0><<<grid, block, 0, st>>>(prm);
+    else
+      partial_mfma_kernel<64, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+  } else if constexpr (D == 128) {
+    if (pl.nb == 2) {
+      if (pl.nt)
+        partial_mfma_kernel<128, 1, 1, 2, 1><<<grid, block, 0, st>>>(prm);
+      else
+        partial_mfma_kernel<128, 1, 1, 2, 0><<<grid, block, 0, st>>>(prm);
+    } else {
+      if (pl.nt)
+        partial_mfma_kernel<128, 1, 1, 1, 1><<<grid, block, 0, st>>>(prm);
+      else
+        partial_mfma_kernel<128, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+    }
+  } else {
+    if (pl.nt)
+      partial_mfma_kernel<256, 2, 1, 1, 1><<<grid, block, 0, st>>>(prm);
+    else
+      partial_mfma_kernel<256, 2, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+  }
   return hipGetLastError();
 }
 

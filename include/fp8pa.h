@@ -130,6 +130,11 @@ typedef struct fp8pa_plan_info {
                                at most 8 query rows per kv head, else 1); a
                                workgroup has heads_per_wg / heads_per_wave *
                                waves_per_head wavefronts */
+  int32_t row_blocks;       /* 16-row MFMA blocks one wavefront carries over the same
+                               K/V registers (1, or 2 for more than 16 query
+                               rows per kv head); rows_per_group = 16 * row_blocks */
+  int32_t nontemporal_kv;   /* 1 when K/V loads bypass cache retention: each byte
+                               is read by one wavefront (row_groups == 1) */
   uint64_t workspace_bytes; /* bytes fp8pa_decode needs in `workspace` */
   uint64_t workspace_lse_offset; /* byte offset of the partial LSE block in the
                                     workspace; the partial outputs start at 0.
