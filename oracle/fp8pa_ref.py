@@ -92,18 +92,21 @@ def attended_range(seq_len: int, q_len: int, i: int, window: int) -> tuple[int, 
 
 
 def _gather(cache: np.ndarray, block_table_row: np.ndarray, g: int, ts: np.ndarray,
-            scale) -> np.ndarray:
+            scale, kv_layout: str = "NHD") -> np.ndarray:
     """Dequantised rows [len(ts), D] of kv head g at logical positions ts.
 
     Token t of the sequence lives in page block_table_row[t // bt] at slot
     t % bt [P4 writer index arithmetic]; the value is decode(code) * scale [P4],
-    `scale` one number or one per head_dim element.  Only the table entries
-    of the positions asked for are read.
+    `scale` one number or one per head_dim element.  A page is token-major
+    ("NHD": [bt, Hkv, D]) or head-major ("HND": [Hkv, bt, D], [P4] gist,
+    NVFP4 KV writer: head stride block_size * dim, token stride dim).  Only
+    the table entries of the positions asked for are read.
     """
-    bt = cache.shape[1]
+    hnd = kv_layout == "HND"
+    bt = cache.shape[2] if hnd else cache.shape[1]
     pages = block_table_row[ts // bt].astype(np.int64)
     slots = ts % bt
-    codes = cache[pages, slots, g, :]
+    codes = cache[pages, g, slots, :] if hnd else cache[pages, slots, g, :]
     return E4M3_TABLE[codes] * np.asarray(scale, dtype=np.float64)
 
 
@@ -146,13 +149,14 @@ def _softmax_rows(scores: np.ndarray, sink: float | None):
 
 def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
            sinks=None, window=0, sm_scale=None, rows=None, key_range=None,
-           key_chunk=16384, k_groups=1):
+           key_chunk=16384, k_groups=1, kv_layout="NHD"):
     """Reference paged decode attention [P1 title/summary], float64.
 
     Arguments (numpy arrays, as the library receives them):
       q_bits      uint16 [B, q_len, Hq, D]  bf16 bit patterns of the queries
-      k_cache     uint8  [num_blocks, bt, Hkv, D]  E4M3 codes (token-major pages)
-      v_cache     uint8  [num_blocks, bt, Hkv, D]
+      k_cache     uint8  [num_blocks, bt, Hkv, D]  E4M3 codes (token-major pages),
+                  or [num_blocks, Hkv, bt, D] with kv_layout="HND" (head-major)
+      v_cache     uint8  the same shape and layout as k_cache
       block_table int32  [B, max_blocks]  page of each logical page index
       seq_lens    int32  [B]  tokens in each sequence, the q_len new ones included
       k_scale, v_scale  float32 [1] (per tensor) or [Hkv] (per kv head); with
@@ -174,7 +178,8 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
     """
     q_bits = np.asarray(q_bits)
     B, q_len, Hq, D = q_bits.shape
-    Hkv = k_cache.shape[2]
+    assert kv_layout in ("NHD", "HND")
+    Hkv = k_cache.shape[1] if kv_layout == "HND" else k_cache.shape[2]
     assert Hq % Hkv == 0, "Hq must be a multiple of Hkv"
     G = Hq // Hkv
     if sm_scale is None:
@@ -218,7 +223,7 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
         scores = np.empty((len(members), n_keys), dtype=np.float64)
         for c0 in range(u_lo, u_hi, key_chunk):
             ts = np.arange(c0, min(c0 + key_chunk, u_hi))
-            kf = _gather(k_cache, block_table[b], g, ts, ks)
+            kf = _gather(k_cache, block_table[b], g, ts, ks, kv_layout)
             scores[:, c0 - u_lo:c0 - u_lo + len(ts)] = sm_scale * (qmat @ kf.T)
         # Pass 2: exact softmax weights of each row over its own key range.
         weights = np.zeros_like(scores)
@@ -238,7 +243,7 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
             live = np.flatnonzero(wchunk.any(axis=0))
             if live.size == 0:
                 continue
-            vf = _gather(v_cache, block_table[b], g, ts[live], vs)
+            vf = _gather(v_cache, block_table[b], g, ts[live], vs, kv_layout)
             acc += wchunk[:, live] @ vf
         for j, n in enumerate(members):
             out[n] = acc[j]

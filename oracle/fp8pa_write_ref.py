@@ -71,16 +71,22 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_cache, v_cache,
-                k_groups=1):
+                k_groups=1, kv_layout="NHD"):
     """Returns copies of (k_cache, v_cache) [num_blocks, bt, Hkv, D] (uint8)
     with every token t whose slot is valid written: element (h, d) of token t
     becomes e4m3(fp32(x * fp32(1 / scale))), x the bf16 value of
     key_bits[t, h, d] (uint16 bit patterns, [T, Hkv, D]) and scale the one
     the decode reads for that element (K: per head_dim group when
-    k_groups > 1, laid out as in the decode oracle's k_scale_of_head)."""
+    k_groups > 1, laid out as in the decode oracle's k_scale_of_head).  With
+    kv_layout="HND" the pools are head-major, [num_blocks, Hkv, bt, D]."""
     k_out = np.array(k_cache, dtype=np.uint8, copy=True)
     v_out = np.array(v_cache, dtype=np.uint8, copy=True)
-    nb, bt, hkv, d = k_out.shape
+    assert kv_layout in ("NHD", "HND")
+    hnd = kv_layout == "HND"
+    if hnd:
+        nb, hkv, bt, d = k_out.shape
+    else:
+        nb, bt, hkv, d = k_out.shape
     ks = np.asarray(k_scale, dtype=np.float32).reshape(-1)
     vs = np.asarray(v_scale, dtype=np.float32).reshape(-1)
     kg = max(1, int(k_groups))
@@ -99,5 +105,9 @@ def cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_cache, v
             for h in range(hkv):
                 inv = (np.float32(1.0) / scales_of(scales, groups, h)).astype(np.float32)
                 prod = (vals[t, h, :] * inv).astype(np.float32)
-                dst[page, off, h, :] = e4m3_encode(prod.astype(np.float64))
+                codes = e4m3_encode(prod.astype(np.float64))
+                if hnd:
+                    dst[page, h, off, :] = codes
+                else:
+                    dst[page, off, h, :] = codes
     return k_out, v_out

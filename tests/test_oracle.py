@@ -226,6 +226,35 @@ def test_k_groups_per_tensor_scale_layout():
     assert list(d) == [3] * 4 + [4] * 4 + [5] * 4
 
 
+# ------------------------------------------------------ head-major (HND) pages
+
+def test_hnd_pages_equal_token_major_pages():
+    """The same pages stored head-major ([blocks, Hkv, bt, D]) decode to
+    exactly the token-major result; poison bytes (NaN codes) in unattended
+    slots catch a read at a wrong place."""
+    for kw in (dict(window=20, sinks=True), dict(scale=("per_head", 0.02, 0.1), k_groups=2)):
+        wl = _wl(**kw)
+        out, lse = oracle.decode(**wl.oracle_kwargs())
+        k2 = np.ascontiguousarray(wl.k_cache.transpose(0, 2, 1, 3))
+        v2 = np.ascontiguousarray(wl.v_cache.transpose(0, 2, 1, 3))
+        kw2 = wl.oracle_kwargs()
+        kw2.update(k_cache=k2, v_cache=v2, kv_layout="HND")
+        out2, lse2 = oracle.decode(**kw2)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+        assert not np.isnan(out).any()
+
+
+def test_hnd_gather_reads_head_major_offsets():
+    """One hand-placed code: head 1, token 5 of a 4-token page layout lives at
+    [page 1, head 1, slot 1] head-major and at [page 1, slot 1, head 1] token-major."""
+    cache = np.zeros((2, 2, 4, 3), np.uint8)      # [blocks, Hkv, bt, D]
+    cache[1, 1, 1, :] = [0x38, 0x40, 0xB8]         # 1.0, 2.0, -1.0
+    got = oracle.fp8pa_ref._gather(cache, np.array([0, 1]), 1, np.array([5]), 1.0, "HND")
+    assert got.tolist() == [[1.0, 2.0, -1.0]]
+    nhd = np.ascontiguousarray(cache.transpose(0, 2, 1, 3))
+    assert oracle.fp8pa_ref._gather(nhd, np.array([0, 1]), 1, np.array([5]), 1.0).tolist() == [[1.0, 2.0, -1.0]]
+
+
 def _scores_row(wl, b, h, ts, i=0):
     """Scores of row (b, i, h) at positions ts computed with torch's E4M3 decode."""
     from tests.brute_force import depage, _codes_to_float, _bf16_to_float

@@ -120,3 +120,23 @@ def test_cache_write_k_groups():
                 want = oracle.e4m3_encode(xb[t, h].astype(np.float64) / np.repeat(row, d // 4))
                 assert np.array_equal(k1[s // bt, s % bt, h], want)
                 assert np.array_equal(v1[s // bt, s % bt, h], oracle.e4m3_encode(xb[t, h].astype(np.float64)))
+
+
+def test_cache_write_hnd_is_the_transposed_nhd_write():
+    nb, bt, hkv, d = 3, 4, 2, 32
+    rng = np.random.default_rng(8)
+    key = rng.standard_normal((7, hkv, d)).astype(np.float32)
+    val = rng.standard_normal((7, hkv, d)).astype(np.float32)
+    slots = np.array([0, 5, -1, 11, 3, 6, 12])
+    ks = np.array([0.5, 0.25, 2.0, 1.0], np.float32)
+    vs = np.array([0.125], np.float32)
+    k0 = rng.integers(0, 256, size=(nb, bt, hkv, d)).astype(np.uint8)
+    v0 = rng.integers(0, 256, size=(nb, bt, hkv, d)).astype(np.uint8)
+    k1, v1 = oracle.cache_write(_bits16(key), _bits16(val), slots, ks, vs, k0, v0, k_groups=2)
+    k2, v2 = oracle.cache_write(_bits16(key), _bits16(val), slots, ks, vs, k0.transpose(0, 2, 1, 3),
+                                v0.transpose(0, 2, 1, 3), k_groups=2, kv_layout="HND")
+    assert np.array_equal(k2, k1.transpose(0, 2, 1, 3)) and np.array_equal(v2, v1.transpose(0, 2, 1, 3))
+
+
+def _bits16(x):
+    return _bf16_bits(x)
