@@ -23,8 +23,10 @@ is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
 timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
 fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
-Two widenings are timed after the decode: the headline workload with K
-scales in four head_dim groups ("k_groups_variant"), and chunked prefill,
+Three widenings are timed after the decode: the headline workload with K
+scales in four head_dim groups ("k_groups_variant"), the headline and the
+windowed head_dim-64 workloads with head-major pages ("hnd_variant"), and
+chunked prefill,
 q_len 16 to 512 new tokens over a paged context ("prefill", in algorithmic
 TFLOP/s against the dense FP8 peak).
 
@@ -124,7 +126,7 @@ def load_traffic(workload_name):
     return None if not h else int(h["read"] + h["write"])
 
 
-def measure(k, steps, warmup, log, use_graph=True, k_groups=1):
+def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD"):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
@@ -132,14 +134,18 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1):
 
     t_gen = time.time()
     wl = make_config(k, k_groups=k_groups)
-    label = f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "")
+    label = f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "") + ("_hnd" if kv_layout == "HND" else "")
     log(f"[bench] {label}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
     dev = torch.device("cuda")
     kvb = kv_bytes(wl)
     copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / max(kvb, 1)))))
     q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    kc0 = torch.from_numpy(wl.k_cache).to(dev)
-    vc0 = torch.from_numpy(wl.v_cache).to(dev)
+    if kv_layout == "HND":  # the same pages stored head-major
+        kc0 = torch.from_numpy(np.ascontiguousarray(wl.k_cache.transpose(0, 2, 1, 3))).to(dev)
+        vc0 = torch.from_numpy(np.ascontiguousarray(wl.v_cache.transpose(0, 2, 1, 3))).to(dev)
+    else:
+        kc0 = torch.from_numpy(wl.k_cache).to(dev)
+        vc0 = torch.from_numpy(wl.v_cache).to(dev)
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(copies - 1)]
     btab = torch.from_numpy(wl.block_table).to(dev)
     sl = torch.from_numpy(wl.seq_lens).to(dev)
@@ -147,7 +153,7 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1):
     vs = torch.from_numpy(wl.v_scale).to(dev)
     sinks = None if wl.sinks is None else torch.from_numpy(wl.sinks).to(dev)
     shape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
-                         max_seq_len=int(wl.seq_lens.max()), k_groups=wl.k_groups)
+                         max_seq_len=int(wl.seq_lens.max()), k_groups=wl.k_groups, kv_layout=kv_layout)
     plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
     nws = fp.fp8pa_workspace_bytes(shape)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
@@ -216,7 +222,7 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1):
     if plan["merge_launched"]:
         pshape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
                               max_seq_len=int(wl.seq_lens.max()), flags=fp.FP8PA_FLAG_PARTIAL_ONLY,
-                              k_groups=wl.k_groups)
+                              k_groups=wl.k_groups, kv_layout=kv_layout)
 
         def partial_only(i):
             kc, vc = pools[i % copies]
@@ -611,6 +617,14 @@ def main():
     kg_res, kg_wl = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph,
                             k_groups=4)
     del kg_wl
+    # the headline and the windowed head_dim-64 workloads with head-major pages
+    hnd = {}
+    for k in (HEADLINE, 3):
+        r, w_ = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph, kv_layout="HND")
+        hnd[f"cfg{k}"] = {"workload": r["describe"] + " kv_layout=HND", "step_us": round(r["step_ms"] * 1e3, 2),
+                          "partial_us": round(r["partial_ms"] * 1e3, 2), "kv_gbps": round(r["kv_gbps"], 1),
+                          "pct_peak": round(r["pct_peak"], 2)}
+        del w_
     prefill = measure_prefill(log)
     cpu = None
     if not args.no_cpu_baseline:
@@ -641,6 +655,7 @@ def main():
             "kv_gbps": round(kg_res["kv_gbps"], 1), "pct_peak": round(kg_res["pct_peak"], 2),
             "partial_kv_gbps": round(kg_res["partial_kv_gbps"], 1),
         },
+        "hnd_variant": hnd,
         "prefill": prefill,
         "per_workload": {
             f"cfg{k}": {

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     FP8PA_FLAG_FORCE_DOT,
     FP8PA_FLAG_FORCE_MFMA,
     FP8PA_FLAG_PARTIAL_ONLY,
+    FP8PA_LAYOUT_HND,
+    FP8PA_LAYOUT_NHD,
     FP8PA_SPLIT_BALANCED,
     FP8PA_SPLIT_DIRECT,
     FP8PA_SPLIT_FIXED,
@@ -52,17 +54,38 @@ __all__ = [
     "FP8PA_FLAG_FORCE_DOT",
     "FP8PA_FLAG_FORCE_MFMA",
     "FP8PA_FLAG_PARTIAL_ONLY",
+    "FP8PA_LAYOUT_HND",
+    "FP8PA_LAYOUT_NHD",
     "FP8PA_SPLIT_BALANCED",
     "FP8PA_SPLIT_DIRECT",
     "FP8PA_SPLIT_FIXED",
 ]
 
 
+def _layout_code(kv_layout):
+    if kv_layout in ("NHD", FP8PA_LAYOUT_NHD):
+        return FP8PA_LAYOUT_NHD
+    if kv_layout in ("HND", FP8PA_LAYOUT_HND):
+        return FP8PA_LAYOUT_HND
+    raise ValueError(f"kv_layout must be 'NHD' or 'HND', not {kv_layout!r}")
+
+
+def _pool_dims(cache, layout):
+    """(num_blocks, bt, Hkv, D) of a pool in the given layout code."""
+    if layout == FP8PA_LAYOUT_HND:
+        nb, Hkv, bt, D = cache.shape
+    else:
+        nb, bt, Hkv, D = cache.shape
+    return nb, bt, Hkv, D
+
+
 def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=None,
-              max_seq_len, num_splits=0, flags=0, k_groups=1) -> Shape:
-    """fp8pa_shape for tensors q [B, q_len, Hq, D] and k_cache [blocks, bt, Hkv, D]."""
+              max_seq_len, num_splits=0, flags=0, k_groups=1, kv_layout="NHD") -> Shape:
+    """fp8pa_shape for tensors q [B, q_len, Hq, D] and k_cache [blocks, bt, Hkv, D]
+    (kv_layout "NHD") or [blocks, Hkv, bt, D] ("HND")."""
     B, q_len, Hq, D = q.shape
-    nb, bt, Hkv, Dk = k_cache.shape
+    layout = _layout_code(kv_layout)
+    nb, bt, Hkv, Dk = _pool_dims(k_cache, layout)
     if Dk != D:
         raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
     if sm_scale is None:
@@ -70,18 +93,20 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
     return make_shape(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                       block_tokens=bt, num_blocks=nb, block_table_stride=block_table.stride(0),
                       max_seq_len=int(max_seq_len), k_scale_count=k_scale.numel(),
-                      v_scale_count=v_scale.numel(), k_groups=int(k_groups), window=int(window),
+                      v_scale_count=v_scale.numel(), k_groups=int(k_groups), kv_layout=layout,
+                      window=int(window),
                       sm_scale=sm_scale,
                       num_splits=int(num_splits), flags=int(flags))
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=None, *,
            window=0, sm_scale=None, max_seq_len=None, num_splits=0, flags=0, out=None, lse=None,
-           workspace=None, stream=None, k_groups=1):
+           workspace=None, stream=None, k_groups=1, kv_layout="NHD"):
     """Runs fp8pa_decode on torch device tensors; returns (out bf16, lse fp32).
 
     q bf16 [B, q_len, Hq, D]; k_cache, v_cache uint8 or float8_e4m3fn
-    [num_blocks, bt, Hkv, D]; block_table int32 [B, stride] (unit column
+    [num_blocks, bt, Hkv, D] (kv_layout "NHD", token-major pages) or
+    [num_blocks, Hkv, bt, D] ("HND", head-major pages); block_table int32 [B, stride] (unit column
     stride); seq_lens int32 [B]; k_scale, v_scale float32 [1] or [Hkv] (with
     k_groups > 1, k_scale is [k_groups] or [Hkv, k_groups]: one scale per
     head_dim group);
@@ -107,7 +132,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
         max_seq_len = int(seq_lens.max().item())
     shape = shape_for(q, k_cache, block_table, k_scale, v_scale, window=window, sm_scale=sm_scale,
                       max_seq_len=max_seq_len, num_splits=num_splits, flags=flags,
-                      k_groups=k_groups)
+                      k_groups=k_groups, kv_layout=kv_layout)
     B, q_len, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, q_len, Hq, D), dtype=torch.bfloat16, device=q.device)
@@ -123,14 +148,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
 
 
 def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *, stream=None,
-                k_groups=1):
+                k_groups=1, kv_layout="NHD"):
     """Runs fp8pa_cache_write on torch device tensors (in place on the caches).
 
     key, value bf16 [T, Hkv, D] with unit stride inside a token row;
     slot_mapping int64 [T] (negative: skip); k_scale, v_scale float32 [1] or
     [Hkv] (k_scale [k_groups] or [Hkv, k_groups] with k_groups > 1);
-    k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D],
-    contiguous.
+    k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D]
+    (kv_layout "NHD") or [num_blocks, Hkv, bt, D] ("HND"), contiguous.
     """
     import torch
 
@@ -145,10 +170,11 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
     T, Hkv, D = key.shape
     if tuple(value.shape) != (T, Hkv, D) or slot_mapping.numel() != T:
         raise ValueError("key, value and slot_mapping disagree on the token count or shape")
-    nb, bt, Hkv_c, D_c = k_cache.shape
+    layout = _layout_code(kv_layout)
+    nb, bt, Hkv_c, D_c = _pool_dims(k_cache, layout)
     if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("cache shape does not match key / value")
     shape = WriteShape(T, key.stride(0), value.stride(0), Hkv, D, bt, nb, k_scale.numel(),
-                       v_scale.numel(), int(k_groups))
+                       v_scale.numel(), int(k_groups), layout)
     fp8pa_cache_write(shape, key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, stream)
     return k_cache, v_cache

@@ -26,6 +26,8 @@ FP8PA_FLAG_PARTIAL_ONLY = 4
 FP8PA_SPLIT_DIRECT = 0
 FP8PA_SPLIT_FIXED = 1
 FP8PA_SPLIT_BALANCED = 2
+FP8PA_LAYOUT_NHD = 0
+FP8PA_LAYOUT_HND = 1
 
 
 class Fp8paError(RuntimeError):
@@ -52,6 +54,7 @@ class Shape(ctypes.Structure):
         ("k_scale_count", ctypes.c_int32),
         ("v_scale_count", ctypes.c_int32),
         ("k_groups", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
@@ -73,6 +76,7 @@ class WriteShape(ctypes.Structure):
         ("k_scale_count", ctypes.c_int32),
         ("v_scale_count", ctypes.c_int32),
         ("k_groups", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 
@@ -170,12 +174,12 @@ def _stream(stream):
 
 def make_shape(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, block_tokens, num_blocks,
                block_table_stride, max_seq_len, k_scale_count=1, v_scale_count=1, k_groups=1,
-               window=0, sm_scale, num_splits=0, flags=0) -> Shape:
+               kv_layout=FP8PA_LAYOUT_NHD, window=0, sm_scale, num_splits=0, flags=0) -> Shape:
     return Shape(batch=batch, q_len=q_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                  head_dim=head_dim, block_tokens=block_tokens, num_blocks=num_blocks,
                  block_table_stride=block_table_stride, max_seq_len=max_seq_len,
                  k_scale_count=k_scale_count, v_scale_count=v_scale_count, k_groups=k_groups,
-                 window=window, sm_scale=float(sm_scale), num_splits=num_splits, flags=flags)
+                 kv_layout=kv_layout, window=window, sm_scale=float(sm_scale), num_splits=num_splits, flags=flags)
 
 
 def fp8pa_plan(shape: Shape, cu_count: int) -> dict:

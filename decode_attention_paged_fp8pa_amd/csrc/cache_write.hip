@@ -43,7 +43,8 @@ struct WriteParams {
   int64_t page_bytes;       // bt * Hkv * D
   int32_t chunks_per_token; // Hkv * D / 8
   int32_t chunks_per_head;  // D / 8
-  int32_t token_bytes;      // Hkv * D
+  int32_t token_bytes;      // bytes between token slots of a page: Hkv * D, or D head-major
+  int32_t head_bytes;       // bytes between kv heads of a page: D, or bt * D head-major
   int32_t bt_shift, bt_mask;
 };
 
@@ -80,7 +81,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
     const float inv = 1.f / p.scale[kv][(p.per_head[kv] ? h * p.groups[kv] : 0) + grp];
     const u32x4 x = *reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 8 * int64_t(c));
     uint8_t* dst = cache + (slot >> p.bt_shift) * p.page_bytes +
-                   int64_t(slot & p.bt_mask) * p.token_bytes + 8 * c;
+                   int64_t(slot & p.bt_mask) * p.token_bytes + int64_t(h) * p.head_bytes +
+                   8 * (c - h * p.chunks_per_head);
     *reinterpret_cast<u32x2*>(dst) = encode8(x, inv);
   }
 }
@@ -111,6 +113,7 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   if (s->key_stride < row || s->value_stride < row) return FP8PA_ERR_INVALID_ARG;
   if (s->key_stride % 8 != 0 || s->value_stride % 8 != 0) return FP8PA_ERR_MISALIGNED;
   if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_layout != FP8PA_LAYOUT_NHD && s->kv_layout != FP8PA_LAYOUT_HND) return FP8PA_ERR_INVALID_ARG;
   const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
   if ((s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg) ||
       (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads))
@@ -147,7 +150,9 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   p.page_bytes = int64_t(s->block_tokens) * row;
   p.chunks_per_token = int32_t(cpt);
   p.chunks_per_head = s->head_dim / 8;
-  p.token_bytes = int32_t(row);
+  const bool hnd = s->kv_layout == FP8PA_LAYOUT_HND;
+  p.token_bytes = hnd ? s->head_dim : int32_t(row);
+  p.head_bytes = hnd ? s->block_tokens * s->head_dim : s->head_dim;
   p.bt_shift = bt_shift;
   p.bt_mask = s->block_tokens - 1;
 

@@ -80,7 +80,8 @@ struct Params {
   float* part_o;
   float* part_lse;
   int64_t page_bytes;  // bt * Hkv * D
-  int32_t tok_stride;  // Hkv * D: bytes between token slots of a page
+  int32_t tok_stride;  // bytes between token slots of a page: Hkv * D, or D head-major
+  int32_t head_stride; // bytes between kv heads of a page: D, or bt * D head-major
   int32_t B, q_len, Hq, Hkv, G, rows, row_groups, hg;
   int32_t upi;           // workgroups per (sequence, split) item
   int32_t num_splits;    // partial slots per query row
@@ -528,8 +529,10 @@ partial_mfma_kernel(Params p) {
   }
 
   const int tok = p.tok_stride;
-  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D + d0;
-  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D + d0;
+  // (paired heads: the pair's first head; its partner's bytes follow it)
+  const size_t hoff = (size_t)(PR == 2 ? 2 * w.g : w.g) * (size_t)p.head_stride + d0;
+  const uint8_t* kbase_g = p.k_cache + hoff;
+  const uint8_t* vbase_g = p.v_cache + hoff;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
   const uint32_t koff = uint32_t(n * tok + KB * qd);
 
@@ -926,8 +929,8 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   }
 
   const int tok = p.tok_stride;
-  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * D + 16 * c;
-  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * D + 16 * c;
+  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * (size_t)p.head_stride + 16 * c;
+  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * (size_t)p.head_stride + 16 * c;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
 
   for (int tt = ts; tt < te; ++tt) {
@@ -1361,7 +1364,9 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.part_lse =
       pl.direct ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.off_lse);
   prm.page_bytes = int64_t(pl.bt) * pl.Hkv * pl.D;
-  prm.tok_stride = pl.Hkv * pl.D;
+  const bool hnd = shape->kv_layout == FP8PA_LAYOUT_HND;
+  prm.tok_stride = hnd ? pl.D : pl.Hkv * pl.D;
+  prm.head_stride = hnd ? pl.bt * pl.D : pl.D;
   prm.q_len = pl.q_len;
   prm.Hq = pl.Hq;
   prm.Hkv = pl.Hkv;

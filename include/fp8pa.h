@@ -73,6 +73,12 @@ typedef enum fp8pa_status {
                                      merge, it is not launched and out / lse are
                                      left unwritten (times the partial kernel) */
 
+/* Byte layout of a KV page (fp8pa_shape.kv_layout, fp8pa_write_shape.kv_layout). */
+#define FP8PA_LAYOUT_NHD 0 /* token-major: [num_blocks][bt][Hkv][D] */
+#define FP8PA_LAYOUT_HND 1 /* head-major:  [num_blocks][Hkv][bt][D] (gist "Qwen3.8-27B ...
+                              on a single RTX 5090", KV cache row and writer: a head's
+                              tokens lie D bytes apart, heads bt * D apart) */
+
 /* Host-known description of one decode call. */
 typedef struct fp8pa_shape {
   int32_t batch;              /* B >= 1 sequences */
@@ -92,6 +98,7 @@ typedef struct fp8pa_shape {
   int32_t k_groups;           /* 0 or 1: one K scale per head (or tensor); 2, 4, 8 or
                                  16: K scale groups along head_dim, D / k_groups >= 32,
                                  group j covering dims [j D / k_groups, (j+1) D / k_groups) */
+  int32_t kv_layout;          /* FP8PA_LAYOUT_NHD (0) or FP8PA_LAYOUT_HND (1), both pools */
   int32_t window;             /* <= 0: none; W > 0: the last W positions */
   float sm_scale;             /* softmax scale applied to q.K; finite */
   int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
@@ -164,8 +171,9 @@ fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t*
  * the top of this file, on the current HIP device.
  *
  *   q            bf16  [B, q_len, Hq, D] contiguous
- *   k_cache      e4m3  [num_blocks, bt, Hkv, D] contiguous (token-major pages)
- *   v_cache      e4m3  [num_blocks, bt, Hkv, D] contiguous
+ *   k_cache      e4m3  [num_blocks, bt, Hkv, D] contiguous (token-major pages), or
+ *                [num_blocks, Hkv, bt, D] with kv_layout = FP8PA_LAYOUT_HND
+ *   v_cache      e4m3  the same shape and layout as k_cache
  *   block_table  int32 [B, block_table_stride]; entry j of row b is the page
  *                that holds tokens [j*bt, (j+1)*bt) of sequence b
  *   seq_lens     int32 [B]; tokens of each sequence, its q_len new ones included
@@ -242,6 +250,7 @@ typedef struct fp8pa_write_shape {
   int32_t v_scale_count;   /* 1 or Hkv */
   int32_t k_groups;        /* as in fp8pa_shape: each key element is encoded against
                               the scale of its head_dim group */
+  int32_t kv_layout;       /* FP8PA_LAYOUT_NHD or FP8PA_LAYOUT_HND, both pools */
 } fp8pa_write_shape;
 
 /*
@@ -252,7 +261,8 @@ typedef struct fp8pa_write_shape {
  *                 elements apart (16-byte aligned)
  *   slot_mapping  int64 [T]
  *   k_scale       float [k_scale_count]; v_scale float [v_scale_count]
- *   k_cache       e4m3 [num_blocks, bt, Hkv, D] (8-byte aligned); v_cache alike
+ *   k_cache       e4m3 [num_blocks, bt, Hkv, D] (8-byte aligned), or
+ *                 [num_blocks, Hkv, bt, D] with kv_layout = FP8PA_LAYOUT_HND; v_cache alike
  *
  * Only the slots named are written.  Two tokens with the same slot race
  * (either may win).  All pointers are device pointers owned by the caller;

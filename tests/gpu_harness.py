@@ -16,13 +16,18 @@ RTOL_OUT = 1e-2
 ATOL_LSE = 1e-3
 
 
-def upload(wl, device="cuda"):
+def upload(wl, device="cuda", kv_layout="NHD"):
+    """Device tensors of a workload; kv_layout "HND" stores the pools head-major."""
     import torch
 
+    def pool(c):
+        return np.ascontiguousarray(c.transpose(0, 2, 1, 3)) if kv_layout == "HND" else c
+
     t = {
+        "layout": kv_layout,
         "q": torch.from_numpy(wl.q_bits.view(np.int16)).to(device).view(torch.bfloat16),
-        "k": torch.from_numpy(wl.k_cache).to(device),
-        "v": torch.from_numpy(wl.v_cache).to(device),
+        "k": torch.from_numpy(pool(wl.k_cache)).to(device),
+        "v": torch.from_numpy(pool(wl.v_cache)).to(device),
         "bt": torch.from_numpy(wl.block_table).to(device),
         "sl": torch.from_numpy(wl.seq_lens).to(device),
         "ks": torch.from_numpy(wl.k_scale).to(device),
@@ -39,7 +44,8 @@ def run(wl, t, num_splits=0, flags=0, out=None, lse=None, workspace=None):
     return fp.decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
                      window=wl.window, sm_scale=wl.sm_scale,
                      max_seq_len=int(wl.seq_lens.max()), num_splits=num_splits, flags=flags,
-                     out=out, lse=lse, workspace=workspace, k_groups=wl.k_groups)
+                     out=out, lse=lse, workspace=workspace, k_groups=wl.k_groups,
+                     kv_layout=t.get("layout", "NHD"))
 
 
 def to_host(out, lse):

@@ -164,12 +164,36 @@ BAD = [
     (dict(k_groups=32, k_scale_count=256), _lib.FP8PA_ERR_INVALID_ARG),  # above 16
     (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),   # 16 dims per group at D = 128
     (dict(k_groups=4), _lib.FP8PA_ERR_INVALID_ARG),                     # Hkv scales, not Hkv * 4
+    (dict(kv_layout=2), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_layout=-1), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(num_splits=-1), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(flags=8), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(flags=3), _lib.FP8PA_ERR_INVALID_ARG),
 ]
+
+
+def test_head_major_pages_turn_off_head_pairing():
+    # cfg3 (D = 64, 8 rows per kv head) pairs kv heads in token-major pages,
+    # where a token's two 64-byte slices are adjacent; head-major pages do not
+    assert CONFIGS[3]["D"] == 64
+    assert fp.fp8pa_plan(cfg_shape(3), 256)["heads_per_wave"] == 2
+    p = fp.fp8pa_plan(cfg_shape(3, kv_layout=fp.FP8PA_LAYOUT_HND), 256)
+    assert p["heads_per_wave"] == 1 and p["variant"] == 1
+
+
+def test_row_blocks_for_many_rows():
+    base = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
+                num_blocks=1024, block_table_stride=64, max_seq_len=1024, sm_scale=0.1)
+    for q_len, nb, rg in ((1, 1, 1), (4, 1, 1), (5, 2, 1), (8, 2, 1), (9, 2, 2), (128, 2, 16)):
+        p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, **base), 256)
+        assert (p["row_blocks"], p["row_groups"], p["rows_per_group"]) == (nb, rg, 16 * nb), q_len
+        # non-temporal loads only where one wavefront reads each K/V byte
+        assert p["nontemporal_kv"] == (1 if rg == 1 else 0)
+    # head_dim 256 splits head_dim over two wavefronts and keeps one row block
+    p = fp.fp8pa_plan(fp.make_shape(q_len=64, **dict(base, head_dim=256)), 256)
+    assert p["row_blocks"] == 1 and p["waves_per_head"] == 2
 
 
 def test_plan_accepts_k_groups():
@@ -330,6 +354,7 @@ WRITE_BAD = [
     (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),    # 16 dims per group
     (dict(k_groups=6, k_scale_count=48), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(k_groups=4, v_scale_count=32), _lib.FP8PA_ERR_INVALID_ARG),    # V keeps one per head
+    (dict(kv_layout=3), _lib.FP8PA_ERR_INVALID_ARG),
 ]
 
 

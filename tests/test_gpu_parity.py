@@ -181,6 +181,21 @@ def test_parity_small(name, flags, ns):
     compare(out, lse, ro, rl, label=f"{name} flags={flags} splits={ns}")
 
 
+HND_CASES = ["gqa4_ragged", "d64_window_sinks", "d256_bt64", "mtp4_window_sinks", "bt1_pages",
+             "pair_q2_perhead", "kg4_gqa_ragged", "prefill_q64", "mha_rows1", "batch130_mqa"]
+
+
+@pytest.mark.parametrize("name", HND_CASES)
+@pytest.mark.parametrize("flags,ns", [(0, 0), (0, 3), (DOT, 0)])
+def test_parity_head_major_pages(name, flags, ns):
+    """The same pages stored head-major ([blocks, Hkv, bt, D]); the oracle's
+    result does not depend on the layout (pinned on the CPU)."""
+    wl, _, (ro, rl) = _small(name)
+    t = upload(wl, kv_layout="HND")
+    out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"{name} HND flags={flags} splits={ns}")
+
+
 def test_parity_output_without_lse_pointer():
     wl, t, (ro, rl) = _small("mtp4_window_sinks")
     out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")

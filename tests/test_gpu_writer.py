@@ -52,6 +52,10 @@ CASES = [
     (1, 1, 64, 32, 1, 0, False, 1),
     # K scales in groups along head_dim
     (37, 8, 128, 16, 5, 0, True, 4),
+    # head-major pages (k_groups negative here: the same case with HND pools)
+    (37, 8, 128, 16, 5, 0, True, -4),
+    (100, 8, 64, 16, 10, 8, True, -1),
+    (64, 4, 256, 64, 2, 24, False, -8),
     (64, 4, 256, 64, 2, 24, False, 8),
     (100, 8, 64, 16, 10, 8, True, 2),
     (20, 2, 256, 16, 3, 0, True, 8),
@@ -60,6 +64,8 @@ CASES = [
 
 @pytest.mark.parametrize("T,Hkv,D,bt,nb,pad,per_head,kg", CASES)
 def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head, kg):
+    layout = "HND" if kg < 0 else "NHD"
+    kg = abs(kg)
     rng = np.random.default_rng(T * 7 + D)
     key = _inputs(rng, T, Hkv, D, pad, True)
     value = _inputs(rng, T, Hkv, D, pad, False)
@@ -78,13 +84,15 @@ def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head, kg):
     nsc = Hkv if per_head else 1
     ks = rng.uniform(0.01, 0.2, size=nsc * kg).astype(np.float32)
     vs = rng.uniform(0.01, 0.2, size=nsc).astype(np.float32)
-    k0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
-    v0 = rng.integers(0, 256, size=(nb, bt, Hkv, D)).astype(np.uint8)
+    pool_shape = (nb, Hkv, bt, D) if layout == "HND" else (nb, bt, Hkv, D)
+    k0 = rng.integers(0, 256, size=pool_shape).astype(np.uint8)
+    v0 = rng.integers(0, 256, size=pool_shape).astype(np.uint8)
     kc, vc = torch.from_numpy(k0).cuda(), torch.from_numpy(v0).cuda()
     fp.cache_write(key, value, torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
-                   torch.from_numpy(vs).cuda(), kc, vc, k_groups=kg)
+                   torch.from_numpy(vs).cuda(), kc, vc, k_groups=kg, kv_layout=layout)
     torch.cuda.synchronize()
-    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, k0, v0, k_groups=kg)
+    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, k0, v0, k_groups=kg,
+                                        kv_layout=layout)
     for got, want, name in ((kc.cpu().numpy(), want_k, "k"), (vc.cpu().numpy(), want_v, "v")):
         nan_w = np.isnan(oracle.E4M3_TABLE[want])
         assert np.array_equal(np.isnan(oracle.E4M3_TABLE[got]), nan_w), name
