@@ -95,9 +95,7 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // At D = 64 with at most 8 query rows per kv head, the MFMA kernel runs
   // two kv heads per wavefront (one 128-byte line per token, all 16 MFMA
   // columns in use); hg then counts head pairs.
-  // (Only in token-major pages, where a token's two head slices are adjacent.)
-  p.pr = (p.variant == kVariantMfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0 &&
-          s->kv_layout == FP8PA_LAYOUT_NHD) ? 2 : 1;
+  p.pr = (p.variant == kVariantMfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
   // More than 16 query rows per kv head (chunked prefill, wide MTP): a
   // wavefront carries two blocks of 16 rows over the same K/V registers, so
   // a tile's loads and V transposes serve both.  (Four blocks need more

@@ -82,6 +82,7 @@ struct Params {
   int64_t page_bytes;  // bt * Hkv * D
   int32_t tok_stride;  // bytes between token slots of a page: Hkv * D, or D head-major
   int32_t head_stride; // bytes between kv heads of a page: D, or bt * D head-major
+  int32_t grp_bytes;   // bytes a 16-token group's descriptor spans from its base
   int32_t B, q_len, Hq, Hkv, G, rows, row_groups, hg;
   int32_t upi;           // workgroups per (sequence, split) item
   int32_t num_splits;    // partial slots per query row
@@ -534,7 +535,11 @@ partial_mfma_kernel(Params p) {
   const uint8_t* kbase_g = p.k_cache + hoff;
   const uint8_t* vbase_g = p.v_cache + hoff;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
-  const uint32_t koff = uint32_t(n * tok + KB * qd);
+  // K bytes of token n: KB * qd onwards in the wavefront's D-byte slice; with
+  // paired heads lane groups 0-1 read the first head's 64 bytes and 2-3 the
+  // second's, head_stride further on (adjacent in token-major pages).
+  const uint32_t koff = PR == 2 ? uint32_t(n * tok + KB * (qd & 1) + (qd >> 1) * p.head_stride)
+                                : uint32_t(n * tok + KB * qd);
 
   // Block-table entries of the split, read once before the loop: lane k of
   // tab[g] holds the page of 16-token group g & 1 of tile ts + 2 k + (g >> 1),
@@ -567,9 +572,13 @@ partial_mfma_kernel(Params p) {
   const int ihi = L - p.q_len + qmin + 1;
   const int ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
 
+  // V bytes: S dims of the wavefront's slice per lane (paired heads: lanes
+  // n < 8 the first head's, n >= 8 the second's)
   uint32_t voff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) voff[j] = uint32_t((4 * qd + j) * tok + S * n);
+  for (int j = 0; j < 4; ++j)
+    voff[j] = PR == 2 ? uint32_t((4 * qd + j) * tok + S * (n & 7) + (n >> 3) * p.head_stride)
+                      : uint32_t((4 * qd + j) * tok + S * n);
 
   // Loads of one 32-token tile into registers, without branches.  A tile at
   // or past `te`, or a 16-token group holding no attended token, gets a
@@ -590,7 +599,7 @@ partial_mfma_kernel(Params p) {
       const bool live = tt < te && gk < uhi && gk + 16 > ulo;
       const int page = __builtin_amdgcn_readlane(tab[2 * odd + grp], step);
       const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
-      const int nrec = live ? 16 * tok : 0;
+      const int nrec = live ? p.grp_bytes : 0;
       const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + base), 0, nrec, kRsrcWord3);
       const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + base), 0, nrec, kRsrcWord3);
       buf_load<KB, AUX>(rk, koff, r.k[grp]);
@@ -1367,6 +1376,8 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   const bool hnd = shape->kv_layout == FP8PA_LAYOUT_HND;
   prm.tok_stride = hnd ? pl.D : pl.Hkv * pl.D;
   prm.head_stride = hnd ? pl.bt * pl.D : pl.D;
+  // a group's tokens, plus with paired head-major heads the second head's
+  prm.grp_bytes = (pl.pr == 2 && hnd) ? prm.head_stride + 16 * pl.D : 16 * prm.tok_stride;
   prm.q_len = pl.q_len;
   prm.Hq = pl.Hq;
   prm.Hkv = pl.Hkv;

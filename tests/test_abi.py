@@ -174,13 +174,13 @@ BAD = [
 ]
 
 
-def test_head_major_pages_turn_off_head_pairing():
-    # cfg3 (D = 64, 8 rows per kv head) pairs kv heads in token-major pages,
-    # where a token's two 64-byte slices are adjacent; head-major pages do not
+def test_head_pairing_in_both_page_layouts():
+    # cfg3 (D = 64, 8 rows per kv head) pairs kv heads per wavefront, with
+    # token-major and head-major pages alike
     assert CONFIGS[3]["D"] == 64
-    assert fp.fp8pa_plan(cfg_shape(3), 256)["heads_per_wave"] == 2
-    p = fp.fp8pa_plan(cfg_shape(3, kv_layout=fp.FP8PA_LAYOUT_HND), 256)
-    assert p["heads_per_wave"] == 1 and p["variant"] == 1
+    for layout in (fp.FP8PA_LAYOUT_NHD, fp.FP8PA_LAYOUT_HND):
+        p = fp.fp8pa_plan(cfg_shape(3, kv_layout=layout), 256)
+        assert p["heads_per_wave"] == 2 and p["variant"] == 1
 
 
 def test_row_blocks_for_many_rows():
