@@ -1,5 +1,6 @@
-"""Float64 CPU oracle for paged flash-decode attention over an E4M3 KV cache,
-and for the writer that fills that cache from bf16 keys and values.
+"""Float64 CPU oracle for paged flash-decode attention over an E4M3 (or
+NVFP4) KV cache, and for the writers that fill those caches from bf16 keys
+and values.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
 links this package; only the tests, the smoke check and the CPU-baseline leg
@@ -26,4 +27,12 @@ from .fp8pa_write_ref import (  # noqa: F401
     E4M3_MAX,
     e4m3_encode,
     cache_write,
+)
+from .nvfp4_ref import (  # noqa: F401
+    E2M1_TABLE,
+    e2m1_decode_code,
+    e2m1_encode,
+    nvfp4_side_bytes,
+    nvfp4_gather,
+    nvfp4_cache_write,
 )

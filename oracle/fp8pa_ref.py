@@ -149,7 +149,8 @@ def _softmax_rows(scores: np.ndarray, sink: float | None):
 
 def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
            sinks=None, window=0, sm_scale=None, rows=None, key_range=None,
-           key_chunk=16384, k_groups=1, kv_layout="NHD"):
+           key_chunk=16384, k_groups=1, kv_layout="NHD", kv_format="e4m3", num_kv_heads=None,
+           block_tokens=None):
     """Reference paged decode attention [P1 title/summary], float64.
 
     Arguments (numpy arrays, as the library receives them):
@@ -157,6 +158,9 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
       k_cache     uint8  [num_blocks, bt, Hkv, D]  E4M3 codes (token-major pages),
                   or [num_blocks, Hkv, bt, D] with kv_layout="HND" (head-major)
       v_cache     uint8  the same shape and layout as k_cache
+                  (kv_format="nvfp4": uint8 [num_blocks, page_stride] NVFP4
+                  pools, read by nvfp4_ref.nvfp4_gather; num_kv_heads and
+                  block_tokens then give the page geometry)
       block_table int32  [B, max_blocks]  page of each logical page index
       seq_lens    int32  [B]  tokens in each sequence, the q_len new ones included
       k_scale, v_scale  float32 [1] (per tensor) or [Hkv] (per kv head); with
@@ -178,8 +182,16 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
     """
     q_bits = np.asarray(q_bits)
     B, q_len, Hq, D = q_bits.shape
-    assert kv_layout in ("NHD", "HND")
-    Hkv = k_cache.shape[1] if kv_layout == "HND" else k_cache.shape[2]
+    assert kv_layout in ("NHD", "HND") and kv_format in ("e4m3", "nvfp4")
+    if kv_format == "nvfp4":
+        from .nvfp4_ref import nvfp4_gather
+        Hkv = int(num_kv_heads)
+
+        def gather(cache, row, g, ts, scale, layout):
+            return nvfp4_gather(cache, row, g, ts, scale, Hkv, int(block_tokens), D, layout)
+    else:
+        Hkv = k_cache.shape[1] if kv_layout == "HND" else k_cache.shape[2]
+        gather = _gather
     assert Hq % Hkv == 0, "Hq must be a multiple of Hkv"
     G = Hq // Hkv
     if sm_scale is None:
@@ -223,7 +235,7 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
         scores = np.empty((len(members), n_keys), dtype=np.float64)
         for c0 in range(u_lo, u_hi, key_chunk):
             ts = np.arange(c0, min(c0 + key_chunk, u_hi))
-            kf = _gather(k_cache, block_table[b], g, ts, ks, kv_layout)
+            kf = gather(k_cache, block_table[b], g, ts, ks, kv_layout)
             scores[:, c0 - u_lo:c0 - u_lo + len(ts)] = sm_scale * (qmat @ kf.T)
         # Pass 2: exact softmax weights of each row over its own key range.
         weights = np.zeros_like(scores)
@@ -243,7 +255,7 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
             live = np.flatnonzero(wchunk.any(axis=0))
             if live.size == 0:
                 continue
-            vf = _gather(v_cache, block_table[b], g, ts[live], vs, kv_layout)
+            vf = gather(v_cache, block_table[b], g, ts[live], vs, kv_layout)
             acc += wchunk[:, live] @ vf
         for j, n in enumerate(members):
             out[n] = acc[j]

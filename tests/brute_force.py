@@ -35,10 +35,33 @@ def depage(cache: np.ndarray, table_row: np.ndarray, seq_len: int) -> np.ndarray
     return np.stack(rows)
 
 
+_FP4_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # OCP E2M1, codes 0..7
+
+
+def depage_nvfp4(pool, table_row, seq_len, Hkv, bt, D, layout):
+    """Contiguous float64 [seq_len, Hkv, D] (code value x block scale) of one
+    sequence of an NVFP4 pool, one element at a time."""
+    out = np.zeros((seq_len, Hkv, D))
+    data_row, sc_row = D // 2, D // 16
+    data_bytes = Hkv * bt * data_row
+    for t in range(seq_len):
+        page = int(table_row[t // bt])
+        slot = t % bt
+        for h in range(Hkv):
+            row = h * bt + slot if layout == "HND" else slot * Hkv + h
+            for d in range(D):
+                byte = int(pool[page, row * data_row + d // 2])
+                nib = (byte >> 4) if (d & 1) else (byte & 0xF)
+                val = _FP4_MAGNITUDES[nib & 7] * (-1.0 if nib & 8 else 1.0)
+                sbyte = np.array([pool[page, data_bytes + row * sc_row + d // 16]], dtype=np.uint8)
+                out[t, h, d] = val * _codes_to_float(sbyte)[0]
+    return out
+
+
 def brute_decode(wl, key_range=None, sinks="from_workload"):
     """Attention of every (b, i, h) row by plain loops; returns (out, lse)."""
     B, q_len, Hq, D = wl.q_bits.shape
-    Hkv = wl.k_cache.shape[2]
+    Hkv = wl.Hkv
     G = Hq // Hkv
     sk = wl.sinks if isinstance(sinks, str) else sinks
     q = _bf16_to_float(wl.q_bits)
@@ -50,8 +73,12 @@ def brute_decode(wl, key_range=None, sinks="from_workload"):
     vs_all = np.asarray(wl.v_scale, dtype=np.float64).reshape(-1)
     for b in range(B):
         L = int(wl.seq_lens[b])
-        K = _codes_to_float(depage(wl.k_cache, wl.block_table[b], L))
-        V = _codes_to_float(depage(wl.v_cache, wl.block_table[b], L))
+        if getattr(wl, "kv_format", "e4m3") == "nvfp4":
+            K = depage_nvfp4(wl.k_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
+            V = depage_nvfp4(wl.v_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
+        else:
+            K = _codes_to_float(depage(wl.k_cache, wl.block_table[b], L))
+            V = _codes_to_float(depage(wl.v_cache, wl.block_table[b], L))
         for i in range(q_len):
             pos = L - q_len + i
             for h in range(Hq):

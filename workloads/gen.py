@@ -69,6 +69,8 @@ class Workload:
     sm_scale: float
     meta: dict = field(default_factory=dict)
     k_groups: int = 1
+    kv_format: str = "e4m3"   # "nvfp4": k_cache / v_cache are uint8 [num_blocks, page_stride]
+    kv_layout: str = "NHD"    # page layout of the nvfp4 pools ("NHD" or "HND")
 
     @property
     def B(self):
@@ -88,21 +90,25 @@ class Workload:
 
     @property
     def Hkv(self):
-        return self.k_cache.shape[2]
+        return self.meta["Hkv"] if self.kv_format == "nvfp4" else self.k_cache.shape[2]
 
     @property
     def bt(self):
-        return self.k_cache.shape[1]
+        return self.meta["bt"] if self.kv_format == "nvfp4" else self.k_cache.shape[1]
 
     @property
     def num_blocks(self):
         return self.k_cache.shape[0]
 
     def oracle_kwargs(self):
-        return dict(q_bits=self.q_bits, k_cache=self.k_cache, v_cache=self.v_cache,
-                    block_table=self.block_table, seq_lens=self.seq_lens,
-                    k_scale=self.k_scale, v_scale=self.v_scale, sinks=self.sinks,
-                    window=self.window, sm_scale=self.sm_scale, k_groups=self.k_groups)
+        kw = dict(q_bits=self.q_bits, k_cache=self.k_cache, v_cache=self.v_cache,
+                  block_table=self.block_table, seq_lens=self.seq_lens,
+                  k_scale=self.k_scale, v_scale=self.v_scale, sinks=self.sinks,
+                  window=self.window, sm_scale=self.sm_scale, k_groups=self.k_groups)
+        if self.kv_format == "nvfp4":
+            kw.update(kv_format="nvfp4", kv_layout=self.kv_layout, num_kv_heads=self.Hkv,
+                      block_tokens=self.bt)
+        return kw
 
     def key_union(self, b):
         """[lo, hi) of positions some query row of sequence b attends."""
@@ -234,3 +240,84 @@ def make_config(k: int, seed: int | None = None, poison: bool = True, k_groups: 
                          window=c["window"], sinks=c["sinks"], sm_scale=c["sm_scale"],
                          poison=poison, k_groups=k_groups,
                          name=f"cfg{k}_{c['name']}" + (f"_kg{k_groups}" if k_groups > 1 else ""))
+
+
+NVFP4_POISON_SCALE = 0x7F   # E4M3 NaN: a block read where nothing is attended yields NaN
+NVFP4_POISON_DATA = 0x77
+
+
+def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", pool=None,
+                        scale=("tensor", 0.05), window=0, sinks=False, sm_scale=None,
+                        poison=True, name="nvfp4", kv_layout="NHD", page_stride=None):
+    """A workload whose K/V pools are NVFP4 pages: uint8 [num_blocks,
+    page_stride], each page one side's data region ([bt][Hkv] or [Hkv][bt]
+    rows of D/2 bytes, two 4-bit codes per byte) followed by its scale region
+    (rows of D/16 E4M3 bytes).  Same draw order as make_workload, with step 5
+    drawing, for every attended position and kv head, D/2 uniform data bytes
+    and D/16 scale bytes uniform over the E4M3 codes 0x48..0x57 (4 to 15).
+    Every other byte is NVFP4_POISON_DATA / NVFP4_POISON_SCALE when `poison`.
+    """
+    rng = np.random.default_rng(seed)
+    if isinstance(seq_lens, tuple) and seq_lens and seq_lens[0] == "uniform":
+        sl = rng.integers(seq_lens[1], seq_lens[2] + 1, size=B).astype(np.int32)
+    elif np.isscalar(seq_lens):
+        sl = np.full((B,), int(seq_lens), dtype=np.int32)
+    else:
+        sl = np.asarray(seq_lens, dtype=np.int32).reshape(B)
+    pages_needed = [(int(n) + bt - 1) // bt for n in sl]
+    num_blocks = max(int(sum(pages_needed)), int(pool or 0), 1)
+    max_blocks = max(max(pages_needed) if pages_needed else 1, 1)
+    order = np.arange(num_blocks, dtype=np.int64) if table == "identity" else rng.permutation(num_blocks)
+    bt_arr = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = pages_needed[b]
+        bt_arr[b, :n] = order[off:off + n]
+        off += n
+    if scale[0] == "tensor":
+        k_scale = np.array([scale[1]], dtype=np.float32)
+        v_scale = np.array([scale[1]], dtype=np.float32)
+    else:
+        k_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
+        v_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
+    qf = rng.standard_normal((B, q_len, Hq, D), dtype=np.float32)
+    q_bits = _bf16_bits(qf)
+    data_row, sc_row = D // 2, D // 16
+    data_bytes = Hkv * bt * data_row
+    side = Hkv * bt * (data_row + sc_row)
+    stride = int(page_stride or side)
+    wl_tmp = Workload(name, q_bits, np.empty((0, bt, Hkv, D), np.uint8), None, bt_arr, sl,
+                      k_scale, v_scale, None, int(window), 0.0)
+    pools = []
+    for _ in ("k", "v"):
+        pool_arr = np.zeros((num_blocks, stride), dtype=np.uint8)
+        if poison:
+            pool_arr[:, :data_bytes] = NVFP4_POISON_DATA
+            pool_arr[:, data_bytes:side] = NVFP4_POISON_SCALE
+            pool_arr[:, side:] = NVFP4_POISON_SCALE
+        for b in range(B):
+            lo, hi = wl_tmp.key_union(b)
+            if not poison:
+                lo, hi = 0, pages_needed[b] * bt
+            if hi <= lo:
+                continue
+            ts = np.arange(lo, hi)
+            pages = bt_arr[b, ts // bt].astype(np.int64)
+            slots = ts % bt
+            data = rng.integers(0, 256, size=(hi - lo, Hkv, data_row), dtype=np.uint8)
+            scl = rng.integers(0x48, 0x58, size=(hi - lo, Hkv, sc_row), dtype=np.uint8)
+            for h in range(Hkv):
+                r = h * bt + slots if kv_layout == "HND" else slots * Hkv + h
+                d_off = r * data_row
+                s_off = data_bytes + r * sc_row
+                pool_arr[pages[:, None], d_off[:, None] + np.arange(data_row)] = data[:, h]
+                pool_arr[pages[:, None], s_off[:, None] + np.arange(sc_row)] = scl[:, h]
+        pools.append(pool_arr)
+    sk = rng.standard_normal((Hq,), dtype=np.float32) if sinks else None
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    return Workload(name=name, q_bits=q_bits, k_cache=pools[0], v_cache=pools[1],
+                    block_table=bt_arr, seq_lens=sl, k_scale=k_scale, v_scale=v_scale,
+                    sinks=sk, window=int(window), sm_scale=float(sm_scale),
+                    meta=dict(seed=seed, poison=poison, Hkv=Hkv, bt=bt, page_stride=stride),
+                    kv_format="nvfp4", kv_layout=kv_layout)
