@@ -28,6 +28,8 @@ FP8PA_SPLIT_FIXED = 1
 FP8PA_SPLIT_BALANCED = 2
 FP8PA_LAYOUT_NHD = 0
 FP8PA_LAYOUT_HND = 1
+FP8PA_KV_E4M3 = 0
+FP8PA_KV_NVFP4 = 1
 
 
 class Fp8paError(RuntimeError):
@@ -55,10 +57,12 @@ class Shape(ctypes.Structure):
         ("v_scale_count", ctypes.c_int32),
         ("k_groups", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("kv_page_stride", ctypes.c_int64),
     ]
 
 
@@ -77,6 +81,8 @@ class WriteShape(ctypes.Structure):
         ("v_scale_count", ctypes.c_int32),
         ("k_groups", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
+        ("kv_page_stride", ctypes.c_int64),
     ]
 
 
@@ -126,6 +132,7 @@ _SIGS = {
     "fp8pa_debug_e4m3_to_f32": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
+    "fp8pa_debug_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
 }
 
 
@@ -174,12 +181,14 @@ def _stream(stream):
 
 def make_shape(*, batch, q_len, num_q_heads, num_kv_heads, head_dim, block_tokens, num_blocks,
                block_table_stride, max_seq_len, k_scale_count=1, v_scale_count=1, k_groups=1,
-               kv_layout=FP8PA_LAYOUT_NHD, window=0, sm_scale, num_splits=0, flags=0) -> Shape:
+               kv_layout=FP8PA_LAYOUT_NHD, kv_format=FP8PA_KV_E4M3, kv_page_stride=0, window=0,
+               sm_scale, num_splits=0, flags=0) -> Shape:
     return Shape(batch=batch, q_len=q_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                  head_dim=head_dim, block_tokens=block_tokens, num_blocks=num_blocks,
                  block_table_stride=block_table_stride, max_seq_len=max_seq_len,
                  k_scale_count=k_scale_count, v_scale_count=v_scale_count, k_groups=k_groups,
-                 kv_layout=kv_layout, window=window, sm_scale=float(sm_scale), num_splits=num_splits, flags=flags)
+                 kv_layout=kv_layout, kv_format=kv_format, kv_page_stride=int(kv_page_stride),
+                 window=window, sm_scale=float(sm_scale), num_splits=num_splits, flags=flags)
 
 
 def fp8pa_plan(shape: Shape, cu_count: int) -> dict:
@@ -240,6 +249,12 @@ def fp8pa_debug_wave_ops(inp, vmax, out, stream=None) -> None:
     st = lib().fp8pa_debug_wave_ops(_ptr(inp), int(vmax), _ptr(out), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_wave_ops")
+
+
+def fp8pa_debug_nvfp4(data, scales, out, n, stream=None) -> None:
+    st = lib().fp8pa_debug_nvfp4(_ptr(data), _ptr(scales), _ptr(out), int(n), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_nvfp4")
 
 
 def fp8pa_debug_mfma_fp8(a, b, c, stream=None) -> None:

@@ -40,11 +40,17 @@ struct WriteParams {
   int64_t num_tokens;
   int64_t chunks;           // num_tokens * chunks_per_token
   int64_t num_slots;        // num_blocks * bt
-  int64_t page_bytes;       // bt * Hkv * D
+  int64_t page_bytes;       // bytes between pages of a pool
   int32_t chunks_per_token; // Hkv * D / 8
   int32_t chunks_per_head;  // D / 8
   int32_t token_bytes;      // bytes between token slots of a page: Hkv * D, or D head-major
   int32_t head_bytes;       // bytes between kv heads of a page: D, or bt * D head-major
+  // NVFP4 pages (token_bytes / head_bytes then count data-region bytes):
+  int32_t sc_off;           // byte offset of a page's scale region
+  int32_t sc_tok, sc_head;  // scale bytes between token slots / kv heads
+  int64_t fp4_blocks;       // num_tokens * Hkv * D / 16
+  int32_t blocks_per_token; // Hkv * D / 16
+  int32_t blocks_per_head;  // D / 16
   int32_t bt_shift, bt_mask;
 };
 
@@ -87,6 +93,67 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
   }
 }
 
+// E2M1 code of t: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
+// even code (the midpoints 0.25, 1.25, 2.5, 5 go down, 0.75, 1.75, 3.5 up),
+// saturating at 6, with t's sign bit.
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float a = fabsf(t);
+  const uint32_t c = a <= 0.25f   ? 0u
+                     : a < 0.75f  ? 1u
+                     : a <= 1.25f ? 2u
+                     : a < 1.75f  ? 3u
+                     : a <= 2.5f  ? 4u
+                     : a < 3.5f   ? 5u
+                     : a <= 5.0f  ? 6u
+                                  : 7u;
+  return c | ((__float_as_uint(t) >> 28) & 8u);
+}
+
+// NVFP4 writer: one thread per 16-element block of a head's row; blockIdx.y
+// 0 keys, 1 values.  Per block: y = x * (1 / scale), scale byte = E4M3 of
+// min(max|y| / 6, 448), codes = E2M1 of y * (1 / that byte's value).
+__global__ __launch_bounds__(256) void cache_write_nvfp4_kernel(WriteParams p) {
+  const int kv = blockIdx.y;
+  const uint16_t* src = p.src[kv];
+  uint8_t* cache = p.cache[kv];
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < p.fp4_blocks;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = i / p.blocks_per_token;
+    const int bi = int(i - t * p.blocks_per_token);
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const int h = bi / p.blocks_per_head;
+    const int blk = bi - h * p.blocks_per_head;
+    const float g = __fdiv_rn(1.f, p.scale[kv][p.per_head[kv] ? h : 0]);
+    const u32x4* x = reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 16 * int64_t(bi));
+    const u32x4 x0 = x[0], x1 = x[1];
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float y[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      y[2 * j] = __uint_as_float(w[j] << 16) * g;
+      y[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) * g;
+      amax = fmaxf(amax, fmaxf(fabsf(y[2 * j]), fabsf(y[2 * j + 1])));
+    }
+    const float sc = fminf(__fdiv_rn(amax, 6.f), kE4M3Max);
+    const uint32_t sbyte = __builtin_amdgcn_cvt_pk_fp8_f32(sc, 0.f, 0u, false) & 0xffu;
+    const float sv = __builtin_amdgcn_cvt_f32_fp8(int(sbyte), 0);
+    const float r = sv > 0.f ? __fdiv_rn(1.f, sv) : 0.f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo |= e2m1_code(y[j] * r) << (4 * j);
+      hi |= e2m1_code(y[8 + j] * r) << (4 * j);
+    }
+    uint8_t* page = cache + (slot >> p.bt_shift) * p.page_bytes;
+    const int64_t off = slot & p.bt_mask;
+    *reinterpret_cast<u32x2*>(page + off * p.token_bytes + int64_t(h) * p.head_bytes + 8 * blk) =
+        u32x2{lo, hi};
+    page[p.sc_off + off * p.sc_tok + int64_t(h) * p.sc_head + blk] = uint8_t(sbyte);
+  }
+}
+
 bool aligned_to(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 int log2_exact(int v) {
@@ -114,6 +181,13 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   if (s->key_stride % 8 != 0 || s->value_stride % 8 != 0) return FP8PA_ERR_MISALIGNED;
   if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_layout != FP8PA_LAYOUT_NHD && s->kv_layout != FP8PA_LAYOUT_HND) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4) return FP8PA_ERR_INVALID_ARG;
+  const bool nv = s->kv_format == FP8PA_KV_NVFP4;
+  if (nv && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_page_stride < 0) return FP8PA_ERR_INVALID_ARG;
+  const int64_t page_stride =
+      kv_page_stride_of(s->kv_page_stride, s->kv_format, s->block_tokens, s->num_kv_heads, s->head_dim);
+  if (page_stride == 0) return FP8PA_ERR_INVALID_ARG;
   const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
   if ((s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg) ||
       (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads))
@@ -147,17 +221,29 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   p.num_tokens = s->num_tokens;
   p.chunks = s->num_tokens * cpt;
   p.num_slots = int64_t(s->num_blocks) * s->block_tokens;
-  p.page_bytes = int64_t(s->block_tokens) * row;
+  p.page_bytes = page_stride;
   p.chunks_per_token = int32_t(cpt);
   p.chunks_per_head = s->head_dim / 8;
   const bool hnd = s->kv_layout == FP8PA_LAYOUT_HND;
-  p.token_bytes = hnd ? s->head_dim : int32_t(row);
-  p.head_bytes = hnd ? s->block_tokens * s->head_dim : s->head_dim;
+  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes
+  const int32_t erow = nv ? s->head_dim / 2 : s->head_dim;
+  p.token_bytes = hnd ? erow : s->num_kv_heads * erow;
+  p.head_bytes = hnd ? s->block_tokens * erow : erow;
+  p.sc_off = s->num_kv_heads * s->block_tokens * (s->head_dim / 2);
+  p.sc_tok = hnd ? s->head_dim / 16 : s->num_kv_heads * (s->head_dim / 16);
+  p.sc_head = hnd ? s->block_tokens * (s->head_dim / 16) : s->head_dim / 16;
+  p.blocks_per_head = s->head_dim / 16;
+  p.blocks_per_token = s->num_kv_heads * p.blocks_per_head;
+  p.fp4_blocks = s->num_tokens * p.blocks_per_token;
   p.bt_shift = bt_shift;
   p.bt_mask = s->block_tokens - 1;
 
-  const int64_t blocks = (p.chunks + 255) / 256;
+  const int64_t work = nv ? p.fp4_blocks : p.chunks;
+  const int64_t blocks = (work + 255) / 256;
   const dim3 grid(unsigned(blocks < 4096 ? blocks : 4096), 2), block(256);
-  cache_write_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
+  if (nv)
+    cache_write_nvfp4_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
+  else
+    cache_write_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }

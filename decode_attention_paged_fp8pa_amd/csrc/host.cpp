@@ -44,6 +44,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     return FP8PA_ERR_INVALID_ARG;
   if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_layout != FP8PA_LAYOUT_NHD && s->kv_layout != FP8PA_LAYOUT_HND) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format == FP8PA_KV_NVFP4 && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_page_stride < 0) return FP8PA_ERR_INVALID_ARG;
   const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
   if (s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg)
     return FP8PA_ERR_INVALID_ARG;
@@ -67,8 +70,10 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   p.bt_shift = log2i(p.bt);
 
   // One page (all kv heads of bt tokens) must be addressable with 32-bit offsets.
-  const int64_t page_bytes = int64_t(p.bt) * p.Hkv * p.D;
-  if (page_bytes > (int64_t(1) << 30)) return FP8PA_ERR_UNSUPPORTED;
+  p.fmt = s->kv_format;
+  p.page_stride = kv_page_stride_of(s->kv_page_stride, p.fmt, p.bt, p.Hkv, p.D);
+  if (p.page_stride == 0) return FP8PA_ERR_INVALID_ARG;
+  if (p.page_stride > (int64_t(1) << 30)) return FP8PA_ERR_UNSUPPORTED;
   const int64_t rows64 = int64_t(p.G) * p.q_len;
   if (rows64 > (int64_t(1) << 20)) return FP8PA_ERR_UNSUPPORTED;
   p.rows = int32_t(rows64);
@@ -76,7 +81,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // Kernel variant: FP8 MFMA where a kv head has enough query rows to fill a
   // useful part of the 16-wide MFMA tile, VALU dot products otherwise (the
   // grouped-nf4-gemm selector's fp8-vs-f32 split, re-derived for gfx950).
-  const bool mfma_ok = p.bt >= 16;
+  // (NVFP4 pages are read by the VALU kernel: its lanes each take one
+  // 16-element block, whose scale then multiplies a partial dot product.)
+  const bool mfma_ok = p.bt >= 16 && p.fmt == FP8PA_KV_E4M3;
   if (s->flags & FP8PA_FLAG_FORCE_MFMA) {
     if (!mfma_ok) return FP8PA_ERR_UNSUPPORTED;
     p.variant = kVariantMfma;

@@ -79,10 +79,14 @@ struct Params {
   float* lse;
   float* part_o;
   float* part_lse;
-  int64_t page_bytes;  // bt * Hkv * D
+  int64_t page_bytes;  // bytes between pages of a pool (the page size when dense)
   int32_t tok_stride;  // bytes between token slots of a page: Hkv * D, or D head-major
   int32_t head_stride; // bytes between kv heads of a page: D, or bt * D head-major
   int32_t grp_bytes;   // bytes a 16-token group's descriptor spans from its base
+  // NVFP4 pages (tok_stride / head_stride then count data-region bytes):
+  int32_t sc_off;      // byte offset of a page's scale region
+  int32_t sc_tok;      // scale bytes between token slots
+  int32_t sc_head;     // scale bytes between kv heads
   int32_t B, q_len, Hq, Hkv, G, rows, row_groups, hg;
   int32_t upi;           // workgroups per (sequence, split) item
   int32_t num_splits;    // partial slots per query row
@@ -868,12 +872,37 @@ partial_mfma_kernel(Params p) {
   }
 }
 
+// Sixteen NVFP4 elements (8 data bytes, element 2i in the low nibble of byte
+// i) as floats: E2M1 decodes exactly, so the conversion's scale is 1.
+__device__ __forceinline__ void fp4x16_to_f32(u32x2 w, float* f) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t x = h == 0 ? w.x : w.y;
+    const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
+    const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
+    const f32x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
+    const f32x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
+    f[8 * h + 0] = b0.x;
+    f[8 * h + 1] = b0.y;
+    f[8 * h + 2] = b1.x;
+    f[8 * h + 3] = b1.y;
+    f[8 * h + 4] = b2.x;
+    f[8 * h + 5] = b2.y;
+    f[8 * h + 6] = b3.x;
+    f[8 * h + 7] = b3.y;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// VALU dot-product partial kernel: D/16 lanes per token, 16 bytes per lane,
-// 4 query rows per wavefront.  Lane l: token kk = l / (D/16) of a round,
-// chunk c = l % (D/16), dims [16 c, 16 c + 16).
+// VALU dot-product partial kernel: D/16 lanes per token, 16 elements per
+// lane, 4 query rows per wavefront.  Lane l: token kk = l / (D/16) of a
+// round, chunk c = l % (D/16), dims [16 c, 16 c + 16).
+//
+// FMT = FP8PA_KV_NVFP4: a lane's 16 elements of a token are one NVFP4 block
+// (8 data bytes and one E4M3 scale byte), so the block scale multiplies the
+// lane's partial q.K before the cross-lane sum, and P before it meets V.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   constexpr int LPK = D / 16;    // lanes per token
   constexpr int KPI = 64 / LPK;  // tokens per round
@@ -937,39 +966,61 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
     for (int j = 0; j < 16; ++j) acc[rr][j] = 0.f;
   }
 
+  constexpr bool NV = FMT == FP8PA_KV_NVFP4;
   const int tok = p.tok_stride;
-  const uint8_t* kbase_g = p.k_cache + (size_t)w.g * (size_t)p.head_stride + 16 * c;
-  const uint8_t* vbase_g = p.v_cache + (size_t)w.g * (size_t)p.head_stride + 16 * c;
+  // a lane's bytes of a token: 16 E4M3 codes, or 8 NVFP4 data bytes and one scale byte
+  const size_t lane_off = (size_t)w.g * (size_t)p.head_stride + (NV ? 8 : 16) * c;
+  const uint8_t* kbase_g = p.k_cache + lane_off;
+  const uint8_t* vbase_g = p.v_cache + lane_off;
+  const size_t sc_lane = (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head + c;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
 
   for (int tt = ts; tt < te; ++tt) {
     const int kb = tt * kTileTokens;
     u32x4 kr[R], vr[R];
+    float ksc[R], vsc[R];  // NVFP4 block scales of the lane's block of each token
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       const int key = kb + rho * KPI + kk;
       kr[rho] = u32x4{0u, 0u, 0u, 0u};
       vr[rho] = u32x4{0u, 0u, 0u, 0u};
+      ksc[rho] = 0.f;
+      vsc[rho] = 0.f;
       if (key >= ulo && key < uhi) {
         const int page = btab[key >> p.bt_shift];
-        const size_t off = (size_t)page * (size_t)p.page_bytes + (size_t)(key & p.bt_mask) * tok;
-        kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
-        vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
+        const size_t pbase = (size_t)page * (size_t)p.page_bytes;
+        const size_t off = pbase + (size_t)(key & p.bt_mask) * tok;
+        if constexpr (NV) {
+          const u32x2 kd = *reinterpret_cast<const u32x2*>(kbase_g + off);
+          const u32x2 vd = *reinterpret_cast<const u32x2*>(vbase_g + off);
+          kr[rho] = u32x4{kd.x, kd.y, 0u, 0u};
+          vr[rho] = u32x4{vd.x, vd.y, 0u, 0u};
+          const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
+          ksc[rho] = __builtin_amdgcn_cvt_f32_fp8(int(p.k_cache[soff]), 0);
+          vsc[rho] = __builtin_amdgcn_cvt_f32_fp8(int(p.v_cache[soff]), 0);
+        } else {
+          kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
+          vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
+        }
       }
     }
     float x[R][RPG];
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       float kf[16];
-      const uint32_t kw[4] = {kr[rho].x, kr[rho].y, kr[rho].z, kr[rho].w};
+      if constexpr (NV) {
+        fp4x16_to_f32(u32x2{kr[rho].x, kr[rho].y}, kf);
+      } else {
+        const uint32_t kw[4] = {kr[rho].x, kr[rho].y, kr[rho].z, kr[rho].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], true);
-        kf[4 * j + 0] = lo.x;
-        kf[4 * j + 1] = lo.y;
-        kf[4 * j + 2] = hi.x;
-        kf[4 * j + 3] = hi.y;
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], true);
+          kf[4 * j + 0] = lo.x;
+          kf[4 * j + 1] = lo.y;
+          kf[4 * j + 2] = hi.x;
+          kf[4 * j + 3] = hi.y;
+        }
       }
       const int key = kb + rho * KPI + kk;
 #pragma unroll
@@ -977,6 +1028,7 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) d = fmaf(kf[j], qf[rr][j], d);
+        if constexpr (NV) d *= ksc[rho];
 #pragma unroll
         for (int s = 1; s < LPK; s <<= 1) d += xor_shfl(d, s);
         x[rho][rr] = (key >= rows[rr].klo && key < rows[rr].khi) ? d : -INFINITY;
@@ -1002,22 +1054,29 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       float vf[16];
-      const uint32_t vw[4] = {vr[rho].x, vr[rho].y, vr[rho].z, vr[rho].w};
+      if constexpr (NV) {
+        fp4x16_to_f32(u32x2{vr[rho].x, vr[rho].y}, vf);
+      } else {
+        const uint32_t vw[4] = {vr[rho].x, vr[rho].y, vr[rho].z, vr[rho].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], true);
-        vf[4 * j + 0] = lo.x;
-        vf[4 * j + 1] = lo.y;
-        vf[4 * j + 2] = hi.x;
-        vf[4 * j + 3] = hi.y;
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], true);
+          vf[4 * j + 0] = lo.x;
+          vf[4 * j + 1] = lo.y;
+          vf[4 * j + 2] = hi.x;
+          vf[4 * j + 3] = hi.y;
+        }
       }
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
         const float pp = x[rho][rr];
         lsum[rr] += pp;
+        // (NVFP4: the block scale of V joins P; a key outside the span has
+        // P = 0 and scale 0)
+        const float pv = NV ? pp * vsc[rho] : pp;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[rr][j] = fmaf(pp, vf[j], acc[rr][j]);
+        for (int j = 0; j < 16; ++j) acc[rr][j] = fmaf(pv, vf[j], acc[rr][j]);
       }
     }
   }
@@ -1207,6 +1266,16 @@ __global__ void debug_e4m3_kernel(const uint8_t* codes, float* out, int n) {
   out[i] = v.x;
 }
 
+__global__ void debug_nvfp4_kernel(const uint8_t* data, const uint8_t* scales, float* out, int n) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  float f[16];
+  fp4x16_to_f32(*reinterpret_cast<const u32x2*>(data + 8 * size_t(k)), f);
+  const float sc = __builtin_amdgcn_cvt_f32_fp8(int(scales[k]), 0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) out[16 * size_t(k) + j] = f[j] * sc;
+}
+
 __global__ void debug_wave_ops_kernel(const int32_t* in, int vmax, int32_t* out) {
   const int lane = threadIdx.x & 63;
   const int v = in[lane];
@@ -1259,7 +1328,10 @@ template <int D>
 hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
   if (pl.variant != kVariantMfma) {
-    partial_dot_kernel<D><<<grid, block, 0, st>>>(prm);
+    if (pl.fmt == FP8PA_KV_NVFP4)
+      partial_dot_kernel<D, FP8PA_KV_NVFP4><<<grid, block, 0, st>>>(prm);
+    else
+      partial_dot_kernel<D, FP8PA_KV_E4M3><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 64) {
     // non-temporal loads only where a wavefront reads whole lines (paired heads)
     if (pl.pr == 2)
@@ -1372,10 +1444,15 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   prm.part_o = pl.direct ? nullptr : static_cast<float*>(workspace);
   prm.part_lse =
       pl.direct ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.off_lse);
-  prm.page_bytes = int64_t(pl.bt) * pl.Hkv * pl.D;
+  prm.page_bytes = pl.page_stride;
   const bool hnd = shape->kv_layout == FP8PA_LAYOUT_HND;
-  prm.tok_stride = hnd ? pl.D : pl.Hkv * pl.D;
-  prm.head_stride = hnd ? pl.bt * pl.D : pl.D;
+  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes
+  const int32_t row = pl.fmt == FP8PA_KV_NVFP4 ? pl.D / 2 : pl.D;
+  prm.tok_stride = hnd ? row : pl.Hkv * row;
+  prm.head_stride = hnd ? pl.bt * row : row;
+  prm.sc_off = pl.Hkv * pl.bt * (pl.D / 2);
+  prm.sc_tok = hnd ? pl.D / 16 : pl.Hkv * (pl.D / 16);
+  prm.sc_head = hnd ? pl.bt * (pl.D / 16) : pl.D / 16;
   // a group's tokens, plus with paired head-major heads the second head's
   prm.grp_bytes = (pl.pr == 2 && hnd) ? prm.head_stride + 16 * pl.D : 16 * prm.tok_stride;
   prm.q_len = pl.q_len;
@@ -1474,6 +1551,16 @@ fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 
+fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
+                               void* stream) {
+  if (n < 0 || (n > 0 && (!data || !scales || !out))) return FP8PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(data) % 8 != 0) return FP8PA_ERR_MISALIGNED;
+  if (n == 0) return FP8PA_OK;
+  debug_nvfp4_kernel<<<dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      data, scales, out, n);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
 fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream) {
   if (!in || !out || vmax < 0) return FP8PA_ERR_INVALID_ARG;
   debug_wave_ops_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(in, vmax, out);
@@ -1487,7 +1574,7 @@ fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, 
 }
 
 const char* fp8pa_version(void) {
-  return "fp8pa 0.1.0 (HIP, gfx950; FP8-MFMA and VALU partial kernels, LSE merge)";
+  return "fp8pa 0.1.0 (HIP, gfx950; FP8-MFMA and VALU partial kernels, E4M3 and NVFP4 pages, LSE merge)";
 }
 
 }  // extern "C"

@@ -34,6 +34,23 @@ inline int32_t k_group_shift(int32_t k_groups, int32_t head_dim) {
   return s;
 }
 
+// Bytes of one page of one pool as the format lays it out (E4M3: bt * Hkv *
+// D; NVFP4: a data region of bt * Hkv * D / 2 bytes, then a scale region of
+// bt * Hkv * D / 16).
+inline int64_t kv_page_bytes(int32_t kv_format, int32_t bt, int32_t hkv, int32_t d) {
+  const int64_t rows = int64_t(bt) * hkv;
+  return kv_format == FP8PA_KV_NVFP4 ? rows * (d / 2 + d / 16) : rows * d;
+}
+
+// The stride between a pool's pages: the caller's, or the dense page size.
+// 0 when the caller's stride is shorter than a page or not a multiple of 16.
+inline int64_t kv_page_stride_of(int64_t stride, int32_t kv_format, int32_t bt, int32_t hkv, int32_t d) {
+  const int64_t dense = kv_page_bytes(kv_format, bt, hkv, d);
+  if (stride == 0) return dense;
+  if (stride < dense || stride % 16 != 0) return 0;
+  return stride;
+}
+
 enum Variant : int32_t { kVariantDot = 0, kVariantMfma = 1 };
 
 struct Plan {
@@ -47,6 +64,8 @@ struct Plan {
   int32_t pr;              // kv heads per wavefront (MFMA at D = 64 with <= 8 rows: 2)
   int32_t nb;              // 16-row blocks per wavefront (MFMA kernel; 1 or 2)
   int32_t nt;              // 1: non-temporal K/V loads (each byte read by one wavefront)
+  int32_t fmt;             // FP8PA_KV_E4M3 or FP8PA_KV_NVFP4
+  int64_t page_stride;     // bytes between pages of a pool
   int32_t upi;             // workgroups per (sequence, split) item: (Hkv / hg) * row_groups
   int32_t split_mode;      // FP8PA_SPLIT_*
   int32_t num_splits;      // partial slots per query row

@@ -79,6 +79,15 @@ typedef enum fp8pa_status {
                               on a single RTX 5090", KV cache row and writer: a head's
                               tokens lie D bytes apart, heads bt * D apart) */
 
+/* Element format of the KV pools (fp8pa_shape.kv_format, fp8pa_write_shape.kv_format). */
+#define FP8PA_KV_E4M3  0 /* one OCP E4M3 byte per element: page = [bt][Hkv][D] or [Hkv][bt][D] */
+#define FP8PA_KV_NVFP4 1 /* NVFP4 (gist "Qwen3.8-27B ... on a single RTX 5090", writer kernel
+                            reshape_and_cache_nvfp4_kernel): each page is a data region of
+                            4-bit E2M1 codes, two per byte (element 2i in the low nibble),
+                            rows of D/2 bytes, followed by a scale region of one E4M3 byte per
+                            16 elements, rows of D/16 bytes; rows are ordered by kv_layout.
+                            A value reads as E2M1(code) * E4M3(block scale) * k_scale (v_scale). */
+
 /* Host-known description of one decode call. */
 typedef struct fp8pa_shape {
   int32_t batch;              /* B >= 1 sequences */
@@ -99,12 +108,17 @@ typedef struct fp8pa_shape {
                                  16: K scale groups along head_dim, D / k_groups >= 32,
                                  group j covering dims [j D / k_groups, (j+1) D / k_groups) */
   int32_t kv_layout;          /* FP8PA_LAYOUT_NHD (0) or FP8PA_LAYOUT_HND (1), both pools */
+  int32_t kv_format;          /* FP8PA_KV_E4M3 (0) or FP8PA_KV_NVFP4 (1; needs k_groups <= 1,
+                                 runs the VALU kernel) */
   int32_t window;             /* <= 0: none; W > 0: the last W positions */
   float sm_scale;             /* softmax scale applied to q.K; finite */
   int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
                                  splits at most (the MFMA kernel still splits so
                                  that no split spans more than 128 tiles) */
   int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
+  int64_t kv_page_stride;     /* bytes between consecutive pages of each pool; 0 = one page's
+                                 own size (dense pools).  Larger strides let K and V pages
+                                 interleave ([K page | V page] per block).  A multiple of 16. */
 } fp8pa_shape;
 
 /* How the keys of a sequence are divided among workgroups. */
@@ -237,6 +251,15 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
  * to nearest with ties to even and saturated to +-448 (the FN format has no
  * infinity); a NaN element gives a NaN code.  fp8pa_decode then reads
  * decode(code) * scale_h.
+ *
+ * NVFP4 pools (kv_format = FP8PA_KV_NVFP4): each 16-element block of a
+ * head's row becomes one E4M3 scale byte and 16 E2M1 codes.  The quantizer
+ * the gist calls is not printed; this library takes, per block,
+ * y = fp32(x * fp32(1 / scale_h)), s = fp32(max|y| / 6), the scale byte =
+ * E4M3 of min(s, 448) (nearest, ties to even), and the codes = E2M1 of
+ * fp32(y * fp32(1 / E4M3(scale byte))), nearest with ties to even, saturated
+ * at 6, keeping the sign bit (all zero codes when the scale decodes to 0).
+ * NaN inputs are outside the format (their block's bytes are unspecified).
  */
 typedef struct fp8pa_write_shape {
   int64_t num_tokens;      /* T >= 0 rows of key, value and slot_mapping */
@@ -251,6 +274,8 @@ typedef struct fp8pa_write_shape {
   int32_t k_groups;        /* as in fp8pa_shape: each key element is encoded against
                               the scale of its head_dim group */
   int32_t kv_layout;       /* FP8PA_LAYOUT_NHD or FP8PA_LAYOUT_HND, both pools */
+  int32_t kv_format;       /* FP8PA_KV_E4M3 or FP8PA_KV_NVFP4 (k_groups <= 1) */
+  int64_t kv_page_stride;  /* as in fp8pa_shape */
 } fp8pa_write_shape;
 
 /*
@@ -262,7 +287,9 @@ typedef struct fp8pa_write_shape {
  *   slot_mapping  int64 [T]
  *   k_scale       float [k_scale_count]; v_scale float [v_scale_count]
  *   k_cache       e4m3 [num_blocks, bt, Hkv, D] (8-byte aligned), or
- *                 [num_blocks, Hkv, bt, D] with kv_layout = FP8PA_LAYOUT_HND; v_cache alike
+ *                 [num_blocks, Hkv, bt, D] with kv_layout = FP8PA_LAYOUT_HND, or NVFP4
+ *                 pages (see FP8PA_KV_NVFP4); pages kv_page_stride bytes apart when it
+ *                 is not 0; v_cache alike
  *
  * Only the slots named are written.  Two tokens with the same slot race
  * (either may win).  All pointers are device pointers owned by the caller;

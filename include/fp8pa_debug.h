@@ -31,6 +31,12 @@ extern "C" {
  * instruction, for i < n.  codes: uint8 [n]; out: float [n]. */
 fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n, void* stream);
 
+/* out[16 k + j] = element j of NVFP4 block k times its scale, for k < n, as
+ * the VALU kernel decodes them: data is uint8 [n][8] (8-byte aligned; element
+ * 2i in the low nibble of byte i), scales uint8 [n] E4M3, out float [16 n]. */
+fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
+                               void* stream);
+
 /* c = a x b for one 16x16x32 FP8 MFMA: a is E4M3 [16][32] (row-major, M x K),
  * b is E4M3 [32][16] (K x N), c is float [16][16] row-major.  The kernel
  * loads the operands and stores the result with the lane layout the decode

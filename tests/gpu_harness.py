@@ -21,10 +21,12 @@ def upload(wl, device="cuda", kv_layout="NHD"):
     import torch
 
     def pool(c):
+        if getattr(wl, "kv_format", "e4m3") == "nvfp4":
+            return c  # the layout is in the pool's bytes
         return np.ascontiguousarray(c.transpose(0, 2, 1, 3)) if kv_layout == "HND" else c
 
     t = {
-        "layout": kv_layout,
+        "layout": wl.kv_layout if getattr(wl, "kv_format", "e4m3") == "nvfp4" else kv_layout,
         "q": torch.from_numpy(wl.q_bits.view(np.int16)).to(device).view(torch.bfloat16),
         "k": torch.from_numpy(pool(wl.k_cache)).to(device),
         "v": torch.from_numpy(pool(wl.v_cache)).to(device),
@@ -45,7 +47,8 @@ def run(wl, t, num_splits=0, flags=0, out=None, lse=None, workspace=None):
                      window=wl.window, sm_scale=wl.sm_scale,
                      max_seq_len=int(wl.seq_lens.max()), num_splits=num_splits, flags=flags,
                      out=out, lse=lse, workspace=workspace, k_groups=wl.k_groups,
-                     kv_layout=t.get("layout", "NHD"))
+                     kv_layout=t.get("layout", "NHD"), kv_format=getattr(wl, "kv_format", "e4m3"),
+                     num_kv_heads=wl.Hkv, block_tokens=wl.bt)
 
 
 def to_host(out, lse):

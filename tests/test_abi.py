@@ -165,6 +165,12 @@ BAD = [
     (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),   # 16 dims per group at D = 128
     (dict(k_groups=4), _lib.FP8PA_ERR_INVALID_ARG),                     # Hkv scales, not Hkv * 4
     (dict(kv_layout=2), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=2), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=1, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),  # no groups with NVFP4
+    (dict(kv_format=1, flags=2), _lib.FP8PA_ERR_UNSUPPORTED),           # NVFP4 runs the VALU kernel
+    (dict(kv_page_stride=-16), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_page_stride=16 * 8 * 128 - 16), _lib.FP8PA_ERR_INVALID_ARG),  # shorter than a page
+    (dict(kv_page_stride=16 * 8 * 128 + 8), _lib.FP8PA_ERR_INVALID_ARG),   # not a multiple of 16
     (dict(kv_layout=-1), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("nan")), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(sm_scale=float("inf")), _lib.FP8PA_ERR_INVALID_ARG),
@@ -181,6 +187,15 @@ def test_head_pairing_in_both_page_layouts():
     for layout in (fp.FP8PA_LAYOUT_NHD, fp.FP8PA_LAYOUT_HND):
         p = fp.fp8pa_plan(cfg_shape(3, kv_layout=layout), 256)
         assert p["heads_per_wave"] == 2 and p["variant"] == 1
+
+
+def test_nvfp4_plans_take_the_dot_kernel():
+    for k in (2, 3, 4):
+        p = fp.fp8pa_plan(cfg_shape(k, kv_format=fp.FP8PA_KV_NVFP4), 256)
+        assert p["variant"] == 0 and p["rows_per_group"] == 4
+    # a page stride that interleaves K and V pages (2 x the NVFP4 page of cfg2:
+    # 16 tokens x 8 heads x (64 + 8) bytes)
+    fp.fp8pa_plan(cfg_shape(2, kv_format=fp.FP8PA_KV_NVFP4, kv_page_stride=2 * 16 * 8 * 72), 256)
 
 
 def test_row_blocks_for_many_rows():
@@ -355,6 +370,9 @@ WRITE_BAD = [
     (dict(k_groups=6, k_scale_count=48), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(k_groups=4, v_scale_count=32), _lib.FP8PA_ERR_INVALID_ARG),    # V keeps one per head
     (dict(kv_layout=3), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=5), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=1, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=1, kv_page_stride=16 * 8 * 72 - 16), _lib.FP8PA_ERR_INVALID_ARG),
 ]
 
 
