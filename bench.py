@@ -23,10 +23,11 @@ is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
 timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
 fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
-Three widenings are timed after the decode: the headline workload with K
+Four widenings are timed after the decode: the headline workload with K
 scales in four head_dim groups ("k_groups_variant"), the headline and the
-windowed head_dim-64 workloads with head-major pages ("hnd_variant"), and
-chunked prefill,
+windowed head_dim-64 workloads with head-major pages ("hnd_variant"), the
+headline batch with NVFP4 pages ("nvfp4_variant", bytes = D/2 + D/16 per
+token, kv head and side), and chunked prefill,
 q_len 16 to 512 new tokens over a paged context ("prefill", in algorithmic
 TFLOP/s against the dense FP8 peak).
 
@@ -73,7 +74,8 @@ def kv_bytes(wl):
     Per attended token per kv head the method must read D bytes of K and D
     of V; tokens outside every row's window are not counted.
     """
-    return wl.attended_positions() * wl.Hkv * wl.D * 2
+    per_row = (wl.D // 2 + wl.D // 16) if wl.kv_format == "nvfp4" else wl.D
+    return wl.attended_positions() * wl.Hkv * per_row * 2
 
 
 def other_bytes(wl):
@@ -126,21 +128,31 @@ def load_traffic(workload_name):
     return None if not h else int(h["read"] + h["write"])
 
 
-def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD"):
+def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", nvfp4=False):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
-    from workloads import make_config
+    from workloads import CONFIGS, make_config, make_nvfp4_workload
 
     t_gen = time.time()
-    wl = make_config(k, k_groups=k_groups)
-    label = f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "") + ("_hnd" if kv_layout == "HND" else "")
+    if nvfp4:  # the same batch shape with NVFP4 pages (random codes and block scales)
+        c = CONFIGS[k]
+        seq = c["seq"]
+        sls = seq[1] if seq[0] == "fixed" else (list(seq[1]) if seq[0] == "list" else ("uniform", seq[1], seq[2]))
+        wl = make_nvfp4_workload(B=c["B"], q_len=c["q_len"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], bt=c["bt"],
+                                 seq_lens=sls, seed=1000 + k, pool=c["pool"], scale=c["scale"],
+                                 window=c["window"], sinks=c["sinks"], sm_scale=c["sm_scale"],
+                                 kv_layout=kv_layout, name=f"cfg{k}_{c['name']}_nvfp4")
+    else:
+        wl = make_config(k, k_groups=k_groups)
+    label = (f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "") + ("_nvfp4" if nvfp4 else "")
+             + ("_hnd" if kv_layout == "HND" else ""))
     log(f"[bench] {label}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
     dev = torch.device("cuda")
     kvb = kv_bytes(wl)
     copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / max(kvb, 1)))))
     q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    if kv_layout == "HND":  # the same pages stored head-major
+    if kv_layout == "HND" and not nvfp4:  # the same pages stored head-major
         kc0 = torch.from_numpy(np.ascontiguousarray(wl.k_cache.transpose(0, 2, 1, 3))).to(dev)
         vc0 = torch.from_numpy(np.ascontiguousarray(wl.v_cache.transpose(0, 2, 1, 3))).to(dev)
     else:
@@ -153,7 +165,8 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD"):
     vs = torch.from_numpy(wl.v_scale).to(dev)
     sinks = None if wl.sinks is None else torch.from_numpy(wl.sinks).to(dev)
     shape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
-                         max_seq_len=int(wl.seq_lens.max()), k_groups=wl.k_groups, kv_layout=kv_layout)
+                         max_seq_len=int(wl.seq_lens.max()), k_groups=wl.k_groups, kv_layout=kv_layout,
+                         kv_format=wl.kv_format, num_kv_heads=wl.Hkv, block_tokens=wl.bt)
     plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
     nws = fp.fp8pa_workspace_bytes(shape)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
@@ -222,7 +235,8 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD"):
     if plan["merge_launched"]:
         pshape = fp.shape_for(q, kc0, btab, ks, vs, window=wl.window, sm_scale=wl.sm_scale,
                               max_seq_len=int(wl.seq_lens.max()), flags=fp.FP8PA_FLAG_PARTIAL_ONLY,
-                              k_groups=wl.k_groups, kv_layout=kv_layout)
+                              k_groups=wl.k_groups, kv_layout=kv_layout, kv_format=wl.kv_format,
+                              num_kv_heads=wl.Hkv, block_tokens=wl.bt)
 
         def partial_only(i):
             kc, vc = pools[i % copies]
@@ -625,6 +639,14 @@ def main():
                           "partial_us": round(r["partial_ms"] * 1e3, 2), "kv_gbps": round(r["kv_gbps"], 1),
                           "pct_peak": round(r["pct_peak"], 2)}
         del w_
+    # the headline batch with NVFP4 pages (head-major, as the gist runs them)
+    r, w_ = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph, kv_layout="HND",
+                    nvfp4=True)
+    nv = {"workload": r["describe"] + " kv_format=nvfp4 kv_layout=HND", "step_us": round(r["step_ms"] * 1e3, 2),
+          "partial_us": round(r["partial_ms"] * 1e3, 2), "kv_bytes": r["kv_bytes"],
+          "kv_gbps": round(r["kv_gbps"], 1), "pct_peak": round(r["pct_peak"], 2),
+          "tokens_per_s": round(r["tokens_per_s"], 1), "variant": "dot" if r["plan"]["variant"] == 0 else "mfma"}
+    del w_
     prefill = measure_prefill(log)
     cpu = None
     if not args.no_cpu_baseline:
@@ -656,6 +678,7 @@ def main():
             "partial_kv_gbps": round(kg_res["partial_kv_gbps"], 1),
         },
         "hnd_variant": hnd,
+        "nvfp4_variant": nv,
         "prefill": prefill,
         "per_workload": {
             f"cfg{k}": {
