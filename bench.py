@@ -569,6 +569,8 @@ def main():
     ap.add_argument("--configs", default="1,2,3,4,5")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the named decode workloads only (for profiler runs)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for profiler passes that do not follow graphs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -605,7 +607,7 @@ def main():
         cfgs.insert(0, HEADLINE)
     results = {}
     head_wl = None
-    ceiling = copy_ceiling(log)
+    ceiling = None if args.decode_only else copy_ceiling(log)
     for k in cfgs:
         res, wl = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph)
         results[k] = res
@@ -626,11 +628,28 @@ def main():
         "kernel_avg_us": round(h["partial_ms"] * 1e3, 2),
         "algorithmic_bytes_per_launch": h["kv_bytes"],
     }
+    writer = kg = hnd = nv = prefill = None
+    if not args.decode_only:
+        writer, kg, hnd, nv, prefill = widenings(args, log)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head_wl, args.cpu_budget, log)
+    emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill)
+
+
+def widenings(args, log):
+    """The library's widenings, timed after the decode workloads."""
     writer = measure_writer(min(args.steps, 100), log)
     # the headline workload with K scales in 4 head_dim groups per kv head
     kg_res, kg_wl = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph,
                             k_groups=4)
     del kg_wl
+    kg = {
+        "workload": kg_res["describe"], "step_us": round(kg_res["step_ms"] * 1e3, 2),
+        "partial_us": round(kg_res["partial_ms"] * 1e3, 2),
+        "kv_gbps": round(kg_res["kv_gbps"], 1), "pct_peak": round(kg_res["pct_peak"], 2),
+        "partial_kv_gbps": round(kg_res["partial_kv_gbps"], 1),
+    }
     # the headline and the windowed head_dim-64 workloads with head-major pages
     hnd = {}
     for k in (HEADLINE, 3):
@@ -648,9 +667,11 @@ def main():
           "tokens_per_s": round(r["tokens_per_s"], 1), "variant": "dot" if r["plan"]["variant"] == 0 else "mfma"}
     del w_
     prefill = measure_prefill(log)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head_wl, args.cpu_budget, log)
+    return writer, kg, hnd, nv, prefill
+
+
+def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill):
+    """Print the one JSON line."""
     line = {
         "metric": METRIC,
         "value": round(h["kv_gbps"], 1),
@@ -671,12 +692,7 @@ def main():
         "cpu_baseline": cpu,
         "copy_ceiling": ceiling,
         "writer": writer,
-        "k_groups_variant": {
-            "workload": kg_res["describe"], "step_us": round(kg_res["step_ms"] * 1e3, 2),
-            "partial_us": round(kg_res["partial_ms"] * 1e3, 2),
-            "kv_gbps": round(kg_res["kv_gbps"], 1), "pct_peak": round(kg_res["pct_peak"], 2),
-            "partial_kv_gbps": round(kg_res["partial_kv_gbps"], 1),
-        },
+        "k_groups_variant": kg,
         "hnd_variant": hnd,
         "nvfp4_variant": nv,
         "prefill": prefill,
