@@ -81,9 +81,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // Kernel variant: FP8 MFMA where a kv head has enough query rows to fill a
   // useful part of the 16-wide MFMA tile, VALU dot products otherwise (the
   // grouped-nf4-gemm selector's fp8-vs-f32 split, re-derived for gfx950).
-  // (NVFP4 pages are read by the VALU kernel: its lanes each take one
-  // 16-element block, whose scale then multiplies a partial dot product.)
-  const bool mfma_ok = p.bt >= 16 && p.fmt == FP8PA_KV_E4M3;
+  // (NVFP4 pages: a bf16-MFMA kernel at head_dim 64 and 128; otherwise the
+  // VALU kernel, whose lanes each take one 16-element block.)
+  const bool mfma_ok = p.bt >= 16 && (p.fmt == FP8PA_KV_E4M3 || p.D <= 128);
   if (s->flags & FP8PA_FLAG_FORCE_MFMA) {
     if (!mfma_ok) return FP8PA_ERR_UNSUPPORTED;
     p.variant = kVariantMfma;
@@ -98,17 +98,18 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // times cost measurably more).  At D = 256 the MFMA kernel splits head_dim
   // over two wavefronts (they exchange partial scores through LDS), which
   // halves their registers.
-  p.ds = (p.variant == kVariantMfma && p.D == 256) ? 2 : 1;
+  const bool fp8_mfma = p.variant == kVariantMfma && p.fmt == FP8PA_KV_E4M3;
+  p.ds = (fp8_mfma && p.D == 256) ? 2 : 1;
   // At D = 64 with at most 8 query rows per kv head, the MFMA kernel runs
   // two kv heads per wavefront (one 128-byte line per token, all 16 MFMA
   // columns in use); hg then counts head pairs.
-  p.pr = (p.variant == kVariantMfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
+  p.pr = (fp8_mfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
   // More than 16 query rows per kv head (chunked prefill, wide MTP): a
   // wavefront carries two blocks of 16 rows over the same K/V registers, so
   // a tile's loads and V transposes serve both.  (Four blocks need more
   // than the 256 registers MFMA operands can use and measured slower.)
   p.nb = 1;
-  if (p.variant == kVariantMfma && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
+  if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
   p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
   const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;
@@ -146,7 +147,7 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // MFMA kernel's registers allow 4 per SIMD at D = 64 and 2 otherwise
   // (head_dim 256 is split over two wavefronts); the dot kernel's 2.
   const int64_t waves_per_cu =
-      (p.variant == kVariantMfma && p.D == 64 && p.pr == 1 && p.nb == 1) ? 16 : 8;
+      (fp8_mfma && p.D == 64 && p.pr == 1 && p.nb == 1) ? 16 : 8;
   const int64_t target_waves = int64_t(cu_count) * waves_per_cu;
   int64_t target_items = target_waves / waves_per_item;
   if (target_items < 1) target_items = 1;

@@ -53,6 +53,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -133,11 +135,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // heads share a line, and an early-evicted line would be fetched twice.
 constexpr int kLoadNT = 2;
 
-// Loads BYTES (4, 8 or a multiple of 16) at byte offset `off` of buffer `r`
-// with cache policy AUX.
+// Loads BYTES (1, 2, 4, 8 or a multiple of 16) at byte offset `off` of
+// buffer `r` with cache policy AUX (1 and 2 bytes: zero-extended into dst[0]).
 template <int BYTES, int AUX>
 __device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint32_t* dst) {
-  if constexpr (BYTES == 4) {
+  if constexpr (BYTES == 1) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, AUX);
+  } else if constexpr (BYTES == 2) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, AUX);
+  } else if constexpr (BYTES == 4) {
     dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
   } else if constexpr (BYTES == 8) {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
@@ -872,6 +878,326 @@ partial_mfma_kernel(Params p) {
   }
 }
 
+// Eight NVFP4 elements (one data dword, element 2i in the low nibble of byte
+// i) times a block scale, as bf16: E2M1 times an E4M3 scale has at most 6
+// significant bits, so every step is exact.  (The conversion's own scale
+// operand applies only a power of two, hence the fp32 multiply.)
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
+  const f32x2 e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc,
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * sc,
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2) * sc,
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3) * sc};
+  bf16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const bf16x2 h = __builtin_convertvector(e[b], bf16x2);
+    r[2 * b] = h.x;
+    r[2 * b + 1] = h.y;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 pages on the matrix cores (head_dim 64 and 128, kv heads with at
+// least 3 query rows).  The lane layout is the FP8-MFMA kernel's (keys on M,
+// the 16 query rows of one kv head on N, V dims S n + e on M for PV), with
+// bf16 16x16x32 MFMAs: K and V are dequantized in registers to bf16 (exact),
+// the bf16 query is used as it is, and P is rounded to bf16, so neither
+// operand needs a hi + lo split.
+//   K, per 16-token group: lane (n, qd) holds dims [D/4 qd, D/4 (qd + 1)) of
+//     token n: D/8 data bytes and D/64 scale bytes (one per 16 dims); QK
+//     k-step c uses dims D/4 qd + 8 c .. + 7, which lie in one block.
+//   V: lane (n, qd) holds dims [S n, S n + S) (S = D/16, inside one block) of
+//     the 8 tokens kap(qd, j): S/2 data bytes and one scale byte each.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(64 * kMaxWgWaves)
+__attribute__((amdgpu_waves_per_eu(2, 8))) void
+partial_mfma_nvfp4_kernel(Params p) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int S = D / 16;        // V dims per lane
+  constexpr int KD = D / 4;        // K dims per lane per token
+  constexpr int KSTEPS = D / 32;   // QK k-steps of 32 dims (8 per lane)
+  constexpr int KDB = KD / 2;      // K data bytes per lane per token
+  constexpr int KSB = KD / 16;     // K scale bytes per lane per token
+  constexpr int VDB = S / 2;       // V data bytes per lane per token
+  constexpr int AUX = NT ? kLoadNT : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int qd = lane >> 4;
+  Work w = work_head(p, 1);
+  const int kvh = w.g;
+  const int rlane = w.rg * kRowsMfma + n;
+  const float ks = p.k_scale[p.k_per_head ? kvh : 0];
+  const float vs = p.v_scale[p.v_per_head ? kvh : 0];
+  float sink2 = -INFINITY;
+  if (p.sinks && p.direct && rlane < p.rows) {
+    const int qi = rlane / p.G;
+    sink2 = p.sinks[kvh * p.G + (rlane - qi * p.G)] * kLog2e;
+  }
+  work_item(p, w);
+  if (!w.active) return;  // uniform over the workgroup
+  const int L = w.L;
+  const int ulo = w.sp.ulo, uhi = w.sp.uhi;
+  const int r0 = w.rg * kRowsMfma;
+  const int r1 = min(r0 + kRowsMfma, p.rows) - 1;
+  const int qmin = r0 / p.G, qmax = r1 / p.G;
+  const TileRange tr = rows_tiles(p, L, qmin, qmax, w.ts, w.te);
+  const int ts = tr.ts, te = tr.te;
+  const Row row = row_of(p, w.b, kvh, rlane, L);
+
+  if (ts >= te && !p.direct && row.valid && qd == 0)
+    p.part_lse[row.out_row * p.num_splits + w.split] = -INFINITY;
+  if (ts >= te && !p.direct) return;
+
+  // ---- online softmax state (log2 units); the sink enters as a score whose
+  // value vector is zero when this split writes the final output.
+  float m = sink2;
+  float lsum = (qd == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
+  f32x4 O[S];
+#pragma unroll
+  for (int e = 0; e < S; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tok = p.tok_stride;   // data bytes between token slots
+  const int stok = p.sc_tok;      // scale bytes between token slots
+  const uint8_t* kd_g = p.k_cache + (size_t)kvh * (size_t)p.head_stride;
+  const uint8_t* vd_g = p.v_cache + (size_t)kvh * (size_t)p.head_stride;
+  const uint8_t* ks_g = p.k_cache + (size_t)p.sc_off + (size_t)kvh * (size_t)p.sc_head;
+  const uint8_t* vs_g = p.v_cache + (size_t)p.sc_off + (size_t)kvh * (size_t)p.sc_head;
+  const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
+  const uint32_t kdoff = uint32_t(n * tok + KDB * qd);
+  const uint32_t ksoff = uint32_t(n * stok + KSB * qd);
+  uint32_t vdoff[4], vsoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vdoff[j] = uint32_t((4 * qd + j) * tok + VDB * n);
+    vsoff[j] = uint32_t((4 * qd + j) * stok + (S * n) / 16);
+  }
+
+  // Block-table entries of the split in registers, as in the FP8 kernel.
+  int tab[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int tt = ts + 2 * lane + (g >> 1);
+    const int gk = tt * kTileTokens + 16 * (g & 1);
+    const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+    tab[g] = live ? btab[gk >> p.bt_shift] : 0;
+  }
+  // the query row as bf16 operands: k-step c takes dims KD qd + 8 c .. + 7
+  u32x4 qraw[KSTEPS];
+  {
+    const uint16_t* qrow = p.q + row.out_row * D + KD * qd;
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c)
+      qraw[c] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int ihi = L - p.q_len + qmin + 1;
+  const int ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
+
+  struct TileRegs {
+    uint32_t kd[2][KDB / 4];
+    uint32_t ks[2];
+    uint32_t vd[8];
+    uint32_t vs[8];
+  };
+  auto load_tile = [&](int tt, TileRegs& r, int odd) {
+    const int kb = tt * kTileTokens;
+    const int step = ((tt - ts) >> 1) & 63;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const int gk = kb + 16 * grp;
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      const int page = __builtin_amdgcn_readlane(tab[2 * odd + grp], step);
+      const size_t pbase = (size_t)page * (size_t)p.page_bytes;
+      const size_t slot = (size_t)(gk & p.bt_mask);
+      const int nd = live ? 16 * tok : 0;
+      const int ns = live ? 16 * stok : 0;
+      const Rsrc rkd = __builtin_amdgcn_make_buffer_rsrc((void*)(kd_g + pbase + slot * tok), 0, nd, kRsrcWord3);
+      const Rsrc rvd = __builtin_amdgcn_make_buffer_rsrc((void*)(vd_g + pbase + slot * tok), 0, nd, kRsrcWord3);
+      const Rsrc rks = __builtin_amdgcn_make_buffer_rsrc((void*)(ks_g + pbase + slot * stok), 0, ns, kRsrcWord3);
+      const Rsrc rvs = __builtin_amdgcn_make_buffer_rsrc((void*)(vs_g + pbase + slot * stok), 0, ns, kRsrcWord3);
+      buf_load<KDB, AUX>(rkd, kdoff, r.kd[grp]);
+      buf_load<KSB, AUX>(rks, ksoff, &r.ks[grp]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        buf_load<VDB, AUX>(rvd, vdoff[j], &r.vd[4 * grp + j]);
+        buf_load<1, AUX>(rvs, vsoff[j], &r.vs[4 * grp + j]);
+      }
+    }
+  };
+
+  float cr;  // score scale into log2 units (> 0; a negative one flips the query)
+  bf16x8 qb[KSTEPS];
+  auto compute_tile = [&](int tt, TileRegs& r) {
+    const int kb = tt * kTileTokens;
+    const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
+    if (edge) {
+      // bytes of tokens outside the sequence's attended span (possibly NaN
+      // scale codes) become 0
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+        const bool in_span = key >= ulo && key < uhi;
+        r.vd[j] = in_span ? r.vd[j] : 0u;
+        r.vs[j] = in_span ? r.vs[j] : 0u;
+      }
+    }
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    float kscale[2][KSB];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+      for (int i = 0; i < KSB; ++i) kscale[grp][i] = __builtin_amdgcn_cvt_f32_fp8(int(r.ks[grp] >> (8 * i)) & 0xff, 0);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const bf16x8 ka = fp4x8_to_bf16(r.kd[0][c], kscale[0][c / 2]);
+      const bf16x8 kbv = fp4x8_to_bf16(r.kd[1][c], kscale[1][c / 2]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbv, qb[c], sb, 0, 0, 0);
+    }
+    float sv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sv[j] = sa[j];
+      sv[j + 4] = sb[j];
+    }
+    if (edge) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+        sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
+      }
+    }
+    float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    ms = max_over_groups(ms);
+    const float mx = ms * cr;
+    const bool bump = mx > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      const float mnew = bump ? mx : m;
+      const float alpha = bump ? exp2_fast(m - mnew) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int e = 0; e < S; ++e) O[e] *= alpha;
+      m = mnew;
+    }
+    const float noff = m == -INFINITY ? 0.f : -m;
+    float pj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], cr, noff));
+    lsum += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+    bf16x8 P;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
+      P[j] = h.x;
+      P[j + 1] = h.y;
+    }
+    // V^T operands: element j of operand e = V[kap(qd, j)][S n + e]
+    float vf[8][S];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sc = __builtin_amdgcn_cvt_f32_fp8(int(r.vs[j]) & 0xff, 0);
+      f32x2 e2[4];
+      e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 0) * sc;
+      e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 1) * sc;
+      if constexpr (S == 8) {
+        e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 2) * sc;
+        e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 3) * sc;
+      }
+#pragma unroll
+      for (int b = 0; b < S / 2; ++b) {
+        vf[j][2 * b] = e2[b].x;
+        vf[j][2 * b + 1] = e2[b].y;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+      bf16x8 vt;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 h = __builtin_convertvector((f32x2{vf[j][e], vf[j + 1][e]}), bf16x2);
+        vt[j] = h.x;
+        vt[j + 1] = h.y;
+      }
+      O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, P, O[e], 0, 0, 0);
+    }
+  };
+
+  TileRegs ta, tb;
+  load_tile(ts, ta, 0);
+  load_tile(ts + 1, tb, 1);
+
+  // ---- stage the query: bf16 as it is; the sign of the score scale moves
+  // into the query so that fma(S, cr, .) keeps a -inf mask at -inf
+  {
+    const float c0 = p.sm_scale * ks * kLog2e;
+    const uint32_t flip = c0 < 0.f ? 0x80008000u : 0u;
+    cr = fmaxf(fabsf(c0), 1e-30f);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const u32x4 v = qraw[c] ^ flip;
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qb[c][2 * i] = __builtin_bit_cast(__bf16, uint16_t(wv[i] & 0xffffu));
+        qb[c][2 * i + 1] = __builtin_bit_cast(__bf16, uint16_t(wv[i] >> 16));
+      }
+    }
+  }
+
+  for (int tt = ts; tt < te; tt += 2) {
+    compute_tile(tt, ta);
+    if (tt + 1 >= te) break;
+    load_tile(tt + 2, ta, 0);
+    compute_tile(tt + 1, tb);
+    load_tile(tt + 3, tb, 1);
+  }
+
+  // ---- epilogue: l over the 4 lane groups, normalise, write
+  lsum += xor_shfl(lsum, 16);
+  lsum += xor_shfl(lsum, 32);
+  if (!row.valid) return;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : vs / lsum;
+  const float lse = empty ? -INFINITY : (m + log2_fast(lsum)) * kLn2;
+  // O[e][i] is output dim S * (4 qd + i) + e of this lane's row
+  const int dlane = S * 4 * qd;
+  if (p.direct) {
+    uint16_t* orow = p.out + row.out_row * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t pk[S / 2];
+#pragma unroll
+      for (int e = 0; e < S; e += 2) pk[e / 2] = pack_bf16x2(O[e][i] * inv, O[e + 1][i] * inv);
+      uint16_t* dst = orow + dlane + S * i;
+      if constexpr (S == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+      } else {
+#pragma unroll
+        for (int v = 0; v < S / 8; ++v)
+          reinterpret_cast<u32x4*>(dst)[v] = u32x4{pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]};
+      }
+    }
+    if (p.lse && qd == 0) p.lse[row.out_row] = lse;
+  } else {
+    const size_t slot = row.out_row * p.num_splits + w.split;
+    if (!empty) {
+      float* prow = p.part_o + slot * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = prow + dlane + S * i;
+#pragma unroll
+        for (int v = 0; v < S / 4; ++v)
+          reinterpret_cast<f32x4*>(dst)[v] =
+              f32x4{O[4 * v][i] * inv, O[4 * v + 1][i] * inv, O[4 * v + 2][i] * inv, O[4 * v + 3][i] * inv};
+      }
+    }
+    if (qd == 0) p.part_lse[slot] = lse;
+  }
+}
+
 // Sixteen NVFP4 elements (8 data bytes, element 2i in the low nibble of byte
 // i) as floats: E2M1 decodes exactly, so the conversion's scale is 1.
 __device__ __forceinline__ void fp4x16_to_f32(u32x2 w, float* f) {
@@ -1327,7 +1653,16 @@ bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(pt
 template <int D>
 hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
-  if (pl.variant != kVariantMfma) {
+  if (pl.variant == kVariantMfma && pl.fmt == FP8PA_KV_NVFP4) {
+    if constexpr (D == 64)
+      partial_mfma_nvfp4_kernel<64, 0><<<grid, block, 0, st>>>(prm);
+    else if constexpr (D == 128) {
+      if (pl.nt)
+        partial_mfma_nvfp4_kernel<128, 1><<<grid, block, 0, st>>>(prm);
+      else
+        partial_mfma_nvfp4_kernel<128, 0><<<grid, block, 0, st>>>(prm);
+    }
+  } else if (pl.variant != kVariantMfma) {
     if (pl.fmt == FP8PA_KV_NVFP4)
       partial_dot_kernel<D, FP8PA_KV_NVFP4><<<grid, block, 0, st>>>(prm);
     else

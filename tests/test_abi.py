@@ -167,7 +167,7 @@ BAD = [
     (dict(kv_layout=2), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_format=2), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_format=1, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),  # no groups with NVFP4
-    (dict(kv_format=1, flags=2), _lib.FP8PA_ERR_UNSUPPORTED),           # NVFP4 runs the VALU kernel
+    (dict(kv_format=1, flags=2, block_tokens=8, block_table_stride=1024), _lib.FP8PA_ERR_UNSUPPORTED),  # MFMA needs bt >= 16
     (dict(kv_page_stride=-16), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_page_stride=16 * 8 * 128 - 16), _lib.FP8PA_ERR_INVALID_ARG),  # shorter than a page
     (dict(kv_page_stride=16 * 8 * 128 + 8), _lib.FP8PA_ERR_INVALID_ARG),   # not a multiple of 16
@@ -189,10 +189,17 @@ def test_head_pairing_in_both_page_layouts():
         assert p["heads_per_wave"] == 2 and p["variant"] == 1
 
 
-def test_nvfp4_plans_take_the_dot_kernel():
-    for k in (2, 3, 4):
+def test_nvfp4_plans():
+    # head_dim 64 and 128: the bf16-MFMA kernel, one head and 16 rows per
+    # wavefront; head_dim 256: the VALU kernel
+    for k in (2, 3):
         p = fp.fp8pa_plan(cfg_shape(k, kv_format=fp.FP8PA_KV_NVFP4), 256)
-        assert p["variant"] == 0 and p["rows_per_group"] == 4
+        assert (p["variant"], p["rows_per_group"], p["heads_per_wave"], p["waves_per_head"]) == (1, 16, 1, 1)
+    p = fp.fp8pa_plan(cfg_shape(4, kv_format=fp.FP8PA_KV_NVFP4), 256)
+    assert p["variant"] == 0 and p["rows_per_group"] == 4
+    with pytest.raises(fp.Fp8paError) as e:
+        fp.fp8pa_plan(cfg_shape(4, kv_format=fp.FP8PA_KV_NVFP4, flags=fp.FP8PA_FLAG_FORCE_MFMA), 256)
+    assert e.value.status == _lib.FP8PA_ERR_UNSUPPORTED
     # a page stride that interleaves K and V pages (2 x the NVFP4 page of cfg2:
     # 16 tokens x 8 heads x (64 + 8) bytes)
     fp.fp8pa_plan(cfg_shape(2, kv_format=fp.FP8PA_KV_NVFP4, kv_page_stride=2 * 16 * 8 * 72), 256)

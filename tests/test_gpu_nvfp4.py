@@ -57,6 +57,11 @@ NV_SMALL = {
     "padded_stride": dict(B=2, q_len=2, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[200, 77], page_stride=4864,
                           sinks=True),
     "tiny_seqs": dict(B=4, q_len=1, Hq=8, Hkv=2, D=64, bt=16, seq_lens=[1, 17, 32, 33]),
+    "d64_hnd_window_per_head": dict(B=3, q_len=1, Hq=32, Hkv=4, D=64, bt=32, seq_lens=[500, 96, 1200],
+                                    window=200, sinks=True, kv_layout="HND", scale=("per_head", 0.02, 0.1)),
+    "prefill_q40": dict(B=2, q_len=40, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[40, 333], sinks=True),
+    "batch130": dict(B=130, q_len=1, Hq=8, Hkv=1, D=128, bt=16,
+                     seq_lens=[1 + (37 * i * i + 11 * i) % 600 for i in range(130)]),
 }
 _cache = {}
 
@@ -69,11 +74,14 @@ def _nv(name):
 
 
 @pytest.mark.parametrize("name", list(NV_SMALL))
-@pytest.mark.parametrize("ns", [0, 1, 3])
-def test_nvfp4_parity_small(name, ns):
+@pytest.mark.parametrize("flags,ns", [(0, 0), (0, 1), (0, 3), (fp.FP8PA_FLAG_FORCE_DOT, 0),
+                                      (fp.FP8PA_FLAG_FORCE_DOT, 3)])
+def test_nvfp4_parity_small(name, flags, ns):
+    """The planner's kernel (bf16 MFMA at head_dim 64/128 with bt >= 16 and
+    >= 3 rows per kv head, else the VALU kernel) and the forced VALU kernel."""
     wl, t, (ro, rl) = _nv(name)
-    out, lse = to_host(*run(wl, t, num_splits=ns))
-    compare(out, lse, ro, rl, label=f"nvfp4 {name} splits={ns}")
+    out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"nvfp4 {name} flags={flags} splits={ns}")
 
 
 def test_nvfp4_interleaved_k_and_v_pages():
