@@ -409,3 +409,47 @@ def test_context_parallel_shards_merge():
     fp.fp8pa_merge(2, rows, wl.Hq, wl.D, po, pl, t["sinks"], out, lse)
     o, l = to_host(out, lse)
     compare(o, l, ro, rl, label="two KV shards + merge")
+
+
+# ------------------------------------------------------------- size limits
+
+@pytest.mark.parametrize("flags", [0, DOT])
+def test_pool_beyond_4_gib(flags):
+    """A 4.9 GiB pool per side (300,000 pages of 16 KiB) whose attended pages
+    sit at its top: page offsets need more than 32 bits.  The oracle reads
+    the same pages renumbered into a small pool (page permutation is pinned
+    to be exact)."""
+    wl = make_workload(B=2, q_len=1, Hq=32, Hkv=8, D=128, bt=16, seq_lens=[700, 1500],
+                       scale=("per_head", 0.02, 0.1), sinks=True, seed=77, table="identity")
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    nbig = 300_000
+    top = nbig - wl.num_blocks                       # small page j lives at big page top + j
+    page = wl.bt * wl.Hkv * wl.D
+    assert top * page > (1 << 32)
+    kbig = torch.full((nbig, wl.bt, wl.Hkv, wl.D), oracle_poison(), dtype=torch.uint8, device="cuda")
+    vbig = torch.full_like(kbig, oracle_poison())
+    kbig[top:] = torch.from_numpy(wl.k_cache).cuda()
+    vbig[top:] = torch.from_numpy(wl.v_cache).cuda()
+    t = upload(wl)
+    t["k"], t["v"] = kbig, vbig
+    t["bt"] = torch.from_numpy(np.where(wl.block_table >= 0, wl.block_table + top, -1).astype(np.int32)).cuda()
+    out, lse = to_host(*run(wl, t, flags=flags))
+    compare(out, lse, ro, rl, label=f"4.9 GiB pool flags={flags}")
+    del kbig, vbig, t
+    torch.cuda.empty_cache()
+
+
+def oracle_poison():
+    from workloads import POISON_CODE
+    return POISON_CODE
+
+
+@pytest.mark.parametrize("D,flags,ns", [(128, 0, 0), (128, DOT, 0), (256, 0, 3), (64, 0, 0), (64, DOT, 2)])
+def test_largest_pages(D, flags, ns):
+    """1024-token pages (the largest the ABI takes), with windows that start
+    and end inside pages."""
+    wl = make_workload(B=2, q_len=2, Hq=8, Hkv=2, D=D, bt=1024, seq_lens=[2500, 700], window=900,
+                       sinks=True, seed=88 + D, scale=("per_head", 0.02, 0.1))
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, upload(wl), num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"bt 1024 D {D} flags={flags} splits={ns}")

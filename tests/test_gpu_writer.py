@@ -138,3 +138,26 @@ def test_writer_then_decode_round_trip(kg):
                            sm_scale=1 / np.sqrt(D), k_groups=kg)
     o, l = to_host(out, lse)
     compare(o, l, ro, rl, label="cache_write -> decode")
+
+
+def test_writer_slots_beyond_4_gib():
+    """Slots in the top pages of a 4.9 GiB pool (byte offsets past 2^32)."""
+    rng = np.random.default_rng(31)
+    T, Hkv, D, bt, nb = 40, 8, 128, 16, 300_000
+    key = torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(torch.bfloat16).cuda()
+    value = -key
+    slots = (nb * bt - 1 - rng.permutation(4 * bt)[:T]).astype(np.int64)
+    assert int(slots.min()) // bt * bt * Hkv * D > (1 << 32)
+    ks = np.full((Hkv,), 0.05, np.float32)
+    kc = torch.zeros((nb, bt, Hkv, D), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    fp.cache_write(key, value, torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
+                   torch.from_numpy(ks).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    top = nb - 4
+    small = np.zeros((4, bt, Hkv, D), np.uint8)
+    wk, wv = oracle.cache_write(_bits(key), _bits(value), slots - top * bt, ks, ks, small, small)
+    assert np.array_equal(kc[top:].cpu().numpy(), wk) and np.array_equal(vc[top:].cpu().numpy(), wv)
+    assert int(kc[:top].sum().item()) == 0
+    del kc, vc
+    torch.cuda.empty_cache()
