@@ -104,12 +104,14 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // two kv heads per wavefront (one 128-byte line per token, all 16 MFMA
   // columns in use); hg then counts head pairs.
   p.pr = (fp8_mfma && p.D == 64 && p.rows <= 8 && p.Hkv % 2 == 0) ? 2 : 1;
-  // More than 16 query rows per kv head (chunked prefill, wide MTP): a
-  // wavefront carries two blocks of 16 rows over the same K/V registers, so
-  // a tile's loads and V transposes serve both.  (Four blocks need more
-  // than the 256 registers MFMA operands can use and measured slower.)
+  // More than 16 query rows per kv head (chunked prefill, wide MTP) at
+  // head_dim 64: a wavefront carries two blocks of 16 rows over the same K/V
+  // registers, so a tile's loads and V transposes serve both (32 rows:
+  // 68 us against 92 us with one block).  At head_dim 128 two blocks spill
+  // registers and measured slower (137 us against 170 us), and four blocks
+  // need more than the 256 registers an MFMA operand can live in.
   p.nb = 1;
-  if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
+  if (fp8_mfma && p.D == 64 && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
   p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
   const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;

@@ -441,9 +441,9 @@ __device__ __forceinline__ TileRange rows_tiles(const Params& p, int L, int qmin
 // only its own head's keys, and of the output only its own head's dims are
 // kept.  All 16 MFMA columns do work and every load reads whole lines.
 //
-// NB = 2 (more than 16 query rows per kv head: chunked prefill, wide MTP):
-// a wavefront takes two blocks of 16 rows over the same K/V registers, so
-// each tile's loads and V transposes serve 32 rows.
+// NB = 2 (head_dim 64 with more than 16 query rows per kv head: chunked
+// prefill, wide MTP): a wavefront takes two blocks of 16 rows over the same
+// K/V registers, so each tile's loads and V transposes serve 32 rows.
 //
 // NT selects non-temporal K/V loads: right when each K/V byte is read by one
 // wavefront (one row group), wrong when several row groups re-read it.
@@ -1676,17 +1676,10 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
     else
       partial_mfma_kernel<64, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 128) {
-    if (pl.nb == 2) {
-      if (pl.nt)
-        partial_mfma_kernel<128, 1, 1, 2, 1><<<grid, block, 0, st>>>(prm);
-      else
-        partial_mfma_kernel<128, 1, 1, 2, 0><<<grid, block, 0, st>>>(prm);
-    } else {
-      if (pl.nt)
-        partial_mfma_kernel<128, 1, 1, 1, 1><<<grid, block, 0, st>>>(prm);
-      else
-        partial_mfma_kernel<128, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
-    }
+    if (pl.nt)
+      partial_mfma_kernel<128, 1, 1, 1, 1><<<grid, block, 0, st>>>(prm);
+    else
+      partial_mfma_kernel<128, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
   } else {
     if (pl.nt)
       partial_mfma_kernel<256, 2, 1, 1, 1><<<grid, block, 0, st>>>(prm);
