@@ -53,6 +53,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -650,6 +651,28 @@ partial_mfma_kernel(Params p) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (KSTEPS == 4) {
+        // A 128-dim slice: one 16x16x128 FP8 MFMA per query part (gfx950's
+        // full-rate form; unit E8M0 scales).  A lane's 32 K bytes and its 32
+        // query bytes cover the same dims, which is all the sum needs.
+        i32x8 ka, kbv, qh, ql;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ka[i] = int(r.k[0][i]);
+          kbv[i] = int(r.k[1][i]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          qh[2 * c] = int(uint32_t(qhi[b][c]));
+          qh[2 * c + 1] = int(uint32_t(uint64_t(qhi[b][c]) >> 32));
+          ql[2 * c] = int(uint32_t(qlo[b][c]));
+          ql[2 * c + 1] = int(uint32_t(uint64_t(qlo[b][c]) >> 32));
+        }
+        sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh, sa, 0, 0, 0, 127, 0, 127);
+        sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, qh, sb, 0, 0, 0, 127, 0, 127);
+        sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql, sa, 0, 0, 0, 127, 0, 127);
+        sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, ql, sb, 0, 0, 0, 127, 0, 127);
+      } else {
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) {
         const long ka = as_long(r.k[0][2 * c], r.k[0][2 * c + 1]);
@@ -658,6 +681,7 @@ partial_mfma_kernel(Params p) {
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[b][c], sb, 0, 0, 0);
         sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[b][c], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[b][c], sb, 0, 0, 0);
+      }
       }
       // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc
       // (one head_dim slice per wavefront), or, when two wavefronts split
