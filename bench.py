@@ -102,8 +102,9 @@ def partial_kernel_name(plan, D):
     """The partial kernel a plan launches, as rocprofv3 names it."""
     if plan["variant"] == 1:
         pr = plan["heads_per_wave"]
+        lw = plan["row_groups_per_wg"] if plan["row_groups_per_wg"] > 1 else 0
         return (f"partial_mfma_kernel<{D * pr}, {plan['waves_per_head']}, {pr}, "
-                f"{plan['row_blocks']}, {plan['nontemporal_kv']}>")
+                f"{plan['row_blocks']}, {plan['nontemporal_kv']}, {lw}>")
     return f"partial_dot_kernel<{D}>"
 
 

@@ -106,6 +106,7 @@ class PlanInfo(ctypes.Structure):
         ("heads_per_wave", ctypes.c_int32),
         ("row_blocks", ctypes.c_int32),
         ("nontemporal_kv", ctypes.c_int32),
+        ("row_groups_per_wg", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
         ("workspace_lse_offset", ctypes.c_uint64),
     ]

@@ -112,6 +112,17 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // need more than the 256 registers an MFMA operand can live in.
   p.nb = 1;
   if (fp8_mfma && p.D == 64 && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
+  // Four or eight row groups of one kv head (many query rows: chunked
+  // prefill) share each K/V tile through LDS: the tile is fetched once per
+  // workgroup instead of once per row group (prefill 1.35-1.5x faster at
+  // head_dim 128).
+  p.lw = 0;
+  if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.D <= 128) {
+    const int32_t rg1 = int32_t(ceil_div(p.rows, kRowsMfma));
+    if (rg1 % 8 == 0) p.lw = 8;
+    else if (rg1 % 4 == 0) p.lw = 4;
+    if (p.lw) p.nb = 1;
+  }
   p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
   const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;
@@ -125,8 +136,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   const int32_t max_hg = kMaxWgWaves / p.ds;
   p.hg = 1;
   while (p.hg * 2 <= max_hg && units % (p.hg * 2) == 0) p.hg *= 2;
-  p.upi = (units / p.hg) * p.row_groups;
-  const int64_t waves_per_item = int64_t(p.upi) * p.hg * p.ds;
+  if (p.lw) p.hg = 1;
+  p.upi = (units / p.hg) * (p.lw ? p.row_groups / p.lw : p.row_groups);
+  const int64_t waves_per_item = int64_t(p.upi) * p.hg * p.ds * (p.lw ? p.lw : 1);
 
   // Tiles a sequence can span: its attended keys, plus one when a window
   // start need not fall on a tile boundary.
@@ -254,6 +266,7 @@ fp8pa_status fp8pa_plan(const fp8pa_shape* shape, int32_t cu_count, fp8pa_plan_i
   out->heads_per_wave = p.pr;
   out->row_blocks = p.variant == fp8pa::kVariantMfma ? p.nb : 1;
   out->nontemporal_kv = p.nt;
+  out->row_groups_per_wg = p.lw ? p.lw : 1;
   out->rows_per_group = p.rpg;
   out->row_groups = p.row_groups;
   out->grid_wgs = p.grid_wgs;

@@ -448,13 +448,14 @@ __device__ __forceinline__ TileRange rows_tiles(const Params& p, int L, int qmin
 //
 // NT selects non-temporal K/V loads: right when each K/V byte is read by one
 // wavefront (one row group), wrong when several row groups re-read it.
-template <int D, int DS, int PR, int NB, int NT>
+template <int D, int DS, int PR, int NB, int NT, int LW>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
 __attribute__((amdgpu_waves_per_eu(NB == 1 && D / DS == 64 ? 4 : D / DS <= 128 ? 2 : 1, 8))) void
 partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
   static_assert(PR == 1 || (PR == 2 && D == 128 && DS == 1), "paired heads");
   static_assert(NB == 1 || (DS == 1 && PR == 1), "row blocks need one whole head per wavefront");
+  static_assert(LW == 0 || ((LW == 4 || LW == 8) && DS == 1 && PR == 1 && NB == 1), "LDS-shared tiles");
   constexpr int DH = D / PR;       // head_dim of the output rows
   constexpr int DW = D / DS;       // head_dim slice of this wavefront
   constexpr int S = DW / 16;       // V bytes per lane per token
@@ -467,11 +468,26 @@ partial_mfma_kernel(Params p) {
   // [wavefront][tile parity][lane][2 x f32x4], for the at most kMaxWgWaves
   // wavefronts of a workgroup.
   __shared__ f32x4 xch[DS == 2 ? kMaxWgWaves * 2 * 64 * 2 : 1];
+  // LW > 0: the LW wavefronts of a workgroup are LW row groups of one kv
+  // head and share each K/V tile through a two-slot LDS ring: [slot][K then
+  // V][32 tokens][D + 16 bytes] (rows padded against bank conflicts).
+  constexpr int LROW = D + 16;
+  constexpr int LSLOT = 2 * kTileTokens * LROW;
+  __shared__ __attribute__((aligned(16))) uint8_t ltile[LW ? 2 * LSLOT : 16];
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int qd = lane >> 4;
   Work w = work_head(p, DS);
+  if constexpr (LW > 0) {
+    const int item = blockIdx.x / p.upi;
+    const int unit = blockIdx.x - item * p.upi;
+    const int rgu = p.row_groups / LW;
+    const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    w.rg = (unit % rgu) * LW + wv;
+    w.g = unit / rgu;
+    w.half = 0;
+  }
   // This lane's rows: kv head kvh, row rlane[b] of that head's rows in block b.
   const int kvh = PR == 2 ? 2 * w.g + (n >> 3) : w.g;
   int rlane[NB];
@@ -507,7 +523,10 @@ partial_mfma_kernel(Params p) {
   // The split's tiles outside the keys some row attends are skipped: with
   // many query rows per sequence (chunked prefill) a row group's causal
   // range ends before the sequence does.
-  const TileRange tr = rows_tiles(p, L, qmin, qmax, w.ts, w.te);
+  // (LW > 0: the range of the workgroup's rows, the same for all its wavefronts)
+  const int tq0 = LW ? ((w.rg / (LW > 0 ? LW : 1)) * (LW > 0 ? LW : 1) * kRowsMfma) / p.G : qmin;
+  const int tq1 = LW ? (min((w.rg / (LW > 0 ? LW : 1) + 1) * (LW > 0 ? LW : 1) * kRowsMfma, p.rows) - 1) / p.G : qmax;
+  const TileRange tr = rows_tiles(p, L, tq0, tq1, w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
   Row row[NB];
 #pragma unroll
@@ -774,8 +793,74 @@ partial_mfma_kernel(Params p) {
   // measured slower on MI355X: more than ~8 KB in flight per wavefront only
   // adds queueing in the memory system.
   TileRegs ta, tb;
-  load_tile(ts, ta, 0);
-  load_tile(ts + 1, tb, 1);
+  // LDS staging (LW > 0): this lane's CH bytes of a tile; a wavefront's
+  // chunks lie in one 16-token group of K or of V
+  constexpr int LWS = LW > 0 ? LW : 1;
+  constexpr int CH = 2 * kTileTokens * D / (64 * LWS);
+  const int swv = int(threadIdx.x >> 6);
+  const int sreg = (swv * 64 * CH) / (16 * D);       // region: K A, K B, V A, V B
+  const int skv = sreg >> 1, sgrp = sreg & 1;
+  const int soff = ((swv * 64 + lane) * CH) % (16 * D);
+  const int stok = soff / D, scol = soff % D;
+  uint32_t sR[CH / 4 > 0 ? CH / 4 : 1];
+  auto stage_load = [&](int t) {
+    const int step = ((t - ts) >> 1) & 63;
+    const int podd = (t - ts) & 1;
+    const int ta0 = sgrp ? tab[1] : tab[0];
+    const int ta2 = sgrp ? tab[3] : tab[2];
+    const int pa = __builtin_amdgcn_readlane(ta0, step);
+    const int pb = __builtin_amdgcn_readlane(ta2, step);
+    const int page = podd ? pb : pa;
+    const int gk = t * kTileTokens + 16 * sgrp;
+    const bool live = t < te && gk < uhi && gk + 16 > ulo;
+    const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
+    const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)((skv ? vbase_g : kbase_g) + base), 0,
+                                                      live ? 16 * tok : 0, kRsrcWord3);
+    buf_load<CH, 0>(rs, uint32_t(stok * tok + scol), sR);
+  };
+  auto stage_write = [&](int slot) {
+    uint8_t* dst = ltile + slot * LSLOT + skv * (kTileTokens * LROW) + (16 * sgrp + stok) * LROW + scol;
+    if constexpr (CH == 8) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{sR[0], sR[1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH / 16; ++i)
+        reinterpret_cast<u32x4*>(dst)[i] = u32x4{sR[4 * i], sR[4 * i + 1], sR[4 * i + 2], sR[4 * i + 3]};
+    }
+  };
+  auto lds_read = [&](int slot, TileRegs& r) {
+    const uint8_t* src = ltile + slot * LSLOT;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const uint8_t* kp = src + (16 * grp + n) * LROW + KB * qd;
+#pragma unroll
+      for (int i = 0; i < KB / 16; ++i) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(kp)[i];
+        r.k[grp][4 * i] = v.x;
+        r.k[grp][4 * i + 1] = v.y;
+        r.k[grp][4 * i + 2] = v.z;
+        r.k[grp][4 * i + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tk = j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4);
+      const uint8_t* vp = src + kTileTokens * LROW + tk * LROW + S * n;
+      if constexpr (SW == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(vp);
+        r.v[j][0] = v.x;
+        r.v[j][1] = v.y;
+      } else {
+        r.v[j][0] = *reinterpret_cast<const uint32_t*>(vp);
+      }
+    }
+  };
+  if constexpr (LW > 0) {
+    stage_load(ts);
+  } else {
+    load_tile(ts, ta, 0);
+    load_tile(ts + 1, tb, 1);
+  }
 
   // ---- stage the query rows: per-row power-of-two scale, E4M3 hi + lo parts
   // One K scale per head goes into the score scale; group scales differ
@@ -841,6 +926,17 @@ partial_mfma_kernel(Params p) {
     }
   }
 
+  if constexpr (LW > 0) {
+    stage_write(0);
+    stage_load(ts + 1);
+    for (int tt = ts; tt < te; ++tt) {
+      __syncthreads();  // tile tt is in its slot; the other slot's readers are done
+      lds_read((tt - ts) & 1, ta);
+      stage_write((tt + 1 - ts) & 1);
+      stage_load(tt + 2);
+      compute_tile(tt, ta);
+    }
+  } else {
   // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {
     compute_tile(tt, ta);
@@ -848,6 +944,7 @@ partial_mfma_kernel(Params p) {
     load_tile(tt + 2, ta, 0);
     compute_tile(tt + 1, tb);
     load_tile(tt + 3, tb, 1);
+  }
   }
 
   // ---- epilogue: l over the 4 lane groups, normalise, write
@@ -1693,22 +1790,30 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
       partial_dot_kernel<D, FP8PA_KV_E4M3><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 64) {
     // non-temporal loads only where a wavefront reads whole lines (paired heads)
-    if (pl.pr == 2)
-      partial_mfma_kernel<128, 1, 2, 1, 1><<<grid, block, 0, st>>>(prm);
+    if (pl.lw == 8)
+      partial_mfma_kernel<64, 1, 1, 1, 0, 8><<<grid, dim3(512), 0, st>>>(prm);
+    else if (pl.lw == 4)
+      partial_mfma_kernel<64, 1, 1, 1, 0, 4><<<grid, dim3(256), 0, st>>>(prm);
+    else if (pl.pr == 2)
+      partial_mfma_kernel<128, 1, 2, 1, 1, 0><<<grid, block, 0, st>>>(prm);
     else if (pl.nb == 2)
-      partial_mfma_kernel<64, 1, 1, 2, 0><<<grid, block, 0, st>>>(prm);
+      partial_mfma_kernel<64, 1, 1, 2, 0, 0><<<grid, block, 0, st>>>(prm);
     else
-      partial_mfma_kernel<64, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+      partial_mfma_kernel<64, 1, 1, 1, 0, 0><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 128) {
-    if (pl.nt)
-      partial_mfma_kernel<128, 1, 1, 1, 1><<<grid, block, 0, st>>>(prm);
+    if (pl.lw == 8)
+      partial_mfma_kernel<128, 1, 1, 1, 0, 8><<<grid, dim3(512), 0, st>>>(prm);
+    else if (pl.lw == 4)
+      partial_mfma_kernel<128, 1, 1, 1, 0, 4><<<grid, dim3(256), 0, st>>>(prm);
+    else if (pl.nt)
+      partial_mfma_kernel<128, 1, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
     else
-      partial_mfma_kernel<128, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+      partial_mfma_kernel<128, 1, 1, 1, 0, 0><<<grid, block, 0, st>>>(prm);
   } else {
     if (pl.nt)
-      partial_mfma_kernel<256, 2, 1, 1, 1><<<grid, block, 0, st>>>(prm);
+      partial_mfma_kernel<256, 2, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
     else
-      partial_mfma_kernel<256, 2, 1, 1, 0><<<grid, block, 0, st>>>(prm);
+      partial_mfma_kernel<256, 2, 1, 1, 0, 0><<<grid, block, 0, st>>>(prm);
   }
   return hipGetLastError();
 }

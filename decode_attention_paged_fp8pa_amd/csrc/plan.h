@@ -62,6 +62,7 @@ struct Plan {
   int32_t hg;              // kv heads per workgroup
   int32_t ds;              // wavefronts per kv head (head_dim split; MFMA at D = 256: 2)
   int32_t pr;              // kv heads per wavefront (MFMA at D = 64 with <= 8 rows: 2)
+  int32_t lw;              // LDS-shared tiles: row groups per workgroup (0: off)
   int32_t nb;              // 16-row blocks per wavefront (MFMA kernel; 1 or 2)
   int32_t nt;              // 1: non-temporal K/V loads (each byte read by one wavefront)
   int32_t fmt;             // FP8PA_KV_E4M3 or FP8PA_KV_NVFP4

@@ -156,6 +156,10 @@ typedef struct fp8pa_plan_info {
                                rows per kv head); rows_per_group = 16 * row_blocks */
   int32_t nontemporal_kv;   /* 1 when K/V loads bypass cache retention: each byte
                                is read by one wavefront (row_groups == 1) */
+  int32_t row_groups_per_wg; /* row groups of one kv head whose wavefronts share each
+                                K/V tile through LDS (4 or 8 with many query rows per
+                                kv head); such a workgroup has that many wavefronts
+                                and heads_per_wg = 1.  Otherwise 1. */
   uint64_t workspace_bytes; /* bytes fp8pa_decode needs in `workspace` */
   uint64_t workspace_lse_offset; /* byte offset of the partial LSE block in the
                                     workspace; the partial outputs start at 0.

@@ -208,18 +208,26 @@ def test_nvfp4_plans():
 def test_row_blocks_for_many_rows():
     base = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
                 num_blocks=1024, block_table_stride=64, max_seq_len=1024, sm_scale=0.1)
-    # head_dim 128: one block of 16 rows per wavefront
-    for q_len, rg in ((1, 1), (4, 1), (5, 2), (8, 2), (9, 3), (128, 32)):
+    # head_dim 128: one block of 16 rows per wavefront; 4 or 8 row groups of
+    # one kv head share each K/V tile through LDS when the row groups divide so
+    for q_len, rg, lw in ((1, 1, 1), (4, 1, 1), (5, 2, 1), (8, 2, 1), (9, 3, 1), (16, 4, 4),
+                          (24, 6, 1), (32, 8, 8), (128, 32, 8)):
         p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, **base), 256)
         assert (p["row_blocks"], p["row_groups"], p["rows_per_group"]) == (1, rg, 16), q_len
+        assert p["row_groups_per_wg"] == lw, q_len
+        if lw > 1:
+            assert p["heads_per_wg"] == 1
+            assert p["grid_wgs"] % (8 // 1 * (rg // lw)) == 0   # Hkv * row_groups / lw units per item
         # non-temporal loads only where one wavefront reads each K/V byte
         assert p["nontemporal_kv"] == (1 if rg == 1 else 0)
-    # head_dim 64: two blocks once a kv head has more than 16 rows; non-temporal
-    # loads only with paired heads (at most 8 rows), whose wavefront reads whole
-    # 128-byte lines
-    for q_len, nb, rg in ((2, 1, 1), (4, 1, 1), (5, 2, 1), (8, 2, 1), (9, 2, 2), (128, 2, 16)):
+    # head_dim 64: two blocks once a kv head has more than 16 rows, unless the
+    # row groups share tiles through LDS; non-temporal loads only with paired
+    # heads (at most 8 rows), whose wavefront reads whole 128-byte lines
+    for q_len, nb, rg, lw in ((2, 1, 1, 1), (4, 1, 1, 1), (5, 2, 1, 1), (8, 2, 1, 1), (9, 2, 2, 1),
+                              (16, 1, 4, 4), (128, 1, 32, 8)):
         p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, **dict(base, head_dim=64)), 256)
         assert (p["row_blocks"], p["row_groups"], p["rows_per_group"]) == (nb, rg, 16 * nb), q_len
+        assert p["row_groups_per_wg"] == lw, q_len
         paired = 4 * q_len <= 8
         assert p["heads_per_wave"] == (2 if paired else 1)
         assert p["nontemporal_kv"] == (1 if paired else 0)

@@ -145,6 +145,12 @@ SMALL = {
     "prefill_q16_d256": dict(B=2, q_len=16, Hq=8, Hkv=2, D=256, bt=64, seq_lens=[16, 1000],
                              scale=("per_head", 0.02, 0.1), sinks=True),
     "prefill_q512": dict(B=1, q_len=512, Hq=4, Hkv=1, D=128, bt=16, seq_lens=[1500]),
+    # 64 rows per kv head: four row groups share each K/V tile through LDS
+    "prefill_q16_lw4": dict(B=2, q_len=16, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[16, 700], window=300,
+                            sinks=True, scale=("per_head", 0.02, 0.1)),
+    "prefill_q16_lw4_d64": dict(B=3, q_len=16, Hq=8, Hkv=2, D=64, bt=32, seq_lens=[40, 333, 1000],
+                                k_groups=2, scale=("per_head", 0.02, 0.1)),
+    "prefill_q32_lw8_hnd_pages": dict(B=2, q_len=32, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[32, 450]),
     "prefill_q32_mha_kg": dict(B=2, q_len=32, Hq=4, Hkv=4, D=128, bt=32, seq_lens=[40, 233],
                                window=64, k_groups=2, scale=("per_head", 0.02, 0.1)),
     "kg4_q4_mtp": dict(B=2, q_len=4, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[130, 44], window=50,
@@ -182,7 +188,8 @@ def test_parity_small(name, flags, ns):
 
 
 HND_CASES = ["gqa4_ragged", "d64_window_sinks", "d256_bt64", "mtp4_window_sinks", "bt1_pages",
-             "pair_q2_perhead", "kg4_gqa_ragged", "prefill_q64", "mha_rows1", "batch130_mqa"]
+             "pair_q2_perhead", "kg4_gqa_ragged", "prefill_q64", "mha_rows1", "batch130_mqa",
+             "prefill_q32_lw8_hnd_pages", "prefill_q16_lw4_d64"]
 
 
 @pytest.mark.parametrize("name", HND_CASES)
