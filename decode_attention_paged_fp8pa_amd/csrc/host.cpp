@@ -112,15 +112,18 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // need more than the 256 registers an MFMA operand can live in.
   p.nb = 1;
   if (fp8_mfma && p.D == 64 && p.ds == 1 && p.pr == 1 && p.rows > kRowsMfma) p.nb = 2;
-  // Four or eight row groups of one kv head (many query rows: chunked
+  // Two, four or eight row groups of one kv head (wide MTP, chunked
   // prefill) share each K/V tile through LDS: the tile is fetched once per
   // workgroup instead of once per row group (prefill 1.35-1.5x faster at
-  // head_dim 128).
+  // head_dim 128; 32 rows 106 us against 137 us).  Two groups at head_dim
+  // 64 stay with the two row blocks above, which need no LDS (68 us
+  // against 85 us shared).
   p.lw = 0;
   if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.D <= 128) {
     const int32_t rg1 = int32_t(ceil_div(p.rows, kRowsMfma));
     if (rg1 % 8 == 0) p.lw = 8;
     else if (rg1 % 4 == 0) p.lw = 4;
+    else if (rg1 % 2 == 0 && p.D == 128) p.lw = 2;
     if (p.lw) p.nb = 1;
   }
   p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;

@@ -455,7 +455,8 @@ partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
   static_assert(PR == 1 || (PR == 2 && D == 128 && DS == 1), "paired heads");
   static_assert(NB == 1 || (DS == 1 && PR == 1), "row blocks need one whole head per wavefront");
-  static_assert(LW == 0 || ((LW == 4 || LW == 8) && DS == 1 && PR == 1 && NB == 1), "LDS-shared tiles");
+  static_assert(LW == 0 || ((LW == 2 || LW == 4 || LW == 8) && DS == 1 && PR == 1 && NB == 1),
+                "LDS-shared tiles");
   constexpr int DH = D / PR;       // head_dim of the output rows
   constexpr int DW = D / DS;       // head_dim slice of this wavefront
   constexpr int S = DW / 16;       // V bytes per lane per token
@@ -545,6 +546,10 @@ partial_mfma_kernel(Params p) {
   }
 
   long qhi[NB][KSTEPS], qlo[NB][KSTEPS];  // query rows in E4M3 hi + lo parts (set below)
+  // A third part where group K scales were folded into the query: q * ks is
+  // an fp32 value, which hi + lo hold to ~8 bits only (a bf16 query they hold
+  // almost exactly), too coarse for the LSE of rows with few keys.
+  long qlo2[NB][KSTEPS];
   float cr[NB];                           // score scales into log2 units
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
@@ -691,6 +696,16 @@ partial_mfma_kernel(Params p) {
         sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, qh, sb, 0, 0, 0, 127, 0, 127);
         sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql, sa, 0, 0, 0, 127, 0, 127);
         sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, ql, sb, 0, 0, 0, 127, 0, 127);
+        if (p.k_groups > 1) {
+          i32x8 q3;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            q3[2 * c] = int(uint32_t(qlo2[b][c]));
+            q3[2 * c + 1] = int(uint32_t(uint64_t(qlo2[b][c]) >> 32));
+          }
+          sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q3, sa, 0, 0, 0, 127, 0, 127);
+          sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, q3, sb, 0, 0, 0, 127, 0, 127);
+        }
       } else {
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) {
@@ -700,6 +715,10 @@ partial_mfma_kernel(Params p) {
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[b][c], sb, 0, 0, 0);
         sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[b][c], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[b][c], sb, 0, 0, 0);
+        if (p.k_groups > 1) {
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo2[b][c], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo2[b][c], sb, 0, 0, 0);
+        }
       }
       }
       // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc
@@ -796,36 +815,54 @@ partial_mfma_kernel(Params p) {
   // LDS staging (LW > 0): this lane's CH bytes of a tile; a wavefront's
   // chunks lie in one 16-token group of K or of V
   constexpr int LWS = LW > 0 ? LW : 1;
-  constexpr int CH = 2 * kTileTokens * D / (64 * LWS);
+  // A tile is four regions (K group A, K group B, V group A, V group B) of
+  // 16 D bytes.  With 4 or 8 wavefronts each wavefront's lanes lie in one
+  // region, CH bytes each; with 2, each wavefront covers two regions.
+  constexpr int RPW = LWS >= 4 ? 1 : 4 / LWS;  // regions per wavefront
+  constexpr int CH = LWS >= 4 ? 2 * kTileTokens * D / (64 * LWS) : 16 * D / 64;
   const int swv = int(threadIdx.x >> 6);
-  const int sreg = (swv * 64 * CH) / (16 * D);       // region: K A, K B, V A, V B
-  const int skv = sreg >> 1, sgrp = sreg & 1;
-  const int soff = ((swv * 64 + lane) * CH) % (16 * D);
-  const int stok = soff / D, scol = soff % D;
-  uint32_t sR[CH / 4 > 0 ? CH / 4 : 1];
+  int sreg[RPW], stok[RPW], scol[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    sreg[rr] = LWS >= 4 ? (swv * 64 * CH) / (16 * D) : swv * RPW + rr;
+    const int off = LWS >= 4 ? ((swv * 64 + lane) * CH) % (16 * D) : lane * CH;
+    stok[rr] = off / D;
+    scol[rr] = off % D;
+  }
+  uint32_t sR[RPW][CH / 4 > 0 ? CH / 4 : 1];
   auto stage_load = [&](int t) {
     const int step = ((t - ts) >> 1) & 63;
     const int podd = (t - ts) & 1;
-    const int ta0 = sgrp ? tab[1] : tab[0];
-    const int ta2 = sgrp ? tab[3] : tab[2];
-    const int pa = __builtin_amdgcn_readlane(ta0, step);
-    const int pb = __builtin_amdgcn_readlane(ta2, step);
-    const int page = podd ? pb : pa;
-    const int gk = t * kTileTokens + 16 * sgrp;
-    const bool live = t < te && gk < uhi && gk + 16 > ulo;
-    const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
-    const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)((skv ? vbase_g : kbase_g) + base), 0,
-                                                      live ? 16 * tok : 0, kRsrcWord3);
-    buf_load<CH, 0>(rs, uint32_t(stok * tok + scol), sR);
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int skv = sreg[rr] >> 1, sgrp = sreg[rr] & 1;
+      const int ta0 = sgrp ? tab[1] : tab[0];
+      const int ta2 = sgrp ? tab[3] : tab[2];
+      const int pa = __builtin_amdgcn_readlane(ta0, step);
+      const int pb = __builtin_amdgcn_readlane(ta2, step);
+      const int page = podd ? pb : pa;
+      const int gk = t * kTileTokens + 16 * sgrp;
+      const bool live = t < te && gk < uhi && gk + 16 > ulo;
+      const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
+      const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)((skv ? vbase_g : kbase_g) + base), 0,
+                                                        live ? 16 * tok : 0, kRsrcWord3);
+      buf_load<CH, 0>(rs, uint32_t(stok[rr] * tok + scol[rr]), sR[rr]);
+    }
   };
   auto stage_write = [&](int slot) {
-    uint8_t* dst = ltile + slot * LSLOT + skv * (kTileTokens * LROW) + (16 * sgrp + stok) * LROW + scol;
-    if constexpr (CH == 8) {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{sR[0], sR[1]};
-    } else {
 #pragma unroll
-      for (int i = 0; i < CH / 16; ++i)
-        reinterpret_cast<u32x4*>(dst)[i] = u32x4{sR[4 * i], sR[4 * i + 1], sR[4 * i + 2], sR[4 * i + 3]};
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int skv = sreg[rr] >> 1, sgrp = sreg[rr] & 1;
+      uint8_t* dst =
+          ltile + slot * LSLOT + skv * (kTileTokens * LROW) + (16 * sgrp + stok[rr]) * LROW + scol[rr];
+      if constexpr (CH == 8) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{sR[rr][0], sR[rr][1]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH / 16; ++i)
+          reinterpret_cast<u32x4*>(dst)[i] =
+              u32x4{sR[rr][4 * i], sR[rr][4 * i + 1], sR[rr][4 * i + 2], sR[rr][4 * i + 3]};
+      }
     }
   };
   auto lds_read = [&](int slot, TileRegs& r) {
@@ -923,6 +960,18 @@ partial_mfma_kernel(Params p) {
       l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
       qhi[b][c] = as_long(h0, h1);
       qlo[b][c] = as_long(l0, l1);
+      uint32_t m0 = 0, m1 = 0;
+      if (grouped) {
+        const f32x2 e0 = __builtin_amdgcn_cvt_pk_f32_fp8(l0, false);
+        const f32x2 e1 = __builtin_amdgcn_cvt_pk_f32_fp8(l0, true);
+        const f32x2 e2 = __builtin_amdgcn_cvt_pk_f32_fp8(l1, false);
+        const f32x2 e3 = __builtin_amdgcn_cvt_pk_f32_fp8(l1, true);
+        m0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - d0.x - e0.x, x[1] - d0.y - e0.y, m0, false);
+        m0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x - e1.x, x[3] - d1.y - e1.y, m0, true);
+        m1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x - e2.x, x[5] - d2.y - e2.y, m1, false);
+        m1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x - e3.x, x[7] - d3.y - e3.y, m1, true);
+      }
+      qlo2[b][c] = as_long(m0, m1);
     }
   }
 
@@ -1794,6 +1843,8 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
       partial_mfma_kernel<64, 1, 1, 1, 0, 8><<<grid, dim3(512), 0, st>>>(prm);
     else if (pl.lw == 4)
       partial_mfma_kernel<64, 1, 1, 1, 0, 4><<<grid, dim3(256), 0, st>>>(prm);
+    else if (pl.lw == 2)
+      partial_mfma_kernel<64, 1, 1, 1, 0, 2><<<grid, dim3(128), 0, st>>>(prm);
     else if (pl.pr == 2)
       partial_mfma_kernel<128, 1, 2, 1, 1, 0><<<grid, block, 0, st>>>(prm);
     else if (pl.nb == 2)
@@ -1805,6 +1856,8 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
       partial_mfma_kernel<128, 1, 1, 1, 0, 8><<<grid, dim3(512), 0, st>>>(prm);
     else if (pl.lw == 4)
       partial_mfma_kernel<128, 1, 1, 1, 0, 4><<<grid, dim3(256), 0, st>>>(prm);
+    else if (pl.lw == 2)
+      partial_mfma_kernel<128, 1, 1, 1, 0, 2><<<grid, dim3(128), 0, st>>>(prm);
     else if (pl.nt)
       partial_mfma_kernel<128, 1, 1, 1, 1, 0><<<grid, block, 0, st>>>(prm);
     else

@@ -208,10 +208,11 @@ def test_nvfp4_plans():
 def test_row_blocks_for_many_rows():
     base = dict(batch=2, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
                 num_blocks=1024, block_table_stride=64, max_seq_len=1024, sm_scale=0.1)
-    # head_dim 128: one block of 16 rows per wavefront; 4 or 8 row groups of
-    # one kv head share each K/V tile through LDS when the row groups divide so
-    for q_len, rg, lw in ((1, 1, 1), (4, 1, 1), (5, 2, 1), (8, 2, 1), (9, 3, 1), (16, 4, 4),
-                          (24, 6, 1), (32, 8, 8), (128, 32, 8)):
+    # head_dim 128: one block of 16 rows per wavefront; 2, 4 or 8 row groups
+    # of one kv head share each K/V tile through LDS when the row groups
+    # divide so (the largest such count)
+    for q_len, rg, lw in ((1, 1, 1), (4, 1, 1), (5, 2, 2), (8, 2, 2), (9, 3, 1), (16, 4, 4),
+                          (24, 6, 2), (28, 7, 1), (32, 8, 8), (48, 12, 4), (128, 32, 8)):
         p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, **base), 256)
         assert (p["row_blocks"], p["row_groups"], p["rows_per_group"]) == (1, rg, 16), q_len
         assert p["row_groups_per_wg"] == lw, q_len
@@ -220,11 +221,11 @@ def test_row_blocks_for_many_rows():
             assert p["grid_wgs"] % (8 // 1 * (rg // lw)) == 0   # Hkv * row_groups / lw units per item
         # non-temporal loads only where one wavefront reads each K/V byte
         assert p["nontemporal_kv"] == (1 if rg == 1 else 0)
-    # head_dim 64: two blocks once a kv head has more than 16 rows, unless the
-    # row groups share tiles through LDS; non-temporal loads only with paired
+    # head_dim 64: two blocks once a kv head has more than 16 rows, unless 4
+    # or 8 row groups share tiles through LDS; non-temporal loads only with paired
     # heads (at most 8 rows), whose wavefront reads whole 128-byte lines
     for q_len, nb, rg, lw in ((2, 1, 1, 1), (4, 1, 1, 1), (5, 2, 1, 1), (8, 2, 1, 1), (9, 2, 2, 1),
-                              (16, 1, 4, 4), (128, 1, 32, 8)):
+                              (16, 1, 4, 4), (24, 2, 3, 1), (128, 1, 32, 8)):
         p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, **dict(base, head_dim=64)), 256)
         assert (p["row_blocks"], p["row_groups"], p["rows_per_group"]) == (nb, rg, 16 * nb), q_len
         assert p["row_groups_per_wg"] == lw, q_len
@@ -347,7 +348,7 @@ def test_balanced_plan_covers_every_tile(seed):
         if p["split_mode"] != fp.FP8PA_SPLIT_BALANCED:
             continue
         items, c = _balanced_items(p, seq, q_len, window)
-        upi = (Hkv // p["heads_per_wg"]) * p["row_groups"]
+        upi = (Hkv // p["heads_per_wg"]) * (p["row_groups"] // p["row_groups_per_wg"])
         # every (sequence, split) item has a workgroup slot and a partial slot
         assert sum(len(v) for v in items.values()) <= p["grid_wgs"] // upi
         assert max(len(v) for v in items.values()) <= p["num_splits"]

@@ -155,6 +155,16 @@ SMALL = {
                                window=64, k_groups=2, scale=("per_head", 0.02, 0.1)),
     "kg4_q4_mtp": dict(B=2, q_len=4, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[130, 44], window=50,
                        scale=("per_head", 0.02, 0.1), sinks=True, k_groups=4),
+    # 32 or 96 rows per kv head at head_dim 128: two row groups share each tile
+    "mtp_q4_g8_lw2": dict(B=3, q_len=4, Hq=64, Hkv=8, D=128, bt=16, seq_lens=[100, 700, 33],
+                          window=50, sinks=True),
+    "prefill_q24_lw2": dict(B=2, q_len=24, Hq=16, Hkv=4, D=128, bt=32, seq_lens=[24, 610],
+                            scale=("per_head", 0.02, 0.1), sinks=True),
+    # group K scales folded into the query with few keys per row: the LSE of
+    # the first rows rests on a handful of scores, so the folded query must be
+    # held to well beyond E4M3's 4 bits
+    "kg4_q8_few_keys_lw2": dict(B=2, q_len=8, Hq=32, Hkv=8, D=128, bt=32, seq_lens=[8, 520],
+                                k_groups=4, scale=("per_head", 0.02, 0.1)),
 }
 
 # (case, flags, num_splits)
@@ -189,7 +199,7 @@ def test_parity_small(name, flags, ns):
 
 HND_CASES = ["gqa4_ragged", "d64_window_sinks", "d256_bt64", "mtp4_window_sinks", "bt1_pages",
              "pair_q2_perhead", "kg4_gqa_ragged", "prefill_q64", "mha_rows1", "batch130_mqa",
-             "prefill_q32_lw8_hnd_pages", "prefill_q16_lw4_d64"]
+             "prefill_q32_lw8_hnd_pages", "prefill_q16_lw4_d64", "prefill_q24_lw2"]
 
 
 @pytest.mark.parametrize("name", HND_CASES)
