@@ -129,7 +129,59 @@ def load_traffic(workload_name):
     return None if not h else int(h["read"] + h["write"])
 
 
-def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", nvfp4=False):
+def sample_gpu_state(busy, seconds_cap=20.0):
+    """GPU clocks and socket power read by `amd-smi metric` (a child process)
+    while `busy()` keeps the GPU running the timed work; None where the tool
+    is missing or its output is not understood.  Taken outside every timed
+    region."""
+    import shutil
+    import subprocess
+
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        proc = subprocess.Popen([exe, "metric", "--clock", "--power", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t_end = time.time() + seconds_cap
+    while proc.poll() is None and time.time() < t_end:
+        busy()
+    try:
+        text, _ = proc.communicate(timeout=max(1.0, t_end - time.time()))
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    try:
+        data = json.loads(text)
+        g = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clock = g["clock"]
+
+        def mhz(entry, key="clk"):
+            v = entry.get(key) if isinstance(entry, dict) else None
+            return v.get("value") if isinstance(v, dict) else None
+
+        gfx = [mhz(v) for k_, v in sorted(clock.items()) if k_.startswith("gfx_")]
+        gfx = [x for x in gfx if isinstance(x, (int, float))]
+        gfx_max = [mhz(v, "max_clk") for k_, v in clock.items() if k_.startswith("gfx_")]
+        gfx_max = [x for x in gfx_max if isinstance(x, (int, float))]
+        power = g.get("power", {}).get("socket_power")
+        return {
+            "tool": "amd-smi metric --clock --power",
+            "sampled": "while the headline step's graph replays",
+            "gfx_clk_mhz_per_xcd": gfx,
+            "gfx_max_clk_mhz": max(gfx_max) if gfx_max else None,
+            "mem_clk_mhz": mhz(clock.get("mem_0", {})),
+            "socket_power_w": power.get("value") if isinstance(power, dict) else None,
+        }
+    except (ValueError, KeyError, IndexError, TypeError, AttributeError):
+        return None
+
+
+def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", nvfp4=False,
+            sample_clocks=False):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
@@ -227,6 +279,12 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", 
               "median_us": round(step_ms * 1e3, 2),
               "p90_us": round(float(np.percentile(per_replay, 90)) * 1e3, 2),
               "replays": REPLAYS}
+    gpu_state = None
+    if sample_clocks:
+        gpu_state = sample_gpu_state(lambda: (graph.replay(), torch.cuda.synchronize()))
+        if gpu_state:
+            log(f"[bench] {label}: under load gfx clock {gpu_state['gfx_clk_mhz_per_xcd']} MHz, memory "
+                f"{gpu_state['mem_clk_mhz']} MHz, socket power {gpu_state['socket_power_w']} W")
     del graph
 
     # the partial kernel alone: the same K steps with the merge launch left
@@ -264,6 +322,7 @@ def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", 
     res = _result(wl, label, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall_ms, graph_ok,
                   partial_ms, merge_ms, log)
     res["spread"] = spread
+    res["gpu_state"] = gpu_state
     del pools, kc0, vc0
     torch.cuda.empty_cache()
     return res, wl
@@ -610,7 +669,8 @@ def main():
     head_wl = None
     ceiling = None if args.decode_only else copy_ceiling(log)
     for k in cfgs:
-        res, wl = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph)
+        res, wl = measure(k, args.steps, args.warmup, log, use_graph=not args.no_graph,
+                          sample_clocks=(k == HEADLINE and not args.decode_only))
         results[k] = res
         if k == HEADLINE:
             head_wl = wl
@@ -691,6 +751,7 @@ def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, pre
                    "tokens_per_s": round(h["tokens_per_s"], 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "gpu_state": h.get("gpu_state"),
         "copy_ceiling": ceiling,
         "writer": writer,
         "k_groups_variant": kg,
