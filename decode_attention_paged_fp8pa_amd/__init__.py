@@ -163,7 +163,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if max_seq_len is None:
-        max_seq_len = int(seq_lens.max().item())
+        max_seq_len = max(1, int(seq_lens.max().item()))   # a batch of empty slots still plans
     shape = shape_for(q, k_cache, block_table, k_scale, v_scale, window=window, sm_scale=sm_scale,
                       max_seq_len=max_seq_len, num_splits=num_splits, flags=flags,
                       k_groups=k_groups, kv_layout=kv_layout, kv_format=kv_format,

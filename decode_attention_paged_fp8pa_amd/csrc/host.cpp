@@ -38,7 +38,6 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   if (s->num_q_heads % s->num_kv_heads != 0) return FP8PA_ERR_INVALID_ARG;
   if (s->num_blocks < 1 || s->max_seq_len < 1 || s->block_table_stride < 1)
     return FP8PA_ERR_INVALID_ARG;
-  if (s->max_seq_len < s->q_len) return FP8PA_ERR_INVALID_ARG;
   if (!is_pow2(s->block_tokens) || s->block_tokens > 1024) return FP8PA_ERR_INVALID_ARG;
   if (ceil_div(s->max_seq_len, s->block_tokens) > s->block_table_stride)
     return FP8PA_ERR_INVALID_ARG;

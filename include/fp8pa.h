@@ -204,9 +204,11 @@ fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t*
  *
  * Alignment: q, k_cache, v_cache and out 16 bytes; workspace 256 bytes;
  * block_table, seq_lens, scales, sinks and lse 4 bytes.
- * Device-side preconditions (not checked): q_len <= seq_lens[b] <= max_seq_len,
+ * Device-side preconditions (not checked): 0 <= seq_lens[b] <= max_seq_len,
  * and block_table[b][j] in [0, num_blocks) for every page j that holds an
- * attended token.  Entries of pages holding no attended token are never
+ * attended token.  A query whose position seq_lens[b] - q_len + i is
+ * negative attends nothing and gets out 0 and lse -inf (the sink's logit
+ * with sinks), so a batch may be padded with 0-token sequences.  Entries of pages holding no attended token are never
  * read and may be -1; cache bytes of tokens no row attends are never used
  * (they may hold NaN codes).
  * Returns FP8PA_ERR_WORKSPACE_TOO_SMALL when workspace_bytes is short and

@@ -45,7 +45,7 @@ def run(wl, t, num_splits=0, flags=0, out=None, lse=None, workspace=None):
 
     return fp.decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
                      window=wl.window, sm_scale=wl.sm_scale,
-                     max_seq_len=int(wl.seq_lens.max()), num_splits=num_splits, flags=flags,
+                     max_seq_len=max(1, int(wl.seq_lens.max())), num_splits=num_splits, flags=flags,
                      out=out, lse=lse, workspace=workspace, k_groups=wl.k_groups,
                      kv_layout=t.get("layout", "NHD"), kv_format=getattr(wl, "kv_format", "e4m3"),
                      num_kv_heads=wl.Hkv, block_tokens=wl.bt)

@@ -57,6 +57,8 @@ NV_SMALL = {
     "padded_stride": dict(B=2, q_len=2, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[200, 77], page_stride=4864,
                           sinks=True),
     "tiny_seqs": dict(B=4, q_len=1, Hq=8, Hkv=2, D=64, bt=16, seq_lens=[1, 17, 32, 33]),
+    # empty batch slots and a sequence shorter than q_len
+    "padded_short_q4": dict(B=3, q_len=4, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[0, 150, 2], sinks=True),
     "d64_hnd_window_per_head": dict(B=3, q_len=1, Hq=32, Hkv=4, D=64, bt=32, seq_lens=[500, 96, 1200],
                                     window=200, sinks=True, kv_layout="HND", scale=("per_head", 0.02, 0.1)),
     "prefill_q40": dict(B=2, q_len=40, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[40, 333], sinks=True),

@@ -109,6 +109,14 @@ SMALL = {
     "q4_window5": dict(B=2, q_len=4, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[64, 97], window=5),
     "seq_eq_qlen": dict(B=2, q_len=4, Hq=8, Hkv=2, D=64, bt=16, seq_lens=[4, 4], sinks=True),
     "tiny_seqs": dict(B=4, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[1, 17, 32, 33]),
+    # a batch padded with empty slots (0 tokens), and sequences shorter than
+    # q_len: rows at negative positions attend nothing
+    "padded_zero_lengths": dict(B=4, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[0, 300, 0, 17],
+                                sinks=True),
+    "short_seqs_q4": dict(B=3, q_len=4, Hq=8, Hkv=2, D=64, bt=16, seq_lens=[2, 0, 90]),
+    "all_slots_empty": dict(B=2, q_len=2, Hq=8, Hkv=2, D=128, bt=16, seq_lens=[0, 0], sinks=True),
+    "short_seqs_prefill_lw4": dict(B=3, q_len=16, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[5, 0, 200],
+                                   sinks=True),
     "mha_rows1": dict(B=2, q_len=1, Hq=8, Hkv=8, D=128, bt=16, seq_lens=[100, 513]),
     "bt1_pages": dict(B=2, q_len=2, Hq=4, Hkv=2, D=64, bt=1, seq_lens=[37, 90], window=10, sinks=True),
     "bt8_d256": dict(B=1, q_len=1, Hq=8, Hkv=4, D=256, bt=8, seq_lens=[300]),
@@ -199,7 +207,7 @@ def test_parity_small(name, flags, ns):
 
 HND_CASES = ["gqa4_ragged", "d64_window_sinks", "d256_bt64", "mtp4_window_sinks", "bt1_pages",
              "pair_q2_perhead", "kg4_gqa_ragged", "prefill_q64", "mha_rows1", "batch130_mqa",
-             "prefill_q32_lw8_hnd_pages", "prefill_q16_lw4_d64", "prefill_q24_lw2"]
+             "prefill_q32_lw8_hnd_pages", "prefill_q16_lw4_d64", "prefill_q24_lw2", "padded_zero_lengths"]
 
 
 @pytest.mark.parametrize("name", HND_CASES)

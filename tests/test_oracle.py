@@ -309,6 +309,27 @@ def test_multi_token_rows_equal_single_token_calls():
         np.testing.assert_allclose(lse[:, i], l1[:, 0], rtol=1e-14, atol=0)
 
 
+@pytest.mark.parametrize("sinks", [True, False])
+def test_padded_and_short_sequences(sinks):
+    """Sequences shorter than q_len, down to 0 tokens (a batch padded with
+    empty slots): a query whose position L - q_len + i is negative attends
+    nothing, so its output is 0 and its LSE the sink logit (or -inf); the
+    other rows follow the plain definition (pure-Python brute force)."""
+    from tests.brute_force import brute_decode
+    wl = make_workload(B=3, q_len=4, Hq=4, Hkv=2, D=16, bt=16, seq_lens=[0, 23, 2], seed=11,
+                       sinks=sinks)
+    out, lse = oracle.decode(**wl.oracle_kwargs())
+    empty_lse = np.broadcast_to(wl.sinks.astype(np.float64), (4, 4)) if sinks else np.full((4, 4), -np.inf)
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    np.testing.assert_array_equal(lse[0], empty_lse)
+    assert np.array_equal(out[2, :2], np.zeros_like(out[2, :2]))
+    np.testing.assert_array_equal(lse[2, :2], empty_lse[:2])
+    assert np.isfinite(lse[1]).all() and np.isfinite(lse[2, 2:]).all()
+    bo, bl = brute_decode(wl)
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-14)
+
+
 def test_constant_keys_closed_form_with_sink():
     wl = _wl(sinks=True, window=0)
     wl.k_cache[:] = 0x38   # every key element decodes to 1.0
