@@ -635,6 +635,9 @@ def main():
                     help="time eager launches only (for profiler passes that do not follow graphs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the known-size device copies used to scale traffic counters")
+    ap.add_argument("--only", choices=ONLY_CHOICES,
+                    help="time one workload alone and print its [bench] line, no JSON line "
+                         "(for kernel traces that attribute every launch to one workload)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("WL_FETCH", "WL_WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="rocprofv3 --pmc output dirs -> profiles/traffic_<workload>.json (no GPU)")
     args = ap.parse_args()
@@ -662,6 +665,9 @@ def main():
     import decode_attention_paged_fp8pa_amd as fp
 
     fp.lib()
+    if args.only:
+        run_only(args, log)
+        return
     cfgs = [int(x) for x in args.configs.split(",") if x]
     if HEADLINE not in cfgs:
         cfgs.insert(0, HEADLINE)
@@ -696,6 +702,30 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head_wl, args.cpu_budget, log)
     emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill)
+
+
+ONLY_CHOICES = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "writer", "cfg2_kg4", "cfg2_hnd", "cfg3_hnd",
+                "cfg2_nvfp4_hnd", "prefill")
+
+
+def run_only(args, log):
+    """One workload of the bench, alone in the process (profiler runs)."""
+    name = args.only
+    graph = not args.no_graph
+    if name == "writer":
+        measure_writer(min(args.steps, 100), log)
+    elif name == "prefill":
+        measure_prefill(log)
+    else:
+        k = int(name[3])
+        kw = {}
+        if name.endswith("_kg4"):
+            kw["k_groups"] = 4
+        if name.endswith("_hnd"):
+            kw["kv_layout"] = "HND"
+        if "_nvfp4" in name:
+            kw["nvfp4"] = True
+        measure(k, args.steps, args.warmup, log, use_graph=graph, **kw)
 
 
 def widenings(args, log):
