@@ -20,7 +20,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Reference passages:
   workspace commit: split-KV producers write partial O and partial LSE that
   one reducer merges.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open, each the plainest one the rest supports:
 positions with q_len > 1 put query i at `seq_len - q_len + i`; a window W > 0
 keeps the last W positions including the query's own; a sink is a per-head
 logit in the units of `sm_scale * q.k` that joins the softmax denominator

@@ -15,7 +15,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Reference passage:
   Parameters: the FP8 type is `torch.float8_e4m3fn` (OCP E4M3 "FN": bias 7,
   largest finite value 448, no infinities, S.1111.111 is NaN).
 
-Readings of what the pages leave open (listed in the design doc):
+Readings of what the pages leave open, each the plainest one the rest supports:
 * rounding is to nearest, ties to even (the OCP default), and a finite
   value beyond the largest magnitude saturates to +-448 (the FN format has
   no infinity to round to); an infinite input saturates the same way; a NaN

@@ -15,7 +15,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Reference passages:
   1, one mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6); the block scale is an
   E4M3 byte, decoded as in the decode oracle.
 
-Readings of what the pages leave open (listed in the design doc):
+Readings of what the pages leave open, each the plainest one the rest supports:
 * element 2 i of a block sits in the low nibble of its byte, 2 i + 1 in the
   high nibble;
 * a value reads as E2M1(code) * E4M3(scale byte) * tensor scale (k_scale or
