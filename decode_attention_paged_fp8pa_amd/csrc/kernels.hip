@@ -54,6 +54,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -475,6 +476,9 @@ partial_mfma_kernel(Params p) {
   constexpr int LROW = D + 16;
   constexpr int LSLOT = 2 * kTileTokens * LROW;
   __shared__ __attribute__((aligned(16))) uint8_t ltile[LW ? 2 * LSLOT : 16];
+  // With the ring, PV's V^T operands are built by transposing LDS reads
+  // instead of byte permutes of each wavefront's own copy.
+  constexpr bool TRV = LW > 0;
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
@@ -647,9 +651,27 @@ partial_mfma_kernel(Params p) {
   // P = hi + lo E4M3 parts, O^T += V^T P^T.  The V^T operands are built
   // once and, with the K operands, serve every row block, which then runs
   // start to finish before the next (one block's temporaries live at a time).
-  auto compute_tile = [&](int tt, TileRegs& r) {
+  auto compute_tile = [&](int tt, TileRegs& r, int slot) {
     const int kb = tt * kTileTokens;
     const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
+    long vt[S];
+    if constexpr (TRV) {
+      // V^T operands straight from the LDS tile with gfx950's transposing
+      // read: in each 16-lane group, lane r names an 8-byte row (token
+      // kap(qd, r / 2), dims 16 e + 8 (r & 1) ...), and lane 8 h + c receives
+      // byte c of rows h, h + 2, ..., h + 14.  So byte j of operand e =
+      // V[kap(qd, j)][16 e + n].  (Tokens outside the span were written as
+      // zeros, so no byte needs clearing here.)
+      const int rt = n >> 1;
+      const int tk = rt < 4 ? 4 * qd + rt : 16 + 4 * qd + (rt - 4);
+      const uint8_t* vrow = ltile + slot * LSLOT + kTileTokens * LROW + tk * LROW + 8 * (n & 1);
+#pragma unroll
+      for (int e = 0; e < S; ++e) {
+        const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vrow + 16 * e));
+        vt[e] = as_long(uint32_t(t.x), uint32_t(t.y));
+      }
+    } else {
     if (edge) {
       // The V bytes of a token outside the sequence's attended span (read
       // whole with its group, possibly NaN codes) become 0, since P = 0
@@ -663,7 +685,6 @@ partial_mfma_kernel(Params p) {
       }
     }
     // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
-    long vt[S];
 #pragma unroll
     for (int wd = 0; wd < SW; ++wd) {
       uint32_t lo4[4], hi4[4];
@@ -671,6 +692,7 @@ partial_mfma_kernel(Params p) {
       transpose4x4(r.v[4][wd], r.v[5][wd], r.v[6][wd], r.v[7][wd], hi4);
 #pragma unroll
       for (int x4 = 0; x4 < 4; ++x4) vt[4 * wd + x4] = as_long(lo4[x4], hi4[x4]);
+    }
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -849,19 +871,24 @@ partial_mfma_kernel(Params p) {
       buf_load<CH, 0>(rs, uint32_t(stok[rr] * tok + scol[rr]), sR[rr]);
     }
   };
-  auto stage_write = [&](int slot) {
+  // `t` is the tile the chunk belongs to: bytes of a token outside the
+  // sequence's attended span (read whole with its 16-token group, possibly
+  // NaN codes) go into LDS as zeros, since P = 0 times NaN is NaN.
+  auto stage_write = [&](int slot, int t) {
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const int skv = sreg[rr] >> 1, sgrp = sreg[rr] & 1;
       uint8_t* dst =
           ltile + slot * LSLOT + skv * (kTileTokens * LROW) + (16 * sgrp + stok[rr]) * LROW + scol[rr];
+      const int key = t * kTileTokens + 16 * sgrp + stok[rr];
+      const uint32_t keep = (key >= ulo && key < uhi) ? ~0u : 0u;
       if constexpr (CH == 8) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{sR[rr][0], sR[rr][1]};
+        *reinterpret_cast<u32x2*>(dst) = u32x2{sR[rr][0] & keep, sR[rr][1] & keep};
       } else {
 #pragma unroll
         for (int i = 0; i < CH / 16; ++i)
-          reinterpret_cast<u32x4*>(dst)[i] =
-              u32x4{sR[rr][4 * i], sR[rr][4 * i + 1], sR[rr][4 * i + 2], sR[rr][4 * i + 3]};
+          reinterpret_cast<u32x4*>(dst)[i] = u32x4{sR[rr][4 * i] & keep, sR[rr][4 * i + 1] & keep,
+                                                   sR[rr][4 * i + 2] & keep, sR[rr][4 * i + 3] & keep};
       }
     }
   };
@@ -879,6 +906,7 @@ partial_mfma_kernel(Params p) {
         r.k[grp][4 * i + 3] = v.w;
       }
     }
+    if constexpr (TRV) return;  // V^T comes from transposing reads in compute_tile
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int tk = j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4);
@@ -976,22 +1004,22 @@ partial_mfma_kernel(Params p) {
   }
 
   if constexpr (LW > 0) {
-    stage_write(0);
+    stage_write(0, ts);
     stage_load(ts + 1);
     for (int tt = ts; tt < te; ++tt) {
       __syncthreads();  // tile tt is in its slot; the other slot's readers are done
       lds_read((tt - ts) & 1, ta);
-      stage_write((tt + 1 - ts) & 1);
+      stage_write((tt + 1 - ts) & 1, tt + 1);
       stage_load(tt + 2);
-      compute_tile(tt, ta);
+      compute_tile(tt, ta, (tt - ts) & 1);
     }
   } else {
   // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {
-    compute_tile(tt, ta);
+    compute_tile(tt, ta, 0);
     if (tt + 1 >= te) break;
     load_tile(tt + 2, ta, 0);
-    compute_tile(tt + 1, tb);
+    compute_tile(tt + 1, tb, 0);
     load_tile(tt + 3, tb, 1);
   }
   }
@@ -999,7 +1027,7 @@ partial_mfma_kernel(Params p) {
   // ---- epilogue: l over the 4 lane groups, normalise, write
   // O[b][e][i] is output dim S * (4 qd + i) + e of this lane's row in block
   // b (with paired heads: of the wavefront's 128, the row's own 64 start at
-  // 64 * (n >> 3)).
+  // 64 * (n >> 3)); with V^T from transposing reads, dim 16 e + 4 qd + i.
   const int dlane = PR == 2 ? S * 4 * (qd & 1) : S * 4 * qd;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -1010,7 +1038,22 @@ partial_mfma_kernel(Params p) {
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : vs / l;
     const float lse = empty ? -INFINITY : (m[b] + log2_fast(l) - kPShift) * kLn2;
-    if (p.direct) {
+    if (TRV && p.direct) {
+      uint16_t* orow = p.out + row[b].out_row * DH + d0 + 4 * qd;
+#pragma unroll
+      for (int e = 0; e < S; ++e)
+        *reinterpret_cast<u32x2*>(orow + 16 * e) =
+            u32x2{pack_bf16x2(O[b][e][0] * inv, O[b][e][1] * inv), pack_bf16x2(O[b][e][2] * inv, O[b][e][3] * inv)};
+      if (p.lse && qd == 0 && w.half == 0) p.lse[row[b].out_row] = lse;
+    } else if (TRV) {
+      const size_t slot = row[b].out_row * p.num_splits + w.split;
+      if (!empty) {
+        float* prow = p.part_o + slot * DH + d0 + 4 * qd;
+#pragma unroll
+        for (int e = 0; e < S; ++e) reinterpret_cast<f32x4*>(prow + 16 * e)[0] = O[b][e] * inv;
+      }
+      if (qd == 0 && w.half == 0) p.part_lse[slot] = lse;
+    } else if (p.direct) {
       uint16_t* orow = p.out + row[b].out_row * DH + d0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
