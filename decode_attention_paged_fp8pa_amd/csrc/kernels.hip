@@ -480,12 +480,13 @@ __device__ __forceinline__ TileRange rows_tiles(const Params& p, int L, int qmin
 // wavefront (one row group), wrong when several row groups re-read it.
 //
 // LW = 2, 4 or 8: the workgroup is LW row groups of one kv head sharing each
-// K/V tile through an LDS ring (chunked prefill, wide MTP).  With 8 the
-// register budget is 128, so a compute unit holds two such workgroups, whose
-// matrix, vector and LDS work then overlap (the 512-token chunk ~18% faster).
+// K/V tile through an LDS ring (chunked prefill, wide MTP).  With 4 or 8 the
+// register budget is 128 (4 wavefronts per SIMD), so a compute unit holds
+// more such workgroups, whose matrix, vector and LDS work then overlap (the
+// 512-token chunk ~18% faster); with 2 the staging registers would spill.
 template <int D, int DS, int PR, int NB, int NT, int LW>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
-__attribute__((amdgpu_waves_per_eu((NB == 1 && D / DS == 64) || LW == 8 ? 4 : D / DS <= 128 ? 2 : 1, 8))) void
+__attribute__((amdgpu_waves_per_eu((NB == 1 && D / DS == 64) || LW >= 4 ? 4 : D / DS <= 128 ? 2 : 1, 8))) void
 partial_mfma_kernel(Params p) {
   static_assert(DS == 1 || DS == 2, "head_dim split");
   static_assert(PR == 1 || (PR == 2 && D == 128 && DS == 1), "paired heads");
@@ -875,7 +876,9 @@ partial_mfma_kernel(Params p) {
   // region, CH bytes each; with 2, each wavefront covers two regions.
   constexpr int RPW = LWS >= 4 ? 1 : 4 / LWS;  // regions per wavefront
   constexpr int CH = LWS >= 4 ? 2 * kTileTokens * D / (64 * LWS) : 16 * D / 64;
-  const int swv = int(threadIdx.x >> 6);
+  // (uniform over the wavefront; saying so keeps the page choice and the
+  // buffer descriptor in scalar registers)
+  const int swv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   int sreg[RPW], stok[RPW], scol[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
