@@ -1316,9 +1316,8 @@ partial_mfma_nvfp4_kernel(Params p) {
         sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
       }
     }
-    float ms = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    ms = max_over_groups(ms);
+    float ms = max3_raw(max3_raw(sv[0], sv[1], sv[2]), max3_raw(sv[3], sv[4], sv[5]), max_raw(sv[6], sv[7]));
+    ms = max_over_groups_raw(ms);
     const float mx = ms * cr;
     const bool bump = mx > m + kLazy;
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
