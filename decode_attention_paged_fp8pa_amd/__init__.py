@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     WriteShape,
     fp8pa_cache_write,
     fp8pa_debug_e4m3_to_f32,
+    fp8pa_debug_lds_tr8,
     fp8pa_debug_mfma_fp8,
     fp8pa_debug_nvfp4,
     fp8pa_debug_wave_ops,

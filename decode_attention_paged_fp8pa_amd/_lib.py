@@ -134,6 +134,7 @@ _SIGS = {
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
     "fp8pa_debug_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
+    "fp8pa_debug_lds_tr8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
 }
 
 
@@ -256,6 +257,12 @@ def fp8pa_debug_nvfp4(data, scales, out, n, stream=None) -> None:
     st = lib().fp8pa_debug_nvfp4(_ptr(data), _ptr(scales), _ptr(out), int(n), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_nvfp4")
+
+
+def fp8pa_debug_lds_tr8(lds_bytes, row_addr, out, stream=None) -> None:
+    st = lib().fp8pa_debug_lds_tr8(_ptr(lds_bytes), _ptr(row_addr), _ptr(out), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_lds_tr8")
 
 
 def fp8pa_debug_mfma_fp8(a, b, c, stream=None) -> None:

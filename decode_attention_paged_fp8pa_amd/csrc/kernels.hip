@@ -1857,6 +1857,19 @@ __global__ void debug_wave_ops_kernel(const int32_t* in, int vmax, int32_t* out)
   out[192 + lane] = tot;
 }
 
+// One transposing LDS read per lane over a 4 KB copy of `src`; row
+// addresses are clamped to 8-byte-aligned offsets inside the copy.
+__global__ void debug_lds_tr8_kernel(const uint8_t* src, const int32_t* addr, uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4096];
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < 4096 / 16; i += 64)
+    reinterpret_cast<u32x4*>(lds)[i] = reinterpret_cast<const u32x4*>(src)[i];
+  __syncthreads();
+  const int a = min(max(addr[lane], 0), 4096 - 8) & ~7;
+  const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(lds + a));
+  reinterpret_cast<u32x2*>(out)[lane] = u32x2{uint32_t(t.x), uint32_t(t.y)};
+}
+
 __global__ void debug_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
@@ -2149,6 +2162,15 @@ fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float
 fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream) {
   if (!in || !out || vmax < 0) return FP8PA_ERR_INVALID_ARG;
   debug_wave_ops_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(in, vmax, out);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_lds_tr8(const uint8_t* lds_bytes, const int32_t* row_addr, uint8_t* out,
+                                 void* stream) {
+  if (!lds_bytes || !row_addr || !out) return FP8PA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(lds_bytes) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return FP8PA_ERR_MISALIGNED;
+  debug_lds_tr8_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(lds_bytes, row_addr, out);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

@@ -11,7 +11,10 @@
  *    the decode kernels assume;
  *  - the wavefront-wide integer sum, maximum and prefix sum (DPP row ops,
  *    permlane swaps, ballot + mbcnt) with which the kernels size a batch's
- *    KV splits on the device.
+ *    KV splits on the device;
+ *  - the lane mapping of gfx950's transposing LDS read ds_read_b64_tr_b8,
+ *    from which the kernels that share K/V tiles through LDS build PV's
+ *    V^T operands.
  *
  * Same conventions as fp8pa.h: device pointers owned by the caller, work
  * queued on `stream` (a hipStream_t passed as void*), a status returned.
@@ -51,6 +54,17 @@ fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, 
  * maximum, out[192 + l] = the total the prefix routine reports.  out: int32
  * [256]. */
 fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream);
+
+/* One wavefront of 64 lanes over a 4 KB LDS copy of lds_bytes (uint8
+ * [4096], 16-byte aligned): lane l performs one ds_read_b64_tr_b8 at LDS
+ * offset row_addr[l] (int32 [64]; clamped to [0, 4088] and rounded down to a
+ * multiple of 8) and stores its 8 result bytes at out[8 l .. 8 l + 7] (uint8
+ * [512], 16-byte aligned).  The mapping the kernels rely on: with
+ * l = 16 g + 8 h + c (c < 8, h < 2), out[8 l + t] =
+ * lds_bytes[row_addr[16 g + 2 t + h] + c] for t < 8, i.e. each 16-lane group
+ * transposes the 16 x 8-byte rows its lanes name. */
+fp8pa_status fp8pa_debug_lds_tr8(const uint8_t* lds_bytes, const int32_t* row_addr, uint8_t* out,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -307,6 +307,8 @@ def test_debug_entry_points_check_arguments():
     assert L.fp8pa_debug_e4m3_to_f32(None, None, 0, None) == _lib.FP8PA_OK
     assert L.fp8pa_debug_mfma_fp8(None, 0x1000, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
     assert L.fp8pa_debug_wave_ops(None, 5, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_lds_tr8(0x1000, None, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_lds_tr8(0x1008, 0x3000, 0x2000, None) == _lib.FP8PA_ERR_MISALIGNED
     assert L.fp8pa_debug_wave_ops(0x1000, -1, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
 
 

@@ -90,6 +90,25 @@ def test_hw_wave_reductions_and_prefix(vmax):
     assert np.all(got[192:] == x64.sum())
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_hw_lds_transposing_read(seed):
+    """The lane mapping of ds_read_b64_tr_b8 that the LDS-shared prefill path
+    builds PV's V^T operands with: lane 16 g + 8 h + c gets byte c of the rows
+    named by lanes 16 g + h, 16 g + h + 2, ..., 16 g + h + 14."""
+    rng = np.random.default_rng(seed)
+    src = rng.integers(0, 256, size=4096, dtype=np.uint8)
+    addr = (rng.integers(0, 4096 // 8, size=64) * 8).astype(np.int32)
+    out = torch.empty(512, dtype=torch.uint8, device="cuda")
+    fp.fp8pa_debug_lds_tr8(torch.from_numpy(src).cuda(), torch.from_numpy(addr).cuda(), out)
+    got = out.cpu().numpy().reshape(64, 8)
+    want = np.empty((64, 8), dtype=np.uint8)
+    for lane in range(64):
+        g, h, c = lane // 16, (lane % 16) // 8, lane % 8
+        for t in range(8):
+            want[lane, t] = src[addr[16 * g + 2 * t + h] + c]
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------- small, every element
 
 SMALL = {
