@@ -417,6 +417,36 @@ def test_graph_capture_replay_cfg5():
         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"replay {it} differs"
 
 
+@pytest.mark.parametrize("name", ["prefill_q64", "prefill_q16_lw4_d64", "mtp_q4_g8_lw2"])
+@pytest.mark.parametrize("ns", [0, 3])
+def test_graph_capture_replay_shared_tiles(name, ns):
+    """The kernels whose row groups share K/V tiles through LDS (8, 4 and 2
+    groups), captured once and replayed: every replay equals the eager call
+    bit for bit."""
+    wl, t, _ = _small(name)
+    out, lse = run(wl, t, num_splits=ns)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(wl, t, num_splits=ns, out=out, lse=lse, workspace=_ws_for(wl, t, ns))
+    for it in range(3):
+        out.fill_(float(it))
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"{name}: replay {it} differs"
+
+
+def _ws_for(wl, t, ns):
+    """A workspace allocated before capture (the library allocates nothing)."""
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=wl.window,
+                         sm_scale=wl.sm_scale, max_seq_len=max(1, int(wl.seq_lens.max())),
+                         num_splits=ns, k_groups=wl.k_groups)
+    return torch.empty(max(fp.fp8pa_workspace_bytes(shape), 256), dtype=torch.uint8, device="cuda")
+
+
 # ------------------------------------------- sharded KV (context parallel)
 
 def test_context_parallel_shards_merge():
