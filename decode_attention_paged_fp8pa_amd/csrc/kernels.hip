@@ -174,25 +174,19 @@ __device__ __forceinline__ float max_over_groups(float v) {
   return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
-// The hardware maximum of finite-or-infinite values.  Written out because
-// fmaxf makes the compiler quiet each input first (an extra instruction per
-// operand in IEEE mode); scores here are MFMA sums or -inf, never NaN.
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// Maxima of scores (MFMA sums or -inf, never NaN) as IEEE 754-2019
+// `maximum`, which gfx950 executes as v_maximum3_f32 as it stands: fmaxf
+// makes the compiler quiet every operand first in IEEE mode (one more
+// instruction per operand).  For non-NaN inputs the two agree up to the sign
+// of a zero maximum, which no caller can observe.
+__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3_nn(float a, float b, float c) { return max_nn(max_nn(a, b), c); }
 // max_over_groups for values that are never NaN
-__device__ __forceinline__ float max_over_groups_raw(float v) {
+__device__ __forceinline__ float max_over_groups_nn(float v) {
   const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = max_raw(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  v = max_nn(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
   const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max_raw(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  return max_nn(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
 // Sum over the same four lanes (n, n + 16, n + 32, n + 48), the same in each.
@@ -813,8 +807,8 @@ partial_mfma_kernel(Params p) {
           sv[j] = (key >= row[b].klo && key < row[b].khi) ? sv[j] : -INFINITY;
         }
       }
-      float ms = max3_raw(max3_raw(sv[0], sv[1], sv[2]), max3_raw(sv[3], sv[4], sv[5]), max_raw(sv[6], sv[7]));
-      ms = max_over_groups_raw(ms);
+      float ms = max3_nn(max3_nn(sv[0], sv[1], sv[2]), max3_nn(sv[3], sv[4], sv[5]), max_nn(sv[6], sv[7]));
+      ms = max_over_groups_nn(ms);
       const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
       // Lazy reference max: move m only when this tile exceeds it by more
       // than kLazy (log2 units), so most tiles skip the O rescale; P stays
@@ -1316,8 +1310,8 @@ partial_mfma_nvfp4_kernel(Params p) {
         sv[j] = (key >= row.klo && key < row.khi) ? sv[j] : -INFINITY;
       }
     }
-    float ms = max3_raw(max3_raw(sv[0], sv[1], sv[2]), max3_raw(sv[3], sv[4], sv[5]), max_raw(sv[6], sv[7]));
-    ms = max_over_groups_raw(ms);
+    float ms = max3_nn(max3_nn(sv[0], sv[1], sv[2]), max3_nn(sv[3], sv[4], sv[5]), max_nn(sv[6], sv[7]));
+    ms = max_over_groups_nn(ms);
     const float mx = ms * cr;
     const bool bump = mx > m + kLazy;
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {

@@ -367,6 +367,46 @@ def test_determinism_and_split_invariance_cfg2():
         assert np.max(np.abs(c[1] - a[1])) < 1e-3
 
 
+def _repeat_bitwise(wl, t, label):
+    """Eight eager calls and three graph replays of one call give the same
+    bits: the kernels have no race and no timing-dependent read (a VALU read
+    of an MFMA result too early, say, shows up here as run-to-run noise)."""
+    ns = 0
+    ref = tuple(x.clone() for x in run(wl, t, num_splits=ns))
+    for i in range(8):
+        got = run(wl, t, num_splits=ns)
+        assert all(torch.equal(g, r) for g, r in zip(got, ref)), f"{label}: eager call {i} differs"
+    out, lse = torch.empty_like(ref[0]), torch.empty_like(ref[1])
+    ws = _ws_for(wl, t, ns)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(wl, t, num_splits=ns, out=out, lse=lse, workspace=ws)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"{label}: replay {i} differs"
+
+
+@pytest.mark.parametrize("k,kg", [(2, 1), (2, 4), (3, 1), (5, 1)])
+def test_bitwise_repeatable_full_workloads(k, kg):
+    if kg == 1:
+        wl, t = _cfg(k)
+    else:
+        _cfg_cache.clear()
+        torch.cuda.empty_cache()
+        wl = make_config(k, k_groups=kg)
+        t = upload(wl)
+    _repeat_bitwise(wl, t, f"cfg{k} k_groups={kg}")
+
+
+@pytest.mark.parametrize("name", ["prefill_q64", "prefill_q16_lw4_d64", "mtp_q4_g8_lw2", "kg4_q8_few_keys_lw2"])
+def test_bitwise_repeatable_shared_tiles(name):
+    wl, t, _ = _small(name)
+    _repeat_bitwise(wl, t, name)
+
+
 def test_block_permutation_invariance_cfg2():
     wl, t = _cfg(2)
     a = to_host(*run(wl, t))
