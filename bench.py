@@ -549,7 +549,20 @@ def cpu_baseline(wl, budget_s, log):
     return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{wl.name}: {seqs} sequence decodes (all {wl.Hq} heads each; the {wl.B}-sequence "
                       f"batch repeated, {passes} pass(es)), {done_bytes} KV bytes in {el:.1f}s; "
-                      f"{done_tokens / el:.3g} tokens/s"}
+                      f"{done_tokens / el:.3g} tokens/s",
+            "host": {"cpu_model": cpu_model(), "cpus_available": ncores, "blas_threads": threads}}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 CALIB_BYTES = 256 << 20
