@@ -1,5 +1,5 @@
 """Float64 CPU oracle for paged flash-decode attention over an E4M3 (or
-NVFP4) KV cache, and for the writers that fill those caches from bf16 keys
+NVFP4 or MXFP8) KV cache, and for the writers that fill those caches from bf16 keys
 and values.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
@@ -35,4 +35,10 @@ from .nvfp4_ref import (  # noqa: F401
     nvfp4_side_bytes,
     nvfp4_gather,
     nvfp4_cache_write,
+)
+from .mxfp8_ref import (  # noqa: F401
+    e8m0_decode,
+    mxfp8_side_bytes,
+    mxfp8_gather,
+    mxfp8_cache_write,
 )

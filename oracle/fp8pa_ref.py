@@ -158,9 +158,10 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
       k_cache     uint8  [num_blocks, bt, Hkv, D]  E4M3 codes (token-major pages),
                   or [num_blocks, Hkv, bt, D] with kv_layout="HND" (head-major)
       v_cache     uint8  the same shape and layout as k_cache
-                  (kv_format="nvfp4": uint8 [num_blocks, page_stride] NVFP4
-                  pools, read by nvfp4_ref.nvfp4_gather; num_kv_heads and
-                  block_tokens then give the page geometry)
+                  (kv_format="nvfp4" / "mxfp8": uint8 [num_blocks,
+                  page_stride] NVFP4 / MXFP8 pools, read by
+                  nvfp4_ref.nvfp4_gather / mxfp8_ref.mxfp8_gather; num_kv_heads
+                  and block_tokens then give the page geometry)
       block_table int32  [B, max_blocks]  page of each logical page index
       seq_lens    int32  [B]  tokens in each sequence, the q_len new ones included
       k_scale, v_scale  float32 [1] (per tensor) or [Hkv] (per kv head); with
@@ -182,13 +183,15 @@ def decode(q_bits, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
     """
     q_bits = np.asarray(q_bits)
     B, q_len, Hq, D = q_bits.shape
-    assert kv_layout in ("NHD", "HND") and kv_format in ("e4m3", "nvfp4")
-    if kv_format == "nvfp4":
+    assert kv_layout in ("NHD", "HND") and kv_format in ("e4m3", "nvfp4", "mxfp8")
+    if kv_format in ("nvfp4", "mxfp8"):
+        from .mxfp8_ref import mxfp8_gather
         from .nvfp4_ref import nvfp4_gather
         Hkv = int(num_kv_heads)
+        blocked = nvfp4_gather if kv_format == "nvfp4" else mxfp8_gather
 
         def gather(cache, row, g, ts, scale, layout):
-            return nvfp4_gather(cache, row, g, ts, scale, Hkv, int(block_tokens), D, layout)
+            return blocked(cache, row, g, ts, scale, Hkv, int(block_tokens), D, layout)
     else:
         Hkv = k_cache.shape[1] if kv_layout == "HND" else k_cache.shape[2]
         gather = _gather

@@ -58,6 +58,24 @@ def depage_nvfp4(pool, table_row, seq_len, Hkv, bt, D, layout):
     return out
 
 
+def depage_mxfp8(pool, table_row, seq_len, Hkv, bt, D, layout):
+    """Contiguous float64 [seq_len, Hkv, D] (E4M3 code value x 2^(scale - 127))
+    of one sequence of an MXFP8 pool, one element at a time."""
+    out = np.zeros((seq_len, Hkv, D))
+    sc_row = D // 32
+    data_bytes = Hkv * bt * D
+    for t in range(seq_len):
+        page = int(table_row[t // bt])
+        slot = t % bt
+        for h in range(Hkv):
+            row = h * bt + slot if layout == "HND" else slot * Hkv + h
+            for d in range(D):
+                code = np.array([pool[page, row * D + d]], dtype=np.uint8)
+                s = int(pool[page, data_bytes + row * sc_row + d // 32])
+                out[t, h, d] = _codes_to_float(code)[0] * (math.nan if s == 255 else 2.0 ** (s - 127))
+    return out
+
+
 def brute_decode(wl, key_range=None, sinks="from_workload"):
     """Attention of every (b, i, h) row by plain loops; returns (out, lse)."""
     B, q_len, Hq, D = wl.q_bits.shape
@@ -76,6 +94,9 @@ def brute_decode(wl, key_range=None, sinks="from_workload"):
         if getattr(wl, "kv_format", "e4m3") == "nvfp4":
             K = depage_nvfp4(wl.k_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
             V = depage_nvfp4(wl.v_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
+        elif getattr(wl, "kv_format", "e4m3") == "mxfp8":
+            K = depage_mxfp8(wl.k_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
+            V = depage_mxfp8(wl.v_cache, wl.block_table[b], L, Hkv, wl.bt, D, wl.kv_layout)
         else:
             K = _codes_to_float(depage(wl.k_cache, wl.block_table[b], L))
             V = _codes_to_float(depage(wl.v_cache, wl.block_table[b], L))

@@ -69,8 +69,8 @@ class Workload:
     sm_scale: float
     meta: dict = field(default_factory=dict)
     k_groups: int = 1
-    kv_format: str = "e4m3"   # "nvfp4": k_cache / v_cache are uint8 [num_blocks, page_stride]
-    kv_layout: str = "NHD"    # page layout of the nvfp4 pools ("NHD" or "HND")
+    kv_format: str = "e4m3"   # "nvfp4" / "mxfp8": k_cache / v_cache are uint8 [num_blocks, page_stride]
+    kv_layout: str = "NHD"    # page layout of those pools ("NHD" or "HND")
 
     @property
     def B(self):
@@ -90,11 +90,11 @@ class Workload:
 
     @property
     def Hkv(self):
-        return self.meta["Hkv"] if self.kv_format == "nvfp4" else self.k_cache.shape[2]
+        return self.meta["Hkv"] if self.kv_format != "e4m3" else self.k_cache.shape[2]
 
     @property
     def bt(self):
-        return self.meta["bt"] if self.kv_format == "nvfp4" else self.k_cache.shape[1]
+        return self.meta["bt"] if self.kv_format != "e4m3" else self.k_cache.shape[1]
 
     @property
     def num_blocks(self):
@@ -105,8 +105,8 @@ class Workload:
                   block_table=self.block_table, seq_lens=self.seq_lens,
                   k_scale=self.k_scale, v_scale=self.v_scale, sinks=self.sinks,
                   window=self.window, sm_scale=self.sm_scale, k_groups=self.k_groups)
-        if self.kv_format == "nvfp4":
-            kw.update(kv_format="nvfp4", kv_layout=self.kv_layout, num_kv_heads=self.Hkv,
+        if self.kv_format != "e4m3":
+            kw.update(kv_format=self.kv_format, kv_layout=self.kv_layout, num_kv_heads=self.Hkv,
                       block_tokens=self.bt)
         return kw
 
@@ -246,9 +246,7 @@ NVFP4_POISON_SCALE = 0x7F   # E4M3 NaN: a block read where nothing is attended y
 NVFP4_POISON_DATA = 0x77
 
 
-def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm", pool=None,
-                        scale=("tensor", 0.05), window=0, sinks=False, sm_scale=None,
-                        poison=True, name="nvfp4", kv_layout="NHD", page_stride=None):
+def make_nvfp4_workload(**kw):
     """A workload whose K/V pools are NVFP4 pages: uint8 [num_blocks,
     page_stride], each page one side's data region ([bt][Hkv] or [Hkv][bt]
     rows of D/2 bytes, two 4-bit codes per byte) followed by its scale region
@@ -257,6 +255,24 @@ def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm
     and D/16 scale bytes uniform over the E4M3 codes 0x48..0x57 (4 to 15).
     Every other byte is NVFP4_POISON_DATA / NVFP4_POISON_SCALE when `poison`.
     """
+    return _make_blockscaled_workload(fmt="nvfp4", **kw)
+
+
+def make_mxfp8_workload(**kw):
+    """A workload whose K/V pools are MXFP8 pages: each page one side's data
+    region (rows of D E4M3 bytes) followed by its scale region (rows of D/32
+    E8M0 bytes), in the same row orders as the NVFP4 pages.  Step 5 draws, for
+    every attended position and kv head, D data bytes uniform over the
+    non-NaN E4M3 codes and D/32 scale bytes uniform over 119..124 (2^-8 to
+    2^-3).  Every other byte is the NaN data code 0x7F or the NaN scale 0xFF
+    when `poison`."""
+    return _make_blockscaled_workload(fmt="mxfp8", **kw)
+
+
+def _make_blockscaled_workload(*, fmt, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm",
+                               pool=None, scale=("tensor", 0.05), window=0, sinks=False,
+                               sm_scale=None, poison=True, name=None, kv_layout="NHD",
+                               page_stride=None):
     rng = np.random.default_rng(seed)
     if isinstance(seq_lens, tuple) and seq_lens and seq_lens[0] == "uniform":
         sl = rng.integers(seq_lens[1], seq_lens[2] + 1, size=B).astype(np.int32)
@@ -282,19 +298,22 @@ def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm
         v_scale = rng.uniform(scale[1], scale[2], size=Hkv).astype(np.float32)
     qf = rng.standard_normal((B, q_len, Hq, D), dtype=np.float32)
     q_bits = _bf16_bits(qf)
-    data_row, sc_row = D // 2, D // 16
+    data_row, sc_row = (D // 2, D // 16) if fmt == "nvfp4" else (D, D // 32)
+    poison_data, poison_scale = ((NVFP4_POISON_DATA, NVFP4_POISON_SCALE) if fmt == "nvfp4"
+                                 else (0x7F, 0xFF))
     data_bytes = Hkv * bt * data_row
     side = Hkv * bt * (data_row + sc_row)
     stride = int(page_stride or side)
+    name = name or fmt
     wl_tmp = Workload(name, q_bits, np.empty((0, bt, Hkv, D), np.uint8), None, bt_arr, sl,
                       k_scale, v_scale, None, int(window), 0.0)
     pools = []
     for _ in ("k", "v"):
         pool_arr = np.zeros((num_blocks, stride), dtype=np.uint8)
         if poison:
-            pool_arr[:, :data_bytes] = NVFP4_POISON_DATA
-            pool_arr[:, data_bytes:side] = NVFP4_POISON_SCALE
-            pool_arr[:, side:] = NVFP4_POISON_SCALE
+            pool_arr[:, :data_bytes] = poison_data
+            pool_arr[:, data_bytes:side] = poison_scale
+            pool_arr[:, side:] = poison_scale
         for b in range(B):
             lo, hi = wl_tmp.key_union(b)
             if not poison:
@@ -305,7 +324,11 @@ def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm
             pages = bt_arr[b, ts // bt].astype(np.int64)
             slots = ts % bt
             data = rng.integers(0, 256, size=(hi - lo, Hkv, data_row), dtype=np.uint8)
-            scl = rng.integers(0x48, 0x58, size=(hi - lo, Hkv, sc_row), dtype=np.uint8)
+            if fmt == "nvfp4":
+                scl = rng.integers(0x48, 0x58, size=(hi - lo, Hkv, sc_row), dtype=np.uint8)
+            else:
+                data[(data & 0x7F) == 0x7F] -= 1          # no NaN codes in attended data
+                scl = rng.integers(119, 125, size=(hi - lo, Hkv, sc_row), dtype=np.uint8)
             for h in range(Hkv):
                 r = h * bt + slots if kv_layout == "HND" else slots * Hkv + h
                 d_off = r * data_row
@@ -320,4 +343,4 @@ def make_nvfp4_workload(*, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm
                     block_table=bt_arr, seq_lens=sl, k_scale=k_scale, v_scale=v_scale,
                     sinks=sk, window=int(window), sm_scale=float(sm_scale),
                     meta=dict(seed=seed, poison=poison, Hkv=Hkv, bt=bt, page_stride=stride),
-                    kv_format="nvfp4", kv_layout=kv_layout)
+                    kv_format=fmt, kv_layout=kv_layout)
