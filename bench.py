@@ -27,7 +27,8 @@ Four widenings are timed after the decode: the headline workload with K
 scales in four head_dim groups ("k_groups_variant"), the headline and the
 windowed head_dim-64 workloads with head-major pages ("hnd_variant"), the
 headline batch with NVFP4 pages ("nvfp4_variant", bytes = D/2 + D/16 per
-token, kv head and side), and chunked prefill,
+token, kv head and side) and with MXFP8 pages ("mxfp8_variant", D + D/32
+bytes), and chunked prefill,
 q_len 16 to 512 new tokens over a paged context ("prefill", in algorithmic
 TFLOP/s against the dense FP8 peak).
 
@@ -74,7 +75,7 @@ def kv_bytes(wl):
     Per attended token per kv head the method must read D bytes of K and D
     of V; tokens outside every row's window are not counted.
     """
-    per_row = (wl.D // 2 + wl.D // 16) if wl.kv_format == "nvfp4" else wl.D
+    per_row = {"nvfp4": wl.D // 2 + wl.D // 16, "mxfp8": wl.D + wl.D // 32}.get(wl.kv_format, wl.D)
     return wl.attended_positions() * wl.Hkv * per_row * 2
 
 
@@ -180,32 +181,34 @@ def sample_gpu_state(busy, seconds_cap=20.0):
         return None
 
 
-def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", nvfp4=False,
+def measure(k, steps, warmup, log, use_graph=True, k_groups=1, kv_layout="NHD", kv_format="e4m3",
             sample_clocks=False):
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
-    from workloads import CONFIGS, make_config, make_nvfp4_workload
+    from workloads import CONFIGS, make_config, make_mxfp8_workload, make_nvfp4_workload
 
     t_gen = time.time()
-    if nvfp4:  # the same batch shape with NVFP4 pages (random codes and block scales)
+    blockscaled = kv_format != "e4m3"
+    if blockscaled:  # the same batch shape with block-scaled pages (random codes and block scales)
         c = CONFIGS[k]
         seq = c["seq"]
         sls = seq[1] if seq[0] == "fixed" else (list(seq[1]) if seq[0] == "list" else ("uniform", seq[1], seq[2]))
-        wl = make_nvfp4_workload(B=c["B"], q_len=c["q_len"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], bt=c["bt"],
+        make = make_nvfp4_workload if kv_format == "nvfp4" else make_mxfp8_workload
+        wl = make(B=c["B"], q_len=c["q_len"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], bt=c["bt"],
                                  seq_lens=sls, seed=1000 + k, pool=c["pool"], scale=c["scale"],
                                  window=c["window"], sinks=c["sinks"], sm_scale=c["sm_scale"],
-                                 kv_layout=kv_layout, name=f"cfg{k}_{c['name']}_nvfp4")
+                                 kv_layout=kv_layout, name=f"cfg{k}_{c['name']}_{kv_format}")
     else:
         wl = make_config(k, k_groups=k_groups)
-    label = (f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "") + ("_nvfp4" if nvfp4 else "")
+    label = (f"cfg{k}" + (f"_kg{k_groups}" if k_groups > 1 else "") + (f"_{kv_format}" if blockscaled else "")
              + ("_hnd" if kv_layout == "HND" else ""))
     log(f"[bench] {label}: generated in {time.time() - t_gen:.1f}s; {describe(wl)}")
     dev = torch.device("cuda")
     kvb = kv_bytes(wl)
     copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / max(kvb, 1)))))
     q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    if kv_layout == "HND" and not nvfp4:  # the same pages stored head-major
+    if kv_layout == "HND" and not blockscaled:  # the same pages stored head-major
         kc0 = torch.from_numpy(np.ascontiguousarray(wl.k_cache.transpose(0, 2, 1, 3))).to(dev)
         vc0 = torch.from_numpy(np.ascontiguousarray(wl.v_cache.transpose(0, 2, 1, 3))).to(dev)
     else:
@@ -718,7 +721,7 @@ def main():
 
 
 ONLY_CHOICES = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "writer", "cfg2_kg4", "cfg2_hnd", "cfg3_hnd",
-                "cfg2_nvfp4_hnd", "prefill")
+                "cfg2_nvfp4_hnd", "cfg2_mxfp8_hnd", "prefill")
 
 
 def run_only(args, log):
@@ -736,8 +739,9 @@ def run_only(args, log):
             kw["k_groups"] = 4
         if name.endswith("_hnd"):
             kw["kv_layout"] = "HND"
-        if "_nvfp4" in name:
-            kw["nvfp4"] = True
+        for f in ("nvfp4", "mxfp8"):
+            if f"_{f}" in name:
+                kw["kv_format"] = f
         measure(k, args.steps, args.warmup, log, use_graph=graph, **kw)
 
 
@@ -763,15 +767,19 @@ def widenings(args, log):
                           "pct_peak": round(r["pct_peak"], 2)}
         del w_
     # the headline batch with NVFP4 pages (head-major, as the gist runs them)
-    r, w_ = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph, kv_layout="HND",
-                    nvfp4=True)
-    nv = {"workload": r["describe"] + " kv_format=nvfp4 kv_layout=HND", "step_us": round(r["step_ms"] * 1e3, 2),
-          "partial_us": round(r["partial_ms"] * 1e3, 2), "kv_bytes": r["kv_bytes"],
-          "kv_gbps": round(r["kv_gbps"], 1), "pct_peak": round(r["pct_peak"], 2),
-          "tokens_per_s": round(r["tokens_per_s"], 1), "variant": "dot" if r["plan"]["variant"] == 0 else "mfma"}
-    del w_
+    # and with MXFP8 pages (the same row orders)
+    bs = {}
+    for f in ("nvfp4", "mxfp8"):
+        r, w_ = measure(HEADLINE, args.steps, args.warmup, log, use_graph=not args.no_graph, kv_layout="HND",
+                        kv_format=f)
+        bs[f] = {"workload": r["describe"] + f" kv_format={f} kv_layout=HND",
+                 "step_us": round(r["step_ms"] * 1e3, 2), "partial_us": round(r["partial_ms"] * 1e3, 2),
+                 "kv_bytes": r["kv_bytes"], "kv_gbps": round(r["kv_gbps"], 1), "pct_peak": round(r["pct_peak"], 2),
+                 "tokens_per_s": round(r["tokens_per_s"], 1),
+                 "variant": "dot" if r["plan"]["variant"] == 0 else "mfma"}
+        del w_
     prefill = measure_prefill(log)
-    return writer, kg, hnd, nv, prefill
+    return writer, kg, hnd, bs, prefill
 
 
 def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill):
@@ -799,7 +807,8 @@ def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, pre
         "writer": writer,
         "k_groups_variant": kg,
         "hnd_variant": hnd,
-        "nvfp4_variant": nv,
+        "nvfp4_variant": (nv or {}).get("nvfp4"),
+        "mxfp8_variant": (nv or {}).get("mxfp8"),
         "prefill": prefill,
         "per_workload": {
             f"cfg{k}": {

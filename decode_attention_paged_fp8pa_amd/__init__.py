@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     FP8PA_FLAG_PARTIAL_ONLY,
     FP8PA_KV_E4M3,
     FP8PA_KV_NVFP4,
+    FP8PA_KV_MXFP8,
     FP8PA_LAYOUT_HND,
     FP8PA_LAYOUT_NHD,
     FP8PA_SPLIT_BALANCED,
@@ -32,6 +33,7 @@ from ._lib import (  # noqa: F401
     fp8pa_cache_write,
     fp8pa_debug_e4m3_to_f32,
     fp8pa_debug_lds_tr8,
+    fp8pa_debug_mxfp8,
     fp8pa_debug_mfma_fp8,
     fp8pa_debug_nvfp4,
     fp8pa_debug_wave_ops,
@@ -60,6 +62,7 @@ __all__ = [
     "FP8PA_FLAG_PARTIAL_ONLY",
     "FP8PA_KV_E4M3",
     "FP8PA_KV_NVFP4",
+    "FP8PA_KV_MXFP8",
     "FP8PA_LAYOUT_HND",
     "FP8PA_LAYOUT_NHD",
     "FP8PA_SPLIT_BALANCED",
@@ -90,7 +93,9 @@ def _format_code(kv_format):
         return FP8PA_KV_E4M3
     if kv_format in ("nvfp4", FP8PA_KV_NVFP4):
         return FP8PA_KV_NVFP4
-    raise ValueError(f"kv_format must be 'e4m3' or 'nvfp4', not {kv_format!r}")
+    if kv_format in ("mxfp8", FP8PA_KV_MXFP8):
+        return FP8PA_KV_MXFP8
+    raise ValueError(f"kv_format must be 'e4m3', 'nvfp4' or 'mxfp8', not {kv_format!r}")
 
 
 def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=None,
@@ -98,14 +103,15 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
               num_kv_heads=None, block_tokens=None) -> Shape:
     """fp8pa_shape for tensors q [B, q_len, Hq, D] and k_cache [blocks, bt, Hkv, D]
     (kv_layout "NHD") or [blocks, Hkv, bt, D] ("HND"); with kv_format
-    "nvfp4", k_cache is uint8 [blocks, page_bytes] (any row stride) and
-    num_kv_heads / block_tokens give the page geometry."""
+    "nvfp4" or "mxfp8", k_cache is uint8 [blocks, page_bytes] (any row
+    stride) and num_kv_heads / block_tokens give the page geometry."""
     B, q_len, Hq, D = q.shape
     layout = _layout_code(kv_layout)
     fmt = _format_code(kv_format)
-    if fmt == FP8PA_KV_NVFP4:
+    if fmt != FP8PA_KV_E4M3:
         if num_kv_heads is None or block_tokens is None or k_cache.dim() != 2:
-            raise ValueError("nvfp4 pools are [num_blocks, page_bytes]; pass num_kv_heads and block_tokens")
+            raise ValueError("block-scaled pools are [num_blocks, page_bytes]; pass num_kv_heads and "
+                             "block_tokens")
         nb, bt, Hkv, Dk = k_cache.shape[0], int(block_tokens), int(num_kv_heads), D
         page_stride = k_cache.stride(0)
     else:
@@ -138,21 +144,22 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
     head_dim group);
     sinks float32 [Hq] or None.  max_seq_len should be given by callers that
     must not synchronise (it is read from seq_lens otherwise).  kv_format
-    "nvfp4": k_cache / v_cache are uint8 [num_blocks, page_bytes] NVFP4 pools
-    (rows may be strided, e.g. views into interleaved [K page | V page]
-    blocks) and num_kv_heads / block_tokens are required.
+    "nvfp4" or "mxfp8": k_cache / v_cache are uint8 [num_blocks, page_bytes]
+    NVFP4 / MXFP8 pools (rows may be strided, e.g. views into interleaved
+    [K page | V page] blocks) and num_kv_heads / block_tokens are required.
     """
     import torch
 
     if q.dtype != torch.bfloat16:
         raise ValueError("q must be bfloat16")
-    nvfp4 = _format_code(kv_format) == FP8PA_KV_NVFP4
+    nvfp4 = _format_code(kv_format) != FP8PA_KV_E4M3   # a block-scaled (paged-region) format
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
     if nvfp4 and (k_cache.dim() != 2 or k_cache.stride(1) != 1 or v_cache.stride() != k_cache.stride()
                   or v_cache.shape != k_cache.shape):
-        raise ValueError("nvfp4 pools must be equal uint8 [num_blocks, page_bytes] with unit column stride")
+        raise ValueError("block-scaled pools must be equal uint8 [num_blocks, page_bytes] with unit "
+                         "column stride")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -192,8 +199,8 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
     [Hkv] (k_scale [k_groups] or [Hkv, k_groups] with k_groups > 1);
     k_cache, v_cache uint8 or float8_e4m3fn [num_blocks, bt, Hkv, D]
     (kv_layout "NHD") or [num_blocks, Hkv, bt, D] ("HND"), contiguous; with
-    kv_format "nvfp4", uint8 [num_blocks, page_bytes] NVFP4 pools (rows may
-    be strided) and block_tokens required.
+    kv_format "nvfp4" or "mxfp8", uint8 [num_blocks, page_bytes] NVFP4 / MXFP8
+    pools (rows may be strided) and block_tokens required.
     """
     import torch
 
@@ -201,12 +208,12 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
             raise ValueError(f"{name} must be bfloat16 [T, Hkv, D] with contiguous token rows")
     fmt = _format_code(kv_format)
-    nvfp4 = fmt == FP8PA_KV_NVFP4
+    nvfp4 = fmt != FP8PA_KV_E4M3   # a block-scaled (paged-region) format
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise ValueError(f"{name} must be a uint8 or float8_e4m3fn pool")
         if nvfp4 and (t.dim() != 2 or t.stride(1) != 1):
-            raise ValueError(f"{name}: nvfp4 pools are uint8 [num_blocks, page_bytes]")
+            raise ValueError(f"{name}: block-scaled pools are uint8 [num_blocks, page_bytes]")
         if not nvfp4 and not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous E4M3 pool")
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
@@ -217,7 +224,7 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
     layout = _layout_code(kv_layout)
     if nvfp4:
         if block_tokens is None or v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
-            raise ValueError("nvfp4 pools must match each other; pass block_tokens")
+            raise ValueError("block-scaled pools must match each other; pass block_tokens")
         nb, bt, page_stride = k_cache.shape[0], int(block_tokens), k_cache.stride(0)
     else:
         nb, bt, Hkv_c, D_c = _pool_dims(k_cache, layout)

@@ -30,6 +30,7 @@ FP8PA_LAYOUT_NHD = 0
 FP8PA_LAYOUT_HND = 1
 FP8PA_KV_E4M3 = 0
 FP8PA_KV_NVFP4 = 1
+FP8PA_KV_MXFP8 = 2
 
 
 class Fp8paError(RuntimeError):
@@ -135,6 +136,7 @@ _SIGS = {
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
     "fp8pa_debug_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_lds_tr8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+    "fp8pa_debug_mxfp8": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
 }
 
 
@@ -257,6 +259,12 @@ def fp8pa_debug_nvfp4(data, scales, out, n, stream=None) -> None:
     st = lib().fp8pa_debug_nvfp4(_ptr(data), _ptr(scales), _ptr(out), int(n), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_nvfp4")
+
+
+def fp8pa_debug_mxfp8(data, scales, out, n, stream=None) -> None:
+    st = lib().fp8pa_debug_mxfp8(_ptr(data), _ptr(scales), _ptr(out), int(n), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_mxfp8")
 
 
 def fp8pa_debug_lds_tr8(lds_bytes, row_addr, out, stream=None) -> None:

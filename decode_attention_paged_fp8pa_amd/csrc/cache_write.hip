@@ -45,20 +45,22 @@ struct WriteParams {
   int32_t chunks_per_head;  // D / 8
   int32_t token_bytes;      // bytes between token slots of a page: Hkv * D, or D head-major
   int32_t head_bytes;       // bytes between kv heads of a page: D, or bt * D head-major
-  // NVFP4 pages (token_bytes / head_bytes then count data-region bytes):
+  // NVFP4 / MXFP8 pages (token_bytes / head_bytes then count data-region bytes):
   int32_t sc_off;           // byte offset of a page's scale region
   int32_t sc_tok, sc_head;  // scale bytes between token slots / kv heads
-  int64_t fp4_blocks;       // num_tokens * Hkv * D / 16
-  int32_t blocks_per_token; // Hkv * D / 16
-  int32_t blocks_per_head;  // D / 16
+  int64_t fp4_blocks;       // scale blocks to write: num_tokens * Hkv * D / (16 or 32)
+  int32_t blocks_per_token; // Hkv * D / (16 or 32)
+  int32_t blocks_per_head;  // D / (16 or 32)
   int32_t bt_shift, bt_mask;
 };
 
 // x * inv in fp32, kept NaN but saturated to +-448 (the encoding has no
 // infinity; fminf / fmaxf would turn a NaN into a bound).
-__device__ __forceinline__ float scaled(uint32_t bf16_bits, float inv) {
-  const float v = __uint_as_float(bf16_bits << 16) * inv;
+__device__ __forceinline__ float clamp_e4m3(float v) {
   return fabsf(v) > kE4M3Max ? copysignf(kE4M3Max, v) : v;
+}
+__device__ __forceinline__ float scaled(uint32_t bf16_bits, float inv) {
+  return clamp_e4m3(__uint_as_float(bf16_bits << 16) * inv);
 }
 
 // Eight bf16 values (four dwords) -> eight E4M3 codes (two dwords).
@@ -154,6 +156,60 @@ __global__ __launch_bounds__(256) void cache_write_nvfp4_kernel(WriteParams p) {
   }
 }
 
+// MXFP8 writer: one thread per 32-element block of a head's row; blockIdx.y
+// 0 keys, 1 values.  Per block (the OCP MX rule): y = x * (1 / scale); the
+// shared exponent X = floor(log2(max|y|)) - 8 (E4M3's largest exponent),
+// clamped to [-127, 127]; the scale byte X + 127; the codes E4M3(y * 2^-X),
+// nearest with ties to even, saturated to +-448.
+__global__ __launch_bounds__(256) void cache_write_mxfp8_kernel(WriteParams p) {
+  const int kv = blockIdx.y;
+  const uint16_t* src = p.src[kv];
+  uint8_t* cache = p.cache[kv];
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < p.fp4_blocks;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = i / p.blocks_per_token;
+    const int bi = int(i - t * p.blocks_per_token);
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const int h = bi / p.blocks_per_head;
+    const int blk = bi - h * p.blocks_per_head;
+    const float g = __fdiv_rn(1.f, p.scale[kv][p.per_head[kv] ? h : 0]);
+    const u32x4* x = reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 32 * int64_t(bi));
+    float y[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = x[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[8 * q + 2 * j] = __uint_as_float(w[j] << 16) * g;
+        y[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) * g;
+        amax = fmaxf(amax, fmaxf(fabsf(y[8 * q + 2 * j]), fabsf(y[8 * q + 2 * j + 1])));
+      }
+    }
+    // floor(log2(amax)) is amax's unbiased exponent (zero and subnormal
+    // maxima fall below -126 and clamp to -127 with it)
+    const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+    const int X = min(max(e - 8, -127), 127);
+    const float m = ldexpf(1.f, -X);  // an exact power of two
+    uint32_t code[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c = 0;
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(y[4 * j] * m), clamp_e4m3(y[4 * j + 1] * m), c, false);
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(y[4 * j + 2] * m), clamp_e4m3(y[4 * j + 3] * m), c, true);
+      code[j] = c;
+    }
+    uint8_t* page = cache + (slot >> p.bt_shift) * p.page_bytes;
+    const int64_t off = slot & p.bt_mask;
+    u32x4* dst = reinterpret_cast<u32x4*>(page + off * p.token_bytes + int64_t(h) * p.head_bytes + 32 * blk);
+    dst[0] = u32x4{code[0], code[1], code[2], code[3]};
+    dst[1] = u32x4{code[4], code[5], code[6], code[7]};
+    page[p.sc_off + off * p.sc_tok + int64_t(h) * p.sc_head + blk] = uint8_t(X + 127);
+  }
+}
+
 bool aligned_to(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 int log2_exact(int v) {
@@ -181,13 +237,17 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   if (s->key_stride % 8 != 0 || s->value_stride % 8 != 0) return FP8PA_ERR_MISALIGNED;
   if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_layout != FP8PA_LAYOUT_NHD && s->kv_layout != FP8PA_LAYOUT_HND) return FP8PA_ERR_INVALID_ARG;
-  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4 && s->kv_format != FP8PA_KV_MXFP8)
+    return FP8PA_ERR_INVALID_ARG;
   const bool nv = s->kv_format == FP8PA_KV_NVFP4;
-  if (nv && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
+  const bool mx = s->kv_format == FP8PA_KV_MXFP8;
+  if ((nv || mx) && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_page_stride < 0) return FP8PA_ERR_INVALID_ARG;
   const int64_t page_stride =
       kv_page_stride_of(s->kv_page_stride, s->kv_format, s->block_tokens, s->num_kv_heads, s->head_dim);
   if (page_stride == 0) return FP8PA_ERR_INVALID_ARG;
+  // block-scaled pages take 8- and 16-byte stores from each page's start
+  if ((nv || mx) && page_stride % 16 != 0) return FP8PA_ERR_MISALIGNED;
   const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
   if ((s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg) ||
       (s->v_scale_count != 1 && s->v_scale_count != s->num_kv_heads))
@@ -225,24 +285,28 @@ extern "C" fp8pa_status fp8pa_cache_write(const fp8pa_write_shape* s, const void
   p.chunks_per_token = int32_t(cpt);
   p.chunks_per_head = s->head_dim / 8;
   const bool hnd = s->kv_layout == FP8PA_LAYOUT_HND;
-  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes
-  const int32_t erow = nv ? s->head_dim / 2 : s->head_dim;
+  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes; and
+  // the scale region's rows (NVFP4: D / 16 bytes, MXFP8: D / 32)
+  const int32_t erow = kv_data_row(s->kv_format, s->head_dim);
+  const int32_t srow = kv_scale_row(s->kv_format, s->head_dim);
   p.token_bytes = hnd ? erow : s->num_kv_heads * erow;
   p.head_bytes = hnd ? s->block_tokens * erow : erow;
-  p.sc_off = s->num_kv_heads * s->block_tokens * (s->head_dim / 2);
-  p.sc_tok = hnd ? s->head_dim / 16 : s->num_kv_heads * (s->head_dim / 16);
-  p.sc_head = hnd ? s->block_tokens * (s->head_dim / 16) : s->head_dim / 16;
-  p.blocks_per_head = s->head_dim / 16;
+  p.sc_off = s->num_kv_heads * s->block_tokens * erow;
+  p.sc_tok = hnd ? srow : s->num_kv_heads * srow;
+  p.sc_head = hnd ? s->block_tokens * srow : srow;
+  p.blocks_per_head = mx ? s->head_dim / 32 : s->head_dim / 16;
   p.blocks_per_token = s->num_kv_heads * p.blocks_per_head;
   p.fp4_blocks = s->num_tokens * p.blocks_per_token;
   p.bt_shift = bt_shift;
   p.bt_mask = s->block_tokens - 1;
 
-  const int64_t work = nv ? p.fp4_blocks : p.chunks;
+  const int64_t work = (nv || mx) ? p.fp4_blocks : p.chunks;
   const int64_t blocks = (work + 255) / 256;
   const dim3 grid(unsigned(blocks < 4096 ? blocks : 4096), 2), block(256);
   if (nv)
     cache_write_nvfp4_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
+  else if (mx)
+    cache_write_mxfp8_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
   else
     cache_write_kernel<<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(p);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;

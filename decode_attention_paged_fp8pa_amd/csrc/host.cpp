@@ -43,8 +43,9 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     return FP8PA_ERR_INVALID_ARG;
   if (!k_groups_ok(s->k_groups, s->head_dim)) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_layout != FP8PA_LAYOUT_NHD && s->kv_layout != FP8PA_LAYOUT_HND) return FP8PA_ERR_INVALID_ARG;
-  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4) return FP8PA_ERR_INVALID_ARG;
-  if (s->kv_format == FP8PA_KV_NVFP4 && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format != FP8PA_KV_E4M3 && s->kv_format != FP8PA_KV_NVFP4 && s->kv_format != FP8PA_KV_MXFP8)
+    return FP8PA_ERR_INVALID_ARG;
+  if (s->kv_format != FP8PA_KV_E4M3 && s->k_groups > 1) return FP8PA_ERR_INVALID_ARG;
   if (s->kv_page_stride < 0) return FP8PA_ERR_INVALID_ARG;
   const int32_t kg = s->k_groups > 1 ? s->k_groups : 1;
   if (s->k_scale_count != kg && s->k_scale_count != s->num_kv_heads * kg)
@@ -72,6 +73,8 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   p.fmt = s->kv_format;
   p.page_stride = kv_page_stride_of(s->kv_page_stride, p.fmt, p.bt, p.Hkv, p.D);
   if (p.page_stride == 0) return FP8PA_ERR_INVALID_ARG;
+  // block-scaled pages are read with 16-byte loads from each page's start
+  if (p.fmt != FP8PA_KV_E4M3 && p.page_stride % 16 != 0) return FP8PA_ERR_MISALIGNED;
   if (p.page_stride > (int64_t(1) << 30)) return FP8PA_ERR_UNSUPPORTED;
   const int64_t rows64 = int64_t(p.G) * p.q_len;
   if (rows64 > (int64_t(1) << 20)) return FP8PA_ERR_UNSUPPORTED;

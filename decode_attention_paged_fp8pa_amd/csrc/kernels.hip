@@ -1123,6 +1123,22 @@ partial_mfma_kernel(Params p) {
 // i) times a block scale, as bf16: E2M1 times an E4M3 scale has at most 6
 // significant bits, so every step is exact.  (The conversion's own scale
 // operand applies only a power of two, hence the fp32 multiply.)
+// An E8M0 scale byte as the float 2^(s - 127) (0xFF: NaN; 0: 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 0xffu ? 0x7fc00000u : s == 0u ? 0x00400000u : s << 23);
+}
+
+// Eight E4M3 codes (two dwords, code 4i + b in byte b of dword i) times a
+// power of two, as bf16: E4M3 has 4 significant bits, so the product is
+// exact (the conversion applies the power of two itself).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1, float sc) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
   const f32x2 e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc,
                       __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * sc,
@@ -1151,17 +1167,21 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
 //   V: lane (n, qd) holds dims [S n, S n + S) (S = D/16, inside one block) of
 //     the 8 tokens kap(qd, j): S/2 data bytes and one scale byte each.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int FMT, int NT>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
 __attribute__((amdgpu_waves_per_eu(2, 8))) void
 partial_mfma_nvfp4_kernel(Params p) {
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(FMT == FP8PA_KV_NVFP4 || FMT == FP8PA_KV_MXFP8, "block-scaled format");
+  constexpr bool MX = FMT == FP8PA_KV_MXFP8;
   constexpr int S = D / 16;        // V dims per lane
   constexpr int KD = D / 4;        // K dims per lane per token
   constexpr int KSTEPS = D / 32;   // QK k-steps of 32 dims (8 per lane)
-  constexpr int KDB = KD / 2;      // K data bytes per lane per token
-  constexpr int KSB = KD / 16;     // K scale bytes per lane per token
-  constexpr int VDB = S / 2;       // V data bytes per lane per token
+  constexpr int KDB = MX ? KD : KD / 2;   // K data bytes per lane per token
+  constexpr int KSB = MX ? 1 : KD / 16;   // K scale bytes per lane per token (one MX block)
+  constexpr int VDB = MX ? S : S / 2;     // V data bytes per lane per token
+  constexpr int VDW = VDB >= 4 ? VDB / 4 : 1;
+  constexpr int BLK = MX ? 32 : 16;       // elements per scale
   constexpr int AUX = NT ? kLoadNT : 0;
 
   const int lane = threadIdx.x & 63;
@@ -1208,12 +1228,12 @@ partial_mfma_nvfp4_kernel(Params p) {
   const uint8_t* vs_g = p.v_cache + (size_t)p.sc_off + (size_t)kvh * (size_t)p.sc_head;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
   const uint32_t kdoff = uint32_t(n * tok + KDB * qd);
-  const uint32_t ksoff = uint32_t(n * stok + KSB * qd);
+  const uint32_t ksoff = uint32_t(n * stok + (KD * qd) / BLK);
   uint32_t vdoff[4], vsoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     vdoff[j] = uint32_t((4 * qd + j) * tok + VDB * n);
-    vsoff[j] = uint32_t((4 * qd + j) * stok + (S * n) / 16);
+    vsoff[j] = uint32_t((4 * qd + j) * stok + (S * n) / BLK);
   }
 
   // Block-table entries of the split in registers, as in the FP8 kernel.
@@ -1239,7 +1259,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   struct TileRegs {
     uint32_t kd[2][KDB / 4];
     uint32_t ks[2];
-    uint32_t vd[8];
+    uint32_t vd[8][VDW];
     uint32_t vs[8];
   };
   auto load_tile = [&](int tt, TileRegs& r, int odd) {
@@ -1262,7 +1282,7 @@ partial_mfma_nvfp4_kernel(Params p) {
       buf_load<KSB, AUX>(rks, ksoff, &r.ks[grp]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        buf_load<VDB, AUX>(rvd, vdoff[j], &r.vd[4 * grp + j]);
+        buf_load<VDB, AUX>(rvd, vdoff[j], r.vd[4 * grp + j]);
         buf_load<1, AUX>(rvs, vsoff[j], &r.vs[4 * grp + j]);
       }
     }
@@ -1280,7 +1300,8 @@ partial_mfma_nvfp4_kernel(Params p) {
       for (int j = 0; j < 8; ++j) {
         const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
         const bool in_span = key >= ulo && key < uhi;
-        r.vd[j] = in_span ? r.vd[j] : 0u;
+#pragma unroll
+        for (int w = 0; w < VDW; ++w) r.vd[j][w] = in_span ? r.vd[j][w] : 0u;
         r.vs[j] = in_span ? r.vs[j] : 0u;
       }
     }
@@ -1289,11 +1310,19 @@ partial_mfma_nvfp4_kernel(Params p) {
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-      for (int i = 0; i < KSB; ++i) kscale[grp][i] = __builtin_amdgcn_cvt_f32_fp8(int(r.ks[grp] >> (8 * i)) & 0xff, 0);
+      for (int i = 0; i < KSB; ++i)
+        kscale[grp][i] = MX ? e8m0_to_f32(r.ks[grp] & 0xff)
+                            : __builtin_amdgcn_cvt_f32_fp8(int(r.ks[grp] >> (8 * i)) & 0xff, 0);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const bf16x8 ka = fp4x8_to_bf16(r.kd[0][c], kscale[0][c / 2]);
-      const bf16x8 kbv = fp4x8_to_bf16(r.kd[1][c], kscale[1][c / 2]);
+      bf16x8 ka, kbv;
+      if constexpr (MX) {
+        ka = e4m3x8_to_bf16(r.kd[0][2 * c], r.kd[0][2 * c + 1], kscale[0][0]);
+        kbv = e4m3x8_to_bf16(r.kd[1][2 * c], r.kd[1][2 * c + 1], kscale[1][0]);
+      } else {
+        ka = fp4x8_to_bf16(r.kd[0][c], kscale[0][c / 2]);
+        kbv = fp4x8_to_bf16(r.kd[1][c], kscale[1][c / 2]);
+      }
       sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sa, 0, 0, 0);
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbv, qb[c], sb, 0, 0, 0);
     }
@@ -1338,13 +1367,24 @@ partial_mfma_nvfp4_kernel(Params p) {
     float vf[8][S];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float sc = __builtin_amdgcn_cvt_f32_fp8(int(r.vs[j]) & 0xff, 0);
       f32x2 e2[4];
-      e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 0) * sc;
-      e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 1) * sc;
-      if constexpr (S == 8) {
-        e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 2) * sc;
-        e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j], 1.0f, 3) * sc;
+      if constexpr (MX) {
+        // E4M3 times a power of two: the conversion applies it exactly
+        const float sc = e8m0_to_f32(r.vs[j] & 0xff);
+        e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, false);
+        e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, true);
+        if constexpr (S == 8) {
+          e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][1], sc, false);
+          e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][1], sc, true);
+        }
+      } else {
+        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(r.vs[j]) & 0xff, 0);
+        e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 0) * sc;
+        e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 1) * sc;
+        if constexpr (S == 8) {
+          e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 2) * sc;
+          e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 3) * sc;
+        }
       }
 #pragma unroll
       for (int b = 0; b < S / 2; ++b) {
@@ -1532,25 +1572,33 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   }
 
   constexpr bool NV = FMT == FP8PA_KV_NVFP4;
+  constexpr bool MX = FMT == FP8PA_KV_MXFP8;
   const int tok = p.tok_stride;
   // a lane's bytes of a token: 16 E4M3 codes, or 8 NVFP4 data bytes and one scale byte
   const size_t lane_off = (size_t)w.g * (size_t)p.head_stride + (NV ? 8 : 16) * c;
   const uint8_t* kbase_g = p.k_cache + lane_off;
   const uint8_t* vbase_g = p.v_cache + lane_off;
-  const size_t sc_lane = (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head + c;
+  // (the lane's block: NVFP4's are its 16 elements, MXFP8's 32 span two lanes)
+  const size_t sc_lane = (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head + (MX ? c / 2 : c);
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
 
   for (int tt = ts; tt < te; ++tt) {
     const int kb = tt * kTileTokens;
     u32x4 kr[R], vr[R];
-    float ksc[R], vsc[R];  // NVFP4 block scales of the lane's block of each token
+    // the block scale bytes of the lane's block of each token, four per word
+    // (decoded where used: fewer live registers than one float per token)
+    uint32_t ksw[(R + 3) / 4], vsw[(R + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (R + 3) / 4; ++i) ksw[i] = vsw[i] = 0u;
+    auto scale_of = [&](const uint32_t* sw, int rho) {
+      const uint32_t b = (sw[rho / 4] >> (8 * (rho % 4))) & 0xffu;
+      return MX ? e8m0_to_f32(b) : __builtin_amdgcn_cvt_f32_fp8(int(b), 0);
+    };
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       const int key = kb + rho * KPI + kk;
       kr[rho] = u32x4{0u, 0u, 0u, 0u};
       vr[rho] = u32x4{0u, 0u, 0u, 0u};
-      ksc[rho] = 0.f;
-      vsc[rho] = 0.f;
       if (key >= ulo && key < uhi) {
         const int page = btab[key >> p.bt_shift];
         const size_t pbase = (size_t)page * (size_t)p.page_bytes;
@@ -1561,11 +1609,16 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
           kr[rho] = u32x4{kd.x, kd.y, 0u, 0u};
           vr[rho] = u32x4{vd.x, vd.y, 0u, 0u};
           const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
-          ksc[rho] = __builtin_amdgcn_cvt_f32_fp8(int(p.k_cache[soff]), 0);
-          vsc[rho] = __builtin_amdgcn_cvt_f32_fp8(int(p.v_cache[soff]), 0);
+          ksw[rho / 4] |= uint32_t(p.k_cache[soff]) << (8 * (rho % 4));
+          vsw[rho / 4] |= uint32_t(p.v_cache[soff]) << (8 * (rho % 4));
         } else {
           kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
           vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
+          if constexpr (MX) {
+            const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
+            ksw[rho / 4] |= uint32_t(p.k_cache[soff]) << (8 * (rho % 4));
+            vsw[rho / 4] |= uint32_t(p.v_cache[soff]) << (8 * (rho % 4));
+          }
         }
       }
     }
@@ -1593,7 +1646,7 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) d = fmaf(kf[j], qf[rr][j], d);
-        if constexpr (NV) d *= ksc[rho];
+        if constexpr (NV || MX) d *= scale_of(ksw, rho);
 #pragma unroll
         for (int s = 1; s < LPK; s <<= 1) d += xor_shfl(d, s);
         x[rho][rr] = (key >= rows[rr].klo && key < rows[rr].khi) ? d : -INFINITY;
@@ -1639,7 +1692,7 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
         lsum[rr] += pp;
         // (NVFP4: the block scale of V joins P; a key outside the span has
         // P = 0 and scale 0)
-        const float pv = NV ? pp * vsc[rho] : pp;
+        const float pv = (NV || MX) ? pp * scale_of(vsw, rho) : pp;
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[rr][j] = fmaf(pv, vf[j], acc[rr][j]);
       }
@@ -1841,6 +1894,21 @@ __global__ void debug_nvfp4_kernel(const uint8_t* data, const uint8_t* scales, f
   for (int j = 0; j < 16; ++j) out[16 * size_t(k) + j] = f[j] * sc;
 }
 
+// MXFP8 block k (32 E4M3 codes and one E8M0 scale) as the bf16 operands the
+// block-scaled MFMA kernel builds from it, widened back to float.
+__global__ void debug_mxfp8_kernel(const uint8_t* data, const uint8_t* scales, float* out, int n) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const float sc = e8m0_to_f32(scales[k]);
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(data + 32 * size_t(k));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 v = e4m3x8_to_bf16(w[2 * q], w[2 * q + 1], sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[32 * size_t(k) + 8 * q + j] = float(v[j]);
+  }
+}
+
 __global__ void debug_wave_ops_kernel(const int32_t* in, int vmax, int32_t* out) {
   const int lane = threadIdx.x & 63;
   const int v = in[lane];
@@ -1907,16 +1975,27 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
   const dim3 grid(pl.grid_wgs), block(64 * pl.hg * pl.ds);
   if (pl.variant == kVariantMfma && pl.fmt == FP8PA_KV_NVFP4) {
     if constexpr (D == 64)
-      partial_mfma_nvfp4_kernel<64, 0><<<grid, block, 0, st>>>(prm);
+      partial_mfma_nvfp4_kernel<64, FP8PA_KV_NVFP4, 0><<<grid, block, 0, st>>>(prm);
     else if constexpr (D == 128) {
       if (pl.nt)
-        partial_mfma_nvfp4_kernel<128, 1><<<grid, block, 0, st>>>(prm);
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_NVFP4, 1><<<grid, block, 0, st>>>(prm);
       else
-        partial_mfma_nvfp4_kernel<128, 0><<<grid, block, 0, st>>>(prm);
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_NVFP4, 0><<<grid, block, 0, st>>>(prm);
+    }
+  } else if (pl.variant == kVariantMfma && pl.fmt == FP8PA_KV_MXFP8) {
+    if constexpr (D == 64)
+      partial_mfma_nvfp4_kernel<64, FP8PA_KV_MXFP8, 0><<<grid, block, 0, st>>>(prm);
+    else if constexpr (D == 128) {
+      if (pl.nt)
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 1><<<grid, block, 0, st>>>(prm);
+      else
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 0><<<grid, block, 0, st>>>(prm);
     }
   } else if (pl.variant != kVariantMfma) {
     if (pl.fmt == FP8PA_KV_NVFP4)
       partial_dot_kernel<D, FP8PA_KV_NVFP4><<<grid, block, 0, st>>>(prm);
+    else if (pl.fmt == FP8PA_KV_MXFP8)
+      partial_dot_kernel<D, FP8PA_KV_MXFP8><<<grid, block, 0, st>>>(prm);
     else
       partial_dot_kernel<D, FP8PA_KV_E4M3><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 64) {
@@ -2038,13 +2117,15 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
       pl.direct ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.off_lse);
   prm.page_bytes = pl.page_stride;
   const bool hnd = shape->kv_layout == FP8PA_LAYOUT_HND;
-  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes
-  const int32_t row = pl.fmt == FP8PA_KV_NVFP4 ? pl.D / 2 : pl.D;
+  // bytes per element row of a head: D codes, or D / 2 NVFP4 data bytes; and
+  // the scale region's rows (NVFP4: D / 16 bytes, MXFP8: D / 32)
+  const int32_t row = kv_data_row(pl.fmt, pl.D);
+  const int32_t srow = kv_scale_row(pl.fmt, pl.D);
   prm.tok_stride = hnd ? row : pl.Hkv * row;
   prm.head_stride = hnd ? pl.bt * row : row;
-  prm.sc_off = pl.Hkv * pl.bt * (pl.D / 2);
-  prm.sc_tok = hnd ? pl.D / 16 : pl.Hkv * (pl.D / 16);
-  prm.sc_head = hnd ? pl.bt * (pl.D / 16) : pl.D / 16;
+  prm.sc_off = pl.Hkv * pl.bt * row;
+  prm.sc_tok = hnd ? srow : pl.Hkv * srow;
+  prm.sc_head = hnd ? pl.bt * srow : srow;
   // a group's tokens, plus with paired head-major heads the second head's
   prm.grp_bytes = (pl.pr == 2 && hnd) ? prm.head_stride + 16 * pl.D : 16 * prm.tok_stride;
   prm.q_len = pl.q_len;
@@ -2143,6 +2224,16 @@ fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 
+fp8pa_status fp8pa_debug_mxfp8(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
+                               void* stream) {
+  if (n < 0 || (n > 0 && (!data || !scales || !out))) return FP8PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(data) % 4 != 0) return FP8PA_ERR_MISALIGNED;
+  if (n == 0) return FP8PA_OK;
+  debug_mxfp8_kernel<<<dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      data, scales, out, n);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
 fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
                                void* stream) {
   if (n < 0 || (n > 0 && (!data || !scales || !out))) return FP8PA_ERR_INVALID_ARG;
@@ -2175,7 +2266,7 @@ fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, 
 }
 
 const char* fp8pa_version(void) {
-  return "fp8pa 0.1.0 (HIP, gfx950; FP8-MFMA and VALU partial kernels, E4M3 and NVFP4 pages, LSE merge)";
+  return "fp8pa 0.1.0 (HIP, gfx950; FP8-MFMA and VALU partial kernels, E4M3, NVFP4 and MXFP8 pages, LSE merge)";
 }
 
 }  // extern "C"

@@ -36,10 +36,17 @@ inline int32_t k_group_shift(int32_t k_groups, int32_t head_dim) {
 
 // Bytes of one page of one pool as the format lays it out (E4M3: bt * Hkv *
 // D; NVFP4: a data region of bt * Hkv * D / 2 bytes, then a scale region of
-// bt * Hkv * D / 16).
+// bt * Hkv * D / 16; MXFP8: bt * Hkv * D data bytes, then bt * Hkv * D / 32).
 inline int64_t kv_page_bytes(int32_t kv_format, int32_t bt, int32_t hkv, int32_t d) {
   const int64_t rows = int64_t(bt) * hkv;
-  return kv_format == FP8PA_KV_NVFP4 ? rows * (d / 2 + d / 16) : rows * d;
+  if (kv_format == FP8PA_KV_NVFP4) return rows * (d / 2 + d / 16);
+  if (kv_format == FP8PA_KV_MXFP8) return rows * (d + d / 32);
+  return rows * d;
+}
+// The bytes of a row's data and scales in a block-scaled format.
+inline int32_t kv_data_row(int32_t kv_format, int32_t d) { return kv_format == FP8PA_KV_NVFP4 ? d / 2 : d; }
+inline int32_t kv_scale_row(int32_t kv_format, int32_t d) {
+  return kv_format == FP8PA_KV_NVFP4 ? d / 16 : kv_format == FP8PA_KV_MXFP8 ? d / 32 : 0;
 }
 
 // The stride between a pool's pages: the caller's, or the dense page size.
@@ -65,7 +72,7 @@ struct Plan {
   int32_t lw;              // LDS-shared tiles: row groups per workgroup (0: off)
   int32_t nb;              // 16-row blocks per wavefront (MFMA kernel; 1 or 2)
   int32_t nt;              // 1: non-temporal K/V loads (each byte read by one wavefront)
-  int32_t fmt;             // FP8PA_KV_E4M3 or FP8PA_KV_NVFP4
+  int32_t fmt;             // FP8PA_KV_E4M3, FP8PA_KV_NVFP4 or FP8PA_KV_MXFP8
   int64_t page_stride;     // bytes between pages of a pool
   int32_t upi;             // workgroups per (sequence, split) item: (Hkv / hg) * row_groups
   int32_t split_mode;      // FP8PA_SPLIT_*

@@ -87,6 +87,12 @@ typedef enum fp8pa_status {
                             rows of D/2 bytes, followed by a scale region of one E4M3 byte per
                             16 elements, rows of D/16 bytes; rows are ordered by kv_layout.
                             A value reads as E2M1(code) * E4M3(block scale) * k_scale (v_scale). */
+#define FP8PA_KV_MXFP8 2 /* MXFP8 (the fish-scales-ops README: 1 x 32 blocks sharing one
+                            power-of-two UE8M0 scale): each page is a data region of E4M3
+                            codes, rows of D bytes, followed by a scale region of one E8M0 byte
+                            per 32 consecutive head_dim elements of a token, rows of D/32 bytes;
+                            rows are ordered by kv_layout as for NVFP4.  A value reads as
+                            E4M3(code) * 2^(s - 127) * k_scale (v_scale); s = 0xFF is NaN. */
 
 /* Host-known description of one decode call. */
 typedef struct fp8pa_shape {
@@ -108,8 +114,8 @@ typedef struct fp8pa_shape {
                                  16: K scale groups along head_dim, D / k_groups >= 32,
                                  group j covering dims [j D / k_groups, (j+1) D / k_groups) */
   int32_t kv_layout;          /* FP8PA_LAYOUT_NHD (0) or FP8PA_LAYOUT_HND (1), both pools */
-  int32_t kv_format;          /* FP8PA_KV_E4M3 (0) or FP8PA_KV_NVFP4 (1; needs k_groups <= 1,
-                                 runs the VALU kernel) */
+  int32_t kv_format;          /* FP8PA_KV_E4M3 (0), FP8PA_KV_NVFP4 (1) or FP8PA_KV_MXFP8 (2);
+                                 the block-scaled formats need k_groups <= 1 */
   int32_t window;             /* <= 0: none; W > 0: the last W positions */
   float sm_scale;             /* softmax scale applied to q.K; finite */
   int32_t num_splits;         /* 0: the library plans; > 0 asks for that many KV
@@ -118,7 +124,9 @@ typedef struct fp8pa_shape {
   int32_t flags;              /* FP8PA_FLAG_* bits, 0 in production */
   int64_t kv_page_stride;     /* bytes between consecutive pages of each pool; 0 = one page's
                                  own size (dense pools).  Larger strides let K and V pages
-                                 interleave ([K page | V page] per block).  A multiple of 16. */
+                                 interleave ([K page | V page] per block).  A multiple of 16;
+                                 NVFP4 and MXFP8 pools whose own page size is not one need it
+                                 (FP8PA_ERR_MISALIGNED otherwise). */
 } fp8pa_shape;
 
 /* How the keys of a sequence are divided among workgroups. */
@@ -266,6 +274,14 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
  * fp32(y * fp32(1 / E4M3(scale byte))), nearest with ties to even, saturated
  * at 6, keeping the sign bit (all zero codes when the scale decodes to 0).
  * NaN inputs are outside the format (their block's bytes are unspecified).
+ *
+ * MXFP8 pools (kv_format = FP8PA_KV_MXFP8): each 32-element block of a head's
+ * row becomes one E8M0 scale byte and 32 E4M3 codes, by the OCP MX rule:
+ * y = fp32(x * fp32(1 / scale_h)); the shared exponent X = floor(log2(max|y|))
+ * - 8 (8 being E4M3's largest exponent), clamped to [-127, 127] (-127 for an
+ * all-zero block); the scale byte X + 127; the codes e4m3(y * 2^-X), nearest
+ * with ties to even and saturated to +-448.  NaN inputs are outside the
+ * format.
  */
 typedef struct fp8pa_write_shape {
   int64_t num_tokens;      /* T >= 0 rows of key, value and slot_mapping */
@@ -280,7 +296,8 @@ typedef struct fp8pa_write_shape {
   int32_t k_groups;        /* as in fp8pa_shape: each key element is encoded against
                               the scale of its head_dim group */
   int32_t kv_layout;       /* FP8PA_LAYOUT_NHD or FP8PA_LAYOUT_HND, both pools */
-  int32_t kv_format;       /* FP8PA_KV_E4M3 or FP8PA_KV_NVFP4 (k_groups <= 1) */
+  int32_t kv_format;       /* FP8PA_KV_E4M3, FP8PA_KV_NVFP4 or FP8PA_KV_MXFP8 (the last two
+                              with k_groups <= 1) */
   int64_t kv_page_stride;  /* as in fp8pa_shape */
 } fp8pa_write_shape;
 
@@ -294,7 +311,7 @@ typedef struct fp8pa_write_shape {
  *   k_scale       float [k_scale_count]; v_scale float [v_scale_count]
  *   k_cache       e4m3 [num_blocks, bt, Hkv, D] (8-byte aligned), or
  *                 [num_blocks, Hkv, bt, D] with kv_layout = FP8PA_LAYOUT_HND, or NVFP4
- *                 pages (see FP8PA_KV_NVFP4); pages kv_page_stride bytes apart when it
+ *                 pages (see FP8PA_KV_NVFP4) or MXFP8 pages; pages kv_page_stride bytes apart when it
  *                 is not 0; v_cache alike
  *
  * Only the slots named are written.  Two tokens with the same slot race

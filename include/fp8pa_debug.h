@@ -40,6 +40,13 @@ fp8pa_status fp8pa_debug_e4m3_to_f32(const uint8_t* codes, float* out, int32_t n
 fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
                                void* stream);
 
+/* out[32 k + j] = element j of MXFP8 block k as the block-scaled MFMA kernel
+ * dequantizes it (E4M3 code times 2^(scale - 127), rounded to bf16, which is
+ * exact), for k < n: data is uint8 [n][32] (4-byte aligned), scales uint8
+ * [n] E8M0, out float [32 n]. */
+fp8pa_status fp8pa_debug_mxfp8(const uint8_t* data, const uint8_t* scales, float* out, int32_t n,
+                               void* stream);
+
 /* c = a x b for one 16x16x32 FP8 MFMA: a is E4M3 [16][32] (row-major, M x K),
  * b is E4M3 [32][16] (K x N), c is float [16][16] row-major.  The kernel
  * loads the operands and stores the result with the lane layout the decode

@@ -21,12 +21,12 @@ def upload(wl, device="cuda", kv_layout="NHD"):
     import torch
 
     def pool(c):
-        if getattr(wl, "kv_format", "e4m3") == "nvfp4":
-            return c  # the layout is in the pool's bytes
+        if getattr(wl, "kv_format", "e4m3") != "e4m3":
+            return c  # block-scaled pools: the layout is in the pool's bytes
         return np.ascontiguousarray(c.transpose(0, 2, 1, 3)) if kv_layout == "HND" else c
 
     t = {
-        "layout": wl.kv_layout if getattr(wl, "kv_format", "e4m3") == "nvfp4" else kv_layout,
+        "layout": wl.kv_layout if getattr(wl, "kv_format", "e4m3") != "e4m3" else kv_layout,
         "q": torch.from_numpy(wl.q_bits.view(np.int16)).to(device).view(torch.bfloat16),
         "k": torch.from_numpy(pool(wl.k_cache)).to(device),
         "v": torch.from_numpy(pool(wl.v_cache)).to(device),

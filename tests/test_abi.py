@@ -165,8 +165,15 @@ BAD = [
     (dict(k_groups=8, k_scale_count=64), _lib.FP8PA_ERR_INVALID_ARG),   # 16 dims per group at D = 128
     (dict(k_groups=4), _lib.FP8PA_ERR_INVALID_ARG),                     # Hkv scales, not Hkv * 4
     (dict(kv_layout=2), _lib.FP8PA_ERR_INVALID_ARG),
-    (dict(kv_format=2), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=3), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_format=1, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),  # no groups with NVFP4
+    (dict(kv_format=2, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),  # nor with MXFP8
+    # block-scaled pages must be 16-byte multiples (head_dim 64, one token and
+    # head per page: 66 MXFP8 / 36 NVFP4 bytes) unless a padded stride is given
+    (dict(kv_format=2, head_dim=64, block_tokens=1, num_kv_heads=1, num_q_heads=1, k_scale_count=1,
+          v_scale_count=1, block_table_stride=8192), _lib.FP8PA_ERR_MISALIGNED),
+    (dict(kv_format=1, head_dim=64, block_tokens=1, num_kv_heads=1, num_q_heads=1, k_scale_count=1,
+          v_scale_count=1, block_table_stride=8192), _lib.FP8PA_ERR_MISALIGNED),
     (dict(kv_format=1, flags=2, block_tokens=8, block_table_stride=1024), _lib.FP8PA_ERR_UNSUPPORTED),  # MFMA needs bt >= 16
     (dict(kv_page_stride=-16), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_page_stride=16 * 8 * 128 - 16), _lib.FP8PA_ERR_INVALID_ARG),  # shorter than a page
@@ -203,6 +210,19 @@ def test_nvfp4_plans():
     # a page stride that interleaves K and V pages (2 x the NVFP4 page of cfg2:
     # 16 tokens x 8 heads x (64 + 8) bytes)
     fp.fp8pa_plan(cfg_shape(2, kv_format=fp.FP8PA_KV_NVFP4, kv_page_stride=2 * 16 * 8 * 72), 256)
+
+
+def test_mxfp8_plans():
+    # the same kernels as NVFP4: the bf16-MFMA kernel at head_dim 64 and 128,
+    # the VALU kernel at 256; a padded stride makes an odd page size legal
+    for k in (2, 3):
+        p = fp.fp8pa_plan(cfg_shape(k, kv_format=fp.FP8PA_KV_MXFP8), 256)
+        assert (p["variant"], p["rows_per_group"], p["heads_per_wave"], p["waves_per_head"]) == (1, 16, 1, 1)
+    p = fp.fp8pa_plan(cfg_shape(4, kv_format=fp.FP8PA_KV_MXFP8), 256)
+    assert p["variant"] == 0 and p["rows_per_group"] == 4
+    fp.fp8pa_plan(cfg_shape(2, kv_format=fp.FP8PA_KV_MXFP8, kv_page_stride=2 * 16 * 8 * 132), 256)
+    fp.fp8pa_plan(cfg_shape(3, kv_format=fp.FP8PA_KV_MXFP8, block_tokens=1, block_table_stride=32768,
+                            kv_page_stride=8 * 66 + 16 - (8 * 66) % 16), 256)
 
 
 def test_row_blocks_for_many_rows():
@@ -405,6 +425,10 @@ WRITE_BAD = [
     (dict(kv_layout=3), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_format=5), _lib.FP8PA_ERR_INVALID_ARG),
     (dict(kv_format=1, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=2, k_groups=2, k_scale_count=16), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=2, kv_page_stride=16 * 8 * 132 - 16), _lib.FP8PA_ERR_INVALID_ARG),
+    (dict(kv_format=2, head_dim=64, block_tokens=1, num_kv_heads=1, k_scale_count=1, v_scale_count=1,
+          key_stride=64, value_stride=64), _lib.FP8PA_ERR_MISALIGNED),
     (dict(kv_format=1, kv_page_stride=16 * 8 * 72 - 16), _lib.FP8PA_ERR_INVALID_ARG),
 ]
 
