@@ -3,7 +3,7 @@ against the oracle.
 
 Decode outputs are compared element by element with the float64 oracle at
 small sizes (token- and head-major pages, padded and interleaved page
-strides, windows, sinks, several splits) and on sampled rows of a
+strides, windows, sinks, several splits) and on every row of a
 full-size ragged GQA batch; the writer's bytes are compared bit for bit.
 """
 
@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_harness import compare, run, sample_rows, to_host, upload
+from tests.gpu_harness import compare, run, to_host, upload
 from workloads import CONFIGS, make_mxfp8_workload
 
 torch = pytest.importorskip("torch")
@@ -101,18 +101,15 @@ def test_mxfp8_interleaved_k_and_v_pages():
 def test_mxfp8_parity_full_size_ragged_gqa():
     """The ragged GQA batch (16 sequences of 1024-8192 tokens, Hq 32, Hkv 8,
     D 128) with MXFP8 pages, in the launch configuration the bench times;
-    sampled rows against the oracle."""
+    every row against the oracle."""
     c = CONFIGS[2]
     wl = make_mxfp8_workload(B=c["B"], q_len=c["q_len"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], bt=c["bt"],
                              seq_lens=("uniform", c["seq"][1], c["seq"][2]), seed=1003, pool=c["pool"],
                              scale=c["scale"], sm_scale=c["sm_scale"], kv_layout="HND")
     t = upload(wl)
     out, lse = to_host(*run(wl, t))
-    rows = sample_rows(wl, 48, seed=5)
-    ro, rl = oracle.decode(**wl.oracle_kwargs(), rows=rows)
-    got_o = np.stack([out[b, i, h] for b, i, h in rows])
-    got_l = np.array([lse[b, i, h] for b, i, h in rows])
-    compare(got_o, got_l, ro, rl, label="mxfp8 full-size ragged GQA")
+    ro, rl = oracle.decode(**wl.oracle_kwargs())   # every row: seconds on the host
+    compare(out, lse, ro, rl, label="mxfp8 full-size ragged GQA")
     # the same bits on every call (no race, no timing-dependent read)
     ref = tuple(x.clone() for x in run(wl, t))
     for i in range(6):
