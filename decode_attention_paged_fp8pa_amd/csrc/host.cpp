@@ -163,10 +163,11 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // sizes one chunk for the batch's real tile count (BALANCED); longer
   // batches, or a caller's split count, get splits of a fixed size.
   // Wavefronts of the partial kernel one compute unit holds at once: the
-  // MFMA kernel's registers allow 4 per SIMD at D = 64 and 2 otherwise
+  // MFMA kernel's registers allow 4 per SIMD at D = 64 and in the LDS-shared
+  // kernels of 4 or 8 row groups (built for 128 registers), 2 otherwise
   // (head_dim 256 is split over two wavefronts); the dot kernel's 2.
   const int64_t waves_per_cu =
-      (fp8_mfma && p.D == 64 && p.pr == 1 && p.nb == 1) ? 16 : 8;
+      ((fp8_mfma && p.D == 64 && p.pr == 1 && p.nb == 1) || p.lw >= 4) ? 16 : 8;
   const int64_t target_waves = int64_t(cu_count) * waves_per_cu;
   int64_t target_items = target_waves / waves_per_item;
   if (target_items < 1) target_items = 1;
