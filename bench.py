@@ -23,7 +23,7 @@ is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
 timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
 fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
-Four widenings are timed after the decode: the headline workload with K
+Five widenings are timed after the decode: the headline workload with K
 scales in four head_dim groups ("k_groups_variant"), the headline and the
 windowed head_dim-64 workloads with head-major pages ("hnd_variant"), the
 headline batch with NVFP4 pages ("nvfp4_variant", bytes = D/2 + D/16 per
