@@ -330,6 +330,13 @@ def test_debug_entry_points_check_arguments():
     assert L.fp8pa_debug_lds_tr8(0x1000, None, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
     assert L.fp8pa_debug_lds_tr8(0x1008, 0x3000, 0x2000, None) == _lib.FP8PA_ERR_MISALIGNED
     assert L.fp8pa_debug_wave_ops(0x1000, -1, 0x2000, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_nvfp4(None, None, None, -1, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_nvfp4(None, None, None, 0, None) == _lib.FP8PA_OK
+    assert L.fp8pa_debug_nvfp4(0x1004, 0x2000, 0x3000, 1, None) == _lib.FP8PA_ERR_MISALIGNED
+    assert L.fp8pa_debug_mxfp8(None, None, None, -1, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_mxfp8(0x1000, None, 0x3000, 1, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert L.fp8pa_debug_mxfp8(None, None, None, 0, None) == _lib.FP8PA_OK
+    assert L.fp8pa_debug_mxfp8(0x1002, 0x2000, 0x3000, 1, None) == _lib.FP8PA_ERR_MISALIGNED
 
 
 def _balanced_items(plan, seq_lens, q_len, window):
