@@ -49,6 +49,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "cache_write",
+    "check_decode_args",
     "fp8pa_cache_write",
     "decode",
     "shape_for",
@@ -130,6 +131,105 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
                       num_splits=int(num_splits), flags=int(flags))
 
 
+def _block_tokens_of(k_cache, kv_layout, kv_format, block_tokens):
+    if _format_code(kv_format) != FP8PA_KV_E4M3:
+        return int(block_tokens)
+    return _pool_dims(k_cache, _layout_code(kv_layout))[1]
+
+
+def _check_table_width(block_table, max_seq_len, k_cache, kv_layout, kv_format, block_tokens):
+    """The table must hold a page for every position below max_seq_len."""
+    bt = _block_tokens_of(k_cache, kv_layout, kv_format, block_tokens)
+    need = -(-int(max_seq_len) // bt)
+    if block_table.shape[1] < need:
+        raise ValueError(f"block_table has {block_table.shape[1]} columns; max_seq_len "
+                         f"{max_seq_len} over {bt}-token pages needs {need}")
+
+
+def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=None, *,
+                      out=None, lse=None, workspace=None, k_groups=1, kv_layout="NHD",
+                      kv_format="e4m3", num_kv_heads=None, block_tokens=None):
+    """Raises ValueError unless the tensors of a decode call have the dtypes,
+    shapes, strides and device the kernels index them with.
+
+    The C ABI sees only pointers and the shape descriptor, so a tensor
+    smaller than the shape says (a caller's out, lse or sinks, a short
+    block_table or seq_lens) would be read or written past its end on the
+    device; every such mismatch is caught here instead.  Pure host checks:
+    no device value is read.
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise ValueError("q must be bfloat16 [B, q_len, Hq, D]")
+    B, q_len, Hq, D = q.shape
+    fmt = _format_code(kv_format)
+    layout = _layout_code(kv_layout)
+    blockscaled = fmt != FP8PA_KV_E4M3
+    dev = q.device
+    named = [("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+             ("seq_lens", seq_lens), ("k_scale", k_scale), ("v_scale", v_scale),
+             ("sinks", sinks), ("out", out), ("lse", lse), ("workspace", workspace)]
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}: every tensor must be on q's device")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if blockscaled:
+        if (k_cache.dim() != 2 or k_cache.stride(1) != 1 or v_cache.stride() != k_cache.stride()
+                or v_cache.shape != k_cache.shape):
+            raise ValueError("block-scaled pools must be equal uint8 [num_blocks, page_bytes] with unit "
+                             "column stride")
+        if num_kv_heads is None or block_tokens is None:
+            raise ValueError("block-scaled pools need num_kv_heads and block_tokens")
+        per_row = D // 2 + D // 16 if fmt == FP8PA_KV_NVFP4 else D + D // 32
+        page = int(block_tokens) * int(num_kv_heads) * per_row
+        if k_cache.shape[1] < page:
+            raise ValueError(f"block-scaled pages hold {k_cache.shape[1]} bytes; the geometry needs {page}")
+        Hkv = int(num_kv_heads)
+    else:
+        if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise ValueError("k_cache and v_cache must be equal 4-D E4M3 pools")
+        _, _, Hkv, Dk = _pool_dims(k_cache, layout)
+        if Dk != D:
+            raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"Hq = {Hq} must be a multiple of Hkv = {Hkv}")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit column stride")
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for a batch of {B}")
+    if seq_lens.dim() != 1 or seq_lens.numel() != B:
+        raise ValueError(f"seq_lens must be int32 [B] = [{B}], not {tuple(seq_lens.shape)}")
+    kg = int(k_groups) if int(k_groups) > 1 else 1
+    for name, t, counts in (("k_scale", k_scale, (kg, Hkv * kg)), ("v_scale", v_scale, (1, Hkv))):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        if t.numel() not in counts:
+            raise ValueError(f"{name} must hold {' or '.join(map(str, counts))} values, not {t.numel()}")
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or sinks.numel() != Hq:
+            raise ValueError(f"sinks must be float32 [Hq] = [{Hq}]")
+    dense = [("q", q), ("seq_lens", seq_lens), ("k_scale", k_scale), ("v_scale", v_scale),
+             ("sinks", sinks)]
+    if not blockscaled:
+        dense += [("k_cache", k_cache), ("v_cache", v_cache)]
+    for name, t in dense:
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is not None:
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, q_len, Hq, D) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {(B, q_len, Hq, D)}")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, q_len, Hq) or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, q_len, Hq)}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=None, *,
            window=0, sm_scale=None, max_seq_len=None, num_splits=0, flags=0, out=None, lse=None,
            workspace=None, stream=None, k_groups=1, kv_layout="NHD", kv_format="e4m3",
@@ -150,28 +250,15 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks=N
     """
     import torch
 
-    if q.dtype != torch.bfloat16:
-        raise ValueError("q must be bfloat16")
-    nvfp4 = _format_code(kv_format) != FP8PA_KV_E4M3   # a block-scaled (paged-region) format
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-            raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
-    if nvfp4 and (k_cache.dim() != 2 or k_cache.stride(1) != 1 or v_cache.stride() != k_cache.stride()
-                  or v_cache.shape != k_cache.shape):
-        raise ValueError("block-scaled pools must be equal uint8 [num_blocks, page_bytes] with unit "
-                         "column stride")
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("block_table and seq_lens must be int32")
-    if block_table.dim() != 2 or block_table.stride(1) != 1:
-        raise ValueError("block_table must be 2-D with unit column stride")
-    dense = (("q", q), ("seq_lens", seq_lens), ("k_scale", k_scale), ("v_scale", v_scale))
-    if not nvfp4:
-        dense += (("k_cache", k_cache), ("v_cache", v_cache))
-    for name, t in dense:
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    if q.device.type != "cuda":
+        raise ValueError("decode runs on the GPU: q must be a cuda tensor")
+    check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks,
+                      out=out, lse=lse, workspace=workspace, k_groups=k_groups,
+                      kv_layout=kv_layout, kv_format=kv_format, num_kv_heads=num_kv_heads,
+                      block_tokens=block_tokens)
     if max_seq_len is None:
         max_seq_len = max(1, int(seq_lens.max().item()))   # a batch of empty slots still plans
+    _check_table_width(block_table, max_seq_len, k_cache, kv_layout, kv_format, block_tokens)
     shape = shape_for(q, k_cache, block_table, k_scale, v_scale, window=window, sm_scale=sm_scale,
                       max_seq_len=max_seq_len, num_splits=num_splits, flags=flags,
                       k_groups=k_groups, kv_layout=kv_layout, kv_format=kv_format,
