@@ -161,3 +161,27 @@ def test_writer_slots_beyond_4_gib():
     assert int(kc[:top].sum().item()) == 0
     del kc, vc
     torch.cuda.empty_cache()
+
+
+def test_writer_golden_reciprocal_order():
+    """The hand-worked cases of tests/golden/writer_reciprocal_order.json on
+    the GPU writer: each element of head h is the golden x under the golden
+    scale of head h, so every code must be the golden one."""
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "writer_reciprocal_order.json")) as f:
+        cases = json.load(f)["cases"]
+    Hkv, D, bt = len(cases), 64, 16
+    bits = np.array([int(c["x_bf16_bits"], 16) for c in cases], dtype=np.uint16)
+    scales = np.array([int(c["scale_f32_bits"], 16) for c in cases], dtype=np.uint32).view(np.float32)
+    want = np.array([int(c["expected_code"], 16) for c in cases], dtype=np.uint8)
+    key_bits = np.repeat(bits[None, :, None], D, axis=2)  # [1, Hkv, D]
+    key = torch.from_numpy(key_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    kc = torch.zeros((1, bt, Hkv, D), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    sc = torch.from_numpy(scales.copy()).cuda()
+    fp.cache_write(key, key, torch.tensor([5], dtype=torch.int64).cuda(), sc, sc, kc, vc)
+    torch.cuda.synchronize()
+    for got in (kc.cpu().numpy(), vc.cpu().numpy()):
+        assert np.array_equal(got[0, 5], np.repeat(want[:, None], D, axis=1))

@@ -140,3 +140,58 @@ def test_cache_write_hnd_is_the_transposed_nhd_write():
 
 def _bits16(x):
     return _bf16_bits(x)
+
+
+def _golden_reciprocal_cases():
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "writer_reciprocal_order.json")
+    with open(path) as f:
+        return json.load(f)["cases"]
+
+
+def _f32(bits_hex):
+    return np.array([int(bits_hex, 16)], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_golden_reciprocal_derivation_is_consistent():
+    """The hand-worked numbers of the golden cases check out in exact
+    rational arithmetic: the stored reciprocal is the fp32 number nearest
+    1/s, and the product rounds to the stated fp32 midpoint."""
+    from fractions import Fraction
+
+    for c in _golden_reciprocal_cases():
+        s = Fraction(float(_f32(c["scale_f32_bits"])))
+        r = Fraction(float(_f32(c["reciprocal_f32_bits"])))
+        e = r.numerator.bit_length() - r.denominator.bit_length()
+        e = e if Fraction(2) ** e <= r else e - 1
+        ulp = Fraction(2) ** (e - 23)
+        assert abs(1 / s - r) <= ulp / 2
+        x = Fraction(float(np.array([int(c["x_bf16_bits"], 16) << 16], dtype=np.uint32).view(np.float32)[0]))
+        prod = x * r
+        p32 = Fraction(float(c["product_f32"].split()[0]))
+        pe = p32.numerator.bit_length() - p32.denominator.bit_length()
+        pe = pe if Fraction(2) ** pe <= p32 else pe - 1
+        assert abs(prod - p32) < Fraction(2) ** (pe - 23) / 2  # strictly nearer than the next fp32
+        # the quotient itself lies strictly above the midpoint: the other code
+        assert x / s > p32
+
+
+def test_cache_write_uses_the_fp32_reciprocal_then_an_fp32_product():
+    """Pinned to the golden cases: a plausible variant of the writer (exact
+    division, a float64 reciprocal, an fp32 division, or encoding the
+    unrounded product) writes the neighbouring code instead."""
+    cases = _golden_reciprocal_cases()
+    hkv = len(cases)
+    key = np.zeros((1, hkv, 1), dtype=np.uint16)
+    ks = np.zeros(hkv, dtype=np.float32)
+    want = []
+    for h, c in enumerate(cases):
+        key[0, h, 0] = int(c["x_bf16_bits"], 16)
+        ks[h] = _f32(c["scale_f32_bits"])
+        want.append(int(c["expected_code"], 16))
+    kc = np.zeros((1, 1, hkv, 1), dtype=np.uint8)
+    k_out, v_out = oracle.cache_write(key, key, np.array([0]), ks, ks, kc, kc.copy())
+    assert k_out[0, 0, :, 0].tolist() == want
+    assert v_out[0, 0, :, 0].tolist() == want
