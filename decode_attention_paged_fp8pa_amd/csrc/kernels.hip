@@ -26,11 +26,11 @@
 //    per-row power-of-two scale, so the scores keep ~2^-8 relative
 //    precision while the K codes go straight from HBM into the MFMA.
 //    The fp32 score accumulator already holds, per lane, the 8 keys that the
-//    PV MFMA's B operand needs, so P = 2^(s - m + 8) is packed in place as
-//    two E4M3 parts, hi + lo, both fed to the PV MFMA (the +8 keeps P in
-//    E4M3's normal range; it cancels in O / l).
-//    V is transposed to keys-along-K with v_perm byte shuffles in registers
-//    (no LDS).
+//    PV MFMA's B operand needs, so P = 2^(s - m) is rounded to bf16 in place
+//    (8 significant bits at any magnitude, so no weight underflows) and PV
+//    runs on the bf16 16x16x32 MFMA; V is transposed to keys-along-K with
+//    v_perm byte shuffles in registers (no LDS) and widened to bf16, which
+//    holds every E4M3 value exactly.
 //  * VALU kernel ("dot"): 16 bytes per lane, D/16 lanes per key, E4M3
 //    decoded with v_cvt_pk_f32_fp8, fp32 FMAs and cross-lane reductions;
 //    used for kv heads with one or two query rows and pages under 16 tokens.
@@ -64,11 +64,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kOob = 0x80000000u;
 // Word 3 of a raw (untyped, unswizzled) buffer descriptor on gfx9 parts.
 constexpr int kRsrcWord3 = 0x00020000;
-// P is stored as E4M3 of p * 2^kPShift with p = 2^(s - m) <= 2^kLazy, where
-// the reference max m trails the true max by at most kLazy (log2 units):
-// 2^(kLazy + kPShift) = 256 stays below E4M3's 448.
-constexpr float kPShift = 4.0f;
-constexpr float kLazy = 4.0f;
+// The online softmax keeps a reference max m that trails the true max by at
+// most kLazy (log2 units): a tile moves m only when it exceeds m by more
+// than that, so P = 2^(s - m) <= 2^kLazy, and most tiles skip rescaling O.
+constexpr float kLazy = 8.0f;
 
 struct Params {
   const uint16_t* q;
@@ -208,6 +207,17 @@ __device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t 
   out[1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
   out[2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
   out[3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+}
+
+// Eight E4M3 codes (two dwords, code 4i + b in byte b of dword i) times a
+// power of two, as bf16: E4M3 has 4 significant bits, so the product is
+// exact (the conversion applies the power of two itself).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1, float sc) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
@@ -592,7 +602,7 @@ partial_mfma_kernel(Params p) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     m[b] = sink2[b];
-    lsum[b] = (qd == 0 && sink2[b] > -INFINITY) ? exp2_fast(kPShift) : 0.f;
+    lsum[b] = (qd == 0 && sink2[b] > -INFINITY) ? 1.f : 0.f;
 #pragma unroll
     for (int e = 0; e < S; ++e) O[b][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -723,6 +733,14 @@ partial_mfma_kernel(Params p) {
       for (int x4 = 0; x4 < 4; ++x4) vt[4 * wd + x4] = as_long(lo4[x4], hi4[x4]);
     }
     }
+    // With two row blocks the V^T operands are widened to bf16 once and
+    // serve both blocks.
+    bf16x8 vtb[NB > 1 ? S : 1];
+    if constexpr (NB > 1) {
+#pragma unroll
+      for (int e = 0; e < S; ++e)
+        vtb[e] = e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -812,7 +830,7 @@ partial_mfma_kernel(Params p) {
       const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
       // Lazy reference max: move m only when this tile exceeds it by more
       // than kLazy (log2 units), so most tiles skip the O rescale; P stays
-      // <= 2^(kLazy + kPShift).
+      // <= 2^kLazy.
       const bool bump = mx > m[b] + kLazy;
       if (__builtin_amdgcn_ballot_w64(bump) != 0) {
         const float mnew = bump ? mx : m[b];
@@ -822,35 +840,26 @@ partial_mfma_kernel(Params p) {
         for (int e = 0; e < S; ++e) O[b][e] *= alpha;
         m[b] = mnew;
       }
-      const float noff = kPShift - (m[b] == -INFINITY ? 0.f : m[b]);
+      const float noff = m[b] == -INFINITY ? 0.f : -m[b];
       float pj[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
       lsum[b] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
 
-      // P = P_hi + P_lo, both E4M3: the pair keeps ~2^-8 relative precision,
-      // which short, peaked rows need (one E4M3 P alone errs by up to 2^-4).
-      uint32_t p0 = 0, p1 = 0, q0 = 0, q1 = 0;
-      p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0], pj[1], p0, false);
-      p0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2], pj[3], p0, true);
-      p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4], pj[5], p1, false);
-      p1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6], pj[7], p1, true);
-      {
-        const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, false);
-        const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(p0, true);
-        const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, false);
-        const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(p1, true);
-        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[0] - d0.x, pj[1] - d0.y, q0, false);
-        q0 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[2] - d1.x, pj[3] - d1.y, q0, true);
-        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[4] - d2.x, pj[5] - d2.y, q1, false);
-        q1 = __builtin_amdgcn_cvt_pk_fp8_f32(pj[6] - d3.x, pj[7] - d3.y, q1, true);
+      // P in bf16 (round to nearest even): 2^-9 relative error per weight at
+      // any magnitude, so a weight far below the row's max still reaches O
+      // (its mass is in lsum as well).
+      bf16x8 P;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
+        P[j] = h.x;
+        P[j + 1] = h.y;
       }
-      const long P = as_long(p0, p1);
-      const long Plo = as_long(q0, q1);
 #pragma unroll
       for (int e = 0; e < S; ++e) {
-        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt[e], P, O[b][e], 0, 0, 0);
-        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vt[e], Plo, O[b][e], 0, 0, 0);
+        const bf16x8 vb = NB > 1 ? vtb[e] : e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
+        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, P, O[b][e], 0, 0, 0);
       }
       // keep the scheduler from interleaving blocks (their temporaries would
       // all be live at once)
@@ -1065,7 +1074,7 @@ partial_mfma_kernel(Params p) {
     if (!row[b].valid) continue;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : vs / l;
-    const float lse = empty ? -INFINITY : (m[b] + log2_fast(l) - kPShift) * kLn2;
+    const float lse = empty ? -INFINITY : (m[b] + log2_fast(l)) * kLn2;
     if (TRV && p.direct) {
       uint16_t* orow = p.out + row[b].out_row * DH + d0 + 4 * qd;
 #pragma unroll
@@ -1128,16 +1137,6 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s == 0xffu ? 0x7fc00000u : s == 0u ? 0x00400000u : s << 23);
 }
 
-// Eight E4M3 codes (two dwords, code 4i + b in byte b of dword i) times a
-// power of two, as bf16: E4M3 has 4 significant bits, so the product is
-// exact (the conversion applies the power of two itself).
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1, float sc) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
-  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
 
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
   const f32x2 e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc,

@@ -194,7 +194,59 @@ SMALL = {
     # held to well beyond E4M3's 4 bits
     "kg4_q8_few_keys_lw2": dict(B=2, q_len=8, Hq=32, Hkv=8, D=128, bt=32, seq_lens=[8, 520],
                                 k_groups=4, scale=("per_head", 0.02, 0.1)),
+    # Softmax weights far below the row's maximum must still reach the output
+    # (their mass is in the denominator either way).  Values have mean 2, so
+    # a kernel that drops small weights from P.V misses ~0.1 * 2 of the output.
+    # One key per (sequence, kv head) scores ~11 nats above ~4000 others:
+    "peaked_row_mean_v": dict(B=2, q_len=1, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[4000, 2500]),
+    # the same with head_dim 64 (two kv heads per wavefront) and a window
+    "peaked_row_mean_v_d64": dict(B=2, q_len=1, Hq=16, Hkv=4, D=64, bt=16, seq_lens=[3000, 1800],
+                                  window=2500),
+    # sinks of +8 and +12 dominate every row: with one split they enter the
+    # partial kernel's running maximum, so every key's weight is ~e^-12
+    "big_positive_sinks_mean_v": dict(B=2, q_len=1, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[3000, 700],
+                                      sinks=True),
+    "big_positive_sinks_mtp": dict(B=2, q_len=4, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[2000, 300],
+                                   sinks=True, window=1000),
 }
+
+
+def _shift_values(wl, mean):
+    """Adds `mean` to every attended value (the E4M3 codes of x / v_scale are
+    re-encoded from x + mean); NaN poison bytes stay as they are."""
+    from workloads.gen import _e4m3_encode
+
+    v = wl.v_cache
+    vs = wl.v_scale.reshape(-1)
+    scale = vs[None, None, :, None] if vs.size > 1 else vs.reshape(1, 1, 1, 1)
+    x = oracle.E4M3_TABLE[v] * scale
+    live = ~np.isnan(x)
+    y = np.where(live, (x + mean) / scale, 0.0)
+    wl.v_cache[...] = np.where(live, _e4m3_encode(y.astype(np.float32)), v)
+
+
+def _peak_one_key(wl, rng, nats=11.0):
+    """Gives every query head of a kv group the same query and, in each
+    sequence, sets one attended key of that group to a multiple of it, so its
+    score stands ~`nats` above the N(0, 1) scores of the others."""
+    from workloads.gen import _bf16_bits, _e4m3_encode
+
+    G = wl.Hq // wl.Hkv
+    q = (wl.q_bits.astype(np.uint32) << 16).view(np.float32).copy()
+    ks = wl.k_scale.reshape(-1)
+    for b in range(wl.B):
+        L = int(wl.seq_lens[b])
+        lo = max(0, L - wl.window) if wl.window > 0 else 0
+        for g in range(wl.Hkv):
+            qg = q[b, :, g * G, :].copy()
+            q[b, :, g * G:(g + 1) * G, :] = qg[:, None, :]
+            qv = qg[-1].astype(np.float64)
+            beta = nats / (wl.sm_scale * float(qv @ qv))
+            t = int(rng.integers(lo, L))
+            page, slot = int(wl.block_table[b, t // wl.bt]), t % wl.bt
+            kscale = ks[g] if ks.size > 1 else ks[0]
+            wl.k_cache[page, slot, g, :] = _e4m3_encode((beta * qv / kscale).astype(np.float32))
+    wl.q_bits[...] = _bf16_bits(q)
 
 # (case, flags, num_splits)
 SMALL_RUNS = []
@@ -214,6 +266,13 @@ def _small(name):
         wl = make_workload(seed=100 + list(SMALL).index(name), **kw)
         if name == "big_negative_sinks":
             wl.sinks[:] = -30.0
+        if name.startswith("peaked_row") or name.startswith("big_positive_sinks"):
+            _shift_values(wl, 2.0)
+        if name.startswith("peaked_row"):
+            _peak_one_key(wl, np.random.default_rng(7))
+        if name.startswith("big_positive_sinks"):
+            wl.sinks[:] = 12.0
+            wl.sinks[::3] = 8.0
         ref = oracle.decode(**wl.oracle_kwargs())
         _small_cache[name] = (wl, upload(wl), ref)
     return _small_cache[name]
