@@ -27,6 +27,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kE4M3Max = 448.f;
+// fp32(1 / 6): the quantizer multiplies the block maximum by it.
+constexpr float kSixth = 1.0f / 6.0f;
 
 struct WriteParams {
   const uint16_t* src[2];   // key, value
@@ -112,8 +114,12 @@ __device__ __forceinline__ uint32_t e2m1_code(float t) {
 }
 
 // NVFP4 writer: one thread per 16-element block of a head's row; blockIdx.y
-// 0 keys, 1 values.  Per block: y = x * (1 / scale), scale byte = E4M3 of
-// min(max|y| / 6, 448), codes = E2M1 of y * (1 / that byte's value).
+// 0 keys, 1 values.  The steps of the quantizer the gist prints
+// (nvfp4_utils.cuh, cvt_warp_fp16_to_fp4, NVFP4 path) with the global scale
+// g = 1 / scale that reshape_and_cache_nvfp4_kernel gives it: block scale
+// s = g * (max|x| * (1/6)), its E4M3 byte (saturating), then the codes E2M1
+// of x * (1 / (E4M3(byte) * (1 / g))).  Every reciprocal here is the
+// correctly rounded fp32 quotient (the page uses an approximate one).
 __global__ __launch_bounds__(256) void cache_write_nvfp4_kernel(WriteParams p) {
   const int kv = blockIdx.y;
   const uint16_t* src = p.src[kv];
@@ -127,6 +133,7 @@ __global__ __launch_bounds__(256) void cache_write_nvfp4_kernel(WriteParams p) {
     const int h = bi / p.blocks_per_head;
     const int blk = bi - h * p.blocks_per_head;
     const float g = __fdiv_rn(1.f, p.scale[kv][p.per_head[kv] ? h : 0]);
+    const float inv_g = __fdiv_rn(1.f, g);
     const u32x4* x = reinterpret_cast<const u32x4*>(src + t * p.stride[kv] + 16 * int64_t(bi));
     const u32x4 x0 = x[0], x1 = x[1];
     const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -134,19 +141,21 @@ __global__ __launch_bounds__(256) void cache_write_nvfp4_kernel(WriteParams p) {
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      y[2 * j] = __uint_as_float(w[j] << 16) * g;
-      y[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) * g;
+      y[2 * j] = __uint_as_float(w[j] << 16);
+      y[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
       amax = fmaxf(amax, fmaxf(fabsf(y[2 * j]), fabsf(y[2 * j + 1])));
     }
-    const float sc = fminf(__fdiv_rn(amax, 6.f), kE4M3Max);
+    // two separate fp32 products, in the page's order (s >= 0, so the clamp
+    // at 448 is the saturating conversion)
+    const float sc = fminf(__fmul_rn(g, __fmul_rn(amax, kSixth)), kE4M3Max);
     const uint32_t sbyte = __builtin_amdgcn_cvt_pk_fp8_f32(sc, 0.f, 0u, false) & 0xffu;
     const float sv = __builtin_amdgcn_cvt_f32_fp8(int(sbyte), 0);
-    const float r = sv > 0.f ? __fdiv_rn(1.f, sv) : 0.f;
+    const float r = sv > 0.f ? __fdiv_rn(1.f, __fmul_rn(sv, inv_g)) : 0.f;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      lo |= e2m1_code(y[j] * r) << (4 * j);
-      hi |= e2m1_code(y[8 + j] * r) << (4 * j);
+      lo |= e2m1_code(__fmul_rn(y[j], r)) << (4 * j);
+      hi |= e2m1_code(__fmul_rn(y[8 + j], r)) << (4 * j);
     }
     uint8_t* page = cache + (slot >> p.bt_shift) * p.page_bytes;
     const int64_t off = slot & p.bt_mask;

@@ -267,13 +267,16 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
  * decode(code) * scale_h.
  *
  * NVFP4 pools (kv_format = FP8PA_KV_NVFP4): each 16-element block of a
- * head's row becomes one E4M3 scale byte and 16 E2M1 codes.  The quantizer
- * the gist calls is not printed; this library takes, per block,
- * y = fp32(x * fp32(1 / scale_h)), s = fp32(max|y| / 6), the scale byte =
- * E4M3 of min(s, 448) (nearest, ties to even), and the codes = E2M1 of
- * fp32(y * fp32(1 / E4M3(scale byte))), nearest with ties to even, saturated
- * at 6, keeping the sign bit (all zero codes when the scale decodes to 0).
- * NaN inputs are outside the format (their block's bytes are unspecified).
+ * head's row becomes one E4M3 scale byte and 16 E2M1 codes, by the steps of
+ * the quantizer the gist prints (nvfp4_utils.cuh, cvt_warp_fp16_to_fp4,
+ * NVFP4 path) with the global scale g = fp32(1 / scale_h) the cache kernel
+ * hands it: s = fp32(g * fp32(max|x| * fp32(1/6))), the scale byte = E4M3
+ * of s (nearest, ties to even, saturating at 448), and the codes = E2M1 of
+ * fp32(x * r) with r = fp32(1 / fp32(E4M3(byte) * fp32(1 / g))) (0 when the
+ * byte decodes to 0), nearest with ties to even, saturated at 6, keeping
+ * the sign bit.  The page forms these reciprocals with an approximate
+ * instruction; this library uses correctly rounded division.  NaN inputs
+ * are outside the format (their block's bytes are unspecified).
  *
  * MXFP8 pools (kv_format = FP8PA_KV_MXFP8): each 32-element block of a head's
  * row becomes one E8M0 scale byte and 32 E4M3 codes, by the OCP MX rule:

@@ -20,12 +20,18 @@ Readings of what the pages leave open, each the plainest one the rest supports:
   high nibble;
 * a value reads as E2M1(code) * E4M3(scale byte) * tensor scale (k_scale or
   v_scale, one per tensor or per kv head);
-* the writer (the quantizer helper the gist calls is not printed) takes, per
-  16-element block, y = fp32(x * fp32(1 / scale)), s = fp32(max|y| / 6), the
-  scale byte = E4M3 of min(s, 448) rounded to nearest even, and the codes =
-  E2M1 of fp32(y * fp32(1 / E4M3(scale byte))) rounded to nearest even with
-  saturation at 6 (all codes 0 when the scale decodes to 0); a code keeps
-  the sign bit of its fp32 value.  NaN inputs are outside the format.
+* the writer follows the quantizer the gist prints (`nvfp4_utils.cuh`,
+  `cvt_warp_fp16_to_fp4`, NVFP4 path) with the global scale g = fp32(1 /
+  scale) that `reshape_and_cache_nvfp4_kernel` passes it.  Per 16-element
+  block of bf16 inputs x: the block maximum a = max|x| (of the inputs
+  themselves); the block scale s = fp32(g * fp32(a * fp32(1 / 6))); the scale
+  byte = E4M3 of s rounded to nearest even, saturating at 448 (s is never
+  negative); the output factor r = fp32(1 / fp32(E4M3(byte) * fp32(1 / g)))
+  when the byte decodes to a nonzero value, else 0; the codes = E2M1 of
+  fp32(x * r), nearest with ties to the even code, saturating at 6 and
+  keeping the sign bit of their fp32 value.  The page forms its reciprocals
+  (of 6, of g and of the product) with an approximate instruction; here each
+  is the correctly rounded fp32 quotient.  NaN inputs are outside the format.
 """
 
 from __future__ import annotations
@@ -34,6 +40,9 @@ import numpy as np
 
 from .fp8pa_ref import E4M3_TABLE
 from .fp8pa_write_ref import e4m3_encode
+
+#: fp32(1 / 6), the reciprocal the quantizer multiplies the block maximum by.
+SIXTH = np.float32(np.float32(1.0) / np.float32(6.0))
 
 __all__ = ["E2M1_TABLE", "e2m1_decode_code", "e2m1_encode", "nvfp4_side_bytes",
            "nvfp4_gather", "nvfp4_cache_write"]
@@ -122,20 +131,19 @@ def nvfp4_cache_write(key_bits, value_bits, slot_mapping, k_scale, v_scale, k_po
                 continue
             page, off = int(slot) // block_tokens, int(slot) % block_tokens
             for h in range(num_kv_heads):
-                g = np.float32(1.0) / sc[h if sc.size > 1 else 0]
-                y = (vals[t, h, :] * g).astype(np.float32)                      # [D]
+                g = np.float32(np.float32(1.0) / sc[h if sc.size > 1 else 0])  # the global scale
+                inv_g = np.float32(np.float32(1.0) / g)
+                x = vals[t, h, :]                                                 # [D] float32
                 doff, soff = _offsets(np.array([page]), np.array([off]), h, num_kv_heads,
                                       block_tokens, head_dim, kv_layout)
                 for blk in range(head_dim // 16):
-                    yb = y[16 * blk: 16 * blk + 16]
-                    s = np.float32(np.max(np.abs(yb)) / np.float32(6.0))
-                    sbyte = int(e4m3_encode(np.float64(min(float(s), 448.0))))
-                    sval = E4M3_TABLE[sbyte]
-                    if sval == 0.0:
-                        codes = np.where(np.signbit(yb), 8, 0).astype(np.uint8)
-                    else:
-                        r = np.float32(np.float32(1.0) / np.float32(sval))
-                        codes = e2m1_encode((yb * r).astype(np.float32).astype(np.float64))
+                    xb = x[16 * blk: 16 * blk + 16]
+                    a = np.float32(np.max(np.abs(xb)))
+                    s = np.float32(g * np.float32(a * SIXTH))
+                    sbyte = int(e4m3_encode(np.float64(s)))
+                    sval = np.float32(E4M3_TABLE[sbyte])
+                    r = np.float32(np.float32(1.0) / np.float32(sval * inv_g)) if sval != 0 else np.float32(0.0)
+                    codes = e2m1_encode((xb * r).astype(np.float32).astype(np.float64))
                     packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
                     out[page, int(doff[0]) + 8 * blk: int(doff[0]) + 8 * blk + 8] = packed
                     out[page, int(soff[0]) + blk] = sbyte

@@ -189,3 +189,31 @@ def test_nvfp4_write_then_decode():
                            sm_scale=1 / np.sqrt(D), kv_format="nvfp4", num_kv_heads=Hkv, block_tokens=bt)
     o, l = to_host(out, lse)
     compare(o, l, ro, rl, label="nvfp4 cache_write -> decode")
+
+
+def test_nvfp4_writer_golden_midpoint_block():
+    """The hand-worked block of tests/golden/nvfp4_writer_midpoint.json
+    through the GPU writer: scale byte 0x44 (the even code at the midpoint
+    2.875) and the stated E2M1 codes, in every block of the row."""
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_writer_midpoint.json")) as f:
+        gd = json.load(f)
+    Hkv, D, bt = 1, 64, 16
+    blk = np.array([int(h, 16) for h in gd["x_bf16_bits"]], dtype=np.uint16)
+    bits = np.tile(blk, D // 16).reshape(1, Hkv, D)
+    key = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ks = torch.from_numpy(np.array([int(gd["k_scale_f32_bits"], 16)], dtype=np.uint32).view(np.float32)).cuda()
+    side = oracle.nvfp4_side_bytes(Hkv, bt, D)
+    kc = torch.zeros((1, side), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    fp.cache_write(key, key, torch.tensor([3], dtype=torch.int64).cuda(), ks, ks, kc, vc,
+                   kv_format="nvfp4", block_tokens=bt)
+    torch.cuda.synchronize()
+    data = [int(h, 16) for h in gd["expected_data_bytes"]] * (D // 16)
+    sbyte = int(gd["expected_scale_byte"], 16)
+    for got in (kc.cpu().numpy()[0], vc.cpu().numpy()[0]):
+        assert got[3 * (D // 2): 4 * (D // 2)].tolist() == data
+        sc0 = bt * (D // 2)
+        assert got[sc0 + 3 * (D // 16): sc0 + 4 * (D // 16)].tolist() == [sbyte] * (D // 16)

@@ -151,3 +151,57 @@ def test_nvfp4_writer_rounds_and_skips():
             # to even are pinned above) and keeps the sign
             assert abs(abs(c) - a_sat) <= np.abs(mags - a_sat).min() + 1e-9
             assert c == 0 or np.sign(c) == np.sign(a)
+
+
+def _nvfp4_golden():
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_writer_midpoint.json")) as f:
+        return json.load(f)
+
+
+def test_nvfp4_golden_derivation_is_consistent():
+    """The golden block's numbers in exact rational arithmetic: fp32(1/6),
+    the global scale, the block scale that rounds onto the E4M3 midpoint
+    2.875, and the other order's scale that stays below it."""
+    from fractions import Fraction
+
+    gd = _nvfp4_golden()
+
+    def f32(h):
+        return Fraction(float(np.array([int(h, 16)], dtype=np.uint32).view(np.float32)[0]))
+
+    def rne32(x):
+        e = x.numerator.bit_length() - x.denominator.bit_length()
+        e = e if Fraction(2) ** e <= x else e - 1
+        ulp = Fraction(2) ** (e - 23)
+        q = x / ulp
+        n = q.numerator // q.denominator
+        rem = q - n
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2):
+            n += 1
+        return n * ulp
+
+    ks, g, sixth = f32(gd["k_scale_f32_bits"]), f32(gd["g_f32_bits"]), f32(gd["sixth_f32_bits"])
+    assert g == rne32(1 / ks) and sixth == rne32(Fraction(1, 6))
+    a = Fraction(1421875, 1000000)
+    s = rne32(g * rne32(a * sixth))
+    assert s == Fraction(23, 8)                                # 2.875, the midpoint of 2.75 and 3
+    assert rne32(rne32(a * g) / 6) < Fraction(23, 8)          # the other order stays below
+
+
+def test_nvfp4_writer_golden_block():
+    """oracle.nvfp4_cache_write on the golden block: the scale byte is the
+    even code at the midpoint and the element codes are the hand-worked ones."""
+    gd = _nvfp4_golden()
+    Hkv, D, bt = 1, 16, 1
+    bits = np.array([int(h, 16) for h in gd["x_bf16_bits"]], dtype=np.uint16).reshape(1, 1, D)
+    ks = np.array([int(gd["k_scale_f32_bits"], 16)], dtype=np.uint32).view(np.float32)
+    side = oracle.nvfp4_side_bytes(Hkv, bt, D)
+    pool = np.zeros((1, side), np.uint8)
+    k_out, v_out = oracle.nvfp4_cache_write(bits, bits, np.array([0]), ks, ks, pool, pool.copy(), Hkv, bt, D)
+    want_data = [int(h, 16) for h in gd["expected_data_bytes"]]
+    for out in (k_out, v_out):
+        assert out[0, :8].tolist() == want_data
+        assert int(out[0, 8]) == int(gd["expected_scale_byte"], 16)
