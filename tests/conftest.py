@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # A mistake planted in the oracle (tests/oracle_mutations.py), for the
+    # check that the pins catch it; never set in a normal run.
+    name = os.environ.get("FP8PA_ORACLE_MUTATION")
+    if name:
+        from tests.oracle_mutations import apply
+
+        apply(name)
