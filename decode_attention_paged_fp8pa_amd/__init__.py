@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     fp8pa_debug_nvfp4,
     fp8pa_debug_wave_ops,
     fp8pa_decode,
+    fp8pa_decode_noalloc,
     fp8pa_merge,
     fp8pa_plan,
     fp8pa_workspace_bytes,
@@ -54,6 +55,7 @@ __all__ = [
     "decode",
     "shape_for",
     "fp8pa_decode",
+    "fp8pa_decode_noalloc",
     "fp8pa_merge",
     "fp8pa_plan",
     "fp8pa_workspace_bytes",

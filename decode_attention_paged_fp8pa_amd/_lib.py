@@ -125,6 +125,8 @@ _SIGS = {
                                              ctypes.POINTER(ctypes.c_size_t)]),
     "fp8pa_decode": (ctypes.c_int, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                     _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "fp8pa_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            _VP, _VP, _VP, _VP]),
     "fp8pa_merge": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    _VP, _VP, _VP, _VP, _VP, _VP]),
     "fp8pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -223,6 +225,15 @@ def fp8pa_decode(shape: Shape, q, k_cache, v_cache, block_table, seq_lens, k_sca
                             int(workspace_bytes), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_decode")
+
+
+def fp8pa_decode_noalloc(shape: Shape, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale,
+                         sinks, out, lse, stream=None) -> None:
+    st = lib().fp8pa_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(sinks), _ptr(out), _ptr(lse), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_decode_noalloc")
 
 
 def fp8pa_merge(num_splits, num_rows, num_q_heads, head_dim, partial_o, partial_lse, sinks, out,

@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdint>
 
@@ -2055,31 +2056,44 @@ hipError_t launch_merge(int D, const MergeArgs& a, int cu, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace fp8pa
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's workspace: one static array per device,
+// kScratchBytes long, that the code object brings with it.  Its name is a
+// host-side stand-in in host code; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.  Calls on one device share
+// the array, so calls that overlap on one device race.  Nothing in it must
+// start at zero: every byte a merge reads was written by the partial pass
+// before it, in stream order.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(FP8PA_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-using namespace fp8pa;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
 
-extern "C" {
-
-fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t* bytes) {
-  if (!shape || !bytes) return FP8PA_ERR_INVALID_ARG;
-  Plan pl;
-  fp8pa_status st = make_plan(shape, 1, &pl);
-  if (st != FP8PA_OK) return st;
-  const int cu = cu_count_of(device);
-  if (cu < 1) return FP8PA_ERR_HIP;
-  st = make_plan(shape, cu, &pl);
-  if (st != FP8PA_OK) return st;
-  *bytes = pl.ws_bytes;
-  return FP8PA_OK;
+// The device address of `dev`'s scratch array (dev must be current), or null
+// when the runtime cannot give it.
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
-fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k_cache,
-                          const void* v_cache, const int32_t* block_table,
-                          const int32_t* seq_lens, const float* k_scale, const float* v_scale,
-                          const float* sinks, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+// Both decode entry points: `scratch_ptr` non-null means the workspace is
+// the device's static scratch array (fp8pa_decode_noalloc), of which the
+// plan may use at most kScratchBytes.
+fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                         const float* sinks, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, bool use_scratch) {
   if (!shape) return FP8PA_ERR_INVALID_ARG;
   Plan pl;
   fp8pa_status st = make_plan(shape, 1, &pl);  // shape checks before touching the GPU
@@ -2097,6 +2111,14 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
   if (cu < 1) return FP8PA_ERR_HIP;
   st = make_plan(shape, cu, &pl);
   if (st != FP8PA_OK) return st;
+  if (use_scratch) {
+    if (pl.ws_bytes > kScratchBytes) return FP8PA_ERR_WORKSPACE_TOO_SMALL;
+    if (pl.ws_bytes > 0) {
+      workspace = scratch_of(dev);
+      if (!workspace) return FP8PA_ERR_HIP;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
     return FP8PA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -2186,6 +2208,44 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
     if (e != hipSuccess) return FP8PA_ERR_HIP;
   }
   return FP8PA_OK;
+}
+
+}  // namespace
+}  // namespace fp8pa
+
+using namespace fp8pa;
+
+extern "C" {
+
+fp8pa_status fp8pa_workspace_bytes(const fp8pa_shape* shape, int device, size_t* bytes) {
+  if (!shape || !bytes) return FP8PA_ERR_INVALID_ARG;
+  Plan pl;
+  fp8pa_status st = make_plan(shape, 1, &pl);
+  if (st != FP8PA_OK) return st;
+  const int cu = cu_count_of(device);
+  if (cu < 1) return FP8PA_ERR_HIP;
+  st = make_plan(shape, cu, &pl);
+  if (st != FP8PA_OK) return st;
+  *bytes = pl.ws_bytes;
+  return FP8PA_OK;
+}
+
+fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, const float* k_scale, const float* v_scale,
+                          const float* sinks, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_impl(shape, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks,
+                     out, lse, workspace, workspace_bytes, stream, false);
+}
+
+fp8pa_status fp8pa_decode_noalloc(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const float* k_scale,
+                                  const float* v_scale, const float* sinks, void* out, float* lse,
+                                  void* stream) {
+  return decode_impl(shape, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, sinks,
+                     out, lse, nullptr, 0, stream, true);
 }
 
 fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_heads,

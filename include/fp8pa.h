@@ -229,6 +229,30 @@ fp8pa_status fp8pa_decode(const fp8pa_shape* shape, const void* q, const void* k
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8pa_decode_noalloc: fp8pa_decode for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It computes exactly what
+ * fp8pa_decode computes, with the same plan and kernels, and takes the same
+ * arguments minus the workspace: the split partials go to a static device
+ * array of FP8PA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * device it runs on until the process ends.  It allocates nothing, and the
+ * array's device address is looked up once per device on the first call
+ * there.  Every call on a device shares that device's array, so calls that
+ * may overlap on one device (different streams, no ordering between them)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Returns FP8PA_ERR_WORKSPACE_TOO_SMALL when the plan's workspace
+ * (fp8pa_workspace_bytes) exceeds FP8PA_NOALLOC_SCRATCH_BYTES, FP8PA_ERR_HIP
+ * when the array's address cannot be obtained or a launch fails, and
+ * otherwise what fp8pa_decode returns for the same arguments.
+ */
+#define FP8PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+fp8pa_status fp8pa_decode_noalloc(const fp8pa_shape* shape, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, const float* k_scale,
+                                  const float* v_scale, const float* sinks, void* out, float* lse,
+                                  void* stream);
+
+/*
  * fp8pa_merge: the log-sum-exp merge of split-KV partials (FlashInfer PR
  * #5591, Summary: one LSE reducer after the split producers).  For each row
  * r < num_rows, with M = max(partial_lse[r, s], sink):
