@@ -92,7 +92,16 @@ typedef enum fp8pa_status {
                             codes, rows of D bytes, followed by a scale region of one E8M0 byte
                             per 32 consecutive head_dim elements of a token, rows of D/32 bytes;
                             rows are ordered by kv_layout as for NVFP4.  A value reads as
-                            E4M3(code) * 2^(s - 127) * k_scale (v_scale); s = 0xFF is NaN. */
+                            E4M3(code) * 2^(s - 127) * k_scale (v_scale); s = 0xFF is NaN.
+                            Supported scale bytes: 10 <= s <= 200.  Within them every element
+                            is a normal bf16 number, so the kernels hold it exactly, and the
+                            P.V sums stay finite (P <= 2^8 times elements below 2^82 over up
+                            to 2^20 keys); the scores sm_scale * q.K stay finite as long as
+                            the caller's queries keep them inside fp32's range.  Bytes 0..9
+                            give elements below bf16's normal range, which the conversion may
+                            flush, and 201..254 may overflow the fp32 sums: results over pages
+                            holding such bytes are unspecified (the bytes live on the device
+                            and are not checked). */
 
 /* Host-known description of one decode call. */
 typedef struct fp8pa_shape {

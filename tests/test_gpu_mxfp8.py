@@ -188,3 +188,32 @@ def test_mxfp8_write_then_decode():
                            sm_scale=1 / np.sqrt(D), kv_format="mxfp8", num_kv_heads=Hkv, block_tokens=bt)
     o, l = to_host(out, lse)
     compare(o, l, ro, rl, label="mxfp8 cache_write -> decode")
+
+
+# Scale-byte centres (K, V) per sequence: with the draw's spread of -2..+3
+# the bytes cover 10..200, the range fp8pa.h supports.
+E8M0_CENTRES = [(12, 197), (40, 12), (70, 150), (100, 70), (121, 121), (150, 40), (180, 180), (197, 100)]
+
+
+@pytest.mark.parametrize("flags", [0, fp.FP8PA_FLAG_FORCE_DOT])
+def test_mxfp8_scale_bytes_across_the_supported_range(flags):
+    """MXFP8 pages whose E8M0 bytes cover 10..200 (elements from 2^-126 to
+    about 2^82).  Sequence b's queries are scaled by 2^(121 - k centre) so that
+    its scores keep the magnitude of the other MXFP8 cases (the LSE bar is
+    absolute), and its outputs, which scale with 2^(v centre - 127), are
+    compared after dividing both sides by 2^(v centre - 121), an exact power
+    of two, so the bar keeps its meaning at every magnitude."""
+    B = len(E8M0_CENTRES)
+    wl = make_mxfp8_workload(B=B, q_len=2, Hq=16, Hkv=4, D=128, bt=16,
+                             seq_lens=[70, 300, 33, 200, 513, 96, 17, 260], seed=61, sinks=True,
+                             scale=("per_head", 0.02, 0.1), e8m0_centers=E8M0_CENTRES)
+    q = (wl.q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for b, (ck, _) in enumerate(E8M0_CENTRES):
+        q[b] *= 2.0 ** (121 - ck)          # exact: a power of two on bf16 values
+    from workloads.gen import _bf16_bits
+    wl.q_bits[...] = _bf16_bits(q.astype(np.float32))
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    o, l = to_host(*run(wl, upload(wl), flags=flags))
+    norm = np.array([2.0 ** (cv - 121) for _, cv in E8M0_CENTRES]).reshape(B, 1, 1, 1)
+    assert np.isfinite(ro).all() and np.isfinite(o).all()
+    compare(o / norm, l, ro / norm, rl, label=f"mxfp8 e8m0 10..200 flags={flags}")

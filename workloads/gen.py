@@ -272,7 +272,11 @@ def make_mxfp8_workload(**kw):
 def _make_blockscaled_workload(*, fmt, B, q_len, Hq, Hkv, D, bt, seq_lens, seed, table="perm",
                                pool=None, scale=("tensor", 0.05), window=0, sinks=False,
                                sm_scale=None, poison=True, name=None, kv_layout="NHD",
-                               page_stride=None):
+                               page_stride=None, e8m0_centers=None):
+    """e8m0_centers (MXFP8 only): per sequence b a pair (k, v) of scale-byte
+    centres; that sequence's K (V) scale bytes are then the usual draw moved
+    to centre + (draw - 121), i.e. centre - 2 .. centre + 3, so the same
+    random stream spreads whole sequences across the E8M0 range."""
     rng = np.random.default_rng(seed)
     if isinstance(seq_lens, tuple) and seq_lens and seq_lens[0] == "uniform":
         sl = rng.integers(seq_lens[1], seq_lens[2] + 1, size=B).astype(np.int32)
@@ -329,6 +333,9 @@ def _make_blockscaled_workload(*, fmt, B, q_len, Hq, Hkv, D, bt, seq_lens, seed,
             else:
                 data[(data & 0x7F) == 0x7F] -= 1          # no NaN codes in attended data
                 scl = rng.integers(119, 125, size=(hi - lo, Hkv, sc_row), dtype=np.uint8)
+                if e8m0_centers is not None:
+                    centre = int(e8m0_centers[b][len(pools)])
+                    scl = (scl.astype(np.int64) - 121 + centre).astype(np.uint8)
             for h in range(Hkv):
                 r = h * bt + slots if kv_layout == "HND" else slots * Hkv + h
                 d_off = r * data_row
