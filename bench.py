@@ -24,7 +24,9 @@ one.  The graph is replayed REPLAYS times: the step time is the median of
 the per-replay averages, reported with p10 / p90.  The partial kernel alone
 is timed from a second graph of the same steps run with
 FP8PA_FLAG_PARTIAL_ONLY (no merge launch).  A 1 GiB device-to-device copy is
-timed as the practical HBM ceiling ("copy_ceiling"), and the KV-cache writer
+timed as the practical HBM ceiling ("copy_ceiling"), and one launch that
+only reads each workload's KV byte count, plus an empty launch, as the floor
+of its step ("read_ceiling"), and the KV-cache writer
 fp8pa_cache_write at a decode step's and a prefill chunk's size ("writer").
 Five widenings are timed after the decode: the ragged GQA batch with K
 scales in four head_dim groups ("k_groups_variant"), that batch and the
@@ -115,7 +117,8 @@ def partial_kernel_name(plan, D):
         lw = plan["row_groups_per_wg"] if plan["row_groups_per_wg"] > 1 else 0
         return (f"partial_mfma_kernel<{D * pr}, {plan['waves_per_head']}, {pr}, "
                 f"{plan['row_blocks']}, {plan['nontemporal_kv']}, {lw}>")
-    return f"partial_dot_kernel<{D}>"
+    return (f"partial_dot_kernel<{D}, 0, {plan['rows_per_group']}"
+            + (", 1>" if plan["nontemporal_kv"] else ">"))
 
 
 def kernel_source_hash():
@@ -373,6 +376,7 @@ def _result(wl, label, kvb, copies, plan, step_ms, eager_ms, wall_ms, graph_wall
     res = dict(
         workload=wl.name,
         describe=describe(wl),
+        D=wl.D,
         kv_bytes=kvb,
         other_bytes=other_bytes(wl),
         copies=copies,
@@ -423,6 +427,61 @@ def copy_ceiling(log):
     torch.cuda.empty_cache()
     return {"bytes_read_plus_written": 2 * n, "median_us": round(t * 1e6, 1), "gbps": round(gbps, 1),
             "pct_of_peak": round(gbps / PEAK_GBPS * 100, 2)}
+
+
+def read_ceiling(results, log, launches=50):
+    """The practical floor of each workload's step: one launch that reads
+    only the workload's KV byte count (fp8pa_debug_stream_read: contiguous
+    chunks, 16-byte loads), cold (buffers rotated through >= 1 GiB), timed
+    from graph replays like the decode; and one empty launch, which the merge
+    kernel adds on top of any partial pass."""
+    import torch
+
+    import decode_attention_paged_fp8pa_amd as fp
+
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+
+    def timed(nbytes, bufs):
+        for i in range(3):
+            fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(REPLAYS):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / launches * 1e3)
+        del g
+        return sorted(per)[len(per) // 2]
+
+    out = {"empty_launch_us": round(timed(0, [sink]), 2)}
+    for k, r in results.items():
+        nbytes = (int(r["kv_bytes"]) + 15) // 16 * 16
+        if nbytes < (64 << 20):
+            continue  # launch-bound: nothing to stream
+        copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / nbytes))))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        us = timed(nbytes, bufs)
+        floor_step = us + (out["empty_launch_us"] if r["merge_ms"] > 0 else 0.0)
+        out[f"cfg{k}"] = {"kv_bytes": nbytes, "read_us": round(us, 2),
+                          "read_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "floor_step_us": round(floor_step, 2),
+                          "floor_pct_of_peak": round(nbytes / (floor_step * 1e-6) / 1e9 / PEAK_GBPS * 100, 1)}
+        log(f"[bench] read ceiling cfg{k}: {nbytes / 1e6:.1f} MB in one launch {us:.1f} us "
+            f"({nbytes / (us * 1e-6) / 1e9:.0f} GB/s); with an empty merge launch {floor_step:.1f} us")
+        del bufs
+        torch.cuda.empty_cache()
+    log(f"[bench] empty launch {out['empty_launch_us']:.2f} us")
+    return out
 
 
 def measure_writer(steps, log):
@@ -679,7 +738,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--configs", default="1,2,3,4,5")
+    ap.add_argument("--configs", default="1,2,3,4,5,6",
+                    help="named workloads 1-5, and 6: the ragged GQA batch as MHA decode (VALU kernel)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
@@ -752,15 +812,16 @@ def main():
         "algorithmic_bytes_per_launch": h["kv_bytes"],
     }
     writer = kg = hnd = nv = prefill = None
+    ceiling_reads = read_ceiling(results, log)
     if not args.decode_only:
         writer, kg, hnd, nv, prefill = widenings(args, log)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head_wl, args.cpu_budget, log)
-    emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill)
+    emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill, ceiling_reads)
 
 
-ONLY_CHOICES = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "writer", "cfg2_kg4", "cfg2_hnd", "cfg3_hnd",
+ONLY_CHOICES = ("cfg1", "cfg2", "cfg3", "cfg4", "cfg5", "cfg6", "writer", "cfg2_kg4", "cfg2_hnd", "cfg3_hnd",
                 "cfg2_nvfp4_hnd", "cfg2_mxfp8_hnd", "prefill")
 
 
@@ -822,7 +883,7 @@ def widenings(args, log):
     return writer, kg, hnd, bs, prefill
 
 
-def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill):
+def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, prefill, ceiling_reads=None):
     """Print the one JSON line."""
     line = {
         "metric": METRIC,
@@ -844,6 +905,7 @@ def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, pre
         "cpu_baseline": cpu,
         "gpu_state": h.get("gpu_state"),
         "copy_ceiling": ceiling,
+        "read_ceiling": ceiling_reads,
         "writer": writer,
         "k_groups_variant": kg,
         "hnd_variant": hnd,
@@ -865,6 +927,7 @@ def emit(args, results, h, head_wl, roof, cpu, ceiling, writer, kg, hnd, nv, pre
                 "warm_graph_step_us": r.get("warm_graph_step_us"),
                 "bar_70pct_of_peak": (bool(r["pct_peak"] >= BAR_PCT) if k in BAR_WORKLOADS
                                       else "not in the bar"),
+                "partial_kernel": partial_kernel_name(r["plan"], r["D"]),
             } for k, r in results.items()},
     }
     print(json.dumps(line), flush=True)

@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     fp8pa_debug_mxfp8,
     fp8pa_debug_mfma_fp8,
     fp8pa_debug_nvfp4,
+    fp8pa_debug_stream_read,
     fp8pa_debug_wave_ops,
     fp8pa_decode,
     fp8pa_decode_noalloc,

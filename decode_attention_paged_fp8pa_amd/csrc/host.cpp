@@ -128,14 +128,21 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     else if (rg1 % 2 == 0 && p.D == 128) p.lw = 2;
     if (p.lw) p.nb = 1;
   }
-  p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb : kRowsDot;
+  // (the VALU kernel carries one row per wavefront for one-row kv heads of
+  // E4M3 pages, MHA decode: no FMAs on empty rows)
+  p.rpg = p.variant == kVariantMfma ? kRowsMfma * p.nb
+                                    : (p.rows == 1 && p.fmt == FP8PA_KV_E4M3 ? 1 : kRowsDot);
   p.row_groups = int32_t(ceil_div(p.rows, p.rpg));
-  const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : kRowsDot;
+  const int32_t rows_unit = p.variant == kVariantMfma ? kRowsMfma : p.rpg;
   const int32_t rows_eff = p.rows < rows_unit ? p.rows : rows_unit;
   // Non-temporal K/V loads keep streamed bytes from pushing reused ones out
   // of the caches; they pay only when no other wavefront reads the same
   // bytes (one row group) and a wavefront reads whole 128-byte lines.
-  p.nt = (p.variant == kVariantMfma && p.row_groups == 1 && p.D * p.pr / p.ds >= 128) ? 1 : 0;
+  // (the VALU kernel: where one row per wavefront carries E4M3 pages)
+  p.nt = (p.row_groups == 1 && p.D * p.pr / p.ds >= 128 &&
+          (p.variant == kVariantMfma || (p.rpg == 1 && p.fmt == FP8PA_KV_E4M3)))
+             ? 1
+             : 0;
 
   const int32_t units = p.Hkv / p.pr;  // wavefront head units per sequence
   const int32_t max_hg = kMaxWgWaves / p.ds;
@@ -153,8 +160,8 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     if (wk < max_keys) max_keys = wk;
   }
   const int64_t n_tiles = ceil_div(max_keys, kTileTokens) + (s->window > 0 ? 1 : 0);
-  // The MFMA kernel holds a split's block-table entries in registers.
-  const int64_t tps_cap = p.variant == kVariantMfma ? kMaxSplitTiles : n_tiles;
+  // Both kernels hold a split's block-table entries in registers.
+  const int64_t tps_cap = kMaxSplitTiles;
   p.tps_cap = int32_t(tps_cap < n_tiles ? tps_cap : n_tiles);
 
   // Splits: enough (sequence, split) items that the busy wavefronts fill the
@@ -234,8 +241,8 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     const int64_t pl = rows_total * splits * 4;
     const int64_t off = ceil_div(po, kWorkspaceAlign) * kWorkspaceAlign;
     p.off_lse = size_t(off);
-    p.off_chunk = size_t(off + ceil_div(pl, kWorkspaceAlign) * kWorkspaceAlign);
-    p.ws_bytes = p.off_chunk + kWorkspaceAlign;
+    p.off_nsplit = size_t(off + ceil_div(pl, kWorkspaceAlign) * kWorkspaceAlign);
+    p.ws_bytes = p.off_nsplit + size_t(ceil_div(int64_t(p.B) * 4, kWorkspaceAlign) * kWorkspaceAlign);
   }
   *plan = p;
   return FP8PA_OK;

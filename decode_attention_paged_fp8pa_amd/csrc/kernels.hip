@@ -99,7 +99,7 @@ struct Params {
   int32_t balanced;      // 1: the chunk comes from the batch's seq_lens
   int32_t target_items;  // balanced plan: items the chunk size aims at
   int32_t min_tiles;     // balanced plan: chunk floor that keeps partials small
-  int32_t* chunk_out;    // balanced plan: the chosen chunk, for the merge
+  int32_t* nsplit_out;   // per sequence: the splits it got (written by its first item), for the merge
   int32_t max_seq_len;
   int32_t bt_shift, bt_mask, table_stride, window;
   int32_t k_per_head, v_per_head, direct;
@@ -164,6 +164,25 @@ __device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint32_t* dst) {
   }
 }
 
+
+// ptr[i] (a wave-uniform index) through a vector-memory load.  A scalar load
+// here would share the lgkm counter with the kernel-argument loads, so the
+// first wait on those would also wait for this round trip.
+__device__ __forceinline__ float uniform_vload(const float* ptr, int i) {
+  const Rsrc r = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, 0, 0x7fffffff, kRsrcWord3);
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, uint32_t(i) * 4u, 0, 0));
+}
+__device__ __forceinline__ int uniform_vload(const int32_t* ptr, int i) {
+  const Rsrc r = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, 0, 0x7fffffff, kRsrcWord3);
+  return int(__builtin_amdgcn_raw_buffer_load_b32(r, uint32_t(i) * 4u, 0, 0));
+}
+// ptr[i] when `use` (wave-uniform), else 0.f without touching memory (a
+// descriptor of size 0; ptr may then be null).  The value is left in flight:
+// its first use, not this call, waits for it.
+__device__ __forceinline__ float maybe_vload(const float* ptr, int i, bool use) {
+  const Rsrc r = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, 0, use ? 0x7fffffff : 0, kRsrcWord3);
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, use ? uint32_t(i) * 4u : 0u, 0, 0));
+}
 
 // Maximum of v over lanes l, l^16, l^32 and l^48 (the four lane groups that
 // hold one MFMA column), with the gfx950 permlane swaps (no LDS round trip).
@@ -347,6 +366,8 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
     w.sp = span_of(w.L, p.q_len, p.window);
     w.ts = w.sp.tile0 + w.split * p.tps;
     w.te = min(w.ts + p.tps, w.sp.tile1);
+    if (p.nsplit_out && w.split == 0 && blockIdx.x % p.upi == 0 && threadIdx.x == 0)
+      p.nsplit_out[w.b] = w.nsplit;
     return;
   }
 
@@ -378,7 +399,6 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
   c = max(c, min(p.min_tiles, max(1, (2 * T) / p.target_items)));
   c = max(c, ceil_div_i(M, p.num_splits));
   c = min(c, p.tps_cap);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *p.chunk_out = c;
   int base = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -398,6 +418,8 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
       w.sp = span_of(w.L, p.q_len, p.window);
       w.ts = w.sp.tile0 + w.split * c;
       w.te = min(w.ts + c, w.sp.tile1);
+      if (p.nsplit_out && w.split == 0 && blockIdx.x % p.upi == 0 && threadIdx.x == 0)
+        p.nsplit_out[w.b] = w.nsplit;
       return;
     }
     base += tot;
@@ -545,15 +567,17 @@ partial_mfma_kernel(Params p) {
   // dims never straddle two groups.
   const int qdim = w.half * DW + KB * (PR == 2 ? (qd & 1) : qd);
   const float ks = p.k_scale[(p.k_per_head ? kvh * p.k_groups : 0) + (qdim >> p.kg_shift)];
-  const float vs = p.v_scale[p.v_per_head ? kvh : 0];
-  float sink2[NB];
+  const float vs = uniform_vload(p.v_scale, p.v_per_head ? kvh : 0);
+  // (the raw sink logits stay in flight until the softmax state is set up)
+  float sink_raw[NB];
+  bool has_sink[NB];
+  const bool sinks_here = p.sinks && p.direct;  // uniform
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    sink2[b] = -INFINITY;
-    if (p.sinks && p.direct && rlane[b] < p.rows) {
-      const int qi = rlane[b] / p.G;
-      sink2[b] = p.sinks[kvh * p.G + (rlane[b] - qi * p.G)] * kLog2e;
-    }
+    has_sink[b] = sinks_here && rlane[b] < p.rows;
+    const int rr = min(rlane[b], p.rows - 1);
+    const int qi = rr / p.G;
+    sink_raw[b] = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
   work_item(p, w);
   if (!w.active) return;  // uniform over the workgroup
@@ -602,8 +626,9 @@ partial_mfma_kernel(Params p) {
   f32x4 O[NB][S];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    m[b] = sink2[b];
-    lsum[b] = (qd == 0 && sink2[b] > -INFINITY) ? 1.f : 0.f;
+    const float sink2 = has_sink[b] ? sink_raw[b] * kLog2e : -INFINITY;
+    m[b] = sink2;
+    lsum[b] = (qd == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
 #pragma unroll
     for (int e = 0; e < S; ++e) O[b][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -626,24 +651,35 @@ partial_mfma_kernel(Params p) {
   // no attended token).  A split spans at most kMaxSplitTiles tiles (64
   // steps), so the loop reads each page number with one readlane from a
   // fixed register, and has no table loads and no waits on them.
+  // (branch-free: a lane whose group holds no attended token reads at an
+  // offset past the descriptor and gets 0, so the four loads issue back to
+  // back with no wait between them)
   int tab[4];
+  {
+    const Rsrc rt = __builtin_amdgcn_make_buffer_rsrc((void*)btab, 0, p.table_stride * 4, kRsrcWord3);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int tt = ts + 2 * lane + (g >> 1);
-    const int gk = tt * kTileTokens + 16 * (g & 1);
-    const bool live = tt < te && gk < uhi && gk + 16 > ulo;
-    tab[g] = live ? btab[gk >> p.bt_shift] : 0;
+    for (int g = 0; g < 4; ++g) {
+      const int tt = ts + 2 * lane + (g >> 1);
+      const int gk = tt * kTileTokens + 16 * (g & 1);
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      tab[g] = int(__builtin_amdgcn_raw_buffer_load_b32(rt, live ? uint32_t(gk >> p.bt_shift) * 4u : kOob,
+                                                         0, 0));
+    }
   }
   // The query rows' raw bf16 bits; converted after the first tiles' loads
-  // are issued, so the two round trips overlap.
+  // are issued, so the two round trips overlap.  Every lane loads (a row
+  // past the last, or the other head's dims, reads row 0's valid bytes) and
+  // keeps zeros where the row is not its own: no branch, no wait between.
   u32x4 qraw[NB][KB / 8];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const uint16_t* qrow = p.q + row[b].out_row * DH + d0 + KB * (PR == 2 ? (qd & 1) : qd);
+    const bool qv = row[b].valid && mine;
 #pragma unroll
-    for (int i = 0; i < KB / 8; ++i)
-      qraw[b][i] = (row[b].valid && mine) ? *reinterpret_cast<const u32x4*>(qrow + 8 * i)
-                                          : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < KB / 8; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * i);
+      qraw[b][i] = qv ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   // Keys every row of this wavefront attends: [ilo, ihi).  A tile inside it
   // needs no score masks; only the others ("edge" tiles: at most the first
@@ -1190,12 +1226,16 @@ partial_mfma_nvfp4_kernel(Params p) {
   Work w = work_head(p, 1);
   const int kvh = w.g;
   const int rlane = w.rg * kRowsMfma + n;
-  const float ks = p.k_scale[p.k_per_head ? kvh : 0];
-  const float vs = p.v_scale[p.v_per_head ? kvh : 0];
-  float sink2 = -INFINITY;
-  if (p.sinks && p.direct && rlane < p.rows) {
-    const int qi = rlane / p.G;
-    sink2 = p.sinks[kvh * p.G + (rlane - qi * p.G)] * kLog2e;
+  const float ks = uniform_vload(p.k_scale, p.k_per_head ? kvh : 0);
+  const float vs = uniform_vload(p.v_scale, p.v_per_head ? kvh : 0);
+  // (left in flight until the softmax state is set up; see the FP8 kernel)
+  const bool sinks_here = p.sinks && p.direct;  // uniform
+  const bool has_sink = sinks_here && rlane < p.rows;
+  float sink_raw;
+  {
+    const int rr = min(rlane, p.rows - 1);
+    const int qi = rr / p.G;
+    sink_raw = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
   work_item(p, w);
   if (!w.active) return;  // uniform over the workgroup
@@ -1214,6 +1254,7 @@ partial_mfma_nvfp4_kernel(Params p) {
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
   // value vector is zero when this split writes the final output.
+  const float sink2 = has_sink ? sink_raw * kLog2e : -INFINITY;
   float m = sink2;
   float lsum = (qd == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
   f32x4 O[S];
@@ -1236,22 +1277,30 @@ partial_mfma_nvfp4_kernel(Params p) {
     vsoff[j] = uint32_t((4 * qd + j) * stok + (S * n) / BLK);
   }
 
-  // Block-table entries of the split in registers, as in the FP8 kernel.
+  // Block-table entries of the split in registers, branch-free, as in the
+  // FP8 kernel.
   int tab[4];
+  {
+    const Rsrc rt = __builtin_amdgcn_make_buffer_rsrc((void*)btab, 0, p.table_stride * 4, kRsrcWord3);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int tt = ts + 2 * lane + (g >> 1);
-    const int gk = tt * kTileTokens + 16 * (g & 1);
-    const bool live = tt < te && gk < uhi && gk + 16 > ulo;
-    tab[g] = live ? btab[gk >> p.bt_shift] : 0;
+    for (int g = 0; g < 4; ++g) {
+      const int tt = ts + 2 * lane + (g >> 1);
+      const int gk = tt * kTileTokens + 16 * (g & 1);
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      tab[g] = int(__builtin_amdgcn_raw_buffer_load_b32(rt, live ? uint32_t(gk >> p.bt_shift) * 4u : kOob,
+                                                         0, 0));
+    }
   }
   // the query row as bf16 operands: k-step c takes dims KD qd + 8 c .. + 7
+  // (loaded by every lane, zeroed where the row is past the last)
   u32x4 qraw[KSTEPS];
   {
     const uint16_t* qrow = p.q + row.out_row * D + KD * qd;
 #pragma unroll
-    for (int c = 0; c < KSTEPS; ++c)
-      qraw[c] = row.valid ? *reinterpret_cast<const u32x4*>(qrow + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < KSTEPS; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
+      qraw[c] = row.valid ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   const int ihi = L - p.q_len + qmin + 1;
   const int ilo = p.window > 0 ? max(0, L - p.q_len + qmax - p.window + 1) : 0;
@@ -1500,19 +1549,30 @@ __device__ __forceinline__ void fp4x16_to_f32(u32x2 w, float* f) {
 
 // ---------------------------------------------------------------------------
 // VALU dot-product partial kernel: D/16 lanes per token, 16 elements per
-// lane, 4 query rows per wavefront.  Lane l: token kk = l / (D/16) of a
-// round, chunk c = l % (D/16), dims [16 c, 16 c + 16).
+// lane, RPG query rows per wavefront (1 for one-row kv heads, MHA decode;
+// else 4).  Lane l: token kk = l / (D/16) of a round, chunk c = l % (D/16),
+// dims [16 c, 16 c + 16).
 //
 // FMT = FP8PA_KV_NVFP4: a lane's 16 elements of a token are one NVFP4 block
 // (8 data bytes and one E4M3 scale byte), so the block scale multiplies the
 // lane's partial q.K before the cross-lane sum, and P before it meets V.
+//
+// Pages of at least 16 tokens: the split's block-table entries are read
+// once into registers (as in the MFMA kernel), each 16-token group's page
+// is a wave-uniform readlane, and every load goes through a buffer
+// descriptor on that group (a key outside the span reads at an offset past
+// it and gets zeros), with two tiles in flight.  Smaller pages read each
+// key's page per lane.
 // ---------------------------------------------------------------------------
-template <int D, int FMT>
+template <int D, int FMT, int RPG, int NT = 0>
 __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   constexpr int LPK = D / 16;    // lanes per token
   constexpr int KPI = 64 / LPK;  // tokens per round
   constexpr int R = kTileTokens / KPI;
-  constexpr int RPG = kRowsDot;
+  constexpr bool NV = FMT == FP8PA_KV_NVFP4;
+  constexpr bool MX = FMT == FP8PA_KV_MXFP8;
+  constexpr int KWB = NV ? 8 : 16;  // data bytes a lane reads per token
+  constexpr int AUX = NT ? kLoadNT : 0;  // K/V load cache policy (NT: one wave reads each line)
 
   const int lane = threadIdx.x & 63;
   const int kk = lane / LPK;
@@ -1538,98 +1598,165 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
     return;
   }
 
+  const int tok = p.tok_stride;
+  // a lane's bytes of a token: 16 E4M3 codes, or 8 NVFP4 data bytes and one scale byte
+  const size_t lane_off = (size_t)w.g * (size_t)p.head_stride + KWB * c;
+  const uint8_t* kbase_g = p.k_cache + lane_off;
+  const uint8_t* vbase_g = p.v_cache + lane_off;
+  // (the lane's block: NVFP4's are its 16 elements, MXFP8's 32 span two lanes)
+  const size_t sc_lane = (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head + (MX ? c / 2 : c);
+  const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
+  // pages of at least 16 tokens: every 16-token group lies in one page (MXFP8
+  // at head_dim 256 keeps the per-lane path: the grouped scale loads would
+  // spill registers there)
+  const bool grouped_pages = p.bt_shift >= 4 && !(MX && D == 256);  // uniform
+
+  // Block-table entries of the split (pages of 16 or more tokens): lane k of
+  // tab[g] holds the page of 16-token group g & 1 of tile ts + 2 k + (g >> 1);
+  // a split spans at most kMaxSplitTiles tiles.  Branch-free, as in the MFMA
+  // kernel.
+  int tab[4] = {0, 0, 0, 0};
+  if (grouped_pages) {
+    const Rsrc rt = __builtin_amdgcn_make_buffer_rsrc((void*)btab, 0, p.table_stride * 4, kRsrcWord3);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int tt = ts + 2 * lane + (g >> 1);
+      const int gk = tt * kTileTokens + 16 * (g & 1);
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      tab[g] = int(__builtin_amdgcn_raw_buffer_load_b32(rt, live ? uint32_t(gk >> p.bt_shift) * 4u : kOob,
+                                                         0, 0));
+    }
+  }
+
   // this lane's 16 dims lie in one K scale group
   const float ks = p.k_scale[(p.k_per_head ? w.g * p.k_groups : 0) + ((16 * c) >> p.kg_shift)];
   const float cq = p.sm_scale * ks * kLog2e;
   float qf[RPG][16];
 #pragma unroll
   for (int rr = 0; rr < RPG; ++rr) {
-    if (rows[rr].valid) {
-      const uint16_t* qrow = p.q + rows[rr].out_row * D + 16 * c;
-      const u32x4 a = reinterpret_cast<const u32x4*>(qrow)[0];
-      const u32x4 b = reinterpret_cast<const u32x4*>(qrow)[1];
-      const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    // (every lane loads a valid row, the first one past the last, and
+    // keeps zeros: no branch between the loads)
+    const uint16_t* qrow = p.q + rows[rr].out_row * D + 16 * c;
+    const u32x4 a = reinterpret_cast<const u32x4*>(qrow)[0];
+    const u32x4 b = reinterpret_cast<const u32x4*>(qrow)[1];
+    const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const float qs = rows[rr].valid ? cq : 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qf[rr][2 * j] = bf16_lo(wv[j]) * cq;
-        qf[rr][2 * j + 1] = bf16_hi(wv[j]) * cq;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qf[rr][j] = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      qf[rr][2 * j] = bf16_lo(wv[j]) * qs;
+      qf[rr][2 * j + 1] = bf16_hi(wv[j]) * qs;
     }
   }
 
   float m[RPG], lsum[RPG], acc[RPG][16];
+  const bool sinks_here = p.sinks && p.direct;  // uniform
 #pragma unroll
   for (int rr = 0; rr < RPG; ++rr) {
-    const float sink2 =
-        (p.sinks && p.direct && rows[rr].valid) ? p.sinks[rows[rr].h] * kLog2e : -INFINITY;
+    const float raw = maybe_vload(p.sinks, rows[rr].h, sinks_here);
+    const float sink2 = (sinks_here && rows[rr].valid) ? raw * kLog2e : -INFINITY;
     m[rr] = sink2;
     lsum[rr] = (kk == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[rr][j] = 0.f;
   }
 
-  constexpr bool NV = FMT == FP8PA_KV_NVFP4;
-  constexpr bool MX = FMT == FP8PA_KV_MXFP8;
-  const int tok = p.tok_stride;
-  // a lane's bytes of a token: 16 E4M3 codes, or 8 NVFP4 data bytes and one scale byte
-  const size_t lane_off = (size_t)w.g * (size_t)p.head_stride + (NV ? 8 : 16) * c;
-  const uint8_t* kbase_g = p.k_cache + lane_off;
-  const uint8_t* vbase_g = p.v_cache + lane_off;
-  // (the lane's block: NVFP4's are its 16 elements, MXFP8's 32 span two lanes)
-  const size_t sc_lane = (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head + (MX ? c / 2 : c);
-  const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
-
-  for (int tt = ts; tt < te; ++tt) {
-    const int kb = tt * kTileTokens;
+  // One tile's K/V (and block-scale) bytes of this lane's tokens.
+  struct TileRegs {
     u32x4 kr[R], vr[R];
     // the block scale bytes of the lane's block of each token, four per word
     // (decoded where used: fewer live registers than one float per token)
     uint32_t ksw[(R + 3) / 4], vsw[(R + 3) / 4];
+  };
+  auto load_grouped = [&](int tt, TileRegs& r, int odd) {
+    const int kb = tt * kTileTokens;
+    const int step = ((tt - ts) >> 1) & 63;
 #pragma unroll
-    for (int i = 0; i < (R + 3) / 4; ++i) ksw[i] = vsw[i] = 0u;
-    auto scale_of = [&](const uint32_t* sw, int rho) {
-      const uint32_t b = (sw[rho / 4] >> (8 * (rho % 4))) & 0xffu;
-      return MX ? e8m0_to_f32(b) : __builtin_amdgcn_cvt_f32_fp8(int(b), 0);
-    };
+    for (int i = 0; i < (R + 3) / 4; ++i) r.ksw[i] = r.vsw[i] = 0u;
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+      const int grp = (rho * KPI) / 16;  // 16-token group of this round (constant)
+      const int gk = kb + 16 * grp;
+      const bool live = tt < te && gk < uhi && gk + 16 > ulo;
+      const int page = __builtin_amdgcn_readlane(tab[2 * odd + grp], step);
+      const size_t pbase = (size_t)page * (size_t)p.page_bytes;
+      const size_t gbase = pbase + (size_t)(gk & p.bt_mask) * tok;
+      const int key = kb + rho * KPI + kk;
+      const bool in_span = key >= ulo && key < uhi;
+      const uint32_t off = in_span ? uint32_t((key - gk) * tok) : kOob;
+      const int nrec = live ? 16 * tok : 0;
+      const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + gbase), 0, nrec, kRsrcWord3);
+      const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + gbase), 0, nrec, kRsrcWord3);
+      if constexpr (NV) {
+        uint32_t kd[2], vd[2];
+        buf_load<8, AUX>(rk, off, kd);
+        buf_load<8, AUX>(rv, off, vd);
+        r.kr[rho] = u32x4{kd[0], kd[1], 0u, 0u};
+        r.vr[rho] = u32x4{vd[0], vd[1], 0u, 0u};
+      } else {
+        uint32_t kd[4], vd[4];
+        buf_load<16, AUX>(rk, off, kd);
+        buf_load<16, AUX>(rv, off, vd);
+        r.kr[rho] = u32x4{kd[0], kd[1], kd[2], kd[3]};
+        r.vr[rho] = u32x4{vd[0], vd[1], vd[2], vd[3]};
+      }
+      if constexpr (NV || MX) {
+        const int snrec = live ? 16 * p.sc_tok : 0;
+        const size_t sbase = pbase + sc_lane + (size_t)(gk & p.bt_mask) * p.sc_tok;
+        const Rsrc rks = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_cache + sbase), 0, snrec, kRsrcWord3);
+        const Rsrc rvs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_cache + sbase), 0, snrec, kRsrcWord3);
+        const uint32_t soff = in_span ? uint32_t((key - gk) * p.sc_tok) : kOob;
+        uint32_t kb8, vb8;
+        buf_load<1, 0>(rks, soff, &kb8);
+        buf_load<1, 0>(rvs, soff, &vb8);
+        r.ksw[rho / 4] |= (kb8 & 0xffu) << (8 * (rho % 4));
+        r.vsw[rho / 4] |= (vb8 & 0xffu) << (8 * (rho % 4));
+      }
+    }
+  };
+  auto load_per_lane = [&](int tt, TileRegs& r) {
+    const int kb = tt * kTileTokens;
+#pragma unroll
+    for (int i = 0; i < (R + 3) / 4; ++i) r.ksw[i] = r.vsw[i] = 0u;
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       const int key = kb + rho * KPI + kk;
-      kr[rho] = u32x4{0u, 0u, 0u, 0u};
-      vr[rho] = u32x4{0u, 0u, 0u, 0u};
-      if (key >= ulo && key < uhi) {
+      r.kr[rho] = u32x4{0u, 0u, 0u, 0u};
+      r.vr[rho] = u32x4{0u, 0u, 0u, 0u};
+      if (tt < te && key >= ulo && key < uhi) {
         const int page = btab[key >> p.bt_shift];
         const size_t pbase = (size_t)page * (size_t)p.page_bytes;
         const size_t off = pbase + (size_t)(key & p.bt_mask) * tok;
         if constexpr (NV) {
           const u32x2 kd = *reinterpret_cast<const u32x2*>(kbase_g + off);
           const u32x2 vd = *reinterpret_cast<const u32x2*>(vbase_g + off);
-          kr[rho] = u32x4{kd.x, kd.y, 0u, 0u};
-          vr[rho] = u32x4{vd.x, vd.y, 0u, 0u};
-          const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
-          ksw[rho / 4] |= uint32_t(p.k_cache[soff]) << (8 * (rho % 4));
-          vsw[rho / 4] |= uint32_t(p.v_cache[soff]) << (8 * (rho % 4));
+          r.kr[rho] = u32x4{kd.x, kd.y, 0u, 0u};
+          r.vr[rho] = u32x4{vd.x, vd.y, 0u, 0u};
         } else {
-          kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
-          vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
-          if constexpr (MX) {
-            const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
-            ksw[rho / 4] |= uint32_t(p.k_cache[soff]) << (8 * (rho % 4));
-            vsw[rho / 4] |= uint32_t(p.v_cache[soff]) << (8 * (rho % 4));
-          }
+          r.kr[rho] = *reinterpret_cast<const u32x4*>(kbase_g + off);
+          r.vr[rho] = *reinterpret_cast<const u32x4*>(vbase_g + off);
+        }
+        if constexpr (NV || MX) {
+          const size_t soff = pbase + sc_lane + (size_t)(key & p.bt_mask) * p.sc_tok;
+          r.ksw[rho / 4] |= uint32_t(p.k_cache[soff]) << (8 * (rho % 4));
+          r.vsw[rho / 4] |= uint32_t(p.v_cache[soff]) << (8 * (rho % 4));
         }
       }
     }
+  };
+  auto scale_of = [&](const uint32_t* sw, int rho) {
+    const uint32_t b = (sw[rho / 4] >> (8 * (rho % 4))) & 0xffu;
+    return MX ? e8m0_to_f32(b) : __builtin_amdgcn_cvt_f32_fp8(int(b), 0);
+  };
+  auto compute_tile = [&](int tt, const TileRegs& r) {
+    const int kb = tt * kTileTokens;
     float x[R][RPG];
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
       float kf[16];
       if constexpr (NV) {
-        fp4x16_to_f32(u32x2{kr[rho].x, kr[rho].y}, kf);
+        fp4x16_to_f32(u32x2{r.kr[rho].x, r.kr[rho].y}, kf);
       } else {
-        const uint32_t kw[4] = {kr[rho].x, kr[rho].y, kr[rho].z, kr[rho].w};
+        const uint32_t kw[4] = {r.kr[rho].x, r.kr[rho].y, r.kr[rho].z, r.kr[rho].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kw[j], false);
@@ -1646,7 +1773,7 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) d = fmaf(kf[j], qf[rr][j], d);
-        if constexpr (NV || MX) d *= scale_of(ksw, rho);
+        if constexpr (NV || MX) d *= scale_of(r.ksw, rho);
 #pragma unroll
         for (int s = 1; s < LPK; s <<= 1) d += xor_shfl(d, s);
         x[rho][rr] = (key >= rows[rr].klo && key < rows[rr].khi) ? d : -INFINITY;
@@ -1673,9 +1800,9 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
     for (int rho = 0; rho < R; ++rho) {
       float vf[16];
       if constexpr (NV) {
-        fp4x16_to_f32(u32x2{vr[rho].x, vr[rho].y}, vf);
+        fp4x16_to_f32(u32x2{r.vr[rho].x, r.vr[rho].y}, vf);
       } else {
-        const uint32_t vw[4] = {vr[rho].x, vr[rho].y, vr[rho].z, vr[rho].w};
+        const uint32_t vw[4] = {r.vr[rho].x, r.vr[rho].y, r.vr[rho].z, r.vr[rho].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vw[j], false);
@@ -1692,10 +1819,40 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
         lsum[rr] += pp;
         // (NVFP4: the block scale of V joins P; a key outside the span has
         // P = 0 and scale 0)
-        const float pv = (NV || MX) ? pp * scale_of(vsw, rho) : pp;
+        const float pv = (NV || MX) ? pp * scale_of(r.vsw, rho) : pp;
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[rr][j] = fmaf(pv, vf[j], acc[rr][j]);
       }
+    }
+  };
+
+  // Two tiles in flight where the registers allow (one query row, or head_dim
+  // 64); with four rows at head_dim 128 or 256 a second tile's registers
+  // would spill, so those load each tile before computing it.
+  constexpr bool kTwoTiles = RPG == 1 || D == 64;
+  if (grouped_pages && !kTwoTiles) {
+    TileRegs ta;
+    for (int tt = ts; tt < te; ++tt) {
+      load_grouped(tt, ta, (tt - ts) & 1);
+      compute_tile(tt, ta);
+    }
+  } else if (grouped_pages) {
+    // two tiles in flight: tile t + 1 loads while tile t is computed
+    TileRegs ta, tb;
+    load_grouped(ts, ta, 0);
+    load_grouped(ts + 1, tb, 1);
+    for (int tt = ts; tt < te; tt += 2) {
+      compute_tile(tt, ta);
+      if (tt + 1 >= te) break;
+      load_grouped(tt + 2, ta, 0);
+      compute_tile(tt + 1, tb);
+      load_grouped(tt + 3, tb, 1);
+    }
+  } else {
+    TileRegs ta;
+    for (int tt = ts; tt < te; ++tt) {
+      load_per_lane(tt, ta);
+      compute_tile(tt, ta);
     }
   }
 
@@ -1758,28 +1915,27 @@ struct MergeArgs {
   const float* sinks;
   uint16_t* out;
   float* lse_out;
-  // Optional: the split plan that wrote the partials, so that a row reads
-  // only the splits its sequence has.  seq_lens == nullptr: num_splits each.
-  const int32_t* seq_lens;
-  const int32_t* chunk;  // the balanced plan's chunk (device word), or nullptr
-  int fixed_chunk;       // the fixed plan's tiles per split
-  int q_len, window, max_seq_len;
+  // Optional: the splits each sequence got (slots 0 .. n - 1 of its rows hold
+  // partials), written by the partial pass; nullptr: every row has num_splits.
+  const int32_t* nsplit;
+  int rows_per_seq;  // B * q_len * Hq rows, q_len * Hq per sequence
 };
 
 // One workgroup per (query row, 64 dims of head_dim); lane l owns dim
 // 64 c + l.  Its W wavefronts take the splits in turn (wavefront w: splits
 // w, w + W, ...) and reduce them to a local (max, sum, weighted sum), which
 // LDS combines when W > 1: rows with many splits so need few dependent
-// round trips.  Each wavefront loads its first LSEs and its first 16 / W
-// partial outputs before the row's split count and the weights are known
-// (the plans fill slots from 0 upwards), which hides a round trip for rows
-// of up to 16 splits; further splits are read only where their weight is
-// nonzero (a ballot over the weights gives their indices, 16 at a time).
+// round trips.  Each wavefront issues the load of its row's split count,
+// its first LSEs and its first 16 / W partial outputs together, before any
+// of them is known (the plans fill slots from 0 upwards): rows of up to 16
+// splits take one round trip; further splits are read only where their
+// weight is nonzero (a ballot over the weights gives their indices, 16 at a
+// time).
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   constexpr int C = D / 64;  // workgroups per row
   constexpr int U = 16;      // partial outputs in flight together per wavefront
-  constexpr int U0 = 16 / W; // of which loaded before the weights are known
+  constexpr int U0 = 16 / W; // loaded before the split count and the weights are known
   __shared__ float red_acc[W][64];
   __shared__ float red_ml[W][2];
   const int row = blockIdx.x / C;
@@ -1787,22 +1943,24 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int S = a.num_splits;
+  // (issued first: the split count is the one value everything else waits on)
+  const int ns_loaded = a.nsplit ? uniform_vload(a.nsplit, row / a.rows_per_seq) : S;
   const float* lrow = a.pl + (size_t)row * S;
   const float* obase = a.po + (size_t)row * S * D + 64 * chunk + lane;
-  // lane i of this wavefront stands for split wv + W * (i0 + i)
+  // lane i of this wavefront stands for split wv + W * (i0 + i).  The first
+  // loads are branch-free (indices clamped to the row's slots, results
+  // selected below), so they all issue before the first wait.
   const int sl0 = wv + W * lane;
-  const float l0 = sl0 < S ? lrow[sl0] : -INFINITY;
+  float l0 = lrow[min(sl0, S - 1)];
   float o0[U0];
 #pragma unroll
-  for (int u = 0; u < U0; ++u) o0[u] = wv + W * u < S ? obase[(size_t)(wv + W * u) * D] : 0.f;
-  int ns = S;
-  if (a.seq_lens) {
-    const int b = row / (a.q_len * a.Hq);
-    const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-    const Span sp = span_of(L, a.q_len, a.window);
-    const int c = a.chunk ? *a.chunk : a.fixed_chunk;
-    ns = __builtin_amdgcn_readfirstlane(splits_of(sp.tile1 - sp.tile0, c, S));
-  }
+  for (int u = 0; u < U0; ++u) o0[u] = obase[(size_t)min(wv + W * u, S - 1) * D];
+  // (nothing below may be scheduled above this point: the split count is
+  // the first value waited for)
+  __builtin_amdgcn_sched_barrier(0);
+  l0 = sl0 < S ? l0 : -INFINITY;
+  // (clamped: a sequence's split count is at least 1 and at most num_splits)
+  const int ns = __builtin_amdgcn_readfirstlane(min(max(ns_loaded, 1), S));
   // this wavefront's splits: wv + W * i for i < nw
   const int nw = ns > wv ? (ns - wv + W - 1) / W : 0;
   float M = lane < nw ? l0 * kLog2e : -INFINITY;
@@ -1932,6 +2090,28 @@ __global__ void debug_lds_tr8_kernel(const uint8_t* src, const int32_t* addr, ui
   reinterpret_cast<u32x2*>(out)[lane] = u32x2{uint32_t(t.x), uint32_t(t.y)};
 }
 
+// Streaming read of n16 16-byte units: workgroup x reads units
+// [x per_wg, (x + 1) per_wg), four loads in flight per lane; the XOR of
+// everything read is stored only in the impossible case that it equals a
+// fixed word, which keeps the loads alive.
+__global__ __launch_bounds__(256) void debug_read_kernel(const u32x4* __restrict__ buf, uint64_t n16,
+                                                         uint64_t per_wg, uint32_t* sink) {
+  const uint64_t base = uint64_t(blockIdx.x) * per_wg;
+  const uint64_t end = base + per_wg < n16 ? base + per_wg : n16;
+  uint32_t acc = 0;
+  for (uint64_t i = base + threadIdx.x; i < end; i += 4 * 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t idx = i + uint64_t(u) * 256;
+      v[u] = idx < end ? __builtin_nontemporal_load(&buf[idx]) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 __global__ void debug_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
@@ -1993,11 +2173,15 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
     }
   } else if (pl.variant != kVariantMfma) {
     if (pl.fmt == FP8PA_KV_NVFP4)
-      partial_dot_kernel<D, FP8PA_KV_NVFP4><<<grid, block, 0, st>>>(prm);
+      partial_dot_kernel<D, FP8PA_KV_NVFP4, kRowsDot><<<grid, block, 0, st>>>(prm);
     else if (pl.fmt == FP8PA_KV_MXFP8)
-      partial_dot_kernel<D, FP8PA_KV_MXFP8><<<grid, block, 0, st>>>(prm);
+      partial_dot_kernel<D, FP8PA_KV_MXFP8, kRowsDot><<<grid, block, 0, st>>>(prm);
+    else if (pl.rpg == 1 && pl.nt)
+      partial_dot_kernel<D, FP8PA_KV_E4M3, 1, 1><<<grid, block, 0, st>>>(prm);
+    else if (pl.rpg == 1)
+      partial_dot_kernel<D, FP8PA_KV_E4M3, 1><<<grid, block, 0, st>>>(prm);
     else
-      partial_dot_kernel<D, FP8PA_KV_E4M3><<<grid, block, 0, st>>>(prm);
+      partial_dot_kernel<D, FP8PA_KV_E4M3, kRowsDot><<<grid, block, 0, st>>>(prm);
   } else if constexpr (D == 64) {
     // non-temporal loads only where a wavefront reads whole lines (paired heads)
     if (pl.lw == 8)
@@ -2165,8 +2349,8 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
   prm.target_items = pl.target_items > 0 ? pl.target_items : 1;
   prm.max_seq_len = shape->max_seq_len;
   prm.min_tiles = pl.min_tiles;
-  prm.chunk_out =
-      pl.direct ? nullptr : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.off_chunk);
+  prm.nsplit_out =
+      pl.direct ? nullptr : reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.off_nsplit);
   prm.bt_shift = pl.bt_shift;
   prm.bt_mask = pl.bt - 1;
   prm.table_stride = shape->block_table_stride;
@@ -2198,12 +2382,8 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
     ma.sinks = sinks;
     ma.out = prm.out;
     ma.lse_out = lse;
-    ma.seq_lens = seq_lens;
-    ma.chunk = prm.balanced ? prm.chunk_out : nullptr;
-    ma.fixed_chunk = pl.tps;
-    ma.q_len = pl.q_len;
-    ma.window = prm.window;
-    ma.max_seq_len = prm.max_seq_len;
+    ma.nsplit = prm.nsplit_out;
+    ma.rows_per_seq = pl.q_len * pl.Hq;
     e = launch_merge(pl.D, ma, cu, hs);
     if (e != hipSuccess) return FP8PA_ERR_HIP;
   }
@@ -2266,7 +2446,8 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
   ma.sinks = sinks;
   ma.out = static_cast<uint16_t*>(out);
   ma.lse_out = lse;
-  ma.seq_lens = nullptr;  // every row merges all num_splits slots
+  ma.nsplit = nullptr;  // every row merges all num_splits slots
+  ma.rows_per_seq = 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
   const int cu = cu_count_of(dev);
@@ -2315,6 +2496,22 @@ fp8pa_status fp8pa_debug_lds_tr8(const uint8_t* lds_bytes, const int32_t* row_ad
   if ((reinterpret_cast<uintptr_t>(lds_bytes) | reinterpret_cast<uintptr_t>(out)) & 15)
     return FP8PA_ERR_MISALIGNED;
   debug_lds_tr8_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(lds_bytes, row_addr, out);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!sink || (bytes > 0 && !buf)) return FP8PA_ERR_INVALID_ARG;
+  if (bytes % 16 != 0) return FP8PA_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return FP8PA_ERR_MISALIGNED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
+  const int cu = cu_count_of(dev);
+  if (cu < 1) return FP8PA_ERR_HIP;
+  const uint64_t n16 = bytes / 16;
+  const unsigned grid = bytes == 0 ? 1u : unsigned(2 * cu);
+  const uint64_t per_wg = (n16 + grid - 1) / grid;
+  debug_read_kernel<<<dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(buf), n16, per_wg, sink);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

@@ -86,7 +86,7 @@ struct Plan {
   int32_t direct;          // 1: the partial kernel writes the final output (one split)
   size_t ws_bytes;         // 0 when direct
   size_t off_lse;          // byte offset of partial_lse in the workspace
-  size_t off_chunk;        // byte offset of the balanced plan's chunk word
+  size_t off_nsplit;       // byte offset of the per-sequence split counts (int32 [B])
   int32_t min_tiles;       // balanced plan: chunk floor (64 keys per query row)
 };
 

@@ -456,3 +456,13 @@ def test_cache_write_checks_pointers_before_the_gpu():
         assert _call_write(s, **{name: addr}) == _lib.FP8PA_ERR_MISALIGNED, name
     # nothing to write: no pointer is needed and nothing is queued
     assert _call_write(_write_shape(num_tokens=0), key=None, value=None, slots=None) == _lib.FP8PA_OK
+
+
+def test_stream_read_diagnostic_argument_checks():
+    """fp8pa_debug_stream_read rejects its bad arguments before any GPU call."""
+    lib = _lib.lib()
+    sink = ctypes.c_uint32(0)
+    assert lib.fp8pa_debug_stream_read(16, 64, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(None, 64, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(16, 65, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(24, 64, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_MISALIGNED

@@ -49,6 +49,12 @@ CONFIGS = {
     5: dict(name="mtp_q4", B=256, q_len=4, Hq=32, Hkv=8, D=128, bt=16,
             seq=("uniform", 1024, 4096), table="perm", pool=None, scale=("tensor", 0.05),
             window=2048, sinks=True, sm_scale=1.0 / math.sqrt(128)),
+    # Not one of the five named workloads: the ragged GQA batch with one query
+    # head per kv head (MHA decode), the shape the VALU dot-product kernel serves.
+    6: dict(name="mha_decode", B=16, q_len=1, Hq=8, Hkv=8, D=128, bt=16,
+            seq=("uniform", 1024, 8192), table="perm", pool=8192,
+            scale=("per_head", 0.02, 0.1), window=0, sinks=False,
+            sm_scale=1.0 / math.sqrt(128)),
 }
 
 
