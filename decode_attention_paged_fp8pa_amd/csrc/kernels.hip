@@ -1667,6 +1667,10 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
     // (decoded where used: fewer live registers than one float per token)
     uint32_t ksw[(R + 3) / 4], vsw[(R + 3) / 4];
   };
+  // (descriptor bases are wave-uniform: the page and the kv head; the lane's
+  // token and chunk go into the per-lane offset)
+  const uint8_t* khead = p.k_cache + (size_t)w.g * (size_t)p.head_stride;
+  const uint8_t* vhead = p.v_cache + (size_t)w.g * (size_t)p.head_stride;
   auto load_grouped = [&](int tt, TileRegs& r, int odd) {
     const int kb = tt * kTileTokens;
     const int step = ((tt - ts) >> 1) & 63;
@@ -1682,10 +1686,10 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
       const size_t gbase = pbase + (size_t)(gk & p.bt_mask) * tok;
       const int key = kb + rho * KPI + kk;
       const bool in_span = key >= ulo && key < uhi;
-      const uint32_t off = in_span ? uint32_t((key - gk) * tok) : kOob;
+      const uint32_t off = in_span ? uint32_t((key - gk) * tok + KWB * c) : kOob;
       const int nrec = live ? 16 * tok : 0;
-      const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_g + gbase), 0, nrec, kRsrcWord3);
-      const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_g + gbase), 0, nrec, kRsrcWord3);
+      const Rsrc rk = __builtin_amdgcn_make_buffer_rsrc((void*)(khead + gbase), 0, nrec, kRsrcWord3);
+      const Rsrc rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vhead + gbase), 0, nrec, kRsrcWord3);
       if constexpr (NV) {
         uint32_t kd[2], vd[2];
         buf_load<8, AUX>(rk, off, kd);
@@ -1701,10 +1705,11 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
       }
       if constexpr (NV || MX) {
         const int snrec = live ? 16 * p.sc_tok : 0;
-        const size_t sbase = pbase + sc_lane + (size_t)(gk & p.bt_mask) * p.sc_tok;
+        const size_t sbase = pbase + (size_t)p.sc_off + (size_t)w.g * (size_t)p.sc_head +
+                             (size_t)(gk & p.bt_mask) * p.sc_tok;
         const Rsrc rks = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_cache + sbase), 0, snrec, kRsrcWord3);
         const Rsrc rvs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_cache + sbase), 0, snrec, kRsrcWord3);
-        const uint32_t soff = in_span ? uint32_t((key - gk) * p.sc_tok) : kOob;
+        const uint32_t soff = in_span ? uint32_t((key - gk) * p.sc_tok + (MX ? c / 2 : c)) : kOob;
         uint32_t kb8, vb8;
         buf_load<1, 0>(rks, soff, &kb8);
         buf_load<1, 0>(rvs, soff, &vb8);
