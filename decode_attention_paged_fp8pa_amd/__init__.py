@@ -33,6 +33,7 @@ from ._lib import (  # noqa: F401
     fp8pa_cache_write,
     fp8pa_debug_e4m3_to_f32,
     fp8pa_debug_lds_tr8,
+    fp8pa_debug_lds_tr16,
     fp8pa_debug_mxfp8,
     fp8pa_debug_mfma_fp8,
     fp8pa_debug_nvfp4,

@@ -2095,6 +2095,21 @@ __global__ void debug_lds_tr8_kernel(const uint8_t* src, const int32_t* addr, ui
   reinterpret_cast<u32x2*>(out)[lane] = u32x2{uint32_t(t.x), uint32_t(t.y)};
 }
 
+// One transposing 16-bit LDS read per lane over a 4 KB copy of `src`; row
+// addresses are clamped to 8-byte-aligned offsets inside the copy.
+__global__ void debug_lds_tr16_kernel(const uint8_t* src, const int32_t* addr, uint8_t* out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4096];
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < 4096 / 16; i += 64)
+    reinterpret_cast<u32x4*>(lds)[i] = reinterpret_cast<const u32x4*>(src)[i];
+  __syncthreads();
+  const int a = min(max(addr[lane], 0), 4096 - 8) & ~7;
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds + a));
+  reinterpret_cast<u32x2*>(out)[lane] =
+      u32x2{uint32_t(uint16_t(t.x)) | (uint32_t(uint16_t(t.y)) << 16), uint32_t(uint16_t(t.z)) | (uint32_t(uint16_t(t.w)) << 16)};
+}
+
 // Streaming read of n16 16-byte units: workgroup x reads units
 // [x per_wg, (x + 1) per_wg), four loads in flight per lane; the XOR of
 // everything read is stored only in the impossible case that it equals a
@@ -2517,6 +2532,14 @@ fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, uint32_t* 
   const uint64_t per_wg = (n16 + grid - 1) / grid;
   debug_read_kernel<<<dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const u32x4*>(buf), n16, per_wg, sink);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_lds_tr16(const uint8_t* lds_bytes, const int32_t* row_addr, uint8_t* out,
+                                  void* stream) {
+  if (!lds_bytes || !row_addr || !out) return FP8PA_ERR_INVALID_ARG;
+  if (!aligned(lds_bytes, 16) || !aligned(out, 16) || !aligned(row_addr, 4)) return FP8PA_ERR_MISALIGNED;
+  debug_lds_tr16_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(lds_bytes, row_addr, out);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

@@ -73,6 +73,14 @@ fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out,
 fp8pa_status fp8pa_debug_lds_tr8(const uint8_t* lds_bytes, const int32_t* row_addr, uint8_t* out,
                                  void* stream);
 
+/* As fp8pa_debug_lds_tr8, with one ds_read_b64_tr_b16 per lane (16-bit
+ * elements, four per lane): out[8 l .. 8 l + 7] holds lane l's four result
+ * elements, little-endian.  The mapping the kernels rely on: with
+ * l = 16 g + 4 h + c (c < 4, h < 4), element t of lane l is element c of the
+ * 8-byte row named by lane 16 g + 4 t + h, for t < 4. */
+fp8pa_status fp8pa_debug_lds_tr16(const uint8_t* lds_bytes, const int32_t* row_addr, uint8_t* out,
+                                  void* stream);
+
 /* One launch that reads `bytes` bytes of `buf` (16-byte aligned, bytes a
  * multiple of 16) and nothing else: two workgroups of 256 lanes per compute
  * unit, each streaming one contiguous chunk with 16-byte non-temporal loads,

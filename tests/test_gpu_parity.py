@@ -111,6 +111,27 @@ def test_hw_lds_transposing_read(seed):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_hw_lds_transposing_read_16bit(seed):
+    """The lane mapping of ds_read_b64_tr_b16 that the LDS-shared kernels
+    build PV's bf16 V^T operands with: lane 16 g + 4 h + c gets, as its
+    element t, 16-bit element c of the 8-byte row named by lane
+    16 g + 4 t + h."""
+    rng = np.random.default_rng(100 + seed)
+    src = rng.integers(0, 256, size=4096, dtype=np.uint8)
+    addr = (rng.integers(0, 4096 // 8, size=64) * 8).astype(np.int32)
+    out = torch.empty(512, dtype=torch.uint8, device="cuda")
+    fp.fp8pa_debug_lds_tr16(torch.from_numpy(src).cuda(), torch.from_numpy(addr).cuda(), out)
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
+    src16 = src.view(np.uint16)
+    want = np.empty((64, 4), dtype=np.uint16)
+    for lane in range(64):
+        g, h, c = lane // 16, (lane % 16) // 4, lane % 4
+        for t in range(4):
+            want[lane, t] = src16[addr[16 * g + 4 * t + h] // 2 + c]
+    assert np.array_equal(got, want), (got[:8], want[:8])
+
+
 # ------------------------------------------------------- small, every element
 
 SMALL = {
