@@ -120,8 +120,10 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
   // head_dim 128; 32 rows 106 us against 137 us).  Two groups at head_dim
   // 64 stay with the two row blocks above, which need no LDS (68 us
   // against 85 us shared).
+  // (not with head_dim scale groups: their third query part would not fit
+  // the LDS-shared kernels' registers)
   p.lw = 0;
-  if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.D <= 128) {
+  if (fp8_mfma && p.ds == 1 && p.pr == 1 && p.D <= 128 && s->k_groups <= 1) {
     const int32_t rg1 = int32_t(ceil_div(p.rows, kRowsMfma));
     if (rg1 % 8 == 0) p.lw = 8;
     else if (rg1 % 4 == 0) p.lw = 4;

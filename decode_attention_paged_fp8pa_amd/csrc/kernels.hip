@@ -58,6 +58,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -533,10 +534,13 @@ partial_mfma_kernel(Params p) {
   // wavefronts of a workgroup.
   __shared__ f32x4 xch[DS == 2 ? kMaxWgWaves * 2 * 64 * 2 : 1];
   // LW > 0: the LW wavefronts of a workgroup are LW row groups of one kv
-  // head and share each K/V tile through a two-slot LDS ring: [slot][K then
-  // V][32 tokens][D + 16 bytes] (rows padded against bank conflicts).
+  // head and share each K/V tile through a two-slot LDS ring: per slot, K as
+  // [32 tokens][D + 16 bytes] of E4M3, then V as [32 tokens][2 D + 32 bytes]
+  // of bf16, widened once while staging instead of once per wavefront (rows
+  // padded so that the transposing reads below hit distinct banks).
   constexpr int LROW = D + 16;
-  constexpr int LSLOT = 2 * kTileTokens * LROW;
+  constexpr int LROWV = 2 * D + 32;
+  constexpr int LSLOT = kTileTokens * (LROW + LROWV);
   __shared__ __attribute__((aligned(16))) uint8_t ltile[LW ? 2 * LSLOT : 16];
   // With the ring, PV's V^T operands are built by transposing LDS reads
   // instead of byte permutes of each wavefront's own copy.
@@ -593,8 +597,10 @@ partial_mfma_kernel(Params p) {
   // many query rows per sequence (chunked prefill) a row group's causal
   // range ends before the sequence does.
   // (LW > 0: the range of the workgroup's rows, the same for all its wavefronts)
-  const int tq0 = LW ? ((w.rg / (LW > 0 ? LW : 1)) * (LW > 0 ? LW : 1) * kRowsMfma) / p.G : qmin;
-  const int tq1 = LW ? (min((w.rg / (LW > 0 ? LW : 1) + 1) * (LW > 0 ? LW : 1) * kRowsMfma, p.rows) - 1) / p.G : qmax;
+  constexpr int kWgRows = (LW > 0 ? LW : 1) * NB * kRowsMfma;
+  const int wg0 = (w.rg / (LW > 0 ? LW : 1)) * kWgRows;
+  const int tq0 = LW ? wg0 / p.G : qmin;
+  const int tq1 = LW ? (min(wg0 + kWgRows, p.rows) - 1) / p.G : qmax;
   const TileRange tr = rows_tiles(p, L, tq0, tq1, w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
   Row row[NB];
@@ -621,7 +627,9 @@ partial_mfma_kernel(Params p) {
   float cr[NB];                           // score scales into log2 units
 
   // ---- online softmax state (log2 units); the sink enters as a score whose
-  // value vector is zero when this split writes the final output.
+  // value vector is zero when this split writes the final output.  (The
+  // denominator sums the fp32 weights: their bf16 roundings, which O gets,
+  // would move the LSE of a row with one dominant key by up to 2^-9.)
   float m[NB], lsum[NB];
   f32x4 O[NB][S];
 #pragma unroll
@@ -724,95 +732,50 @@ partial_mfma_kernel(Params p) {
   };
 
   // One tile: S^T = K Q^T, mask, online softmax with a lazy reference max,
-  // P = hi + lo E4M3 parts, O^T += V^T P^T.  The V^T operands are built
-  // once and, with the K operands, serve every row block, which then runs
-  // start to finish before the next (one block's temporaries live at a time).
-  auto compute_tile = [&](int tt, TileRegs& r, int slot) {
-    const int kb = tt * kTileTokens;
-    const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
-    long vt[S];
-    if constexpr (TRV) {
-      // V^T operands straight from the LDS tile with gfx950's transposing
-      // read: in each 16-lane group, lane r names an 8-byte row (token
-      // kap(qd, r / 2), dims 16 e + 8 (r & 1) ...), and lane 8 h + c receives
-      // byte c of rows h, h + 2, ..., h + 14.  So byte j of operand e =
-      // V[kap(qd, j)][16 e + n].  (Tokens outside the span were written as
-      // zeros, so no byte needs clearing here.)
-      const int rt = n >> 1;
-      const int tk = rt < 4 ? 4 * qd + rt : 16 + 4 * qd + (rt - 4);
-      const uint8_t* vrow = ltile + slot * LSLOT + kTileTokens * LROW + tk * LROW + 8 * (n & 1);
+  // P in bf16, O^T += V^T P^T, in three parts: qk_block (the MFMAs of one
+  // row block's scores), soft_block (its softmax step, giving P) and the PV
+  // MFMAs.  The V^T operands are built once and, with the K operands, serve
+  // every row block.
+  // Raw scores of row block b: lane (n, qd) gets tokens kap(qd, 0..3) in sa
+  // and kap(qd, 4..7) in sb of row n.
+  auto qk_block = [&](const TileRegs& r, int b, f32x4& sa, f32x4& sb) {
+    sa = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (the third query part exists only with head_dim scale groups, which
+    // the LDS-shared kernels do not take)
+    const bool third = LW == 0 && p.k_groups > 1;
+    if constexpr (KSTEPS == 4) {
+      // A 128-dim slice: one 16x16x128 FP8 MFMA per query part (gfx950's
+      // full-rate form; unit E8M0 scales).  A lane's 32 K bytes and its 32
+      // query bytes cover the same dims, which is all the sum needs.
+      i32x8 ka, kbv, qh, ql;
 #pragma unroll
-      for (int e = 0; e < S; ++e) {
-        const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2*)(vrow + 16 * e));
-        vt[e] = as_long(uint32_t(t.x), uint32_t(t.y));
+      for (int i = 0; i < 8; ++i) {
+        ka[i] = int(r.k[0][i]);
+        kbv[i] = int(r.k[1][i]);
       }
-    } else {
-    if (edge) {
-      // The V bytes of a token outside the sequence's attended span (read
-      // whole with its group, possibly NaN codes) become 0, since P = 0
-      // times NaN is NaN.
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-        const bool in_span = key >= ulo && key < uhi;
-#pragma unroll
-        for (int e = 0; e < SW; ++e) r.v[j][e] = in_span ? r.v[j][e] : 0u;
+      for (int c = 0; c < 4; ++c) {
+        qh[2 * c] = int(uint32_t(qhi[b][c]));
+        qh[2 * c + 1] = int(uint32_t(uint64_t(qhi[b][c]) >> 32));
+        ql[2 * c] = int(uint32_t(qlo[b][c]));
+        ql[2 * c + 1] = int(uint32_t(uint64_t(qlo[b][c]) >> 32));
       }
-    }
-    // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
-#pragma unroll
-    for (int wd = 0; wd < SW; ++wd) {
-      uint32_t lo4[4], hi4[4];
-      transpose4x4(r.v[0][wd], r.v[1][wd], r.v[2][wd], r.v[3][wd], lo4);
-      transpose4x4(r.v[4][wd], r.v[5][wd], r.v[6][wd], r.v[7][wd], hi4);
-#pragma unroll
-      for (int x4 = 0; x4 < 4; ++x4) vt[4 * wd + x4] = as_long(lo4[x4], hi4[x4]);
-    }
-    }
-    // With two row blocks the V^T operands are widened to bf16 once and
-    // serve both blocks.
-    bf16x8 vtb[NB > 1 ? S : 1];
-    if constexpr (NB > 1) {
-#pragma unroll
-      for (int e = 0; e < S; ++e)
-        vtb[e] = e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KSTEPS == 4) {
-        // A 128-dim slice: one 16x16x128 FP8 MFMA per query part (gfx950's
-        // full-rate form; unit E8M0 scales).  A lane's 32 K bytes and its 32
-        // query bytes cover the same dims, which is all the sum needs.
-        i32x8 ka, kbv, qh, ql;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ka[i] = int(r.k[0][i]);
-          kbv[i] = int(r.k[1][i]);
-        }
+      sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh, sa, 0, 0, 0, 127, 0, 127);
+      sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, qh, sb, 0, 0, 0, 127, 0, 127);
+      sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql, sa, 0, 0, 0, 127, 0, 127);
+      sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, ql, sb, 0, 0, 0, 127, 0, 127);
+      if (third) {
+        i32x8 q3;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          qh[2 * c] = int(uint32_t(qhi[b][c]));
-          qh[2 * c + 1] = int(uint32_t(uint64_t(qhi[b][c]) >> 32));
-          ql[2 * c] = int(uint32_t(qlo[b][c]));
-          ql[2 * c + 1] = int(uint32_t(uint64_t(qlo[b][c]) >> 32));
+          q3[2 * c] = int(uint32_t(qlo2[b][c]));
+          q3[2 * c + 1] = int(uint32_t(uint64_t(qlo2[b][c]) >> 32));
         }
-        sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh, sa, 0, 0, 0, 127, 0, 127);
-        sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, qh, sb, 0, 0, 0, 127, 0, 127);
-        sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql, sa, 0, 0, 0, 127, 0, 127);
-        sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, ql, sb, 0, 0, 0, 127, 0, 127);
-        if (p.k_groups > 1) {
-          i32x8 q3;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            q3[2 * c] = int(uint32_t(qlo2[b][c]));
-            q3[2 * c + 1] = int(uint32_t(uint64_t(qlo2[b][c]) >> 32));
-          }
-          sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q3, sa, 0, 0, 0, 127, 0, 127);
-          sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, q3, sb, 0, 0, 0, 127, 0, 127);
-        }
-      } else {
+        sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q3, sa, 0, 0, 0, 127, 0, 127);
+        sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, q3, sb, 0, 0, 0, 127, 0, 127);
+      }
+    } else {
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) {
         const long ka = as_long(r.k[0][2 * c], r.k[0][2 * c + 1]);
@@ -821,113 +784,191 @@ partial_mfma_kernel(Params p) {
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qhi[b][c], sb, 0, 0, 0);
         sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo[b][c], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo[b][c], sb, 0, 0, 0);
-        if (p.k_groups > 1) {
+        if (third) {
           sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka, qlo2[b][c], sa, 0, 0, 0);
           sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kbv, qlo2[b][c], sb, 0, 0, 0);
         }
       }
-      }
-      // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc
-      // (one head_dim slice per wavefront), or, when two wavefronts split
-      // head_dim, the sum of both slices' scaled scores exchanged through LDS.
-      float sv[8];
-      float csc = cr[b];
-      if constexpr (DS == 2) {
-        const int parity = (tt - ts) & 1;
-        const int wv = int(threadIdx.x >> 6);
-        f32x4* own = &xch[((wv * 2 + parity) * 64 + lane) * 2];
-        own[0] = sa * csc;
-        own[1] = sb * csc;
-        __syncthreads();
-        const f32x4* other = &xch[(((wv ^ 1) * 2 + parity) * 64 + lane) * 2];
-        const f32x4 oa = other[0], ob = other[1];
+    }
+  };
+
+  // The softmax step of row block b on tile tt's raw scores; returns P.
+  auto soft_block = [&](int tt, int b, const f32x4& sa, const f32x4& sb) {
+    const int kb = tt * kTileTokens;
+    const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
+    // Scores of this lane's 8 tokens: raw MFMA sums scaled later by csc
+    // (one head_dim slice per wavefront), or, when two wavefronts split
+    // head_dim, the sum of both slices' scaled scores exchanged through LDS.
+    float sv[8];
+    float csc = cr[b];
+    if constexpr (DS == 2) {
+      const int parity = (tt - ts) & 1;
+      const int wv = int(threadIdx.x >> 6);
+      f32x4* own = &xch[((wv * 2 + parity) * 64 + lane) * 2];
+      own[0] = sa * csc;
+      own[1] = sb * csc;
+      __syncthreads();
+      const f32x4* other = &xch[(((wv ^ 1) * 2 + parity) * 64 + lane) * 2];
+      const f32x4 oa = other[0], ob = other[1];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sv[j] = sa[j] * csc + oa[j];
-          sv[j + 4] = sb[j] * csc + ob[j];
-        }
-        csc = 1.f;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sv[j] = sa[j];
-          sv[j + 4] = sb[j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = sa[j] * csc + oa[j];
+        sv[j + 4] = sb[j] * csc + ob[j];
       }
+      csc = 1.f;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = sa[j];
+        sv[j + 4] = sb[j];
+      }
+    }
+    if (edge) {
+      // a token this row does not attend scores -inf
+      // (the barrier keeps this a branch: as selects it would run on every
+      // tile, and only a sequence's first and last tiles need it)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+        sv[j] = (key >= row[b].klo && key < row[b].khi) ? sv[j] : -INFINITY;
+      }
+    }
+    // Lazy reference max: move m only when this tile exceeds it by more
+    // than kLazy (log2 units), so most tiles skip the O rescale; P stays
+    // <= 2^kLazy.  Only then is the row's max over its four lane groups
+    // needed (csc > 0, so the scaled max is the max of the scaled).
+    const float ms = max3_nn(max3_nn(sv[0], sv[1], sv[2]), max3_nn(sv[3], sv[4], sv[5]), max_nn(sv[6], sv[7]));
+    if (__builtin_amdgcn_ballot_w64(ms * csc > m[b] + kLazy) != 0) {
+      const float mx = max_over_groups_nn(ms) * csc;
+      const bool bump = mx > m[b] + kLazy;  // the same in the row's four lanes
+      const float mnew = bump ? mx : m[b];
+      const float alpha = bump ? exp2_fast(m[b] - mnew) : 1.f;
+      lsum[b] *= alpha;
+#pragma unroll
+      for (int e = 0; e < S; ++e) O[b][e] *= alpha;
+      m[b] = mnew;
+    }
+    const float noff = m[b] == -INFINITY ? 0.f : -m[b];
+    float pj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
+    lsum[b] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+    // P in bf16 (round to nearest even): 2^-9 relative error per weight at
+    // any magnitude, so a weight far below the row's max still reaches O
+    // (its mass is in lsum as well).
+    bf16x8 P;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
+      P[j] = h.x;
+      P[j + 1] = h.y;
+    }
+    return P;
+  };
+
+  // PV from the bf16 LDS tile in `slot` (LW > 0), with gfx950's 16-bit
+  // transposing read: in each 16-lane group, lane r names an 8-byte row
+  // (token 4 qd + r / 4, dims 16 e + 4 (r & 3) ...), and lane 4 h + c
+  // receives element c of rows h, h + 4, h + 8, h + 12.  So element t of the
+  // read = V[4 qd + t][16 e + n], and a second read 16 tokens on gives
+  // elements 4..7: operand e holds V[kap(qd, j)][16 e + n], read once for
+  // every row block.  (Tokens outside the span were written as zeros, so
+  // nothing needs clearing.)
+  auto pv_lds = [&](int slot, const bf16x8 (&Pb)[NB]) {
+    const uint8_t* vrow = ltile + slot * LSLOT + kTileTokens * LROW + (4 * qd + (n >> 2)) * LROWV + 8 * (n & 3);
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(vrow + 32 * e));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(vrow + 16 * LROWV + 32 * e));
+      const bf16x8 vb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, Pb[b], O[b][e], 0, 0, 0);
+    }
+  };
+
+  // One whole tile from registers (LW = 0) or from LDS slot `slot`.
+  auto compute_tile = [&](int tt, TileRegs& r, int slot) {
+    const int kb = tt * kTileTokens;
+    const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
+    long vt[TRV ? 1 : S];
+    if constexpr (!TRV) {
       if (edge) {
-        // a token this row does not attend scores -inf
+        // The V bytes of a token outside the sequence's attended span (read
+        // whole with its group, possibly NaN codes) become 0, since P = 0
+        // times NaN is NaN.
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
-          sv[j] = (key >= row[b].klo && key < row[b].khi) ? sv[j] : -INFINITY;
+          const bool in_span = key >= ulo && key < uhi;
+#pragma unroll
+          for (int e = 0; e < SW; ++e) r.v[j][e] = in_span ? r.v[j][e] : 0u;
         }
       }
-      float ms = max3_nn(max3_nn(sv[0], sv[1], sv[2]), max3_nn(sv[3], sv[4], sv[5]), max_nn(sv[6], sv[7]));
-      ms = max_over_groups_nn(ms);
-      const float mx = ms * csc;  // csc > 0, so the scaled max is the max of the scaled
-      // Lazy reference max: move m only when this tile exceeds it by more
-      // than kLazy (log2 units), so most tiles skip the O rescale; P stays
-      // <= 2^kLazy.
-      const bool bump = mx > m[b] + kLazy;
-      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
-        const float mnew = bump ? mx : m[b];
-        const float alpha = bump ? exp2_fast(m[b] - mnew) : 1.f;
-        lsum[b] *= alpha;
+      // V^T operands: byte j of operand e = V[kap(qd, j)][S * n + e]
 #pragma unroll
-        for (int e = 0; e < S; ++e) O[b][e] *= alpha;
-        m[b] = mnew;
+      for (int wd = 0; wd < SW; ++wd) {
+        uint32_t lo4[4], hi4[4];
+        transpose4x4(r.v[0][wd], r.v[1][wd], r.v[2][wd], r.v[3][wd], lo4);
+        transpose4x4(r.v[4][wd], r.v[5][wd], r.v[6][wd], r.v[7][wd], hi4);
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) vt[4 * wd + x4] = as_long(lo4[x4], hi4[x4]);
       }
-      const float noff = m[b] == -INFINITY ? 0.f : -m[b];
-      float pj[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], csc, noff));
-      lsum[b] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
-
-      // P in bf16 (round to nearest even): 2^-9 relative error per weight at
-      // any magnitude, so a weight far below the row's max still reaches O
-      // (its mass is in lsum as well).
-      bf16x8 P;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
-        P[j] = h.x;
-        P[j + 1] = h.y;
-      }
-#pragma unroll
-      for (int e = 0; e < S; ++e) {
-        const bf16x8 vb = NB > 1 ? vtb[e] : e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
-        O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, P, O[b][e], 0, 0, 0);
-      }
-      // keep the scheduler from interleaving blocks (their temporaries would
-      // all be live at once)
-      if constexpr (NB > 1) __builtin_amdgcn_sched_barrier(0);
     }
+    // With two row blocks the V^T operands are widened to bf16 once and
+    // serve both blocks.
+    bf16x8 vtb[NB > 1 && !TRV ? S : 1];
+    if constexpr (NB > 1 && !TRV) {
+#pragma unroll
+      for (int e = 0; e < S; ++e)
+        vtb[e] = e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
+    }
+    bf16x8 Pb[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      f32x4 sa, sb;
+      qk_block(r, b, sa, sb);
+      Pb[b] = soft_block(tt, b, sa, sb);
+      if constexpr (!TRV) {
+#pragma unroll
+        for (int e = 0; e < S; ++e) {
+          const bf16x8 vb = NB > 1 ? vtb[e] : e4m3x8_to_bf16(uint32_t(vt[e]), uint32_t(uint64_t(vt[e]) >> 32), 1.0f);
+          O[b][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, Pb[b], O[b][e], 0, 0, 0);
+        }
+        // keep the scheduler from interleaving blocks (their temporaries
+        // would all be live at once)
+        if constexpr (NB > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (TRV) pv_lds(slot, Pb);
   };
   // Two register buffers in turn: while one tile computes, the next tile's
   // loads are in flight (8 KB per wavefront at D = 128).  Deeper pipelines
   // measured slower on MI355X: more than ~8 KB in flight per wavefront only
   // adds queueing in the memory system.
   TileRegs ta, tb;
-  // LDS staging (LW > 0): this lane's CH bytes of a tile; a wavefront's
-  // chunks lie in one 16-token group of K or of V
-  constexpr int LWS = LW > 0 ? LW : 1;
-  // A tile is four regions (K group A, K group B, V group A, V group B) of
-  // 16 D bytes.  With 4 or 8 wavefronts each wavefront's lanes lie in one
-  // region, CH bytes each; with 2, each wavefront covers two regions.
-  constexpr int RPW = LWS >= 4 ? 1 : 4 / LWS;  // regions per wavefront
-  constexpr int CH = LWS >= 4 ? 2 * kTileTokens * D / (64 * LWS) : 16 * D / 64;
+  // LDS staging (LW > 0).  A tile is four regions (K group A, K group B, V
+  // group A, V group B) of 16 tokens x D bytes.  The workgroup's wavefronts
+  // form two halves that stage alternate tiles: half h loads the tiles t with
+  // (t - ts) & 1 == h, each of its LW / 2 wavefronts RPW whole regions, a
+  // lane CH = D / 4 bytes of one token per region.  A tile is loaded three
+  // loop steps before it is computed and written into LDS one step before,
+  // so the loads have two steps to arrive, and a wavefront never has more
+  // than its own one set in flight (its waits are exact).
+  constexpr int LWS = LW > 0 ? LW : 2;
+  constexpr int RPW = 8 / LWS;  // regions per wavefront
+  constexpr int CH = D / 4;
   // (uniform over the wavefront; saying so keeps the page choice and the
   // buffer descriptor in scalar registers)
   const int swv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  int sreg[RPW], stok[RPW], scol[RPW];
+  const int shalf = swv / (LWS / 2);
+  const int stok = lane >> 2, scol = (lane & 3) * CH;
+  int sreg[RPW];
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    sreg[rr] = LWS >= 4 ? (swv * 64 * CH) / (16 * D) : swv * RPW + rr;
-    const int off = LWS >= 4 ? ((swv * 64 + lane) * CH) % (16 * D) : lane * CH;
-    stok[rr] = off / D;
-    scol[rr] = off % D;
-  }
-  uint32_t sR[RPW][CH / 4 > 0 ? CH / 4 : 1];
+  for (int rr = 0; rr < RPW; ++rr) sreg[rr] = (swv % (LWS / 2)) * RPW + rr;
+  uint32_t sR[RPW][CH / 4];
   auto stage_load = [&](int t) {
     const int step = ((t - ts) >> 1) & 63;
     const int podd = (t - ts) & 1;
@@ -944,27 +985,35 @@ partial_mfma_kernel(Params p) {
       const size_t base = (size_t)page * (size_t)p.page_bytes + (size_t)(gk & p.bt_mask) * tok;
       const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc((void*)((skv ? vbase_g : kbase_g) + base), 0,
                                                         live ? 16 * tok : 0, kRsrcWord3);
-      buf_load<CH, 0>(rs, uint32_t(stok[rr] * tok + scol[rr]), sR[rr]);
+      buf_load<CH, 0>(rs, uint32_t(stok * tok + scol), sR[rr]);
     }
   };
   // `t` is the tile the chunk belongs to: bytes of a token outside the
   // sequence's attended span (read whole with its 16-token group, possibly
-  // NaN codes) go into LDS as zeros, since P = 0 times NaN is NaN.
+  // NaN codes) go into LDS as zeros, since P = 0 times NaN is NaN.  V bytes
+  // go in widened to bf16 (exact).
   auto stage_write = [&](int slot, int t) {
+    // (uniform: a tile wholly inside the span needs no clearing)
+    const bool whole = t * kTileTokens >= ulo && (t + 1) * kTileTokens <= uhi;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
-      const int skv = sreg[rr] >> 1, sgrp = sreg[rr] & 1;
-      uint8_t* dst =
-          ltile + slot * LSLOT + skv * (kTileTokens * LROW) + (16 * sgrp + stok[rr]) * LROW + scol[rr];
-      const int key = t * kTileTokens + 16 * sgrp + stok[rr];
-      const uint32_t keep = (key >= ulo && key < uhi) ? ~0u : 0u;
-      if constexpr (CH == 8) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{sR[rr][0] & keep, sR[rr][1] & keep};
+      const int skv = sreg[rr] >> 1, sgrp = sreg[rr] & 1;  // uniform over the wavefront
+      if (!whole) {
+        const int key = t * kTileTokens + 16 * sgrp + stok;
+        const bool in_span = key >= ulo && key < uhi;
+#pragma unroll
+        for (int i = 0; i < CH / 4; ++i) sR[rr][i] = in_span ? sR[rr][i] : 0u;
+      }
+      if (skv) {
+        uint8_t* dst = ltile + slot * LSLOT + kTileTokens * LROW + (16 * sgrp + stok) * LROWV + 2 * scol;
+#pragma unroll
+        for (int i = 0; i < CH / 8; ++i)
+          reinterpret_cast<bf16x8*>(dst)[i] = e4m3x8_to_bf16(sR[rr][2 * i], sR[rr][2 * i + 1], 1.0f);
       } else {
+        uint8_t* dst = ltile + slot * LSLOT + (16 * sgrp + stok) * LROW + scol;
 #pragma unroll
         for (int i = 0; i < CH / 16; ++i)
-          reinterpret_cast<u32x4*>(dst)[i] = u32x4{sR[rr][4 * i] & keep, sR[rr][4 * i + 1] & keep,
-                                                   sR[rr][4 * i + 2] & keep, sR[rr][4 * i + 3] & keep};
+          reinterpret_cast<u32x4*>(dst)[i] = u32x4{sR[rr][4 * i], sR[rr][4 * i + 1], sR[rr][4 * i + 2], sR[rr][4 * i + 3]};
       }
     }
   };
@@ -982,22 +1031,10 @@ partial_mfma_kernel(Params p) {
         r.k[grp][4 * i + 3] = v.w;
       }
     }
-    if constexpr (TRV) return;  // V^T comes from transposing reads in compute_tile
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tk = j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4);
-      const uint8_t* vp = src + kTileTokens * LROW + tk * LROW + S * n;
-      if constexpr (SW == 2) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(vp);
-        r.v[j][0] = v.x;
-        r.v[j][1] = v.y;
-      } else {
-        r.v[j][0] = *reinterpret_cast<const uint32_t*>(vp);
-      }
-    }
+    // (V^T comes from transposing reads in compute_tile)
   };
   if constexpr (LW > 0) {
-    stage_load(ts);
+    stage_load(ts + shalf);
   } else {
     load_tile(ts, ta, 0);
     load_tile(ts + 1, tb, 1);
@@ -1079,14 +1116,21 @@ partial_mfma_kernel(Params p) {
   }
 
   if constexpr (LW > 0) {
-    stage_write(0, ts);
-    stage_load(ts + 1);
+    // Tile t goes into LDS slot (t - ts) & 1: loaded by its half at step
+    // t - 3, written at step t - 1, computed at step t.
+    if (shalf == 0) {
+      stage_write(0, ts);
+      stage_load(ts + 2);
+    }
     for (int tt = ts; tt < te; ++tt) {
+      const int odd = (tt - ts) & 1;
       __syncthreads();  // tile tt is in its slot; the other slot's readers are done
-      lds_read((tt - ts) & 1, ta);
-      stage_write((tt + 1 - ts) & 1, tt + 1);
-      stage_load(tt + 2);
-      compute_tile(tt, ta, (tt - ts) & 1);
+      lds_read(odd, ta);
+      if (shalf != odd) {
+        stage_write(odd ^ 1, tt + 1);
+        stage_load(tt + 3);
+      }
+      compute_tile(tt, ta, odd);
     }
   } else {
   // two tiles in flight: tile t + 1 loads while tile t is computed
@@ -1106,8 +1150,7 @@ partial_mfma_kernel(Params p) {
   const int dlane = PR == 2 ? S * 4 * (qd & 1) : S * 4 * qd;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    float l = lsum[b];
-    l = sum_over_groups(l);
+    const float l = sum_over_groups(lsum[b]);
     if (!row[b].valid) continue;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : vs / l;

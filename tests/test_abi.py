@@ -252,6 +252,10 @@ def test_row_blocks_for_many_rows():
         paired = 4 * q_len <= 8
         assert p["heads_per_wave"] == (2 if paired else 1)
         assert p["nontemporal_kv"] == (1 if paired else 0)
+    # head_dim scale groups keep their third query part: no LDS-shared tiles
+    for q_len in (16, 32, 128):
+        p = fp.fp8pa_plan(fp.make_shape(q_len=q_len, k_groups=4, k_scale_count=8 * 4, **base), 256)
+        assert p["row_groups_per_wg"] == 1, q_len
     # head_dim 256 splits head_dim over two wavefronts and keeps one row block
     p = fp.fp8pa_plan(fp.make_shape(q_len=64, **dict(base, head_dim=256)), 256)
     assert p["row_blocks"] == 1 and p["waves_per_head"] == 2
