@@ -40,6 +40,7 @@
 #include <atomic>
 #include <mutex>
 #include <cmath>
+#include <type_traits>
 #include <cstdint>
 
 #include "../../include/fp8pa.h"
@@ -59,6 +60,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -70,6 +73,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 // most kLazy (log2 units): a tile moves m only when it exceeds m by more
 // than that, so P = 2^(s - m) <= 2^kLazy, and most tiles skip rescaling O.
 constexpr float kLazy = 8.0f;
+// f16 P is taken as 2^kPShift16 times its value: with P <= 2^kLazy before
+// the shift it stays below 2^15 (under f16's 65504).
+constexpr float kPShift16 = 7.0f;
 
 struct Params {
   const uint16_t* q;
@@ -1218,6 +1224,18 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 }
 
 
+// Eight NVFP4 elements times an E4M3 block scale (as an f16 pair {s, s}),
+// in f16: an E2M1 value times an E4M3 scale has at most 6 significant bits
+// and lies in [2^-10, 2688], so the conversion and the packed multiply are
+// exact.
+__device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t w, f16x2 sc) {
+  const f16x2 a = f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * sc;
+  const f16x2 b = f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * sc;
+  const f16x2 c = f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * sc;
+  const f16x2 d = f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * sc;
+  return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
   const f32x2 e[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0) * sc,
                       __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1) * sc,
@@ -1234,12 +1252,13 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 pages on the matrix cores (head_dim 64 and 128, kv heads with at
-// least 3 query rows).  The lane layout is the FP8-MFMA kernel's (keys on M,
-// the 16 query rows of one kv head on N, V dims S n + e on M for PV), with
-// bf16 16x16x32 MFMAs: K and V are dequantized in registers to bf16 (exact),
-// the bf16 query is used as it is, and P is rounded to bf16, so neither
-// operand needs a hi + lo split.
+// Block-scaled pages on the matrix cores (head_dim 64 and 128, kv heads
+// with at least 3 query rows).  The lane layout is the FP8-MFMA kernel's
+// (keys on M, the 16 query rows of one kv head on N, V dims S n + e on M for
+// PV), with 16x16x32 MFMAs on exactly dequantized K and V, so neither
+// operand needs a hi + lo split: MXFP8 in bf16 (the bf16 query as it is, P
+// rounded to bf16), NVFP4 in f16 (one conversion and one packed multiply
+// per two elements; the query times a power of two, P rounded to f16).
 //   K, per 16-token group: lane (n, qd) holds dims [D/4 qd, D/4 (qd + 1)) of
 //     token n: D/8 data bytes and D/64 scale bytes (one per 16 dims); QK
 //     k-step c uses dims D/4 qd + 8 c .. + 7, which lie in one block.
@@ -1262,6 +1281,13 @@ partial_mfma_nvfp4_kernel(Params p) {
   constexpr int VDW = VDB >= 4 ? VDB / 4 : 1;
   constexpr int BLK = MX ? 32 : 16;       // elements per scale
   constexpr int AUX = NT ? kLoadNT : 0;
+  // Operand type of the MFMAs: bf16 for MXFP8 (the E8M0 scale applies in
+  // the conversion), f16 for NVFP4 (the E4M3 scale applies with one packed
+  // f16 multiply per two elements, exactly; P is taken as 2^kPShift16 times
+  // its value, which keeps weights down to 2^-21 of the row's max normal in
+  // f16, and the LSE takes the shift back out).
+  using OpT = std::conditional_t<MX, bf16x8, f16x8>;
+  constexpr float kShift = MX ? 0.f : kPShift16;
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
@@ -1299,7 +1325,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   // value vector is zero when this split writes the final output.
   const float sink2 = has_sink ? sink_raw * kLog2e : -INFINITY;
   float m = sink2;
-  float lsum = (qd == 0 && sink2 > -INFINITY) ? 1.f : 0.f;
+  float lsum = (qd == 0 && sink2 > -INFINITY) ? exp2f(kShift) : 0.f;
   f32x4 O[S];
 #pragma unroll
   for (int e = 0; e < S; ++e) O[e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1381,7 +1407,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   };
 
   float cr;  // score scale into log2 units (> 0; a negative one flips the query)
-  bf16x8 qb[KSTEPS];
+  OpT qb[KSTEPS];
   auto compute_tile = [&](int tt, TileRegs& r) {
     const int kb = tt * kTileTokens;
     const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
@@ -1398,25 +1424,32 @@ partial_mfma_nvfp4_kernel(Params p) {
       }
     }
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    float kscale[2][KSB];
+    if constexpr (MX) {
+      float kscale[2];
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp)
+      for (int grp = 0; grp < 2; ++grp) kscale[grp] = e8m0_to_f32(r.ks[grp] & 0xff);
 #pragma unroll
-      for (int i = 0; i < KSB; ++i)
-        kscale[grp][i] = MX ? e8m0_to_f32(r.ks[grp] & 0xff)
-                            : __builtin_amdgcn_cvt_f32_fp8(int(r.ks[grp] >> (8 * i)) & 0xff, 0);
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      bf16x8 ka, kbv;
-      if constexpr (MX) {
-        ka = e4m3x8_to_bf16(r.kd[0][2 * c], r.kd[0][2 * c + 1], kscale[0][0]);
-        kbv = e4m3x8_to_bf16(r.kd[1][2 * c], r.kd[1][2 * c + 1], kscale[1][0]);
-      } else {
-        ka = fp4x8_to_bf16(r.kd[0][c], kscale[0][c / 2]);
-        kbv = fp4x8_to_bf16(r.kd[1][c], kscale[1][c / 2]);
+      for (int c = 0; c < KSTEPS; ++c) {
+        const bf16x8 ka = e4m3x8_to_bf16(r.kd[0][2 * c], r.kd[0][2 * c + 1], kscale[0]);
+        const bf16x8 kbv = e4m3x8_to_bf16(r.kd[1][2 * c], r.kd[1][2 * c + 1], kscale[1]);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbv, qb[c], sb, 0, 0, 0);
       }
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbv, qb[c], sb, 0, 0, 0);
+    } else {
+      // the lane's KSB (<= 2) E4M3 block scales of each group as f16
+      f16x2 ksc[2];
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) ksc[grp] = f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.ks[grp], 1.0f, false));
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const int blk = (c * 8) / 16;  // the lane's block of k-step c
+        const f16x2 sa2 = blk ? __builtin_shufflevector(ksc[0], ksc[0], 1, 1) : __builtin_shufflevector(ksc[0], ksc[0], 0, 0);
+        const f16x2 sb2 = blk ? __builtin_shufflevector(ksc[1], ksc[1], 1, 1) : __builtin_shufflevector(ksc[1], ksc[1], 0, 0);
+        const f16x8 ka = fp4x8_to_f16(r.kd[0][c], sa2);
+        const f16x8 kbv = fp4x8_to_f16(r.kd[1][c], sb2);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kbv, qb[c], sb, 0, 0, 0);
+      }
     }
     float sv[8];
 #pragma unroll
@@ -1443,57 +1476,85 @@ partial_mfma_nvfp4_kernel(Params p) {
       for (int e = 0; e < S; ++e) O[e] *= alpha;
       m = mnew;
     }
-    const float noff = m == -INFINITY ? 0.f : -m;
+    const float noff = (m == -INFINITY ? 0.f : -m) + kShift;
     float pj[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(fmaf(sv[j], cr, noff));
     lsum += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
-    bf16x8 P;
+    OpT P;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
-      P[j] = h.x;
-      P[j + 1] = h.y;
-    }
-    // V^T operands: element j of operand e = V[kap(qd, j)][S n + e]
-    float vf[8][S];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f32x2 e2[4];
       if constexpr (MX) {
+        const bf16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), bf16x2);
+        P[j] = h.x;
+        P[j + 1] = h.y;
+      } else {
+        const f16x2 h = __builtin_convertvector((f32x2{pj[j], pj[j + 1]}), f16x2);
+        P[j] = h.x;
+        P[j + 1] = h.y;
+      }
+    }
+    if constexpr (!MX) {
+      // V^T operands in f16: token j's S dims as S/2 scaled f16 pairs, then
+      // operand e takes element e of tokens kap(qd, 0..7), two tokens per
+      // dword by a byte permute.
+      uint32_t vh[8][S / 2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs[j], 1.0f, false);
+        const f16x2 sc = __builtin_shufflevector(s2, s2, 0, 0);
+        const uint32_t w = r.vd[j][0];
+        vh[j][0] = __builtin_bit_cast(uint32_t, f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * sc);
+        vh[j][1] = __builtin_bit_cast(uint32_t, f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * sc);
+        if constexpr (S == 8) {
+          vh[j][2] = __builtin_bit_cast(uint32_t, f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * sc);
+          vh[j][3] = __builtin_bit_cast(uint32_t, f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * sc);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < S / 2; ++b) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          lo[j / 2] = __builtin_amdgcn_perm(vh[j + 1][b], vh[j][b], 0x05040100u);
+          hi[j / 2] = __builtin_amdgcn_perm(vh[j + 1][b], vh[j][b], 0x07060302u);
+        }
+        O[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, (u32x4{lo[0], lo[1], lo[2], lo[3]})),
+                                                          P, O[2 * b], 0, 0, 0);
+        O[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(f16x8, (u32x4{hi[0], hi[1], hi[2], hi[3]})), P, O[2 * b + 1], 0, 0, 0);
+      }
+    } else {
+      // V^T operands: element j of operand e = V[kap(qd, j)][S n + e]
+      float vf[8][S];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
         // E4M3 times a power of two: the conversion applies it exactly
         const float sc = e8m0_to_f32(r.vs[j] & 0xff);
+        f32x2 e2[4];
         e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, false);
         e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, true);
         if constexpr (S == 8) {
           e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][1], sc, false);
           e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][1], sc, true);
         }
-      } else {
-        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(r.vs[j]) & 0xff, 0);
-        e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 0) * sc;
-        e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 1) * sc;
-        if constexpr (S == 8) {
-          e2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 2) * sc;
-          e2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.vd[j][0], 1.0f, 3) * sc;
+#pragma unroll
+        for (int b = 0; b < S / 2; ++b) {
+          vf[j][2 * b] = e2[b].x;
+          vf[j][2 * b + 1] = e2[b].y;
         }
       }
 #pragma unroll
-      for (int b = 0; b < S / 2; ++b) {
-        vf[j][2 * b] = e2[b].x;
-        vf[j][2 * b + 1] = e2[b].y;
-      }
-    }
+      for (int e = 0; e < S; ++e) {
+        bf16x8 vt;
 #pragma unroll
-    for (int e = 0; e < S; ++e) {
-      bf16x8 vt;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 h = __builtin_convertvector((f32x2{vf[j][e], vf[j + 1][e]}), bf16x2);
-        vt[j] = h.x;
-        vt[j + 1] = h.y;
+        for (int j = 0; j < 8; j += 2) {
+          const bf16x2 h = __builtin_convertvector((f32x2{vf[j][e], vf[j + 1][e]}), bf16x2);
+          vt[j] = h.x;
+          vt[j + 1] = h.y;
+        }
+        O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, P, O[e], 0, 0, 0);
       }
-      O[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, P, O[e], 0, 0, 0);
     }
   };
 
@@ -1501,20 +1562,51 @@ partial_mfma_nvfp4_kernel(Params p) {
   load_tile(ts, ta, 0);
   load_tile(ts + 1, tb, 1);
 
-  // ---- stage the query: bf16 as it is; the sign of the score scale moves
-  // into the query so that fma(S, cr, .) keeps a -inf mask at -inf
+  // ---- stage the query: bf16 as it is (MXFP8), or in f16 times a per-row
+  // power of two that puts its largest element in [2^14, 2^15) (NVFP4; exact
+  // for every element above 2^-24 of that); the sign of the score scale
+  // moves into the query so that fma(S, cr, .) keeps a -inf mask at -inf
   {
     const float c0 = p.sm_scale * ks * kLog2e;
     const uint32_t flip = c0 < 0.f ? 0x80008000u : 0u;
     cr = fmaxf(fabsf(c0), 1e-30f);
+    if constexpr (MX) {
 #pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      const u32x4 v = qraw[c] ^ flip;
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      for (int c = 0; c < KSTEPS; ++c) {
+        const u32x4 v = qraw[c] ^ flip;
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qb[c][2 * i] = __builtin_bit_cast(__bf16, uint16_t(wv[i] & 0xffffu));
-        qb[c][2 * i + 1] = __builtin_bit_cast(__bf16, uint16_t(wv[i] >> 16));
+        for (int i = 0; i < 4; ++i) {
+          qb[c][2 * i] = __builtin_bit_cast(__bf16, uint16_t(wv[i] & 0xffffu));
+          qb[c][2 * i + 1] = __builtin_bit_cast(__bf16, uint16_t(wv[i] >> 16));
+        }
+      }
+    } else {
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
+      }
+      amax = max_over_groups(amax);
+      int se = 0;
+      if (amax > 0.f) {
+        const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+        se = min(max(14 - e, -120), 120);
+      }
+      const float qs = __uint_as_float(uint32_t(se + 127) << 23);
+      cr = fmaxf(fabsf(c0) / qs, 1e-30f);
+      const float sg = c0 < 0.f ? -qs : qs;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 h = __builtin_convertvector((f32x2{bf16_lo(wv[i]) * sg, bf16_hi(wv[i]) * sg}), f16x2);
+          qb[c][2 * i] = h.x;
+          qb[c][2 * i + 1] = h.y;
+        }
       }
     }
   }
@@ -1532,7 +1624,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   if (!row.valid) return;
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : vs / lsum;
-  const float lse = empty ? -INFINITY : (m + log2_fast(lsum)) * kLn2;
+  const float lse = empty ? -INFINITY : (m - kShift + log2_fast(lsum)) * kLn2;
   // O[e][i] is output dim S * (4 qd + i) + e of this lane's row
   const int dlane = S * 4 * qd;
   if (p.direct) {
