@@ -142,7 +142,7 @@ def load_traffic(workload_name):
     return None if not h else int(h["read"] + h["write"])
 
 
-def sample_gpu_state(busy, seconds_cap=20.0, what="the headline step's graph replays"):
+def sample_gpu_state(busy, seconds_cap=20.0):
     """GPU clocks and socket power read by `amd-smi metric` (a child process)
     while `busy()` keeps the GPU running the timed work; None where the tool
     is missing or its output is not understood.  Taken outside every timed
@@ -152,6 +152,10 @@ def sample_gpu_state(busy, seconds_cap=20.0, what="the headline step's graph rep
 
     exe = shutil.which("amd-smi")
     if exe is None:
+        return None
+    # Under a profiler, whose preloaded library starts the GPU runtime in
+    # every child, the tool's own exec would be refused: no sample then.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
         return None
     try:
         proc = subprocess.Popen([exe, "metric", "--clock", "--power", "--json"],
@@ -183,7 +187,7 @@ def sample_gpu_state(busy, seconds_cap=20.0, what="the headline step's graph rep
         power = g.get("power", {}).get("socket_power")
         return {
             "tool": "amd-smi metric --clock --power",
-            "sampled": f"while {what}",
+            "sampled": "while the headline step's graph replays",
             "gfx_clk_mhz_per_xcd": gfx,
             "gfx_max_clk_mhz": max(gfx_max) if gfx_max else None,
             "mem_clk_mhz": mhz(clock.get("mem_0", {})),
@@ -536,7 +540,6 @@ def measure_writer(steps, log):
 
 
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
-PEAK_CLOCK_MHZ = 2400.0     # the engine clock that peak assumes
 PREFILL_SHAPES = (
     # name, B, q_len, Hq, Hkv, D, bt, context (seq_len, the chunk included)
     ("chunk512_ctx32k", 2, 512, 32, 8, 128, 16, 32768),
@@ -552,9 +555,7 @@ def measure_prefill(log, steps=5):
     P.V, a multiply and an add each), against the dense FP8 peak; the
     matrix cores spend twice the time an FP8-only pass would (the query goes
     in as an E4M3 hi + lo pair, and P.V runs in bf16, at half the FP8 rate).
-    Timed from graph replays like the decode.  The published peak assumes
-    the 2400 MHz engine clock: the clock sampled under this load is logged
-    with the peak it implies."""
+    Timed from graph replays like the decode."""
     import torch
 
     import decode_attention_paged_fp8pa_amd as fp
@@ -611,18 +612,6 @@ def measure_prefill(log, steps=5):
                      "num_splits": plan["num_splits"], "grid_wgs": plan["grid_wgs"]}
         log(f"[bench] prefill {name}: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
             f"({tflops / PEAK_FP8_TFLOPS * 100:.2f}% of dense FP8 peak), splits {plan['num_splits']}")
-        if name == PREFILL_SHAPES[0][0]:
-            st = sample_gpu_state(lambda: (g.replay(), torch.cuda.synchronize()),
-                                  what=f"the {name} graph replays")
-            if st and st["gfx_clk_mhz_per_xcd"]:
-                clk = float(np.median(st["gfx_clk_mhz_per_xcd"]))
-                peak_at = PEAK_FP8_TFLOPS * clk / PEAK_CLOCK_MHZ
-                st["fp8_peak_at_sampled_clock_tflops"] = round(peak_at, 1)
-                st["pct_of_fp8_peak_at_sampled_clock"] = round(tflops / peak_at * 100, 2)
-                out[name]["gpu_state"] = st
-                log(f"[bench] prefill {name}: under load gfx clock {st['gfx_clk_mhz_per_xcd']} MHz, "
-                    f"socket power {st['socket_power_w']} W: {st['pct_of_fp8_peak_at_sampled_clock']:.2f}% "
-                    f"of the FP8 peak at that clock ({peak_at:.0f} TFLOP/s)")
         del g, kc, vc, q, ws
         torch.cuda.empty_cache()
     return out
