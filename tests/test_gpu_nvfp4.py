@@ -79,9 +79,43 @@ def _nv(name):
 @pytest.mark.parametrize("flags,ns", [(0, 0), (0, 1), (0, 3), (fp.FP8PA_FLAG_FORCE_DOT, 0),
                                       (fp.FP8PA_FLAG_FORCE_DOT, 3)])
 def test_nvfp4_parity_small(name, flags, ns):
-    """The planner's kernel (bf16 MFMA at head_dim 64/128 with bt >= 16 and
+    """The planner's kernel (f16 MFMA at head_dim 64/128 with bt >= 16 and
     >= 3 rows per kv head, else the VALU kernel) and the forced VALU kernel."""
     wl, t, (ro, rl) = _nv(name)
+    out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"nvfp4 {name} flags={flags} splits={ns}")
+
+
+# Large positive sinks dominate every row; with one split they enter the
+# partial kernel's running maximum, so every key's weight is e^-8 .. e^-14 of
+# it.  V codes are made non-negative (mean > 0), so a kernel that loses small
+# weights from P.V (its P is f16, shifted by 2^7) misses a visible share of
+# the output while the denominator keeps their mass.
+NV_SINKS = {
+    "big_sinks_mean_v": dict(B=2, q_len=1, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[3000, 700], sinks=True),
+    "big_sinks_mtp_d64_hnd": dict(B=2, q_len=4, Hq=16, Hkv=4, D=64, bt=16, seq_lens=[2000, 300], sinks=True,
+                                  window=1000, kv_layout="HND"),
+}
+_sinks_cache = {}
+
+
+def _nv_sinks(name):
+    if name not in _sinks_cache:
+        kw = NV_SINKS[name]
+        wl = make_nvfp4_workload(seed=400 + list(NV_SINKS).index(name), **kw)
+        data_bytes = kw["Hkv"] * kw["bt"] * kw["D"] // 2
+        wl.v_cache[:, :data_bytes] &= 0x77          # clear each E2M1 code's sign bit
+        wl.sinks[:] = 12.0
+        wl.sinks[::3] = 8.0
+        wl.sinks[1::4] = 14.0
+        _sinks_cache[name] = (wl, upload(wl), oracle.decode(**wl.oracle_kwargs()))
+    return _sinks_cache[name]
+
+
+@pytest.mark.parametrize("name", list(NV_SINKS))
+@pytest.mark.parametrize("flags,ns", [(0, 0), (0, 1), (0, 3), (fp.FP8PA_FLAG_FORCE_DOT, 1)])
+def test_nvfp4_parity_big_positive_sinks(name, flags, ns):
+    wl, t, (ro, rl) = _nv_sinks(name)
     out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
     compare(out, lse, ro, rl, label=f"nvfp4 {name} flags={flags} splits={ns}")
 
