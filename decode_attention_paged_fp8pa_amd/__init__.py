@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     fp8pa_debug_lds_tr16,
     fp8pa_debug_mxfp8,
     fp8pa_debug_mfma_fp8,
+    fp8pa_debug_mfma_scale_fp8,
     fp8pa_debug_nvfp4,
     fp8pa_debug_stream_read,
     fp8pa_debug_wave_ops,

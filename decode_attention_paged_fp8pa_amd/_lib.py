@@ -137,6 +137,7 @@ _SIGS = {
     "fp8pa_debug_stream_read": (ctypes.c_int, [_VP, ctypes.c_uint64, _VP, _VP]),
     "fp8pa_debug_lds_tr16": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+    "fp8pa_debug_mfma_scale_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
     "fp8pa_debug_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_lds_tr8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
@@ -296,6 +297,12 @@ def fp8pa_debug_lds_tr16(lds_bytes, row_addr, out, stream=None) -> None:
     st = lib().fp8pa_debug_lds_tr16(_ptr(lds_bytes), _ptr(row_addr), _ptr(out), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_lds_tr16")
+
+
+def fp8pa_debug_mfma_scale_fp8(a, a_scale, b, c, stream=None) -> None:
+    st = lib().fp8pa_debug_mfma_scale_fp8(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(c), _stream(stream))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_mfma_scale_fp8")
 
 
 def fp8pa_debug_mfma_fp8(a, b, c, stream=None) -> None:

@@ -1287,6 +1287,17 @@ partial_mfma_nvfp4_kernel(Params p) {
   // its value, which keeps weights down to 2^-21 of the row's max normal in
   // f16, and the LSE takes the shift back out).
   using OpT = std::conditional_t<MX, bf16x8, f16x8>;
+  // MXFP8 at head_dim 128: QK runs on the block-scaled FP8 MFMA
+  // (v_mfma_scale_f32_16x16x128_f8f6f4) with the K codes as they are and
+  // each 32-element block's E8M0 byte as an A scale; the query goes in as
+  // E4M3 hi + lo parts under a per-row power of two, as in the E4M3 kernel.
+  // That MFMA's operand layout (pinned by test_hw_mfma_block_scale_layout):
+  // lane group g holds k = 16 g .. 16 g + 15 in bytes 0-15 and k = 64 + 16 g
+  // .. in bytes 16-31, and the 32 k of block b take lane group b's scale.
+  // So with k = head_dim, lane (n, g) loads dims [16 g, 16 g + 16) and
+  // [64 + 16 g, 64 + 16 g + 16) of token n (and of the query), and block g's
+  // scale byte.  (At head_dim 64 the kernel uses bf16 MFMAs.)
+  constexpr bool MXQ = MX && D == 128;
   constexpr float kShift = MX ? 0.f : kPShift16;
 
   const int lane = threadIdx.x & 63;
@@ -1337,7 +1348,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   const uint8_t* ks_g = p.k_cache + (size_t)p.sc_off + (size_t)kvh * (size_t)p.sc_head;
   const uint8_t* vs_g = p.v_cache + (size_t)p.sc_off + (size_t)kvh * (size_t)p.sc_head;
   const int32_t* btab = p.block_table + (size_t)w.b * p.table_stride;
-  const uint32_t kdoff = uint32_t(n * tok + KDB * qd);
+  const uint32_t kdoff = uint32_t(n * tok + (MXQ ? 16 : KDB) * qd);
   const uint32_t ksoff = uint32_t(n * stok + (KD * qd) / BLK);
   uint32_t vdoff[4], vsoff[4];
 #pragma unroll
@@ -1364,10 +1375,10 @@ partial_mfma_nvfp4_kernel(Params p) {
   // (loaded by every lane, zeroed where the row is past the last)
   u32x4 qraw[KSTEPS];
   {
-    const uint16_t* qrow = p.q + row.out_row * D + KD * qd;
+    const uint16_t* qrow = p.q + row.out_row * D + (MXQ ? 16 : KD) * qd;
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + (MXQ ? 8 * (c & 1) + 64 * (c >> 1) : 8 * c));
       qraw[c] = row.valid ? v : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -1396,7 +1407,12 @@ partial_mfma_nvfp4_kernel(Params p) {
       const Rsrc rvd = __builtin_amdgcn_make_buffer_rsrc((void*)(vd_g + pbase + slot * tok), 0, nd, kRsrcWord3);
       const Rsrc rks = __builtin_amdgcn_make_buffer_rsrc((void*)(ks_g + pbase + slot * stok), 0, ns, kRsrcWord3);
       const Rsrc rvs = __builtin_amdgcn_make_buffer_rsrc((void*)(vs_g + pbase + slot * stok), 0, ns, kRsrcWord3);
-      buf_load<KDB, AUX>(rkd, kdoff, r.kd[grp]);
+      if constexpr (MXQ) {
+        buf_load<16, AUX>(rkd, kdoff, r.kd[grp]);
+        buf_load<16, AUX>(rkd, kdoff + 64u, r.kd[grp] + 4);
+      } else {
+        buf_load<KDB, AUX>(rkd, kdoff, r.kd[grp]);
+      }
       buf_load<KSB, AUX>(rks, ksoff, &r.ks[grp]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1408,6 +1424,7 @@ partial_mfma_nvfp4_kernel(Params p) {
 
   float cr;  // score scale into log2 units (> 0; a negative one flips the query)
   OpT qb[KSTEPS];
+  i32x8 qh8, ql8;  // (MXQ: the query's E4M3 hi and lo parts)
   auto compute_tile = [&](int tt, TileRegs& r) {
     const int kb = tt * kTileTokens;
     const bool edge = kb < ilo || kb + kTileTokens > ihi;  // uniform
@@ -1424,7 +1441,19 @@ partial_mfma_nvfp4_kernel(Params p) {
       }
     }
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (MX) {
+    if constexpr (MXQ) {
+      i32x8 ka, kbv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ka[i] = int(r.kd[0][i]);
+        kbv[i] = int(r.kd[1][i]);
+      }
+      const int sca = int(r.ks[0] & 0xff), scb = int(r.ks[1] & 0xff);
+      sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh8, sa, 0, 0, 0, sca, 0, 127);
+      sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, qh8, sb, 0, 0, 0, scb, 0, 127);
+      sa = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql8, sa, 0, 0, 0, sca, 0, 127);
+      sb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kbv, ql8, sb, 0, 0, 0, scb, 0, 127);
+    } else if constexpr (MX) {
       float kscale[2];
 #pragma unroll
       for (int grp = 0; grp < 2; ++grp) kscale[grp] = e8m0_to_f32(r.ks[grp] & 0xff);
@@ -1570,7 +1599,53 @@ partial_mfma_nvfp4_kernel(Params p) {
     const float c0 = p.sm_scale * ks * kLog2e;
     const uint32_t flip = c0 < 0.f ? 0x80008000u : 0u;
     cr = fmaxf(fabsf(c0), 1e-30f);
-    if constexpr (MX) {
+    if constexpr (MXQ) {
+      // E4M3 hi + lo parts of q times 2^se, 2^se putting the row's largest
+      // element in [128, 256) (the E4M3 kernel's staging)
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
+      }
+      amax = max_over_groups(amax);
+      int se = 0;
+      if (amax > 0.f) {
+        const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+        se = min(max(7 - e, -120), 120);
+      }
+      const float qs = __uint_as_float(uint32_t(se + 127) << 23);
+      cr = fmaxf(fabsf(c0) / qs, 1e-30f);
+      const float sg = c0 < 0.f ? -qs : qs;
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf16_lo(wv[i]) * sg;
+          x[2 * i + 1] = bf16_hi(wv[i]) * sg;
+        }
+        uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+        h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
+        h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
+        h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
+        h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
+        const f32x2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
+        const f32x2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
+        const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
+        const f32x2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
+        l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - d0.x, x[1] - d0.y, l0, false);
+        l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - d1.x, x[3] - d1.y, l0, true);
+        l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - d2.x, x[5] - d2.y, l1, false);
+        l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d3.x, x[7] - d3.y, l1, true);
+        qh8[2 * c] = int(h0);
+        qh8[2 * c + 1] = int(h1);
+        ql8[2 * c] = int(l0);
+        ql8[2 * c + 1] = int(l1);
+      }
+    } else if constexpr (MX) {
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) {
         const u32x4 v = qraw[c] ^ flip;
@@ -2286,6 +2361,28 @@ __global__ void debug_mfma_kernel(const uint8_t* a, const uint8_t* b, float* c) 
   for (int i = 0; i < 4; ++i) c[(4 * qd + i) * 16 + n] = acc[i];
 }
 
+// One block-scaled 16x16x128 FP8 MFMA: lane (n, qd) = (l % 16, l / 16) holds
+// bytes a[n][32 qd .. 32 qd + 31] of A, b[32 qd .. 32 qd + 31][n] of B, and
+// the E8M0 byte a_scale[n][qd] as its A scale (B's scale is 1).
+__global__ void debug_mfma_scale_kernel(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, float* c) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  i32x8 av, bv;
+  for (int w = 0; w < 8; ++w) {
+    uint32_t x = 0, y = 0;
+    for (int j = 0; j < 4; ++j) {
+      x |= uint32_t(a[n * 128 + 32 * qd + 4 * w + j]) << (8 * j);
+      y |= uint32_t(b[(32 * qd + 4 * w + j) * 16 + n]) << (8 * j);
+    }
+    av[w] = int(x);
+    bv[w] = int(y);
+  }
+  const int sa = int(a_scale[n * 4 + qd]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, sa, 0, 127);
+  for (int i = 0; i < 4; ++i) c[(4 * qd + i) * 16 + n] = acc[i];
+}
+
 // ---------------------------------------------------------------------------
 // Host helpers
 // ---------------------------------------------------------------------------
@@ -2681,6 +2778,13 @@ fp8pa_status fp8pa_debug_lds_tr16(const uint8_t* lds_bytes, const int32_t* row_a
 fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, void* stream) {
   if (!a || !b || !c) return FP8PA_ERR_INVALID_ARG;
   debug_mfma_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(a, b, c);
+  return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
+}
+
+fp8pa_status fp8pa_debug_mfma_scale_fp8(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, float* c,
+                                        void* stream) {
+  if (!a || !a_scale || !b || !c) return FP8PA_ERR_INVALID_ARG;
+  debug_mfma_scale_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(a, a_scale, b, c);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

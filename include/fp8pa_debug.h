@@ -55,6 +55,16 @@ fp8pa_status fp8pa_debug_mxfp8(const uint8_t* data, const uint8_t* scales, float
  * if that layout is the hardware's. */
 fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, void* stream);
 
+/* c = (a scaled) x b for one block-scaled 16x16x128 FP8 MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 operands): a is E4M3 [16][128]
+ * (M x K), b is E4M3 [128][16] (K x N), a_scale is E8M0 [16][4], c is float
+ * [16][16] row-major.  Lane l = 16 qd + n loads A row n, bytes 32 qd .. +31,
+ * B column n, rows 32 qd .. +31, and a_scale[n][qd] as its A scale byte (B's
+ * scale is 1); the result is stored with rows 4 qd + i, column n.  The GPU
+ * test states which A elements each lane's scale multiplies. */
+fp8pa_status fp8pa_debug_mfma_scale_fp8(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, float* c,
+                                        void* stream);
+
 /* One wavefront of 64 lanes, lane l holding in[l] (int32 [64], each in
  * [0, vmax], vmax >= 0): out[l] = the exclusive prefix sum in[0] + ... +
  * in[l-1], out[64 + l] = the wavefront sum, out[128 + l] = the wavefront

@@ -76,6 +76,40 @@ def test_hw_mfma_fp8_accumulation_precision():
     assert np.all(np.abs(_mfma(a, b) - want) <= scale * 2.0 ** -10)
 
 
+def _scaled_mfma_ref(a, sa, b):
+    """The block-scaled 16x16x128 FP8 MFMA as the kernels use it: lane group
+    g's bytes 0-15 (a[m][32 g + j]) are k = 16 g + j and its bytes 16-31 are
+    k = 64 + 16 g + (j - 16), for A and B alike, and the 32 k of block c
+    (k // 32 = c) take row m's scale byte from lane group c, sa[m][c]."""
+    k = np.arange(128)
+    g = np.where(k < 64, k // 16, (k - 64) // 16)
+    j = np.where(k < 64, k % 16, 16 + (k - 64) % 16)
+    A = oracle.E4M3_TABLE[a[:, 32 * g + j]] * np.exp2(sa[:, k // 32].astype(np.float64) - 127)
+    B = oracle.E4M3_TABLE[b[32 * g + j, :]]
+    return A @ B, np.abs(A) @ np.abs(B)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_hw_mfma_block_scale_layout(seed):
+    """The lane layout and scale assignment of v_mfma_scale_f32_16x16x128_f8f6f4
+    that the MXFP8 kernel relies on (each lane's A scale multiplies one
+    32-element block of its row, laid out as above): random codes, E8M0
+    scales 120..134 per row and block, against the exact sum within the
+    MFMA's accumulation precision."""
+    rng = np.random.default_rng(50 + seed)
+    a = rng.integers(0, 0x78, size=(16, 128)).astype(np.uint8)
+    a |= (rng.integers(0, 2, size=a.shape) << 7).astype(np.uint8)
+    b = rng.integers(0, 0x78, size=(128, 16)).astype(np.uint8)
+    b |= (rng.integers(0, 2, size=b.shape) << 7).astype(np.uint8)
+    sa = rng.integers(120, 135, size=(16, 4)).astype(np.uint8)
+    c = torch.empty(256, dtype=torch.float32, device="cuda")
+    fp.fp8pa_debug_mfma_scale_fp8(torch.from_numpy(a).cuda(), torch.from_numpy(sa).cuda(),
+                                  torch.from_numpy(b).cuda(), c)
+    got = c.cpu().numpy().reshape(16, 16).astype(np.float64)
+    want, mag = _scaled_mfma_ref(a, sa, b)
+    assert np.all(np.abs(got - want) <= mag * 2.0 ** -10)
+
+
 @pytest.mark.parametrize("vmax", [0, 1, 7, 300, 65535])
 def test_hw_wave_reductions_and_prefix(vmax):
     rng = np.random.default_rng(vmax)
