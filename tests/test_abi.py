@@ -39,6 +39,32 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(handle, n), f"{n} declared in include/ but not exported"
 
 
+# The HIP runtime entry points the library may import: kernel registration
+# and launch, device queries, the error state and the no-allocation entry
+# point's symbol lookup.  No allocation, free, memset, copy, stream or event
+# creation, or synchronisation: no call path can allocate or block, under
+# graph capture or not, whatever torch's allocator reports.
+ALLOWED_HIP_IMPORTS = {
+    "__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+    "__hipRegisterFunction", "__hipRegisterVar", "__hipUnregisterFatBinary",
+    "hipDeviceGetAttribute", "hipGetDevice", "hipGetLastError", "hipGetSymbolAddress", "hipLaunchKernel",
+}
+
+
+def test_library_imports_no_allocation_or_synchronisation():
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    r = subprocess.run([nm, "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
+    imported = {line.split()[-1].split("@")[0] for line in r.stdout.splitlines() if line.strip()}
+    hip = {name for name in imported if "hip" in name.lower()}
+    assert hip, "no HIP imports found: not the built library?"
+    assert hip <= ALLOWED_HIP_IMPORTS, f"unexpected HIP runtime imports: {sorted(hip - ALLOWED_HIP_IMPORTS)}"
+
+
 def test_status_strings_and_version():
     assert fp.status_string(0) == "ok"
     for s in range(1, 6):
