@@ -114,6 +114,7 @@ struct Params {
   int32_t kg_shift;  // log2 of the dims per K scale group
   int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
   int32_t pr;  // kv heads per wavefront (MFMA kernel: 2 pairs heads at D = 64)
+  int32_t xcd; // 1: each XCD's workgroups take one contiguous range of logical indices
   float sm_scale;
 };
 
@@ -347,10 +348,23 @@ struct Work {
 // The kv head, row group and head_dim part of this wavefront: these follow
 // from the workgroup index alone, so loads that need only them can be issued
 // before the (sequence, split) item is resolved.
+// The workgroup's logical index.  Workgroups go to the 8 XCDs in turn
+// (block i to XCD i % 8); with p.xcd each XCD's workgroups take one
+// contiguous range of logical indices, so the workgroups of one item (which
+// re-read the same K/V tiles when several row groups of a kv head share
+// them) run on one XCD and meet those bytes in its L2.
+__device__ __forceinline__ int logical_block(const Params& p) {
+  const int i = blockIdx.x;
+  if (!p.xcd) return i;
+  const int n = gridDim.x, x = i & 7, q = n >> 3, r = n & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (i >> 3);
+}
+
 __device__ __forceinline__ Work work_head(const Params& p, int ds) {
   Work w;
-  const int item = blockIdx.x / p.upi;
-  const int unit = blockIdx.x - item * p.upi;
+  const int bid = logical_block(p);
+  const int item = bid / p.upi;
+  const int unit = bid - item * p.upi;
   w.rg = unit % p.row_groups;
   const int gg = unit / p.row_groups;
   // the wavefront index is uniform across the wave; saying so keeps every
@@ -362,7 +376,8 @@ __device__ __forceinline__ Work work_head(const Params& p, int ds) {
 }
 
 __device__ __forceinline__ void work_item(const Params& p, Work& w) {
-  const int item = blockIdx.x / p.upi;
+  const int bid = logical_block(p);
+  const int item = bid / p.upi;
   w.active = true;
 
   if (!p.balanced) {
@@ -373,7 +388,7 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
     w.sp = span_of(w.L, p.q_len, p.window);
     w.ts = w.sp.tile0 + w.split * p.tps;
     w.te = min(w.ts + p.tps, w.sp.tile1);
-    if (p.nsplit_out && w.split == 0 && blockIdx.x % p.upi == 0 && threadIdx.x == 0)
+    if (p.nsplit_out && w.split == 0 && bid % p.upi == 0 && threadIdx.x == 0)
       p.nsplit_out[w.b] = w.nsplit;
     return;
   }
@@ -425,7 +440,7 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
       w.sp = span_of(w.L, p.q_len, p.window);
       w.ts = w.sp.tile0 + w.split * c;
       w.te = min(w.ts + c, w.sp.tile1);
-      if (p.nsplit_out && w.split == 0 && blockIdx.x % p.upi == 0 && threadIdx.x == 0)
+      if (p.nsplit_out && w.split == 0 && bid % p.upi == 0 && threadIdx.x == 0)
         p.nsplit_out[w.b] = w.nsplit;
       return;
     }
@@ -557,8 +572,9 @@ partial_mfma_kernel(Params p) {
   const int qd = lane >> 4;
   Work w = work_head(p, DS);
   if constexpr (LW > 0) {
-    const int item = blockIdx.x / p.upi;
-    const int unit = blockIdx.x - item * p.upi;
+    const int bid = logical_block(p);
+    const int item = bid / p.upi;
+    const int unit = bid - item * p.upi;
     const int rgu = p.row_groups / LW;
     const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     w.rg = (unit % rgu) * LW + wv;
@@ -2594,6 +2610,7 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
   prm.B = pl.B;
   prm.hg = pl.hg;
   prm.upi = pl.upi;
+  prm.xcd = pl.lw > 0 ? 1 : 0;
   prm.num_splits = pl.num_splits;
   prm.tps = pl.tps;
   prm.tps_cap = pl.tps_cap;
