@@ -73,6 +73,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 // most kLazy (log2 units): a tile moves m only when it exceeds m by more
 // than that, so P = 2^(s - m) <= 2^kLazy, and most tiles skip rescaling O.
 constexpr float kLazy = 8.0f;
+constexpr float kMinNormal = 1.17549435e-38f;  // the least normal fp32 value
 // f16 P is taken as 2^kPShift16 times its value: with P <= 2^kLazy before
 // the shift it stays below 2^15 (under f16's 65504).
 constexpr float kPShift16 = 7.0f;
@@ -1099,9 +1100,10 @@ partial_mfma_kernel(Params p) {
     float c0 = p.sm_scale * (grouped ? 1.f : ks) * kLog2e / qs;
     // Scores are scaled as fma(S, cr, .) with cr > 0, so a -inf mask stays
     // -inf: a negative scale's sign moves into the query, and a zero scale
-    // becomes a tiny positive one (its scores stay ~0).
+    // becomes the least normal float (its scores stay ~0; any nonzero
+    // scale, however small, is kept as it is).
     const float qsign = c0 < 0.f ? -qs : qs;
-    cr[b] = fmaxf(fabsf(c0), 1e-30f);
+    cr[b] = fmaxf(fabsf(c0), kMinNormal);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       float x[8];
@@ -1607,42 +1609,42 @@ partial_mfma_nvfp4_kernel(Params p) {
   load_tile(ts, ta, 0);
   load_tile(ts + 1, tb, 1);
 
-  // ---- stage the query: bf16 as it is (MXFP8), or in f16 times a per-row
-  // power of two that puts its largest element in [2^14, 2^15) (NVFP4; exact
-  // for every element above 2^-24 of that); the sign of the score scale
-  // moves into the query so that fma(S, cr, .) keeps a -inf mask at -inf
+  // ---- stage the query under a per-row power of two 2^se, which puts the
+  // row's largest element in [2^T, 2^(T+1)): T = 7 for E4M3 hi + lo parts
+  // (MXFP8 at head_dim 128, as in the E4M3 kernel), 14 for f16 (NVFP4: exact
+  // for every element above 2^-24 of the largest), 0 for bf16 (MXFP8 at
+  // head_dim 64: exact).  2^-se moves into the score scale, and the sign of
+  // that scale into the query, so that fma(S, cr, .) keeps a -inf mask at
+  // -inf; a zero scale becomes the least normal float (scores stay ~0).
   {
+    constexpr int T = MXQ ? 7 : MX ? 0 : 14;
     const float c0 = p.sm_scale * ks * kLog2e;
-    const uint32_t flip = c0 < 0.f ? 0x80008000u : 0u;
-    cr = fmaxf(fabsf(c0), 1e-30f);
-    if constexpr (MXQ) {
-      // E4M3 hi + lo parts of q times 2^se, 2^se putting the row's largest
-      // element in [128, 256) (the E4M3 kernel's staging)
-      float amax = 0.f;
+    float amax = 0.f;
 #pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) {
-        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+    for (int c = 0; c < KSTEPS; ++c) {
+      const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
+    }
+    amax = max_over_groups(amax);
+    int se = 0;
+    if (amax > 0.f) {
+      const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
+      se = min(max(T - e, -120), 120);
+    }
+    const float qs = __uint_as_float(uint32_t(se + 127) << 23);
+    cr = fmaxf(fabsf(c0) / qs, kMinNormal);
+    const float sg = c0 < 0.f ? -qs : qs;
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(wv[i]) * sg;
+        x[2 * i + 1] = bf16_hi(wv[i]) * sg;
       }
-      amax = max_over_groups(amax);
-      int se = 0;
-      if (amax > 0.f) {
-        const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
-        se = min(max(7 - e, -120), 120);
-      }
-      const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-      cr = fmaxf(fabsf(c0) / qs, 1e-30f);
-      const float sg = c0 < 0.f ? -qs : qs;
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) {
-        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = bf16_lo(wv[i]) * sg;
-          x[2 * i + 1] = bf16_hi(wv[i]) * sg;
-        }
+      if constexpr (MXQ) {
         uint32_t h0 = 0, h1 = 0, l0 = 0, l1 = 0;
         h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
         h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
@@ -1660,43 +1662,18 @@ partial_mfma_nvfp4_kernel(Params p) {
         qh8[2 * c + 1] = int(h1);
         ql8[2 * c] = int(l0);
         ql8[2 * c + 1] = int(l1);
-      }
-    } else if constexpr (MX) {
+      } else {
 #pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) {
-        const u32x4 v = qraw[c] ^ flip;
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qb[c][2 * i] = __builtin_bit_cast(__bf16, uint16_t(wv[i] & 0xffffu));
-          qb[c][2 * i + 1] = __builtin_bit_cast(__bf16, uint16_t(wv[i] >> 16));
-        }
-      }
-    } else {
-      float amax = 0.f;
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) {
-        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
-      }
-      amax = max_over_groups(amax);
-      int se = 0;
-      if (amax > 0.f) {
-        const int e = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;
-        se = min(max(14 - e, -120), 120);
-      }
-      const float qs = __uint_as_float(uint32_t(se + 127) << 23);
-      cr = fmaxf(fabsf(c0) / qs, 1e-30f);
-      const float sg = c0 < 0.f ? -qs : qs;
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) {
-        const uint32_t wv[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f16x2 h = __builtin_convertvector((f32x2{bf16_lo(wv[i]) * sg, bf16_hi(wv[i]) * sg}), f16x2);
-          qb[c][2 * i] = h.x;
-          qb[c][2 * i + 1] = h.y;
+        for (int i = 0; i < 8; i += 2) {
+          if constexpr (MX) {
+            const bf16x2 h = __builtin_convertvector((f32x2{x[i], x[i + 1]}), bf16x2);
+            qb[c][i] = h.x;
+            qb[c][i + 1] = h.y;
+          } else {
+            const f16x2 h = __builtin_convertvector((f32x2{x[i], x[i + 1]}), f16x2);
+            qb[c][i] = h.x;
+            qb[c][i + 1] = h.y;
+          }
         }
       }
     }
