@@ -1,0 +1,47 @@
+"""A sweep of the shape space against the oracle: GQA ratios from 1 (MHA) to
+64 (one kv head for 64 query heads), 1, 2 and 5 query tokens, head_dim 64,
+128 and 256, so every planner branch is taken (VALU kernel, paired heads,
+two row blocks, head_dim split, LDS-shared row groups of 2, 4 and 8); and a
+batch past the balanced planner's limit (fixed splits)."""
+
+import pytest
+
+import oracle
+from tests.gpu_harness import compare, run, to_host, upload
+from workloads import make_workload
+
+torch = pytest.importorskip("torch")
+fp = pytest.importorskip("decode_attention_paged_fp8pa_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp.lib()
+
+
+RATIOS = [(4, 4), (8, 4), (12, 4), (20, 4), (28, 4), (32, 4), (64, 4), (64, 1)]   # (Hq, Hkv)
+CASES = [(hq, hkv, ql, d) for hq, hkv in RATIOS for ql in (1, 2, 5) for d in (64, 128, 256)]
+
+
+@pytest.mark.parametrize("hq,hkv,ql,d", CASES)
+def test_shape_sweep(hq, hkv, ql, d):
+    wl = make_workload(seed=900 + CASES.index((hq, hkv, ql, d)), B=2, q_len=ql, Hq=hq, Hkv=hkv, D=d, bt=16,
+                       seq_lens=[333, 70], window=250 if ql != 2 else 0, sinks=ql != 1)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, upload(wl)))
+    compare(out, lse, ro, rl, label=f"Hq={hq} Hkv={hkv} q_len={ql} D={d}")
+
+
+@pytest.mark.parametrize("flags", [0, fp.FP8PA_FLAG_FORCE_DOT])
+def test_batch_past_the_balanced_limit(flags):
+    """300 sequences (the balanced plan reads all seq_lens for up to 256):
+    fixed-size splits from max_seq_len, ragged lengths, empty slots."""
+    seq = [0 if i % 17 == 0 else 1 + (53 * i * i + 7 * i) % 900 for i in range(300)]
+    wl = make_workload(seed=990, B=300, q_len=1, Hq=8, Hkv=2, D=128, bt=16, seq_lens=seq, sinks=True)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, upload(wl), flags=flags))
+    compare(out, lse, ro, rl, label=f"B=300 flags={flags}")
