@@ -94,6 +94,18 @@ def _pool_dims(cache, layout):
     return nb, bt, Hkv, D
 
 
+def _e4m3_page_stride(cache):
+    """Bytes between the pages of a 4-D E4M3 pool that is dense inside each
+    page: 0 when the pool is dense altogether (or has one page), the page
+    stride otherwise (e.g. K and V pages interleaved in one buffer); None when
+    a page itself is strided."""
+    if cache.dim() != 4 or cache.stride(3) != 1 or cache.stride(2) != cache.shape[3] \
+            or cache.stride(1) != cache.shape[2] * cache.shape[3]:
+        return None
+    page = cache.shape[1] * cache.shape[2] * cache.shape[3]
+    return 0 if cache.shape[0] <= 1 or cache.stride(0) == page else int(cache.stride(0))
+
+
 def _format_code(kv_format):
     if kv_format in ("e4m3", FP8PA_KV_E4M3):
         return FP8PA_KV_E4M3
@@ -122,7 +134,7 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
         page_stride = k_cache.stride(0)
     else:
         nb, bt, Hkv, Dk = _pool_dims(k_cache, layout)
-        page_stride = 0
+        page_stride = _e4m3_page_stride(k_cache) or 0
     if Dk != D:
         raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
     if sm_scale is None:
@@ -196,6 +208,9 @@ def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sca
     else:
         if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
             raise ValueError("k_cache and v_cache must be equal 4-D E4M3 pools")
+        if _e4m3_page_stride(k_cache) is None or v_cache.stride() != k_cache.stride():
+            raise ValueError("E4M3 pools must be dense inside each page, with equal strides "
+                             "(pages may be strided, e.g. K and V pages interleaved)")
         _, _, Hkv, Dk = _pool_dims(k_cache, layout)
         if Dk != D:
             raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
@@ -220,8 +235,6 @@ def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sca
             raise ValueError(f"sinks must be float32 [Hq] = [{Hq}]")
     dense = [("q", q), ("seq_lens", seq_lens), ("k_scale", k_scale), ("v_scale", v_scale),
              ("sinks", sinks)]
-    if not blockscaled:
-        dense += [("k_cache", k_cache), ("v_cache", v_cache)]
     for name, t in dense:
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -306,8 +319,8 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
             raise ValueError(f"{name} must be a uint8 or float8_e4m3fn pool")
         if nvfp4 and (t.dim() != 2 or t.stride(1) != 1):
             raise ValueError(f"{name}: block-scaled pools are uint8 [num_blocks, page_bytes]")
-        if not nvfp4 and not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous E4M3 pool")
+        if not nvfp4 and _e4m3_page_stride(t) is None:
+            raise ValueError(f"{name} must be an E4M3 pool dense inside each page")
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be contiguous int64")
     T, Hkv, D = key.shape
@@ -320,9 +333,10 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
         nb, bt, page_stride = k_cache.shape[0], int(block_tokens), k_cache.stride(0)
     else:
         nb, bt, Hkv_c, D_c = _pool_dims(k_cache, layout)
-        if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
-            raise ValueError("cache shape does not match key / value")
-        page_stride = 0
+        if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape) \
+                or v_cache.stride() != k_cache.stride():
+            raise ValueError("cache shape or strides do not match key / value")
+        page_stride = _e4m3_page_stride(k_cache) or 0
     shape = WriteShape(T, key.stride(0), value.stride(0), Hkv, D, bt, nb, k_scale.numel(),
                        v_scale.numel(), int(k_groups), layout, fmt, page_stride)
     fp8pa_cache_write(shape, key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, stream)

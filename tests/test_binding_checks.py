@@ -112,6 +112,22 @@ def test_blockscaled_page_bytes():
         fp.check_decode_args(*args, kv_format="nvfp4")  # geometry missing
 
 
+def test_e4m3_pages_interleaved_in_one_buffer():
+    """K and V pages interleaved in one buffer ([blocks, 2, bt, Hkv, D]):
+    each pool is dense inside a page, and the shape carries the page stride."""
+    buf = torch.zeros((NB, 2, BT, HKV, D), dtype=torch.uint8)
+    k, v = buf[:, 0], buf[:, 1]
+    _check(k_cache=k, v_cache=v)
+    a = _valid()
+    shape = fp.shape_for(a["q"], k, a["block_table"], a["k_scale"], a["v_scale"], max_seq_len=40)
+    assert shape.kv_page_stride == 2 * BT * HKV * D
+    assert fp.shape_for(a["q"], a["k_cache"], a["block_table"], a["k_scale"], a["v_scale"],
+                        max_seq_len=40).kv_page_stride == 0
+    # V's pages must be laid out like K's
+    with pytest.raises(ValueError):
+        _check(k_cache=k, v_cache=torch.zeros((NB, BT, HKV, D), dtype=torch.uint8))
+
+
 def test_table_width_against_max_seq_len():
     a = _valid()
     fp._check_table_width(a["block_table"], 4 * BT, a["k_cache"], "NHD", "e4m3", None)

@@ -356,6 +356,22 @@ def test_parity_head_major_pages(name, flags, ns):
     compare(out, lse, ro, rl, label=f"{name} HND flags={flags} splits={ns}")
 
 
+@pytest.mark.parametrize("name", ["gqa4_ragged", "prefill_q64", "d256_bt64"])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("flags,ns", [(0, 0), (0, 3), (DOT, 0)])
+def test_parity_interleaved_e4m3_pages(name, layout, flags, ns):
+    """K and V pages interleaved in one buffer ([blocks, 2, page]): the pools
+    are strided views whose page stride is two pages, and the result is the
+    dense pools' (the oracle's)."""
+    wl, _, (ro, rl) = _small(name)
+    t = upload(wl, kv_layout=layout)
+    buf = torch.stack([t["k"], t["v"]], dim=1)
+    t["k"], t["v"] = buf[:, 0], buf[:, 1]
+    assert t["k"].stride(0) == 2 * t["k"][0].numel()
+    out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
+    compare(out, lse, ro, rl, label=f"{name} interleaved {layout} flags={flags} splits={ns}")
+
+
 def test_parity_output_without_lse_pointer():
     wl, t, (ro, rl) = _small("mtp4_window_sinks")
     out = torch.empty(tuple(wl.q_bits.shape), dtype=torch.bfloat16, device="cuda")

@@ -100,6 +100,36 @@ def test_writer_codes_match_oracle(T, Hkv, D, bt, nb, pad, per_head, kg):
         assert not diff.any(), (name, np.argwhere(diff)[:5], got[diff][:5], want[diff][:5])
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_writer_into_interleaved_pages(layout):
+    """K and V pages interleaved in one buffer ([blocks, 2, page]): the pools
+    are strided views, each written exactly where the dense pools would be,
+    and the other half of every page keeps its bytes."""
+    T, Hkv, D, bt, nb = 40, 4, 128, 16, 6
+    rng = np.random.default_rng(31)
+    key = _inputs(rng, T, Hkv, D, 0, True)
+    value = _inputs(rng, T, Hkv, D, 0, False)
+    slots = rng.permutation(nb * bt)[:T].astype(np.int64)
+    slots[::7] = -1
+    ks = rng.uniform(0.01, 0.2, size=Hkv).astype(np.float32)
+    vs = rng.uniform(0.01, 0.2, size=Hkv).astype(np.float32)
+    page = (Hkv, bt, D) if layout == "HND" else (bt, Hkv, D)
+    buf0 = rng.integers(0, 256, size=(nb, 2) + page).astype(np.uint8)
+    buf = torch.from_numpy(buf0).cuda()
+    kc, vc = buf[:, 0], buf[:, 1]
+    fp.cache_write(key, value, torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
+                   torch.from_numpy(vs).cuda(), kc, vc, kv_layout=layout)
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.cache_write(_bits(key), _bits(value), slots, ks, vs, buf0[:, 0].copy(),
+                                        buf0[:, 1].copy(), kv_layout=layout)
+    got = buf.cpu().numpy()
+    for half, want, name in ((0, want_k, "k"), (1, want_v, "v")):
+        g = got[:, half]
+        nan_w = np.isnan(oracle.E4M3_TABLE[want])
+        assert np.array_equal(np.isnan(oracle.E4M3_TABLE[g]), nan_w), name
+        assert not ((g != want) & ~nan_w).any(), name
+
+
 @pytest.mark.parametrize("kg", [1, 4])
 def test_writer_then_decode_round_trip(kg):
     # keys and values of two sequences written by the library, then read back
