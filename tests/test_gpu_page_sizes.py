@@ -47,3 +47,13 @@ def test_page_sizes(fmt, bt, flags, ns):
     wl, t, (ro, rl) = _case(fmt, bt)
     out, lse = to_host(*run(wl, t, num_splits=ns, flags=flags))
     compare(out, lse, ro, rl, label=f"{fmt} bt={bt} flags={flags} splits={ns}")
+
+
+@pytest.mark.parametrize("fmt", list(MAKE))
+@pytest.mark.parametrize("ns", [2, 7, 64, 500])
+def test_forced_split_counts(fmt, ns):
+    """A caller's split count, from a few to far more splits than a sequence
+    has tiles (the extra splits hold no keys and must merge as nothing)."""
+    wl, t, (ro, rl) = _case(fmt, 16)
+    out, lse = to_host(*run(wl, t, num_splits=ns))
+    compare(out, lse, ro, rl, label=f"{fmt} splits={ns}")
