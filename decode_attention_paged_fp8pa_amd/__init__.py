@@ -98,12 +98,23 @@ def _e4m3_page_stride(cache):
     """Bytes between the pages of a 4-D E4M3 pool that is dense inside each
     page: 0 when the pool is dense altogether (or has one page), the page
     stride otherwise (e.g. K and V pages interleaved in one buffer); None when
-    a page itself is strided."""
-    if cache.dim() != 4 or cache.stride(3) != 1 or cache.stride(2) != cache.shape[3] \
-            or cache.stride(1) != cache.shape[2] * cache.shape[3]:
+    a page itself is strided.  The stride of a dimension of size 1 is never
+    used to address anything, so it is not looked at (torch leaves it
+    arbitrary, e.g. in a transposed view of pages of one token)."""
+    if cache.dim() != 4:
         return None
-    page = cache.shape[1] * cache.shape[2] * cache.shape[3]
-    return 0 if cache.shape[0] <= 1 or cache.stride(0) == page else int(cache.stride(0))
+    dense = 1
+    for d in (3, 2, 1):
+        if cache.shape[d] != 1 and cache.stride(d) != dense:
+            return None
+        dense *= cache.shape[d]
+    return 0 if cache.shape[0] <= 1 or cache.stride(0) == dense else int(cache.stride(0))
+
+
+def _row_stride(pool):
+    """Bytes between the pages of a 2-D block-scaled pool (0 = dense, or one
+    page, whose row stride addresses nothing)."""
+    return 0 if pool.shape[0] <= 1 else int(pool.stride(0))
 
 
 def _format_code(kv_format):
@@ -131,7 +142,7 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
             raise ValueError("block-scaled pools are [num_blocks, page_bytes]; pass num_kv_heads and "
                              "block_tokens")
         nb, bt, Hkv, Dk = k_cache.shape[0], int(block_tokens), int(num_kv_heads), D
-        page_stride = k_cache.stride(0)
+        page_stride = _row_stride(k_cache)
     else:
         nb, bt, Hkv, Dk = _pool_dims(k_cache, layout)
         page_stride = _e4m3_page_stride(k_cache) or 0
@@ -194,8 +205,8 @@ def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sca
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
     if blockscaled:
-        if (k_cache.dim() != 2 or k_cache.stride(1) != 1 or v_cache.stride() != k_cache.stride()
-                or v_cache.shape != k_cache.shape):
+        if (k_cache.dim() != 2 or v_cache.shape != k_cache.shape or k_cache.stride(1) != 1
+                or v_cache.stride(1) != 1 or _row_stride(v_cache) != _row_stride(k_cache)):
             raise ValueError("block-scaled pools must be equal uint8 [num_blocks, page_bytes] with unit "
                              "column stride")
         if num_kv_heads is None or block_tokens is None:
@@ -208,7 +219,7 @@ def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sca
     else:
         if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
             raise ValueError("k_cache and v_cache must be equal 4-D E4M3 pools")
-        if _e4m3_page_stride(k_cache) is None or v_cache.stride() != k_cache.stride():
+        if _e4m3_page_stride(k_cache) is None or _e4m3_page_stride(v_cache) != _e4m3_page_stride(k_cache):
             raise ValueError("E4M3 pools must be dense inside each page, with equal strides "
                              "(pages may be strided, e.g. K and V pages interleaved)")
         _, _, Hkv, Dk = _pool_dims(k_cache, layout)
@@ -328,13 +339,13 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
         raise ValueError("key, value and slot_mapping disagree on the token count or shape")
     layout = _layout_code(kv_layout)
     if nvfp4:
-        if block_tokens is None or v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        if block_tokens is None or v_cache.shape != k_cache.shape or _row_stride(v_cache) != _row_stride(k_cache):
             raise ValueError("block-scaled pools must match each other; pass block_tokens")
-        nb, bt, page_stride = k_cache.shape[0], int(block_tokens), k_cache.stride(0)
+        nb, bt, page_stride = k_cache.shape[0], int(block_tokens), _row_stride(k_cache)
     else:
         nb, bt, Hkv_c, D_c = _pool_dims(k_cache, layout)
         if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape) \
-                or v_cache.stride() != k_cache.stride():
+                or _e4m3_page_stride(v_cache) != _e4m3_page_stride(k_cache):
             raise ValueError("cache shape or strides do not match key / value")
         page_stride = _e4m3_page_stride(k_cache) or 0
     shape = WriteShape(T, key.stride(0), value.stride(0), Hkv, D, bt, nb, k_scale.numel(),

@@ -128,6 +128,30 @@ def test_e4m3_pages_interleaved_in_one_buffer():
         _check(k_cache=k, v_cache=torch.zeros((NB, BT, HKV, D), dtype=torch.uint8))
 
 
+def test_size_one_dimensions_keep_any_stride():
+    """A dimension of size 1 addresses nothing, so its stride does not count:
+    head-major pools of one-token pages made by transposing token-major ones
+    (torch keeps them as views with the old stride) are dense, and so are
+    one-page pools sliced out of a wider buffer; a page that is really
+    strided is still refused."""
+    hnd = torch.zeros((NB, 1, HKV, D), dtype=torch.uint8).transpose(1, 2)
+    assert hnd.is_contiguous() and hnd.stride(2) != D
+    assert fp._e4m3_page_stride(hnd) == 0
+    a = _valid(k_cache=hnd, v_cache=torch.zeros((NB, HKV, 1, D), dtype=torch.uint8),
+               block_table=torch.zeros((B, 64), dtype=torch.int32))
+    fp.check_decode_args(a.pop("q"), a.pop("k_cache"), a.pop("v_cache"), a.pop("block_table"),
+                         a.pop("seq_lens"), a.pop("k_scale"), a.pop("v_scale"), a.pop("sinks"),
+                         kv_layout="HND", **a)
+    one_page = torch.zeros((2, BT, HKV, D), dtype=torch.uint8)[:1]
+    assert fp._e4m3_page_stride(one_page) == 0
+    wide = torch.zeros((1, 4096), dtype=torch.uint8)
+    assert fp._row_stride(wide[:, :2048].t().contiguous().t()) == 0
+    strided_rows = torch.zeros((NB, BT, HKV, 2 * D), dtype=torch.uint8)[..., :D]
+    assert fp._e4m3_page_stride(strided_rows) is None
+    with pytest.raises(ValueError):
+        _check(k_cache=strided_rows, v_cache=strided_rows)
+
+
 def test_table_width_against_max_seq_len():
     a = _valid()
     fp._check_table_width(a["block_table"], 4 * BT, a["k_cache"], "NHD", "e4m3", None)
