@@ -436,7 +436,8 @@ def copy_ceiling(log):
 def read_ceiling(results, log, launches=50):
     """The practical floor of each workload's step: one launch that reads
     only the workload's KV byte count (fp8pa_debug_stream_read: contiguous
-    chunks, 16-byte loads), cold (buffers rotated through >= 1 GiB), timed
+    chunks, 16-byte loads; and at the ragged GQA batch's byte count with 4-
+    and 8-byte loads too), cold (buffers rotated through >= 1 GiB), timed
     from graph replays like the decode; and one empty launch, which the merge
     kernel adds on top of any partial pass."""
     import torch
@@ -445,14 +446,14 @@ def read_ceiling(results, log, launches=50):
 
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
 
-    def timed(nbytes, bufs):
+    def timed(nbytes, bufs, load_bytes=16):
         for i in range(3):
-            fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink)
+            fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink, load_bytes=load_bytes)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(launches):
-                fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink)
+                fp.fp8pa_debug_stream_read(bufs[i % len(bufs)], nbytes, sink, load_bytes=load_bytes)
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -468,6 +469,20 @@ def read_ceiling(results, log, launches=50):
         return sorted(per)[len(per) // 2]
 
     out = {"empty_launch_us": round(timed(0, [sink]), 2)}
+    # The same read with 4-, 8- and 16-byte loads (1x, 2x, 4x the load
+    # instructions for the same bytes), at the ragged GQA batch's byte count.
+    if 2 in results:
+        nbytes = (int(results[2]["kv_bytes"]) + 15) // 16 * 16
+        copies = int(min(16, max(2, math.ceil(MALL_FLUSH_BYTES / nbytes))))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        widths = {}
+        for w in (16, 8, 4):
+            widths[w] = round(timed(nbytes, bufs, w), 2)
+        out["load_width_us"] = {"kv_bytes": nbytes, **{f"{w}B": us for w, us in widths.items()}}
+        log(f"[bench] read ceiling by load width, {nbytes / 1e6:.1f} MB: " +
+            ", ".join(f"{w}-byte loads {us:.1f} us" for w, us in widths.items()))
+        del bufs
+        torch.cuda.empty_cache()
     for k, r in results.items():
         nbytes = (int(r["kv_bytes"]) + 15) // 16 * 16
         if nbytes < (64 << 20):

@@ -134,7 +134,7 @@ _SIGS = {
     "fp8pa_cache_write": (ctypes.c_int, [ctypes.POINTER(WriteShape), _VP, _VP, _VP, _VP, _VP, _VP,
                                          _VP, _VP]),
     "fp8pa_debug_e4m3_to_f32": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP]),
-    "fp8pa_debug_stream_read": (ctypes.c_int, [_VP, ctypes.c_uint64, _VP, _VP]),
+    "fp8pa_debug_stream_read": (ctypes.c_int, [_VP, ctypes.c_uint64, ctypes.c_int32, _VP, _VP]),
     "fp8pa_debug_lds_tr16": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_mfma_scale_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
@@ -263,8 +263,8 @@ def fp8pa_debug_e4m3_to_f32(codes, out, n, stream=None) -> None:
         raise Fp8paError(st, "fp8pa_debug_e4m3_to_f32")
 
 
-def fp8pa_debug_stream_read(buf, nbytes, sink, stream=None) -> None:
-    st = lib().fp8pa_debug_stream_read(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream))
+def fp8pa_debug_stream_read(buf, nbytes, sink, stream=None, load_bytes=16) -> None:
+    st = lib().fp8pa_debug_stream_read(_ptr(buf), int(nbytes), int(load_bytes), _ptr(sink), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_stream_read")
 

@@ -2317,20 +2317,30 @@ __global__ void debug_lds_tr16_kernel(const uint8_t* src, const int32_t* addr, u
 // [x per_wg, (x + 1) per_wg), four loads in flight per lane; the XOR of
 // everything read is stored only in the impossible case that it equals a
 // fixed word, which keeps the loads alive.
-__global__ __launch_bounds__(256) void debug_read_kernel(const u32x4* __restrict__ buf, uint64_t n16,
+// W-byte loads (4, 8 or 16): the buffer is n W-byte words; a workgroup
+// streams per_wg of them, 64 bytes per lane in flight whatever W is.
+template <int W>
+__global__ __launch_bounds__(256) void debug_read_kernel(const uint8_t* __restrict__ buf, uint64_t n,
                                                          uint64_t per_wg, uint32_t* sink) {
+  using T = std::conditional_t<W == 16, u32x4, std::conditional_t<W == 8, u32x2, uint32_t>>;
+  constexpr int U = 64 / W;
+  const T* words = reinterpret_cast<const T*>(buf);
   const uint64_t base = uint64_t(blockIdx.x) * per_wg;
-  const uint64_t end = base + per_wg < n16 ? base + per_wg : n16;
+  const uint64_t end = base + per_wg < n ? base + per_wg : n;
   uint32_t acc = 0;
-  for (uint64_t i = base + threadIdx.x; i < end; i += 4 * 256) {
-    u32x4 v[4];
+  for (uint64_t i = base + threadIdx.x; i < end; i += U * 256) {
+    T v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint64_t idx = i + uint64_t(u) * 256;
-      v[u] = idx < end ? __builtin_nontemporal_load(&buf[idx]) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = idx < end ? __builtin_nontemporal_load(&words[idx]) : T{};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u) {
+      if constexpr (W == 16) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      else if constexpr (W == 8) acc ^= v[u].x ^ v[u].y;
+      else acc ^= v[u];
+    }
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
@@ -2745,19 +2755,27 @@ fp8pa_status fp8pa_debug_lds_tr8(const uint8_t* lds_bytes, const int32_t* row_ad
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 
-fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, int32_t load_bytes, uint32_t* sink,
+                                     void* stream) {
   if (!sink || (bytes > 0 && !buf)) return FP8PA_ERR_INVALID_ARG;
   if (bytes % 16 != 0) return FP8PA_ERR_INVALID_ARG;
+  if (load_bytes != 4 && load_bytes != 8 && load_bytes != 16) return FP8PA_ERR_INVALID_ARG;
   if (!aligned(buf, 16) || !aligned(sink, 4)) return FP8PA_ERR_MISALIGNED;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
   const int cu = cu_count_of(dev);
   if (cu < 1) return FP8PA_ERR_HIP;
-  const uint64_t n16 = bytes / 16;
+  const uint64_t n = bytes / uint64_t(load_bytes);
   const unsigned grid = bytes == 0 ? 1u : unsigned(2 * cu);
-  const uint64_t per_wg = (n16 + grid - 1) / grid;
-  debug_read_kernel<<<dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const u32x4*>(buf), n16, per_wg, sink);
+  const uint64_t per_wg = (n + grid - 1) / grid;
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (load_bytes == 16)
+    debug_read_kernel<16><<<dim3(grid), dim3(256), 0, st>>>(b, n, per_wg, sink);
+  else if (load_bytes == 8)
+    debug_read_kernel<8><<<dim3(grid), dim3(256), 0, st>>>(b, n, per_wg, sink);
+  else
+    debug_read_kernel<4><<<dim3(grid), dim3(256), 0, st>>>(b, n, per_wg, sink);
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 

@@ -93,12 +93,15 @@ fp8pa_status fp8pa_debug_lds_tr16(const uint8_t* lds_bytes, const int32_t* row_a
 
 /* One launch that reads `bytes` bytes of `buf` (16-byte aligned, bytes a
  * multiple of 16) and nothing else: two workgroups of 256 lanes per compute
- * unit, each streaming one contiguous chunk with 16-byte non-temporal loads,
- * four in flight per lane.  It is the practical ceiling of a kernel that
- * must read that many bytes from HBM in one launch (the benchmark times it
- * at each workload's KV byte count); bytes = 0 launches one empty workgroup,
- * the launch's own cost.  sink: one device uint32 the kernel may write. */
-fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+ * unit, each streaming one contiguous chunk with non-temporal loads of
+ * load_bytes (4, 8 or 16; else FP8PA_ERR_INVALID_ARG) each, 64 bytes in
+ * flight per lane.  It is the practical ceiling of a kernel that must read
+ * that many bytes from HBM in one launch (the benchmark times it at each
+ * workload's KV byte count, and at each load width); bytes = 0 launches one
+ * empty workgroup, the launch's own cost.  sink: one device uint32 the kernel
+ * may write. */
+fp8pa_status fp8pa_debug_stream_read(const void* buf, uint64_t bytes, int32_t load_bytes, uint32_t* sink,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -492,7 +492,10 @@ def test_stream_read_diagnostic_argument_checks():
     """fp8pa_debug_stream_read rejects its bad arguments before any GPU call."""
     lib = _lib.lib()
     sink = ctypes.c_uint32(0)
-    assert lib.fp8pa_debug_stream_read(16, 64, None, None) == _lib.FP8PA_ERR_INVALID_ARG
-    assert lib.fp8pa_debug_stream_read(None, 64, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_INVALID_ARG
-    assert lib.fp8pa_debug_stream_read(16, 65, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_INVALID_ARG
-    assert lib.fp8pa_debug_stream_read(24, 64, ctypes.addressof(sink), None) == _lib.FP8PA_ERR_MISALIGNED
+    s = ctypes.addressof(sink)
+    assert lib.fp8pa_debug_stream_read(16, 64, 16, None, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(None, 64, 16, s, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(16, 65, 16, s, None) == _lib.FP8PA_ERR_INVALID_ARG
+    for w in (0, 2, 12, 32, -16):
+        assert lib.fp8pa_debug_stream_read(16, 64, w, s, None) == _lib.FP8PA_ERR_INVALID_ARG
+    assert lib.fp8pa_debug_stream_read(24, 64, 16, s, None) == _lib.FP8PA_ERR_MISALIGNED
