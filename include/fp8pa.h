@@ -36,9 +36,11 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller; they must
- *    stay valid until the work queued on `stream` has finished.  The library
- *    allocates nothing, keeps no per-call state and never synchronises; the
- *    only state it holds is a cache of each device's compute-unit count.
+ *    stay valid until the work queued on `stream` has finished.  No call
+ *    allocates, keeps per-call state or synchronises; the library holds a
+ *    cache of each device's compute-unit count and, for
+ *    fp8pa_decode_noalloc only, one fixed scratch array per device (a
+ *    static device array, with its address looked up once per device).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is queued on it and the call returns at once; a call can be
  *    captured into a hipGraph from its first use.
