@@ -98,9 +98,11 @@ def _e4m3_page_stride(cache):
     """Bytes between the pages of a 4-D E4M3 pool that is dense inside each
     page: 0 when the pool is dense altogether (or has one page), the page
     stride otherwise (e.g. K and V pages interleaved in one buffer); None when
-    a page itself is strided.  The stride of a dimension of size 1 is never
-    used to address anything, so it is not looked at (torch leaves it
-    arbitrary, e.g. in a transposed view of pages of one token)."""
+    a page itself is strided, or pages overlap (a stride below one page, e.g.
+    an expanded view: the kernels would read past the storage).  The stride
+    of a dimension of size 1 is never used to address anything, so it is not
+    looked at (torch leaves it arbitrary, e.g. in a transposed view of pages
+    of one token)."""
     if cache.dim() != 4:
         return None
     dense = 1
@@ -108,13 +110,18 @@ def _e4m3_page_stride(cache):
         if cache.shape[d] != 1 and cache.stride(d) != dense:
             return None
         dense *= cache.shape[d]
-    return 0 if cache.shape[0] <= 1 or cache.stride(0) == dense else int(cache.stride(0))
+    if cache.shape[0] <= 1 or cache.stride(0) == dense:
+        return 0
+    return int(cache.stride(0)) if cache.stride(0) > dense else None
 
 
 def _row_stride(pool):
-    """Bytes between the pages of a 2-D block-scaled pool (0 = dense, or one
-    page, whose row stride addresses nothing)."""
-    return 0 if pool.shape[0] <= 1 else int(pool.stride(0))
+    """Bytes between the pages of a 2-D block-scaled pool: 0 when dense or of
+    one page (whose row stride addresses nothing), None when pages overlap (a
+    row stride below the row, e.g. an expanded view)."""
+    if pool.shape[0] <= 1:
+        return 0
+    return int(pool.stride(0)) if pool.stride(0) >= pool.shape[1] else None
 
 
 def _format_code(kv_format):
@@ -145,7 +152,10 @@ def shape_for(q, k_cache, block_table, k_scale, v_scale, *, window=0, sm_scale=N
         page_stride = _row_stride(k_cache)
     else:
         nb, bt, Hkv, Dk = _pool_dims(k_cache, layout)
-        page_stride = _e4m3_page_stride(k_cache) or 0
+        page_stride = _e4m3_page_stride(k_cache)
+    if page_stride is None:
+        raise ValueError("the pool's pages overlap or a page is strided: the kernels need each page "
+                         "dense and pages at least one page apart")
     if Dk != D:
         raise ValueError(f"head_dim mismatch: q has {D}, cache has {Dk}")
     if sm_scale is None:
@@ -206,7 +216,8 @@ def check_decode_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_sca
             raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
     if blockscaled:
         if (k_cache.dim() != 2 or v_cache.shape != k_cache.shape or k_cache.stride(1) != 1
-                or v_cache.stride(1) != 1 or _row_stride(v_cache) != _row_stride(k_cache)):
+                or v_cache.stride(1) != 1 or _row_stride(k_cache) is None
+                or _row_stride(v_cache) != _row_stride(k_cache)):
             raise ValueError("block-scaled pools must be equal uint8 [num_blocks, page_bytes] with unit "
                              "column stride")
         if num_kv_heads is None or block_tokens is None:
@@ -331,7 +342,7 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
         if nvfp4 and (t.dim() != 2 or t.stride(1) != 1):
             raise ValueError(f"{name}: block-scaled pools are uint8 [num_blocks, page_bytes]")
         if not nvfp4 and _e4m3_page_stride(t) is None:
-            raise ValueError(f"{name} must be an E4M3 pool dense inside each page")
+            raise ValueError(f"{name} must be an E4M3 pool dense inside each page, its pages not overlapping")
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be contiguous int64")
     T, Hkv, D = key.shape
@@ -339,8 +350,10 @@ def cache_write(key, value, slot_mapping, k_scale, v_scale, k_cache, v_cache, *,
         raise ValueError("key, value and slot_mapping disagree on the token count or shape")
     layout = _layout_code(kv_layout)
     if nvfp4:
-        if block_tokens is None or v_cache.shape != k_cache.shape or _row_stride(v_cache) != _row_stride(k_cache):
-            raise ValueError("block-scaled pools must match each other; pass block_tokens")
+        if (block_tokens is None or v_cache.shape != k_cache.shape or _row_stride(k_cache) is None
+                or _row_stride(v_cache) != _row_stride(k_cache)):
+            raise ValueError("block-scaled pools must match each other, with rows that do not overlap; "
+                             "pass block_tokens")
         nb, bt, page_stride = k_cache.shape[0], int(block_tokens), _row_stride(k_cache)
     else:
         nb, bt, Hkv_c, D_c = _pool_dims(k_cache, layout)

@@ -152,6 +152,35 @@ def test_size_one_dimensions_keep_any_stride():
         _check(k_cache=strided_rows, v_cache=strided_rows)
 
 
+def test_overlapping_pages_are_refused():
+    """Pools whose page stride is below one page (an expanded view, stride 0)
+    would send the kernels past the storage: refused in every path that
+    builds a shape from tensors, E4M3 and block-scaled."""
+    one = torch.zeros((1, BT, HKV, D), dtype=torch.uint8)
+    expanded = one.expand(NB, BT, HKV, D)
+    assert expanded.stride(0) == 0
+    assert fp._e4m3_page_stride(expanded) is None
+    with pytest.raises(ValueError):
+        _check(k_cache=expanded, v_cache=expanded)
+    a = _valid()
+    with pytest.raises(ValueError):
+        fp.shape_for(a["q"], expanded, a["block_table"], a["k_scale"], a["v_scale"], max_seq_len=40)
+    rows = torch.zeros((1, 4096), dtype=torch.uint8).expand(NB, 4096)
+    assert fp._row_stride(rows) is None
+    with pytest.raises(ValueError):
+        fp.shape_for(a["q"], rows, a["block_table"], a["k_scale"], a["v_scale"], max_seq_len=40,
+                     kv_format="nvfp4", num_kv_heads=HKV, block_tokens=BT)
+    # rows that overlap partly (stride below the row length)
+    base = torch.zeros(NB * 2048 + 2048, dtype=torch.uint8)
+    partly = base.as_strided((NB, 4096), (2048, 1))
+    assert fp._row_stride(partly) is None
+    # a writer into such pools is refused before any launch
+    key = torch.zeros((2, HKV, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fp.cache_write(key, key, torch.zeros(2, dtype=torch.int64), torch.ones(1), torch.ones(1),
+                       expanded, expanded)
+
+
 def test_table_width_against_max_seq_len():
     a = _valid()
     fp._check_table_width(a["block_table"], 4 * BT, a["k_cache"], "NHD", "e4m3", None)
