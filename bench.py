@@ -710,7 +710,7 @@ def _counter_rows(csv_dir, counter):
     for f in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                m = re.search(r"(\w+<[\d, ]+>|__amd_\w+)", r["Kernel_Name"])
+                m = re.search(r"(\w+<[\w, ]+>|__amd_\w+)", r["Kernel_Name"])
                 rows.append((int(r["Dispatch_Id"]), m.group(1) if m else r["Kernel_Name"][:40],
                              float(r["Counter_Value"])))
     return sorted(rows)

@@ -1283,12 +1283,13 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
 //   V: lane (n, qd) holds dims [S n, S n + S) (S = D/16, inside one block) of
 //     the 8 tokens kap(qd, j): S/2 data bytes and one scale byte each.
 // ---------------------------------------------------------------------------
-template <int D, int FMT, int NT>
+template <int D, int FMT, int NT, bool HV = false>
 __global__ __launch_bounds__(64 * kMaxWgWaves)
 __attribute__((amdgpu_waves_per_eu(2, 8))) void
 partial_mfma_nvfp4_kernel(Params p) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(FMT == FP8PA_KV_NVFP4 || FMT == FP8PA_KV_MXFP8, "block-scaled format");
+  static_assert(!HV || D == 128, "whole-record V scale loads");
   constexpr bool MX = FMT == FP8PA_KV_MXFP8;
   constexpr int S = D / 16;        // V dims per lane
   constexpr int KD = D / 4;        // K dims per lane per token
@@ -1374,6 +1375,14 @@ partial_mfma_nvfp4_kernel(Params p) {
     vdoff[j] = uint32_t((4 * qd + j) * tok + VDB * n);
     vsoff[j] = uint32_t((4 * qd + j) * stok + (S * n) / BLK);
   }
+  // HV (scale records of consecutive tokens adjacent, RB bytes each, as in
+  // head-major pages): a lane's four tokens of a group have one run of 4 RB
+  // bytes of V scales, read with one 16-byte load (MXFP8) instead of four
+  // one-byte loads; the lane takes its byte out of each record.  (The form
+  // also holds for NVFP4's 8-byte records, two 16-byte loads, which measured
+  // slower than the one-byte loads there; only MXFP8 takes it.)
+  constexpr int RB = D / BLK;
+  const uint32_t vsrun = uint32_t(4 * qd * RB);
 
   // Block-table entries of the split in registers, branch-free, as in the
   // FP8 kernel.
@@ -1407,7 +1416,7 @@ partial_mfma_nvfp4_kernel(Params p) {
     uint32_t kd[2][KDB / 4];
     uint32_t ks[2];
     uint32_t vd[8][VDW];
-    uint32_t vs[8];
+    uint32_t vs[HV ? 2 * RB : 8];  // HV: the group's 4 records; else one byte per token
   };
   auto load_tile = [&](int tt, TileRegs& r, int odd) {
     const int kb = tt * kTileTokens;
@@ -1432,10 +1441,11 @@ partial_mfma_nvfp4_kernel(Params p) {
         buf_load<KDB, AUX>(rkd, kdoff, r.kd[grp]);
       }
       buf_load<KSB, AUX>(rks, ksoff, &r.ks[grp]);
+      if constexpr (HV) buf_load<4 * RB, AUX>(rvs, vsrun, &r.vs[RB * grp]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         buf_load<VDB, AUX>(rvd, vdoff[j], r.vd[4 * grp + j]);
-        buf_load<1, AUX>(rvs, vsoff[j], &r.vs[4 * grp + j]);
+        if constexpr (!HV) buf_load<1, AUX>(rvs, vsoff[j], &r.vs[4 * grp + j]);
       }
     }
   };
@@ -1455,7 +1465,7 @@ partial_mfma_nvfp4_kernel(Params p) {
         const bool in_span = key >= ulo && key < uhi;
 #pragma unroll
         for (int w = 0; w < VDW; ++w) r.vd[j][w] = in_span ? r.vd[j][w] : 0u;
-        r.vs[j] = in_span ? r.vs[j] : 0u;
+        if constexpr (!HV) r.vs[j] = in_span ? r.vs[j] : 0u;
       }
     }
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -1541,6 +1551,25 @@ partial_mfma_nvfp4_kernel(Params p) {
         P[j + 1] = h.y;
       }
     }
+    // This lane's V scale byte of token kap(qd, j) (in the low byte): with HV
+    // out of the group's records (block (S n) / BLK of record j & 3), a token
+    // outside the attended span taking 0 as its data bytes did.
+    uint32_t vsj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (HV) {
+        const int blk = (S * n) / BLK;
+        const int wi = RB * (j >> 2) + (RB / 4) * (j & 3);
+        const uint32_t wv = RB == 8 ? ((blk >> 2) ? r.vs[wi + 1] : r.vs[wi]) : r.vs[wi];
+        vsj[j] = wv >> (8 * (blk & 3));
+        if (edge) {
+          const int key = kb + (j < 4 ? 4 * qd + j : 16 + 4 * qd + (j - 4));
+          vsj[j] = key >= ulo && key < uhi ? vsj[j] : 0u;
+        }
+      } else {
+        vsj[j] = r.vs[j];
+      }
+    }
     if constexpr (!MX) {
       // V^T operands in f16: token j's S dims as S/2 scaled f16 pairs, then
       // operand e takes element e of tokens kap(qd, 0..7), two tokens per
@@ -1548,7 +1577,7 @@ partial_mfma_nvfp4_kernel(Params p) {
       uint32_t vh[8][S / 2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.vs[j], 1.0f, false);
+        const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsj[j], 1.0f, false);
         const f16x2 sc = __builtin_shufflevector(s2, s2, 0, 0);
         const uint32_t w = r.vd[j][0];
         vh[j][0] = __builtin_bit_cast(uint32_t, f16x2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * sc);
@@ -1577,7 +1606,7 @@ partial_mfma_nvfp4_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // E4M3 times a power of two: the conversion applies it exactly
-        const float sc = e8m0_to_f32(r.vs[j] & 0xff);
+        const float sc = e8m0_to_f32(vsj[j] & 0xff);
         f32x2 e2[4];
         e2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, false);
         e2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.vd[j][0], sc, true);
@@ -2412,6 +2441,8 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
     if constexpr (D == 64)
       partial_mfma_nvfp4_kernel<64, FP8PA_KV_NVFP4, 0><<<grid, block, 0, st>>>(prm);
     else if constexpr (D == 128) {
+      // (one-byte V scale loads: the whole-record form measured slower with
+      // NVFP4's 8-byte records)
       if (pl.nt)
         partial_mfma_nvfp4_kernel<128, FP8PA_KV_NVFP4, 1><<<grid, block, 0, st>>>(prm);
       else
@@ -2421,8 +2452,15 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
     if constexpr (D == 64)
       partial_mfma_nvfp4_kernel<64, FP8PA_KV_MXFP8, 0><<<grid, block, 0, st>>>(prm);
     else if constexpr (D == 128) {
-      if (pl.nt)
+      // whole-record V scale loads where the records of consecutive tokens
+      // are adjacent (head-major pages, or one kv head)
+      const bool hv = prm.sc_tok == 128 / 32;
+      if (pl.nt && hv)
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 1, true><<<grid, block, 0, st>>>(prm);
+      else if (pl.nt)
         partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 1><<<grid, block, 0, st>>>(prm);
+      else if (hv)
+        partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 0, true><<<grid, block, 0, st>>>(prm);
       else
         partial_mfma_nvfp4_kernel<128, FP8PA_KV_MXFP8, 0><<<grid, block, 0, st>>>(prm);
     }
