@@ -3,7 +3,8 @@ caller owns the workspace), so decodes of different batches issued on two
 side streams, interleaved and overlapping, must give bit for bit what the
 same calls give one after the other on the default stream; the stream
 argument must be the one the work goes on; and a cache write followed by a
-decode on one side stream must see the written pages."""
+decode on one side stream must see the written pages.  Also: pools typed
+torch.float8_e4m3fn behave exactly as the same bytes typed uint8."""
 
 import numpy as np
 import pytest
@@ -115,3 +116,30 @@ def test_write_then_decode_on_a_side_stream():
     want_k, want_v = oracle.cache_write(bits(key), bits(val), np.array(slots, dtype=np.int64), wl.k_scale,
                                         wl.v_scale, wl.k_cache, wl.v_cache)
     assert np.array_equal(kw["k_cache"], want_k) and np.array_equal(kw["v_cache"], want_v)
+
+
+def test_float8_typed_pools_equal_byte_pools():
+    """Pools may be torch.float8_e4m3fn as well as uint8 (the same bytes):
+    decode and the cache writer give the same results bit for bit."""
+    wl = make_workload(B=3, q_len=2, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[300, 1000, 17], window=500,
+                       sinks=True, seed=906)
+    t = upload(wl)
+    t8 = dict(t)
+    t8["k"] = t["k"].clone().view(torch.float8_e4m3fn)
+    t8["v"] = t["v"].clone().view(torch.float8_e4m3fn)
+    o1, l1 = run(wl, t)
+    o2, l2 = run(wl, t8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    compare(*to_host(o2, l2), ro, rl, label="float8_e4m3fn pools")
+    # the writer into both forms of the same pages
+    rng = np.random.default_rng(907)
+    T = 40
+    key = torch.from_numpy(rng.standard_normal((T, wl.Hkv, wl.D)).astype(np.float32)).to("cuda").bfloat16()
+    val = torch.from_numpy(rng.standard_normal((T, wl.Hkv, wl.D)).astype(np.float32)).to("cuda").bfloat16()
+    slots = torch.from_numpy(rng.permutation(t["k"].shape[0] * wl.bt)[:T].astype(np.int64)).to("cuda")
+    fp.cache_write(key, val, slots, t["ks"], t["vs"], t["k"], t["v"])
+    fp.cache_write(key, val, slots, t8["ks"], t8["vs"], t8["k"], t8["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(t["k"], t8["k"].view(torch.uint8)) and torch.equal(t["v"], t8["v"].view(torch.uint8))
