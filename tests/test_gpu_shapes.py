@@ -1,8 +1,9 @@
 """A sweep of the shape space against the oracle: GQA ratios from 1 (MHA) to
 64 (one kv head for 64 query heads), 1, 2 and 5 query tokens, head_dim 64,
 128 and 256, so every planner branch is taken (VALU kernel, paired heads,
-two row blocks, head_dim split, LDS-shared row groups of 2, 4 and 8); and a
-batch past the balanced planner's limit (fixed splits)."""
+two row blocks, head_dim split, LDS-shared row groups of 2, 4 and 8); a
+batch past the balanced planner's limit (fixed splits); a sequence of 2^20
+tokens; and a max_seq_len bound far above the real lengths."""
 
 import pytest
 
@@ -45,3 +46,35 @@ def test_batch_past_the_balanced_limit(flags):
     ro, rl = oracle.decode(**wl.oracle_kwargs())
     out, lse = to_host(*run(wl, upload(wl), flags=flags))
     compare(out, lse, ro, rl, label=f"B=300 flags={flags}")
+
+
+@pytest.mark.parametrize("window", [0, 700000])
+def test_million_token_sequence(window):
+    """A sequence of 2^20 tokens beside a shorter one (the longest named
+    workload has 196,608): 256 splits of 128 tiles for the long one, a pool
+    of ~335 MB, every output row against the oracle, on the planned kernel
+    and the VALU kernel."""
+    wl = make_workload(seed=951, B=2, q_len=2, Hq=8, Hkv=2, D=64, bt=256, seq_lens=[1 << 20, 300001],
+                       window=window, sinks=True)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    t = upload(wl)
+    for flags in (0, fp.FP8PA_FLAG_FORCE_DOT):
+        out, lse = to_host(*run(wl, t, flags=flags))
+        compare(out, lse, ro, rl, label=f"2^20 tokens window={window} flags={flags}")
+
+
+@pytest.mark.parametrize("flags", [0, fp.FP8PA_FLAG_FORCE_DOT])
+def test_max_seq_len_far_above_the_lengths(flags):
+    """max_seq_len is only a bound: a caller that passes 2^20 for sequences of
+    5 to 2,000 tokens (the table as wide as the bound asks) gets the same
+    results; the plan and workspace follow the bound, the kernels the real
+    lengths."""
+    bound = 1 << 20
+    wl = make_workload(seed=952, B=3, q_len=1, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[100, 5, 2000],
+                       extra_table_cols=bound // 16 - 125, sinks=True)
+    assert wl.block_table.shape[1] >= bound // 16
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    t = upload(wl)
+    out, lse = fp.decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
+                         window=wl.window, sm_scale=wl.sm_scale, max_seq_len=bound, flags=flags)
+    compare(*to_host(out, lse), ro, rl, label=f"max_seq_len 2^20, flags={flags}")
