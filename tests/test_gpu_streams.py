@@ -4,7 +4,8 @@ side streams, interleaved and overlapping, must give bit for bit what the
 same calls give one after the other on the default stream; the stream
 argument must be the one the work goes on; and a cache write followed by a
 decode on one side stream must see the written pages.  Also: pools typed
-torch.float8_e4m3fn behave exactly as the same bytes typed uint8."""
+torch.float8_e4m3fn behave exactly as the same bytes typed uint8, and sinks
+at -inf add nothing."""
 
 import numpy as np
 import pytest
@@ -143,3 +144,32 @@ def test_float8_typed_pools_equal_byte_pools():
     fp.cache_write(key, val, slots, t8["ks"], t8["vs"], t8["k"], t8["v"])
     torch.cuda.synchronize()
     assert torch.equal(t["k"], t8["k"].view(torch.uint8)) and torch.equal(t["v"], t8["v"].view(torch.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "nvfp4"])
+@pytest.mark.parametrize("flags,ns", [(0, 0), (0, 1), (fp.FP8PA_FLAG_FORCE_DOT, 0)])
+def test_sinks_at_minus_infinity(fmt, flags, ns):
+    """A sink of -inf adds nothing: every sink at -inf gives the no-sink
+    result bit for bit (one split, where the partial kernel folds the sink,
+    and several, where the merge does), and a mix of -inf and finite sinks
+    matches the oracle."""
+    make = make_workload if fmt == "e4m3" else make_nvfp4_workload
+    kw = dict(B=3, q_len=2, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[500, 3, 1400], window=600, sinks=True, seed=960)
+    if fmt != "e4m3":
+        kw["kv_layout"] = "HND"
+    wl = make(**kw)
+    t = upload(wl)
+    ref_o, ref_l = fp.decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], None,
+                             window=wl.window, sm_scale=wl.sm_scale, max_seq_len=int(wl.seq_lens.max()),
+                             num_splits=ns, flags=flags, kv_layout=t["layout"], kv_format=fmt,
+                             num_kv_heads=wl.Hkv, block_tokens=wl.bt)
+    t["sinks"] = torch.full_like(t["sinks"], float("-inf"))
+    o, l = run(wl, t, num_splits=ns, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    mixed = wl.sinks.copy()
+    mixed[::2] = -np.inf
+    wl.sinks[:] = mixed
+    t["sinks"] = torch.from_numpy(mixed).cuda()
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    compare(*to_host(*run(wl, t, num_splits=ns, flags=flags)), ro, rl, label=f"{fmt} mixed -inf sinks")
