@@ -2268,6 +2268,101 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
     a.lse_out[row] = empty ? -INFINITY : (Mtu + log2_fast(Lsum)) * kLn2;
 }
 
+// The same merge for many rows with few splits each (chunked prefill: tens
+// of thousands of rows of 2-8 splits), where one wavefront per (row, 64
+// dims) would need several dependent rounds of tiny workgroups: a wavefront
+// takes 4 whole rows, 16 lanes each (D / 16 dims per lane), and issues the
+// LSEs and partial outputs of a row's first U splits together with its
+// split count, so a row of up to U splits takes one round trip; further
+// splits follow in batches of U.  Splits past a row's count, read before the
+// count is known, are dropped, and a zero weight never multiplies a partial
+// (an empty split's payload may be anything).
+template <int D>
+__global__ __launch_bounds__(64) void merge_rows_kernel(MergeArgs a) {
+  constexpr int VPL = D / 16;          // dims per lane
+  constexpr int NV = VPL / 4;          // their float4s
+  constexpr int U = D == 256 ? 4 : 8;  // splits per batch
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int row0 = int(blockIdx.x) * 4 + (lane >> 4);
+  const bool valid = row0 < a.num_rows;
+  const int row = valid ? row0 : a.num_rows - 1;
+  const int S = a.num_splits;
+  // (issued first: the split count is the one value everything else waits on)
+  const int ns_loaded = a.nsplit ? a.nsplit[row / a.rows_per_seq] : S;
+  const float* lrow = a.pl + (size_t)row * S;
+  const f32x4* orow = reinterpret_cast<const f32x4*>(a.po + (size_t)row * S * D + l16 * VPL);
+  float lv[U];
+  f32x4 ov[U][NV];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int sl = min(u, S - 1);
+    lv[u] = lrow[sl];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) ov[u][v] = orow[(size_t)sl * (D / 4) + v];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int ns = min(max(ns_loaded, 1), S);
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) M = u < ns ? fmaxf(M, lv[u] * kLog2e) : M;
+  for (int sl = U; sl < ns; ++sl) M = fmaxf(M, lrow[sl] * kLog2e);
+  const float Mu = M == -INFINITY ? 0.f : M;  // every weight is 0 then
+  float lpart = 0.f;
+  f32x4 acc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto take = [&](const float (&l)[U], const f32x4 (&o)[U][NV], int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = base + u < ns ? exp2_fast(l[u] * kLog2e - Mu) : 0.f;
+      lpart += w;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[v][i] = w > 0.f ? fmaf(w, o[u][v][i], acc[v][i]) : acc[v][i];
+      }
+    }
+  };
+  take(lv, ov, 0);
+  for (int base = U; base < ns; base += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = min(base + u, ns - 1);
+      lv[u] = lrow[sl];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) ov[u][v] = orow[(size_t)sl * (D / 4) + v];
+    }
+    take(lv, ov, base);
+  }
+  // combine: the sink joins once, in log2 units like the partial maxima
+  const float sink2 = a.sinks ? a.sinks[row % a.Hq] * kLog2e : -INFINITY;
+  const float Mt = fmaxf(sink2, M);
+  const float Mtu = Mt == -INFINITY ? 0.f : Mt;
+  const float f = M > -INFINITY ? exp2_fast(M - Mtu) : 0.f;
+  const float Lsum = fmaf(f, lpart, sink2 > -INFINITY ? exp2_fast(sink2 - Mtu) : 0.f);
+  const bool empty = !(Lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / Lsum;
+  if (!valid) return;
+  uint32_t packed[VPL / 2];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    packed[2 * v] = pack_bf16x2(f * acc[v][0] * inv, f * acc[v][1] * inv);
+    packed[2 * v + 1] = pack_bf16x2(f * acc[v][2] * inv, f * acc[v][3] * inv);
+  }
+  uint32_t* orow_out = reinterpret_cast<uint32_t*>(a.out + (size_t)row * D + l16 * VPL);
+  if constexpr (VPL == 4) {
+    *reinterpret_cast<u32x2*>(orow_out) = u32x2{packed[0], packed[1]};
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL / 8; ++v)
+      reinterpret_cast<u32x4*>(orow_out)[v] =
+          u32x4{packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]};
+  }
+  if (a.lse_out && l16 == 0)
+    a.lse_out[row] = empty ? -INFINITY : (Mtu + log2_fast(Lsum)) * kLn2;
+}
+
 // ---------------------------------------------------------------------------
 // Diagnostics: the conversion instruction and the MFMA operand layout the
 // kernels rely on.
@@ -2511,12 +2606,20 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
 
 // Wavefronts per merge workgroup: one while the rows alone give each compute
 // unit a few workgroups, four (splits of a row in parallel) for few rows.
-int merge_waves(int64_t workgroups, int cu) { return workgroups >= 4 * int64_t(cu) ? 1 : 4; }
+// Wavefronts per (row, 64 dims) workgroup: 4 when the rows give fewer than 4
+// workgroups per CU, 1 up to 32 per CU (one resident round), and beyond that
+// 0: the many-rows kernel (4 whole rows per wavefront).
+int merge_waves(int64_t workgroups, int cu) {
+  if (workgroups > 32 * int64_t(cu)) return 0;
+  return workgroups >= 4 * int64_t(cu) ? 1 : 4;
+}
 
 template <int D>
 void launch_merge_d(const MergeArgs& a, int waves, hipStream_t st) {
   const dim3 grid(unsigned(int64_t(a.num_rows) * (D / 64)));
-  if (waves == 1)
+  if (waves == 0)
+    merge_rows_kernel<D><<<dim3(unsigned((a.num_rows + 3) / 4)), dim3(64), 0, st>>>(a);
+  else if (waves == 1)
     merge_kernel<D, 1><<<grid, dim3(64), 0, st>>>(a);
   else
     merge_kernel<D, 4><<<grid, dim3(256), 0, st>>>(a);

@@ -450,6 +450,32 @@ def test_merge_matches_oracle(D):
         compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"merge D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 8, 9, 20])
+def test_merge_many_rows_matches_oracle(D, S):
+    """More rows than one round of (row, 64 dims) workgroups holds (chunked
+    prefill): the many-rows merge, 4 rows per wavefront, splits in batches,
+    a row count that is not a multiple of 4, empty splits with NaN payloads."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    R, Hq = (32 * cu) // (D // 64) + 7, 8
+    rng = np.random.default_rng(1000 * D + S)
+    po = rng.standard_normal((R, S, D)).astype(np.float32)
+    pl = (rng.standard_normal((R, S)) * 3).astype(np.float32)
+    pl[rng.random((R, S)) < 0.25] = -np.inf
+    pl[5, :] = -np.inf
+    po[np.isneginf(pl)] = np.nan
+    sinks = rng.standard_normal(Hq).astype(np.float32)
+    for use_sinks in (False, True):
+        out = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((R,), dtype=torch.float32, device="cuda")
+        sk = torch.from_numpy(sinks).cuda() if use_sinks else None
+        fp.fp8pa_merge(S, R, Hq, D, torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), sk, out, lse)
+        torch.cuda.synchronize()
+        ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64),
+                              np.tile(sinks, R // Hq + 1)[:R] if use_sinks else None)
+        compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"many-rows merge D={D} S={S}")
+
+
 # --------------------------------------------------- full-size named workloads
 
 _cfg_cache = {}

@@ -78,3 +78,15 @@ def test_max_seq_len_far_above_the_lengths(flags):
     out, lse = fp.decode(t["q"], t["k"], t["v"], t["bt"], t["sl"], t["ks"], t["vs"], t["sinks"],
                          window=wl.window, sm_scale=wl.sm_scale, max_seq_len=bound, flags=flags)
     compare(*to_host(out, lse), ro, rl, label=f"max_seq_len 2^20, flags={flags}")
+
+
+@pytest.mark.parametrize("ns", [0, 3])
+def test_prefill_rows_past_one_merge_round(ns):
+    """A 256-token chunk of 16 query heads over two sequences: 8,192 rows, so
+    the splits merge through the many-rows merge; every row against the
+    oracle."""
+    wl = make_workload(seed=953, B=2, q_len=256, Hq=16, Hkv=4, D=128, bt=16, seq_lens=[2600, 900], window=1500,
+                       sinks=True)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, upload(wl), num_splits=ns))
+    compare(out, lse, ro, rl, label=f"prefill 8192 rows, splits={ns}")
