@@ -681,22 +681,28 @@ partial_mfma_kernel(Params p) {
   // i.e. of the four groups that loop step k loads (0 for a group that holds
   // no attended token).  A split spans at most kMaxSplitTiles tiles (64
   // steps), so the loop reads each page number with one readlane from a
-  // fixed register, and has no table loads and no waits on them.
+  // fixed register, and has no table loads and no waits on them.  (The
+  // LDS-shared kernels take splits of up to 2 kMaxSplitTiles tiles: each
+  // staging wavefront loads the next window of entries into the same
+  // registers just before it stages its first tile there, one wait per 128
+  // tiles; fewer splits for long chunks, so half the partial outputs to
+  // write and merge and half the workgroup rounds.)
   // (branch-free: a lane whose group holds no attended token reads at an
   // offset past the descriptor and gets 0, so the four loads issue back to
   // back with no wait between them)
   int tab[4];
-  {
-    const Rsrc rt = __builtin_amdgcn_make_buffer_rsrc((void*)btab, 0, p.table_stride * 4, kRsrcWord3);
+  const Rsrc rtab = __builtin_amdgcn_make_buffer_rsrc((void*)btab, 0, p.table_stride * 4, kRsrcWord3);
+  auto load_table = [&](int t0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int tt = ts + 2 * lane + (g >> 1);
+      const int tt = t0 + 2 * lane + (g >> 1);
       const int gk = tt * kTileTokens + 16 * (g & 1);
       const bool live = tt < te && gk < uhi && gk + 16 > ulo;
-      tab[g] = int(__builtin_amdgcn_raw_buffer_load_b32(rt, live ? uint32_t(gk >> p.bt_shift) * 4u : kOob,
+      tab[g] = int(__builtin_amdgcn_raw_buffer_load_b32(rtab, live ? uint32_t(gk >> p.bt_shift) * 4u : kOob,
                                                          0, 0));
     }
-  }
+  };
+  load_table(ts);
   // The query rows' raw bf16 bits; converted after the first tiles' loads
   // are issued, so the two round trips overlap.  Every lane loads (a row
   // past the last, or the other head's dims, reads row 0's valid bytes) and
@@ -1146,7 +1152,7 @@ partial_mfma_kernel(Params p) {
       stage_write(0, ts);
       stage_load(ts + 2);
     }
-    for (int tt = ts; tt < te; ++tt) {
+    auto step = [&](int tt) {
       const int odd = (tt - ts) & 1;
       __syncthreads();  // tile tt is in its slot; the other slot's readers are done
       lds_read(odd, ta);
@@ -1155,7 +1161,15 @@ partial_mfma_kernel(Params p) {
         stage_load(tt + 3);
       }
       compute_tile(tt, ta, odd);
-    }
+    };
+    // Steps before ts + 125 stage tiles of the first window of table
+    // entries; both halves have staged their last one by then, so the
+    // second window loads there, outside the loops.
+    const int tmid = min(te, ts + kMaxSplitTiles - 3);
+    int tt = ts;
+    for (; tt < tmid; ++tt) step(tt);
+    if (tt < te) load_table(ts + kMaxSplitTiles);
+    for (; tt < te; ++tt) step(tt);
   } else {
   // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {

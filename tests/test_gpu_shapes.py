@@ -90,3 +90,26 @@ def test_prefill_rows_past_one_merge_round(ns):
     ro, rl = oracle.decode(**wl.oracle_kwargs())
     out, lse = to_host(*run(wl, upload(wl), num_splits=ns))
     compare(out, lse, ro, rl, label=f"prefill 8192 rows, splits={ns}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("window", [0, 9000])
+@pytest.mark.parametrize("ns", [0, 1, 2])
+def test_prefill_splits_past_one_table_window(d, window, ns):
+    """Row groups sharing tiles through LDS take splits of up to 256 tiles,
+    whose block-table entries sit in two 128-tile register windows: a
+    64-token chunk over 12,000 tokens (375 tiles) split in one, two or the
+    planner's number of parts (splits of 188-256 tiles cross into the
+    second window), every row against the oracle."""
+    wl = make_workload(seed=954, B=1, q_len=64, Hq=16, Hkv=4, D=d, bt=16, seq_lens=[12000], window=window,
+                       sinks=True)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    t = upload(wl)
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=window, max_seq_len=12000,
+                         num_splits=ns)
+    plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["row_groups_per_wg"] > 1
+    if ns:
+        assert plan["tiles_per_split"] > 128
+    out, lse = to_host(*run(wl, t, num_splits=ns))
+    compare(out, lse, ro, rl, label=f"LDS-shared splits past 128 tiles D={d} window={window} splits={ns}")
