@@ -162,9 +162,10 @@ fp8pa_status make_plan(const fp8pa_shape* s, int32_t cu_count, Plan* plan) {
     if (wk < max_keys) max_keys = wk;
   }
   const int64_t n_tiles = ceil_div(max_keys, kTileTokens) + (s->window > 0 ? 1 : 0);
-  // Both kernels hold a split's block-table entries in registers: one
-  // window of kMaxSplitTiles tiles, two in the LDS-shared kernels.
-  const int64_t tps_cap = p.lw ? 2 * kMaxSplitTiles : kMaxSplitTiles;
+  // Both kernels hold a split's block-table entries in registers, one
+  // window of kMaxSplitTiles tiles; the LDS-shared kernels reload the window
+  // as they go, so their splits may be longer.
+  const int64_t tps_cap = p.lw ? kMaxSplitTilesLds : kMaxSplitTiles;
   p.tps_cap = int32_t(tps_cap < n_tiles ? tps_cap : n_tiles);
 
   // Splits: enough (sequence, split) items that the busy wavefronts fill the

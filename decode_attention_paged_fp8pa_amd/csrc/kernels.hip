@@ -682,11 +682,11 @@ partial_mfma_kernel(Params p) {
   // no attended token).  A split spans at most kMaxSplitTiles tiles (64
   // steps), so the loop reads each page number with one readlane from a
   // fixed register, and has no table loads and no waits on them.  (The
-  // LDS-shared kernels take splits of up to 2 kMaxSplitTiles tiles: each
+  // LDS-shared kernels take splits of up to kMaxSplitTilesLds tiles: each
   // staging wavefront loads the next window of entries into the same
   // registers just before it stages its first tile there, one wait per 128
-  // tiles; fewer splits for long chunks, so half the partial outputs to
-  // write and merge and half the workgroup rounds.)
+  // tiles; fewer splits for long chunks, so fewer partial outputs to write
+  // and merge and fewer workgroup rounds.)
   // (branch-free: a lane whose group holds no attended token reads at an
   // offset past the descriptor and gets 0, so the four loads issue back to
   // back with no wait between them)
@@ -1162,14 +1162,17 @@ partial_mfma_kernel(Params p) {
       }
       compute_tile(tt, ta, odd);
     };
-    // Steps before ts + 125 stage tiles of the first window of table
-    // entries; both halves have staged their last one by then, so the
-    // second window loads there, outside the loops.
-    const int tmid = min(te, ts + kMaxSplitTiles - 3);
+    // Steps before w0 + 125 stage tiles of the table window that starts at
+    // w0; both halves have staged their last one by then, so the next
+    // window's entries load there, between two runs of the loop.
     int tt = ts;
-    for (; tt < tmid; ++tt) step(tt);
-    if (tt < te) load_table(ts + kMaxSplitTiles);
-    for (; tt < te; ++tt) step(tt);
+#pragma unroll 1
+    for (int w0 = ts;; w0 += kMaxSplitTiles) {
+      const int tend = min(te, w0 + kMaxSplitTiles - 3);
+      for (; tt < tend; ++tt) step(tt);
+      if (tt >= te) break;
+      load_table(w0 + kMaxSplitTiles);
+    }
   } else {
   // two tiles in flight: tile t + 1 loads while tile t is computed
   for (int tt = ts; tt < te; tt += 2) {

@@ -14,7 +14,8 @@ constexpr int kRowsMfma = 16;        // query rows per wavefront: the MFMA N dim
 constexpr int kRowsDot = 4;          // query rows per wavefront in the VALU dot kernel
 constexpr size_t kWorkspaceAlign = 256;
 constexpr int kMaxWgWaves = 8;       // wavefronts of a partial-kernel workgroup, at most
-constexpr int kMaxSplitTiles = 128;  // tiles an MFMA split may span (64 two-tile steps, a lane each; twice that in the LDS-shared kernels)
+constexpr int kMaxSplitTiles = 128;  // tiles an MFMA split may span (64 two-tile steps, a lane each)
+constexpr int kMaxSplitTilesLds = 1024;  // ... in the LDS-shared kernels, which reload the table window
 constexpr int kMaxBalancedBatch = 256; // sequences a wavefront scans (4 per lane)
 
 // K scale groups along head_dim: 0 and 1 both mean one group; otherwise 2, 4,

@@ -287,26 +287,29 @@ def test_row_blocks_for_many_rows():
     assert p["row_blocks"] == 1 and p["waves_per_head"] == 2
 
 
-def test_long_chunk_splits_span_two_table_windows():
-    """The LDS-shared kernels hold two 128-tile windows of block-table
-    entries, so a long chunk's fixed splits span up to 256 tiles (4 splits
-    of a 32,768-token context instead of 8); the other kernels keep 128."""
+def test_long_chunk_splits_span_several_table_windows():
+    """The LDS-shared kernels reload their 128-tile window of block-table
+    entries as they go, so a long chunk's fixed splits span up to 1,024
+    tiles (2 splits of a 32,768-token context, one round of workgroups,
+    instead of 8); the other kernels keep 128."""
     s = fp.make_shape(batch=2, q_len=512, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
                       num_blocks=4096, block_table_stride=2048, max_seq_len=32768, sm_scale=0.1)
     p = fp.fp8pa_plan(s, 256)
     assert p["row_groups_per_wg"] == 8
-    assert p["split_mode"] == fp.FP8PA_SPLIT_FIXED and p["tiles_per_split"] == 256 and p["num_splits"] == 4
-    assert p["max_tiles_per_split"] == 256
+    assert p["split_mode"] == fp.FP8PA_SPLIT_FIXED and p["tiles_per_split"] == 512 and p["num_splits"] == 2
+    assert p["max_tiles_per_split"] == 1024 and p["grid_wgs"] == 512
     # one query row per kv head: no LDS sharing, 128-tile splits
     s1 = fp.make_shape(batch=2, q_len=1, num_q_heads=8, num_kv_heads=8, head_dim=128, block_tokens=16,
                        num_blocks=4096, block_table_stride=2048, max_seq_len=32768, sm_scale=0.1)
     p1 = fp.fp8pa_plan(s1, 256)
     assert p1["row_groups_per_wg"] <= 1 and p1["max_tiles_per_split"] <= 128
-    # a caller's split count still bounds the chunk by the windows
-    s2 = fp.make_shape(batch=2, q_len=512, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
-                       num_blocks=4096, block_table_stride=2048, max_seq_len=32768, sm_scale=0.1, num_splits=2)
-    p2 = fp.fp8pa_plan(s2, 256)
-    assert p2["tiles_per_split"] == 256 and p2["num_splits"] == 4
+    # a caller's split count is honoured up to the cap
+    for ns, tps in ((1, 1024), (2, 512), (3, 342)):
+        s2 = fp.make_shape(batch=2, q_len=512, num_q_heads=32, num_kv_heads=8, head_dim=128, block_tokens=16,
+                           num_blocks=4096, block_table_stride=2048, max_seq_len=32768, sm_scale=0.1,
+                           num_splits=ns)
+        p2 = fp.fp8pa_plan(s2, 256)
+        assert p2["tiles_per_split"] == tps and p2["num_splits"] == ns
 
 
 def test_plan_accepts_k_groups():
@@ -439,7 +442,8 @@ def test_balanced_plan_covers_every_tile(seed):
         assert sum(len(v) for v in items.values()) <= p["grid_wgs"] // upi
         assert max(len(v) for v in items.values()) <= p["num_splits"]
         # the splits of a sequence tile its key span exactly, each within the
-        # block-table registers (<= 128 tiles; 256 in the LDS-shared kernels)
+        # block-table registers (<= 128 tiles; the LDS-shared kernels reload
+        # them every 128 tiles, up to 1,024)
         for b, L in enumerate(seq):
             spans = items[b]
             lo = (max(0, L - q_len - window + 1) if window > 0 else 0) // 32
@@ -448,7 +452,7 @@ def test_balanced_plan_covers_every_tile(seed):
                 assert a1 == b0 and a0 < a1
             for a0, a1 in spans:
                 if p["variant"] == 1:
-                    assert a1 - a0 <= (256 if p["row_groups_per_wg"] > 1 else 128)
+                    assert a1 - a0 <= (1024 if p["row_groups_per_wg"] > 1 else 128)
 
 
 def _write_shape(**over):

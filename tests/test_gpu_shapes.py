@@ -94,18 +94,19 @@ def test_prefill_rows_past_one_merge_round(ns):
 
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("window", [0, 9000])
-@pytest.mark.parametrize("ns", [0, 1, 2])
-def test_prefill_splits_past_one_table_window(d, window, ns):
-    """Row groups sharing tiles through LDS take splits of up to 256 tiles,
-    whose block-table entries sit in two 128-tile register windows: a
-    64-token chunk over 12,000 tokens (375 tiles) split in one, two or the
-    planner's number of parts (splits of 188-256 tiles cross into the
-    second window), every row against the oracle."""
-    wl = make_workload(seed=954, B=1, q_len=64, Hq=16, Hkv=4, D=d, bt=16, seq_lens=[12000], window=window,
+@pytest.mark.parametrize("ns,ctx", [(0, 12000), (1, 12000), (2, 12000), (1, 40000)])
+def test_prefill_splits_past_one_table_window(d, window, ns, ctx):
+    """Row groups sharing tiles through LDS take splits of up to 1,024
+    tiles, reloading their 128-tile register window of block-table entries
+    as they go: a 64-token chunk over 12,000 tokens (375 tiles) in one
+    (3 windows, the output written directly), two or the planner's number
+    of parts, and over 40,000 tokens (1,250 tiles: a 1,024-tile split, 8
+    windows), every row against the oracle."""
+    wl = make_workload(seed=954, B=1, q_len=64, Hq=16, Hkv=4, D=d, bt=16, seq_lens=[ctx], window=window,
                        sinks=True)
     ro, rl = oracle.decode(**wl.oracle_kwargs())
     t = upload(wl)
-    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=window, max_seq_len=12000,
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], window=window, max_seq_len=ctx,
                          num_splits=ns)
     plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
     assert plan["row_groups_per_wg"] > 1
