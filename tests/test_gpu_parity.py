@@ -429,13 +429,16 @@ def test_workspace_too_small_is_reported():
 # ------------------------------------------------------------------ merge
 
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_merge_matches_oracle(D):
-    rng = np.random.default_rng(D)
-    R, S, Hq = 40, 5, 8
+@pytest.mark.parametrize("R,S", [(40, 5), (10, 100), (3, 300)])
+def test_merge_matches_oracle(D, R, S):
+    """Few splits (one wavefront per row and 64 dims, or four), and many
+    (sixteen wavefronts per row and 64 dims, each a share of the splits)."""
+    rng = np.random.default_rng(D + 7 * S)
+    Hq = 8
     po = rng.standard_normal((R, S, D)).astype(np.float32)
     pl = (rng.standard_normal((R, S)) * 3).astype(np.float32)
     pl[rng.random((R, S)) < 0.25] = -np.inf
-    pl[3, :] = -np.inf
+    pl[min(3, R - 1), :] = -np.inf
     po[np.isneginf(pl)] = np.nan            # never read for an empty split
     sinks = rng.standard_normal(Hq).astype(np.float32)
     for use_sinks in (False, True):
@@ -447,7 +450,7 @@ def test_merge_matches_oracle(D):
         torch.cuda.synchronize()
         ro, rl = oracle.merge(po.astype(np.float64), pl.astype(np.float64),
                               np.tile(sinks, R // Hq + 1)[:R] if use_sinks else None)
-        compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"merge D={D}")
+        compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, label=f"merge D={D} R={R} S={S}")
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
