@@ -418,10 +418,21 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
   // which keeps the tile range, and so every buffer descriptor, scalar)
   const int T = __builtin_amdgcn_readfirstlane(wave_sum_i(tsum));
   const int M = __builtin_amdgcn_readfirstlane(wave_max_i(tmax));
-  int c = ceil_div_i(T, p.target_items);
-  c = max(c, min(p.min_tiles, max(1, (2 * T) / p.target_items)));
-  c = max(c, ceil_div_i(M, p.num_splits));
-  c = min(c, p.tps_cap);
+  const int floor_c = max(min(p.min_tiles, max(1, (2 * T) / p.target_items)), ceil_div_i(M, p.num_splits));
+  int c = min(max(ceil_div_i(T, p.target_items), floor_c), p.tps_cap);
+  // The grid holds target_items + B items, and sum_b ceil(n_b / c) <= T / c
+  // + B is what keeps c >= T / target_items within it.  That bound is loose
+  // (sequences of equal length reach T / c): a chunk of T / (target_items +
+  // B) is taken instead when its items still fit, so that one round of
+  // workgroups carries less per workgroup.
+  const int slots = p.target_items + p.B;
+  const int ct = min(max(ceil_div_i(T, slots), floor_c), p.tps_cap);
+  if (ct < c) {
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt += lane + 64 * j < p.B ? splits_of(nj[j], ct, p.num_splits) : 0;
+    if (__builtin_amdgcn_readfirstlane(wave_sum_i(cnt)) <= slots) c = ct;
+  }
   int base = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

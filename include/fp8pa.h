@@ -145,7 +145,9 @@ typedef struct fp8pa_shape {
 #define FP8PA_SPLIT_FIXED    1 /* every sequence: splits of tiles_per_split tiles */
 #define FP8PA_SPLIT_BALANCED 2 /* the kernel reads all seq_lens and picks one chunk size
                                   (<= max_tiles_per_split) so that the (sequence, split)
-                                  items of the whole batch come to about target_items;
+                                  items of the whole batch come to about target_items,
+                                  never more than the target_items + batch workgroup
+                                  slots (the smaller chunk T / slots where it fits);
                                   idle workgroups exit */
 
 /* The plan one call will run (see fp8pa_plan). */

@@ -405,12 +405,22 @@ def _balanced_items(plan, seq_lens, q_len, window):
     n = [span(L)[1] - span(L)[0] for L in seq_lens]
     T, M = sum(n), max(n)
     tgt = plan["target_items"]
-    c = max(-(-T // tgt), min(plan["tiles_per_split"], max(1, 2 * T // tgt)), -(-M // plan["num_splits"]))
-    c = min(c, plan["max_tiles_per_split"])
+    ns_max = plan["num_splits"]
+
+    def splits(x, c):
+        return min(-(-x // c), ns_max) if x > 0 else 1
+
+    floor_c = max(min(plan["tiles_per_split"], max(1, 2 * T // tgt)), -(-M // ns_max))
+    c = min(max(-(-T // tgt), floor_c), plan["max_tiles_per_split"])
+    # the tighter chunk T / (target + B), where its items fit the target + B slots
+    slots = tgt + len(seq_lens)
+    ct = min(max(-(-T // slots), floor_c), plan["max_tiles_per_split"])
+    if ct < c and sum(splits(x, ct) for x in n) <= slots:
+        c = ct
     out = {}
     for b, L in enumerate(seq_lens):
         t0, t1 = span(L)
-        ns = min(-(-n[b] // c), plan["num_splits"]) if n[b] > 0 else 1
+        ns = splits(n[b], c)
         out[b] = [(t0 + s * c, min(t0 + s * c + c, t1)) for s in range(ns)]
     return out, c
 
@@ -454,6 +464,30 @@ def test_balanced_plan_covers_every_tile(seed):
                 if p["variant"] == 1:
                     assert a1 - a0 <= (1024 if p["row_groups_per_wg"] > 1 else 128)
 
+
+
+@pytest.mark.parametrize("B,q_len,Hq,Hkv,L,want_c", [
+    (16, 16, 32, 8, 8192, 32),   # LDS-shared, 4 row groups: 8 splits x 16 = all 128 slots
+    (16, 1, 32, 8, 4096, 8),     # MFMA decode: 16 splits x 16 = 256 slots
+    (16, 1, 8, 8, 2000, 4),      # VALU decode (MHA): 16 splits x 16 = 256 slots
+])
+def test_balanced_chunk_fills_the_slots_for_equal_lengths(B, q_len, Hq, Hkv, L, want_c):
+    """Equal lengths reach the items bound exactly, so the chunk T / (target
+    + B) fits: one round of workgroups, each with the least work (the looser
+    T / target would leave slots idle and give every workgroup more)."""
+    s = fp.make_shape(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, block_tokens=16,
+                      num_blocks=1 << 16, block_table_stride=-(-L // 16), max_seq_len=L, sm_scale=0.1)
+    p = fp.fp8pa_plan(s, 256)
+    assert p["split_mode"] == fp.FP8PA_SPLIT_BALANCED
+    items, c = _balanced_items(p, [L] * B, q_len, 0)
+    slots = p["target_items"] + B
+    assert c == want_c
+    assert sum(len(v) for v in items.values()) == slots
+    upi = (Hkv // p["heads_per_wg"]) * (p["row_groups"] // p["row_groups_per_wg"])
+    assert p["grid_wgs"] == slots * upi
+    # the looser chunk would have left slots idle
+    T = B * -(-L // 32)
+    assert -(-T // p["target_items"]) > c
 
 def _write_shape(**over):
     kw = dict(num_tokens=4, key_stride=1024, value_stride=1024, num_kv_heads=8, head_dim=128,

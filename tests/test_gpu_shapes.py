@@ -114,3 +114,33 @@ def test_prefill_splits_past_one_table_window(d, window, ns, ctx):
         assert plan["tiles_per_split"] > 128
     out, lse = to_host(*run(wl, t, num_splits=ns))
     compare(out, lse, ro, rl, label=f"LDS-shared splits past 128 tiles D={d} window={window} splits={ns}")
+
+
+EQUAL_LENGTHS = [
+    # (B, q_len, Hq, Hkv, D, length): the MFMA kernel, the VALU kernel (MHA)
+    # and the LDS-shared kernel of four row groups (a 16-token prefill chunk)
+    (16, 1, 32, 8, 128, 4096),
+    (16, 1, 8, 8, 128, 2000),
+    (16, 16, 32, 8, 128, 8192),
+]
+
+
+@pytest.mark.parametrize("B,ql,hq,hkv,d,L", EQUAL_LENGTHS)
+def test_balanced_equal_lengths_fill_every_slot(B, ql, hq, hkv, d, L):
+    """Sequences of one length: the balanced chunk is T / slots (every
+    workgroup slot of the grid gets an item) rather than the looser
+    T / (slots - B); every output row against the oracle."""
+    from tests.test_abi import _balanced_items
+
+    wl = make_workload(seed=995 + L, B=B, q_len=ql, Hq=hq, Hkv=hkv, D=d, bt=16, seq_lens=[L] * B,
+                       poison=False)
+    t = upload(wl)
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], sm_scale=wl.sm_scale, max_seq_len=L)
+    plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["split_mode"] == fp.FP8PA_SPLIT_BALANCED
+    items, c = _balanced_items(plan, [L] * B, ql, 0)
+    n = -(-L // 32)
+    assert sum(len(v) for v in items.values()) == B * -(-n // c)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, t))
+    compare(out, lse, ro, rl, label=f"B={B} q_len={ql} Hq={hq} Hkv={hkv} L={L} chunk {c}")
