@@ -489,6 +489,29 @@ def test_balanced_chunk_fills_the_slots_for_equal_lengths(B, q_len, Hq, Hkv, L, 
     T = B * -(-L // 32)
     assert -(-T // p["target_items"]) > c
 
+
+@pytest.mark.parametrize("q_len,Hq,Hkv,lens,want_c", [
+    (2, 8, 8, [5085, 2774, 2270, 5884, 5711, 4095, 2456, 1340, 5625, 1685, 3381, 4080, 1516, 1959, 4474, 1264,
+               4078, 5673, 4136, 3912, 2836, 5810], 11),
+    (1, 32, 8, [4161, 3420, 5205, 2506, 2790, 2814, 2231, 169, 4104, 3136, 1265, 4340, 1425, 2623, 2371, 2469,
+                3072, 2976, 3474, 868, 5734, 624, 1445], 9),
+])
+def test_balanced_chunk_keeps_the_bound_when_the_tight_one_overflows(q_len, Hq, Hkv, lens, want_c):
+    """Ragged lengths where T / slots would give more items than slots: the
+    looser chunk T / target stays (one chunk smaller would overflow)."""
+    B = len(lens)
+    s = fp.make_shape(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, block_tokens=16,
+                      num_blocks=1 << 16, block_table_stride=-(-max(lens) // 16), max_seq_len=max(lens),
+                      sm_scale=0.1)
+    p = fp.fp8pa_plan(s, 256)
+    assert p["split_mode"] == fp.FP8PA_SPLIT_BALANCED
+    items, c = _balanced_items(p, lens, q_len, 0)
+    assert c == want_c
+    slots = p["target_items"] + B
+    n = [-(-L // 32) for L in lens]
+    assert sum(-(-x // (c - 1)) for x in n) > slots
+    assert sum(len(v) for v in items.values()) <= slots
+
 def _write_shape(**over):
     kw = dict(num_tokens=4, key_stride=1024, value_stride=1024, num_kv_heads=8, head_dim=128,
               block_tokens=16, num_blocks=8, k_scale_count=8, v_scale_count=1, k_groups=1)

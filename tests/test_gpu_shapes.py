@@ -144,3 +144,30 @@ def test_balanced_equal_lengths_fill_every_slot(B, ql, hq, hkv, d, L):
     ro, rl = oracle.decode(**wl.oracle_kwargs())
     out, lse = to_host(*run(wl, t))
     compare(out, lse, ro, rl, label=f"B={B} q_len={ql} Hq={hq} Hkv={hkv} L={L} chunk {c}")
+
+
+# Ragged batches whose tighter chunk would give more items than slots (the
+# kernel counts them and keeps the looser chunk): the VALU kernel (MHA,
+# 2 query tokens) and the MFMA kernel.
+FALLBACK = [
+    (2, 8, 8, [5085, 2774, 2270, 5884, 5711, 4095, 2456, 1340, 5625, 1685, 3381, 4080, 1516, 1959, 4474, 1264,
+               4078, 5673, 4136, 3912, 2836, 5810]),
+    (1, 32, 8, [4161, 3420, 5205, 2506, 2790, 2814, 2231, 169, 4104, 3136, 1265, 4340, 1425, 2623, 2371, 2469,
+                3072, 2976, 3474, 868, 5734, 624, 1445]),
+]
+
+
+@pytest.mark.parametrize("ql,hq,hkv,lens", FALLBACK)
+def test_balanced_tight_chunk_that_overflows_is_not_taken(ql, hq, hkv, lens):
+    from tests.test_abi import _balanced_items
+
+    wl = make_workload(seed=997 + hq, B=len(lens), q_len=ql, Hq=hq, Hkv=hkv, D=128, bt=16, seq_lens=lens)
+    t = upload(wl)
+    shape = fp.shape_for(t["q"], t["k"], t["bt"], t["ks"], t["vs"], sm_scale=wl.sm_scale, max_seq_len=max(lens))
+    plan = fp.fp8pa_plan(shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["split_mode"] == fp.FP8PA_SPLIT_BALANCED
+    items, c = _balanced_items(plan, lens, ql, 0)
+    assert sum(len(v) for v in items.values()) <= plan["target_items"] + len(lens)
+    ro, rl = oracle.decode(**wl.oracle_kwargs())
+    out, lse = to_host(*run(wl, t))
+    compare(out, lse, ro, rl, label=f"ragged B={len(lens)} q_len={ql} Hq={hq} chunk {c}")
