@@ -570,6 +570,9 @@ def measure_prefill(log, steps=5):
     P.V, a multiply and an add each), against the dense FP8 peak; the
     matrix cores spend twice the time an FP8-only pass would (the query goes
     in as an E4M3 hi + lo pair, and P.V runs in bf16, at half the FP8 rate).
+    A chunk of few rows per kv head reads more KV bytes per FLOP than the
+    FP8 ridge (625 FLOP/byte): its bound is HBM, its rate the KV bytes (2 D
+    per attended key and kv head) against 8 TB/s; both rates are reported.
     Timed from graph replays like the decode."""
     import torch
 
@@ -582,6 +585,8 @@ def measure_prefill(log, steps=5):
         wl = make_workload(B=B, q_len=ql, Hq=Hq, Hkv=Hkv, D=D, bt=bt, seq_lens=[ctx] * B, seed=17,
                            poison=False, scale=("per_head", 0.02, 0.1), name=name)
         flops = sum(4 * D * Hq * (ctx - ql + i + 1) for i in range(ql)) * B
+        kv_bytes = B * ctx * Hkv * 2 * D
+        bound = "hbm" if kv_bytes / (PEAK_GBPS * 1e9) > flops / (PEAK_FP8_TFLOPS * 1e12) else "mfma"
         dev = "cuda"
         q = torch.from_numpy(wl.q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         kc = torch.from_numpy(wl.k_cache).to(dev)
@@ -623,10 +628,13 @@ def measure_prefill(log, steps=5):
         out[name] = {"workload": f"B={B} q_len={ql} Hq={Hq} Hkv={Hkv} D={D} bt={bt} seq_len={ctx}",
                      "us": round(t * 1e6, 1), "algorithmic_flops": flops, "tflops": round(tflops, 1),
                      "pct_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS * 100, 2),
+                     "kv_bytes": kv_bytes, "kv_gbps": round(kv_bytes / t / 1e9, 1),
+                     "pct_of_hbm_peak": round(kv_bytes / t / 1e9 / PEAK_GBPS * 100, 2), "bound": bound,
                      "variant": "mfma" if plan["variant"] == 1 else "dot",
                      "num_splits": plan["num_splits"], "grid_wgs": plan["grid_wgs"]}
         log(f"[bench] prefill {name}: {t * 1e6:.1f} us, {tflops:.1f} TFLOP/s "
-            f"({tflops / PEAK_FP8_TFLOPS * 100:.2f}% of dense FP8 peak), splits {plan['num_splits']}")
+            f"({tflops / PEAK_FP8_TFLOPS * 100:.2f}% of dense FP8 peak), KV {kv_bytes / t / 1e9:.0f} GB/s "
+            f"({kv_bytes / t / 1e9 / PEAK_GBPS * 100:.1f}% of 8 TB/s), {bound}-bound, splits {plan['num_splits']}")
         del g, kc, vc, q, ws
         torch.cuda.empty_cache()
     return out
