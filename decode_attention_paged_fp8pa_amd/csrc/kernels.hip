@@ -115,7 +115,6 @@ struct Params {
   int32_t kg_shift;  // log2 of the dims per K scale group
   int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
   int32_t pr;  // kv heads per wavefront (MFMA kernel: 2 pairs heads at D = 64)
-  int32_t xcd; // 1: each XCD's workgroups take one contiguous range of logical indices
   float sm_scale;
 };
 
@@ -191,6 +190,11 @@ __device__ __forceinline__ int uniform_vload(const int32_t* ptr, int i) {
 __device__ __forceinline__ float maybe_vload(const float* ptr, int i, bool use) {
   const Rsrc r = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, 0, use ? 0x7fffffff : 0, kRsrcWord3);
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, use ? uint32_t(i) * 4u : 0u, 0, 0));
+}
+
+__device__ __forceinline__ int maybe_vload(const int32_t* ptr, int i, bool use) {
+  const Rsrc r = __builtin_amdgcn_make_buffer_rsrc((void*)ptr, 0, use ? 0x7fffffff : 0, kRsrcWord3);
+  return int(__builtin_amdgcn_raw_buffer_load_b32(r, use ? uint32_t(i) * 4u : 0u, 0, 0));
 }
 
 // Maximum of v over lanes l, l^16, l^32 and l^48 (the four lane groups that
@@ -293,17 +297,21 @@ __device__ __forceinline__ int wave_max_i(int v) {
 }
 
 // Exclusive prefix sum over the 64 lanes of v, 0 <= v <= vmax, and the
-// total: one ballot and one mbcnt per bit of vmax (no LDS).
+// total (no LDS): an inclusive scan by DPP within each row of 16 lanes
+// (shifts right by 1, 2, 4 and 8, zero-filled), then the row broadcasts that
+// add row 0's total into row 1 and row 2's into row 3 (lane 15 of the row
+// before), and lane 31's running total into rows 2 and 3.
 __device__ __forceinline__ int wave_excl_prefix_i(int v, int vmax, int& total) {
-  int pre = 0, tot = 0;
-  for (int k = 0; (vmax >> k) != 0; ++k) {
-    const uint64_t m = __ballot((v >> k) & 1);
-    const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-    pre += int(below) << k;
-    tot += __popcll(m) << k;
-  }
-  total = tot;
-  return pre;
+  (void)vmax;
+  int s = v;
+  s += __builtin_amdgcn_update_dpp(0, s, 0x111, 0xF, 0xF, false);  // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, s, 0x112, 0xF, 0xF, false);  // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xF, false);  // row_shr:4
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xF, false);  // row_shr:8
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+  total = __builtin_amdgcn_readlane(s, 63);
+  return s - v;
 }
 
 // Keys of sequence b that some query row attends: [ulo, uhi), covered by the
@@ -350,20 +358,45 @@ struct Work {
 // from the workgroup index alone, so loads that need only them can be issued
 // before the (sequence, split) item is resolved.
 // The workgroup's logical index.  Workgroups go to the 8 XCDs in turn
-// (block i to XCD i % 8); with p.xcd each XCD's workgroups take one
+// (block i to XCD i % 8); with XCD each XCD's workgroups take one
 // contiguous range of logical indices, so the workgroups of one item (which
 // re-read the same K/V tiles when several row groups of a kv head share
-// them) run on one XCD and meet those bytes in its L2.
-__device__ __forceinline__ int logical_block(const Params& p) {
-  const int i = blockIdx.x;
-  if (!p.xcd) return i;
+// them) run on one XCD and meet those bytes in its L2.  (A compile-time
+// choice: a branch on a kernel argument here would make the wavefront wait
+// for that argument before it issues the loads of the others.)
+template <bool XCD>
+__device__ __forceinline__ int logical_block(int i) {
+  if constexpr (!XCD) return i;
   const int n = gridDim.x, x = i & 7, q = n >> 3, r = n & 7;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (i >> 3);
 }
 
-__device__ __forceinline__ Work work_head(const Params& p, int ds) {
+// The kernel arguments a partial kernel's prologue reads, requested in one
+// batch of scalar loads before the first wait.  Left to itself the compiler
+// issues them in two or three dependent rounds (the arguments behind one
+// address are loaded only once that address is needed), and each round is a
+// trip to memory before the first vector load can go out.  An empty asm that
+// takes them all as scalar operands makes them all live at its point, and
+// the workgroup index it passes through (and returns) makes every step of
+// the work item come after it
+__device__ __forceinline__ int prologue_args(const Params& p) {
+  int blk = blockIdx.x;
+  asm volatile("" : "+s"(blk)
+               : "s"(p.q), "s"(p.k_cache), "s"(p.v_cache), "s"(p.block_table), "s"(p.seq_lens),
+                 "s"(p.k_scale), "s"(p.v_scale), "s"(p.sinks), "s"(p.B), "s"(p.q_len), "s"(p.G),
+                 "s"(p.rows), "s"(p.row_groups), "s"(p.hg), "s"(p.upi), "s"(p.num_splits),
+                 "s"(p.balanced), "s"(p.max_seq_len), "s"(p.k_per_head), "s"(p.v_per_head),
+                 "s"(p.direct), "s"(p.k_groups), "s"(p.kg_shift), "s"(p.window), "s"(int(gridDim.x)));
+  // (and no arithmetic on a loaded argument may be hoisted above it, where
+  // its wait would split the batch)
+  __builtin_amdgcn_sched_barrier(0);
+  return blk;
+}
+
+template <bool XCD = false>
+__device__ __forceinline__ Work work_head(const Params& p, int ds, int blk) {
   Work w;
-  const int bid = logical_block(p);
+  const int bid = logical_block<XCD>(blk);
   const int item = bid / p.upi;
   const int unit = bid - item * p.upi;
   w.rg = unit % p.row_groups;
@@ -376,8 +409,31 @@ __device__ __forceinline__ Work work_head(const Params& p, int ds) {
   return w;
 }
 
-__device__ __forceinline__ void work_item(const Params& p, Work& w) {
-  const int bid = logical_block(p);
+// seq_lens[l + 64 j], j < 4, for lane l (0 past the batch), requested first
+// thing: the chain seq_lens -> work item -> block table -> K/V pages is the
+// kernel's critical path, and everything else the prologue loads can wait.
+// A descriptor sized to the batch returns 0 past it, so the four loads are
+// branch-free and all in flight together.  (Only the balanced plan reads
+// them.)
+struct SeqLens {
+  int v[4];
+};
+
+__device__ __forceinline__ SeqLens seq_lens_in_flight(const Params& p) {
+  const int lane = threadIdx.x & 63;
+  const Rsrc slr = __builtin_amdgcn_make_buffer_rsrc((void*)p.seq_lens, 0, p.B * 4, kRsrcWord3);
+  SeqLens s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s.v[j] = int(__builtin_amdgcn_raw_buffer_load_b32(slr, uint32_t(lane + 64 * j) * 4u, 0, 0));
+  // (kept here: the scheduler would otherwise sink them below the other
+  // prologue loads and the arithmetic that addresses those)
+  __builtin_amdgcn_sched_barrier(0);
+  return s;
+}
+
+template <bool XCD = false>
+__device__ __forceinline__ void work_item(const Params& p, Work& w, int blk, const SeqLens& sl) {
+  const int bid = logical_block<XCD>(blk);
   const int item = bid / p.upi;
   w.active = true;
 
@@ -408,7 +464,7 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = lane + 64 * j;
-    Lj[j] = b < p.B ? seq_len_of(p, b) : 0;
+    Lj[j] = b < p.B ? min(max(sl.v[j], 0), p.max_seq_len) : 0;
     const Span sp = span_of(Lj[j], p.q_len, p.window);
     nj[j] = b < p.B ? sp.tile1 - sp.tile0 : 0;
     tsum += nj[j];
@@ -430,7 +486,10 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
   if (ct < c) {
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cnt += lane + 64 * j < p.B ? splits_of(nj[j], ct, p.num_splits) : 0;
+    for (int j = 0; j < 4; ++j) {
+      if (64 * j >= p.B) break;  // (uniform: no lane holds a sequence)
+      cnt += lane + 64 * j < p.B ? splits_of(nj[j], ct, p.num_splits) : 0;
+    }
     if (__builtin_amdgcn_readfirstlane(wave_sum_i(cnt)) <= slots) c = ct;
   }
   int base = 0;
@@ -467,9 +526,10 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w) {
   w.ts = w.te = 0;
 }
 
-__device__ __forceinline__ Work work_of(const Params& p, int ds) {
-  Work w = work_head(p, ds);
-  work_item(p, w);
+__device__ __forceinline__ Work work_of(const Params& p, int ds, int blk) {
+  const SeqLens sl = seq_lens_in_flight(p);
+  Work w = work_head(p, ds, blk);
+  work_item(p, w, blk, sl);
   return w;
 }
 
@@ -579,12 +639,14 @@ partial_mfma_kernel(Params p) {
   // instead of byte permutes of each wavefront's own copy.
   constexpr bool TRV = LW > 0;
 
+  const int blk = prologue_args(p);
+  const SeqLens sl = seq_lens_in_flight(p);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int qd = lane >> 4;
-  Work w = work_head(p, DS);
+  Work w = work_head<(LW > 0)>(p, DS, blk);
   if constexpr (LW > 0) {
-    const int bid = logical_block(p);
+    const int bid = logical_block<true>(blk);
     const int item = bid / p.upi;
     const int unit = bid - item * p.upi;
     const int rgu = p.row_groups / LW;
@@ -617,7 +679,7 @@ partial_mfma_kernel(Params p) {
     const int qi = rr / p.G;
     sink_raw[b] = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
-  work_item(p, w);
+  work_item<(LW > 0)>(p, w, blk, sl);
   if (!w.active) return;  // uniform over the workgroup
   const int d0 = w.half * DW;      // first dim of this wavefront's slice
   const int L = w.L;
@@ -1347,10 +1409,12 @@ partial_mfma_nvfp4_kernel(Params p) {
   constexpr bool MXQ = MX && D == 128;
   constexpr float kShift = MX ? 0.f : kPShift16;
 
+  const int blk = prologue_args(p);
+  const SeqLens sl = seq_lens_in_flight(p);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int qd = lane >> 4;
-  Work w = work_head(p, 1);
+  Work w = work_head(p, 1, blk);
   const int kvh = w.g;
   const int rlane = w.rg * kRowsMfma + n;
   const float ks = uniform_vload(p.k_scale, p.k_per_head ? kvh : 0);
@@ -1364,7 +1428,7 @@ partial_mfma_nvfp4_kernel(Params p) {
     const int qi = rr / p.G;
     sink_raw = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
-  work_item(p, w);
+  work_item(p, w, blk, sl);
   if (!w.active) return;  // uniform over the workgroup
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
@@ -1834,10 +1898,11 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   constexpr int KWB = NV ? 8 : 16;  // data bytes a lane reads per token
   constexpr int AUX = NT ? kLoadNT : 0;  // K/V load cache policy (NT: one wave reads each line)
 
+  const int blk = prologue_args(p);
   const int lane = threadIdx.x & 63;
   const int kk = lane / LPK;
   const int c = lane % LPK;
-  const Work w = work_of(p, 1);
+  const Work w = work_of(p, 1, blk);
   if (!w.active) return;  // uniform over the workgroup
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
@@ -2175,6 +2240,7 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 
 struct MergeArgs {
   int num_splits, num_rows, Hq;
+  int rows_per_seq;  // B * q_len * Hq rows, q_len * Hq per sequence
   const float* po;
   const float* pl;
   const float* sinks;
@@ -2183,8 +2249,18 @@ struct MergeArgs {
   // Optional: the splits each sequence got (slots 0 .. n - 1 of its rows hold
   // partials), written by the partial pass; nullptr: every row has num_splits.
   const int32_t* nsplit;
-  int rows_per_seq;  // B * q_len * Hq rows, q_len * Hq per sequence
 };
+
+// The merge's kernel arguments in one batch of scalar loads, as for the
+// partial kernels: the returned workgroup index orders the rest after them.
+__device__ __forceinline__ int merge_args(const MergeArgs& a) {
+  int blk = blockIdx.x;
+  asm volatile("" : "+s"(blk)
+               : "s"(a.num_splits), "s"(a.num_rows), "s"(a.Hq), "s"(a.po), "s"(a.pl), "s"(a.sinks),
+                 "s"(a.out), "s"(a.lse_out), "s"(a.nsplit), "s"(a.rows_per_seq));
+  __builtin_amdgcn_sched_barrier(0);
+  return blk;
+}
 
 // One workgroup per (query row, 64 dims of head_dim); lane l owns dim
 // 64 c + l.  Its W wavefronts take the splits in turn (wavefront w: splits
@@ -2203,13 +2279,16 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   constexpr int U0 = 16 / W; // loaded before the split count and the weights are known
   __shared__ float red_acc[W][64];
   __shared__ float red_ml[W][2];
-  const int row = blockIdx.x / C;
-  const int chunk = blockIdx.x - row * C;
+  const int blk = merge_args(a);
+  const int row = blk / C;
+  const int chunk = blk - row * C;
   const int lane = threadIdx.x & 63;
   const int wv = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int S = a.num_splits;
-  // (issued first: the split count is the one value everything else waits on)
-  const int ns_loaded = a.nsplit ? uniform_vload(a.nsplit, row / a.rows_per_seq) : S;
+  // (issued first: the split count is the one value everything else waits
+  // on; branch-free, so that no wait for it lands before the loads below)
+  const bool has_ns = a.nsplit != nullptr;
+  const int ns_raw = maybe_vload(a.nsplit, row / a.rows_per_seq, has_ns);
   const float* lrow = a.pl + (size_t)row * S;
   const float* obase = a.po + (size_t)row * S * D + 64 * chunk + lane;
   // lane i of this wavefront stands for split wv + W * (i0 + i).  The first
@@ -2224,8 +2303,12 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   // the first value waited for)
   __builtin_amdgcn_sched_barrier(0);
   l0 = sl0 < S ? l0 : -INFINITY;
+  // (the count is first touched here: without the asm the compiler would
+  // clamp it above the loads, and wait for it there)
+  int ns_v = ns_raw;
+  asm volatile("" : "+v"(ns_v));
   // (clamped: a sequence's split count is at least 1 and at most num_splits)
-  const int ns = __builtin_amdgcn_readfirstlane(min(max(ns_loaded, 1), S));
+  const int ns = __builtin_amdgcn_readfirstlane(has_ns ? min(max(ns_v, 1), S) : S);
   // this wavefront's splits: wv + W * i for i < nw
   const int nw = ns > wv ? (ns - wv + W - 1) / W : 0;
   float M = lane < nw ? l0 * kLog2e : -INFINITY;
@@ -2310,14 +2393,17 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(MergeArgs a) {
   constexpr int VPL = D / 16;          // dims per lane
   constexpr int NV = VPL / 4;          // their float4s
   constexpr int U = D == 256 ? 4 : 8;  // splits per batch
+  const int blk = merge_args(a);
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
-  const int row0 = int(blockIdx.x) * 4 + (lane >> 4);
+  const int row0 = blk * 4 + (lane >> 4);
   const bool valid = row0 < a.num_rows;
   const int row = valid ? row0 : a.num_rows - 1;
   const int S = a.num_splits;
-  // (issued first: the split count is the one value everything else waits on)
-  const int ns_loaded = a.nsplit ? a.nsplit[row / a.rows_per_seq] : S;
+  // (issued first: the split count is the one value everything else waits
+  // on; branch-free, so that no wait for it lands before the loads below)
+  const bool has_ns = a.nsplit != nullptr;
+  const int ns_raw = maybe_vload(a.nsplit, row / a.rows_per_seq, has_ns);
   const float* lrow = a.pl + (size_t)row * S;
   const f32x4* orow = reinterpret_cast<const f32x4*>(a.po + (size_t)row * S * D + l16 * VPL);
   float lv[U];
@@ -2330,7 +2416,10 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(MergeArgs a) {
     for (int v = 0; v < NV; ++v) ov[u][v] = orow[(size_t)sl * (D / 4) + v];
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int ns = min(max(ns_loaded, 1), S);
+  // (first touched here, as in merge_kernel)
+  int ns_v = ns_raw;
+  asm volatile("" : "+v"(ns_v));
+  const int ns = has_ns ? min(max(ns_v, 1), S) : S;
   float M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < U; ++u) M = u < ns ? fmaxf(M, lv[u] * kLog2e) : M;
@@ -2766,7 +2855,6 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
   prm.B = pl.B;
   prm.hg = pl.hg;
   prm.upi = pl.upi;
-  prm.xcd = pl.lw > 0 ? 1 : 0;
   prm.num_splits = pl.num_splits;
   prm.tps = pl.tps;
   prm.tps_cap = pl.tps_cap;
