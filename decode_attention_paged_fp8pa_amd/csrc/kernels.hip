@@ -78,6 +78,17 @@ constexpr float kMinNormal = 1.17549435e-38f;  // the least normal fp32 value
 // the shift it stays below 2^15 (under f16's 65504).
 constexpr float kPShift16 = 7.0f;
 
+// Division of 0 <= n < 2^31 by a divisor d >= 1 that the host knows: with
+// 2^(l-1) < d <= 2^l, m = ceil(2^(31+l) / d) fits 32 bits and
+// n / d = floor(n * m / 2^(31+l)) exactly (n * (m - 2^(31+l)/d) / 2^(31+l)
+// < 2^-l <= 1/d never carries the quotient past the next integer).  A
+// multiply and a shift instead of the ~25 instructions of a general
+// division; the prologue's divisions sit on its critical path.
+struct FastDiv {
+  uint32_t m;
+  uint32_t sh;  // 31 + l
+};
+
 struct Params {
   const uint16_t* q;
   const uint8_t* k_cache;
@@ -116,6 +127,9 @@ struct Params {
   int32_t ds;  // wavefronts that split one kv head's head_dim (MFMA kernel, D = 256)
   int32_t pr;  // kv heads per wavefront (MFMA kernel: 2 pairs heads at D = 64)
   float sm_scale;
+  // the same divisors for fdiv: upi, row_groups, G, num_splits, target_items
+  // and target_items + B (1 where unused)
+  FastDiv d_upi, d_rg, d_G, d_ns, d_ti, d_slots;
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -259,6 +273,10 @@ __device__ __forceinline__ long as_long(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
+__device__ __forceinline__ int fdiv(int n, FastDiv d) {
+  return int(uint32_t((uint64_t(uint32_t(n)) * d.m) >> d.sh));
+}
+
 // Wavefront reductions without LDS: DPP within each row of 16 lanes (quad
 // swaps, then half-row and row mirrors), then the gfx950 permlane swaps,
 // which pair lane l with l ^ 32 and l ^ 16.  Every lane gets the result.
@@ -397,10 +415,10 @@ template <bool XCD = false>
 __device__ __forceinline__ Work work_head(const Params& p, int ds, int blk) {
   Work w;
   const int bid = logical_block<XCD>(blk);
-  const int item = bid / p.upi;
+  const int item = fdiv(bid, p.d_upi);
   const int unit = bid - item * p.upi;
-  w.rg = unit % p.row_groups;
-  const int gg = unit / p.row_groups;
+  const int gg = fdiv(unit, p.d_rg);
+  w.rg = unit - gg * p.row_groups;
   // the wavefront index is uniform across the wave; saying so keeps every
   // address derived from it (descriptor bases, table rows) in scalar registers
   const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
@@ -434,18 +452,18 @@ __device__ __forceinline__ SeqLens seq_lens_in_flight(const Params& p) {
 template <bool XCD = false>
 __device__ __forceinline__ void work_item(const Params& p, Work& w, int blk, const SeqLens& sl) {
   const int bid = logical_block<XCD>(blk);
-  const int item = bid / p.upi;
+  const int item = fdiv(bid, p.d_upi);
   w.active = true;
 
   if (!p.balanced) {
-    w.b = item / p.num_splits;
+    w.b = fdiv(item, p.d_ns);
     w.split = item - w.b * p.num_splits;
     w.nsplit = p.num_splits;
     w.L = seq_len_of(p, w.b);
     w.sp = span_of(w.L, p.q_len, p.window);
     w.ts = w.sp.tile0 + w.split * p.tps;
     w.te = min(w.ts + p.tps, w.sp.tile1);
-    if (p.nsplit_out && w.split == 0 && bid % p.upi == 0 && threadIdx.x == 0)
+    if (p.nsplit_out && w.split == 0 && bid == item * p.upi && threadIdx.x == 0)
       p.nsplit_out[w.b] = w.nsplit;
     return;
   }
@@ -474,15 +492,15 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w, int blk, con
   // which keeps the tile range, and so every buffer descriptor, scalar)
   const int T = __builtin_amdgcn_readfirstlane(wave_sum_i(tsum));
   const int M = __builtin_amdgcn_readfirstlane(wave_max_i(tmax));
-  const int floor_c = max(min(p.min_tiles, max(1, (2 * T) / p.target_items)), ceil_div_i(M, p.num_splits));
-  int c = min(max(ceil_div_i(T, p.target_items), floor_c), p.tps_cap);
+  const int floor_c = max(min(p.min_tiles, max(1, fdiv(2 * T, p.d_ti))), fdiv(M + p.num_splits - 1, p.d_ns));
+  int c = min(max(fdiv(T + p.target_items - 1, p.d_ti), floor_c), p.tps_cap);
   // The grid holds target_items + B items, and sum_b ceil(n_b / c) <= T / c
   // + B is what keeps c >= T / target_items within it.  That bound is loose
   // (sequences of equal length reach T / c): a chunk of T / (target_items +
   // B) is taken instead when its items still fit, so that one round of
   // workgroups carries less per workgroup.
   const int slots = p.target_items + p.B;
-  const int ct = min(max(ceil_div_i(T, slots), floor_c), p.tps_cap);
+  const int ct = min(max(fdiv(T + slots - 1, p.d_slots), floor_c), p.tps_cap);
   if (ct < c) {
     int cnt = 0;
 #pragma unroll
@@ -511,7 +529,7 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w, int blk, con
       w.sp = span_of(w.L, p.q_len, p.window);
       w.ts = w.sp.tile0 + w.split * c;
       w.te = min(w.ts + c, w.sp.tile1);
-      if (p.nsplit_out && w.split == 0 && bid % p.upi == 0 && threadIdx.x == 0)
+      if (p.nsplit_out && w.split == 0 && bid == item * p.upi && threadIdx.x == 0)
         p.nsplit_out[w.b] = w.nsplit;
       return;
     }
@@ -545,7 +563,7 @@ __device__ __forceinline__ Row row_of(const Params& p, int b, int g, int r, int 
   Row o;
   o.valid = r < p.rows;
   const int rr = o.valid ? r : 0;
-  o.qi = rr / p.G;
+  o.qi = fdiv(rr, p.d_G);
   o.h = g * p.G + (rr - o.qi * p.G);
   const int pos = L - p.q_len + o.qi;
   o.khi = min(pos + 1, L);
@@ -647,7 +665,7 @@ partial_mfma_kernel(Params p) {
   Work w = work_head<(LW > 0)>(p, DS, blk);
   if constexpr (LW > 0) {
     const int bid = logical_block<true>(blk);
-    const int item = bid / p.upi;
+    const int item = fdiv(bid, p.d_upi);
     const int unit = bid - item * p.upi;
     const int rgu = p.row_groups / LW;
     const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
@@ -676,7 +694,7 @@ partial_mfma_kernel(Params p) {
   for (int b = 0; b < NB; ++b) {
     has_sink[b] = sinks_here && rlane[b] < p.rows;
     const int rr = min(rlane[b], p.rows - 1);
-    const int qi = rr / p.G;
+    const int qi = fdiv(rr, p.d_G);
     sink_raw[b] = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
   work_item<(LW > 0)>(p, w, blk, sl);
@@ -688,15 +706,15 @@ partial_mfma_kernel(Params p) {
   // the query positions qmin..qmax they belong to.
   const int r0 = PR == 2 ? 0 : w.rg * NB * kRowsMfma;
   const int r1 = PR == 2 ? p.rows - 1 : min(r0 + NB * kRowsMfma, p.rows) - 1;
-  const int qmin = r0 / p.G, qmax = r1 / p.G;
+  const int qmin = fdiv(r0, p.d_G), qmax = fdiv(r1, p.d_G);
   // The split's tiles outside the keys some row attends are skipped: with
   // many query rows per sequence (chunked prefill) a row group's causal
   // range ends before the sequence does.
   // (LW > 0: the range of the workgroup's rows, the same for all its wavefronts)
   constexpr int kWgRows = (LW > 0 ? LW : 1) * NB * kRowsMfma;
   const int wg0 = (w.rg / (LW > 0 ? LW : 1)) * kWgRows;
-  const int tq0 = LW ? wg0 / p.G : qmin;
-  const int tq1 = LW ? (min(wg0 + kWgRows, p.rows) - 1) / p.G : qmax;
+  const int tq0 = LW ? fdiv(wg0, p.d_G) : qmin;
+  const int tq1 = LW ? fdiv(min(wg0 + kWgRows, p.rows) - 1, p.d_G) : qmax;
   const TileRange tr = rows_tiles(p, L, tq0, tq1, w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
   Row row[NB];
@@ -1425,7 +1443,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   float sink_raw;
   {
     const int rr = min(rlane, p.rows - 1);
-    const int qi = rr / p.G;
+    const int qi = fdiv(rr, p.d_G);
     sink_raw = maybe_vload(p.sinks, kvh * p.G + (rr - qi * p.G), sinks_here);
   }
   work_item(p, w, blk, sl);
@@ -1434,7 +1452,7 @@ partial_mfma_nvfp4_kernel(Params p) {
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
   const int r0 = w.rg * kRowsMfma;
   const int r1 = min(r0 + kRowsMfma, p.rows) - 1;
-  const int qmin = r0 / p.G, qmax = r1 / p.G;
+  const int qmin = fdiv(r0, p.d_G), qmax = fdiv(r1, p.d_G);
   const TileRange tr = rows_tiles(p, L, qmin, qmax, w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
   const Row row = row_of(p, w.b, kvh, rlane, L);
@@ -1907,7 +1925,7 @@ __global__ __launch_bounds__(512) void partial_dot_kernel(Params p) {
   const int L = w.L;
   const int ulo = w.sp.ulo, uhi = w.sp.uhi;
   const int r0 = w.rg * RPG, r1 = min(r0 + RPG, p.rows) - 1;
-  const TileRange tr = rows_tiles(p, L, r0 / p.G, r1 / p.G, w.ts, w.te);
+  const TileRange tr = rows_tiles(p, L, fdiv(r0, p.d_G), fdiv(r1, p.d_G), w.ts, w.te);
   const int ts = tr.ts, te = tr.te;
 
   Row rows[RPG];
@@ -2726,6 +2744,18 @@ hipError_t launch_partial(const Plan& pl, const Params& prm, hipStream_t st) {
 // Wavefronts per (row, 64 dims) workgroup: 4 when the rows give fewer than 4
 // workgroups per CU, 1 up to 32 per CU (one resident round), and beyond that
 // 0: the many-rows kernel (4 whole rows per wavefront).
+// The multiplier and shift for fdiv by d (d < 1 is taken as 1: such a
+// divisor is never used).
+FastDiv fast_div(int64_t d) {
+  if (d < 1) d = 1;
+  uint32_t l = 0;
+  while ((int64_t(1) << l) < d) ++l;
+  FastDiv f;
+  f.sh = 31 + l;
+  f.m = uint32_t(((uint64_t(1) << f.sh) + uint64_t(d) - 1) / uint64_t(d));
+  return f;
+}
+
 int merge_waves(int64_t workgroups, int cu) {
   if (workgroups > 32 * int64_t(cu)) return 0;
   return workgroups >= 4 * int64_t(cu) ? 1 : 4;
@@ -2876,6 +2906,12 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
   prm.ds = pl.ds;
   prm.pr = pl.pr;
   prm.sm_scale = shape->sm_scale;
+  prm.d_upi = fast_div(prm.upi);
+  prm.d_rg = fast_div(prm.row_groups);
+  prm.d_G = fast_div(prm.G);
+  prm.d_ns = fast_div(prm.num_splits);
+  prm.d_ti = fast_div(prm.target_items);
+  prm.d_slots = fast_div(int64_t(prm.target_items) + prm.B);
 
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
