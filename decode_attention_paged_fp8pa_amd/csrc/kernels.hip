@@ -2267,6 +2267,7 @@ struct MergeArgs {
   // Optional: the splits each sequence got (slots 0 .. n - 1 of its rows hold
   // partials), written by the partial pass; nullptr: every row has num_splits.
   const int32_t* nsplit;
+  FastDiv d_rps;  // rows_per_seq for fdiv
 };
 
 // The merge's kernel arguments in one batch of scalar loads, as for the
@@ -2275,7 +2276,8 @@ __device__ __forceinline__ int merge_args(const MergeArgs& a) {
   int blk = blockIdx.x;
   asm volatile("" : "+s"(blk)
                : "s"(a.num_splits), "s"(a.num_rows), "s"(a.Hq), "s"(a.po), "s"(a.pl), "s"(a.sinks),
-                 "s"(a.out), "s"(a.lse_out), "s"(a.nsplit), "s"(a.rows_per_seq));
+                 "s"(a.out), "s"(a.lse_out), "s"(a.nsplit), "s"(a.rows_per_seq), "s"(a.d_rps.m),
+                 "s"(a.d_rps.sh));
   __builtin_amdgcn_sched_barrier(0);
   return blk;
 }
@@ -2306,7 +2308,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(MergeArgs a) {
   // (issued first: the split count is the one value everything else waits
   // on; branch-free, so that no wait for it lands before the loads below)
   const bool has_ns = a.nsplit != nullptr;
-  const int ns_raw = maybe_vload(a.nsplit, row / a.rows_per_seq, has_ns);
+  const int ns_raw = maybe_vload(a.nsplit, fdiv(row, a.d_rps), has_ns);
   const float* lrow = a.pl + (size_t)row * S;
   const float* obase = a.po + (size_t)row * S * D + 64 * chunk + lane;
   // lane i of this wavefront stands for split wv + W * (i0 + i).  The first
@@ -2421,7 +2423,7 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(MergeArgs a) {
   // (issued first: the split count is the one value everything else waits
   // on; branch-free, so that no wait for it lands before the loads below)
   const bool has_ns = a.nsplit != nullptr;
-  const int ns_raw = maybe_vload(a.nsplit, row / a.rows_per_seq, has_ns);
+  const int ns_raw = maybe_vload(a.nsplit, fdiv(row, a.d_rps), has_ns);
   const float* lrow = a.pl + (size_t)row * S;
   const f32x4* orow = reinterpret_cast<const f32x4*>(a.po + (size_t)row * S * D + l16 * VPL);
   float lv[U];
@@ -2933,6 +2935,7 @@ fp8pa_status decode_impl(const fp8pa_shape* shape, const void* q, const void* k_
     ma.lse_out = lse;
     ma.nsplit = prm.nsplit_out;
     ma.rows_per_seq = pl.q_len * pl.Hq;
+    ma.d_rps = fast_div(ma.rows_per_seq);
     e = launch_merge(pl.D, ma, cu, hs);
     if (e != hipSuccess) return FP8PA_ERR_HIP;
   }
@@ -2997,6 +3000,7 @@ fp8pa_status fp8pa_merge(int32_t num_splits, int32_t num_rows, int32_t num_q_hea
   ma.lse_out = lse;
   ma.nsplit = nullptr;  // every row merges all num_splits slots
   ma.rows_per_seq = 1;
+  ma.d_rps = fast_div(1);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FP8PA_ERR_HIP;
   const int cu = cu_count_of(dev);
