@@ -39,6 +39,7 @@ from ._lib import (  # noqa: F401
     fp8pa_debug_mfma_scale_fp8,
     fp8pa_debug_nvfp4,
     fp8pa_debug_stream_read,
+    fp8pa_debug_fast_div,
     fp8pa_debug_wave_ops,
     fp8pa_decode,
     fp8pa_decode_noalloc,

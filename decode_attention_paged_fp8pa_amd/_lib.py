@@ -139,6 +139,8 @@ _SIGS = {
     "fp8pa_debug_mfma_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_mfma_scale_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP]),
     "fp8pa_debug_wave_ops": (ctypes.c_int, [_VP, ctypes.c_int32, _VP, _VP]),
+    "fp8pa_debug_fast_div": (ctypes.c_int, [ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32),
+                                            ctypes.POINTER(ctypes.c_uint32)]),
     "fp8pa_debug_nvfp4": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
     "fp8pa_debug_lds_tr8": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
     "fp8pa_debug_mxfp8": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP]),
@@ -267,6 +269,15 @@ def fp8pa_debug_stream_read(buf, nbytes, sink, stream=None, load_bytes=16) -> No
     st = lib().fp8pa_debug_stream_read(_ptr(buf), int(nbytes), int(load_bytes), _ptr(sink), _stream(stream))
     if st != FP8PA_OK:
         raise Fp8paError(st, "fp8pa_debug_stream_read")
+
+
+def fp8pa_debug_fast_div(d: int) -> tuple[int, int]:
+    """(multiplier, shift) the kernels divide by d with (host only)."""
+    m, sh = ctypes.c_uint32(), ctypes.c_uint32()
+    st = lib().fp8pa_debug_fast_div(int(d), ctypes.byref(m), ctypes.byref(sh))
+    if st != FP8PA_OK:
+        raise Fp8paError(st, "fp8pa_debug_fast_div")
+    return m.value, sh.value
 
 
 def fp8pa_debug_wave_ops(inp, vmax, out, stream=None) -> None:

@@ -3037,6 +3037,14 @@ fp8pa_status fp8pa_debug_nvfp4(const uint8_t* data, const uint8_t* scales, float
   return hipGetLastError() == hipSuccess ? FP8PA_OK : FP8PA_ERR_HIP;
 }
 
+fp8pa_status fp8pa_debug_fast_div(int64_t d, uint32_t* m, uint32_t* shift) {
+  if (!m || !shift) return FP8PA_ERR_INVALID_ARG;
+  const FastDiv f = fast_div(d);
+  *m = f.m;
+  *shift = f.sh;
+  return FP8PA_OK;
+}
+
 fp8pa_status fp8pa_debug_wave_ops(const int32_t* in, int32_t vmax, int32_t* out, void* stream) {
   if (!in || !out || vmax < 0) return FP8PA_ERR_INVALID_ARG;
   debug_wave_ops_kernel<<<dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(in, vmax, out);

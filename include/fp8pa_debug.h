@@ -65,6 +65,14 @@ fp8pa_status fp8pa_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, 
 fp8pa_status fp8pa_debug_mfma_scale_fp8(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, float* c,
                                         void* stream);
 
+/* The multiplier and shift the kernels divide by a host-known divisor with
+ * (host only, no GPU): for d >= 1 (d < 1 is taken as 1), *m and *shift such
+ * that n / d == (uint64_t)n * *m >> *shift for every 0 <= n < 2^31.  The
+ * kernels take them for the workgroups per item, the row groups, the query
+ * heads per kv head, the split slots and the merge's rows per sequence.
+ * Returns FP8PA_ERR_INVALID_ARG for null outputs. */
+fp8pa_status fp8pa_debug_fast_div(int64_t d, uint32_t* m, uint32_t* shift);
+
 /* One wavefront of 64 lanes, lane l holding in[l] (int32 [64], each in
  * [0, vmax], vmax >= 0): out[l] = the exclusive prefix sum in[0] + ... +
  * in[l-1], out[64 + l] = the wavefront sum, out[128 + l] = the wavefront

@@ -10,6 +10,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import decode_attention_paged_fp8pa_amd as fp
@@ -582,3 +583,31 @@ def test_stream_read_diagnostic_argument_checks():
     for w in (0, 2, 12, 32, -16):
         assert lib.fp8pa_debug_stream_read(16, 64, w, s, None) == _lib.FP8PA_ERR_INVALID_ARG
     assert lib.fp8pa_debug_stream_read(24, 64, 16, s, None) == _lib.FP8PA_ERR_MISALIGNED
+
+
+def test_fast_division_multipliers_match_integer_division():
+    """The multiply-and-shift the kernels divide by host-known divisors with
+    (workgroups per item, row groups, query heads per kv head, split slots,
+    rows per sequence) equals integer division for every numerator below
+    2^31: checked here against Python's // on divisors 1..4096, every power
+    of two and its neighbours, and random ones, at the numerators where an
+    off-by-one would show (multiples of d and their neighbours, the top of
+    the range) plus random ones."""
+    rng = np.random.default_rng(31)
+    divisors = list(range(1, 4097)) + [2 ** k + e for k in range(1, 31) for e in (-1, 0, 1)]
+    divisors += [int(x) for x in rng.integers(1, 2 ** 31 - 1, size=500)]
+    top = 2 ** 31 - 1
+    for d in divisors:
+        m, sh = fp.fp8pa_debug_fast_div(d)
+        assert 0 < m < 2 ** 32 and 31 <= sh <= 62
+        ks = [1, 2, 3, 1000, top // d]
+        ns = [0, 1, d - 1, d, d + 1, top, top - 1]
+        ns += [k * d + r for k in ks for r in (-1, 0, 1, d - 1)]
+        ns += [int(x) for x in rng.integers(0, top, size=16)]
+        for n in ns:
+            if 0 <= n <= top:
+                assert (n * m) >> sh == n // d, (n, d, m, sh)
+    # divisors below 1 are taken as 1; null outputs are refused
+    assert fp.fp8pa_debug_fast_div(0) == fp.fp8pa_debug_fast_div(1)
+    L = _lib.lib()
+    assert L.fp8pa_debug_fast_div(7, None, None) == _lib.FP8PA_ERR_INVALID_ARG
