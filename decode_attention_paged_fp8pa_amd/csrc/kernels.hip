@@ -431,8 +431,8 @@ __device__ __forceinline__ Work work_head(const Params& p, int ds, int blk) {
 // thing: the chain seq_lens -> work item -> block table -> K/V pages is the
 // kernel's critical path, and everything else the prologue loads can wait.
 // A descriptor sized to the batch returns 0 past it, so the four loads are
-// branch-free and all in flight together.  (Only the balanced plan reads
-// them.)
+// branch-free and all in flight together.  The balanced plan reads them
+// all; fixed plans read their own sequence's from them.
 struct SeqLens {
   int v[4];
 };
@@ -459,7 +459,15 @@ __device__ __forceinline__ void work_item(const Params& p, Work& w, int blk, con
     w.b = fdiv(item, p.d_ns);
     w.split = item - w.b * p.num_splits;
     w.nsplit = p.num_splits;
-    w.L = seq_len_of(p, w.b);
+    // (from the early loads for the first 256 sequences: lane b & 63 of load
+    // b >> 6; a later sequence of a larger batch is loaded here)
+    if (w.b < 256) {
+      const int j = w.b >> 6;
+      const int v = j == 0 ? sl.v[0] : j == 1 ? sl.v[1] : j == 2 ? sl.v[2] : sl.v[3];
+      w.L = min(max(__builtin_amdgcn_readlane(v, w.b & 63), 0), p.max_seq_len);
+    } else {
+      w.L = seq_len_of(p, w.b);
+    }
     w.sp = span_of(w.L, p.q_len, p.window);
     w.ts = w.sp.tile0 + w.split * p.tps;
     w.te = min(w.ts + p.tps, w.sp.tile1);
