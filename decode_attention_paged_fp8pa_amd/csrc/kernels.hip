@@ -396,7 +396,7 @@ __device__ __forceinline__ int logical_block(int i) {
 // trip to memory before the first vector load can go out.  An empty asm that
 // takes them all as scalar operands makes them all live at its point, and
 // the workgroup index it passes through (and returns) makes every step of
-// the work item come after it
+// the work item come after it.
 __device__ __forceinline__ int prologue_args(const Params& p) {
   int blk = blockIdx.x;
   asm volatile("" : "+s"(blk)
@@ -439,7 +439,8 @@ struct SeqLens {
 
 __device__ __forceinline__ SeqLens seq_lens_in_flight(const Params& p) {
   const int lane = threadIdx.x & 63;
-  const Rsrc slr = __builtin_amdgcn_make_buffer_rsrc((void*)p.seq_lens, 0, p.B * 4, kRsrcWord3);
+  // (the size in bytes saturates: lanes read at most sequence 255)
+  const Rsrc slr = __builtin_amdgcn_make_buffer_rsrc((void*)p.seq_lens, 0, min(p.B, 0x1fffffff) * 4, kRsrcWord3);
   SeqLens s;
 #pragma unroll
   for (int j = 0; j < 4; ++j) s.v[j] = int(__builtin_amdgcn_raw_buffer_load_b32(slr, uint32_t(lane + 64 * j) * 4u, 0, 0));
